@@ -1,0 +1,25 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    config.addinivalue_line("markers", "slow: builds large synthetic tables or corpora")
+
+
+@pytest.fixture(scope="session")
+def tiny_workload():
+    from synth import configs
+    return configs.tiny()
+
+
+@pytest.fixture(scope="session")
+def tiny_oracle(tiny_workload):
+    from oracle import Oracle
+    return Oracle(tiny_workload.tokens, tiny_workload.specials, tiny_workload.grammar)
