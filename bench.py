@@ -1,0 +1,178 @@
+"""Encode throughput of the byte-level BPE path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload main]
+
+One step is one bbpe_encode_segments call over the whole workload (every
+step of the path: UTF-8 validation, chunk cuts, specials, split, merge,
+ordered assembly), with the text, offsets, tables and workspace already
+resident in device memory.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "encode input MB/s + tokens/s on 1 MI355X; % of HBM roofline; ids bit-exact"
+HBM_PEAK_GBS = 8000.0
+
+WORKLOAD_DESC = {
+    "main": "main: one 4,200,000-byte allow_special=false segment (70% prose, 15% JSON, 10% code, "
+            "5% multibyte), 100,256-rank table + 5 specials, cl100k split, tiktoken-safe",
+    "tiny": "tiny: one 65,536-byte ASCII segment, 1,280-rank table, cl100k split",
+    "agentic": "agentic: 300 typed segments, 4,000,000 characters, 100,256-rank table",
+    "ragged": "ragged: 4,096 requests of 512-8,192 bytes, 100,256-rank table",
+}
+
+
+def algorithmic_bytes(kernel: str, n: int, n_seg: int, n_ids: int, n_pieces: int,
+                      table_bytes_touched: int) -> int:
+    """Bytes a kernel must move by the definition of its step (one launch).
+
+    k_merge: the pieces' bytes, their start offsets, the ids and the
+      per-piece id counts it writes, and the rank-table traffic of the
+      method's merge loop (key bytes + 4 per lookup, counted by the oracle).
+    front kernels (one pass over the text): the text bytes plus 64-bit masks
+      in and out (1/8 byte per text byte each).
+    """
+    if kernel == "k_merge":
+        return n + 4 * n_pieces + 4 * n_ids + 4 * n_pieces + table_bytes_touched
+    if kernel in ("k_count", "k_spans", "k_split_agg", "k_split"):
+        return n + n // 8 * (3 if kernel != "k_count" else 1)
+    if kernel == "k_pieces":
+        return n // 8 + 4 * n_pieces
+    if kernel == "k_assemble":
+        return 4 * n_ids * 2 + 8 * n_pieces
+    return n
+
+
+def cpu_baseline(w, budget_s: float = 10.0, max_reps: int = 8) -> dict:
+    """The oracle (plain single-threaded C++) over the whole workload,
+    repeated until about budget_s seconds of CPU work."""
+    from oracle import Oracle
+    orc = Oracle(w.tokens, w.specials, w.grammar)
+    reps = 0
+    total = 0.0
+    n_ids = 0
+    while reps < max_reps and (total < budget_s or reps == 0):
+        t0 = time.perf_counter()
+        ids, _ = orc.encode_segments(w.segments, w.tiktoken_safe)
+        total += time.perf_counter() - t0
+        n_ids = len(ids)
+        reps += 1
+    nb = w.text_bytes
+    return {"value": round(nb * reps / total / 1e6, 3), "unit": "MB/s", "cores": 1,
+            "kind": "oracle",
+            "tokens_per_s": round(n_ids * reps / total, 1),
+            "sample": "whole %s workload (%d bytes) encoded %d times single-threaded, %.1f s"
+                      % (w.name, nb, reps, total)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="main")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: every box in this setup has a single MI355X and the "
+              "encode path here is single-GPU (see the multi-GPU design notes); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import byte_level_bpe_amd as B
+    from synth import configs
+
+    w = configs.ALL[args.workload]()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tok = B.load_ranks(w.tokens, w.specials, w.grammar)
+    text, seg_off, allow, total = B.to_device_segments(w.segments, dev)
+    n_seg = len(w.segments)
+    ids = torch.empty(max(1, total), dtype=torch.int32, device=dev)
+    id_off = torch.empty(n_seg + 1, dtype=torch.int64, device=dev)
+    tok.upload(dev)
+    tok.workspace(total, n_seg, dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        return tok.encode_device(text, seg_off, allow, total, w.tiktoken_safe, ids=ids,
+                                 id_off=id_off, stream=stream)[2]
+
+    for _ in range(args.warmup):
+        n_ids = step()
+    torch.cuda.synchronize()
+    tok.set_timing(True)
+    tok.timing_reset()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        n_ids = step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dev_ms = ev0.elapsed_time(ev1)
+    rep = tok.timing_report()
+    tok.set_timing(False)
+
+    ms_per_step = wall * 1e3 / args.steps
+    mbs = total * args.steps / wall / 1e6
+    tps = n_ids * args.steps / wall
+
+    # algorithmic bytes of the whole call (oracle-instrumented table traffic)
+    from oracle import Oracle
+    orc = Oracle(w.tokens, w.specials, w.grammar)
+    orc.reset_counters()
+    oids, _ = orc.encode_segments(w.segments, w.tiktoken_safe)
+    cnt = orc.counters()
+    assert len(oids) == n_ids, "id count differs from the oracle"
+    b_alg = total + 4 * n_ids + 8 * (n_seg + 1) + cnt["lookup_bytes"]
+    per_kernel = {k: v[0] / max(1, v[1]) for k, v in rep.items()}
+    dom = max(rep, key=lambda k: rep[k][0])
+    dom_ms = per_kernel[dom]
+    dom_bytes = algorithmic_bytes(dom, total, n_seg, n_ids, cnt["pieces"], cnt["lookup_bytes"])
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(mbs, 2),
+        "unit": "MB/s",
+        "tokens_per_s": round(tps, 1),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "device_ms_per_step": round(dev_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_DESC.get(args.workload, args.workload),
+                   "bytes": total, "segments": n_seg, "ids": n_ids, "ranks": len(w.tokens)},
+        "call_roofline": {"alg_bytes": b_alg, "frac_of_8TBs": round(b_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+                          "pieces": cnt["pieces"], "table_bytes": cnt["lookup_bytes"]},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
+                     "traffic": None, "avg_ms": round(dom_ms, 5), "alg_bytes_per_launch": dom_bytes},
+        "kernels_avg_ms": {k: round(v, 5) for k, v in sorted(per_kernel.items(), key=lambda kv: -kv[1])},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,298 @@
+// Device helpers for the gfx950 kernels: the per-lane 64-byte text window,
+// UTF-8 decoding into per-word class bitmasks, and wave64 scans.
+//
+// Layout: one lane owns one "word" of 64 consecutive text bytes; bit i of a
+// 64-bit mask describes byte (64*word + i).  A character's class bits are set
+// on all of its bytes; LEAD marks its first byte.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bbpe_internal.h"
+
+namespace bbpe {
+
+// ---------------------------------------------------------------------------
+// Cross-word shifts.  shl(x, prev, k): bit i takes x's bit i-k (bytes before,
+// from the previous word for i < k).  shr(x, next, k): bit i takes bit i+k.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t shl(uint64_t x, uint64_t prev, int k) {
+  return (x << k) | (prev >> (64 - k));
+}
+__device__ __forceinline__ uint64_t shr(uint64_t x, uint64_t next, int k) {
+  return (x >> k) | (next << (64 - k));
+}
+__device__ __forceinline__ uint64_t bit(int i) { return uint64_t(1) << i; }
+
+__device__ __forceinline__ uint64_t shfl_up64(uint64_t v, int d) {
+  return __shfl_up(static_cast<unsigned long long>(v), d, 64);
+}
+__device__ __forceinline__ uint64_t shfl_down64(uint64_t v, int d) {
+  return __shfl_down(static_cast<unsigned long long>(v), d, 64);
+}
+
+// Inclusive prefix sum over the 64 lanes of the wave.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+__device__ __forceinline__ int64_t wave_incl_max(int64_t v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int64_t o = __shfl_up(static_cast<long long>(v), d, 64);
+    if (lane >= d && o > v) v = o;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// 96-byte text window of a lane: bytes [base-16, base+80) of the text, zero
+// outside [0, n).  Loaded with 16-byte vector loads where fully in range.
+// ---------------------------------------------------------------------------
+struct Window {
+  uint32_t w[24];
+  __device__ __forceinline__ uint32_t at(int k) const {  // k in [-16, 80)
+    const int q = k + 16;
+    return (w[q >> 2] >> ((q & 3) * 8)) & 0xFFu;
+  }
+};
+
+__device__ __forceinline__ void load_window(const uint8_t *__restrict__ text, uint64_t n,
+                                            int64_t base, Window &win) {
+  if (base >= 16 && uint64_t(base) + 80 <= n) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(text + base - 16);
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      const uint4 v = p[q];
+      win.w[4 * q + 0] = v.x;
+      win.w[4 * q + 1] = v.y;
+      win.w[4 * q + 2] = v.z;
+      win.w[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 24; ++q) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int64_t idx = base - 16 + 4 * q + j;
+        uint32_t b = (idx >= 0 && uint64_t(idx) < n) ? uint32_t(text[idx]) : 0u;
+        v |= b << (8 * j);
+      }
+      win.w[q] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-word masks.
+// ---------------------------------------------------------------------------
+struct WordMasks {
+  uint64_t valid;  // byte index < n
+  uint64_t lead;   // first byte of a character (stray bytes count as their own char)
+  uint64_t L;      // \p{L}
+  uint64_t N;      // \p{N}
+  uint64_t WS;     // \s (White_Space)
+  uint64_t CR;     // \r or \n
+  uint64_t SP;     // U+0020
+  uint64_t AP;     // U+0027
+  uint64_t M;      // \p{M}
+  uint64_t LU;     // Lu, Lt
+  uint64_t LL;     // Ll
+  uint64_t LB;     // Lm, Lo
+  // ASCII byte patterns for the contraction clause: s d m t / l / v / e / r
+  // (either case), and the two bytes of U+017F
+  uint64_t c_sdmt, c_l, c_v, c_e, c_r, c_ls0, c_ls1;
+  uint32_t err;    // first invalid-sequence byte in [0,64), or 64
+};
+
+__device__ __forceinline__ uint32_t class_of(const DevTables &T, uint32_t cp) {
+  if (cp < 0x80) {
+    const uint32_t lc = cp | 0x20u;
+    if (cp >= 'A' && cp <= 'Z') return CC_LU;
+    if (lc >= 'a' && lc <= 'z') return CC_LL;
+    if (cp >= '0' && cp <= '9') return CC_N;
+    if (cp == ' ' || (cp >= 9 && cp <= 13)) return CC_WS;
+    return CC_OTHER;
+  }
+  const uint32_t blk = T.uni1[cp >> 8];
+  return T.uni2[blk * 256u + (cp & 0xFFu)];
+}
+
+// Length of the UTF-8 sequence announced by a lead byte, 0 if the byte
+// cannot start a sequence.
+__device__ __forceinline__ int utf8_len(uint32_t b) {
+  if (b < 0x80) return 1;
+  if (b < 0xC2) return 0;
+  if (b < 0xE0) return 2;
+  if (b < 0xF0) return 3;
+  if (b < 0xF5) return 4;
+  return 0;
+}
+
+// Decodes the sequence starting at window index k; ok = a complete, minimal,
+// non-surrogate code point <= U+10FFFF that crosses no segment start.
+// segmask bit j (j in [0,128)) marks a segment start at window index j-8.
+__device__ __forceinline__ uint32_t decode_at(const Window &win, int k, uint64_t seg_lo,
+                                              uint64_t seg_hi, int64_t avail, int &len,
+                                              bool &ok) {
+  const uint32_t b0 = win.at(k);
+  len = utf8_len(b0);
+  ok = len > 0 && len <= avail;
+  if (len <= 1) return b0;
+  uint32_t cp = b0 & (0x7Fu >> len);
+#pragma unroll
+  for (int j = 1; j < 4; ++j) {
+    if (j < len) {
+      const uint32_t b = win.at(k + j);
+      ok = ok && ((b & 0xC0u) == 0x80u);
+      const int s = k + j + 8;  // position in segmask
+      const bool segstart = s < 64 ? ((seg_lo >> s) & 1) : ((seg_hi >> (s - 64)) & 1);
+      ok = ok && !segstart;
+      cp = (cp << 6) | (b & 0x3Fu);
+    }
+  }
+  if (len == 3 && cp < 0x800) ok = false;
+  if (len == 4 && (cp < 0x10000 || cp > 0x10FFFF)) ok = false;
+  if (cp >= 0xD800 && cp <= 0xDFFF) ok = false;
+  return cp;
+}
+
+// Classify the 64 bytes of one word.  base: absolute offset of byte 0;
+// n: text length; seg_lo/seg_hi: segment starts at window indices -8..119.
+__device__ __forceinline__ void classify_word(const DevTables &T, const Window &win,
+                                              int64_t base, uint64_t n, uint64_t seg_lo,
+                                              uint64_t seg_hi, WordMasks &m) {
+  m.valid = 0;
+  if (base >= 0 && uint64_t(base) < n) {
+    const uint64_t left = n - uint64_t(base);
+    m.valid = left >= 64 ? ~uint64_t(0) : (bit(int(left)) - 1);
+  }
+  m.lead = m.L = m.N = m.WS = m.CR = m.SP = m.AP = m.M = m.LU = m.LL = m.LB = 0;
+  m.c_sdmt = m.c_l = m.c_v = m.c_e = m.c_r = m.c_ls0 = m.c_ls1 = 0;
+  m.err = 64;
+  if (!m.valid) return;
+  const int64_t avail0 = int64_t(n) - base;  // bytes available from index 0
+
+  // The character covering byte 0 may start up to three bytes earlier: find
+  // the nearest non-continuation byte among the three before and decode it.
+  uint32_t cur = CC_OTHER;
+  int rem = 0;
+  {
+    int kf = 0;
+    if ((win.at(-1) & 0xC0u) != 0x80u) kf = 1;
+    else if ((win.at(-2) & 0xC0u) != 0x80u) kf = 2;
+    else if ((win.at(-3) & 0xC0u) != 0x80u) kf = 3;
+    if (kf > 0 && base - kf >= 0) {
+      int len = 0;
+      bool ok = false;
+      uint32_t cp = 0;
+      if (kf == 1) cp = decode_at(win, -1, seg_lo, seg_hi, avail0 + 1, len, ok);
+      else if (kf == 2) cp = decode_at(win, -2, seg_lo, seg_hi, avail0 + 2, len, ok);
+      else cp = decode_at(win, -3, seg_lo, seg_hi, avail0 + 3, len, ok);
+      if (ok && len > kf) {
+        cur = class_of(T, cp);
+        rem = len - kf;
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const uint32_t b = win.at(i);
+    const bool cont_byte = (b & 0xC0u) == 0x80u;
+    const bool seg_i = (i + 8 < 64) ? ((seg_lo >> (i + 8)) & 1) : ((seg_hi >> (i + 8 - 64)) & 1);
+    uint32_t cls;
+    bool is_lead;
+    if (cont_byte && rem > 0 && !seg_i) {
+      --rem;
+      cls = cur;
+      is_lead = false;
+    } else {
+      is_lead = true;
+      if (cont_byte) {
+        cls = CC_OTHER;  // stray continuation byte
+        rem = 0;
+        if (m.err == 64) m.err = uint32_t(i);
+      } else {
+        int len;
+        bool ok;
+        const uint32_t cp = decode_at(win, i, seg_lo, seg_hi, avail0 - i, len, ok);
+        cls = ok ? class_of(T, cp) : uint32_t(CC_OTHER);
+        rem = ok ? len - 1 : 0;
+        if (!ok && m.err == 64) m.err = uint32_t(i);
+      }
+      cur = cls;
+    }
+    const uint64_t bi = bit(i);
+    if (is_lead) m.lead |= bi;
+    if (cls == CC_LU) { m.L |= bi; m.LU |= bi; }
+    if (cls == CC_LL) { m.L |= bi; m.LL |= bi; }
+    if (cls == CC_LO) { m.L |= bi; m.LB |= bi; }
+    if (cls == CC_N) m.N |= bi;
+    if (cls == CC_WS) m.WS |= bi;
+    if (cls == CC_M) m.M |= bi;
+    if (b == '\r' || b == '\n') m.CR |= bi;
+    if (b == ' ') m.SP |= bi;
+    if (b == '\'') m.AP |= bi;
+    const uint32_t lc = b | 0x20u;
+    if (lc == 's' || lc == 'd' || lc == 'm' || lc == 't') m.c_sdmt |= bi;
+    if (lc == 'l') m.c_l |= bi;
+    if (lc == 'v') m.c_v |= bi;
+    if (lc == 'e') m.c_e |= bi;
+    if (lc == 'r') m.c_r |= bi;
+    if (b == 0xC5) m.c_ls0 |= bi;
+    if (b == 0xBF) m.c_ls1 |= bi;
+  }
+  // bytes past the end of the text belong to nothing
+  const uint64_t v = m.valid;
+  m.lead &= v; m.L &= v; m.N &= v; m.WS &= v; m.CR &= v; m.SP &= v; m.AP &= v; m.M &= v;
+  m.LU &= v; m.LL &= v; m.LB &= v;
+  m.c_sdmt &= v; m.c_l &= v; m.c_v &= v; m.c_e &= v; m.c_r &= v; m.c_ls0 &= v; m.c_ls1 &= v;
+  if (m.err < 64 && !((v >> m.err) & 1)) m.err = 64;
+}
+
+// Segment starts at window indices -8..119 of a lane (bit j <-> index j-8),
+// found by binary search in seg_off[0..n_seg].  Also returns the index of the
+// last non-empty... segment containing byte `base` (or the first segment).
+__device__ __forceinline__ void segment_marks(const uint64_t *__restrict__ seg_off, uint32_t n_seg,
+                                              int64_t base, uint64_t &lo, uint64_t &hi,
+                                              uint32_t &seg_at_base) {
+  lo = hi = 0;
+  // first s with seg_off[s] >= base - 8
+  const int64_t from = base - 8;
+  uint32_t a = 0, b = n_seg;  // search in [0, n_seg)
+  while (a < b) {
+    uint32_t mid = (a + b) >> 1;
+    if (int64_t(seg_off[mid]) < from) a = mid + 1;
+    else b = mid;
+  }
+  for (uint32_t s = a; s < n_seg; ++s) {
+    const int64_t o = int64_t(seg_off[s]);
+    if (o >= base + 120) break;
+    const int j = int(o - from);
+    if (j < 64) lo |= bit(j);
+    else hi |= bit(j - 64);
+  }
+  // segment containing byte base: last s with seg_off[s] <= base
+  a = 0;
+  b = n_seg;
+  while (a < b) {
+    uint32_t mid = (a + b) >> 1;
+    if (int64_t(seg_off[mid]) <= base) a = mid + 1;
+    else b = mid;
+  }
+  seg_at_base = a > 0 ? a - 1 : 0;
+}
+
+}  // namespace bbpe

@@ -1,0 +1,379 @@
+// Host planner of the encode path: table upload, workspace layout and the
+// kernel sequence of bbpe_encode_segments / bbpe_pretokenize_segments.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <algorithm>
+#include <utility>
+#include <vector>
+
+#include "../../include/bbpe.h"
+#include "bbpe_internal.h"
+#include "bbpe_kernels.h"
+#include "bbpe_tokenizer.h"
+
+using namespace bbpe;
+
+namespace {
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+struct WsLayout {
+  uint64_t status, tile_nchar, tile_lastchg, tile_charbase, tile_chgcarry, seg_local, seg_charstart,
+      ss, spst, spc, ps, tile_fn, tile_carry, tile_np, piece_start, piece_cnt, tmp_ids, scan_part,
+      long_list, lrank, lpart, lalive, lmin, total;
+  uint64_t n_words;
+  uint32_t n_tiles;
+};
+
+WsLayout layout_for(uint64_t n, uint32_t n_seg) {
+  WsLayout L{};
+  const uint64_t W = (n + 63) / 64;
+  const uint64_t T = (W + TILE_WORDS - 1) / TILE_WORDS;
+  L.n_words = W;
+  L.n_tiles = uint32_t(T);
+  uint64_t o = 0;
+  auto take = [&](uint64_t &field, uint64_t bytes) {
+    field = o;
+    o = align256(o + bytes);
+  };
+  take(L.status, sizeof(Status));
+  take(L.tile_nchar, 4 * (T + 1));
+  take(L.tile_lastchg, 4 * (T + 1));
+  take(L.tile_charbase, 8 * (T + 1));
+  take(L.tile_chgcarry, 8 * (T + 1));
+  take(L.seg_local, 4 * (uint64_t(n_seg) + 1));
+  take(L.seg_charstart, 8 * (uint64_t(n_seg) + 1));
+  take(L.ss, 8 * (W + 1));
+  take(L.spst, 8 * (W + 1));
+  take(L.spc, 8 * (W + 1));
+  take(L.ps, 8 * (W + 1));
+  take(L.tile_fn, 4 * (T + 1));
+  take(L.tile_carry, 4 * (T + 1));
+  take(L.tile_np, 4 * (T + 1));
+  take(L.piece_start, 4 * (n + 1));
+  take(L.piece_cnt, 4 * (n + 1));
+  take(L.tmp_ids, 4 * (n + 1));
+  take(L.scan_part, 4 * ((n + 1) / 4096 + 2));
+  take(L.long_list, 4 * (n / 64 + 1));
+  take(L.lrank, 4 * (n + 1));
+  take(L.lpart, 4 * (n + 1));
+  take(L.lalive, n + 1);
+  take(L.lmin, 8 * (n / 32 + 2));
+  L.total = o;
+  return L;
+}
+
+__global__ void k_init(EncodeArgs a) {
+  if (threadIdx.x == 0) {
+    Status *s = a.ws.status;
+    s->err_pos = ~0ull;
+    s->n_pieces = 0;
+    s->n_ids = 0;
+    s->n_long = 0;
+    s->pad = 0;
+    s->n_chars = 0;
+    s->err_seg = 0;
+    // offsets must start at 0 and end at the text length (monotonicity is
+    // checked by k_check_offsets); every later kernel exits when pad2 is set
+    const bool ok = a.seg_off[0] == 0 && a.seg_off[a.n_seg] == a.n;
+    s->pad2 = ok ? 0u : 1u;
+  }
+}
+
+__global__ void k_check_offsets(EncodeArgs a) {
+  for (uint32_t s = blockIdx.x * blockDim.x + threadIdx.x; s < a.n_seg; s += gridDim.x * blockDim.x)
+    if (a.seg_off[s + 1] < a.seg_off[s]) a.ws.status->pad2 = 1u;
+}
+
+// id offsets of an empty text: all zero
+__global__ void k_zero_offsets(EncodeArgs a) {
+  for (uint32_t s = blockIdx.x * blockDim.x + threadIdx.x; s <= a.n_seg; s += gridDim.x * blockDim.x)
+    a.id_off[s] = 0;
+}
+
+__global__ void k_copy_pieces(EncodeArgs a, uint32_t *starts, uint64_t cap, uint8_t *is_special) {
+  if (a.ws.status->pad2) return;
+  const uint32_t P = uint32_t(a.ws.status->n_pieces);
+  if (P > cap) return;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < P; i += gridDim.x * blockDim.x) {
+    const uint32_t s = a.ws.piece_start[i];
+    starts[i] = s;
+    if (is_special) is_special[i] = uint8_t((a.ws.spst[s >> 6] >> (s & 63)) & 1);
+  }
+}
+
+__global__ void k_err_seg(EncodeArgs a) {
+  const unsigned long long e = a.ws.status->err_pos;
+  if (threadIdx.x == 0 && e != ~0ull) {
+    uint32_t lo = 0, hi = a.n_seg;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (a.seg_off[mid] <= e) lo = mid + 1;
+      else hi = mid;
+    }
+    a.ws.status->err_seg = lo > 0 ? lo - 1 : 0;
+  }
+}
+
+#define HIP_OK(x)                               \
+  do {                                          \
+    if ((x) != hipSuccess) return BBPE_E_HIP;   \
+  } while (0)
+
+// Launches kernels on one stream; with timing enabled on the handle, every
+// launch is bracketed by two events from the handle's pool.
+struct Launcher {
+  bbpe_tokenizer *t;
+  hipStream_t st;
+  std::vector<std::pair<int, size_t>> recs;  // (kernel index, first event)
+  size_t next = 0;
+
+  int kernel_index(const char *name) {
+    for (size_t i = 0; i < t->t_names.size(); ++i)
+      if (t->t_names[i] == name) return int(i);
+    t->t_names.emplace_back(name);
+    t->t_ms.push_back(0.0);
+    t->t_launches.push_back(0);
+    return int(t->t_names.size() - 1);
+  }
+  hipEvent_t event(size_t i) {
+    while (t->t_events.size() <= i) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) e = nullptr;
+      t->t_events.push_back(e);
+    }
+    return static_cast<hipEvent_t>(t->t_events[i]);
+  }
+  template <typename K, typename... A>
+  void operator()(const char *name, K kernel, dim3 grid, dim3 block, A... args) {
+    const bool timed = t->timing;
+    if (timed) (void)hipEventRecord(event(next), st);
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+    if (timed) {
+      (void)hipEventRecord(event(next + 1), st);
+      recs.emplace_back(kernel_index(name), next);
+      next += 2;
+    }
+  }
+  // after the stream has been synchronised
+  void collect() {
+    for (auto &r : recs) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, event(r.second), event(r.second + 1)) == hipSuccess) {
+        t->t_ms[size_t(r.first)] += ms;
+        t->t_launches[size_t(r.first)] += 1;
+      }
+    }
+    recs.clear();
+  }
+};
+
+// Validates arguments and carves the workspace.
+int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t *d_seg_off,
+            const uint8_t *d_allow, uint32_t n_seg, uint32_t flags, void *d_ws, uint64_t ws_bytes,
+            EncodeArgs &a, WsLayout &L) {
+  if (!t || !d_seg_off || (n_seg && !d_allow)) return BBPE_E_INVALID_ARG;
+  if (n && (!d_text || (reinterpret_cast<uintptr_t>(d_text) & 15))) return BBPE_E_INVALID_ARG;
+  if (n >= (uint64_t(1) << 32) - 64 || (flags & ~uint32_t(BBPE_TIKTOKEN_SAFE))) return BBPE_E_INVALID_ARG;
+  if (n_seg == 0 && n != 0) return BBPE_E_INVALID_ARG;
+  if (!t->d_image) return BBPE_E_STATE;
+  if (t->grammar != BBPE_GRAMMAR_CL100K) return BBPE_E_INVALID_ARG;  // o200k-style split: not built yet
+  L = layout_for(n, n_seg);
+  if (!d_ws || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(d_ws) & 255)) return BBPE_E_WORKSPACE;
+  uint8_t *w = static_cast<uint8_t *>(d_ws);
+  a = EncodeArgs{};
+  a.T = t->dev;
+  a.text = d_text;
+  a.n = n;
+  a.seg_off = d_seg_off;
+  a.allow = d_allow;
+  a.n_seg = n_seg;
+  a.flags = flags;
+  a.n_words = L.n_words;
+  a.n_tiles = L.n_tiles;
+  a.ws.status = reinterpret_cast<Status *>(w + L.status);
+  a.ws.tile_nchar = reinterpret_cast<uint32_t *>(w + L.tile_nchar);
+  a.ws.tile_lastchg = reinterpret_cast<int32_t *>(w + L.tile_lastchg);
+  a.ws.tile_charbase = reinterpret_cast<unsigned long long *>(w + L.tile_charbase);
+  a.ws.tile_chgcarry = reinterpret_cast<long long *>(w + L.tile_chgcarry);
+  a.ws.seg_local = reinterpret_cast<uint32_t *>(w + L.seg_local);
+  a.ws.seg_charstart = reinterpret_cast<unsigned long long *>(w + L.seg_charstart);
+  a.ws.ss = reinterpret_cast<uint64_t *>(w + L.ss);
+  a.ws.spst = reinterpret_cast<uint64_t *>(w + L.spst);
+  a.ws.spc = reinterpret_cast<uint64_t *>(w + L.spc);
+  a.ws.ps = reinterpret_cast<uint64_t *>(w + L.ps);
+  a.ws.tile_fn = reinterpret_cast<uint32_t *>(w + L.tile_fn);
+  a.ws.tile_carry = reinterpret_cast<uint32_t *>(w + L.tile_carry);
+  a.ws.tile_np = reinterpret_cast<uint32_t *>(w + L.tile_np);
+  a.ws.piece_start = reinterpret_cast<uint32_t *>(w + L.piece_start);
+  a.ws.piece_cnt = reinterpret_cast<uint32_t *>(w + L.piece_cnt);
+  a.ws.tmp_ids = reinterpret_cast<int32_t *>(w + L.tmp_ids);
+  a.ws.scan_part = reinterpret_cast<uint32_t *>(w + L.scan_part);
+  a.ws.long_list = reinterpret_cast<uint32_t *>(w + L.long_list);
+  a.ws.lrank = reinterpret_cast<int32_t *>(w + L.lrank);
+  a.ws.lpart = reinterpret_cast<int32_t *>(w + L.lpart);
+  a.ws.lalive = w + L.lalive;
+  a.ws.lmin = reinterpret_cast<unsigned long long *>(w + L.lmin);
+  return BBPE_OK;
+}
+
+// Steps up to the ordered list of piece starts.
+void launch_front(Launcher &go, const EncodeArgs &a, const WsLayout &L) {
+  go("k_init", k_init, dim3(1), dim3(64), a);
+  if (a.n_seg)
+    go("k_check_offsets", k_check_offsets, dim3(std::min<uint32_t>(1024, (a.n_seg + 255) / 256)),
+       dim3(256), a);
+  if (a.n == 0) return;
+  const uint32_t T = L.n_tiles;
+  go("k_count", k_count, dim3(T), dim3(64), a);
+  go("k_scan_chars", k_scan_chars, dim3(1), dim3(1024), a);
+  go("k_spans", k_spans, dim3(T), dim3(64), a);
+  go("k_split_agg", k_split_agg, dim3(T), dim3(64), a);
+  go("k_scan_split", k_scan_split, dim3(1), dim3(1024), a);
+  go("k_split", k_split, dim3(T), dim3(64), a);
+  go("k_scan_tiles_np", k_scan_tiles_np, dim3(1), dim3(1024), a);
+  go("k_pieces", k_pieces, dim3(T), dim3(64), a);
+}
+
+// Reads the status block (the call's one host synchronisation).
+int finish(bbpe_tokenizer *t, Launcher &go, const EncodeArgs &a, Status &h) {
+  HIP_OK(hipGetLastError());
+  HIP_OK(hipMemcpyAsync(&h, a.ws.status, sizeof(Status), hipMemcpyDeviceToHost, go.st));
+  HIP_OK(hipStreamSynchronize(go.st));
+  go.collect();
+  if (h.pad2) return BBPE_E_INVALID_ARG;
+  if (h.err_pos != ~0ull) {
+    t->err_seg = h.err_seg;
+    t->err_byte = h.err_pos;
+    return BBPE_E_UTF8;
+  }
+  return BBPE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bbpe_upload_tables(bbpe_tokenizer *t, void *d_mem, uint64_t bytes, void *stream) {
+  if (!t || !d_mem) return BBPE_E_INVALID_ARG;
+  if (bytes < t->layout.total || (reinterpret_cast<uintptr_t>(d_mem) & 255)) return BBPE_E_INVALID_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  HIP_OK(hipMemcpyAsync(d_mem, t->image.data(), t->layout.total, hipMemcpyHostToDevice, st));
+  HIP_OK(hipStreamSynchronize(st));
+  const uint8_t *b = static_cast<const uint8_t *>(d_mem);
+  const ImageLayout &L = t->layout;
+  DevTables &d = t->dev;
+  d.slots = reinterpret_cast<const Slot *>(b + L.slots);
+  d.blob = b + L.blob;
+  d.pair = reinterpret_cast<const int32_t *>(b + L.pair);
+  d.atom = reinterpret_cast<const int32_t *>(b + L.atom);
+  d.uni1 = reinterpret_cast<const uint16_t *>(b + L.uni1);
+  d.uni2 = b + L.uni2;
+  d.sp_bytes = b + L.sp_bytes;
+  d.sp_off = reinterpret_cast<const uint32_t *>(b + L.sp_off);
+  d.sp_id = reinterpret_cast<const int32_t *>(b + L.sp_id);
+  t->d_image = b;
+  return BBPE_OK;
+}
+
+int bbpe_workspace_bytes(const bbpe_tokenizer *t, uint64_t n, uint32_t n_seg, uint64_t *out) {
+  if (!t || !out) return BBPE_E_INVALID_ARG;
+  if (n >= (uint64_t(1) << 32) - 64) return BBPE_E_INVALID_ARG;
+  *out = layout_for(n, n_seg).total;
+  return BBPE_OK;
+}
+
+int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
+                         const uint64_t *d_seg_off, const uint8_t *d_allow, uint32_t n_seg,
+                         uint32_t flags, void *d_ws, uint64_t ws_bytes, int32_t *d_ids,
+                         uint64_t ids_cap, int64_t *d_id_off, uint64_t *n_ids, void *stream) {
+  if (!d_id_off || !n_ids || (ids_cap && !d_ids)) return BBPE_E_INVALID_ARG;
+  EncodeArgs a;
+  WsLayout L;
+  int rc = prepare(t, d_text, n, d_seg_off, d_allow, n_seg, flags, d_ws, ws_bytes, a, L);
+  if (rc) return rc;
+  a.ids = d_ids;
+  a.ids_cap = ids_cap;
+  a.id_off = d_id_off;
+  Launcher go{t, reinterpret_cast<hipStream_t>(stream)};
+  launch_front(go, a, L);
+  const uint32_t seg_grid = std::min<uint32_t>(1024, (n_seg + 256) / 256);
+  if (n == 0) {
+    go("k_zero_offsets", k_zero_offsets, dim3(seg_grid), dim3(256), a);
+  } else {
+    const uint32_t merge_grid = uint32_t(std::min<uint64_t>((n + 63) / 64, 8192));
+    go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
+    const uint32_t long_grid = uint32_t(std::min<uint64_t>(n / 64 + 1, 2048));
+    go("k_merge_long", k_merge_long, dim3(long_grid), dim3(64), a);
+    const uint32_t nscan = uint32_t((n + 1 + 4095) / 4096);
+    go("k_scan_reduce", k_scan_reduce, dim3(nscan), dim3(256), a);
+    go("k_scan_partials", k_scan_partials, dim3(1), dim3(1024), a);
+    go("k_scan_down", k_scan_down, dim3(nscan), dim3(256), a);
+    const uint32_t agrid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
+    go("k_assemble", k_assemble, dim3(agrid), dim3(256), a);
+    go("k_seg_offsets", k_seg_offsets, dim3(seg_grid), dim3(256), a);
+  }
+  Status h{};
+  rc = finish(t, go, a, h);
+  if (rc) return rc;
+  *n_ids = h.n_ids;
+  if (h.n_ids > ids_cap) return BBPE_E_CAPACITY;
+  return BBPE_OK;
+}
+
+int bbpe_pretokenize_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
+                              const uint64_t *d_seg_off, const uint8_t *d_allow, uint32_t n_seg,
+                              uint32_t flags, void *d_ws, uint64_t ws_bytes, uint32_t *d_starts,
+                              uint64_t starts_cap, uint8_t *d_is_special, uint64_t *n_pieces,
+                              void *stream) {
+  if (!n_pieces || (starts_cap && !d_starts)) return BBPE_E_INVALID_ARG;
+  EncodeArgs a;
+  WsLayout L;
+  int rc = prepare(t, d_text, n, d_seg_off, d_allow, n_seg, flags, d_ws, ws_bytes, a, L);
+  if (rc) return rc;
+  Launcher go{t, reinterpret_cast<hipStream_t>(stream)};
+  launch_front(go, a, L);
+  if (n) {
+    const uint32_t g = uint32_t(std::min<uint64_t>((n + 255) / 256, 4096));
+    go("k_copy_pieces", k_copy_pieces, dim3(g), dim3(256), a, d_starts, starts_cap, d_is_special);
+    go("k_err_seg", k_err_seg, dim3(1), dim3(64), a);
+  }
+  Status h{};
+  rc = finish(t, go, a, h);
+  if (rc) return rc;
+  *n_pieces = h.n_pieces;
+  if (h.n_pieces > starts_cap) return BBPE_E_CAPACITY;
+  return BBPE_OK;
+}
+
+int bbpe_set_timing(bbpe_tokenizer *t, int enable) {
+  if (!t) return BBPE_E_INVALID_ARG;
+  t->timing = enable != 0;
+  return BBPE_OK;
+}
+
+int bbpe_timing_report(const bbpe_tokenizer *t, uint32_t idx, const char **name, double *total_ms,
+                       uint64_t *launches) {
+  if (!t || idx >= t->t_names.size()) return BBPE_E_INVALID_ARG;
+  if (name) *name = t->t_names[idx].c_str();
+  if (total_ms) *total_ms = t->t_ms[idx];
+  if (launches) *launches = t->t_launches[idx];
+  return BBPE_OK;
+}
+
+void bbpe_free(bbpe_tokenizer *t) {
+  if (!t) return;
+  for (void *e : t->t_events)
+    if (e) (void)hipEventDestroy(static_cast<hipEvent_t>(e));
+  delete t;
+}
+
+int bbpe_timing_reset(bbpe_tokenizer *t) {
+  if (!t) return BBPE_E_INVALID_ARG;
+  for (auto &v : t->t_ms) v = 0.0;
+  for (auto &v : t->t_launches) v = 0;
+  return BBPE_OK;
+}
+
+}  // extern "C"

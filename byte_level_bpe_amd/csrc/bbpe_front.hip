@@ -1,0 +1,286 @@
+// Front half of the encode path on gfx950: UTF-8 validation and character
+// counting, tiktoken-safe chunk cuts, special-token matching, and the split
+// into pre-tokens.  One wave (64 lanes) per tile; lane l of tile t looks at
+// text word 62*t + l - 1 and owns it for 1 <= l <= 62.
+#include <hip/hip_runtime.h>
+
+#include "bbpe_device.h"
+#include "bbpe_kernels.h"
+
+namespace bbpe {
+
+// ---------------------------------------------------------------------------
+// Step 1: classify every byte, report the first invalid UTF-8 sequence, count
+// characters per tile, record the last whitespace/non-whitespace change of
+// each tile (for the 25,000-character run cuts) and where each segment starts
+// in character terms.  Also clears the span masks written by step 3.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(64) k_count(EncodeArgs a) {
+  if (a.ws.status->pad2) return;
+  const int lane = threadIdx.x;
+  const uint32_t t = blockIdx.x;
+  const int64_t w = int64_t(t) * TILE_WORDS + lane - 1;
+  const int64_t base = w * 64;
+  const bool owned = lane >= 1 && lane <= int(TILE_WORDS) && w < int64_t(a.n_words);
+
+  Window win;
+  load_window(a.text, a.n, base, win);
+  uint64_t seg_lo, seg_hi;
+  uint32_t seg_at;
+  segment_marks(a.seg_off, a.n_seg, base, seg_lo, seg_hi, seg_at);
+  WordMasks m;
+  classify_word(a.T, win, base, a.n, seg_lo, seg_hi, m);
+
+  const uint64_t segb = ((seg_lo >> 8) | (seg_hi << 56)) & m.valid;  // segment starts in [0,64)
+  const uint64_t ws_prev = shfl_up64(m.WS, 1);
+  const uint64_t chg = m.lead & (segb | (m.WS ^ shl(m.WS, ws_prev, 1)));
+
+  const uint32_t nch = owned ? uint32_t(__popcll(m.lead)) : 0u;
+  const uint32_t incl = wave_incl_sum(nch, lane);
+  const uint32_t excl = incl - nch;
+  // local (tile) character index of this word's last change, or -1
+  int32_t last = -1;
+  if (owned && chg) {
+    const int hb = 63 - __clzll(chg);
+    last = int32_t(excl + uint32_t(__popcll(m.lead & (bit(hb) - 1))));
+  }
+  // max over lanes
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    int32_t o = __shfl_xor(last, d, 64);
+    last = o > last ? o : last;
+  }
+  if (lane == 63) {
+    a.ws.tile_nchar[t] = incl;  // owned lanes only contribute
+  }
+  if (lane == 0) a.ws.tile_lastchg[t] = last;
+
+  if (owned) {
+    if (m.err < 64) atomicMin(&a.ws.status->err_pos, (unsigned long long)(base + m.err));
+    // segment starts inside this word: their local character index
+    uint64_t sb = segb;
+    if (sb) {
+      // walk segments whose start lies in [base, base+64)
+      uint32_t s = seg_at;
+      while (s > 0 && a.seg_off[s - 1] >= uint64_t(base)) --s;
+      for (; s < a.n_seg && a.seg_off[s] < uint64_t(base) + 64; ++s) {
+        if (int64_t(a.seg_off[s]) < base) continue;
+        const int j = int(a.seg_off[s] - uint64_t(base));
+        a.ws.seg_local[s] = excl + uint32_t(__popcll(m.lead & (bit(j) - 1)));
+      }
+    }
+    a.ws.ss[w] = 0;
+    a.ws.spst[w] = 0;
+    a.ws.spc[w] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Step 2 (one workgroup): character base of every tile, character index of
+// every segment start, and the last run change before every tile.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) k_scan_chars(EncodeArgs a) {
+  if (a.ws.status->pad2) return;
+  __shared__ unsigned long long s_sum[1024];
+  __shared__ long long s_max[1024];
+  const uint32_t T = a.n_tiles;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t per = (T + 1023) / 1024;
+  const uint32_t t0 = tid * per, t1 = min(T, t0 + per);
+  unsigned long long sum = 0;
+  for (uint32_t t = t0; t < t1; ++t) sum += a.ws.tile_nchar[t];
+  s_sum[tid] = sum;
+  __syncthreads();
+  for (uint32_t d = 1; d < 1024; d <<= 1) {
+    unsigned long long v = tid >= d ? s_sum[tid - d] : 0;
+    __syncthreads();
+    s_sum[tid] += v;
+    __syncthreads();
+  }
+  unsigned long long run = s_sum[tid] - sum;  // exclusive
+  long long mx = -1;
+  for (uint32_t t = t0; t < t1; ++t) {
+    a.ws.tile_charbase[t] = run;
+    const int32_t lc = a.ws.tile_lastchg[t];
+    if (lc >= 0) mx = max(mx, (long long)(run + uint32_t(lc)));
+    run += a.ws.tile_nchar[t];
+  }
+  s_max[tid] = mx;
+  __syncthreads();
+  for (uint32_t d = 1; d < 1024; d <<= 1) {
+    long long v = tid >= d ? s_max[tid - d] : -1;
+    __syncthreads();
+    s_max[tid] = max(s_max[tid], v);
+    __syncthreads();
+  }
+  long long carry = tid > 0 ? s_max[tid - 1] : -1;
+  for (uint32_t t = t0; t < t1; ++t) {
+    a.ws.tile_chgcarry[t] = carry;
+    const int32_t lc = a.ws.tile_lastchg[t];
+    if (lc >= 0) carry = max(carry, (long long)(a.ws.tile_charbase[t] + uint32_t(lc)));
+  }
+  const unsigned long long total = s_sum[1023];
+  for (uint32_t s = tid; s <= a.n_seg; s += 1024) {
+    const uint64_t o = a.seg_off[s];
+    if (s == a.n_seg || o >= a.n) {
+      a.ws.seg_charstart[s] = total;
+    } else {
+      const uint32_t tile = uint32_t((o >> 6) / TILE_WORDS);
+      a.ws.seg_charstart[s] = a.ws.tile_charbase[tile] + a.ws.seg_local[s];
+    }
+  }
+  if (tid == 0) a.ws.status->n_chars = total;
+}
+
+// ---------------------------------------------------------------------------
+// Step 3: span structure.  With tiktoken-safe chunking a cut falls before
+// every 400,000th character of a segment and, inside each 400,000-character
+// window, 25,000 characters after the start of every whitespace or
+// non-whitespace run (repeatedly).  In allow_special segments every special
+// string found inside one chunk becomes a special piece.  Outputs the masks
+// SS (a span starts here: segment start, cut or end of a special), SPST (a
+// special starts here) and SPC (byte inside a special).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool special_at(const EncodeArgs &a, uint64_t p, uint64_t seg_end,
+                                           uint32_t &len) {
+  const uint32_t b = a.text[p];
+  if (!((a.T.sp_first[b >> 5] >> (b & 31)) & 1)) return false;
+  for (uint32_t k = 0; k < a.T.n_sp; ++k) {
+    const uint32_t o = a.T.sp_off[k], L = a.T.sp_off[k + 1] - o;
+    if (p + L > seg_end) continue;
+    bool eq = true;
+    for (uint32_t j = 0; j < L && eq; ++j) eq = a.text[p + j] == a.T.sp_bytes[o + j];
+    if (eq) {
+      len = L;
+      return true;
+    }
+  }
+  return false;
+}
+
+__global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
+  if (a.ws.status->pad2) return;
+  const int lane = threadIdx.x;
+  const uint32_t t = blockIdx.x;
+  const int64_t w = int64_t(t) * TILE_WORDS + lane - 1;
+  const int64_t base = w * 64;
+  const bool owned = lane >= 1 && lane <= int(TILE_WORDS) && w < int64_t(a.n_words);
+  const bool live = lane >= 1 && w < int64_t(a.n_words);  // owned or the right halo
+
+  Window win;
+  load_window(a.text, a.n, base, win);
+  uint64_t seg_lo, seg_hi;
+  uint32_t seg_at;
+  segment_marks(a.seg_off, a.n_seg, base, seg_lo, seg_hi, seg_at);
+  WordMasks m;
+  classify_word(a.T, win, base, a.n, seg_lo, seg_hi, m);
+  const uint64_t segb = ((seg_lo >> 8) | (seg_hi << 56)) & m.valid;
+  const uint64_t ws_prev = shfl_up64(m.WS, 1);
+  const uint64_t chg = m.lead & (segb | (m.WS ^ shl(m.WS, ws_prev, 1)));
+
+  // character index of this word's first character and the last run change
+  // before it (lanes 1..63 are contiguous with the tile's character base)
+  const uint32_t nch = (lane >= 1) ? uint32_t(__popcll(m.lead)) : 0u;
+  const uint32_t incl = wave_incl_sum(nch, lane);
+  const uint64_t tile_base = a.ws.tile_charbase[t];
+  const uint64_t c0 = tile_base + (incl - nch);
+  int64_t lastchg = -1;
+  if (lane >= 1 && chg) {
+    const int hb = 63 - __clzll(chg);
+    lastchg = int64_t(c0 + uint32_t(__popcll(m.lead & (bit(hb) - 1))));
+  }
+  const int64_t incl_chg = wave_incl_max(lastchg, lane);
+  int64_t chg_before = __shfl_up(static_cast<long long>(incl_chg), 1, 64);
+  if (lane <= 1) chg_before = -1;
+  chg_before = max(chg_before, (int64_t)a.ws.tile_chgcarry[t]);
+
+  uint64_t cut = 0;
+  if (live && (a.flags & BBPE_TIKTOKEN_SAFE) && m.valid) {
+    // state at the first character of the word
+    uint32_t s = seg_at;
+    uint64_t segcs = a.ws.seg_charstart[s];
+    uint64_t c = c0;
+    uint64_t nw, rs, nr;
+    {
+      const uint64_t off = c > segcs ? c - segcs : 0;
+      uint64_t k = (off + 399999) / 400000;
+      if (k == 0) k = 1;
+      nw = segcs + 400000ull * k;                   // next window boundary >= c
+      const uint64_t ws0 = c > segcs ? segcs + 400000ull * ((c - 1 - segcs) / 400000) : segcs;
+      rs = max(uint64_t(chg_before < 0 ? 0 : chg_before), ws0);
+      if (rs < segcs) rs = segcs;
+      uint64_t kk = c > rs ? (c - rs + 24999) / 25000 : 1;
+      if (kk == 0) kk = 1;
+      nr = rs + 25000ull * kk;                      // next run cut >= c
+    }
+    uint64_t leads = m.lead;
+    while (leads) {
+      const int i = __ffsll(static_cast<unsigned long long>(leads)) - 1;
+      leads &= leads - 1;
+      if ((segb >> i) & 1) {
+        while (s + 1 < a.n_seg && a.seg_off[s + 1] <= uint64_t(base + i)) ++s;
+        segcs = c;
+        nw = c + 400000ull;
+        rs = c;
+        nr = c + 25000ull;
+      } else if (c == nw) {
+        cut |= bit(i);
+        rs = c;
+        nw += 400000ull;
+        nr = c + 25000ull;
+      } else if ((chg >> i) & 1) {
+        rs = c;
+        nr = c + 25000ull;
+      } else if (c == nr) {
+        cut |= bit(i);
+        nr += 25000ull;
+      }
+      ++c;
+    }
+  }
+  const uint64_t brk = segb | cut;                   // span starts known so far
+  const uint64_t brk_next = shfl_down64(brk, 1);
+
+  uint64_t sp_st = 0, sp_in = 0, sp_in_next = 0, ss_end = 0, ss_end_next = 0;
+  if (live && a.T.n_sp > 0 && m.valid) {
+    uint32_t s = seg_at;
+    uint64_t cand = m.lead;
+    while (cand) {
+      const int i = __ffsll(static_cast<unsigned long long>(cand)) - 1;
+      cand &= cand - 1;
+      const uint64_t p = uint64_t(base) + uint64_t(i);
+      while (s + 1 < a.n_seg && a.seg_off[s + 1] <= p) ++s;
+      if (!a.allow[s]) continue;
+      uint32_t L;
+      if (!special_at(a, p, min(a.seg_off[s + 1], a.n), L)) continue;
+      // no chunk cut strictly inside the special
+      const int e = i + int(L);  // end, exclusive, in [i+1, i+64]
+      uint64_t inner_lo = 0, inner_hi = 0;  // bits i+1 .. e-1 over this and the next word
+      for (int j = i + 1; j < e; ++j) {
+        if (j < 64) inner_lo |= bit(j);
+        else inner_hi |= bit(j - 64);
+      }
+      if ((inner_lo & brk) || (inner_hi & brk_next)) continue;
+      sp_st |= bit(i);
+      for (int j = i; j < e; ++j) {
+        if (j < 64) sp_in |= bit(j);
+        else sp_in_next |= bit(j - 64);
+      }
+      if (e < 64) ss_end |= bit(e);
+      else ss_end_next |= bit(e - 64);
+      cand &= (e >= 64) ? 0 : ~(bit(e) - 1);  // continue after the special
+    }
+  }
+  if (owned) {
+    const uint64_t ss = brk | ss_end;
+    if (ss) atomicOr(reinterpret_cast<unsigned long long *>(&a.ws.ss[w]), ss);
+    if (sp_st) atomicOr(reinterpret_cast<unsigned long long *>(&a.ws.spst[w]), sp_st);
+    if (sp_in) atomicOr(reinterpret_cast<unsigned long long *>(&a.ws.spc[w]), sp_in);
+    if (w + 1 < int64_t(a.n_words)) {
+      if (sp_in_next) atomicOr(reinterpret_cast<unsigned long long *>(&a.ws.spc[w + 1]), sp_in_next);
+      if (ss_end_next) atomicOr(reinterpret_cast<unsigned long long *>(&a.ws.ss[w + 1]), ss_end_next);
+    }
+  }
+}
+
+}  // namespace bbpe

@@ -1,0 +1,101 @@
+// Internal layout shared by the host planner and the gfx950 kernels.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIP__)
+#define BBPE_HD __host__ __device__ __forceinline__
+#else
+#define BBPE_HD inline
+#endif
+
+namespace bbpe {
+
+// ---------------------------------------------------------------------------
+// Character classes (one code per code point, see gen_unicode_classes.py)
+// ---------------------------------------------------------------------------
+enum CharClass : uint8_t {
+  CC_OTHER = 0, CC_LU = 1, CC_LL = 2, CC_LO = 3, CC_N = 4, CC_WS = 5, CC_M = 6
+};
+
+// ---------------------------------------------------------------------------
+// Rank hash table: open addressing, linear probing, 16-byte slots.
+//   k8   : the first 8 key bytes, little endian, zero padded
+//   meta : bits 0-7 key length, bit 8 "self-consistent" (merging the key's
+//          own bytes yields exactly this key), bits 9-31 offset of the key in
+//          the key blob
+//   rank : the id, or -1 for an empty slot
+// ---------------------------------------------------------------------------
+struct Slot {
+  uint64_t k8;
+  uint32_t meta;
+  int32_t rank;
+};
+static_assert(sizeof(Slot) == 16, "slot is 16 bytes");
+
+constexpr uint32_t META_SELF = 1u << 8;
+constexpr uint32_t META_OFF_SHIFT = 9;
+constexpr uint32_t MAX_BLOB = 1u << 23;
+constexpr int32_t RANK_NONE = 0x7fffffff;  // "pair not in the table"
+
+// MurmurHash3's 64-bit finaliser (Appleby), applied per 8-byte word.
+BBPE_HD uint64_t fmix64(uint64_t x) {
+  x ^= x >> 33;
+  x *= 0xff51afd7ed558ccdull;
+  x ^= x >> 33;
+  x *= 0xc4ceb9fe1a85ec53ull;
+  x ^= x >> 33;
+  return x;
+}
+
+// Hash of a key given as little-endian zero-padded 8-byte words.
+BBPE_HD uint64_t hash_seed(uint32_t len) { return (uint64_t(len) + 1) * 0x9E3779B97F4A7C15ull; }
+BBPE_HD uint64_t hash_step(uint64_t h, uint64_t w) { return fmix64(h ^ w); }
+
+// ---------------------------------------------------------------------------
+// Device view of the uploaded tables (passed to kernels by value).
+// ---------------------------------------------------------------------------
+struct DevTables {
+  const Slot *slots;
+  const uint8_t *blob;
+  const int32_t *pair;      // [65536] rank of the 2-byte key (a,b) at a*256+b, or RANK_NONE
+  const int32_t *atom;      // [256] rank of each single byte
+  const uint16_t *uni1;     // [4352]
+  const uint8_t *uni2;      // [blocks*256]
+  const uint8_t *sp_bytes;  // special strings
+  const uint32_t *sp_off;   // [n_sp+1]
+  const int32_t *sp_id;     // [n_sp]
+  uint32_t slot_mask;
+  uint32_t n_sp;
+  uint32_t sp_first[8];     // bitmap of first bytes of specials
+  int32_t grammar;
+  uint32_t max_key_len;
+};
+
+// Byte offsets of each table inside the uploaded image.
+struct ImageLayout {
+  uint64_t slots, blob, pair, atom, uni1, uni2, sp_bytes, sp_off, sp_id, total;
+  uint32_t n_slots;
+};
+
+// ---------------------------------------------------------------------------
+// Text tiling.  A "word" is 64 consecutive text bytes (one lane); a tile is
+// one wave of 64 lanes that owns TILE_WORDS words and sees one extra word on
+// each side (lanes 0 and 63) for neighbour context.
+// ---------------------------------------------------------------------------
+constexpr uint32_t TILE_WORDS = 62;
+constexpr uint32_t TILE_BYTES = TILE_WORDS * 64;
+
+// Status block at the start of the workspace.
+struct Status {
+  unsigned long long err_pos;     // first invalid UTF-8 byte (absolute), or ~0
+  unsigned long long n_pieces;
+  unsigned long long n_ids;
+  unsigned int n_long;            // pieces handed to the long-piece tier
+  unsigned int pad;
+  unsigned long long n_chars;
+  unsigned int err_seg;           // segment of err_pos
+  unsigned int pad2;
+};
+
+}  // namespace bbpe

@@ -1,0 +1,69 @@
+// Kernel arguments and entry points of the encode path (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bbpe.h"
+#include "bbpe_internal.h"
+
+namespace bbpe {
+
+// Device workspace, carved out of the caller's buffer by the host planner.
+struct WsPtrs {
+  Status *status;
+  uint32_t *tile_nchar;             // [T] characters per tile
+  int32_t *tile_lastchg;            // [T] tile-local index of the last run change, or -1
+  unsigned long long *tile_charbase;  // [T] index of the tile's first character
+  long long *tile_chgcarry;         // [T] last run change before the tile, or -1
+  uint32_t *seg_local;              // [S+1] tile-local character index of each segment start
+  unsigned long long *seg_charstart;  // [S+1]
+  uint64_t *ss, *spst, *spc;        // [W] span start / special start / inside special
+  uint64_t *ps;                     // [W] piece starts
+  uint32_t *tile_fn;                // [T] split transfer functions
+  uint32_t *tile_carry;             // [T] split state entering each tile
+  uint32_t *tile_np;                // [T+1] pieces per tile, then their exclusive scan
+  uint32_t *piece_start;            // [P+1]
+  uint32_t *piece_cnt;              // [P+1] ids per piece, then their exclusive scan
+  int32_t *tmp_ids;                 // [N] ids of each piece, at the piece's byte offset
+  uint32_t *scan_part;              // [N/4096+2] partial sums of the piece scan
+  uint32_t *long_list;              // [N/64+1] pieces for the long-piece tier
+  int32_t *lrank;                   // [N] long tier: pair rank at each part start
+  int32_t *lpart;                   // [N] long tier: rank of the part starting here
+  uint8_t *lalive;                  // [N] long tier: 1 where a part starts
+  unsigned long long *lmin;         // [W] long tier: per-word minimum (rank<<32 | position)
+};
+
+struct EncodeArgs {
+  DevTables T;
+  const uint8_t *text;
+  uint64_t n;
+  const uint64_t *seg_off;
+  const uint8_t *allow;
+  uint32_t n_seg;
+  uint32_t flags;
+  uint64_t n_words;
+  uint32_t n_tiles;
+  int32_t *ids;
+  uint64_t ids_cap;
+  int64_t *id_off;
+  WsPtrs ws;
+};
+
+__global__ void k_count(EncodeArgs a);
+__global__ void k_scan_chars(EncodeArgs a);
+__global__ void k_spans(EncodeArgs a);
+__global__ void k_split_agg(EncodeArgs a);
+__global__ void k_scan_split(EncodeArgs a);
+__global__ void k_split(EncodeArgs a);
+__global__ void k_scan_tiles_np(EncodeArgs a);
+__global__ void k_pieces(EncodeArgs a);
+__global__ void k_merge(EncodeArgs a);
+__global__ void k_merge_long(EncodeArgs a);
+__global__ void k_scan_reduce(EncodeArgs a);
+__global__ void k_scan_partials(EncodeArgs a);
+__global__ void k_scan_down(EncodeArgs a);
+__global__ void k_assemble(EncodeArgs a);
+__global__ void k_seg_offsets(EncodeArgs a);
+
+}  // namespace bbpe

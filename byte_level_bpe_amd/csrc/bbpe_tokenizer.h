@@ -1,0 +1,45 @@
+// Host-side tokenizer handle (opaque to callers of bbpe.h).
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "bbpe_internal.h"
+
+struct bbpe_tokenizer {
+  int grammar = 0;
+  uint32_t n_ranks = 0;
+  int32_t max_id = -1;
+  // decode map: id -> (offset into dec_blob, length); dense when ids are dense
+  std::vector<uint8_t> dec_blob;
+  std::vector<uint64_t> dec_dense;  // (off << 8) | len, or ~0 when absent
+  std::unordered_map<int32_t, uint64_t> dec_sparse;
+  bool dense = true;
+  // specials
+  std::vector<std::string> sp;
+  std::vector<int32_t> sp_id;
+  // device image, built on the host at load time and copied by upload
+  bbpe::ImageLayout layout{};
+  std::vector<uint8_t> image;
+  const uint8_t *d_image = nullptr;
+  bbpe::DevTables dev{};
+  uint32_t max_key_len = 0;
+  uint32_t n_self_consistent = 0;
+  // per-kernel timing (diagnostics)
+  bool timing = false;
+  std::vector<std::string> t_names;
+  std::vector<double> t_ms;
+  std::vector<uint64_t> t_launches;
+  std::vector<void *> t_events;  // hipEvent_t pool, two per launch
+  // last UTF-8 error
+  uint32_t err_seg = 0;
+  uint64_t err_byte = 0;
+};
+
+namespace bbpe {
+// Hash of a host key (same function the kernels apply to text slices).
+uint64_t hash_key(const uint8_t *p, uint32_t len);
+}  // namespace bbpe

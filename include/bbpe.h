@@ -1,0 +1,210 @@
+/* bbpe.h -- byte-level BPE encoder for AMD MI355X (gfx950), C ABI.
+ *
+ * The encode path of a tiktoken-style byte-level BPE tokenizer, run as HIP
+ * kernels on one GPU:
+ *
+ *   * a mergeable-ranks table maps byte strings to ids; the rank is the id and
+ *     all 256 single bytes are present, so encoding always terminates
+ *     (tiktoken deep-dive page, "An encoding is three objects" and "The byte
+ *     floor");
+ *   * text arrives as ordered (text, allow_special) segments handled in one
+ *     native call; with tiktoken-safe chunking each segment is cut into pieces
+ *     of at most 400,000 characters, whose whitespace / non-whitespace runs
+ *     are cut at 25,000 characters, and every chunk is encoded as its own
+ *     text (Baseten page, "Why Kimi K3 tokenization is non-trivial" and "One
+ *     native call for the whole serving path");
+ *   * specials are matched by an exact-string pass outside BPE, only in
+ *     segments whose allow_special flag is set; elsewhere a literal special
+ *     string is ordinary text (tiktoken deep-dive page, "Special tokens");
+ *   * each span is cut by a fixed split grammar whose cuts merges never
+ *     cross (tiktoken deep-dive page, "The split pattern"; the o200k-style
+ *     variant from "r50k, cl100k, o200k");
+ *   * each pre-token is merged by repeatedly joining the adjacent pair of
+ *     lowest rank, leftmost on ties (tiktoken deep-dive page, "Inside
+ *     encode").
+ *
+ * Conventions.  Every function returns an int status: 0 (BBPE_OK) or a
+ * negative BBPE_E_* code.  Functions never throw and never print.  "Host"
+ * pointers are ordinary CPU memory; "device" pointers are HIP device memory
+ * on the current device.  The caller owns every buffer it passes; the
+ * library owns only the opaque tokenizer handle and its host copy of the
+ * table.  Device buffers are normally PyTorch tensors: PyTorch provides the
+ * memory and the stream, the library provides the kernels.
+ */
+#ifndef BBPE_H
+#define BBPE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct bbpe_tokenizer bbpe_tokenizer; /* opaque; immutable once uploaded */
+
+enum {
+  BBPE_OK = 0,
+  BBPE_E_INVALID_ARG = -1, /* null pointer, bad size, misaligned text, bad flag */
+  BBPE_E_TABLE = -2,       /* ranks table violates the format (see load_ranks) */
+  BBPE_E_SPECIAL = -3,     /* special-token list violates the format */
+  BBPE_E_UTF8 = -4,        /* a segment is not valid UTF-8 (see error_detail) */
+  BBPE_E_CAPACITY = -5,    /* ids_capacity too small; *n_ids holds the need */
+  BBPE_E_BAD_ID = -6,      /* decode met an id that is neither rank nor special */
+  BBPE_E_HIP = -7,         /* a HIP runtime call failed */
+  BBPE_E_WORKSPACE = -8,   /* workspace missing or smaller than required */
+  BBPE_E_STATE = -9        /* tables not uploaded yet */
+};
+
+/* Split grammars.  CL100K is the pattern printed on the tiktoken deep-dive
+ * page ("The split pattern"), with possessive quantifiers.  O200K_STYLE
+ * replaces its first two clauses by one letter clause split by Unicode case
+ * categories with the contraction appended to the word ("r50k, cl100k,
+ * o200k"):  [^\r\n\p{L}\p{N}]?+ (U*+ W++ | U++ W*+) (?i:'[sdmt]|'ll|'ve|'re)?+
+ * with U = [\p{Lu}\p{Lt}\p{Lm}\p{Lo}\p{M}] and W = [\p{Ll}\p{Lm}\p{Lo}\p{M}],
+ * followed by the cl100k clauses from the digit clause on. */
+enum { BBPE_GRAMMAR_CL100K = 0, BBPE_GRAMMAR_O200K_STYLE = 1 };
+
+/* encode flags */
+enum {
+  BBPE_TIKTOKEN_SAFE = 1u << 0 /* 400k-character windows, 25k-character run cuts */
+};
+
+/* Limits of this implementation. */
+#define BBPE_MAX_KEY_BYTES 128u      /* longest mergeable key (tiktoken deep-dive, "The byte floor") */
+#define BBPE_MAX_SPECIALS 1024u
+#define BBPE_MAX_SPECIAL_BYTES 64u   /* longest special-token string */
+
+/* Build a tokenizer from a ranks table held in host memory.
+ *
+ *   key_bytes, key_off[n+1]: key i is key_bytes[key_off[i] .. key_off[i+1]);
+ *   ranks[n]:                its rank (= token id), 0 <= rank < 2^31;
+ *   special_bytes, special_off[ns+1], special_ids[ns]: special tokens;
+ *   grammar:                 BBPE_GRAMMAR_*.
+ *
+ * Rejected with BBPE_E_TABLE: n == 0, an empty key, a key longer than
+ * BBPE_MAX_KEY_BYTES, a duplicate key or rank, a negative rank, or a missing
+ * single-byte key (all 256 must be present).  Rejected with BBPE_E_SPECIAL:
+ * more than BBPE_MAX_SPECIALS specials, an empty special, one longer than
+ * BBPE_MAX_SPECIAL_BYTES, one that is not valid UTF-8, a duplicate string or
+ * id, an id that is also a rank, one special that is a prefix of another, or
+ * two specials that can overlap in some text (a proper suffix of one equal to
+ * a proper prefix of another, or one inside another).
+ * On success *out receives the handle and *device_table_bytes the size of the
+ * device memory that bbpe_upload_tables needs.  The library copies what it
+ * needs; the caller keeps ownership of every input. */
+int bbpe_load_ranks(const uint8_t *key_bytes, const uint64_t *key_off, const int32_t *ranks,
+                    uint32_t n, const uint8_t *special_bytes, const uint64_t *special_off,
+                    const int32_t *special_ids, uint32_t ns, int grammar,
+                    bbpe_tokenizer **out, uint64_t *device_table_bytes);
+
+/* Same, reading tiktoken's text format ("base64(bytes) SP rank LF" per line)
+ * from a host file.  BBPE_E_TABLE also covers unreadable files and malformed
+ * lines. */
+int bbpe_load_ranks_tiktoken_file(const char *path, const uint8_t *special_bytes,
+                                  const uint64_t *special_off, const int32_t *special_ids,
+                                  uint32_t ns, int grammar, bbpe_tokenizer **out,
+                                  uint64_t *device_table_bytes);
+
+/* Copy the device image of the tables (hash table, pair table, Unicode class
+ * tables, specials) into caller-owned device memory d_table_mem of at least
+ * device_table_bytes bytes, 256-byte aligned, on hip_stream (a hipStream_t,
+ * may be null for the null stream).  The memory must stay valid and unchanged
+ * for as long as the handle encodes.  Returns after the copy has completed. */
+int bbpe_upload_tables(bbpe_tokenizer *tok, void *d_table_mem, uint64_t bytes,
+                       void *hip_stream);
+
+/* Device workspace needed to encode total_text_bytes bytes in n_seg segments. */
+int bbpe_workspace_bytes(const bbpe_tokenizer *tok, uint64_t total_text_bytes, uint32_t n_seg,
+                         uint64_t *out_bytes);
+
+/* Encode n_seg segments in one call.
+ *
+ *   d_text:           device, the concatenated UTF-8 bytes of all segments,
+ *                     16-byte aligned; NUL is an ordinary byte;
+ *   total_bytes:      host copy of d_seg_off[n_seg] (the text length, below
+ *                     2^32 - 64), so that the call needs no early read-back;
+ *   d_seg_off[n_seg+1]: device, uint64 byte offsets; segment s is
+ *                     d_text[d_seg_off[s] .. d_seg_off[s+1]); d_seg_off[0]
+ *                     must be 0, offsets non-decreasing, and
+ *                     d_seg_off[n_seg] == total_bytes (checked on the device:
+ *                     BBPE_E_INVALID_ARG otherwise);
+ *   d_allow_special[n_seg]: device, 1 = match specials in this segment,
+ *                     0 = specials are ordinary text;
+ *   flags:            BBPE_TIKTOKEN_SAFE or 0;
+ *   d_workspace:      device scratch of at least bbpe_workspace_bytes(),
+ *                     256-byte aligned; its contents are not preserved;
+ *   d_ids:            device output, int32, capacity ids_capacity;
+ *   d_id_off[n_seg+1]: device output, int64: the ids of segment s are
+ *                     d_ids[d_id_off[s] .. d_id_off[s+1]);
+ *   *n_ids:           host output, the number of ids written;
+ *   hip_stream:       the stream all work is enqueued on.
+ *
+ * The total number of ids never exceeds the number of text bytes, so a
+ * capacity equal to the byte count always suffices.  With a smaller capacity
+ * the call returns BBPE_E_CAPACITY, sets *n_ids to the count needed and
+ * leaves d_ids unspecified.  Invalid UTF-8 in any segment returns
+ * BBPE_E_UTF8; bbpe_error_detail then reports the first offending segment and
+ * byte.  The call synchronises the stream once, at its end, to read the
+ * status and *n_ids; that is its only host synchronisation. */
+int bbpe_encode_segments(bbpe_tokenizer *tok, const uint8_t *d_text, uint64_t total_bytes,
+                         const uint64_t *d_seg_off, const uint8_t *d_allow_special,
+                         uint32_t n_seg, uint32_t flags,
+                         void *d_workspace, uint64_t workspace_bytes, int32_t *d_ids,
+                         uint64_t ids_capacity, int64_t *d_id_off, uint64_t *n_ids,
+                         void *hip_stream);
+
+/* Pre-tokenization only: the same segment handling, chunking, special pass
+ * and split as bbpe_encode_segments, without merging.  Writes the byte offset
+ * (into d_text) of every piece in text order to d_starts (device, uint32,
+ * capacity starts_cap) and, when d_is_special is not null, 1 for pieces that
+ * are special tokens and 0 otherwise (device, uint8).  *n_pieces (host)
+ * receives the count; BBPE_E_CAPACITY if it exceeds starts_cap.  Pieces
+ * never cross a chunk cut, a special or a segment boundary (tiktoken
+ * deep-dive page, "The split pattern": merges never cross a cut).  Same
+ * arguments, errors and synchronisation as bbpe_encode_segments. */
+int bbpe_pretokenize_segments(bbpe_tokenizer *tok, const uint8_t *d_text, uint64_t total_bytes,
+                              const uint64_t *d_seg_off, const uint8_t *d_allow_special,
+                              uint32_t n_seg, uint32_t flags, void *d_workspace,
+                              uint64_t workspace_bytes, uint32_t *d_starts, uint64_t starts_cap,
+                              uint8_t *d_is_special, uint64_t *n_pieces, void *hip_stream);
+
+/* Decode host ids to bytes (host memory): the concatenation of each token's
+ * bytes; specials decode to their strings.  The result is bytes, not text: a
+ * token may end inside a UTF-8 character (tiktoken deep-dive page, "Pitfalls
+ * that bite in production").  Returns BBPE_E_BAD_ID for an id that is neither
+ * a rank nor a special (*out_len = its index), BBPE_E_CAPACITY if cap is too
+ * small (*out_len = bytes needed). */
+int bbpe_decode(const bbpe_tokenizer *tok, const int32_t *ids, uint64_t n, uint8_t *out,
+                uint64_t cap, uint64_t *out_len);
+
+/* Details of the last BBPE_E_UTF8 from bbpe_encode_segments on this handle:
+ * the segment index and the absolute byte offset in d_text of the first
+ * invalid sequence. */
+int bbpe_error_detail(const bbpe_tokenizer *tok, uint32_t *segment, uint64_t *byte_offset);
+
+/* Number of ranks and the largest id (rank or special) of the table. */
+int bbpe_table_info(const bbpe_tokenizer *tok, uint32_t *n_ranks, int32_t *max_id,
+                    uint32_t *n_specials, int *grammar);
+
+/* Diagnostics: per-kernel device time.  With timing enabled, every later
+ * encode or pretokenize call on this handle brackets each kernel launch with
+ * a pair of HIP events on the call's stream and, after the call's final
+ * synchronisation, adds the elapsed time to that kernel's running total.
+ * bbpe_timing_report returns, for kernel index idx (0, 1, ... until it
+ * returns BBPE_E_INVALID_ARG), its name (a static string), the total
+ * milliseconds and the number of launches since the last reset. */
+int bbpe_set_timing(bbpe_tokenizer *tok, int enable);
+int bbpe_timing_report(const bbpe_tokenizer *tok, uint32_t idx, const char **name,
+                       double *total_ms, uint64_t *launches);
+int bbpe_timing_reset(bbpe_tokenizer *tok);
+
+void bbpe_free(bbpe_tokenizer *tok);
+
+/* A static English description of a status code. */
+const char *bbpe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BBPE_H */

@@ -267,6 +267,10 @@ struct Oracle {
   // instrumentation of the merge loop (lookups it performs, excluding the
   // final per-piece read-out, which equals the merge that made the piece)
   uint64_t n_lookups = 0, lookup_key_bytes = 0, n_pieces = 0;
+  // when set, pieces are recorded (absolute byte offset, special flag)
+  // instead of merged
+  std::vector<std::pair<uint64_t, uint8_t>> *piece_sink = nullptr;
+  uint64_t sink_base = 0;  // absolute offset of the current segment
 
   int32_t rank_of(const uint8_t *p, size_t n) const {
     auto it = ranks.find(std::string(reinterpret_cast<const char *>(p), n));
@@ -321,7 +325,8 @@ struct Oracle {
       size_t m = match_at(s, p, grammar);
       if (m == 0) return -1;  // unreachable: every character is covered
       size_t b0 = ch.off[c0 + p], b1 = ch.off[c0 + p + m];
-      merge(text + b0, b1 - b0, out);
+      if (piece_sink) piece_sink->emplace_back(sink_base + b0, 0);
+      else merge(text + b0, b1 - b0, out);
       p += m;
     }
     return 0;
@@ -346,7 +351,8 @@ struct Oracle {
       }
       if (!hit) { ++c; continue; }
       if (encode_span(text, ch, span_c0, c, out)) return -1;
-      out.push_back(hit->second);
+      if (piece_sink) piece_sink->emplace_back(sink_base + b, 1);
+      else out.push_back(hit->second);
       size_t b_after = b + hit->first.size();
       while (c < c1 && ch.off[c] < b_after) ++c;  // specials end on a character boundary
       span_c0 = c;
@@ -446,14 +452,16 @@ void oracle_reset_counters(void *h) {
 
 // Encode segments.  Returns 0, -4 (invalid UTF-8: *err_seg, *err_byte set),
 // -5 (capacity: *n_ids set to the required count) or -1 (internal).
-int oracle_encode(void *h, const uint8_t *text, const uint64_t *seg_off, const uint8_t *allow,
-                  uint32_t nseg, int safe, int32_t *ids, uint64_t cap, int64_t *id_off,
-                  uint64_t *n_ids, uint64_t *err_seg, uint64_t *err_byte) {
-  Oracle *o = static_cast<Oracle *>(h);
-  std::vector<int32_t> out;
+}  // extern "C"
+
+namespace {
+int run_segments(Oracle *o, const uint8_t *text, const uint64_t *seg_off, const uint8_t *allow,
+                 uint32_t nseg, int safe, std::vector<int32_t> &out, int64_t *id_off,
+                 uint64_t *err_seg, uint64_t *err_byte) {
   Chars ch;
   for (uint32_t s = 0; s < nseg; ++s) {
-    id_off[s] = int64_t(out.size());
+    if (id_off) id_off[s] = int64_t(out.size());
+    o->sink_base = seg_off[s];
     const uint8_t *t = text + seg_off[s];
     size_t n = seg_off[s + 1] - seg_off[s];
     size_t bad = decode_utf8(t, n, ch);
@@ -469,10 +477,45 @@ int oracle_encode(void *h, const uint8_t *text, const uint64_t *seg_off, const u
       if (o->encode_chunk(t, ch, cuts[k], cuts[k + 1], allow[s] != 0, out)) return -1;
     }
   }
-  id_off[nseg] = int64_t(out.size());
+  if (id_off) id_off[nseg] = int64_t(out.size());
+  return 0;
+}
+}  // namespace
+
+extern "C" {
+
+int oracle_encode(void *h, const uint8_t *text, const uint64_t *seg_off, const uint8_t *allow,
+                  uint32_t nseg, int safe, int32_t *ids, uint64_t cap, int64_t *id_off,
+                  uint64_t *n_ids, uint64_t *err_seg, uint64_t *err_byte) {
+  Oracle *o = static_cast<Oracle *>(h);
+  std::vector<int32_t> out;
+  o->piece_sink = nullptr;
+  int st = run_segments(o, text, seg_off, allow, nseg, safe, out, id_off, err_seg, err_byte);
+  if (st) return st;
   *n_ids = out.size();
   if (out.size() > cap) return -5;
   std::copy(out.begin(), out.end(), ids);
+  return 0;
+}
+
+// Pieces of whole segments (chunking, specials, split) without merging:
+// absolute byte offsets of piece starts and a special flag per piece.
+int oracle_pieces(void *h, const uint8_t *text, const uint64_t *seg_off, const uint8_t *allow,
+                  uint32_t nseg, int safe, uint64_t *starts, uint8_t *is_special, uint64_t cap,
+                  uint64_t *n_out, uint64_t *err_seg, uint64_t *err_byte) {
+  Oracle *o = static_cast<Oracle *>(h);
+  std::vector<std::pair<uint64_t, uint8_t>> sink;
+  std::vector<int32_t> unused;
+  o->piece_sink = &sink;
+  int st = run_segments(o, text, seg_off, allow, nseg, safe, unused, nullptr, err_seg, err_byte);
+  o->piece_sink = nullptr;
+  if (st) return st;
+  *n_out = sink.size();
+  if (sink.size() > cap) return -5;
+  for (size_t i = 0; i < sink.size(); ++i) {
+    starts[i] = sink[i].first;
+    is_special[i] = sink[i].second;
+  }
   return 0;
 }
 

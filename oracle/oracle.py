@@ -40,6 +40,8 @@ def _load():
         lib.oracle_reset_counters.argtypes = [P]
         lib.oracle_encode.restype = C.c_int
         lib.oracle_encode.argtypes = [P, P, P, P, C.c_uint32, C.c_int, P, C.c_uint64, P, P, P, P]
+        lib.oracle_pieces.restype = C.c_int
+        lib.oracle_pieces.argtypes = [P, P, P, P, C.c_uint32, C.c_int, P, P, C.c_uint64, P, P, P]
         lib.oracle_split.restype = C.c_int
         lib.oracle_split.argtypes = [P, P, C.c_uint64, P, C.c_uint64, P]
         lib.oracle_chunks.restype = C.c_int
@@ -118,6 +120,28 @@ class Oracle:
         if st != 0:
             raise OracleError(st, "segment %d byte %d" % (es.value, eb.value))
         return ids[:n.value].copy(), id_off
+
+    def pieces(self, segments, tiktoken_safe: bool = True):
+        """Piece start offsets (absolute, into the concatenated text) and a
+        special flag per piece, without merging."""
+        lib = _load()
+        text = b"".join(s for s, _ in segments)
+        tarr = np.frombuffer(text or b"\0", dtype=np.uint8)
+        off = np.zeros(len(segments) + 1, dtype=np.uint64)
+        off[1:] = np.cumsum([len(s) for s, _ in segments])
+        allow = np.array([1 if a else 0 for _, a in segments] or [0], dtype=np.uint8)
+        cap = max(1, len(text))
+        starts = np.empty(cap, dtype=np.uint64)
+        spec = np.empty(cap, dtype=np.uint8)
+        n = C.c_uint64(0)
+        es = C.c_uint64(0)
+        eb = C.c_uint64(0)
+        st = lib.oracle_pieces(self._h, _ptr(tarr), _ptr(off), _ptr(allow), len(segments),
+                               1 if tiktoken_safe else 0, _ptr(starts), _ptr(spec), cap,
+                               C.byref(n), C.byref(es), C.byref(eb))
+        if st != 0:
+            raise OracleError(st, "segment %d byte %d" % (es.value, eb.value))
+        return starts[:n.value].copy(), spec[:n.value].copy()
 
     def encode(self, text: bytes, allow_special: bool = False, tiktoken_safe: bool = True):
         return self.encode_segments([(text, allow_special)], tiktoken_safe)[0]

@@ -415,12 +415,12 @@ def ragged_requests(seed: int, n_req: int = 4096, lo: int = 512, hi: int = 8192,
     out = []
     pos = 0
     for L in lens:
-        # align the request start to a character boundary, then cut <= L bytes
-        while pos < len(pool) and (pool[pos] & 0xC0) == 0x80:
-            pos += 1
-        b = _truncate_utf8(pool[pos:pos + int(L)], int(L))
-        out.append(b)
-        pos += len(b)
+        # cut at most L bytes, ending on a character boundary
+        end = min(len(pool), pos + int(L))
+        while end > pos and end < len(pool) and (pool[end] & 0xC0) == 0x80:
+            end -= 1
+        out.append(pool[pos:end])
+        pos = end
     return out
 
 
@@ -478,6 +478,10 @@ def agentic_segments(seed: int, specials: list[str], total_chars: int = 4_000_00
     ilens[rest[0]] += budget - int(ilens.sum())
     space_seg = int(order[min_long])          # a mid-size segment gets the space run
     lit_seg = int(order[min_long + 1])        # and another the literal specials
+    # one continuous stream of the main mix, cut into the text segments, with
+    # request ids and hashes interleaved
+    pool = mix.blocks(int(budget * 1.25) + 65536).decode("utf-8")
+    pos = 0
     texts: list[str] = []
     for i in range(n_text):
         L = int(ilens[i])
@@ -485,12 +489,16 @@ def agentic_segments(seed: int, specials: list[str], total_chars: int = 4_000_00
         have = 0
         while have < L:
             k = float(rng.uniform(1)[0])
-            if k < 0.05:
+            if k < 0.02:
                 c = " request " + _uuid(rng) + " "
-            elif k < 0.08:
+            elif k < 0.03:
                 c = " sha " + _hexhash(rng, 40 if float(rng.uniform(1)[0]) < 0.5 else 64) + "\n"
             else:
-                c = mix.blocks(min(4096, max(64, 2 * (L - have)))).decode("utf-8")
+                n = min(L - have, int(rng.integers(200, 4000, 1)[0]))
+                if pos + n > len(pool):
+                    pos = 0
+                c = pool[pos:pos + n]
+                pos += n
             chunks.append(c)
             have += len(c)
         t = "".join(chunks)
@@ -500,7 +508,7 @@ def agentic_segments(seed: int, specials: list[str], total_chars: int = 4_000_00
         if i == lit_seg:
             ins = "".join(" please explain the literal token %s now" % sp for sp in specials)
             t = t[:L // 2] + ins + t[L // 2:]
-        texts.append(t[:L] if i not in (space_seg, lit_seg) else t[:L])
+        texts.append(t[:L])
     # the insertions above may have pushed the space run or the literals past
     # the cut; place them inside the kept prefix by construction
     segs: list[tuple[bytes, bool]] = []

@@ -1,0 +1,257 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element
+by element.  Integer work, so the bar is bit-exact: every piece boundary,
+every id and every segment offset."""
+import random
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import byte_level_bpe_amd as B  # noqa: E402
+from oracle import Oracle  # noqa: E402
+from oracle.oracle import OracleError  # noqa: E402
+from tests.brute import atoms_permuted  # noqa: E402
+
+SPECIALS = [(b"<|endoftext|>", 100257), (b"<|fim_prefix|>", 100258),
+            (b"<|fim_middle|>", 100259), (b"<|fim_suffix|>", 100260),
+            (b"<|endofprompt|>", 100276)]
+
+ALPHABET = (list("abstlvedrmSTLVEDRM'") + ["ſ", " ", " ", "\t", "\n", "\r", "\x0b", "\x0c",
+            "\x85", "\xa0", " ", "　", "1", "9", "०", "²", "Ⅳ", "!", ".", "-", '"',
+            "’", "\x00", "😀", "中", "क", "ि", "्", "A", "Z", "ǅ", "ʰ", "É", "é"])
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def first_mismatch(a, b):
+    n = min(len(a), len(b))
+    d = np.nonzero(np.asarray(a[:n]) != np.asarray(b[:n]))[0]
+    return int(d[0]) if len(d) else n
+
+
+def assert_pieces(tok, orc, segs, safe=True, what=""):
+    gs, gsp = tok.pretokenize_segments(segs, safe)
+    gs = gs.cpu().numpy().astype(np.int64)
+    gsp = gsp.cpu().numpy()
+    os_, osp = orc.pieces(segs, safe)
+    os_ = os_.astype(np.int64)
+    if not (np.array_equal(gs, os_) and np.array_equal(gsp, osp)):
+        k = first_mismatch(gs, os_)
+        text = b"".join(s for s, _ in segs)
+        at = int(os_[k]) if k < len(os_) else (int(gs[k]) if k < len(gs) else len(text))
+        ctx = text[max(0, at - 24):at + 24]
+        raise AssertionError("%s: pieces differ at piece %d (gpu %s, oracle %s), n gpu %d oracle %d,"
+                             " context %r" % (what, k, gs[k:k + 4].tolist(), os_[k:k + 4].tolist(),
+                                             len(gs), len(os_), ctx))
+
+
+def assert_ids(tok, orc, segs, safe=True, what=""):
+    ids, id_off = tok.encode_segments(segs, safe)
+    ids = ids.cpu().numpy()
+    id_off = id_off.cpu().numpy()
+    oids, ooff = orc.encode_segments(segs, safe)
+    if not np.array_equal(ids, oids):
+        k = first_mismatch(ids, oids)
+        raise AssertionError("%s: ids differ at %d: gpu %s oracle %s (n %d vs %d)"
+                             % (what, k, ids[k:k + 6].tolist(), oids[k:k + 6].tolist(),
+                                len(ids), len(oids)))
+    assert np.array_equal(id_off, ooff), what
+
+
+def make(tokens, specials=(), grammar=0):
+    return B.load_ranks(tokens, specials, grammar), Oracle(tokens, specials, grammar)
+
+
+@pytest.fixture(scope="module")
+def atoms():
+    return make(atoms_permuted(1), SPECIALS, 0)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    from synth import configs
+    w = configs.tiny()
+    return w, make(w.tokens, w.specials, w.grammar)
+
+
+def _fuzz(seed, n, maxlen, alphabet=ALPHABET):
+    r = random.Random(seed)
+    return ["".join(r.choice(alphabet) for _ in range(r.randint(1, maxlen))).encode()
+            for _ in range(n)]
+
+
+# ----------------------------------------------------------------- split ----
+
+def test_split_fuzz_short_segments(atoms):
+    tok, orc = atoms
+    segs = [(s, False) for s in _fuzz(1, 4000, 16)]
+    say("split fuzz: 4000 short segments")
+    assert_pieces(tok, orc, segs, what="short segments")
+
+
+def test_split_fuzz_one_long_segment(atoms):
+    tok, orc = atoms
+    text = b"".join(_fuzz(2, 20000, 16))
+    say("split fuzz: one segment of %d bytes" % len(text))
+    assert_pieces(tok, orc, [(text, False)], what="one long segment")
+
+
+def test_split_long_runs_cross_tiles(atoms):
+    tok, orc = atoms
+    r = random.Random(3)
+    parts = []
+    for _ in range(400):
+        k = r.random()
+        if k < 0.2:
+            parts.append("7" * r.randint(1, 9000))
+        elif k < 0.4:
+            parts.append("".join(r.choice([" ", " ", "\t", "\n", "\r", " "]) for _ in range(r.randint(1, 9000))))
+        elif k < 0.55:
+            parts.append("!" * r.randint(1, 5000) + r.choice(["", "\n\n", "a", " b"]))
+        elif k < 0.7:
+            parts.append("x" * r.randint(1, 9000))
+        elif k < 0.8:
+            parts.append("٣" * r.randint(1, 3000))  # 2-byte digits
+        else:
+            parts.append("".join(r.choice(ALPHABET) for _ in range(r.randint(1, 50))))
+    text = "".join(parts).encode()
+    say("split long runs: %d bytes" % len(text))
+    assert_pieces(tok, orc, [(text, False)], safe=False, what="long runs, no chunking")
+    assert_pieces(tok, orc, [(text, False)], safe=True, what="long runs, chunking")
+
+
+def test_split_segment_boundaries(atoms):
+    tok, orc = atoms
+    r = random.Random(4)
+    segs = []
+    for _ in range(3000):
+        n = r.choice([0, 0, 1, 2, 3, 5, 8, 63, 64, 65, 127, 200])
+        segs.append(("".join(r.choice(ALPHABET) for _ in range(n)).encode(), r.random() < 0.5))
+    say("segment boundaries: %d segments" % len(segs))
+    assert_pieces(tok, orc, segs, what="segment boundaries")
+    assert_ids(tok, orc, segs, what="segment boundaries")
+
+
+# -------------------------------------------------------------- specials ----
+
+def test_specials_fuzz(atoms):
+    tok, orc = atoms
+    r = random.Random(5)
+    sp = [s for s, _ in SPECIALS]
+    segs = []
+    for _ in range(1500):
+        parts = []
+        for _ in range(r.randint(0, 8)):
+            if r.random() < 0.3:
+                parts.append(r.choice(sp))
+            elif r.random() < 0.1:
+                parts.append(r.choice(sp)[:r.randint(1, 8)])  # partial literal
+            else:
+                parts.append("".join(r.choice(ALPHABET) for _ in range(r.randint(0, 10))).encode())
+        segs.append((b"".join(parts), r.random() < 0.6))
+    say("specials fuzz")
+    assert_pieces(tok, orc, segs, what="specials")
+    assert_ids(tok, orc, segs, what="specials")
+
+
+# -------------------------------------------------------------- chunking ----
+
+def test_chunking_space_run_and_windows(atoms):
+    tok, orc = atoms
+    a = "word " * 300 + " " * 60000 + "tail " + ("é" * 30000 + " ") * 14 + "<|endoftext|>"
+    segs = [(a.encode(), True), (b"x" * 70000, False), ("中" * 410000).encode() + b"<|endoftext|>", ]
+    segs = [segs[0], segs[1], (segs[2], True)]
+    say("chunking: %d bytes" % sum(len(s) for s, _ in segs))
+    assert_pieces(tok, orc, segs, safe=True, what="chunking")
+    assert_pieces(tok, orc, segs, safe=False, what="no chunking")
+
+
+def test_special_straddling_window_cut(atoms):
+    tok, orc = atoms
+    text = ("ab " * 133333 + "<|endoftext|>tail").encode()
+    say("special straddling a 400k cut")
+    assert_pieces(tok, orc, [(text, True)], safe=True, what="straddle")
+    assert_ids(tok, orc, [(text, True)], safe=True, what="straddle ids")
+
+
+# ------------------------------------------------------------------- ids ----
+
+def test_tiny_workload(tiny):
+    w, (tok, orc) = tiny
+    say("tiny workload")
+    assert_pieces(tok, orc, w.segments, what="tiny")
+    assert_ids(tok, orc, w.segments, what="tiny")
+
+
+def test_encode_fuzz_tiny_table(tiny):
+    w, (tok, orc) = tiny
+    alpha = list("abcdefghijklmnopqrstuvwxyz      ABC'.,;!?\n\t0123456789") + ["é", "中", "😀"]
+    segs = [(s, False) for s in _fuzz(6, 3000, 40, alpha)]
+    say("encode fuzz with the tiny table")
+    assert_ids(tok, orc, segs, what="tiny fuzz")
+    text = b" ".join(_fuzz(7, 3000, 200, alpha))
+    assert_ids(tok, orc, [(text, False)], what="tiny fuzz long")
+
+
+def test_long_pieces_tiny_table(tiny):
+    w, (tok, orc) = tiny
+    r = random.Random(8)
+    segs = []
+    for _ in range(60):
+        L = r.choice([65, 100, 128, 300, 1000, 3000])
+        segs.append(("".join(r.choice("abcdeinorst") for _ in range(L)).encode(), False))
+        segs.append(((" " * L + "x").encode(), False))
+    say("long pieces")
+    assert_ids(tok, orc, segs, what="long pieces")
+
+
+# ---------------------------------------------------------------- errors ----
+
+@pytest.mark.parametrize("bad,pos", [(b"ab\xc0\x80", 2), (b"a\xed\xa0\x80", 1),
+                                     (b"\xe4\xb8", 0), (b"xy\xf4\x90\x80\x80", 2),
+                                     (b"\x80", 0), (b"ok\xe0\x9f\xbf", 2), (b"\xff", 0),
+                                     (b"a" * 100 + b"\xe4\xb8" + b"b" * 100, 100)])
+def test_invalid_utf8(atoms, bad, pos):
+    tok, orc = atoms
+    segs = [(b"fine text", False), (bad, False), (b"more", False)]
+    say("utf8 error case", bad[:12])
+    with pytest.raises(B.BBPEError) as e:
+        tok.encode_segments(segs)
+    assert e.value.status == B.E_UTF8
+    assert (e.value.segment, e.value.byte_offset) == (1, 9 + pos)
+    with pytest.raises(OracleError):
+        orc.encode_segments(segs)
+
+
+def test_utf8_char_split_across_segments(atoms):
+    tok, _ = atoms
+    c = "中".encode()
+    say("utf8 split across segments")
+    with pytest.raises(B.BBPEError) as e:
+        tok.encode_segments([(b"x" + c[:1], False), (c[1:] + b"y", False)])
+    assert (e.value.segment, e.value.byte_offset) == (0, 1)
+
+
+def test_capacity_and_empty(atoms):
+    tok, orc = atoms
+    say("capacity and empty inputs")
+    text, off, allow, total = B.to_device_segments([(b"hello world", False)])
+    small = torch.empty(3, dtype=torch.int32, device="cuda")
+    with pytest.raises(B.BBPEError) as e:
+        tok.encode_device(text, off, allow, total, ids=small)
+    assert e.value.status == B.E_CAPACITY
+    ids, id_off = tok.encode_segments([(b"", False), (b"", True)])
+    assert ids.numel() == 0 and id_off.cpu().tolist() == [0, 0, 0]
+    assert_ids(tok, orc, [(b"", False), (b"a", False), (b"", False)], what="empty")

@@ -1,0 +1,51 @@
+"""GPU parity on the full-size workloads: every id and every segment offset
+of the HIP path equals the oracle's, and decode restores the text."""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import byte_level_bpe_amd as B  # noqa: E402
+from oracle import Oracle  # noqa: E402
+from synth import configs  # noqa: E402
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("name", ["tiny", "main", "agentic", "ragged"])
+def test_workload_parity(name):
+    w = configs.ALL[name]()
+    tok = B.load_ranks(w.tokens, w.specials, w.grammar)
+    orc = Oracle(w.tokens, w.specials, w.grammar)
+    say("workload", name, w.text_bytes, "bytes", len(w.segments), "segments")
+    ids, id_off = tok.encode_segments(w.segments, w.tiktoken_safe)
+    ids = ids.cpu().numpy()
+    id_off = id_off.cpu().numpy()
+    oids, ooff = orc.encode_segments(w.segments, w.tiktoken_safe)
+    if not np.array_equal(ids, oids):
+        n = min(len(ids), len(oids))
+        d = np.nonzero(ids[:n] != oids[:n])[0]
+        k = int(d[0]) if len(d) else n
+        raise AssertionError("%s: %d vs %d ids, first difference at %d: gpu %s oracle %s"
+                             % (name, len(ids), len(oids), k, ids[k:k + 8].tolist(),
+                                oids[k:k + 8].tolist()))
+    assert np.array_equal(id_off, ooff)
+    text = b"".join(s for s, _ in w.segments)
+    assert tok.decode(ids) == text
+    assert len(ids) <= len(text)
+
+
+def test_large_workload_parity():
+    pytest.skip("the o200k-style split is not yet implemented in the HIP path")
