@@ -53,7 +53,7 @@ def algorithmic_bytes(kernel: str, n: int, n_seg: int, n_ids: int, n_pieces: int
     return n
 
 
-def cpu_baseline(w, budget_s: float = 10.0, max_reps: int = 8) -> dict:
+def cpu_baseline(w, budget_s: float = 10.0, max_reps: int = 200) -> dict:
     """The oracle (plain single-threaded C++) over the whole workload,
     repeated until about budget_s seconds of CPU work."""
     from oracle import Oracle

@@ -1,0 +1,200 @@
+// Classification of one 64-byte word into per-class bitmasks (gfx950).
+//
+// ASCII bytes are classified four at a time with SWAR range tests on 32-bit
+// words (the high bit of each byte lane carries the result), so the common
+// all-ASCII word needs no per-byte branches.  Bytes >= 0x80 are handled by a
+// slow path that decodes only the multi-byte characters, reading their bytes
+// from the text, validates UTF-8 and looks up the code point's class.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bbpe_device.h"
+
+namespace bbpe {
+
+// For four bytes < 0x80 packed in d: 0x80 in every byte lane whose byte is >= lo (lo <= 0x80).
+__device__ __forceinline__ uint32_t swar_ge(uint32_t d, uint32_t lo) {
+  return (d + (0x80808080u - lo * 0x01010101u)) & 0x80808080u;
+}
+__device__ __forceinline__ uint32_t swar_in(uint32_t d, uint32_t lo, uint32_t hi) {
+  return swar_ge(d, lo) & ~swar_ge(d, hi + 1);
+}
+__device__ __forceinline__ uint32_t swar_eq(uint32_t d, uint32_t c) { return swar_in(d, c, c); }
+// the four byte-lane flags (bit 7 of each byte) as a 4-bit value
+__device__ __forceinline__ uint64_t gather4(uint32_t f) {
+  return uint64_t((((f >> 7) * 0x00204081u) >> 21) & 0xFu);
+}
+
+// Bits [i, i+len) of a 64-bit mask, clipped to [0, 64).
+__device__ __forceinline__ uint64_t bit_range(int i, int len) {
+  const int e = min(64, i + len);
+  if (e <= i) return 0;
+  const uint64_t hi = (e == 64) ? ~uint64_t(0) : (bit(e) - 1);
+  return hi & ~(bit(i) - 1);
+}
+
+__device__ __forceinline__ bool seg_start_at(uint64_t seg_lo, uint64_t seg_hi, int k) {
+  const int s = k + 8;  // window index k -> segment-mask bit k + 8
+  if (s < 0 || s >= 128) return false;
+  return s < 64 ? ((seg_lo >> s) & 1) : ((seg_hi >> (s - 64)) & 1);
+}
+
+// Decode the sequence whose lead byte is at text offset base + i (i may be
+// negative down to -3), reading bytes from the text.  ok = complete, minimal,
+// no surrogate, <= U+10FFFF, inside the text and crossing no segment start.
+__device__ __forceinline__ uint32_t decode_text(const uint8_t *__restrict__ text, uint64_t n,
+                                                int64_t base, int i, uint64_t seg_lo,
+                                                uint64_t seg_hi, int &len, bool &ok) {
+  const int64_t p = base + i;
+  const uint32_t b0 = text[p];
+  len = utf8_len(b0);
+  ok = len > 0 && uint64_t(p) + uint64_t(len) <= n;
+  if (!ok || len == 1) return b0;
+  uint32_t cp = b0 & (0x7Fu >> len);
+  for (int j = 1; j < len; ++j) {
+    const uint32_t b = text[p + j];
+    ok = ok && ((b & 0xC0u) == 0x80u) && !seg_start_at(seg_lo, seg_hi, i + j);
+    cp = (cp << 6) | (b & 0x3Fu);
+  }
+  if (len == 3 && cp < 0x800) ok = false;
+  if (len == 4 && (cp < 0x10000 || cp > 0x10FFFF)) ok = false;
+  if (cp >= 0xD800 && cp <= 0xDFFF) ok = false;
+  return cp;
+}
+
+// Set the class bits of one multi-byte character occupying bits `bits`.
+// (selects rather than branches, so that the masks stay in registers)
+__device__ __forceinline__ void add_class(WordMasks &m, uint32_t cls, uint64_t bits) {
+  m.LU |= (cls == CC_LU) ? bits : 0;
+  m.LL |= (cls == CC_LL) ? bits : 0;
+  m.LB |= (cls == CC_LO) ? bits : 0;
+  m.N |= (cls == CC_N) ? bits : 0;
+  m.WS |= (cls == CC_WS) ? bits : 0;
+  m.M |= (cls == CC_M) ? bits : 0;
+}
+
+// Classify the 64 bytes of the word at text offset base (window = bytes
+// [base-16, base+80)).  seg_lo/seg_hi: segment starts at window indices
+// -8..119 (bit j <-> index j-8).
+__device__ __forceinline__ void classify_word(const DevTables &T, const uint8_t *__restrict__ text,
+                                              const Window &win, int64_t base, uint64_t n,
+                                              uint64_t seg_lo, uint64_t seg_hi, WordMasks &m) {
+  m.valid = 0;
+  if (base >= 0 && uint64_t(base) < n) {
+    const uint64_t left = n - uint64_t(base);
+    m.valid = left >= 64 ? ~uint64_t(0) : (bit(int(left)) - 1);
+  }
+  m.lead = m.L = m.N = m.WS = m.CR = m.SP = m.AP = m.M = m.LU = m.LL = m.LB = 0;
+  m.c_sdmt = m.c_l = m.c_v = m.c_e = m.c_r = m.c_ls0 = m.c_ls1 = 0;
+  m.err = 64;
+  m.na = 0;
+  if (!m.valid) return;
+
+  uint64_t asc = 0, hi2 = 0;  // ASCII bytes; bytes >= 0xC0 (lead bytes of multi-byte chars)
+  uint32_t ap_near = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const uint32_t raw = win.w[4 + q];
+    const uint32_t a4 = ~raw & 0x80808080u;
+    // with bit 7 cleared no byte lane can carry into the next one; the
+    // results for non-ASCII lanes are masked off by a4
+    const uint32_t d = raw & 0x7F7F7F7Fu;
+    const int sh = 4 * q;
+    asc |= gather4(a4) << sh;
+    hi2 |= gather4(raw & (raw << 1) & 0x80808080u) << sh;
+    m.LU |= gather4(swar_in(d, 0x41, 0x5A) & a4) << sh;
+    m.LL |= gather4(swar_in(d, 0x61, 0x7A) & a4) << sh;
+    m.N |= gather4(swar_in(d, 0x30, 0x39) & a4) << sh;
+    m.WS |= gather4((swar_in(d, 9, 13) | swar_eq(d, 32)) & a4) << sh;
+    m.CR |= gather4((swar_eq(d, 10) | swar_eq(d, 13)) & a4) << sh;
+    m.SP |= gather4(swar_eq(d, 32) & a4) << sh;
+    const uint32_t ap = swar_eq(d, 39) & a4;
+    m.AP |= gather4(ap) << sh;
+    ap_near |= ap;
+  }
+  {  // apostrophes in the two bytes before the word also look into it
+    const uint32_t raw = win.w[3];
+    ap_near |= swar_eq(raw & 0x7F7F7F7Fu, 39) & ~raw & 0x80800000u;
+  }
+  if (ap_near) {
+    // letters a contraction may consist of: s d m t l v e r, either case
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t raw = win.w[4 + q];
+      const uint32_t a4 = ~raw & 0x80808080u;
+      const uint32_t lc = (raw & 0x7F7F7F7Fu) | 0x20202020u;
+      const int sh = 4 * q;
+      m.c_sdmt |= gather4((swar_eq(lc, 's') | swar_eq(lc, 'd') | swar_eq(lc, 'm') | swar_eq(lc, 't')) & a4) << sh;
+      m.c_l |= gather4(swar_eq(lc, 'l') & a4) << sh;
+      m.c_v |= gather4(swar_eq(lc, 'v') & a4) << sh;
+      m.c_e |= gather4(swar_eq(lc, 'e') & a4) << sh;
+      m.c_r |= gather4(swar_eq(lc, 'r') & a4) << sh;
+    }
+  }
+  uint64_t lead = asc;
+
+  const uint64_t non = ~asc & m.valid;
+  m.na = non;
+  if (non) {
+    // multi-byte characters: continuation bytes are covered by a valid lead
+    uint64_t covered = 0;
+    uint32_t err = 64;
+    // a character that began up to three bytes before the word
+    if (!(hi2 & 1) && (non & 1)) {
+      int kf = 0;
+      if ((win.at(-1) & 0xC0u) != 0x80u) kf = 1;
+      else if ((win.at(-2) & 0xC0u) != 0x80u) kf = 2;
+      else if ((win.at(-3) & 0xC0u) != 0x80u) kf = 3;
+      if (kf > 0 && base - kf >= 0) {
+        int len;
+        bool ok;
+        const uint32_t cp = decode_text(text, n, base, -kf, seg_lo, seg_hi, len, ok);
+        if (ok && len > kf) {
+          const uint64_t bits = bit_range(0, len - kf);
+          covered |= bits;
+          add_class(m, class_of(T, cp), bits);
+          if (cp == 0x17F) m.c_ls1 |= 1;  // its second byte
+        }
+      }
+    }
+    uint64_t leads = hi2 & m.valid;
+    // invalid lead bytes (C0, C1, F5..FF) are >= 0xC0 too; decode_text rejects them
+    while (leads) {
+      const int i = __ffsll(static_cast<unsigned long long>(leads)) - 1;
+      leads &= leads - 1;
+      int len;
+      bool ok;
+      const uint32_t cp = decode_text(text, n, base, i, seg_lo, seg_hi, len, ok);
+      lead |= bit(i);
+      if (!ok) {
+        err = min(err, uint32_t(i));
+        continue;
+      }
+      const uint64_t bits = bit_range(i, len);
+      covered |= bits & ~bit(i);
+      add_class(m, class_of(T, cp), bits);
+      if (cp == 0x17F) {
+        m.c_ls0 |= bit(i);
+        if (i + 1 < 64) m.c_ls1 |= bit(i + 1);
+      }
+    }
+    // continuation bytes that no valid character claims are errors; they
+    // count as characters of their own (class "other")
+    const uint64_t cont = non & ~hi2;
+    const uint64_t stray = cont & ~covered;
+    if (stray) err = min(err, uint32_t(__ffsll(static_cast<unsigned long long>(stray)) - 1));
+    lead |= stray;
+    m.err = err;
+  }
+  const uint64_t v = m.valid;
+  m.L = m.LU | m.LL | m.LB;
+  m.lead = lead & v;
+  m.L &= v; m.N &= v; m.WS &= v; m.CR &= v; m.SP &= v; m.AP &= v; m.M &= v;
+  m.LU &= v; m.LL &= v; m.LB &= v;
+  m.c_sdmt &= v; m.c_l &= v; m.c_v &= v; m.c_e &= v; m.c_r &= v; m.c_ls0 &= v; m.c_ls1 &= v;
+  if (m.err < 64 && !((v >> m.err) & 1)) m.err = 64;
+}
+
+}  // namespace bbpe

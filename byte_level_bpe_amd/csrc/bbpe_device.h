@@ -113,6 +113,7 @@ struct WordMasks {
   // ASCII byte patterns for the contraction clause: s d m t / l / v / e / r
   // (either case), and the two bytes of U+017F
   uint64_t c_sdmt, c_l, c_v, c_e, c_r, c_ls0, c_ls1;
+  uint64_t na;     // bytes >= 0x80
   uint32_t err;    // first invalid-sequence byte in [0,64), or 64
 };
 
@@ -138,128 +139,6 @@ __device__ __forceinline__ int utf8_len(uint32_t b) {
   if (b < 0xF0) return 3;
   if (b < 0xF5) return 4;
   return 0;
-}
-
-// Decodes the sequence starting at window index k; ok = a complete, minimal,
-// non-surrogate code point <= U+10FFFF that crosses no segment start.
-// segmask bit j (j in [0,128)) marks a segment start at window index j-8.
-__device__ __forceinline__ uint32_t decode_at(const Window &win, int k, uint64_t seg_lo,
-                                              uint64_t seg_hi, int64_t avail, int &len,
-                                              bool &ok) {
-  const uint32_t b0 = win.at(k);
-  len = utf8_len(b0);
-  ok = len > 0 && len <= avail;
-  if (len <= 1) return b0;
-  uint32_t cp = b0 & (0x7Fu >> len);
-#pragma unroll
-  for (int j = 1; j < 4; ++j) {
-    if (j < len) {
-      const uint32_t b = win.at(k + j);
-      ok = ok && ((b & 0xC0u) == 0x80u);
-      const int s = k + j + 8;  // position in segmask
-      const bool segstart = s < 64 ? ((seg_lo >> s) & 1) : ((seg_hi >> (s - 64)) & 1);
-      ok = ok && !segstart;
-      cp = (cp << 6) | (b & 0x3Fu);
-    }
-  }
-  if (len == 3 && cp < 0x800) ok = false;
-  if (len == 4 && (cp < 0x10000 || cp > 0x10FFFF)) ok = false;
-  if (cp >= 0xD800 && cp <= 0xDFFF) ok = false;
-  return cp;
-}
-
-// Classify the 64 bytes of one word.  base: absolute offset of byte 0;
-// n: text length; seg_lo/seg_hi: segment starts at window indices -8..119.
-__device__ __forceinline__ void classify_word(const DevTables &T, const Window &win,
-                                              int64_t base, uint64_t n, uint64_t seg_lo,
-                                              uint64_t seg_hi, WordMasks &m) {
-  m.valid = 0;
-  if (base >= 0 && uint64_t(base) < n) {
-    const uint64_t left = n - uint64_t(base);
-    m.valid = left >= 64 ? ~uint64_t(0) : (bit(int(left)) - 1);
-  }
-  m.lead = m.L = m.N = m.WS = m.CR = m.SP = m.AP = m.M = m.LU = m.LL = m.LB = 0;
-  m.c_sdmt = m.c_l = m.c_v = m.c_e = m.c_r = m.c_ls0 = m.c_ls1 = 0;
-  m.err = 64;
-  if (!m.valid) return;
-  const int64_t avail0 = int64_t(n) - base;  // bytes available from index 0
-
-  // The character covering byte 0 may start up to three bytes earlier: find
-  // the nearest non-continuation byte among the three before and decode it.
-  uint32_t cur = CC_OTHER;
-  int rem = 0;
-  {
-    int kf = 0;
-    if ((win.at(-1) & 0xC0u) != 0x80u) kf = 1;
-    else if ((win.at(-2) & 0xC0u) != 0x80u) kf = 2;
-    else if ((win.at(-3) & 0xC0u) != 0x80u) kf = 3;
-    if (kf > 0 && base - kf >= 0) {
-      int len = 0;
-      bool ok = false;
-      uint32_t cp = 0;
-      if (kf == 1) cp = decode_at(win, -1, seg_lo, seg_hi, avail0 + 1, len, ok);
-      else if (kf == 2) cp = decode_at(win, -2, seg_lo, seg_hi, avail0 + 2, len, ok);
-      else cp = decode_at(win, -3, seg_lo, seg_hi, avail0 + 3, len, ok);
-      if (ok && len > kf) {
-        cur = class_of(T, cp);
-        rem = len - kf;
-      }
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < 64; ++i) {
-    const uint32_t b = win.at(i);
-    const bool cont_byte = (b & 0xC0u) == 0x80u;
-    const bool seg_i = (i + 8 < 64) ? ((seg_lo >> (i + 8)) & 1) : ((seg_hi >> (i + 8 - 64)) & 1);
-    uint32_t cls;
-    bool is_lead;
-    if (cont_byte && rem > 0 && !seg_i) {
-      --rem;
-      cls = cur;
-      is_lead = false;
-    } else {
-      is_lead = true;
-      if (cont_byte) {
-        cls = CC_OTHER;  // stray continuation byte
-        rem = 0;
-        if (m.err == 64) m.err = uint32_t(i);
-      } else {
-        int len;
-        bool ok;
-        const uint32_t cp = decode_at(win, i, seg_lo, seg_hi, avail0 - i, len, ok);
-        cls = ok ? class_of(T, cp) : uint32_t(CC_OTHER);
-        rem = ok ? len - 1 : 0;
-        if (!ok && m.err == 64) m.err = uint32_t(i);
-      }
-      cur = cls;
-    }
-    const uint64_t bi = bit(i);
-    if (is_lead) m.lead |= bi;
-    if (cls == CC_LU) { m.L |= bi; m.LU |= bi; }
-    if (cls == CC_LL) { m.L |= bi; m.LL |= bi; }
-    if (cls == CC_LO) { m.L |= bi; m.LB |= bi; }
-    if (cls == CC_N) m.N |= bi;
-    if (cls == CC_WS) m.WS |= bi;
-    if (cls == CC_M) m.M |= bi;
-    if (b == '\r' || b == '\n') m.CR |= bi;
-    if (b == ' ') m.SP |= bi;
-    if (b == '\'') m.AP |= bi;
-    const uint32_t lc = b | 0x20u;
-    if (lc == 's' || lc == 'd' || lc == 'm' || lc == 't') m.c_sdmt |= bi;
-    if (lc == 'l') m.c_l |= bi;
-    if (lc == 'v') m.c_v |= bi;
-    if (lc == 'e') m.c_e |= bi;
-    if (lc == 'r') m.c_r |= bi;
-    if (b == 0xC5) m.c_ls0 |= bi;
-    if (b == 0xBF) m.c_ls1 |= bi;
-  }
-  // bytes past the end of the text belong to nothing
-  const uint64_t v = m.valid;
-  m.lead &= v; m.L &= v; m.N &= v; m.WS &= v; m.CR &= v; m.SP &= v; m.AP &= v; m.M &= v;
-  m.LU &= v; m.LL &= v; m.LB &= v;
-  m.c_sdmt &= v; m.c_l &= v; m.c_v &= v; m.c_e &= v; m.c_r &= v; m.c_ls0 &= v; m.c_ls1 &= v;
-  if (m.err < 64 && !((v >> m.err) & 1)) m.err = 64;
 }
 
 // Segment starts at window indices -8..119 of a lane (bit j <-> index j-8),

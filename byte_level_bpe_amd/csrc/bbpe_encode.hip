@@ -21,7 +21,7 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 struct WsLayout {
   uint64_t status, tile_nchar, tile_lastchg, tile_charbase, tile_chgcarry, seg_local, seg_charstart,
       ss, spst, spc, ps, tile_fn, tile_carry, tile_np, piece_start, piece_cnt, tmp_ids, scan_part,
-      long_list, lrank, lpart, lalive, lmin, total;
+      long_list, mid_list, lrank, lpart, lalive, lmin, total;
   uint64_t n_words;
   uint32_t n_tiles;
 };
@@ -56,6 +56,7 @@ WsLayout layout_for(uint64_t n, uint32_t n_seg) {
   take(L.tmp_ids, 4 * (n + 1));
   take(L.scan_part, 4 * ((n + 1) / 4096 + 2));
   take(L.long_list, 4 * (n / 64 + 1));
+  take(L.mid_list, 4 * (n / 32 + 1));
   take(L.lrank, 4 * (n + 1));
   take(L.lpart, 4 * (n + 1));
   take(L.lalive, n + 1);
@@ -71,7 +72,7 @@ __global__ void k_init(EncodeArgs a) {
     s->n_pieces = 0;
     s->n_ids = 0;
     s->n_long = 0;
-    s->pad = 0;
+    s->n_mid = 0;
     s->n_chars = 0;
     s->err_seg = 0;
     // offsets must start at 0 and end at the text length (monotonicity is
@@ -211,6 +212,7 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
   a.ws.tmp_ids = reinterpret_cast<int32_t *>(w + L.tmp_ids);
   a.ws.scan_part = reinterpret_cast<uint32_t *>(w + L.scan_part);
   a.ws.long_list = reinterpret_cast<uint32_t *>(w + L.long_list);
+  a.ws.mid_list = reinterpret_cast<uint32_t *>(w + L.mid_list);
   a.ws.lrank = reinterpret_cast<int32_t *>(w + L.lrank);
   a.ws.lpart = reinterpret_cast<int32_t *>(w + L.lpart);
   a.ws.lalive = w + L.lalive;
@@ -273,6 +275,7 @@ int bbpe_upload_tables(bbpe_tokenizer *t, void *d_mem, uint64_t bytes, void *str
   d.sp_bytes = b + L.sp_bytes;
   d.sp_off = reinterpret_cast<const uint32_t *>(b + L.sp_off);
   d.sp_id = reinterpret_cast<const int32_t *>(b + L.sp_id);
+  d.inner = reinterpret_cast<const uint32_t *>(b + L.inner);
   t->d_image = b;
   return BBPE_OK;
 }
@@ -296,6 +299,7 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
   a.ids = d_ids;
   a.ids_cap = ids_cap;
   a.id_off = d_id_off;
+  a.merge_units = 1;
   Launcher go{t, reinterpret_cast<hipStream_t>(stream)};
   launch_front(go, a, L);
   const uint32_t seg_grid = std::min<uint32_t>(1024, (n_seg + 256) / 256);
@@ -304,6 +308,8 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
   } else {
     const uint32_t merge_grid = uint32_t(std::min<uint64_t>((n + 63) / 64, 8192));
     go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
+    const uint32_t mid_grid = uint32_t(std::min<uint64_t>(n / 32 + 1, 4096));
+    go("k_merge_mid", k_merge_mid, dim3(mid_grid), dim3(64), a);
     const uint32_t long_grid = uint32_t(std::min<uint64_t>(n / 64 + 1, 2048));
     go("k_merge_long", k_merge_long, dim3(long_grid), dim3(64), a);
     const uint32_t nscan = uint32_t((n + 1 + 4095) / 4096);

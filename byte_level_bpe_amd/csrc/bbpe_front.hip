@@ -4,6 +4,7 @@
 // text word 62*t + l - 1 and owns it for 1 <= l <= 62.
 #include <hip/hip_runtime.h>
 
+#include "bbpe_classify.h"
 #include "bbpe_device.h"
 #include "bbpe_kernels.h"
 
@@ -29,7 +30,7 @@ __global__ void __launch_bounds__(64) k_count(EncodeArgs a) {
   uint32_t seg_at;
   segment_marks(a.seg_off, a.n_seg, base, seg_lo, seg_hi, seg_at);
   WordMasks m;
-  classify_word(a.T, win, base, a.n, seg_lo, seg_hi, m);
+  classify_word(a.T, a.text, win, base, a.n, seg_lo, seg_hi, m);
 
   const uint64_t segb = ((seg_lo >> 8) | (seg_hi << 56)) & m.valid;  // segment starts in [0,64)
   const uint64_t ws_prev = shfl_up64(m.WS, 1);
@@ -173,7 +174,7 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
   uint32_t seg_at;
   segment_marks(a.seg_off, a.n_seg, base, seg_lo, seg_hi, seg_at);
   WordMasks m;
-  classify_word(a.T, win, base, a.n, seg_lo, seg_hi, m);
+  classify_word(a.T, a.text, win, base, a.n, seg_lo, seg_hi, m);
   const uint64_t segb = ((seg_lo >> 8) | (seg_hi << 56)) & m.valid;
   const uint64_t ws_prev = shfl_up64(m.WS, 1);
   const uint64_t chg = m.lead & (segb | (m.WS ^ shl(m.WS, ws_prev, 1)));

@@ -65,6 +65,7 @@ struct DevTables {
   const uint8_t *sp_bytes;  // special strings
   const uint32_t *sp_off;   // [n_sp+1]
   const int32_t *sp_id;     // [n_sp]
+  const uint32_t *inner;    // [2048] bit (a*256+b): the byte pair (a,b) occurs inside some key
   uint32_t slot_mask;
   uint32_t n_sp;
   uint32_t sp_first[8];     // bitmap of first bytes of specials
@@ -74,7 +75,7 @@ struct DevTables {
 
 // Byte offsets of each table inside the uploaded image.
 struct ImageLayout {
-  uint64_t slots, blob, pair, atom, uni1, uni2, sp_bytes, sp_off, sp_id, total;
+  uint64_t slots, blob, pair, atom, uni1, uni2, sp_bytes, sp_off, sp_id, inner, total;
   uint32_t n_slots;
 };
 
@@ -91,8 +92,8 @@ struct Status {
   unsigned long long err_pos;     // first invalid UTF-8 byte (absolute), or ~0
   unsigned long long n_pieces;
   unsigned long long n_ids;
-  unsigned int n_long;            // pieces handed to the long-piece tier
-  unsigned int pad;
+  unsigned int n_long;            // units handed to the long tier
+  unsigned int n_mid;             // units handed to the mid tier
   unsigned long long n_chars;
   unsigned int err_seg;           // segment of err_pos
   unsigned int pad2;

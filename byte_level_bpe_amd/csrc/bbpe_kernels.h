@@ -27,7 +27,8 @@ struct WsPtrs {
   uint32_t *piece_cnt;              // [P+1] ids per piece, then their exclusive scan
   int32_t *tmp_ids;                 // [N] ids of each piece, at the piece's byte offset
   uint32_t *scan_part;              // [N/4096+2] partial sums of the piece scan
-  uint32_t *long_list;              // [N/64+1] pieces for the long-piece tier
+  uint32_t *long_list;              // [N/64+1] units for the long tier
+  uint32_t *mid_list;               // [N/32+1] units for the mid tier
   int32_t *lrank;                   // [N] long tier: pair rank at each part start
   int32_t *lpart;                   // [N] long tier: rank of the part starting here
   uint8_t *lalive;                  // [N] long tier: 1 where a part starts
@@ -44,6 +45,7 @@ struct EncodeArgs {
   uint32_t flags;
   uint64_t n_words;
   uint32_t n_tiles;
+  int32_t merge_units;   // 1: cut pieces into merge units (encode); 0: pieces (pre-tokenize)
   int32_t *ids;
   uint64_t ids_cap;
   int64_t *id_off;
@@ -59,6 +61,7 @@ __global__ void k_split(EncodeArgs a);
 __global__ void k_scan_tiles_np(EncodeArgs a);
 __global__ void k_pieces(EncodeArgs a);
 __global__ void k_merge(EncodeArgs a);
+__global__ void k_merge_mid(EncodeArgs a);
 __global__ void k_merge_long(EncodeArgs a);
 __global__ void k_scan_reduce(EncodeArgs a);
 __global__ void k_scan_partials(EncodeArgs a);

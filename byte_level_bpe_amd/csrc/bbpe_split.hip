@@ -19,6 +19,7 @@
 // compose across lanes (wave scans) and across tiles (a one-workgroup scan).
 #include <hip/hip_runtime.h>
 
+#include "bbpe_classify.h"
 #include "bbpe_device.h"
 #include "bbpe_kernels.h"
 
@@ -256,15 +257,14 @@ __device__ __forceinline__ uint64_t split_finish_g1(const SplitWord &o, uint64_t
 }
 
 __device__ __forceinline__ void lane_setup(const EncodeArgs &a, int lane, uint32_t t, int64_t &w,
-                                           WordMasks &m) {
+                                           WordMasks &m, Window &win) {
   w = int64_t(t) * TILE_WORDS + lane - 1;
   const int64_t base = w * 64;
-  Window win;
   load_window(a.text, a.n, base, win);
   uint64_t seg_lo, seg_hi;
   uint32_t seg_at;
   segment_marks(a.seg_off, a.n_seg, base, seg_lo, seg_hi, seg_at);
-  classify_word(a.T, win, base, a.n, seg_lo, seg_hi, m);
+  classify_word(a.T, a.text, win, base, a.n, seg_lo, seg_hi, m);
 }
 
 // previous-byte CR/LF within the span (needed by the emit pass)
@@ -280,7 +280,8 @@ __global__ void __launch_bounds__(64) k_split_agg(EncodeArgs a) {
   const uint32_t t = blockIdx.x;
   int64_t w;
   WordMasks m;
-  lane_setup(a, lane, t, w, m);
+  Window win;
+  lane_setup(a, lane, t, w, m, win);
   SplitWord o;
   split_word_g1(a, w, m, o);
   const bool owned = lane >= 1 && lane <= int(TILE_WORDS);
@@ -354,7 +355,8 @@ __global__ void __launch_bounds__(64) k_split(EncodeArgs a) {
   const uint32_t t = blockIdx.x;
   int64_t w;
   WordMasks m;
-  lane_setup(a, lane, t, w, m);
+  Window win;
+  lane_setup(a, lane, t, w, m, win);
   SplitWord o;
   split_word_g1(a, w, m, o);
   const bool owned = lane >= 1 && lane <= int(TILE_WORDS) && w < int64_t(a.n_words);
@@ -380,7 +382,25 @@ __global__ void __launch_bounds__(64) k_split(EncodeArgs a) {
   const uint32_t st = fcr_apply(exc, (carry >> 8) & 0xFFu);
   const uint32_t v = fv_apply(exv, (carry >> 16) & 1u);
   const uint64_t pCRm = prev_cr(o);
-  const uint64_t ps = split_finish_g1(o, pCRm, ph, st, v) & m.valid;
+  uint64_t ps = split_finish_g1(o, pCRm, ph, st, v) & m.valid;
+  if (a.merge_units) {
+    // Merge units: a byte pair that occurs inside no key can never be merged
+    // across (the merged part would be a key containing it), so the piece is
+    // cut there into independent units.  Checked where a non-ASCII byte is
+    // involved, which is where long pieces come from; skipping a check only
+    // leaves a unit longer, never changes the ids.
+    const uint64_t na_prev = shfl_up64(m.na, 1);
+    const uint64_t cand = o.IN & ~ps & ~o.SS & m.valid & (m.na | shl(m.na, na_prev, 1));
+    if (cand) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        if ((cand >> i) & 1) {
+          const uint32_t pr = (win.at(i - 1) << 8) | win.at(i);
+          if (!((a.T.inner[pr >> 5] >> (pr & 31)) & 1)) ps |= bit(i);
+        }
+      }
+    }
+  }
   const uint32_t np = owned ? uint32_t(__popcll(ps)) : 0u;
   if (owned) a.ws.ps[w] = ps;
   const uint32_t tot = wave_sum(np);

@@ -168,6 +168,7 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
   L.blob = o; o = align256(o + blob_bytes + 16);
   L.pair = o; o = align256(o + 65536 * 4);
   L.atom = o; o = align256(o + 256 * 4);
+  L.inner = o; o = align256(o + 65536 / 8);
   L.uni1 = o; o = align256(o + sizeof(kUniStage1));
   L.uni2 = o; o = align256(o + sizeof(kUniStage2));
   L.sp_bytes = o; o = align256(o + sp_bytes + 16);
@@ -204,6 +205,16 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
   int32_t *pair = reinterpret_cast<int32_t *>(img + L.pair);
   for (int i = 0; i < 65536; ++i) pair[i] = bbpe::RANK_NONE;
   int32_t *atom = reinterpret_cast<int32_t *>(img + L.atom);
+  // byte pairs that occur inside some key: a merge across any other pair is
+  // impossible, because the merged part would be a key containing it
+  uint32_t *inner = reinterpret_cast<uint32_t *>(img + L.inner);
+  for (uint32_t i = 0; i < n; ++i) {
+    const std::string &k = keys[i];
+    for (size_t j = 0; j + 1 < k.size(); ++j) {
+      const uint32_t pr = uint32_t(uint8_t(k[j])) * 256u + uint8_t(k[j + 1]);
+      inner[pr >> 5] |= 1u << (pr & 31);
+    }
+  }
   for (uint32_t i = 0; i < n; ++i) {
     const std::string &k = keys[i];
     if (k.size() == 2) pair[uint8_t(k[0]) * 256 + uint8_t(k[1])] = rk[i];
