@@ -112,19 +112,25 @@ def main():
     for _ in range(args.warmup):
         n_ids = step()
     torch.cuda.synchronize()
-    tok.set_timing(True)
-    tok.timing_reset()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # timed region: K whole calls, one event pair per call on the launch stream
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for k in range(args.steps):
         n_ids = step()
-    ev1.record(stream)
+        evs[k + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dev_ms = ev0.elapsed_time(ev1)
+    step_ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps))
+    dev_ms = evs[0].elapsed_time(evs[-1])
+    # per-kernel durations: the same K calls again with an event pair around
+    # every kernel launch (same stream); kept out of the timed region above
+    tok.set_timing(True)
+    tok.timing_reset()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     rep = tok.timing_report()
     tok.set_timing(False)
 
@@ -155,6 +161,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "device_ms_per_step": round(dev_ms / args.steps, 4),
+        "step_ms": {"median": round(step_ms[len(step_ms) // 2], 4), "min": round(step_ms[0], 4),
+                    "max": round(step_ms[-1], 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -5,11 +5,14 @@
 // pairs; repeatedly merge the lowest (leftmost on ties); recompute only the
 // two pairs that touch the merged part.  A merged part's id is the rank that
 // merged it; a part never merged is a single byte with its atom's rank.
-// Three tiers by unit length:
-//   short (<= 32 bytes): one lane per unit, bytes / pair ranks / part ids
-//     in registers with static indexing;
-//   mid (<= 1024 bytes): one wave per unit, state in LDS, argmin by a wave
-//     reduction;
+//
+// k_probe (one thread per unit) settles specials, single bytes and units
+// that are keys whose own merges rebuild them; the units left are listed by
+// length and merged by k_merge in three tiers:
+//   short (<= 32 bytes): one lane per unit, bytes / pair ranks / part ids in
+//     registers with static indexing;
+//   wave (<= 512 bytes): one wave per unit, eight positions per lane in
+//     registers, argmin by a wave reduction;
 //   long: one wave per unit, state in global memory.
 #include <hip/hip_runtime.h>
 
@@ -129,21 +132,19 @@ __device__ __forceinline__ int32_t special_id(const DevTables &T, const uint8_t 
 }
 
 // ---------------------------------------------------------------------------
-// Short tier: units of at most SK bytes, one lane each, in registers.
+// Unit bytes in registers: units of at most SK bytes, one lane each.
 // ---------------------------------------------------------------------------
-constexpr int SK = 32;
-constexpr int SNB = SK / 4 + 3;  // dwords of unit bytes, with room for 8-byte slices
-constexpr uint32_t MID_MAX = 1024;
-
+template <int SK>
 struct UnitBytes {
-  uint32_t d[SNB];
+  static constexpr int NB = SK / 4 + 3;  // dwords, with room for 8-byte slices
+  uint32_t d[NB];
   __device__ __forceinline__ uint32_t byte(int j) const { return (d[j >> 2] >> (8 * (j & 3))) & 0xFFu; }
-  // bytes a .. a+7 (a dynamic, a + 8 <= 4 * SNB)
+  // bytes a .. a+7 (a dynamic, a + 8 <= 4 * NB)
   __device__ __forceinline__ uint64_t slice8(uint32_t a) const {
     const uint32_t q = a >> 2, o = a & 3u;
     uint32_t x0 = 0, x1 = 0, x2 = 0;
 #pragma unroll
-    for (int qq = 0; qq + 2 < SNB; ++qq) {
+    for (int qq = 0; qq + 2 < NB; ++qq) {
       const bool hit = uint32_t(qq) == q;
       x0 = hit ? d[qq] : x0;
       x1 = hit ? d[qq + 1] : x1;
@@ -152,6 +153,12 @@ struct UnitBytes {
     const uint32_t lo = __builtin_amdgcn_alignbyte(x1, x0, o);
     const uint32_t hi = __builtin_amdgcn_alignbyte(x2, x1, o);
     return (uint64_t(hi) << 32) | lo;
+  }
+  __device__ __forceinline__ bool operator==(const UnitBytes &o) const {
+    bool eq = true;
+#pragma unroll
+    for (int q = 0; q < NB; ++q) eq = eq && d[q] == o.d[q];
+    return eq;
   }
 };
 
@@ -165,15 +172,17 @@ __device__ __forceinline__ uint32_t text_dword(const uint8_t *__restrict__ text,
 }
 
 // bytes [s, s+m) of the text, zero beyond m (m <= SK)
+template <int SK>
 __device__ __forceinline__ void load_unit(const uint8_t *__restrict__ text, uint64_t n, uint32_t s,
-                                          uint32_t m, UnitBytes &u) {
+                                          uint32_t m, UnitBytes<SK> &u) {
+  constexpr int NB = UnitBytes<SK>::NB;
   const uint64_t a0 = s & ~3u;
   const uint32_t off = s & 3u;
-  uint32_t raw[SNB + 1];
+  uint32_t raw[NB + 1];
 #pragma unroll
-  for (int q = 0; q <= SNB; ++q) raw[q] = (4u * q < off + m) ? text_dword(text, n, a0 + 4u * q) : 0u;
+  for (int q = 0; q <= NB; ++q) raw[q] = (4u * q < off + m) ? text_dword(text, n, a0 + 4u * q) : 0u;
 #pragma unroll
-  for (int q = 0; q < SNB; ++q) {
+  for (int q = 0; q < NB; ++q) {
     const uint32_t v = __builtin_amdgcn_alignbyte(raw[q + 1], raw[q], off);
     const int lim = int(m) - 4 * q;
     const uint32_t keep = lim >= 4 ? 0xFFFFFFFFu : (lim <= 0 ? 0u : ((1u << (8 * lim)) - 1));
@@ -181,8 +190,9 @@ __device__ __forceinline__ void load_unit(const uint8_t *__restrict__ text, uint
   }
 }
 
-__device__ __forceinline__ void unit_hash(const UnitBytes &u, uint32_t a, uint32_t len, uint64_t &h,
-                                          uint64_t &k8) {
+template <int SK>
+__device__ __forceinline__ void unit_hash(const UnitBytes<SK> &u, uint32_t a, uint32_t len,
+                                          uint64_t &h, uint64_t &k8) {
   h = hash_seed(len);
   k8 = 0;
   for (uint32_t i = 0; i < len; i += 8) {
@@ -192,7 +202,8 @@ __device__ __forceinline__ void unit_hash(const UnitBytes &u, uint32_t a, uint32
   }
 }
 
-__device__ __forceinline__ bool unit_rest_eq(const UnitBytes &u, uint32_t a, uint32_t len,
+template <int SK>
+__device__ __forceinline__ bool unit_rest_eq(const UnitBytes<SK> &u, uint32_t a, uint32_t len,
                                              const uint8_t *b) {
   for (uint32_t i = 8; i < len; i += 8) {
     const uint32_t k = min(8u, len - i);
@@ -205,7 +216,8 @@ __device__ __forceinline__ bool unit_rest_eq(const UnitBytes &u, uint32_t a, uin
 
 // Ranks of two keys of the unit, [a1, a1+l1) and [a2, a2+l2) (len 0 = none),
 // with the first probes of both issued together.
-__device__ __forceinline__ void unit_lookup2(const DevTables &T, const UnitBytes &u, uint32_t a1,
+template <int SK>
+__device__ __forceinline__ void unit_lookup2(const DevTables &T, const UnitBytes<SK> &u, uint32_t a1,
                                              uint32_t l1, uint32_t a2, uint32_t l2, int32_t &r1,
                                              int32_t &r2) {
   const bool v1 = l1 > 0 && l1 <= T.max_key_len, v2 = l2 > 0 && l2 <= T.max_key_len;
@@ -239,9 +251,12 @@ __device__ __forceinline__ void unit_lookup2(const DevTables &T, const UnitBytes
 
 __device__ __forceinline__ uint32_t above32(int j) { return ~((2u << j) - 1u); }
 
-// Merge a unit of 2 <= m <= SK bytes; writes its ids to out, returns their count.
-__device__ __forceinline__ uint32_t merge_short(const DevTables &T, const UnitBytes &u, uint32_t m,
-                                                int32_t *out) {
+// Merge a unit of 2 <= m <= SK bytes held in registers: pair ranks r[j] and
+// part ids pr[j] at every part start j, part starts as the bit mask bnd.
+// Writes the ids to out and returns their count.
+template <int SK>
+__device__ __forceinline__ uint32_t merge_short(const DevTables &T, const UnitBytes<SK> &u,
+                                                uint32_t m, int32_t *out) {
   int32_t r[SK], pr[SK];
 #pragma unroll
   for (int j = 0; j < SK; ++j) {
@@ -286,56 +301,196 @@ __device__ __forceinline__ uint32_t merge_short(const DevTables &T, const UnitBy
   return c;
 }
 
-__global__ void __launch_bounds__(64) k_merge(EncodeArgs a) {
+// ---------------------------------------------------------------------------
+// Probe pass: one thread per unit.
+// ---------------------------------------------------------------------------
+constexpr uint32_t WNS = 8;                // positions per lane in the wave tier
+constexpr uint32_t WAVE_MAX = 64 * WNS;    // longest unit the wave tier holds
+
+// Every unit: specials, single bytes and units that are keys whose own
+// merges rebuild them get their id here; the rest are listed for k_merge by
+// length.  Each block gathers its list entries in LDS and reserves room in
+// the global lists with one atomic per list (per-wave atomics on four
+// shared counters serialise at the L2).
+constexpr uint32_t PROBE_BLOCK = 256;
+
+__global__ void __launch_bounds__(PROBE_BLOCK) k_probe(EncodeArgs a) {
   if (a.ws.status->pad2) return;
-  const uint32_t P = uint32_t(a.ws.status->n_pieces);
+  Status *st = a.ws.status;
+  const uint32_t P = uint32_t(st->n_pieces);
   const DevTables &T = a.T;
-  for (uint32_t i = blockIdx.x * 64 + threadIdx.x; i < P; i += gridDim.x * 64) {
-    const uint32_t s = a.ws.piece_start[i];
-    const uint32_t m = a.ws.piece_start[i + 1] - s;
-    int32_t *out = a.ws.tmp_ids + s;
-    if ((a.ws.spst[s >> 6] >> (s & 63)) & 1) {
-      out[0] = special_id(T, a.text + s, m);
-      a.ws.piece_cnt[i] = 1;
-      continue;
-    }
-    if (m == 1) {
-      out[0] = T.atom[a.text[s]];
-      a.ws.piece_cnt[i] = 1;
-      continue;
-    }
-    if (m > uint32_t(SK)) {
-      uint32_t meta = 0;
-      const int32_t r = lookup_text(T, a.text + s, m, meta);
-      if (r != RANK_NONE && (meta & META_SELF)) {
-        out[0] = r;
-        a.ws.piece_cnt[i] = 1;
-      } else if (m <= MID_MAX) {
-        a.ws.mid_list[atomicAdd(&a.ws.status->n_mid, 1u)] = i;
+  __shared__ unsigned int s_cnt[4], s_base[4];
+  __shared__ uint32_t s_list[4][PROBE_BLOCK];
+  for (uint32_t b = blockIdx.x * PROBE_BLOCK; b < P; b += gridDim.x * PROBE_BLOCK) {
+    const uint32_t i = b + threadIdx.x;
+    int tier = 0;  // 1: <= 16 bytes, 2: <= 32, 3: wave, 4: long
+    if (i < P) {
+      const uint32_t s = a.ws.piece_start[i];
+      const uint32_t m = a.ws.piece_start[i + 1] - s;
+      int32_t id = -1;
+      if ((a.ws.spst[s >> 6] >> (s & 63)) & 1) {
+        id = special_id(T, a.text + s, m);
+      } else if (m == 1) {
+        id = T.atom[a.text[s]];
+      } else if (m <= 32) {
+        UnitBytes<32> u;
+        load_unit(a.text, a.n, s, m, u);
+        uint64_t h, k8;
+        unit_hash(u, 0, m, h, k8);
+        uint32_t meta = 0;
+        const int32_t r = m <= T.max_key_len
+                              ? probe(T, h, k8, m, meta,
+                                      [&](const uint8_t *bb) { return unit_rest_eq(u, 0, m, bb); })
+                              : RANK_NONE;
+        if (r != RANK_NONE && (meta & META_SELF)) id = r;
+        else tier = m <= 16 ? 1 : 2;
+      } else if (m <= T.max_key_len) {
+        uint32_t meta = 0;
+        const int32_t r = lookup_text(T, a.text + s, m, meta);
+        if (r != RANK_NONE && (meta & META_SELF)) id = r;
+        else tier = m <= WAVE_MAX ? 3 : 4;
       } else {
-        a.ws.long_list[atomicAdd(&a.ws.status->n_long, 1u)] = i;
+        tier = m <= WAVE_MAX ? 3 : 4;
       }
-      continue;
+      if (id >= 0) {
+        a.ws.tmp_ids[s] = id;
+        a.ws.piece_cnt[i] = 1;
+      }
     }
-    UnitBytes u;
-    load_unit(a.text, a.n, s, m, u);
-    // a unit that is itself a key whose own merges rebuild it
-    uint64_t h, k8;
-    unit_hash(u, 0, m, h, k8);
-    uint32_t meta = 0;
-    const int32_t r = probe(T, h, k8, m, meta,
-                            [&](const uint8_t *b) { return unit_rest_eq(u, 0, m, b); });
-    if (r != RANK_NONE && (meta & META_SELF)) {
-      out[0] = r;
-      a.ws.piece_cnt[i] = 1;
-      continue;
+    if (threadIdx.x < 4) s_cnt[threadIdx.x] = 0;
+    __syncthreads();
+    if (tier) s_list[tier - 1][atomicAdd(&s_cnt[tier - 1], 1u)] = i;
+    __syncthreads();
+    if (threadIdx.x < 4 && s_cnt[threadIdx.x]) {
+      unsigned int *cnt = threadIdx.x == 0 ? &st->n_l16
+                          : threadIdx.x == 1 ? &st->n_l32
+                          : threadIdx.x == 2 ? &st->n_lw : &st->n_ll;
+      s_base[threadIdx.x] = atomicAdd(cnt, s_cnt[threadIdx.x]);
     }
-    a.ws.piece_cnt[i] = merge_short(T, u, m, out);
+    __syncthreads();
+#pragma unroll
+    for (int L = 0; L < 4; ++L) {
+      uint32_t *list = L == 0 ? a.ws.l16 : L == 1 ? a.ws.l32 : L == 2 ? a.ws.lw : a.ws.ll;
+      for (uint32_t k = threadIdx.x; k < s_cnt[L]; k += PROBE_BLOCK) list[s_base[L] + k] = s_list[L][k];
+    }
+    __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// Wave tiers
+// Wave tier: one wave per unit of 33..WAVE_MAX bytes.  Position j lives in
+// lane j % 64, slot j / 64: its pair rank (RANK_NONE unless a part with a
+// right neighbour starts at j) and the id of the part starting at j.  The
+// part starts are a wave-uniform bit mask.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int32_t wave_min_i32(int32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const int32_t o = __shfl_xor(v, d, 64);
+    v = o < v ? o : v;
+  }
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// first set bit at position >= x, or m
+__device__ __forceinline__ uint32_t next_set(const uint64_t (&A)[WNS], uint32_t x, uint32_t m) {
+  uint32_t res = m;
+#pragma unroll
+  for (int t = int(WNS) - 1; t >= 0; --t) {
+    const uint32_t lo = 64u * uint32_t(t);
+    uint64_t w = A[t];
+    if (x >= lo + 64) w = 0;
+    else if (x > lo) w &= ~0ull << (x - lo);
+    res = w ? lo + uint32_t(__ffsll(static_cast<unsigned long long>(w)) - 1) : res;
+  }
+  return res;
+}
+
+// last set bit at position < x, or -1
+__device__ __forceinline__ int prev_set(const uint64_t (&A)[WNS], uint32_t x) {
+  int res = -1;
+#pragma unroll
+  for (int t = 0; t < int(WNS); ++t) {
+    const uint32_t lo = 64u * uint32_t(t);
+    uint64_t w = A[t];
+    if (x <= lo) w = 0;
+    else if (x < lo + 64) w &= (1ull << (x - lo)) - 1;
+    res = w ? int(lo) + 63 - __clzll(static_cast<long long>(w)) : res;
+  }
+  return res;
+}
+
+__device__ void merge_wave(const EncodeArgs &a, uint32_t i, int lane) {
+  const DevTables &T = a.T;
+  const uint32_t s = a.ws.piece_start[i];
+  const uint32_t m = a.ws.piece_start[i + 1] - s;
+  const uint8_t *p = a.text + s;
+  int32_t r[WNS], pr[WNS];
+  uint64_t A[WNS];
+#pragma unroll
+  for (uint32_t t = 0; t < WNS; ++t) {
+    const uint32_t j = 64u * t + uint32_t(lane);
+    const uint32_t b0 = j < m ? p[j] : 0u, b1 = j + 1 < m ? p[j + 1] : 0u;
+    r[t] = j + 1 < m ? T.pair[b0 * 256u + b1] : RANK_NONE;
+    pr[t] = j < m ? T.atom[b0] : 0;
+    const uint32_t lo = 64u * t;
+    A[t] = m >= lo + 64 ? ~0ull : (m > lo ? (1ull << (m - lo)) - 1 : 0ull);
+  }
+  for (uint32_t round = 0; round + 1 < m; ++round) {
+    int32_t lm = RANK_NONE;
+#pragma unroll
+    for (uint32_t t = 0; t < WNS; ++t) lm = r[t] < lm ? r[t] : lm;
+    const int32_t best = wave_min_i32(lm);
+    if (best == RANK_NONE) break;
+    uint32_t bj = m;  // leftmost position holding the minimum
+#pragma unroll
+    for (int t = int(WNS) - 1; t >= 0; --t) {
+      const unsigned long long bal = __ballot(r[t] == best);
+      bj = bal ? 64u * uint32_t(t) + uint32_t(__ffsll(bal) - 1) : bj;
+    }
+    const uint32_t k = next_set(A, bj + 1, m);   // the part merged into bj
+    const uint32_t k2 = next_set(A, k + 1, m);   // end of the merged part
+    const uint32_t end2 = k2 < m ? next_set(A, k2 + 1, m) : m;
+    const int q = prev_set(A, bj);
+    // lane 0: the merged part with its right neighbour; lane 1: the left
+    // neighbour with the merged part (both lookups run side by side)
+    uint32_t ks = 0, kl = 0;
+    if (lane == 0 && k2 < m) { ks = bj; kl = end2 - bj; }
+    if (lane == 1 && q >= 0) { ks = uint32_t(q); kl = k2 - uint32_t(q); }
+    int32_t rv = RANK_NONE;
+    if (kl) {
+      uint32_t meta;
+      rv = lookup_text(T, p + ks, kl, meta);
+    }
+    const int32_t nb = __shfl(rv, 0, 64), nq = __shfl(rv, 1, 64);
+#pragma unroll
+    for (uint32_t t = 0; t < WNS; ++t) {
+      const uint32_t j = 64u * t + uint32_t(lane);
+      r[t] = j == k ? RANK_NONE : r[t];
+      r[t] = j == bj ? nb : r[t];
+      pr[t] = j == bj ? best : pr[t];
+      r[t] = (q >= 0 && j == uint32_t(q)) ? nq : r[t];
+      A[t] = (k >> 6) == t ? A[t] & ~(1ull << (k & 63)) : A[t];
+    }
+  }
+  uint32_t c = 0;
+  const unsigned long long below = (1ull << lane) - 1;
+#pragma unroll
+  for (uint32_t t = 0; t < WNS; ++t) {
+    if ((A[t] >> lane) & 1) a.ws.tmp_ids[s + c + uint32_t(__popcll(A[t] & below))] = pr[t];
+    c += uint32_t(__popcll(A[t]));
+  }
+  a.ws.piece_cnt[i] = c;  // c is the same in every lane
+}
+
+// ---------------------------------------------------------------------------
+// Long tier: one wave per unit longer than WAVE_MAX.  Arrays indexed by text
+// byte position (units never overlap): lrank = pair rank at a part start,
+// lpart = id of the part starting there, lalive = 1 where a part starts;
+// per-64-byte-block minima of (rank << 32 | offset) in lmin, at index
+// s/32 + block (a unit of m > 64 bytes needs ceil(m/64) <= floor(m/32)
+// entries, so units never share one).  Lane 0 applies each merge;
+// device-scope fences make its stores visible to the other lanes.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
 #pragma unroll
@@ -346,108 +501,6 @@ __device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v)
   return v;
 }
 
-// Mid tier: one wave per unit of at most MID_MAX bytes, all state in LDS.
-__global__ void __launch_bounds__(64) k_merge_mid(EncodeArgs a) {
-  if (a.ws.status->pad2) return;
-  __shared__ uint8_t s_b[MID_MAX];
-  __shared__ int32_t s_r[MID_MAX];
-  __shared__ int32_t s_pr[MID_MAX];
-  __shared__ unsigned long long s_alive[MID_MAX / 64];
-  const int lane = threadIdx.x;
-  const uint32_t nm = a.ws.status->n_mid;
-  const DevTables &T = a.T;
-  for (uint32_t li = blockIdx.x; li < nm; li += gridDim.x) {
-    const uint32_t i = a.ws.mid_list[li];
-    const uint32_t s = a.ws.piece_start[i];
-    const uint32_t m = a.ws.piece_start[i + 1] - s;
-    const uint32_t nw = (m + 63) / 64;
-    for (uint32_t j = uint32_t(lane); j < m; j += 64) s_b[j] = a.text[s + j];
-    __syncthreads();
-    for (uint32_t j = uint32_t(lane); j < m; j += 64) {
-      s_r[j] = (j + 1 < m) ? T.pair[uint32_t(s_b[j]) * 256u + s_b[j + 1]] : RANK_NONE;
-      s_pr[j] = T.atom[s_b[j]];
-    }
-    for (uint32_t wd = uint32_t(lane); wd < nw; wd += 64) {
-      const uint32_t left = m - wd * 64;
-      s_alive[wd] = left >= 64 ? ~0ull : ((1ull << left) - 1);
-    }
-    __syncthreads();
-    // next / previous part start after / before position p (parts are keys,
-    // at most BBPE_MAX_KEY_BYTES long, so at most three words are read)
-    auto next_alive = [&](uint32_t p) -> uint32_t {
-      uint32_t x = p + 1;
-      while (x < m) {
-        const uint32_t wd = x >> 6;
-        const unsigned long long bits = s_alive[wd] & (~0ull << (x & 63));
-        if (bits) return wd * 64 + uint32_t(__ffsll(bits) - 1);
-        x = (wd + 1) * 64;
-      }
-      return m;
-    };
-    auto prev_alive = [&](uint32_t p) -> int {
-      int x = int(p) - 1;
-      while (x >= 0) {
-        const uint32_t wd = uint32_t(x) >> 6;
-        const unsigned long long msk = (x & 63) == 63 ? ~0ull : ((1ull << ((x & 63) + 1)) - 1);
-        const unsigned long long bits = s_alive[wd] & msk;
-        if (bits) return int(wd * 64 + 63 - __clzll(bits));
-        x = int(wd * 64) - 1;
-      }
-      return -1;
-    };
-    for (uint32_t round = 0; round + 1 < m; ++round) {
-      unsigned long long key = ~0ull;
-      for (uint32_t j = uint32_t(lane); j < m; j += 64) {
-        const int32_t rv = s_r[j];
-        const unsigned long long kk =
-            rv == RANK_NONE ? ~0ull : ((static_cast<unsigned long long>(uint32_t(rv)) << 32) | j);
-        key = kk < key ? kk : key;
-      }
-      key = wave_min_u64(key);
-      if (key == ~0ull) break;
-      const int32_t best = int32_t(key >> 32);
-      const uint32_t bj = uint32_t(key & 0xffffffffu);
-      const uint32_t k = next_alive(bj);
-      const uint32_t k2 = next_alive(k);  // start of the part after the merged one
-      const uint32_t end2 = (k2 < m) ? next_alive(k2) : m;
-      const int q = prev_alive(bj);
-      // lane 0 looks up the merged part with its right neighbour, lane 1 the
-      // left neighbour with the merged part
-      int32_t rv = RANK_NONE;
-      uint32_t meta;
-      if (lane == 0 && k2 < m) rv = lookup_text(T, a.text + s + bj, end2 - bj, meta);
-      if (lane == 1 && q >= 0) rv = lookup_text(T, a.text + s + uint32_t(q), k2 - uint32_t(q), meta);
-      const int32_t nb = __shfl(rv, 0, 64), nq = __shfl(rv, 1, 64);
-      __syncthreads();
-      if (lane == 0) {
-        s_alive[k >> 6] &= ~(1ull << (k & 63));
-        s_r[k] = RANK_NONE;
-        s_r[bj] = nb;
-        s_pr[bj] = best;
-        if (q >= 0) s_r[q] = nq;
-      }
-      __syncthreads();
-    }
-    uint32_t c = 0;
-    for (uint32_t j0 = 0; j0 < m; j0 += 64) {
-      const uint32_t j = j0 + uint32_t(lane);
-      const bool hit = j < m && ((s_alive[j >> 6] >> (j & 63)) & 1);
-      const unsigned long long bal = __ballot(hit);
-      if (hit) a.ws.tmp_ids[s + c + uint32_t(__popcll(bal & ((1ull << lane) - 1)))] = s_pr[j];
-      c += uint32_t(__popcll(bal));
-    }
-    if (lane == 0) a.ws.piece_cnt[i] = c;
-    __syncthreads();
-  }
-}
-
-// Long tier: one wave per unit longer than MID_MAX.  Arrays indexed by text
-// byte position (units never overlap): lrank = pair rank at a part start,
-// lpart = id of the part starting there, lalive = 1 where a part starts;
-// per-64-byte-block minima of (rank << 32 | offset) in lmin, at index
-// s/32 + block (a unit of m > 64 bytes needs ceil(m/64) <= floor(m/32)
-// entries, so units never share one).  Lane 0 applies each merge;
-// device-scope fences make its stores visible to the other lanes.
 __device__ __forceinline__ bool alive(const EncodeArgs &a, uint32_t pos) {
   return a.ws.lalive[pos] != 0;
 }
@@ -464,103 +517,138 @@ __device__ __forceinline__ unsigned long long block_min(const EncodeArgs &a, uin
   return wave_min_u64(key);
 }
 
-__global__ void __launch_bounds__(64) k_merge_long(EncodeArgs a) {
-  if (a.ws.status->pad2) return;
-  const int lane = threadIdx.x;
-  const uint32_t nl = a.ws.status->n_long;
+__device__ void merge_long(const EncodeArgs &a, uint32_t i, int lane) {
   const DevTables &T = a.T;
-  for (uint32_t li = blockIdx.x; li < nl; li += gridDim.x) {
-    const uint32_t i = a.ws.long_list[li];
-    const uint32_t s = a.ws.piece_start[i];
-    const uint32_t m = a.ws.piece_start[i + 1] - s;
-    const uint8_t *p = a.text + s;
-    unsigned long long *lmin = a.ws.lmin + (s >> 5);
-    const uint32_t nblk = (m + 63) / 64;
-    for (uint32_t j = uint32_t(lane); j < m; j += 64) {
-      a.ws.lrank[s + j] = (j + 1 < m) ? T.pair[uint32_t(p[j]) * 256u + p[j + 1]] : RANK_NONE;
-      a.ws.lpart[s + j] = T.atom[p[j]];
-      a.ws.lalive[s + j] = 1;
+  const uint32_t s = a.ws.piece_start[i];
+  const uint32_t m = a.ws.piece_start[i + 1] - s;
+  const uint8_t *p = a.text + s;
+  unsigned long long *lmin = a.ws.lmin + (s >> 5);
+  const uint32_t nblk = (m + 63) / 64;
+  for (uint32_t j = uint32_t(lane); j < m; j += 64) {
+    a.ws.lrank[s + j] = (j + 1 < m) ? T.pair[uint32_t(p[j]) * 256u + p[j + 1]] : RANK_NONE;
+    a.ws.lpart[s + j] = T.atom[p[j]];
+    a.ws.lalive[s + j] = 1;
+  }
+  __threadfence();
+  for (uint32_t b = 0; b < nblk; ++b) {
+    const unsigned long long v = block_min(a, s, m, b, lane);
+    if (lane == 0) lmin[b] = v;
+  }
+  __threadfence();
+  // every round removes one part, so at most m - 1 rounds
+  for (uint32_t round = 0; round + 1 < m; ++round) {
+    unsigned long long key = ~0ull;
+    for (uint32_t b = uint32_t(lane); b < nblk; b += 64) {
+      const unsigned long long v = lmin[b];
+      key = v < key ? v : key;
     }
-    __threadfence();
-    for (uint32_t b = 0; b < nblk; ++b) {
-      const unsigned long long v = block_min(a, s, m, b, lane);
-      if (lane == 0) lmin[b] = v;
+    key = wave_min_u64(key);
+    if (key == ~0ull) break;
+    const int32_t best = int32_t(key >> 32);
+    const uint32_t bj = uint32_t(key & 0xffffffffu);
+    // the part after bj starts within BBPE_MAX_KEY_BYTES (parts are keys)
+    uint32_t k = m;
+    for (uint32_t off = 1; off <= BBPE_MAX_KEY_BYTES + 1 && k == m; off += 64) {
+      const uint32_t j = bj + off + uint32_t(lane);
+      const unsigned long long bal = __ballot(j < m && alive(a, s + j));
+      if (bal) k = bj + off + uint32_t(__ffsll(bal) - 1);
     }
-    __threadfence();
-    // every round removes one part, so at most m - 1 rounds
-    for (uint32_t round = 0; round + 1 < m; ++round) {
-      unsigned long long key = ~0ull;
-      for (uint32_t b = uint32_t(lane); b < nblk; b += 64) {
-        const unsigned long long v = lmin[b];
-        key = v < key ? v : key;
-      }
-      key = wave_min_u64(key);
-      if (key == ~0ull) break;
-      const int32_t best = int32_t(key >> 32);
-      const uint32_t bj = uint32_t(key & 0xffffffffu);
-      // the part after bj starts within BBPE_MAX_KEY_BYTES (parts are keys)
-      uint32_t k = m;
-      for (uint32_t off = 1; off <= BBPE_MAX_KEY_BYTES + 1 && k == m; off += 64) {
-        const uint32_t j = bj + off + uint32_t(lane);
+    if (k >= m) break;  // cannot happen: a ranked pair has a right part
+    uint32_t k2 = m;
+    for (uint32_t off = 1; off <= BBPE_MAX_KEY_BYTES + 1 && k2 == m; off += 64) {
+      const uint32_t j = k + off + uint32_t(lane);
+      const unsigned long long bal = __ballot(j < m && alive(a, s + j));
+      if (bal) k2 = k + off + uint32_t(__ffsll(bal) - 1);
+    }
+    uint32_t end2 = m;
+    if (k2 < m) {
+      for (uint32_t off = 1; off <= BBPE_MAX_KEY_BYTES + 1 && end2 == m; off += 64) {
+        const uint32_t j = k2 + off + uint32_t(lane);
         const unsigned long long bal = __ballot(j < m && alive(a, s + j));
-        if (bal) k = bj + off + uint32_t(__ffsll(bal) - 1);
+        if (bal) end2 = k2 + off + uint32_t(__ffsll(bal) - 1);
       }
-      if (k >= m) break;  // cannot happen: a ranked pair has a right part
-      uint32_t k2 = m;
-      for (uint32_t off = 1; off <= BBPE_MAX_KEY_BYTES + 1 && k2 == m; off += 64) {
-        const uint32_t j = k + off + uint32_t(lane);
-        const unsigned long long bal = __ballot(j < m && alive(a, s + j));
-        if (bal) k2 = k + off + uint32_t(__ffsll(bal) - 1);
-      }
-      uint32_t end2 = m;
-      if (k2 < m) {
-        for (uint32_t off = 1; off <= BBPE_MAX_KEY_BYTES + 1 && end2 == m; off += 64) {
-          const uint32_t j = k2 + off + uint32_t(lane);
-          const unsigned long long bal = __ballot(j < m && alive(a, s + j));
-          if (bal) end2 = k2 + off + uint32_t(__ffsll(bal) - 1);
-        }
-      }
-      uint32_t q = m;
-      for (uint32_t off = 1; off <= BBPE_MAX_KEY_BYTES + 1 && q == m; off += 64) {
-        const int64_t j = int64_t(bj) - int64_t(off) - lane;
-        const unsigned long long bal = __ballot(j >= 0 && alive(a, s + uint32_t(j)));
-        if (bal) q = bj - off - uint32_t(__ffsll(bal) - 1);
-      }
-      int32_t rv = RANK_NONE;
+    }
+    uint32_t q = m;
+    for (uint32_t off = 1; off <= BBPE_MAX_KEY_BYTES + 1 && q == m; off += 64) {
+      const int64_t j = int64_t(bj) - int64_t(off) - lane;
+      const unsigned long long bal = __ballot(j >= 0 && alive(a, s + uint32_t(j)));
+      if (bal) q = bj - off - uint32_t(__ffsll(bal) - 1);
+    }
+    int32_t rv = RANK_NONE;
+    uint32_t ks = 0, kl = 0;
+    if (lane == 0 && k2 < m) { ks = bj; kl = end2 - bj; }
+    if (lane == 1 && q < m) { ks = q; kl = k2 - q; }
+    if (kl) {
       uint32_t meta;
-      if (lane == 0 && k2 < m) rv = lookup_text(T, p + bj, end2 - bj, meta);
-      if (lane == 1 && q < m) rv = lookup_text(T, p + q, k2 - q, meta);
-      const int32_t nb = __shfl(rv, 0, 64), nq = __shfl(rv, 1, 64);
-      if (lane == 0) {
-        a.ws.lalive[s + k] = 0;
-        a.ws.lpart[s + bj] = best;
-        a.ws.lrank[s + bj] = nb;
-        if (q < m) a.ws.lrank[s + q] = nq;
-        a.ws.lrank[s + k] = RANK_NONE;
-      }
-      __threadfence();
-      const uint32_t b0 = bj / 64, bk = k / 64, bq = (q < m) ? q / 64 : b0;
-      unsigned long long v = block_min(a, s, m, b0, lane);
-      if (lane == 0) lmin[b0] = v;
-      if (bk != b0) {
-        v = block_min(a, s, m, bk, lane);
-        if (lane == 0) lmin[bk] = v;
-      }
-      if (bq != b0 && bq != bk) {
-        v = block_min(a, s, m, bq, lane);
-        if (lane == 0) lmin[bq] = v;
-      }
-      __threadfence();
+      rv = lookup_text(T, p + ks, kl, meta);
     }
-    uint32_t c = 0;
-    for (uint32_t j0 = 0; j0 < m; j0 += 64) {
-      const uint32_t j = j0 + uint32_t(lane);
-      const bool hit = j < m && alive(a, s + j);
-      const unsigned long long bal = __ballot(hit);
-      if (hit) a.ws.tmp_ids[s + c + uint32_t(__popcll(bal & ((1ull << lane) - 1)))] = a.ws.lpart[s + j];
-      c += uint32_t(__popcll(bal));
+    const int32_t nb = __shfl(rv, 0, 64), nq = __shfl(rv, 1, 64);
+    if (lane == 0) {
+      a.ws.lalive[s + k] = 0;
+      a.ws.lpart[s + bj] = best;
+      a.ws.lrank[s + bj] = nb;
+      if (q < m) a.ws.lrank[s + q] = nq;
+      a.ws.lrank[s + k] = RANK_NONE;
     }
-    if (lane == 0) a.ws.piece_cnt[i] = c;
+    __threadfence();
+    const uint32_t b0 = bj / 64, bk = k / 64, bq = (q < m) ? q / 64 : b0;
+    unsigned long long v = block_min(a, s, m, b0, lane);
+    if (lane == 0) lmin[b0] = v;
+    if (bk != b0) {
+      v = block_min(a, s, m, bk, lane);
+      if (lane == 0) lmin[bk] = v;
+    }
+    if (bq != b0 && bq != bk) {
+      v = block_min(a, s, m, bq, lane);
+      if (lane == 0) lmin[bq] = v;
+    }
+    __threadfence();
+  }
+  uint32_t c = 0;
+  for (uint32_t j0 = 0; j0 < m; j0 += 64) {
+    const uint32_t j = j0 + uint32_t(lane);
+    const bool hit = j < m && alive(a, s + j);
+    const unsigned long long bal = __ballot(hit);
+    if (hit) a.ws.tmp_ids[s + c + uint32_t(__popcll(bal & ((1ull << lane) - 1)))] = a.ws.lpart[s + j];
+    c += uint32_t(__popcll(bal));
+  }
+  a.ws.piece_cnt[i] = c;  // c is the same in every lane
+}
+
+template <int SK>
+__device__ __forceinline__ void merge_short_unit(const EncodeArgs &a, uint32_t i) {
+  const uint32_t s = a.ws.piece_start[i];
+  const uint32_t m = a.ws.piece_start[i + 1] - s;
+  UnitBytes<SK> u;
+  load_unit(a.text, a.n, s, m, u);
+  a.ws.piece_cnt[i] = merge_short<SK>(a.T, u, m, a.ws.tmp_ids + s);
+}
+
+// Merge of every listed unit.  Work items in order: long units (the longest
+// chains), wave units, then chunks of 64 short units (one lane each); wave
+// w takes items w, w + G, w + 2G, ... (G waves in the grid), so the long
+// chains start first and short work fills the machine beside them.  The
+// item index is wave-uniform by construction: no lane-0 ticket and
+// broadcast, which lets the compiler split the loop per lane.
+__global__ void __launch_bounds__(64) k_merge(EncodeArgs a) {
+  if (a.ws.status->pad2) return;
+  const Status *st = a.ws.status;
+  const int lane = int(threadIdx.x);
+  const uint32_t nll = st->n_ll, nlw = st->n_lw, n32 = st->n_l32, n16 = st->n_l16;
+  const uint32_t e_ll = nll, e_lw = e_ll + nlw, e_32 = e_lw + (n32 + 63) / 64,
+                 e_16 = e_32 + (n16 + 63) / 64;
+  for (uint32_t item = blockIdx.x; item < e_16; item += gridDim.x) {
+    if (item < e_ll) {
+      merge_long(a, a.ws.ll[item], lane);
+    } else if (item < e_lw) {
+      merge_wave(a, a.ws.lw[item - e_ll], lane);
+    } else if (item < e_32) {
+      const uint32_t x = (item - e_lw) * 64 + uint32_t(lane);
+      if (x < n32) merge_short_unit<32>(a, a.ws.l32[x]);
+    } else {
+      const uint32_t x = (item - e_32) * 64 + uint32_t(lane);
+      if (x < n16) merge_short_unit<16>(a, a.ws.l16[x]);
+    }
   }
 }
 
@@ -644,21 +732,44 @@ __global__ void __launch_bounds__(SCAN_BLOCK) k_scan_down(EncodeArgs a) {
   uint32_t run = block_excl_scan(sum, sh, total) + a.ws.scan_part[blockIdx.x];
   for (uint32_t k = 0; k < SCAN_ITEMS; ++k) {
     const uint32_t i = b0 + threadIdx.x * SCAN_ITEMS + k;
-    if (i <= P) a.ws.piece_cnt[i] = run;  // piece_cnt[P] becomes the total
+    if (i <= P) a.ws.piece_off[i] = run;  // piece_off[P] is the total
     run += v[k];
   }
 }
 
-// ids in order: unit i's ids go to [id_base[i], id_base[i+1])
-__global__ void __launch_bounds__(256) k_assemble(EncodeArgs a) {
+// ids in order: unit i's ids go to [piece_off[i], piece_off[i+1]).  A
+// thread copies the ids of its unit; units with many ids (long runs the
+// merge left unmerged) are copied by the whole block afterwards.
+constexpr uint32_t ASM_BLOCK = 256, ASM_SMALL = 16;
+
+__global__ void __launch_bounds__(ASM_BLOCK) k_assemble(EncodeArgs a) {
   if (a.ws.status->pad2) return;
   const uint32_t P = uint32_t(a.ws.status->n_pieces);
-  const uint32_t total = P ? a.ws.piece_cnt[P] : 0u;
-  for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < P; i += gridDim.x * 256) {
-    const uint32_t o = a.ws.piece_cnt[i], e = a.ws.piece_cnt[i + 1];
-    const uint32_t s = a.ws.piece_start[i];
-    if (e <= a.ids_cap)
-      for (uint32_t j = 0; j < e - o; ++j) a.ids[o + j] = a.ws.tmp_ids[s + j];
+  const uint32_t total = P ? a.ws.piece_off[P] : 0u;
+  __shared__ unsigned int s_nbig;
+  __shared__ uint32_t s_big[ASM_BLOCK];
+  const bool fits = total <= a.ids_cap;
+  for (uint32_t b = blockIdx.x * ASM_BLOCK; b < P; b += gridDim.x * ASM_BLOCK) {
+    if (threadIdx.x == 0) s_nbig = 0;
+    __syncthreads();
+    const uint32_t i = b + threadIdx.x;
+    if (i < P && fits) {
+      const uint32_t o = a.ws.piece_off[i], e = a.ws.piece_off[i + 1];
+      const uint32_t s = a.ws.piece_start[i];
+      if (e - o <= ASM_SMALL) {
+        for (uint32_t j = 0; j < e - o; ++j) a.ids[o + j] = a.ws.tmp_ids[s + j];
+      } else {
+        s_big[atomicAdd(&s_nbig, 1u)] = i;
+      }
+    }
+    __syncthreads();
+    for (uint32_t k = 0; k < s_nbig; ++k) {
+      const uint32_t u = s_big[k];
+      const uint32_t o = a.ws.piece_off[u], e = a.ws.piece_off[u + 1];
+      const uint32_t s = a.ws.piece_start[u];
+      for (uint32_t j = threadIdx.x; j < e - o; j += ASM_BLOCK) a.ids[o + j] = a.ws.tmp_ids[s + j];
+    }
+    __syncthreads();
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) a.ws.status->n_ids = total;
 }
@@ -676,7 +787,7 @@ __global__ void __launch_bounds__(256) k_seg_offsets(EncodeArgs a) {
       if (a.ws.piece_start[mid] < o) lo = mid + 1;
       else hi = mid;
     }
-    a.id_off[s] = P ? int64_t(a.ws.piece_cnt[lo]) : 0;
+    a.id_off[s] = P ? int64_t(a.ws.piece_off[lo]) : 0;
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     const unsigned long long e = a.ws.status->err_pos;

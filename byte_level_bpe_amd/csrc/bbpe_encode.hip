@@ -20,8 +20,8 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 struct WsLayout {
   uint64_t status, tile_nchar, tile_lastchg, tile_charbase, tile_chgcarry, seg_local, seg_charstart,
-      ss, spst, spc, ps, tile_fn, tile_carry, tile_np, piece_start, piece_cnt, tmp_ids, scan_part,
-      long_list, mid_list, lrank, lpart, lalive, lmin, total;
+      ss, spst, spc, ps, tile_fn, tile_carry, tile_np, piece_start, piece_cnt, piece_off,
+      tmp_ids, scan_part, l16, l32, lw, ll, lrank, lpart, lalive, lmin, total;
   uint64_t n_words;
   uint32_t n_tiles;
 };
@@ -53,10 +53,14 @@ WsLayout layout_for(uint64_t n, uint32_t n_seg) {
   take(L.tile_np, 4 * (T + 1));
   take(L.piece_start, 4 * (n + 1));
   take(L.piece_cnt, 4 * (n + 1));
+  take(L.piece_off, 4 * (n + 1));
   take(L.tmp_ids, 4 * (n + 1));
   take(L.scan_part, 4 * ((n + 1) / 4096 + 2));
-  take(L.long_list, 4 * (n / 64 + 1));
-  take(L.mid_list, 4 * (n / 32 + 1));
+  // units to merge have at least 2 / 17 / 33 / 513 bytes
+  take(L.l16, 4 * (n / 2 + 1));
+  take(L.l32, 4 * (n / 17 + 1));
+  take(L.lw, 4 * (n / 33 + 1));
+  take(L.ll, 4 * (n / 513 + 1));
   take(L.lrank, 4 * (n + 1));
   take(L.lpart, 4 * (n + 1));
   take(L.lalive, n + 1);
@@ -71,8 +75,11 @@ __global__ void k_init(EncodeArgs a) {
     s->err_pos = ~0ull;
     s->n_pieces = 0;
     s->n_ids = 0;
-    s->n_long = 0;
-    s->n_mid = 0;
+    s->n_ll = 0;
+    s->n_lw = 0;
+    s->n_l32 = 0;
+    s->n_l16 = 0;
+    s->spare[0] = s->spare[1] = 0;
     s->n_chars = 0;
     s->err_seg = 0;
     // offsets must start at 0 and end at the text length (monotonicity is
@@ -209,10 +216,13 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
   a.ws.tile_np = reinterpret_cast<uint32_t *>(w + L.tile_np);
   a.ws.piece_start = reinterpret_cast<uint32_t *>(w + L.piece_start);
   a.ws.piece_cnt = reinterpret_cast<uint32_t *>(w + L.piece_cnt);
+  a.ws.piece_off = reinterpret_cast<uint32_t *>(w + L.piece_off);
   a.ws.tmp_ids = reinterpret_cast<int32_t *>(w + L.tmp_ids);
   a.ws.scan_part = reinterpret_cast<uint32_t *>(w + L.scan_part);
-  a.ws.long_list = reinterpret_cast<uint32_t *>(w + L.long_list);
-  a.ws.mid_list = reinterpret_cast<uint32_t *>(w + L.mid_list);
+  a.ws.l16 = reinterpret_cast<uint32_t *>(w + L.l16);
+  a.ws.l32 = reinterpret_cast<uint32_t *>(w + L.l32);
+  a.ws.lw = reinterpret_cast<uint32_t *>(w + L.lw);
+  a.ws.ll = reinterpret_cast<uint32_t *>(w + L.ll);
   a.ws.lrank = reinterpret_cast<int32_t *>(w + L.lrank);
   a.ws.lpart = reinterpret_cast<int32_t *>(w + L.lpart);
   a.ws.lalive = w + L.lalive;
@@ -306,12 +316,11 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
   if (n == 0) {
     go("k_zero_offsets", k_zero_offsets, dim3(seg_grid), dim3(256), a);
   } else {
-    const uint32_t merge_grid = uint32_t(std::min<uint64_t>((n + 63) / 64, 8192));
+    const uint32_t probe_grid = uint32_t(std::min<uint64_t>((n + 1023) / 1024, 16384));
+    go("k_probe", k_probe, dim3(probe_grid), dim3(256), a);
+    // persistent waves draining the merge queue
+    const uint32_t merge_grid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
     go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
-    const uint32_t mid_grid = uint32_t(std::min<uint64_t>(n / 32 + 1, 4096));
-    go("k_merge_mid", k_merge_mid, dim3(mid_grid), dim3(64), a);
-    const uint32_t long_grid = uint32_t(std::min<uint64_t>(n / 64 + 1, 2048));
-    go("k_merge_long", k_merge_long, dim3(long_grid), dim3(64), a);
     const uint32_t nscan = uint32_t((n + 1 + 4095) / 4096);
     go("k_scan_reduce", k_scan_reduce, dim3(nscan), dim3(256), a);
     go("k_scan_partials", k_scan_partials, dim3(1), dim3(1024), a);

@@ -92,11 +92,14 @@ struct Status {
   unsigned long long err_pos;     // first invalid UTF-8 byte (absolute), or ~0
   unsigned long long n_pieces;
   unsigned long long n_ids;
-  unsigned int n_long;            // units handed to the long tier
-  unsigned int n_mid;             // units handed to the mid tier
+  unsigned int n_ll;              // units to merge, longer than one wave holds
+  unsigned int n_lw;              // ... that one wave holds in registers
   unsigned long long n_chars;
   unsigned int err_seg;           // segment of err_pos
-  unsigned int pad2;
+  unsigned int pad2;              // nonzero: invalid segment offsets, every kernel exits
+  unsigned int n_l32;             // ... of 17-32 bytes
+  unsigned int n_l16;             // ... of 2-16 bytes
+  unsigned int spare[2];
 };
 
 }  // namespace bbpe

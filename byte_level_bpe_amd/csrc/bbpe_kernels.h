@@ -24,11 +24,11 @@ struct WsPtrs {
   uint32_t *tile_carry;             // [T] split state entering each tile
   uint32_t *tile_np;                // [T+1] pieces per tile, then their exclusive scan
   uint32_t *piece_start;            // [P+1]
-  uint32_t *piece_cnt;              // [P+1] ids per piece, then their exclusive scan
+  uint32_t *piece_cnt;              // [P] ids per unit
+  uint32_t *piece_off;              // [P+1] exclusive scan of the ids per unit
   int32_t *tmp_ids;                 // [N] ids of each piece, at the piece's byte offset
   uint32_t *scan_part;              // [N/4096+2] partial sums of the piece scan
-  uint32_t *long_list;              // [N/64+1] units for the long tier
-  uint32_t *mid_list;               // [N/32+1] units for the mid tier
+  uint32_t *l16, *l32, *lw, *ll;    // units to merge, by length
   int32_t *lrank;                   // [N] long tier: pair rank at each part start
   int32_t *lpart;                   // [N] long tier: rank of the part starting here
   uint8_t *lalive;                  // [N] long tier: 1 where a part starts
@@ -60,9 +60,8 @@ __global__ void k_scan_split(EncodeArgs a);
 __global__ void k_split(EncodeArgs a);
 __global__ void k_scan_tiles_np(EncodeArgs a);
 __global__ void k_pieces(EncodeArgs a);
+__global__ void k_probe(EncodeArgs a);
 __global__ void k_merge(EncodeArgs a);
-__global__ void k_merge_mid(EncodeArgs a);
-__global__ void k_merge_long(EncodeArgs a);
 __global__ void k_scan_reduce(EncodeArgs a);
 __global__ void k_scan_partials(EncodeArgs a);
 __global__ void k_scan_down(EncodeArgs a);
