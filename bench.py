@@ -29,6 +29,8 @@ WORKLOAD_DESC = {
     "tiny": "tiny: one 65,536-byte ASCII segment, 1,280-rank table, cl100k split",
     "agentic": "agentic: 300 typed segments, 4,000,000 characters, 100,256-rank table",
     "ragged": "ragged: 4,096 requests of 512-8,192 bytes, 100,256-rank table",
+    "large": "large: one 67,108,864-byte segment (50% Latin prose, 40% Devanagari/CJK, 10% digit/"
+             "punctuation runs), 200,000-rank table, o200k-style split, tiktoken-safe",
 }
 
 

@@ -48,7 +48,7 @@ WsLayout layout_for(uint64_t n, uint32_t n_seg) {
   take(L.spst, 8 * (W + 1));
   take(L.spc, 8 * (W + 1));
   take(L.ps, 8 * (W + 1));
-  take(L.tile_fn, 4 * (T + 1));
+  take(L.tile_fn, 8 * (T + 1));
   take(L.tile_carry, 4 * (T + 1));
   take(L.tile_np, 4 * (T + 1));
   take(L.piece_start, 4 * (n + 1));
@@ -186,7 +186,6 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
   if (n >= (uint64_t(1) << 32) - 64 || (flags & ~uint32_t(BBPE_TIKTOKEN_SAFE))) return BBPE_E_INVALID_ARG;
   if (n_seg == 0 && n != 0) return BBPE_E_INVALID_ARG;
   if (!t->d_image) return BBPE_E_STATE;
-  if (t->grammar != BBPE_GRAMMAR_CL100K) return BBPE_E_INVALID_ARG;  // o200k-style split: not built yet
   L = layout_for(n, n_seg);
   if (!d_ws || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(d_ws) & 255)) return BBPE_E_WORKSPACE;
   uint8_t *w = static_cast<uint8_t *>(d_ws);
@@ -211,7 +210,7 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
   a.ws.spst = reinterpret_cast<uint64_t *>(w + L.spst);
   a.ws.spc = reinterpret_cast<uint64_t *>(w + L.spc);
   a.ws.ps = reinterpret_cast<uint64_t *>(w + L.ps);
-  a.ws.tile_fn = reinterpret_cast<uint32_t *>(w + L.tile_fn);
+  a.ws.tile_fn = reinterpret_cast<uint64_t *>(w + L.tile_fn);
   a.ws.tile_carry = reinterpret_cast<uint32_t *>(w + L.tile_carry);
   a.ws.tile_np = reinterpret_cast<uint32_t *>(w + L.tile_np);
   a.ws.piece_start = reinterpret_cast<uint32_t *>(w + L.piece_start);
@@ -241,9 +240,15 @@ void launch_front(Launcher &go, const EncodeArgs &a, const WsLayout &L) {
   go("k_count", k_count, dim3(T), dim3(64), a);
   go("k_scan_chars", k_scan_chars, dim3(1), dim3(1024), a);
   go("k_spans", k_spans, dim3(T), dim3(64), a);
-  go("k_split_agg", k_split_agg, dim3(T), dim3(64), a);
-  go("k_scan_split", k_scan_split, dim3(1), dim3(1024), a);
-  go("k_split", k_split, dim3(T), dim3(64), a);
+  if (a.T.grammar == BBPE_GRAMMAR_O200K_STYLE) {
+    go("k_split_agg_o200k", k_split_agg_o200k, dim3(T), dim3(64), a);
+    go("k_scan_split_o200k", k_scan_split_o200k, dim3(1), dim3(1024), a);
+    go("k_split_o200k", k_split_o200k, dim3(T), dim3(64), a);
+  } else {
+    go("k_split_agg", k_split_agg, dim3(T), dim3(64), a);
+    go("k_scan_split", k_scan_split, dim3(1), dim3(1024), a);
+    go("k_split", k_split, dim3(T), dim3(64), a);
+  }
   go("k_scan_tiles_np", k_scan_tiles_np, dim3(1), dim3(1024), a);
   go("k_pieces", k_pieces, dim3(T), dim3(64), a);
 }

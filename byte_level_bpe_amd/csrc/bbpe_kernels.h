@@ -20,7 +20,7 @@ struct WsPtrs {
   unsigned long long *seg_charstart;  // [S+1]
   uint64_t *ss, *spst, *spc;        // [W] span start / special start / inside special
   uint64_t *ps;                     // [W] piece starts
-  uint32_t *tile_fn;                // [T] split transfer functions
+  uint64_t *tile_fn;                // [T] split transfer functions
   uint32_t *tile_carry;             // [T] split state entering each tile
   uint32_t *tile_np;                // [T+1] pieces per tile, then their exclusive scan
   uint32_t *piece_start;            // [P+1]
@@ -58,6 +58,9 @@ __global__ void k_spans(EncodeArgs a);
 __global__ void k_split_agg(EncodeArgs a);
 __global__ void k_scan_split(EncodeArgs a);
 __global__ void k_split(EncodeArgs a);
+__global__ void k_split_agg_o200k(EncodeArgs a);
+__global__ void k_scan_split_o200k(EncodeArgs a);
+__global__ void k_split_o200k(EncodeArgs a);
 __global__ void k_scan_tiles_np(EncodeArgs a);
 __global__ void k_pieces(EncodeArgs a);
 __global__ void k_probe(EncodeArgs a);

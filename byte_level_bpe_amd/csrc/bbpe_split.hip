@@ -1,22 +1,28 @@
-// Split of every span into pre-tokens (cl100k grammar), as piece-start bits.
+// Split of every span into pre-tokens, as piece-start bits, for the cl100k
+// grammar and the o200k-style grammar.
 //
-// The printed pattern is applied leftmost-first with possessive quantifiers
-// (tiktoken deep-dive page, "The split pattern").  Rather than running a
-// regex engine, each lane derives the match starts of its 64-byte word from
-// class bitmasks: whether a match starts at a character depends only on the
-// characters a few bytes around it, except for three quantities that are
-// carried along the text:
+// The printed patterns are applied leftmost-first with possessive
+// quantifiers (tiktoken deep-dive page, "The split pattern"; the o200k-style
+// letter clause from "r50k, cl100k, o200k").  Rather than running a regex
+// engine, each lane derives the match starts of its 64-byte word from class
+// bitmasks: whether a match starts at a character depends only on the
+// characters a few bytes around it, except for quantities carried along the
+// text:
 //   * the position of a digit inside its digit run, modulo 3 (digit groups of
-//     at most three);
-//   * whether a run of CR/LF characters at the start of a whitespace run was
-//     preceded by punctuation (the punctuation clause then swallows those
-//     CR/LF characters, and the whitespace clauses restart after them);
+//     at most three);                                            (both)
 //   * whether a run of non-CR/LF whitespace reaches a non-space character of
 //     the same span (the last CR/LF of a whitespace run ends a match only if
-//     the whitespace after it is followed by a non-space character).
-// The first two flow left to right, the third right to left.  Each lane
-// summarises its word as a transfer function on the carried state; functions
-// compose across lanes (wave scans) and across tiles (a one-workgroup scan).
+//     the whitespace after it is followed by a non-space character); (both)
+//   * cl100k: whether a run of CR/LF characters at the start of a whitespace
+//     run was preceded by punctuation (the punctuation clause then swallows
+//     those CR/LF characters, and the whitespace clauses restart after them);
+//   * o200k-style: the state of an eleven-state automaton over letters, marks and
+//     punctuation, which also covers the CR/LF run of the cl100k case (see
+//     "o200k-style letter automaton" below).
+// The digit phase and the automaton flow left to right, the whitespace
+// quantity right to left.  Each lane summarises its word as a transfer
+// function on the carried state; functions compose across lanes (wave scans)
+// and across tiles (a one-workgroup scan).
 #include <hip/hip_runtime.h>
 
 #include "bbpe_classify.h"
@@ -25,19 +31,28 @@
 
 namespace bbpe {
 
+// ---------------------------------------------------------------------------
 // Transfer-function encodings.
 //   digit phase: states 0,1,2 (index of the last digit in its run, mod 3) and
 //                3 (not in a digit run); 4 entries of 2 bits.
 //   CR run:      states 0 (none), 1 (CR/LF run that followed punctuation),
-//                2 (other CR/LF run); 3 entries of 2 bits.
+//                2 (other CR/LF run); 3 entries of 2 bits.      (cl100k)
+//   letter:      the o200k-style automaton, 11 entries of 4 bits.
 //   v (RTL):     state = "the non-CR/LF whitespace continuing here ends at a
 //                non-space character of the span"; 2 entries of 1 bit.
+// A word's or tile's functions are packed in 64 bits: digit in bits 0-7,
+// v in bits 8-9, CR run / letter from bit 16.
+// ---------------------------------------------------------------------------
 constexpr uint32_t FDIG_ID = 0xE4u;  // 3,2,1,0
 constexpr uint32_t FCR_ID = 0x24u;   // 2,1,0
 constexpr uint32_t FV_ID = 0x2u;     // 1,0
+constexpr uint32_t NLET = 11;
+constexpr uint64_t FLET_ID = 0xA9876543210ull;
+constexpr uint64_t FLET_ONES = 0x11111111111ull;
 
 __device__ __forceinline__ uint32_t fdig_apply(uint32_t f, uint32_t s) { return (f >> (2 * s)) & 3u; }
 __device__ __forceinline__ uint32_t fcr_apply(uint32_t f, uint32_t s) { return (f >> (2 * s)) & 3u; }
+__device__ __forceinline__ uint32_t flet_apply(uint64_t f, uint32_t s) { return uint32_t(f >> (4 * s)) & 15u; }
 __device__ __forceinline__ uint32_t fv_apply(uint32_t f, uint32_t s) { return (f >> s) & 1u; }
 // f first, then g
 __device__ __forceinline__ uint32_t fdig_then(uint32_t f, uint32_t g) {
@@ -52,28 +67,163 @@ __device__ __forceinline__ uint32_t fcr_then(uint32_t f, uint32_t g) {
   for (uint32_t s = 0; s < 3; ++s) h |= fcr_apply(g, fcr_apply(f, s)) << (2 * s);
   return h;
 }
+__device__ __forceinline__ uint64_t flet_then(uint64_t f, uint64_t g) {
+  uint64_t h = 0;
+#pragma unroll
+  for (uint32_t s = 0; s < NLET; ++s) h |= uint64_t(flet_apply(g, flet_apply(f, s))) << (4 * s);
+  return h;
+}
 __device__ __forceinline__ uint32_t fv_then(uint32_t f, uint32_t g) {
   uint32_t h = 0;
 #pragma unroll
   for (uint32_t s = 0; s < 2; ++s) h |= fv_apply(g, fv_apply(f, s)) << s;
   return h;
 }
-// packed: bits 0-7 digit, 8-13 CR, 16-17 v
-__device__ __forceinline__ uint32_t pack_fn(uint32_t d, uint32_t c, uint32_t v) {
-  return d | (c << 8) | (v << 16);
+
+// The left-to-right part of a packed function (digit + CR run or letter).
+template <int G>
+__device__ __forceinline__ uint64_t ltr_id() {
+  return uint64_t(FDIG_ID) | ((G == 0 ? uint64_t(FCR_ID) : FLET_ID) << 16);
+}
+template <int G>
+__device__ __forceinline__ uint64_t ltr_then(uint64_t f, uint64_t g) {
+  const uint64_t d = fdig_then(uint32_t(f & 0xFFu), uint32_t(g & 0xFFu));
+  const uint64_t x = G == 0 ? uint64_t(fcr_then(uint32_t(f >> 16) & 0x3Fu, uint32_t(g >> 16) & 0x3Fu))
+                            : flet_then(f >> 16, g >> 16);
+  return d | (x << 16);
+}
+template <int G>
+__device__ __forceinline__ uint32_t ltr_apply_x(uint64_t f, uint32_t s) {
+  return G == 0 ? fcr_apply(uint32_t(f >> 16) & 0x3Fu, s) : flet_apply(f >> 16, s);
 }
 
-struct SplitWord {
-  // carried-state inputs to the per-byte machines
-  uint64_t SS, SPST, IN, BRK, LD, N_, CR_, NC, WS_, pN, pO;
-  uint64_t static_starts;  // starts that need no carried state
-  uint32_t f_dig, f_cr, f_v;
+// ---------------------------------------------------------------------------
+// o200k-style letter automaton.  The letter clause is an optional prefix
+// character P (not CR/LF, letter or digit), then the longest run of U
+// characters (Lu Lt Lm Lo M), then the longest run of W characters (Ll Lm
+// Lo M), at least one character in all, then an optional contraction; the
+// other clauses are cl100k's.  Per character, in text order:
+//   F   a match starts at the next character        F1  inside a CR/LF run that
+//   F2  inside another CR/LF run                        followed punctuation
+//   PS  the last character (O or M) started a match and prefixes letters or
+//       starts a punctuation run
+//   PSP the last character is a space (prefixes letters or punctuation; a
+//       CR/LF after it is whitespace, not the punctuation clause's tail)
+//   PW  the last character is other whitespace (prefixes letters only)
+//   LU  inside the letters, no W-only (Ll) character yet
+//   LW  inside the letters after a W-only character
+//   Q   inside a punctuation run
+//   C1, C2  one / two characters of a contraction still to come
+// Character kinds: X (outside the span), CR, SP (U+0020), WS (other
+// whitespace), N, U (Lu Lt), W (Ll), B (Lm Lo), M, O (other), A1 / A2 (an
+// apostrophe followed by a one / two character contraction).  Whitespace and
+// digit starts are not decided here.
+// ---------------------------------------------------------------------------
+enum : uint32_t { S_F = 0, S_F1, S_F2, S_PS, S_PSP, S_PW, S_LU, S_LW, S_Q, S_C1, S_C2 };
+enum : uint32_t { K_X = 0, K_CR, K_SP, K_WS, K_N, K_U, K_W, K_B, K_M, K_O, K_A1, K_A2, K_COUNT };
+
+struct LetStep {
+  uint32_t next;
+  bool start;
 };
+constexpr bool in_set(uint32_t st, uint32_t a, uint32_t b = 99, uint32_t c = 99, uint32_t d = 99) {
+  return st == a || st == b || st == c || st == d;
+}
+constexpr LetStep let_step(uint32_t st, uint32_t k) {
+  if (k == K_X || k == K_N) return {S_F, false};
+  if (k == K_SP) return {S_PSP, false};
+  if (k == K_WS) return {S_PW, false};
+  if (k == K_CR) return {in_set(st, S_F1, S_F2) ? st : (in_set(st, S_Q, S_PS) ? S_F1 : S_F2), false};
+  if (st == S_C1) return {S_F, false};
+  if (st == S_C2) return {S_C1, false};
+  const bool pend = in_set(st, S_PS, S_PSP, S_PW);  // a prefix character waits
+  if (k == K_U) return {S_LU, !(pend || st == S_LU)};
+  if (k == K_W) return {S_LW, !(pend || in_set(st, S_LU, S_LW))};
+  if (k == K_B) {
+    if (in_set(st, S_LU, S_LW)) return {st, false};
+    return {S_LU, !pend};
+  }
+  if (k == K_M) {
+    if (in_set(st, S_LU, S_LW)) return {st, false};
+    if (pend) return {S_LU, false};
+    if (st == S_Q) return {S_Q, false};
+    return {S_PS, true};
+  }
+  if ((k == K_A1 || k == K_A2) && in_set(st, S_LU, S_LW)) return {k == K_A1 ? S_C1 : S_C2, false};
+  // punctuation
+  if (in_set(st, S_Q, S_PS, S_PSP)) return {S_Q, false};
+  return {S_PS, true};
+}
+constexpr uint64_t let_table(uint32_t k) {
+  uint64_t t = 0;
+  for (uint32_t s = 0; s < NLET; ++s) t |= uint64_t(let_step(s, k).next) << (4 * s);
+  return t;
+}
+constexpr uint32_t let_starts(uint32_t k) {
+  uint32_t m = 0;
+  for (uint32_t s = 0; s < NLET; ++s) m |= uint32_t(let_step(s, k).start) << s;
+  return m;
+}
+__device__ __forceinline__ void let_kind(uint32_t k, uint64_t &t, uint32_t &sm) {
+  switch (k) {
+#define BBPE_KIND(K) \
+  case K: t = let_table(K); sm = let_starts(K); break;
+    BBPE_KIND(K_CR) BBPE_KIND(K_SP) BBPE_KIND(K_WS) BBPE_KIND(K_N) BBPE_KIND(K_U) BBPE_KIND(K_W)
+    BBPE_KIND(K_B) BBPE_KIND(K_M) BBPE_KIND(K_O) BBPE_KIND(K_A1) BBPE_KIND(K_A2)
+#undef BBPE_KIND
+    default: t = let_table(K_X); sm = let_starts(K_X); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-word split state.
+// ---------------------------------------------------------------------------
+struct SplitWord {
+  uint64_t SS, SPST, IN, BRK, LD, N_, CR_, NC, WS_, pN, pO;
+  uint64_t K0, K1, K2, K3;   // o200k-style: character kind bit planes
+  uint64_t todo;             // o200k-style: bytes the automaton steps on
+  uint64_t WstCR;            // o200k-style: CR/LF that begins a whitespace run
+  uint64_t static_starts;    // starts that need no carried state
+  uint32_t f_dig, f_v, f_cr;
+  uint64_t f_let;
+};
+
+// Digit-phase and v transfer functions of the word (both grammars).
+__device__ __forceinline__ void digit_v_fns(const SplitWord &o, const uint64_t NLD_runstart,
+                                            uint32_t &fd, uint32_t &fv) {
+  const uint64_t runstart = NLD_runstart;
+  if (o.N_ == ~uint64_t(0) && runstart == 0) {
+    const uint32_t cnt = uint32_t(__popcll(o.LD)) % 3u;
+    fd = 0;
+#pragma unroll
+    for (uint32_t s = 0; s < 3; ++s) fd |= ((s + cnt) % 3u) << (2 * s);
+    fd |= ((cnt + 2u) % 3u) << 6;
+  } else {
+    uint32_t ph = 3;
+    for (int i = 0; i < 64; ++i) {
+      const uint64_t b = bit(i);
+      if (o.N_ & o.LD & b) ph = (runstart & b) ? 0u : (ph == 3u ? 0u : (ph + 1u) % 3u);
+      else if (!(o.N_ & b)) ph = 3;
+    }
+    fd = ph * 0x55u;  // constant function
+  }
+  const uint64_t prop = o.NC & ~o.BRK;
+  if (prop == ~uint64_t(0)) {
+    fv = FV_ID;
+  } else {
+    // v at byte 0 is fixed by the first non-propagating byte
+    const int i = __ffsll(static_cast<unsigned long long>(~prop)) - 1;
+    const uint64_t b = bit(i);
+    const uint32_t v = (o.BRK & b) ? 0u : ((o.WS_ & b) ? 0u : 1u);
+    fv = v * 3u;
+  }
+}
 
 // Everything of the split that does not depend on the carried states, plus
 // this word's transfer functions.  Must be called by all 64 lanes.
-__device__ __forceinline__ void split_word_g1(const EncodeArgs &a, int64_t w, const WordMasks &m,
-                                              SplitWord &o) {
+template <int G>
+__device__ __forceinline__ void split_word(const EncodeArgs &a, int64_t w, const WordMasks &m,
+                                           SplitWord &o) {
   const bool inrange = w >= 0 && w < int64_t(a.n_words);
   const uint64_t SS = inrange ? a.ws.ss[w] : 0;
   const uint64_t SPST = inrange ? a.ws.spst[w] : 0;
@@ -81,7 +231,7 @@ __device__ __forceinline__ void split_word_g1(const EncodeArgs &a, int64_t w, co
   const uint64_t IN = m.valid & ~SPC;
   const uint64_t BRK = SS | SPST | ~m.valid;
   const uint64_t L_ = m.L & IN, N_ = m.N & IN, WS_ = m.WS & IN, CR_ = m.CR & IN, SP_ = m.SP & IN;
-  const uint64_t O_ = IN & ~(m.L | m.N | m.WS);
+  const uint64_t O_ = IN & ~(m.L | m.N | m.WS);  // punctuation, marks included
   const uint64_t LD = m.lead & IN;
   const uint64_t CONT = m.valid & ~m.lead;
   const uint64_t INB = IN & ~BRK;
@@ -102,39 +252,21 @@ __device__ __forceinline__ void split_word_g1(const EncodeArgs &a, int64_t w, co
   const uint64_t pWS = shl(WS_, WSq, 1) & ~SS, pCR = shl(CR_, CRq, 1) & ~SS;
   const uint64_t pSP = shl(SP_, SPq, 1) & ~SS, pO = shl(O_, Oq, 1) & ~SS;
 
-  // punctuation (any non-letter, non-digit, non-space character): a match
-  // starts at the first character of a punctuation run unless a single
-  // space before it joins the run
-  const uint64_t OST = O_ & LD & ~pO & ~pSP;
-  // an apostrophe that starts a match and is followed, inside the span, by
-  // s d m t (either case, or U+017F) or ll / ve / re: the contraction clause
-  const uint64_t APc = m.AP & OST;
+  // contractions after an apostrophe, inside the span: s d m t (either case,
+  // or U+017F) one character on, or ll / ve / re
   const uint64_t nb1 = shr(INB, INBn, 1), nb2 = shr(INB, INBn, 2);
   const uint64_t s1 = shr(m.c_sdmt, sdmtn, 1);
-  const uint64_t C2M = APc & s1 & nb1;  // the match ends two bytes on
   const uint64_t ls = shr(m.c_ls0, ls0n, 1) & shr(m.c_ls1, ls1n, 2);
   const uint64_t two = (shr(m.c_l, ln, 1) & shr(m.c_l, ln, 2)) | (shr(m.c_v, vn, 1) & shr(m.c_e, en, 2)) |
                        (shr(m.c_r, rn, 1) & shr(m.c_e, en, 2));
-  const uint64_t C3M = APc & nb1 & nb2 & (ls | (two & ~s1));  // three bytes on
 
-  const uint64_t OSTq = shfl_up64(OST, 1), C2q = shfl_up64(C2M, 1), C3q = shfl_up64(C3M, 1);
-  const uint64_t R = shl(C2M, C2q, 2) | shl(C3M, C3q, 3);
-  const uint64_t k1 = shl(CONT, CONTq, 1), k2 = shl(CONT, CONTq, 2), k3 = shl(CONT, CONTq, 3);
-  // OST at the first byte of the character that ends at byte i-1
-  const uint64_t PLOST = shl(OST, OSTq, 1) | (shl(OST, OSTq, 2) & k1) | (shl(OST, OSTq, 3) & k1 & k2) |
-                         (shl(OST, OSTq, 4) & k1 & k2 & k3);
-  // letters: a match starts at a letter after CR/LF or a digit, after
-  // punctuation unless that punctuation is one character that starts a match
-  // (it then prefixes the letters), and inside a letter run only where a
-  // contraction ended
-  const uint64_t startL = L_ & LD & (SS | pCR | pN | (pO & ~PLOST) | (pL & R));
-
-  // whitespace: a run starts a match where it begins, unless punctuation
-  // before it swallowed its leading CR/LF characters (handled by the CR
-  // machine); the last non-CR/LF character of a run starts a match when a
-  // non-space character of the span follows; the first character after the
-  // run's last CR/LF starts one when the rest of the run is followed by a
-  // non-space character (the v machine)
+  // whitespace: a run starts a match where it begins (cl100k: unless
+  // punctuation before it swallowed its leading CR/LF characters, handled by
+  // the CR machine; o200k-style: by the automaton); the last non-CR/LF
+  // character of a run starts a match when a non-space character of the
+  // span follows; the first character after the run's last CR/LF starts one
+  // when the rest of the run is followed by a non-space character (the v
+  // machine)
   const uint64_t Wst = WS_ & LD & ~pWS;
   const uint64_t NC = WS_ & ~CR_;
   const uint64_t n1 = shr(GL, GLn, 1), kn1 = shr(CONT, CONTn, 1), kn2 = shr(CONT, CONTn, 2);
@@ -142,7 +274,6 @@ __device__ __forceinline__ void split_word_g1(const EncodeArgs &a, int64_t w, co
   const uint64_t nextGL = n1 | (shr(GL, GLn, 2) & kn1) | (shr(GL, GLn, 3) & kn1 & kn2) |
                           (shr(GL, GLn, 4) & kn1 & kn2 & kn3);
   const uint64_t WL = NC & LD & nextGL;
-  const uint64_t startW_static = (Wst & ~pO) | (Wst & pO & ~CR_) | WL;
 
   o.SS = SS;
   o.SPST = SPST;
@@ -155,31 +286,54 @@ __device__ __forceinline__ void split_word_g1(const EncodeArgs &a, int64_t w, co
   o.WS_ = WS_;
   o.pN = pN;
   o.pO = pO;
-  o.static_starts = startL | OST | startW_static | SPST;
+
+  if (G == 0) {
+    // punctuation (any non-letter, non-digit, non-space character): a match
+    // starts at the first character of a punctuation run unless a single
+    // space before it joins the run
+    const uint64_t OST = O_ & LD & ~pO & ~pSP;
+    // an apostrophe that starts a match and is followed by a contraction:
+    // the contraction clause
+    const uint64_t APc = m.AP & OST;
+    const uint64_t C2M = APc & s1 & nb1;  // the match ends two bytes on
+    const uint64_t C3M = APc & nb1 & nb2 & (ls | (two & ~s1));  // three bytes on
+    const uint64_t OSTq = shfl_up64(OST, 1), C2q = shfl_up64(C2M, 1), C3q = shfl_up64(C3M, 1);
+    const uint64_t R = shl(C2M, C2q, 2) | shl(C3M, C3q, 3);
+    const uint64_t k1 = shl(CONT, CONTq, 1), k2 = shl(CONT, CONTq, 2), k3 = shl(CONT, CONTq, 3);
+    // OST at the first byte of the character that ends at byte i-1
+    const uint64_t PLOST = shl(OST, OSTq, 1) | (shl(OST, OSTq, 2) & k1) | (shl(OST, OSTq, 3) & k1 & k2) |
+                           (shl(OST, OSTq, 4) & k1 & k2 & k3);
+    // letters: a match starts at a letter after CR/LF or a digit, after
+    // punctuation unless that punctuation is one character that starts a
+    // match (it then prefixes the letters), and inside a letter run only
+    // where a contraction ended
+    const uint64_t startL = L_ & LD & (SS | pCR | pN | (pO & ~PLOST) | (pL & R));
+    const uint64_t startW_static = (Wst & ~pO) | (Wst & pO & ~CR_) | WL;
+    o.static_starts = startL | OST | startW_static | SPST;
+    o.K0 = o.K1 = o.K2 = o.K3 = o.todo = o.WstCR = 0;
+  } else {
+    const uint64_t APL = m.AP & LD;
+    const uint64_t A1 = APL & ((s1 & nb1) | (ls & nb1 & nb2));
+    const uint64_t A2 = APL & nb1 & nb2 & two & ~A1;
+    const uint64_t SPm = SP_, WSm = NC & ~SP_;
+    const uint64_t Um = m.LU & IN, Wm = m.LL & IN, Bm = m.LB & IN, Mm = m.M & IN;
+    const uint64_t Om = O_ & ~Mm & ~A1 & ~A2;
+    // kind codes: X0 CR1 SP2 WS3 N4 U5 W6 B7 M8 O9 A1=10 A2=11
+    o.K0 = CR_ | WSm | Um | Bm | Om | A2;
+    o.K1 = SPm | WSm | Wm | Bm | A1 | A2;
+    o.K2 = N_ | Um | Wm | Bm;
+    o.K3 = Mm | Om | A1 | A2;
+    o.todo = m.lead & m.valid;  // special bytes are kind X
+    o.WstCR = Wst & CR_;
+    o.static_starts = (Wst & ~CR_) | WL | SPST;
+  }
 
   // transfer functions
-  // digits: identity-like (shift by count) only when the whole word continues a digit run
-  {
-    const uint64_t runstart = N_ & LD & (SS | ~pN);
-    uint32_t fd;
-    if (N_ == ~uint64_t(0) && runstart == 0) {
-      const uint32_t cnt = uint32_t(__popcll(LD)) % 3u;
-      fd = 0;
-#pragma unroll
-      for (uint32_t s = 0; s < 3; ++s) fd |= ((s + cnt) % 3u) << (2 * s);
-      fd |= ((cnt + 2u) % 3u) << 6;
-    } else {
-      uint32_t ph = 3;
-      for (int i = 0; i < 64; ++i) {
-        const uint64_t b = bit(i);
-        if (N_ & LD & b) ph = (runstart & b) ? 0u : (ph == 3u ? 0u : (ph + 1u) % 3u);
-        else if (!(N_ & b)) ph = 3;
-      }
-      fd = ph * 0x55u;  // constant function
-    }
-    o.f_dig = fd;
-  }
-  {
+  uint32_t fd, fv;
+  digit_v_fns(o, N_ & LD & (SS | ~pN), fd, fv);
+  o.f_dig = fd;
+  o.f_v = fv;
+  if (G == 0) {
     uint32_t fc;
     if ((CR_ & ~SS) == ~uint64_t(0)) {
       fc = ((pO & 1) ? 1u : 2u) | (1u << 2) | (2u << 4);
@@ -194,28 +348,54 @@ __device__ __forceinline__ void split_word_g1(const EncodeArgs &a, int64_t w, co
       fc = st * 0x15u;
     }
     o.f_cr = fc;
-  }
-  {
-    const uint64_t prop = NC & ~BRK;
-    uint32_t fv;
-    if (prop == ~uint64_t(0)) {
-      fv = FV_ID;
-    } else {
-      // v at byte 0 is fixed by the first non-propagating byte
-      const int i = __ffsll(static_cast<unsigned long long>(~prop)) - 1;
-      const uint64_t b = bit(i);
-      const uint32_t v = (BRK & b) ? 0u : ((WS_ & b) ? 0u : 1u);
-      fv = v * 3u;
+    o.f_let = 0;
+  } else {
+    // the automaton over the word from every entry state; once all entry
+    // states agree (after a space, a digit, a span start, ...) one state is
+    // enough
+    uint64_t f = FLET_ID;
+    bool konst = false;
+    uint32_t cst = 0;
+    for (int i = 0; i < 64; ++i) {
+      if (!((o.todo >> i) & 1)) continue;
+      const uint32_t k = uint32_t((o.K0 >> i) & 1) | (uint32_t((o.K1 >> i) & 1) << 1) |
+                         (uint32_t((o.K2 >> i) & 1) << 2) | (uint32_t((o.K3 >> i) & 1) << 3);
+      uint64_t t;
+      uint32_t sm;
+      let_kind(k, t, sm);
+      if ((SS >> i) & 1) {
+        konst = true;
+        cst = S_F;
+      }
+      if (konst) {
+        cst = flet_apply(t, cst);
+      } else {
+        f = flet_then(f, t);
+        if ((f & 15u) * FLET_ONES == f) {
+          konst = true;
+          cst = uint32_t(f & 15u);
+        }
+      }
     }
-    o.f_v = fv;
+    o.f_let = konst ? uint64_t(cst) * FLET_ONES : f;
+    o.f_cr = 0;
   }
 }
 
-// Per-byte machines with known inputs: digit-group starts, the whitespace
-// restart after swallowed CR/LF, and the v bits (VN bit i = v at byte i+1).
-__device__ __forceinline__ uint64_t split_finish_g1(const SplitWord &o, uint64_t pCRmask, uint32_t ph,
-                                                    uint32_t st, uint32_t v) {
-  uint64_t PH0 = 0, E2b = 0, VN = 0;
+template <int G>
+__device__ __forceinline__ uint64_t pack_word_fn(const SplitWord &o) {
+  const uint64_t x = G == 0 ? uint64_t(o.f_cr) : o.f_let;
+  return uint64_t(o.f_dig) | (uint64_t(o.f_v) << 8) | (x << 16);
+}
+
+// Per-byte machines with known inputs: digit-group starts, the v bits (VN
+// bit i = v at byte i+1), and the CR machine (cl100k) or the letter
+// automaton (o200k-style).  xs = CR state or automaton state entering the
+// word.
+template <int G>
+__device__ __forceinline__ uint64_t split_finish(const SplitWord &o, uint64_t pCRmask, uint32_t ph,
+                                                 uint32_t xs, uint32_t v) {
+  uint64_t PH0 = 0, E2b = 0, VN = 0, extra = 0;
   const uint64_t NLD = o.N_ & o.LD;
   const uint64_t runstart = NLD & (o.SS | ~o.pN);
   if (o.N_) {
@@ -229,18 +409,40 @@ __device__ __forceinline__ uint64_t split_finish_g1(const SplitWord &o, uint64_t
       }
     }
   }
-  if (o.CR_ | (st != 0)) {
-    for (int i = 0; i < 64; ++i) {
-      const uint64_t b = bit(i);
-      if (!(o.IN & b)) {
-        st = 0;
-      } else if (o.CR_ & b) {
-        st = (o.SS & b) ? 2u : (st == 0 ? ((o.pO & b) ? 1u : 2u) : st);
-      } else {
-        if (st == 1 && (o.NC & o.LD & b) && !(o.SS & b)) E2b |= b;
-        st = 0;
+  if (G == 0) {
+    uint32_t st = xs;
+    if (o.CR_ | (st != 0)) {
+      for (int i = 0; i < 64; ++i) {
+        const uint64_t b = bit(i);
+        if (!(o.IN & b)) {
+          st = 0;
+        } else if (o.CR_ & b) {
+          st = (o.SS & b) ? 2u : (st == 0 ? ((o.pO & b) ? 1u : 2u) : st);
+        } else {
+          if (st == 1 && (o.NC & o.LD & b) && !(o.SS & b)) E2b |= b;
+          st = 0;
+        }
       }
     }
+  } else {
+    uint32_t st = xs;
+    uint64_t LS = 0, PQ = 0, F1m = 0;
+    for (int i = 0; i < 64; ++i) {
+      if (!((o.todo >> i) & 1)) continue;
+      const uint64_t b = bit(i);
+      if (o.SS & b) st = S_F;
+      const uint32_t k = uint32_t((o.K0 >> i) & 1) | (uint32_t((o.K1 >> i) & 1) << 1) |
+                         (uint32_t((o.K2 >> i) & 1) << 2) | (uint32_t((o.K3 >> i) & 1) << 3);
+      uint64_t t;
+      uint32_t sm;
+      let_kind(k, t, sm);
+      PQ |= (st == S_Q || st == S_PS) ? b : 0;
+      F1m |= (st == S_F1) ? b : 0;
+      LS |= ((sm >> st) & 1) ? b : 0;
+      st = flet_apply(t, st);
+    }
+    E2b = o.NC & o.LD & ~o.SS & F1m;
+    extra = LS | (o.WstCR & ~PQ);
   }
   const uint64_t Qcand = o.NC & o.LD & pCRmask;
   if (Qcand) {
@@ -253,7 +455,7 @@ __device__ __forceinline__ uint64_t split_finish_g1(const SplitWord &o, uint64_t
     }
   }
   const uint64_t startN = NLD & (o.SS | ~o.pN | PH0);
-  return o.static_starts | startN | E2b | (Qcand & VN);
+  return o.static_starts | startN | E2b | extra | (Qcand & VN);
 }
 
 __device__ __forceinline__ void lane_setup(const EncodeArgs &a, int lane, uint32_t t, int64_t &w,
@@ -273,8 +475,22 @@ __device__ __forceinline__ uint64_t prev_cr(const SplitWord &o) {
   return shl(o.CR_, q, 1) & ~o.SS;
 }
 
+// Wave scans of the lanes' packed functions: LTR parts inclusive in lane
+// order, the v part inclusive in reverse lane order.
+template <int G>
+__device__ __forceinline__ void wave_scan_fns(uint64_t &ltr, uint32_t &fv, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t pl = __shfl_up(static_cast<unsigned long long>(ltr), d, 64);
+    const uint32_t nv = __shfl_down(fv, d, 64);
+    if (lane >= d) ltr = ltr_then<G>(pl, ltr);
+    if (lane + d < 64) fv = fv_then(nv, fv);
+  }
+}
+
 // Step 4: per-tile transfer functions.
-__global__ void __launch_bounds__(64) k_split_agg(EncodeArgs a) {
+template <int G>
+__device__ __forceinline__ void split_agg_body(const EncodeArgs &a) {
   if (a.ws.status->pad2) return;
   const int lane = threadIdx.x;
   const uint32_t t = blockIdx.x;
@@ -283,73 +499,68 @@ __global__ void __launch_bounds__(64) k_split_agg(EncodeArgs a) {
   Window win;
   lane_setup(a, lane, t, w, m, win);
   SplitWord o;
-  split_word_g1(a, w, m, o);
+  split_word<G>(a, w, m, o);
   const bool owned = lane >= 1 && lane <= int(TILE_WORDS);
-  uint32_t fd = owned ? o.f_dig : FDIG_ID, fc = owned ? o.f_cr : FCR_ID, fv = owned ? o.f_v : FV_ID;
-  // left-to-right composition (lane order) and right-to-left for v
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t pd = __shfl_up(fd, d, 64), pc = __shfl_up(fc, d, 64);
-    const uint32_t nv = __shfl_down(fv, d, 64);
-    if (lane >= d) {
-      fd = fdig_then(pd, fd);
-      fc = fcr_then(pc, fc);
-    }
-    if (lane + d < 64) fv = fv_then(nv, fv);
-  }
+  const uint64_t pk = pack_word_fn<G>(o);
+  uint64_t ltr = owned ? (pk & ~uint64_t(0x300)) : ltr_id<G>();
+  uint32_t fv = owned ? o.f_v : FV_ID;
+  wave_scan_fns<G>(ltr, fv, lane);
   const uint32_t fv0 = __shfl(fv, 0, 64);
-  if (lane == 63) a.ws.tile_fn[t] = pack_fn(fd, fc, fv0);
+  if (lane == 63) a.ws.tile_fn[t] = ltr | (uint64_t(fv0) << 8);
 }
+__global__ void __launch_bounds__(64) k_split_agg(EncodeArgs a) { split_agg_body<0>(a); }
+__global__ void __launch_bounds__(64) k_split_agg_o200k(EncodeArgs a) { split_agg_body<1>(a); }
 
 // Step 5 (one workgroup): the carried state entering every tile.
-__global__ void __launch_bounds__(1024) k_scan_split(EncodeArgs a) {
+template <int G>
+__device__ __forceinline__ void scan_split_body(const EncodeArgs &a) {
   if (a.ws.status->pad2) return;
-  __shared__ uint32_t s_f[1024];
+  __shared__ uint64_t s_f[1024];
   __shared__ uint32_t s_g[1024];
   const uint32_t T = a.n_tiles;
   const uint32_t tid = threadIdx.x;
   const uint32_t per = (T + 1023) / 1024;
   const uint32_t t0 = tid * per, t1 = min(T, t0 + per);
-  uint32_t fd = FDIG_ID, fc = FCR_ID, gv = FV_ID;
-  for (uint32_t t = t0; t < t1; ++t) {
-    const uint32_t f = a.ws.tile_fn[t];
-    fd = fdig_then(fd, f & 0xFFu);
-    fc = fcr_then(fc, (f >> 8) & 0x3Fu);
-  }
-  for (uint32_t t = t1; t > t0; --t) gv = fv_then(gv, (a.ws.tile_fn[t - 1] >> 16) & 3u);
-  s_f[tid] = fd | (fc << 8);
+  uint64_t f = ltr_id<G>();
+  uint32_t gv = FV_ID;
+  for (uint32_t t = t0; t < t1; ++t) f = ltr_then<G>(f, a.ws.tile_fn[t] & ~uint64_t(0x300));
+  for (uint32_t t = t1; t > t0; --t) gv = fv_then(gv, uint32_t(a.ws.tile_fn[t - 1] >> 8) & 3u);
+  s_f[tid] = f;
   s_g[tid] = gv;
   __syncthreads();
-  // exclusive scans over threads: LTR for (digit, CR), RTL for v
+  // exclusive scans over threads: LTR for (digit, CR / letter), RTL for v
   for (uint32_t d = 1; d < 1024; d <<= 1) {
-    const uint32_t lf = tid >= d ? s_f[tid - d] : (FDIG_ID | (FCR_ID << 8));
+    const uint64_t lf = tid >= d ? s_f[tid - d] : ltr_id<G>();
     const uint32_t rg = tid + d < 1024 ? s_g[tid + d] : FV_ID;
     __syncthreads();
-    const uint32_t cur = s_f[tid];
-    s_f[tid] = fdig_then(lf & 0xFFu, cur & 0xFFu) | (fcr_then((lf >> 8) & 0x3Fu, (cur >> 8) & 0x3Fu) << 8);
+    s_f[tid] = ltr_then<G>(lf, s_f[tid]);
     s_g[tid] = fv_then(rg, s_g[tid]);
     __syncthreads();
   }
-  const uint32_t ex_f = tid > 0 ? s_f[tid - 1] : (FDIG_ID | (FCR_ID << 8));
+  const uint64_t ex_f = tid > 0 ? s_f[tid - 1] : ltr_id<G>();
   const uint32_t ex_g = tid + 1 < 1024 ? s_g[tid + 1] : FV_ID;
-  uint32_t dig = fdig_apply(ex_f & 0xFFu, 3u);  // text starts outside any digit run
-  uint32_t cr = fcr_apply((ex_f >> 8) & 0x3Fu, 0u);
+  // the text starts outside any digit run, with no CR run / in state F
+  uint32_t dig = fdig_apply(uint32_t(ex_f & 0xFFu), 3u);
+  uint32_t x = ltr_apply_x<G>(ex_f, 0u);
   for (uint32_t t = t0; t < t1; ++t) {
-    a.ws.tile_carry[t] = (a.ws.tile_carry[t] & ~0xFFFFu) | dig | (cr << 8);
-    const uint32_t f = a.ws.tile_fn[t];
-    dig = fdig_apply(f & 0xFFu, dig);
-    cr = fcr_apply((f >> 8) & 0x3Fu, cr);
+    a.ws.tile_carry[t] = (a.ws.tile_carry[t] & ~0xFFFFu) | dig | (x << 8);
+    const uint64_t fn = a.ws.tile_fn[t];
+    dig = fdig_apply(uint32_t(fn & 0xFFu), dig);
+    x = ltr_apply_x<G>(fn, x);
   }
   __syncthreads();
   uint32_t v = fv_apply(ex_g, 0u);  // past the end of the text: a break
   for (uint32_t t = t1; t > t0; --t) {
     a.ws.tile_carry[t - 1] = (a.ws.tile_carry[t - 1] & 0xFFFFu) | (v << 16);
-    v = fv_apply((a.ws.tile_fn[t - 1] >> 16) & 3u, v);
+    v = fv_apply(uint32_t(a.ws.tile_fn[t - 1] >> 8) & 3u, v);
   }
 }
+__global__ void __launch_bounds__(1024) k_scan_split(EncodeArgs a) { scan_split_body<0>(a); }
+__global__ void __launch_bounds__(1024) k_scan_split_o200k(EncodeArgs a) { scan_split_body<1>(a); }
 
 // Step 6: piece-start bits of every word and the number of pieces per tile.
-__global__ void __launch_bounds__(64) k_split(EncodeArgs a) {
+template <int G>
+__device__ __forceinline__ void split_body(const EncodeArgs &a) {
   if (a.ws.status->pad2) return;
   const int lane = threadIdx.x;
   const uint32_t t = blockIdx.x;
@@ -358,31 +569,24 @@ __global__ void __launch_bounds__(64) k_split(EncodeArgs a) {
   Window win;
   lane_setup(a, lane, t, w, m, win);
   SplitWord o;
-  split_word_g1(a, w, m, o);
+  split_word<G>(a, w, m, o);
   const bool owned = lane >= 1 && lane <= int(TILE_WORDS) && w < int64_t(a.n_words);
-  uint32_t fd = (lane >= 1 && lane <= int(TILE_WORDS)) ? o.f_dig : FDIG_ID;
-  uint32_t fc = (lane >= 1 && lane <= int(TILE_WORDS)) ? o.f_cr : FCR_ID;
-  uint32_t fv = (lane >= 1 && lane <= int(TILE_WORDS)) ? o.f_v : FV_ID;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t pd = __shfl_up(fd, d, 64), pc = __shfl_up(fc, d, 64);
-    const uint32_t nv = __shfl_down(fv, d, 64);
-    if (lane >= d) {
-      fd = fdig_then(pd, fd);
-      fc = fcr_then(pc, fc);
-    }
-    if (lane + d < 64) fv = fv_then(nv, fv);
-  }
+  const bool mine = lane >= 1 && lane <= int(TILE_WORDS);
+  const uint64_t pk = pack_word_fn<G>(o);
+  uint64_t ltr = mine ? (pk & ~uint64_t(0x300)) : ltr_id<G>();
+  uint32_t fv = mine ? o.f_v : FV_ID;
+  wave_scan_fns<G>(ltr, fv, lane);
   // exclusive: state entering this lane's word
-  uint32_t exd = __shfl_up(fd, 1, 64), exc = __shfl_up(fc, 1, 64), exv = __shfl_down(fv, 1, 64);
-  if (lane == 0) { exd = FDIG_ID; exc = FCR_ID; }
+  uint64_t exl = __shfl_up(static_cast<unsigned long long>(ltr), 1, 64);
+  uint32_t exv = __shfl_down(fv, 1, 64);
+  if (lane == 0) exl = ltr_id<G>();
   if (lane == 63) exv = FV_ID;
   const uint32_t carry = a.ws.tile_carry[t];
-  const uint32_t ph = fdig_apply(exd, carry & 0xFFu);
-  const uint32_t st = fcr_apply(exc, (carry >> 8) & 0xFFu);
+  const uint32_t ph = fdig_apply(uint32_t(exl & 0xFFu), carry & 0xFFu);
+  const uint32_t xs = ltr_apply_x<G>(exl, (carry >> 8) & 0xFFu);
   const uint32_t v = fv_apply(exv, (carry >> 16) & 1u);
   const uint64_t pCRm = prev_cr(o);
-  uint64_t ps = split_finish_g1(o, pCRm, ph, st, v) & m.valid;
+  uint64_t ps = split_finish<G>(o, pCRm, ph, xs, v) & m.valid;
   if (a.merge_units) {
     // Merge units: a byte pair that occurs inside no key can never be merged
     // across (the merged part would be a key containing it), so the piece is
@@ -406,5 +610,7 @@ __global__ void __launch_bounds__(64) k_split(EncodeArgs a) {
   const uint32_t tot = wave_sum(np);
   if (lane == 0) a.ws.tile_np[t] = tot;
 }
+__global__ void __launch_bounds__(64) k_split(EncodeArgs a) { split_body<0>(a); }
+__global__ void __launch_bounds__(64) k_split_o200k(EncodeArgs a) { split_body<1>(a); }
 
 }  // namespace bbpe

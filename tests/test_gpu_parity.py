@@ -74,9 +74,10 @@ def make(tokens, specials=(), grammar=0):
     return B.load_ranks(tokens, specials, grammar), Oracle(tokens, specials, grammar)
 
 
-@pytest.fixture(scope="module")
-def atoms():
-    return make(atoms_permuted(1), SPECIALS, 0)
+@pytest.fixture(scope="module", params=[0, 1], ids=["cl100k", "o200k"])
+def atoms(request):
+    """Atoms-only table (ids = per-byte ranks) under each split grammar."""
+    return make(atoms_permuted(1), SPECIALS, request.param)
 
 
 @pytest.fixture(scope="module")
@@ -203,6 +204,35 @@ def test_encode_fuzz_tiny_table(tiny):
     assert_ids(tok, orc, segs, what="tiny fuzz")
     text = b" ".join(_fuzz(7, 3000, 200, alpha))
     assert_ids(tok, orc, [(text, False)], what="tiny fuzz long")
+
+
+@pytest.fixture(scope="module")
+def large_table():
+    from synth import configs
+    w = configs.large()
+    return w, make(w.tokens, w.specials, w.grammar)
+
+
+def test_encode_slices_large_table(large_table):
+    """o200k-style split and merge with the 200,000-rank table on slices of the
+    large workload's text (Latin, Devanagari, CJK, digit runs), cut at
+    character boundaries."""
+    w, (tok, orc) = large_table
+    text = w.segments[0][0]
+    r = random.Random(9)
+    segs = []
+    for _ in range(40):
+        a = r.randrange(0, len(text) - 70000)
+        n = r.randint(1, 60000)
+        seg = text[a:a + n]
+        while seg and (seg[0] & 0xC0) == 0x80:
+            seg = seg[1:]
+        while seg and (seg[-1] & 0x80):
+            seg = seg[:-1]
+        segs.append((seg, False))
+    say("large-table slices: %d bytes" % sum(len(s) for s, _ in segs))
+    assert_pieces(tok, orc, segs, what="large slices")
+    assert_ids(tok, orc, segs, what="large slices")
 
 
 def test_long_pieces_tiny_table(tiny):

@@ -24,7 +24,7 @@ def need_gpu():
         pytest.skip("no GPU")
 
 
-@pytest.mark.parametrize("name", ["tiny", "main", "agentic", "ragged"])
+@pytest.mark.parametrize("name", ["tiny", "main", "agentic", "ragged", "large"])
 def test_workload_parity(name):
     w = configs.ALL[name]()
     tok = B.load_ranks(w.tokens, w.specials, w.grammar)
@@ -46,6 +46,3 @@ def test_workload_parity(name):
     assert tok.decode(ids) == text
     assert len(ids) <= len(text)
 
-
-def test_large_workload_parity():
-    pytest.skip("the o200k-style split is not yet implemented in the HIP path")
