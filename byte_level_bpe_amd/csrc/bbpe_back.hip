@@ -13,7 +13,8 @@
 //     registers with static indexing;
 //   wave (<= 512 bytes): one wave per unit, eight positions per lane in
 //     registers, argmin by a wave reduction;
-//   long: one wave per unit, state in global memory.
+//   long: one wave per unit, state in global memory, pairs of the least rank
+//     merged in batches.
 #include <hip/hip_runtime.h>
 
 #include "bbpe_device.h"
@@ -484,37 +485,89 @@ __device__ void merge_wave(const EncodeArgs &a, uint32_t i, int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// Long tier: one wave per unit longer than WAVE_MAX.  Arrays indexed by text
-// byte position (units never overlap): lrank = pair rank at a part start,
-// lpart = id of the part starting there, lalive = 1 where a part starts;
-// per-64-byte-block minima of (rank << 32 | offset) in lmin, at index
-// s/32 + block (a unit of m > 64 bytes needs ceil(m/64) <= floor(m/32)
-// entries, so units never share one).  Lane 0 applies each merge;
-// device-scope fences make its stores visible to the other lanes.
+// Long tier: one wave per unit longer than WAVE_MAX, state in global memory.
+// Per position j of the unit (text byte s + j): lrank = rank of the pair that
+// starts with the part starting at j, lpart = id of that part.  Per 64-position
+// block b of the unit, at index (s >> 5) + b (a unit of m > 64 bytes needs
+// ceil(m/64) <= floor(m/32) entries, so units never share one): lbits = part
+// starts, lsel = pairs chosen this round, lmin = least pair rank, ldirty =
+// lmin stale.
+//
+// Each round takes the least rank R and merges in one batch the leftmost
+// non-overlapping pairs of rank R: in every run of consecutive parts whose
+// pairs all rank R, the 1st, 3rd, 5th ... pair.  Taken one at a time in text
+// order these are exactly the merges the one-at-a-time loop makes, as long as
+// every pair it creates on the way ranks above R; so the two pairs each merge
+// creates are looked up in the state the one-at-a-time loop has at that merge
+// (the part before it already merged if it was chosen, the part after it not
+// yet), and the batch stops after the first merge that creates a pair of rank
+// <= R.  The leftmost pair of rank R is always chosen, so every round merges.
+// Runs of one repeated character (tens of thousands of spaces) take a few
+// rounds per doubling of the part length instead of one round per merge.
+// Lanes own blocks; device-scope fences order the phases of a round.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
+struct LongUnit {
+  const EncodeArgs &a;
+  uint32_t s, m, nb;
+  unsigned long long *bits, *sel;
+  int32_t *mn;
+  uint32_t *dirty;
+  __device__ __forceinline__ int32_t &rank(uint32_t j) const { return a.ws.lrank[s + j]; }
+  __device__ __forceinline__ int32_t &part(uint32_t j) const { return a.ws.lpart[s + j]; }
+  // first part start >= x, or m
+  __device__ __forceinline__ uint32_t next(uint32_t x) const {
+    if (x >= m) return m;
+    uint32_t b = x >> 6;
+    unsigned long long w = bits[b] & (~0ull << (x & 63));
+    while (!w) {
+      if (++b >= nb) return m;
+      w = bits[b];
+    }
+    return min(m, 64 * b + uint32_t(__ffsll(w) - 1));
+  }
+  // last part start < x, or -1
+  __device__ __forceinline__ int prev(uint32_t x) const {
+    if (x == 0) return -1;
+    const uint32_t y = x - 1;
+    uint32_t b = y >> 6;
+    unsigned long long w = bits[b] & ((y & 63) == 63 ? ~0ull : ((2ull << (y & 63)) - 1));
+    while (!w) {
+      if (b == 0) return -1;
+      w = bits[--b];
+    }
+    return int(64 * b + 63 - uint32_t(__clzll(static_cast<long long>(w))));
+  }
+  __device__ __forceinline__ bool chosen(uint32_t j) const { return (sel[j >> 6] >> (j & 63)) & 1; }
+  // Pair ranks of the part starts of block b: the least one, and the mask of
+  // those equal to R.  All 64 loads are issued without branches (addresses
+  // clamped into the unit) so that they overlap.
+  __device__ __forceinline__ int32_t block_scan(uint32_t b, unsigned long long A, int32_t R,
+                                                unsigned long long &eq) const {
+    int32_t r = RANK_NONE;
+    eq = 0;
+    const uint32_t j0 = 64 * b;
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    unsigned long long o = __shfl_xor(v, d, 64);
-    v = o < v ? o : v;
+    for (uint32_t q = 0; q < 64; q += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (uint32_t t = 0; t < 8; ++t) v[t] = rank(min(j0 + q + t, m - 1));
+#pragma unroll
+      for (uint32_t t = 0; t < 8; ++t) {
+        const bool on = (A >> (q + t)) & 1;
+        r = on ? min(r, v[t]) : r;
+        eq |= (on && v[t] == R) ? (1ull << (q + t)) : 0ull;
+      }
+    }
+    return r;
   }
-  return v;
-}
+};
 
-__device__ __forceinline__ bool alive(const EncodeArgs &a, uint32_t pos) {
-  return a.ws.lalive[pos] != 0;
-}
-
-// minimum key over the parts of local block blk of the unit [s, s+m)
-__device__ __forceinline__ unsigned long long block_min(const EncodeArgs &a, uint32_t s, uint32_t m,
-                                                        uint32_t blk, int lane) {
-  const uint32_t j = blk * 64 + uint32_t(lane);
-  unsigned long long key = ~0ull;
-  if (j < m && alive(a, s + j)) {
-    const int32_t r = a.ws.lrank[s + j];
-    if (r != RANK_NONE) key = (static_cast<unsigned long long>(uint32_t(r)) << 32) | j;
-  }
-  return wave_min_u64(key);
+// Chain-parity function of a block: bit 1 = constant, bit 0 = value (xor
+// mask if not constant).  State = "the next pair of rank R in the current
+// run of such pairs has an odd index".
+__device__ __forceinline__ uint32_t chain_then(uint32_t f, uint32_t g) {
+  if (g & 2) return g;
+  return (f & 2) | ((f ^ g) & 1);
 }
 
 __device__ void merge_long(const EncodeArgs &a, uint32_t i, int lane) {
@@ -522,95 +575,175 @@ __device__ void merge_long(const EncodeArgs &a, uint32_t i, int lane) {
   const uint32_t s = a.ws.piece_start[i];
   const uint32_t m = a.ws.piece_start[i + 1] - s;
   const uint8_t *p = a.text + s;
-  unsigned long long *lmin = a.ws.lmin + (s >> 5);
-  const uint32_t nblk = (m + 63) / 64;
+  const uint32_t base = s >> 5;
+  LongUnit U{a, s, m, (m + 63) / 64, a.ws.lbits + base, a.ws.lsel + base, a.ws.lmin + base,
+             a.ws.ldirty + base};
+  const uint32_t nb = U.nb;
   for (uint32_t j = uint32_t(lane); j < m; j += 64) {
-    a.ws.lrank[s + j] = (j + 1 < m) ? T.pair[uint32_t(p[j]) * 256u + p[j + 1]] : RANK_NONE;
-    a.ws.lpart[s + j] = T.atom[p[j]];
-    a.ws.lalive[s + j] = 1;
+    U.rank(j) = (j + 1 < m) ? T.pair[uint32_t(p[j]) * 256u + p[j + 1]] : RANK_NONE;
+    U.part(j) = T.atom[p[j]];
+  }
+  for (uint32_t b = uint32_t(lane); b < nb; b += 64) {
+    const uint32_t left = m - 64 * b;
+    U.bits[b] = left >= 64 ? ~0ull : ((1ull << left) - 1);
+    U.sel[b] = 0;
+    U.dirty[b] = 0;
   }
   __threadfence();
-  for (uint32_t b = 0; b < nblk; ++b) {
-    const unsigned long long v = block_min(a, s, m, b, lane);
-    if (lane == 0) lmin[b] = v;
+  for (uint32_t b = uint32_t(lane); b < nb; b += 64) {
+    unsigned long long eq;
+    U.mn[b] = U.block_scan(b, U.bits[b], RANK_NONE, eq);
   }
   __threadfence();
-  // every round removes one part, so at most m - 1 rounds
-  for (uint32_t round = 0; round + 1 < m; ++round) {
-    unsigned long long key = ~0ull;
-    for (uint32_t b = uint32_t(lane); b < nblk; b += 64) {
-      const unsigned long long v = lmin[b];
-      key = v < key ? v : key;
+
+  for (;;) {
+    int32_t R = RANK_NONE;
+    for (uint32_t b = uint32_t(lane); b < nb; b += 64) R = min(R, U.mn[b]);
+    R = wave_min_i32(R);
+    if (R == RANK_NONE) break;
+
+    // 1. choose the pairs: chain parity scanned over blocks, 64 at a time
+    uint32_t carry = 0;
+    for (uint32_t b0 = 0; b0 < nb; b0 += 64) {
+      const uint32_t b = b0 + uint32_t(lane);
+      unsigned long long A = 0, C = 0;
+      if (b < nb) {
+        A = U.bits[b];
+        if (U.mn[b] == R) U.block_scan(b, A, R, C);
+      }
+      const unsigned long long N = A & ~C;
+      uint32_t f;
+      if (A == 0) {
+        f = 0;
+      } else if (N == 0) {
+        f = uint32_t(__popcll(C)) & 1u;
+      } else {
+        const int h = 63 - __clzll(static_cast<long long>(N));
+        const unsigned long long after = h == 63 ? 0ull : (C & (~0ull << (h + 1)));
+        f = 2u | (uint32_t(__popcll(after)) & 1u);
+      }
+      uint32_t inc = f;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = uint32_t(__shfl_up(int(inc), d, 64));
+        if (lane >= d) inc = chain_then(o, inc);
+      }
+      uint32_t ex = uint32_t(__shfl_up(int(inc), 1, 64));
+      if (lane == 0) ex = 0;  // identity
+      uint32_t st = (ex & 2) ? (ex & 1) : (carry ^ (ex & 1));
+      unsigned long long S = 0;
+      unsigned long long w = A;
+      while (w) {
+        const uint32_t t = uint32_t(__ffsll(w) - 1);
+        w &= w - 1;
+        if ((C >> t) & 1) {
+          if (st == 0) S |= 1ull << t;
+          st ^= 1u;
+        } else {
+          st = 0;
+        }
+      }
+      if (b < nb) U.sel[b] = S;
+      const uint32_t last = uint32_t(__shfl(int(inc), 63, 64));
+      carry = (last & 2) ? (last & 1) : (carry ^ (last & 1));
     }
-    key = wave_min_u64(key);
-    if (key == ~0ull) break;
-    const int32_t best = int32_t(key >> 32);
-    const uint32_t bj = uint32_t(key & 0xffffffffu);
-    // the part after bj starts within BBPE_MAX_KEY_BYTES (parts are keys)
-    uint32_t k = m;
-    for (uint32_t off = 1; off <= BBPE_MAX_KEY_BYTES + 1 && k == m; off += 64) {
-      const uint32_t j = bj + off + uint32_t(lane);
-      const unsigned long long bal = __ballot(j < m && alive(a, s + j));
-      if (bal) k = bj + off + uint32_t(__ffsll(bal) - 1);
-    }
-    if (k >= m) break;  // cannot happen: a ranked pair has a right part
-    uint32_t k2 = m;
-    for (uint32_t off = 1; off <= BBPE_MAX_KEY_BYTES + 1 && k2 == m; off += 64) {
-      const uint32_t j = k + off + uint32_t(lane);
-      const unsigned long long bal = __ballot(j < m && alive(a, s + j));
-      if (bal) k2 = k + off + uint32_t(__ffsll(bal) - 1);
-    }
-    uint32_t end2 = m;
-    if (k2 < m) {
-      for (uint32_t off = 1; off <= BBPE_MAX_KEY_BYTES + 1 && end2 == m; off += 64) {
-        const uint32_t j = k2 + off + uint32_t(lane);
-        const unsigned long long bal = __ballot(j < m && alive(a, s + j));
-        if (bal) end2 = k2 + off + uint32_t(__ffsll(bal) - 1);
+    __threadfence();
+
+    // 2. the pairs each chosen merge creates, and the first merge after which
+    // the batch must stop
+    uint32_t stop = 0xFFFFFFFFu;
+    for (uint32_t b = uint32_t(lane); b < nb; b += 64) {
+      unsigned long long S = U.sel[b];
+      while (S) {
+        const uint32_t j = 64 * b + uint32_t(__ffsll(S) - 1);
+        S &= S - 1;
+        const uint32_t k = U.next(j + 1);
+        const uint32_t k2 = U.next(k + 1);
+        const uint32_t k3 = k2 < m ? U.next(k2 + 1) : m;
+        const int y = U.prev(j);
+        int pf = y;
+        if (y >= 0) {
+          const int z = U.prev(uint32_t(y));
+          if (z >= 0 && U.chosen(uint32_t(z))) pf = z;  // y merged into z
+        }
+        uint32_t meta;
+        const int32_t nl = pf >= 0 ? lookup_text(T, p + pf, k2 - uint32_t(pf), meta) : RANK_NONE;
+        const int32_t nr = k2 < m ? lookup_text(T, p + j, k3 - j, meta) : RANK_NONE;
+        a.ws.lnl[s + j] = nl;
+        a.ws.lnr[s + j] = nr;
+        if (nl <= R || nr <= R) stop = min(stop, j);
       }
     }
-    uint32_t q = m;
-    for (uint32_t off = 1; off <= BBPE_MAX_KEY_BYTES + 1 && q == m; off += 64) {
-      const int64_t j = int64_t(bj) - int64_t(off) - lane;
-      const unsigned long long bal = __ballot(j >= 0 && alive(a, s + uint32_t(j)));
-      if (bal) q = bj - off - uint32_t(__ffsll(bal) - 1);
-    }
-    int32_t rv = RANK_NONE;
-    uint32_t ks = 0, kl = 0;
-    if (lane == 0 && k2 < m) { ks = bj; kl = end2 - bj; }
-    if (lane == 1 && q < m) { ks = q; kl = k2 - q; }
-    if (kl) {
-      uint32_t meta;
-      rv = lookup_text(T, p + ks, kl, meta);
-    }
-    const int32_t nb = __shfl(rv, 0, 64), nq = __shfl(rv, 1, 64);
-    if (lane == 0) {
-      a.ws.lalive[s + k] = 0;
-      a.ws.lpart[s + bj] = best;
-      a.ws.lrank[s + bj] = nb;
-      if (q < m) a.ws.lrank[s + q] = nq;
-      a.ws.lrank[s + k] = RANK_NONE;
+    stop = uint32_t(wave_min_i32(int32_t(min(stop, 0x7FFFFFFFu))));
+    __threadfence();
+
+    // 3. apply the merges up to and including `stop`
+    for (uint32_t b = uint32_t(lane); b < nb && 64 * b <= stop; b += 64) {
+      unsigned long long S = U.sel[b];
+      while (S) {
+        const uint32_t j = 64 * b + uint32_t(__ffsll(S) - 1);
+        S &= S - 1;
+        if (j > stop) break;
+        const uint32_t k = U.next(j + 1);
+        const uint32_t k2 = U.next(k + 1);
+        const int y = U.prev(j);
+        int pf = y;
+        if (y >= 0) {
+          const int z = U.prev(uint32_t(y));
+          if (z >= 0 && U.chosen(uint32_t(z))) pf = z;
+        }
+        U.part(j) = R;
+        U.rank(k) = RANK_NONE;
+        if (pf >= 0) {
+          U.rank(uint32_t(pf)) = a.ws.lnl[s + j];
+          U.dirty[uint32_t(pf) >> 6] = 1;
+        }
+        // the pair to the right, unless the next part merges too (its own
+        // left pair is then this part's right pair)
+        if (!(k2 < m && k2 <= stop && U.chosen(k2))) U.rank(j) = a.ws.lnr[s + j];
+        U.dirty[j >> 6] = 1;
+        U.dirty[k >> 6] = 1;
+      }
     }
     __threadfence();
-    const uint32_t b0 = bj / 64, bk = k / 64, bq = (q < m) ? q / 64 : b0;
-    unsigned long long v = block_min(a, s, m, b0, lane);
-    if (lane == 0) lmin[b0] = v;
-    if (bk != b0) {
-      v = block_min(a, s, m, bk, lane);
-      if (lane == 0) lmin[bk] = v;
+    // the merged right parts stop being part starts
+    for (uint32_t b = uint32_t(lane); b < nb && 64 * b <= stop; b += 64) {
+      unsigned long long S = U.sel[b];
+      while (S) {
+        const uint32_t j = 64 * b + uint32_t(__ffsll(S) - 1);
+        S &= S - 1;
+        if (j > stop) break;
+        const uint32_t k = U.next(j + 1);
+        atomicAnd(&U.bits[k >> 6], ~(1ull << (k & 63)));
+      }
     }
-    if (bq != b0 && bq != bk) {
-      v = block_min(a, s, m, bq, lane);
-      if (lane == 0) lmin[bq] = v;
+    __threadfence();
+    for (uint32_t b = uint32_t(lane); b < nb; b += 64) {
+      U.sel[b] = 0;
+      if (U.dirty[b]) {
+        unsigned long long eq;
+        U.mn[b] = U.block_scan(b, U.bits[b], RANK_NONE, eq);
+        U.dirty[b] = 0;
+      }
     }
     __threadfence();
   }
+
+  // output: ids in order; block counts scanned across lanes
   uint32_t c = 0;
-  for (uint32_t j0 = 0; j0 < m; j0 += 64) {
-    const uint32_t j = j0 + uint32_t(lane);
-    const bool hit = j < m && alive(a, s + j);
-    const unsigned long long bal = __ballot(hit);
-    if (hit) a.ws.tmp_ids[s + c + uint32_t(__popcll(bal & ((1ull << lane) - 1)))] = a.ws.lpart[s + j];
-    c += uint32_t(__popcll(bal));
+  for (uint32_t b0 = 0; b0 < nb; b0 += 64) {
+    const uint32_t b = b0 + uint32_t(lane);
+    const unsigned long long A = b < nb ? U.bits[b] : 0ull;
+    const uint32_t cnt = uint32_t(__popcll(A));
+    const uint32_t incl = wave_incl_sum(cnt, lane);
+    uint32_t o = c + incl - cnt;
+    unsigned long long w = A;
+    while (w) {
+      const uint32_t t = uint32_t(__ffsll(w) - 1);
+      w &= w - 1;
+      a.ws.tmp_ids[s + o++] = U.part(64 * b + t);
+    }
+    c += uint32_t(__shfl(int(incl), 63, 64));
   }
   a.ws.piece_cnt[i] = c;  // c is the same in every lane
 }
@@ -624,24 +757,21 @@ __device__ __forceinline__ void merge_short_unit(const EncodeArgs &a, uint32_t i
   a.ws.piece_cnt[i] = merge_short<SK>(a.T, u, m, a.ws.tmp_ids + s);
 }
 
-// Merge of every listed unit.  Work items in order: long units (the longest
-// chains), wave units, then chunks of 64 short units (one lane each); wave
-// w takes items w, w + G, w + 2G, ... (G waves in the grid), so the long
-// chains start first and short work fills the machine beside them.  The
-// item index is wave-uniform by construction: no lane-0 ticket and
-// broadcast, which lets the compiler split the loop per lane.
+// Merge of the listed units up to WAVE_MAX bytes.  Work items in order: wave
+// units (the longest chains), then chunks of 64 short units (one lane each);
+// wave w takes items w, w + G, w + 2G, ... (G waves in the grid), so the long
+// chains start first and short work fills the machine beside them.  The item
+// index is wave-uniform by construction: no lane-0 ticket and broadcast,
+// which lets the compiler split the loop per lane.
 __global__ void __launch_bounds__(64) k_merge(EncodeArgs a) {
   if (a.ws.status->pad2) return;
   const Status *st = a.ws.status;
   const int lane = int(threadIdx.x);
-  const uint32_t nll = st->n_ll, nlw = st->n_lw, n32 = st->n_l32, n16 = st->n_l16;
-  const uint32_t e_ll = nll, e_lw = e_ll + nlw, e_32 = e_lw + (n32 + 63) / 64,
-                 e_16 = e_32 + (n16 + 63) / 64;
+  const uint32_t nlw = st->n_lw, n32 = st->n_l32, n16 = st->n_l16;
+  const uint32_t e_lw = nlw, e_32 = e_lw + (n32 + 63) / 64, e_16 = e_32 + (n16 + 63) / 64;
   for (uint32_t item = blockIdx.x; item < e_16; item += gridDim.x) {
-    if (item < e_ll) {
-      merge_long(a, a.ws.ll[item], lane);
-    } else if (item < e_lw) {
-      merge_wave(a, a.ws.lw[item - e_ll], lane);
+    if (item < e_lw) {
+      merge_wave(a, a.ws.lw[item], lane);
     } else if (item < e_32) {
       const uint32_t x = (item - e_lw) * 64 + uint32_t(lane);
       if (x < n32) merge_short_unit<32>(a, a.ws.l32[x]);
@@ -650,6 +780,15 @@ __global__ void __launch_bounds__(64) k_merge(EncodeArgs a) {
       if (x < n16) merge_short_unit<16>(a, a.ws.l16[x]);
     }
   }
+}
+
+// Merge of the units longer than WAVE_MAX, one wave each (its own kernel:
+// sharing one with the register tiers costs those their occupancy).
+__global__ void __launch_bounds__(64) k_merge_long(EncodeArgs a) {
+  if (a.ws.status->pad2) return;
+  const uint32_t nll = a.ws.status->n_ll;
+  for (uint32_t item = blockIdx.x; item < nll; item += gridDim.x)
+    merge_long(a, a.ws.ll[item], int(threadIdx.x));
 }
 
 // ---------------------------------------------------------------------------

@@ -21,7 +21,7 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 struct WsLayout {
   uint64_t status, tile_nchar, tile_lastchg, tile_charbase, tile_chgcarry, seg_local, seg_charstart,
       ss, spst, spc, ps, tile_fn, tile_carry, tile_np, piece_start, piece_cnt, piece_off,
-      tmp_ids, scan_part, l16, l32, lw, ll, lrank, lpart, lalive, lmin, total;
+      tmp_ids, scan_part, l16, l32, lw, ll, lrank, lpart, lnl, lnr, lbits, lsel, lmin, ldirty, total;
   uint64_t n_words;
   uint32_t n_tiles;
 };
@@ -63,8 +63,12 @@ WsLayout layout_for(uint64_t n, uint32_t n_seg) {
   take(L.ll, 4 * (n / 513 + 1));
   take(L.lrank, 4 * (n + 1));
   take(L.lpart, 4 * (n + 1));
-  take(L.lalive, n + 1);
-  take(L.lmin, 8 * (n / 32 + 2));
+  take(L.lnl, 4 * (n + 1));
+  take(L.lnr, 4 * (n + 1));
+  take(L.lbits, 8 * (n / 32 + 2));
+  take(L.lsel, 8 * (n / 32 + 2));
+  take(L.lmin, 4 * (n / 32 + 2));
+  take(L.ldirty, 4 * (n / 32 + 2));
   L.total = o;
   return L;
 }
@@ -224,8 +228,12 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
   a.ws.ll = reinterpret_cast<uint32_t *>(w + L.ll);
   a.ws.lrank = reinterpret_cast<int32_t *>(w + L.lrank);
   a.ws.lpart = reinterpret_cast<int32_t *>(w + L.lpart);
-  a.ws.lalive = w + L.lalive;
-  a.ws.lmin = reinterpret_cast<unsigned long long *>(w + L.lmin);
+  a.ws.lnl = reinterpret_cast<int32_t *>(w + L.lnl);
+  a.ws.lnr = reinterpret_cast<int32_t *>(w + L.lnr);
+  a.ws.lbits = reinterpret_cast<unsigned long long *>(w + L.lbits);
+  a.ws.lsel = reinterpret_cast<unsigned long long *>(w + L.lsel);
+  a.ws.lmin = reinterpret_cast<int32_t *>(w + L.lmin);
+  a.ws.ldirty = reinterpret_cast<uint32_t *>(w + L.ldirty);
   return BBPE_OK;
 }
 
@@ -323,7 +331,8 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
   } else {
     const uint32_t probe_grid = uint32_t(std::min<uint64_t>((n + 1023) / 1024, 16384));
     go("k_probe", k_probe, dim3(probe_grid), dim3(256), a);
-    // persistent waves draining the merge queue
+    const uint32_t long_grid = uint32_t(std::min<uint64_t>(n / 513 + 1, 2048));
+    go("k_merge_long", k_merge_long, dim3(long_grid), dim3(64), a);
     const uint32_t merge_grid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
     go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
     const uint32_t nscan = uint32_t((n + 1 + 4095) / 4096);

@@ -29,10 +29,14 @@ struct WsPtrs {
   int32_t *tmp_ids;                 // [N] ids of each piece, at the piece's byte offset
   uint32_t *scan_part;              // [N/4096+2] partial sums of the piece scan
   uint32_t *l16, *l32, *lw, *ll;    // units to merge, by length
-  int32_t *lrank;                   // [N] long tier: pair rank at each part start
-  int32_t *lpart;                   // [N] long tier: rank of the part starting here
-  uint8_t *lalive;                  // [N] long tier: 1 where a part starts
-  unsigned long long *lmin;         // [W] long tier: per-word minimum (rank<<32 | position)
+  // long tier, per text position: pair rank at each part start, id of the
+  // part starting there, and the two created-pair ranks of a batch merge
+  int32_t *lrank, *lpart, *lnl, *lnr;
+  // long tier, per 64-position block of a unit (index (s >> 5) + block):
+  // part starts, selected pair starts, least pair rank, stale-minimum flag
+  unsigned long long *lbits, *lsel;
+  int32_t *lmin;
+  uint32_t *ldirty;
 };
 
 struct EncodeArgs {
@@ -65,6 +69,7 @@ __global__ void k_scan_tiles_np(EncodeArgs a);
 __global__ void k_pieces(EncodeArgs a);
 __global__ void k_probe(EncodeArgs a);
 __global__ void k_merge(EncodeArgs a);
+__global__ void k_merge_long(EncodeArgs a);
 __global__ void k_scan_reduce(EncodeArgs a);
 __global__ void k_scan_partials(EncodeArgs a);
 __global__ void k_scan_down(EncodeArgs a);

@@ -247,6 +247,52 @@ def test_long_pieces_tiny_table(tiny):
     assert_ids(tok, orc, segs, what="long pieces")
 
 
+def test_long_units_adversarial_tables():
+    """Units over 512 bytes (the batched long tier) under random tables over
+    {a, b}: keys of 2-6 bytes with random ranks, so that merges of equal rank
+    often create pairs of lower rank (the batch must stop there)."""
+    import itertools
+    for ti in range(10):
+        r = random.Random(100 + ti)
+        tab = dict(atoms_permuted(1))
+        keys = [bytes(k) for L in range(2, 7) for k in itertools.product(b"ab", repeat=L)]
+        r.shuffle(keys)
+        chosen = keys[:r.randint(8, 40)]
+        for k, rk in zip(chosen, r.sample(range(256, 656), len(chosen))):
+            tab[k] = rk
+        tok, orc = make(tab, [], 0)
+        segs = []
+        for _ in range(4):
+            n = r.randint(520, 3000)
+            mode = r.random()
+            if mode < 0.3:
+                seg = b"a" * n
+            elif mode < 0.6:
+                seg = (b"ab" * n)[:n]
+            else:
+                seg = bytes(r.choice(b"aab") for _ in range(n))
+            segs.append((seg, False))
+        say("adversarial long units, table", ti)
+        assert_ids(tok, orc, segs, safe=False, what="adversarial table %d" % ti)
+
+
+def test_long_runs_main_table():
+    """Runs of one character and repeated patterns with the 100,256-rank
+    table, chunked and unchunked."""
+    from synth import configs
+    w = configs.main()
+    tok, orc = make(w.tokens, w.specials, w.grammar)
+    r = random.Random(10)
+    segs = [((" " * 30000 + "x").encode(), False), (("-" * 3000).encode(), False),
+            (("=" * 2001 + "a").encode(), False), (("ab" * 700).encode(), False),
+            ("".join(r.choice("abcdeinorst") for _ in range(1500)).encode(), False),
+            (("\t" * 900 + " " * 700 + "\n" * 600 + "z").encode(), False),
+            ((" " * 60001).encode(), False), (("*" * 800 + "/" * 700).encode(), False)]
+    say("long runs, main table")
+    assert_ids(tok, orc, segs, safe=False, what="runs unchunked")
+    assert_ids(tok, orc, segs, safe=True, what="runs chunked")
+
+
 # ---------------------------------------------------------------- errors ----
 
 @pytest.mark.parametrize("bad,pos", [(b"ab\xc0\x80", 2), (b"a\xed\xa0\x80", 1),
