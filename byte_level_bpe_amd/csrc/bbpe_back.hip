@@ -11,8 +11,9 @@
 // length and merged by k_merge in three tiers:
 //   short (<= 32 bytes): one lane per unit, bytes / pair ranks / part ids in
 //     registers with static indexing;
-//   wave (<= 512 bytes): one wave per unit, eight positions per lane in
-//     registers, argmin by a wave reduction;
+//   group (<= 512 bytes): 16, 32 or 64 lanes per unit (<= 128, 256, 512
+//     bytes), eight positions per lane in registers, argmin by a reduction
+//     over the group;
 //   long: one wave per unit, state in global memory, pairs of the least rank
 //     merged in batches.
 #include <hip/hip_runtime.h>
@@ -82,19 +83,25 @@ __device__ __forceinline__ uint64_t low_bytes(uint64_t w, uint32_t k) {  // keep
   return k >= 8 ? w : (w & ((uint64_t(1) << (8 * k)) - 1));
 }
 
-// Probe the table for a key with hash h, first word k8 and length len; the
-// remaining bytes (for len > 8) are checked by `rest_eq(blob_ptr)`.
+// Probe the table for a key with hash h, first two words k8 / k8b (zero
+// padded) and length len; bytes 16.. (for len > 16) are checked by
+// `rest_eq(blob_ptr)`.  The slot and its second key word load together.
+__device__ __forceinline__ bool slot_match(const DevTables &T, const Slot &sl, uint64_t e, uint64_t k8,
+                                           uint64_t k8b, uint32_t len) {
+  return (sl.meta & 0xFFu) == len && sl.k8 == k8 && (len <= 8 || e == k8b);
+}
 template <typename RestEq>
-__device__ __forceinline__ int32_t probe(const DevTables &T, uint64_t h, uint64_t k8, uint32_t len,
-                                         uint32_t &meta, RestEq rest_eq) {
+__device__ __forceinline__ int32_t probe(const DevTables &T, uint64_t h, uint64_t k8, uint64_t k8b,
+                                         uint32_t len, uint32_t &meta, RestEq rest_eq) {
   uint32_t idx = uint32_t(h) & T.slot_mask;
   for (;;) {
-    const Slot s = T.slots[idx];
-    if (s.rank < 0) return RANK_NONE;
-    if ((s.meta & 0xFFu) == len && s.k8 == k8 &&
-        (len <= 8 || rest_eq(T.blob + (s.meta >> META_OFF_SHIFT)))) {
-      meta = s.meta;
-      return s.rank;
+    const Slot sl = T.slots[idx];
+    const uint64_t e = T.ext[idx];
+    if (sl.rank < 0) return RANK_NONE;
+    if (slot_match(T, sl, e, k8, k8b, len) &&
+        (len <= 16 || rest_eq(T.blob + (sl.meta >> META_OFF_SHIFT)))) {
+      meta = sl.meta;
+      return sl.rank;
     }
     idx = (idx + 1) & T.slot_mask;
   }
@@ -104,17 +111,18 @@ __device__ __forceinline__ int32_t probe(const DevTables &T, uint64_t h, uint64_
 __device__ __forceinline__ int32_t lookup_text(const DevTables &T, const uint8_t *__restrict__ p,
                                                uint32_t len, uint32_t &meta) {
   if (len > T.max_key_len) return RANK_NONE;
-  uint64_t h = hash_seed(len);
-  uint64_t k8 = 0;
-  for (uint32_t i = 0; i < len; i += 8) {
+  auto word = [&](uint32_t i) __attribute__((always_inline)) {  // bytes i.. of the key, zero padded
     const uint32_t k = min(8u, len - i);
     uint64_t wv = 0;
     for (uint32_t j = 0; j < k; ++j) wv |= uint64_t(p[i + j]) << (8 * j);
-    if (i == 0) k8 = wv;
-    h = hash_step(h, wv);
-  }
-  return probe(T, h, k8, len, meta, [&](const uint8_t *b) {
-    for (uint32_t j = 8; j < len; ++j)
+    return wv;
+  };
+  const uint64_t k8 = word(0), k8b = len > 8 ? word(8) : 0ull;
+  uint64_t h = hash_step(hash_seed(len), k8);
+  if (len > 8) h = hash_step(h, k8b);
+  for (uint32_t i = 16; i < len; i += 8) h = hash_step(h, word(i));
+  return probe(T, h, k8, k8b, len, meta, [&](const uint8_t *b) __attribute__((always_inline)) {
+    for (uint32_t j = 16; j < len; ++j)
       if (b[j] != p[j]) return false;
     return true;
   });
@@ -193,20 +201,21 @@ __device__ __forceinline__ void load_unit(const uint8_t *__restrict__ text, uint
 
 template <int SK>
 __device__ __forceinline__ void unit_hash(const UnitBytes<SK> &u, uint32_t a, uint32_t len,
-                                          uint64_t &h, uint64_t &k8) {
-  h = hash_seed(len);
-  k8 = 0;
-  for (uint32_t i = 0; i < len; i += 8) {
-    const uint64_t w = low_bytes(u.slice8(a + i), len - i);
-    if (i == 0) k8 = w;
-    h = hash_step(h, w);
-  }
+                                          uint64_t &h, uint64_t &k8, uint64_t &k8b) {
+  // (the first two words are named outside the loop: selecting them inside
+  // it let the compiler build a dynamically indexed array in scratch)
+  k8 = low_bytes(u.slice8(a), len);
+  k8b = len > 8 ? low_bytes(u.slice8(a + 8), len - 8) : 0ull;
+  h = hash_step(hash_seed(len), k8);
+  if (len > 8) h = hash_step(h, k8b);
+  for (uint32_t i = 16; i < len; i += 8) h = hash_step(h, low_bytes(u.slice8(a + i), len - i));
 }
 
+// key bytes 16..len of the unit slice [a, a+len) against the blob
 template <int SK>
 __device__ __forceinline__ bool unit_rest_eq(const UnitBytes<SK> &u, uint32_t a, uint32_t len,
                                              const uint8_t *b) {
-  for (uint32_t i = 8; i < len; i += 8) {
+  for (uint32_t i = 16; i < len; i += 8) {
     const uint32_t k = min(8u, len - i);
     uint64_t bw = 0;
     for (uint32_t j = 0; j < k; ++j) bw |= uint64_t(b[i + j]) << (8 * j);
@@ -222,31 +231,32 @@ __device__ __forceinline__ void unit_lookup2(const DevTables &T, const UnitBytes
                                              uint32_t l1, uint32_t a2, uint32_t l2, int32_t &r1,
                                              int32_t &r2) {
   const bool v1 = l1 > 0 && l1 <= T.max_key_len, v2 = l2 > 0 && l2 <= T.max_key_len;
-  uint64_t h1 = 0, k1 = 0, h2 = 0, k2 = 0;
-  if (v1) unit_hash(u, a1, l1, h1, k1);
-  if (v2) unit_hash(u, a2, l2, h2, k2);
+  uint64_t h1 = 0, k1 = 0, x1 = 0, h2 = 0, k2 = 0, x2 = 0;
+  if (v1) unit_hash(u, a1, l1, h1, k1, x1);
+  if (v2) unit_hash(u, a2, l2, h2, k2, x2);
   const uint32_t i1 = uint32_t(h1) & T.slot_mask, i2 = uint32_t(h2) & T.slot_mask;
   Slot s1{0, 0, -1}, s2{0, 0, -1};
-  if (v1) s1 = T.slots[i1];
-  if (v2) s2 = T.slots[i2];
+  uint64_t e1 = 0, e2 = 0;
+  if (v1) { s1 = T.slots[i1]; e1 = T.ext[i1]; }
+  if (v2) { s2 = T.slots[i2]; e2 = T.ext[i2]; }
   uint32_t meta;
   r1 = RANK_NONE;
   r2 = RANK_NONE;
   if (v1 && s1.rank >= 0) {
-    if ((s1.meta & 0xFFu) == l1 && s1.k8 == k1 &&
-        (l1 <= 8 || unit_rest_eq(u, a1, l1, T.blob + (s1.meta >> META_OFF_SHIFT))))
+    if (slot_match(T, s1, e1, k1, x1, l1) &&
+        (l1 <= 16 || unit_rest_eq(u, a1, l1, T.blob + (s1.meta >> META_OFF_SHIFT))))
       r1 = s1.rank;
     else
-      r1 = probe(T, h1 + 1, k1, l1, meta,
-                 [&](const uint8_t *b) { return unit_rest_eq(u, a1, l1, b); });
+      r1 = probe(T, h1 + 1, k1, x1, l1, meta,
+                 [&](const uint8_t *b) __attribute__((always_inline)) { return unit_rest_eq(u, a1, l1, b); });
   }
   if (v2 && s2.rank >= 0) {
-    if ((s2.meta & 0xFFu) == l2 && s2.k8 == k2 &&
-        (l2 <= 8 || unit_rest_eq(u, a2, l2, T.blob + (s2.meta >> META_OFF_SHIFT))))
+    if (slot_match(T, s2, e2, k2, x2, l2) &&
+        (l2 <= 16 || unit_rest_eq(u, a2, l2, T.blob + (s2.meta >> META_OFF_SHIFT))))
       r2 = s2.rank;
     else
-      r2 = probe(T, h2 + 1, k2, l2, meta,
-                 [&](const uint8_t *b) { return unit_rest_eq(u, a2, l2, b); });
+      r2 = probe(T, h2 + 1, k2, x2, l2, meta,
+                 [&](const uint8_t *b) __attribute__((always_inline)) { return unit_rest_eq(u, a2, l2, b); });
   }
 }
 
@@ -305,8 +315,9 @@ __device__ __forceinline__ uint32_t merge_short(const DevTables &T, const UnitBy
 // ---------------------------------------------------------------------------
 // Probe pass: one thread per unit.
 // ---------------------------------------------------------------------------
-constexpr uint32_t WNS = 8;                // positions per lane in the wave tier
-constexpr uint32_t WAVE_MAX = 64 * WNS;    // longest unit the wave tier holds
+constexpr uint32_t WNS = 8;                // positions per lane in the group tiers
+constexpr uint32_t WAVE_MAX = 64 * WNS;    // longest unit the group tiers hold
+constexpr uint32_t GROUP_PACK_MIN = 4096;  // group units above which several share a wave
 
 // Every unit: specials, single bytes and units that are keys whose own
 // merges rebuild them get their id here; the rest are listed for k_merge by
@@ -320,11 +331,12 @@ __global__ void __launch_bounds__(PROBE_BLOCK) k_probe(EncodeArgs a) {
   Status *st = a.ws.status;
   const uint32_t P = uint32_t(st->n_pieces);
   const DevTables &T = a.T;
-  __shared__ unsigned int s_cnt[4], s_base[4];
-  __shared__ uint32_t s_list[4][PROBE_BLOCK];
+  constexpr uint32_t NLIST = 6;
+  __shared__ unsigned int s_cnt[NLIST], s_base[NLIST];
+  __shared__ uint32_t s_list[NLIST][PROBE_BLOCK];
   for (uint32_t b = blockIdx.x * PROBE_BLOCK; b < P; b += gridDim.x * PROBE_BLOCK) {
     const uint32_t i = b + threadIdx.x;
-    int tier = 0;  // 1: <= 16 bytes, 2: <= 32, 3: wave, 4: long
+    int tier = 0;  // list: 1 <= 16 bytes, 2 <= 32, 3 <= 128, 4 <= 256, 5 <= 512, 6 longer
     if (i < P) {
       const uint32_t s = a.ws.piece_start[i];
       const uint32_t m = a.ws.piece_start[i + 1] - s;
@@ -336,42 +348,43 @@ __global__ void __launch_bounds__(PROBE_BLOCK) k_probe(EncodeArgs a) {
       } else if (m <= 32) {
         UnitBytes<32> u;
         load_unit(a.text, a.n, s, m, u);
-        uint64_t h, k8;
-        unit_hash(u, 0, m, h, k8);
+        uint64_t h, k8, k8b;
+        unit_hash(u, 0, m, h, k8, k8b);
         uint32_t meta = 0;
         const int32_t r = m <= T.max_key_len
-                              ? probe(T, h, k8, m, meta,
-                                      [&](const uint8_t *bb) { return unit_rest_eq(u, 0, m, bb); })
+                              ? probe(T, h, k8, k8b, m, meta,
+                                      [&](const uint8_t *bb) __attribute__((always_inline)) { return unit_rest_eq(u, 0, m, bb); })
                               : RANK_NONE;
         if (r != RANK_NONE && (meta & META_SELF)) id = r;
         else tier = m <= 16 ? 1 : 2;
-      } else if (m <= T.max_key_len) {
-        uint32_t meta = 0;
-        const int32_t r = lookup_text(T, a.text + s, m, meta);
-        if (r != RANK_NONE && (meta & META_SELF)) id = r;
-        else tier = m <= WAVE_MAX ? 3 : 4;
       } else {
-        tier = m <= WAVE_MAX ? 3 : 4;
+        uint32_t meta = 0;
+        const int32_t r = m <= T.max_key_len ? lookup_text(T, a.text + s, m, meta) : RANK_NONE;
+        if (r != RANK_NONE && (meta & META_SELF)) id = r;
+        else tier = m <= 128 ? 3 : m <= 256 ? 4 : m <= WAVE_MAX ? 5 : 6;
       }
       if (id >= 0) {
         a.ws.tmp_ids[s] = id;
         a.ws.piece_cnt[i] = 1;
       }
     }
-    if (threadIdx.x < 4) s_cnt[threadIdx.x] = 0;
+    if (threadIdx.x < NLIST) s_cnt[threadIdx.x] = 0;
     __syncthreads();
     if (tier) s_list[tier - 1][atomicAdd(&s_cnt[tier - 1], 1u)] = i;
     __syncthreads();
-    if (threadIdx.x < 4 && s_cnt[threadIdx.x]) {
-      unsigned int *cnt = threadIdx.x == 0 ? &st->n_l16
+    if (threadIdx.x < NLIST && s_cnt[threadIdx.x]) {
+      unsigned int *cnt = threadIdx.x == 0   ? &st->n_l16
                           : threadIdx.x == 1 ? &st->n_l32
-                          : threadIdx.x == 2 ? &st->n_lw : &st->n_ll;
+                          : threadIdx.x == 2 ? &st->n_g16
+                          : threadIdx.x == 3 ? &st->n_g32
+                          : threadIdx.x == 4 ? &st->n_g64 : &st->n_ll;
       s_base[threadIdx.x] = atomicAdd(cnt, s_cnt[threadIdx.x]);
     }
     __syncthreads();
 #pragma unroll
-    for (int L = 0; L < 4; ++L) {
-      uint32_t *list = L == 0 ? a.ws.l16 : L == 1 ? a.ws.l32 : L == 2 ? a.ws.lw : a.ws.ll;
+    for (uint32_t L = 0; L < NLIST; ++L) {
+      uint32_t *list = L == 0 ? a.ws.l16 : L == 1 ? a.ws.l32 : L == 2 ? a.ws.g16
+                       : L == 3 ? a.ws.g32 : L == 4 ? a.ws.g64 : a.ws.ll;
       for (uint32_t k = threadIdx.x; k < s_cnt[L]; k += PROBE_BLOCK) list[s_base[L] + k] = s_list[L][k];
     }
     __syncthreads();
@@ -379,10 +392,14 @@ __global__ void __launch_bounds__(PROBE_BLOCK) k_probe(EncodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Wave tier: one wave per unit of 33..WAVE_MAX bytes.  Position j lives in
-// lane j % 64, slot j / 64: its pair rank (RANK_NONE unless a part with a
-// right neighbour starts at j) and the id of the part starting at j.  The
-// part starts are a wave-uniform bit mask.
+// Group tier: units of 33..WAVE_MAX bytes, a group of G lanes per unit (64/G
+// units per wave), P positions per lane in registers.  Position j of a unit
+// lives in lane j % G of its group, slot j / G: its pair rank (RANK_NONE
+// unless a part with a right neighbour starts at j) and the id of the part
+// starting at j.  The part starts are a G-bit mask per slot, the same in
+// every lane of the group.  Each round: group argmin (butterfly over the
+// group's lanes, then the lowest position holding it), then two lanes of
+// the group look up the merged part's new pairs side by side.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int32_t wave_min_i32(int32_t v) {
 #pragma unroll
@@ -393,95 +410,135 @@ __device__ __forceinline__ int32_t wave_min_i32(int32_t v) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
-// first set bit at position >= x, or m
-__device__ __forceinline__ uint32_t next_set(const uint64_t (&A)[WNS], uint32_t x, uint32_t m) {
-  uint32_t res = m;
-#pragma unroll
-  for (int t = int(WNS) - 1; t >= 0; --t) {
-    const uint32_t lo = 64u * uint32_t(t);
-    uint64_t w = A[t];
-    if (x >= lo + 64) w = 0;
-    else if (x > lo) w &= ~0ull << (x - lo);
-    res = w ? lo + uint32_t(__ffsll(static_cast<unsigned long long>(w)) - 1) : res;
-  }
-  return res;
+// Minimum over the 64 lanes by DPP (row shifts, then row broadcasts 15 and
+// 31; no LDS round trips), read back from lane 63.
+__device__ __forceinline__ int32_t dpp_wave_min(int32_t v) {
+  constexpr int32_t I = 0x7fffffff;
+  v = min(v, __builtin_amdgcn_update_dpp(I, v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = min(v, __builtin_amdgcn_update_dpp(I, v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = min(v, __builtin_amdgcn_update_dpp(I, v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = min(v, __builtin_amdgcn_update_dpp(I, v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = min(v, __builtin_amdgcn_update_dpp(I, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = min(v, __builtin_amdgcn_update_dpp(I, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
-// last set bit at position < x, or -1
-__device__ __forceinline__ int prev_set(const uint64_t (&A)[WNS], uint32_t x) {
-  int res = -1;
+template <uint32_t G, uint32_t P>
+struct GroupMask {
+  uint64_t w[P];
+  static constexpr uint64_t full = G == 64 ? ~0ull : ((1ull << G) - 1);
+  // first set position >= x, or m
+  __device__ __forceinline__ uint32_t next(uint32_t x, uint32_t m) const {
+    uint32_t res = m;
 #pragma unroll
-  for (int t = 0; t < int(WNS); ++t) {
-    const uint32_t lo = 64u * uint32_t(t);
-    uint64_t w = A[t];
-    if (x <= lo) w = 0;
-    else if (x < lo + 64) w &= (1ull << (x - lo)) - 1;
-    res = w ? int(lo) + 63 - __clzll(static_cast<long long>(w)) : res;
+    for (int t = int(P) - 1; t >= 0; --t) {
+      const uint32_t lo = G * uint32_t(t);
+      uint64_t v = w[t];
+      if (x >= lo + G) v = 0;
+      else if (x > lo) v &= ~0ull << (x - lo);
+      res = v ? lo + uint32_t(__ffsll(static_cast<unsigned long long>(v)) - 1) : res;
+    }
+    return res;
   }
-  return res;
-}
+  // last set position < x, or -1
+  __device__ __forceinline__ int prev(uint32_t x) const {
+    int res = -1;
+#pragma unroll
+    for (int t = 0; t < int(P); ++t) {
+      const uint32_t lo = G * uint32_t(t);
+      uint64_t v = w[t];
+      if (x <= lo) v = 0;
+      else if (x < lo + G) v &= (1ull << (x - lo)) - 1;
+      res = v ? int(lo) + 63 - __clzll(static_cast<long long>(v)) : res;
+    }
+    return res;
+  }
+};
 
-__device__ void merge_wave(const EncodeArgs &a, uint32_t i, int lane) {
+template <uint32_t G, uint32_t P>
+__device__ void merge_group(const EncodeArgs &a, const uint32_t *list, uint32_t count,
+                            uint32_t first, int lane) {
   const DevTables &T = a.T;
-  const uint32_t s = a.ws.piece_start[i];
-  const uint32_t m = a.ws.piece_start[i + 1] - s;
+  const uint32_t g = uint32_t(lane) / G, gl = uint32_t(lane) % G;
+  const uint32_t x = first + g;
+  const bool live = x < count;
+  const uint32_t i = live ? list[x] : 0u;
+  const uint32_t s = live ? a.ws.piece_start[i] : 0u;
+  const uint32_t m = live ? a.ws.piece_start[i + 1] - s : 0u;
   const uint8_t *p = a.text + s;
-  int32_t r[WNS], pr[WNS];
-  uint64_t A[WNS];
+  int32_t r[P], pr[P];
+  GroupMask<G, P> A;
 #pragma unroll
-  for (uint32_t t = 0; t < WNS; ++t) {
-    const uint32_t j = 64u * t + uint32_t(lane);
+  for (uint32_t t = 0; t < P; ++t) {
+    const uint32_t j = G * t + gl;
     const uint32_t b0 = j < m ? p[j] : 0u, b1 = j + 1 < m ? p[j + 1] : 0u;
     r[t] = j + 1 < m ? T.pair[b0 * 256u + b1] : RANK_NONE;
     pr[t] = j < m ? T.atom[b0] : 0;
-    const uint32_t lo = 64u * t;
-    A[t] = m >= lo + 64 ? ~0ull : (m > lo ? (1ull << (m - lo)) - 1 : 0ull);
+    const uint32_t lo = G * t;
+    A.w[t] = m >= lo + G ? A.full : (m > lo ? (1ull << (m - lo)) - 1 : 0ull);
   }
-  for (uint32_t round = 0; round + 1 < m; ++round) {
-    int32_t lm = RANK_NONE;
+  for (;;) {
+    int32_t best = RANK_NONE;
 #pragma unroll
-    for (uint32_t t = 0; t < WNS; ++t) lm = r[t] < lm ? r[t] : lm;
-    const int32_t best = wave_min_i32(lm);
-    if (best == RANK_NONE) break;
-    uint32_t bj = m;  // leftmost position holding the minimum
+    for (uint32_t t = 0; t < P; ++t) best = r[t] < best ? r[t] : best;
+    if (G == 64) {
+      best = dpp_wave_min(best);
+    } else {
 #pragma unroll
-    for (int t = int(WNS) - 1; t >= 0; --t) {
-      const unsigned long long bal = __ballot(r[t] == best);
-      bj = bal ? 64u * uint32_t(t) + uint32_t(__ffsll(bal) - 1) : bj;
+      for (uint32_t d = 1; d < G; d <<= 1) {
+        const int32_t o = __shfl_xor(best, int(d), 64);
+        best = o < best ? o : best;
+      }
     }
-    const uint32_t k = next_set(A, bj + 1, m);   // the part merged into bj
-    const uint32_t k2 = next_set(A, k + 1, m);   // end of the merged part
-    const uint32_t end2 = k2 < m ? next_set(A, k2 + 1, m) : m;
-    const int q = prev_set(A, bj);
-    // lane 0: the merged part with its right neighbour; lane 1: the left
-    // neighbour with the merged part (both lookups run side by side)
+    const bool act = best != RANK_NONE;
+    if (!__ballot(act)) break;  // every group of the wave is done
+    uint32_t bj = m;  // lowest position of the group holding the minimum
+#pragma unroll
+    for (int t = int(P) - 1; t >= 0; --t) {
+      const unsigned long long bal = __ballot(act && r[t] == best);
+      const uint64_t gb = (bal >> (g * G)) & A.full;
+      bj = gb ? G * uint32_t(t) + uint32_t(__ffsll(static_cast<unsigned long long>(gb)) - 1) : bj;
+    }
+    uint32_t k = m, k2 = m, end2 = m;
+    int q = -1;
+    if (act) {
+      k = A.next(bj + 1, m);   // the part merged into bj
+      k2 = A.next(k + 1, m);   // end of the merged part
+      end2 = k2 < m ? A.next(k2 + 1, m) : m;
+      q = A.prev(bj);
+    }
+    // group lane 0: the merged part with its right neighbour; lane 1: the
+    // left neighbour with the merged part
     uint32_t ks = 0, kl = 0;
-    if (lane == 0 && k2 < m) { ks = bj; kl = end2 - bj; }
-    if (lane == 1 && q >= 0) { ks = uint32_t(q); kl = k2 - uint32_t(q); }
+    if (act && gl == 0 && k2 < m) { ks = bj; kl = end2 - bj; }
+    if (act && gl == 1 && q >= 0) { ks = uint32_t(q); kl = k2 - uint32_t(q); }
     int32_t rv = RANK_NONE;
     if (kl) {
       uint32_t meta;
       rv = lookup_text(T, p + ks, kl, meta);
     }
-    const int32_t nb = __shfl(rv, 0, 64), nq = __shfl(rv, 1, 64);
+    const int32_t nb = __shfl(rv, int(g * G), 64), nq = __shfl(rv, int(g * G + 1), 64);
+    if (act) {
 #pragma unroll
-    for (uint32_t t = 0; t < WNS; ++t) {
-      const uint32_t j = 64u * t + uint32_t(lane);
-      r[t] = j == k ? RANK_NONE : r[t];
-      r[t] = j == bj ? nb : r[t];
-      pr[t] = j == bj ? best : pr[t];
-      r[t] = (q >= 0 && j == uint32_t(q)) ? nq : r[t];
-      A[t] = (k >> 6) == t ? A[t] & ~(1ull << (k & 63)) : A[t];
+      for (uint32_t t = 0; t < P; ++t) {
+        const uint32_t j = G * t + gl;
+        r[t] = j == k ? RANK_NONE : r[t];
+        r[t] = j == bj ? nb : r[t];
+        pr[t] = j == bj ? best : pr[t];
+        r[t] = (q >= 0 && j == uint32_t(q)) ? nq : r[t];
+        A.w[t] = (k / G) == t ? A.w[t] & ~(1ull << (k % G)) : A.w[t];
+      }
     }
   }
+  if (!live) return;
   uint32_t c = 0;
-  const unsigned long long below = (1ull << lane) - 1;
+  const uint64_t below = (1ull << gl) - 1;
 #pragma unroll
-  for (uint32_t t = 0; t < WNS; ++t) {
-    if ((A[t] >> lane) & 1) a.ws.tmp_ids[s + c + uint32_t(__popcll(A[t] & below))] = pr[t];
-    c += uint32_t(__popcll(A[t]));
+  for (uint32_t t = 0; t < P; ++t) {
+    if ((A.w[t] >> gl) & 1) a.ws.tmp_ids[s + c + uint32_t(__popcll(A.w[t] & below))] = pr[t];
+    c += uint32_t(__popcll(A.w[t]));
   }
-  a.ws.piece_cnt[i] = c;  // c is the same in every lane
+  a.ws.piece_cnt[i] = c;  // c is the same in every lane of the group
 }
 
 // ---------------------------------------------------------------------------
@@ -757,27 +814,50 @@ __device__ __forceinline__ void merge_short_unit(const EncodeArgs &a, uint32_t i
   a.ws.piece_cnt[i] = merge_short<SK>(a.T, u, m, a.ws.tmp_ids + s);
 }
 
-// Merge of the listed units up to WAVE_MAX bytes.  Work items in order: wave
-// units (the longest chains), then chunks of 64 short units (one lane each);
-// wave w takes items w, w + G, w + 2G, ... (G waves in the grid), so the long
-// chains start first and short work fills the machine beside them.  The item
-// index is wave-uniform by construction: no lane-0 ticket and broadcast,
-// which lets the compiler split the loop per lane.
-__global__ void __launch_bounds__(64) k_merge(EncodeArgs a) {
+// Merge of the short units: chunks of 64 units (one lane each), 17-32 bytes
+// first.  Wave w takes items w, w + G, w + 2G, ... (G waves in the grid).
+// The item index is wave-uniform by construction: no lane-0 ticket and
+// broadcast, which lets the compiler split the loop per lane.  Three waves
+// per SIMD: the register tiers fit in 168 VGPRs without spilling.
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge(EncodeArgs a) {
   if (a.ws.status->pad2) return;
   const Status *st = a.ws.status;
   const int lane = int(threadIdx.x);
-  const uint32_t nlw = st->n_lw, n32 = st->n_l32, n16 = st->n_l16;
-  const uint32_t e_lw = nlw, e_32 = e_lw + (n32 + 63) / 64, e_16 = e_32 + (n16 + 63) / 64;
+  const uint32_t n32 = st->n_l32, n16 = st->n_l16;
+  const uint32_t e_32 = (n32 + 63) / 64, e_16 = e_32 + (n16 + 63) / 64;
   for (uint32_t item = blockIdx.x; item < e_16; item += gridDim.x) {
-    if (item < e_lw) {
-      merge_wave(a, a.ws.lw[item], lane);
-    } else if (item < e_32) {
-      const uint32_t x = (item - e_lw) * 64 + uint32_t(lane);
+    if (item < e_32) {
+      const uint32_t x = item * 64 + uint32_t(lane);
       if (x < n32) merge_short_unit<32>(a, a.ws.l32[x]);
     } else {
       const uint32_t x = (item - e_32) * 64 + uint32_t(lane);
       if (x < n16) merge_short_unit<16>(a, a.ws.l16[x]);
+    }
+  }
+}
+
+// Merge of the units of 33..WAVE_MAX bytes, longest first.  Few units: one
+// wave each, positions per lane sized to the list's longest unit (their
+// chains are the critical path, and a wave shared by several units waits for
+// the slowest probe of all of them every round).  Many: 16 or 32 lanes per
+// unit, for throughput.  Runs beside k_merge (another stream).
+__global__ void __launch_bounds__(64) k_merge_group(EncodeArgs a) {
+  if (a.ws.status->pad2) return;
+  const Status *st = a.ws.status;
+  const int lane = int(threadIdx.x);
+  const uint32_t n64 = st->n_g64, n32g = st->n_g32, n16g = st->n_g16;
+  const bool pack = n64 + n32g + n16g > GROUP_PACK_MIN;
+  const uint32_t e64 = n64, e32g = e64 + (pack ? (n32g + 1) / 2 : n32g);
+  const uint32_t e16g = e32g + (pack ? (n16g + 3) / 4 : n16g);
+  for (uint32_t item = blockIdx.x; item < e16g; item += gridDim.x) {
+    if (item < e64) {
+      merge_group<64, 8>(a, a.ws.g64, n64, item, lane);
+    } else if (item < e32g) {
+      if (pack) merge_group<32, 8>(a, a.ws.g32, n32g, (item - e64) * 2, lane);
+      else merge_group<64, 4>(a, a.ws.g32, n32g, item - e64, lane);
+    } else {
+      if (pack) merge_group<16, 8>(a, a.ws.g16, n16g, (item - e32g) * 4, lane);
+      else merge_group<64, 2>(a, a.ws.g16, n16g, item - e32g, lane);
     }
   }
 }

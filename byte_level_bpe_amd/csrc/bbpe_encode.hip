@@ -21,7 +21,7 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 struct WsLayout {
   uint64_t status, tile_nchar, tile_lastchg, tile_charbase, tile_chgcarry, seg_local, seg_charstart,
       ss, spst, spc, ps, tile_fn, tile_carry, tile_np, piece_start, piece_cnt, piece_off,
-      tmp_ids, scan_part, l16, l32, lw, ll, lrank, lpart, lnl, lnr, lbits, lsel, lmin, ldirty, total;
+      tmp_ids, scan_part, l16, l32, g16, g32, g64, ll, lrank, lpart, lnl, lnr, lbits, lsel, lmin, ldirty, total;
   uint64_t n_words;
   uint32_t n_tiles;
 };
@@ -59,7 +59,9 @@ WsLayout layout_for(uint64_t n, uint32_t n_seg) {
   // units to merge have at least 2 / 17 / 33 / 513 bytes
   take(L.l16, 4 * (n / 2 + 1));
   take(L.l32, 4 * (n / 17 + 1));
-  take(L.lw, 4 * (n / 33 + 1));
+  take(L.g16, 4 * (n / 33 + 1));
+  take(L.g32, 4 * (n / 129 + 1));
+  take(L.g64, 4 * (n / 257 + 1));
   take(L.ll, 4 * (n / 513 + 1));
   take(L.lrank, 4 * (n + 1));
   take(L.lpart, 4 * (n + 1));
@@ -80,10 +82,11 @@ __global__ void k_init(EncodeArgs a) {
     s->n_pieces = 0;
     s->n_ids = 0;
     s->n_ll = 0;
-    s->n_lw = 0;
+    s->n_g16 = 0;
     s->n_l32 = 0;
     s->n_l16 = 0;
-    s->spare[0] = s->spare[1] = 0;
+    s->n_g32 = 0;
+    s->n_g64 = 0;
     s->n_chars = 0;
     s->err_seg = 0;
     // offsets must start at 0 and end at the text length (monotonicity is
@@ -133,11 +136,13 @@ __global__ void k_err_seg(EncodeArgs a) {
     if ((x) != hipSuccess) return BBPE_E_HIP;   \
   } while (0)
 
-// Launches kernels on one stream; with timing enabled on the handle, every
-// launch is bracketed by two events from the handle's pool.
+// Launches kernels on the caller's stream `st` (or, after use(), another);
+// with timing enabled on the handle, every launch is bracketed by two events
+// from the handle's pool.
 struct Launcher {
   bbpe_tokenizer *t;
   hipStream_t st;
+  hipStream_t cur = st;
   std::vector<std::pair<int, size_t>> recs;  // (kernel index, first event)
   size_t next = 0;
 
@@ -160,15 +165,16 @@ struct Launcher {
   template <typename K, typename... A>
   void operator()(const char *name, K kernel, dim3 grid, dim3 block, A... args) {
     const bool timed = t->timing;
-    if (timed) (void)hipEventRecord(event(next), st);
-    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+    if (timed) (void)hipEventRecord(event(next), cur);
+    hipLaunchKernelGGL(kernel, grid, block, 0, cur, args...);
     if (timed) {
-      (void)hipEventRecord(event(next + 1), st);
+      (void)hipEventRecord(event(next + 1), cur);
       recs.emplace_back(kernel_index(name), next);
       next += 2;
     }
   }
-  // after the stream has been synchronised
+  void use(hipStream_t s) { cur = s; }
+  // after the streams have been synchronised
   void collect() {
     for (auto &r : recs) {
       float ms = 0.f;
@@ -180,6 +186,24 @@ struct Launcher {
     recs.clear();
   }
 };
+
+// The handle's second stream and its fork/join events, created once.
+int ensure_aux(bbpe_tokenizer *t) {
+  if (t->aux_stream) return BBPE_OK;
+  hipStream_t s = nullptr;
+  hipEvent_t f = nullptr, j = nullptr;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return BBPE_E_HIP;
+  if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+    if (f) (void)hipEventDestroy(f);
+    (void)hipStreamDestroy(s);
+    return BBPE_E_HIP;
+  }
+  t->aux_stream = s;
+  t->ev_fork = f;
+  t->ev_join = j;
+  return BBPE_OK;
+}
 
 // Validates arguments and carves the workspace.
 int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t *d_seg_off,
@@ -224,7 +248,9 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
   a.ws.scan_part = reinterpret_cast<uint32_t *>(w + L.scan_part);
   a.ws.l16 = reinterpret_cast<uint32_t *>(w + L.l16);
   a.ws.l32 = reinterpret_cast<uint32_t *>(w + L.l32);
-  a.ws.lw = reinterpret_cast<uint32_t *>(w + L.lw);
+  a.ws.g16 = reinterpret_cast<uint32_t *>(w + L.g16);
+  a.ws.g32 = reinterpret_cast<uint32_t *>(w + L.g32);
+  a.ws.g64 = reinterpret_cast<uint32_t *>(w + L.g64);
   a.ws.ll = reinterpret_cast<uint32_t *>(w + L.ll);
   a.ws.lrank = reinterpret_cast<int32_t *>(w + L.lrank);
   a.ws.lpart = reinterpret_cast<int32_t *>(w + L.lpart);
@@ -290,6 +316,7 @@ int bbpe_upload_tables(bbpe_tokenizer *t, void *d_mem, uint64_t bytes, void *str
   const ImageLayout &L = t->layout;
   DevTables &d = t->dev;
   d.slots = reinterpret_cast<const Slot *>(b + L.slots);
+  d.ext = reinterpret_cast<const uint64_t *>(b + L.ext);
   d.blob = b + L.blob;
   d.pair = reinterpret_cast<const int32_t *>(b + L.pair);
   d.atom = reinterpret_cast<const int32_t *>(b + L.atom);
@@ -323,6 +350,8 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
   a.ids_cap = ids_cap;
   a.id_off = d_id_off;
   a.merge_units = 1;
+  rc = ensure_aux(t);
+  if (rc) return rc;
   Launcher go{t, reinterpret_cast<hipStream_t>(stream)};
   launch_front(go, a, L);
   const uint32_t seg_grid = std::min<uint32_t>(1024, (n_seg + 256) / 256);
@@ -331,10 +360,21 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
   } else {
     const uint32_t probe_grid = uint32_t(std::min<uint64_t>((n + 1023) / 1024, 16384));
     go("k_probe", k_probe, dim3(probe_grid), dim3(256), a);
+    // the group and long tiers (few units, long dependent chains) run on the
+    // second stream beside the short tier
+    hipStream_t aux = static_cast<hipStream_t>(t->aux_stream);
+    HIP_OK(hipEventRecord(static_cast<hipEvent_t>(t->ev_fork), go.st));
+    HIP_OK(hipStreamWaitEvent(aux, static_cast<hipEvent_t>(t->ev_fork), 0));
+    go.use(aux);
     const uint32_t long_grid = uint32_t(std::min<uint64_t>(n / 513 + 1, 2048));
     go("k_merge_long", k_merge_long, dim3(long_grid), dim3(64), a);
+    const uint32_t group_grid = uint32_t(std::min<uint64_t>(n / 33 + 1, 4096));
+    go("k_merge_group", k_merge_group, dim3(group_grid), dim3(64), a);
+    HIP_OK(hipEventRecord(static_cast<hipEvent_t>(t->ev_join), aux));
+    go.use(go.st);
     const uint32_t merge_grid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
     go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
+    HIP_OK(hipStreamWaitEvent(go.st, static_cast<hipEvent_t>(t->ev_join), 0));
     const uint32_t nscan = uint32_t((n + 1 + 4095) / 4096);
     go("k_scan_reduce", k_scan_reduce, dim3(nscan), dim3(256), a);
     go("k_scan_partials", k_scan_partials, dim3(1), dim3(1024), a);
@@ -395,6 +435,12 @@ void bbpe_free(bbpe_tokenizer *t) {
   if (!t) return;
   for (void *e : t->t_events)
     if (e) (void)hipEventDestroy(static_cast<hipEvent_t>(e));
+  if (t->aux_stream) {
+    (void)hipStreamSynchronize(static_cast<hipStream_t>(t->aux_stream));
+    (void)hipEventDestroy(static_cast<hipEvent_t>(t->ev_fork));
+    (void)hipEventDestroy(static_cast<hipEvent_t>(t->ev_join));
+    (void)hipStreamDestroy(static_cast<hipStream_t>(t->aux_stream));
+  }
   delete t;
 }
 

@@ -214,7 +214,11 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
       if (kk == 0) kk = 1;
       nr = rs + 25000ull * kk;                      // next run cut >= c
     }
-    uint64_t leads = m.lead;
+    // a run change only moves the next run cut later, so with no segment
+    // start in the word and both boundaries beyond its last character there
+    // is no cut here
+    const uint64_t c_end = c + uint64_t(__popcll(m.lead));
+    uint64_t leads = (segb == 0 && nw >= c_end && nr >= c_end) ? 0ull : m.lead;
     while (leads) {
       const int i = __ffsll(static_cast<unsigned long long>(leads)) - 1;
       leads &= leads - 1;
@@ -243,7 +247,18 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
   const uint64_t brk_next = shfl_down64(brk, 1);
 
   uint64_t sp_st = 0, sp_in = 0, sp_in_next = 0, ss_end = 0, ss_end_next = 0;
+  // does any segment overlapping this word allow specials?
+  bool any_allow = false;
   if (live && a.T.n_sp > 0 && m.valid) {
+    uint32_t s = seg_at;
+    any_allow = a.allow[s] != 0;
+    for (uint64_t sb = segb; sb && !any_allow; sb &= sb - 1) {
+      const uint64_t p = uint64_t(base) + uint64_t(__ffsll(static_cast<unsigned long long>(sb)) - 1);
+      while (s + 1 < a.n_seg && a.seg_off[s + 1] <= p) ++s;
+      any_allow = a.allow[s] != 0;
+    }
+  }
+  if (any_allow) {
     uint32_t s = seg_at;
     uint64_t cand = m.lead;
     while (cand) {

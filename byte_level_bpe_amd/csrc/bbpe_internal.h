@@ -25,6 +25,8 @@ enum CharClass : uint8_t {
 //          own bytes yields exactly this key), bits 9-31 offset of the key in
 //          the key blob
 //   rank : the id, or -1 for an empty slot
+// A parallel array holds key bytes 8..15, so keys of up to 16 bytes compare
+// without reading the blob.
 // ---------------------------------------------------------------------------
 struct Slot {
   uint64_t k8;
@@ -57,6 +59,7 @@ BBPE_HD uint64_t hash_step(uint64_t h, uint64_t w) { return fmix64(h ^ w); }
 // ---------------------------------------------------------------------------
 struct DevTables {
   const Slot *slots;
+  const uint64_t *ext;      // [slots] key bytes 8..15 of each slot's key, zero padded
   const uint8_t *blob;
   const int32_t *pair;      // [65536] rank of the 2-byte key (a,b) at a*256+b, or RANK_NONE
   const int32_t *atom;      // [256] rank of each single byte
@@ -75,7 +78,7 @@ struct DevTables {
 
 // Byte offsets of each table inside the uploaded image.
 struct ImageLayout {
-  uint64_t slots, blob, pair, atom, uni1, uni2, sp_bytes, sp_off, sp_id, inner, total;
+  uint64_t slots, ext, blob, pair, atom, uni1, uni2, sp_bytes, sp_off, sp_id, inner, total;
   uint32_t n_slots;
 };
 
@@ -93,13 +96,14 @@ struct Status {
   unsigned long long n_pieces;
   unsigned long long n_ids;
   unsigned int n_ll;              // units to merge, longer than one wave holds
-  unsigned int n_lw;              // ... that one wave holds in registers
+  unsigned int n_g16;             // ... of 33-128 bytes
   unsigned long long n_chars;
   unsigned int err_seg;           // segment of err_pos
   unsigned int pad2;              // nonzero: invalid segment offsets, every kernel exits
   unsigned int n_l32;             // ... of 17-32 bytes
   unsigned int n_l16;             // ... of 2-16 bytes
-  unsigned int spare[2];
+  unsigned int n_g32;             // ... of 129-256 bytes
+  unsigned int n_g64;             // ... of 257-512 bytes
 };
 
 }  // namespace bbpe

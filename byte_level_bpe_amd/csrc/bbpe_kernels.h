@@ -28,7 +28,7 @@ struct WsPtrs {
   uint32_t *piece_off;              // [P+1] exclusive scan of the ids per unit
   int32_t *tmp_ids;                 // [N] ids of each piece, at the piece's byte offset
   uint32_t *scan_part;              // [N/4096+2] partial sums of the piece scan
-  uint32_t *l16, *l32, *lw, *ll;    // units to merge, by length
+  uint32_t *l16, *l32, *g16, *g32, *g64, *ll;  // units to merge, by length
   // long tier, per text position: pair rank at each part start, id of the
   // part starting there, and the two created-pair ranks of a batch merge
   int32_t *lrank, *lpart, *lnl, *lnr;
@@ -70,6 +70,7 @@ __global__ void k_pieces(EncodeArgs a);
 __global__ void k_probe(EncodeArgs a);
 __global__ void k_merge(EncodeArgs a);
 __global__ void k_merge_long(EncodeArgs a);
+__global__ void k_merge_group(EncodeArgs a);
 __global__ void k_scan_reduce(EncodeArgs a);
 __global__ void k_scan_partials(EncodeArgs a);
 __global__ void k_scan_down(EncodeArgs a);

@@ -165,6 +165,7 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
   ImageLayout L{};
   uint64_t o = 0;
   L.slots = o; o = align256(o + uint64_t(n_slots) * sizeof(Slot));
+  L.ext = o; o = align256(o + uint64_t(n_slots) * 8);
   L.blob = o; o = align256(o + blob_bytes + 16);
   L.pair = o; o = align256(o + 65536 * 4);
   L.atom = o; o = align256(o + 256 * 4);
@@ -181,6 +182,7 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
   uint8_t *img = t->image.data();
 
   Slot *slots = reinterpret_cast<Slot *>(img + L.slots);
+  uint64_t *ext = reinterpret_cast<uint64_t *>(img + L.ext);
   for (uint32_t i = 0; i < n_slots; ++i) slots[i] = Slot{0, 0, -1};
   uint8_t *blob = img + L.blob;
   uint64_t boff = 0;
@@ -189,8 +191,9 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
     const std::string &k = keys[i];
     const uint8_t *kp = reinterpret_cast<const uint8_t *>(k.data());
     memcpy(blob + boff, kp, k.size());
-    uint64_t k8 = 0;
+    uint64_t k8 = 0, k8b = 0;
     for (size_t j = 0; j < k.size() && j < 8; ++j) k8 |= uint64_t(kp[j]) << (8 * j);
+    for (size_t j = 8; j < k.size() && j < 16; ++j) k8b |= uint64_t(kp[j]) << (8 * (j - 8));
     bool self = self_consistent(k, rk[i], ranks);
     n_self += self;
     uint32_t meta = uint32_t(k.size()) | (self ? bbpe::META_SELF : 0u) |
@@ -199,6 +202,7 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
     uint32_t idx = uint32_t(h) & (n_slots - 1);
     while (slots[idx].rank >= 0) idx = (idx + 1) & (n_slots - 1);
     slots[idx] = Slot{k8, meta, rk[i]};
+    ext[idx] = k8b;
     boff += k.size();
   }
   t->n_self_consistent = n_self;

@@ -34,6 +34,11 @@ struct bbpe_tokenizer {
   std::vector<double> t_ms;
   std::vector<uint64_t> t_launches;
   std::vector<void *> t_events;  // hipEvent_t pool, two per launch
+  // second stream for merge tiers that run beside the short tier, and the
+  // two events that fork it from and join it back to the caller's stream
+  // (created at the first encode, on the device current then)
+  void *aux_stream = nullptr;
+  void *ev_fork = nullptr, *ev_join = nullptr;
   // last UTF-8 error
   uint32_t err_seg = 0;
   uint64_t err_byte = 0;

@@ -247,6 +247,27 @@ def test_long_pieces_tiny_table(tiny):
     assert_ids(tok, orc, segs, what="long pieces")
 
 
+def test_group_tier_units_main_table():
+    """Units of 33-512 bytes with the 100,256-rank table: a few hundred (one
+    wave per unit) and over 4,096 (several units share a wave), so both
+    launch shapes of the group tier run."""
+    from synth import configs
+    w = configs.main()
+    tok, orc = make(w.tokens, w.specials, w.grammar)
+    rng = np.random.default_rng(33)
+    common, rare = b"etaoinshrdlc", b"umwfgypbvkjxqz"
+    for nw in (300, 4500):
+        words = []
+        for i in range(nw):
+            L = int(rng.integers(33, 513)) if i % 7 else int(rng.integers(33, 140))
+            pick = rng.random(L) < 0.8
+            words.append(b" " + bytes(common[x % 12] if c else rare[x % 14]
+                                      for x, c in zip(rng.integers(0, 1 << 16, L), pick)))
+        segs = [(b"".join(words[:nw // 2]), False), (b"".join(words[nw // 2:]), False)]
+        say("group tier units", nw)
+        assert_ids(tok, orc, segs, safe=True, what="group tier %d units" % nw)
+
+
 def test_long_units_adversarial_tables():
     """Units over 512 bytes (the batched long tier) under random tables over
     {a, b}: keys of 2-6 bytes with random ranks, so that merges of equal rank
