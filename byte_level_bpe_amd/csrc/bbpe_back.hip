@@ -5,6 +5,9 @@
 // pairs; repeatedly merge the lowest (leftmost on ties); recompute only the
 // two pairs that touch the merged part.  A merged part's id is the rank that
 // merged it; a part never merged is a single byte with its atom's rank.
+// Every part is a key, so after the first round (byte pairs, from the
+// 256x256 pair table) each recomputed pair is looked up by the two part ids
+// in the merge table: one bucket load, no key bytes.
 //
 // k_probe (one thread per unit) settles specials, single bytes and units
 // that are keys whose own merges rebuild them; the units left are listed by
@@ -128,6 +131,75 @@ __device__ __forceinline__ int32_t lookup_text(const DevTables &T, const uint8_t
   });
 }
 
+// ---------------------------------------------------------------------------
+// Merge table lookups: the rank of bytes(a) + bytes(b) for part ids a, b.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void mt_load(const DevTables &T, uint32_t b, uint64_t (&e)[MT_BUCKET]) {
+  const ulonglong2 *q = reinterpret_cast<const ulonglong2 *>(T.mt + uint64_t(b) * MT_BUCKET);
+#pragma unroll
+  for (uint32_t k = 0; k < MT_BUCKET / 2; ++k) {
+    const ulonglong2 v = q[k];
+    e[2 * k] = v.x;
+    e[2 * k + 1] = v.y;
+  }
+}
+
+// rank in the bucket, or RANK_NONE; `more` when the bucket is full without it
+__device__ __forceinline__ int32_t mt_find(const uint64_t (&e)[MT_BUCKET], uint64_t want, bool &more) {
+  int32_t r = RANK_NONE;
+  bool full = true;
+#pragma unroll
+  for (uint32_t k = 0; k < MT_BUCKET; ++k) {
+    r = (e[k] >> MT_ID_BITS) == want ? int32_t(e[k] & MT_ID_MASK) : r;
+    full = full && (e[k] >> 63);
+  }
+  more = full && r == RANK_NONE;
+  return r;
+}
+
+// the buckets after a full one
+__device__ __attribute__((noinline)) int32_t mt_rest(const DevTables &T, uint32_t b, uint64_t want) {
+  for (;;) {
+    b = (b + 1) & T.mt_mask;
+    uint64_t e[MT_BUCKET];
+    mt_load(T, b, e);
+    bool more;
+    const int32_t r = mt_find(e, want, more);
+    if (!more) return r;
+  }
+}
+
+__device__ __forceinline__ int32_t merge_rank(const DevTables &T, uint32_t a, uint32_t b) {
+  const uint64_t k = mt_key(a, b);
+  const uint32_t x = mt_bucket(k, T.mt_shift);
+  const uint64_t want = (uint64_t(1) << (2 * MT_ID_BITS)) | k;
+  uint64_t e[MT_BUCKET];
+  mt_load(T, x, e);
+  bool more;
+  const int32_t r = mt_find(e, want, more);
+  return more ? mt_rest(T, x, want) : r;
+}
+
+// two lookups (v1 / v2: wanted) with both buckets loaded before either is used
+__device__ __forceinline__ void merge_rank2(const DevTables &T, bool v1, uint32_t a1, uint32_t b1,
+                                            bool v2, uint32_t a2, uint32_t b2, int32_t &r1,
+                                            int32_t &r2) {
+  const uint64_t k1 = mt_key(a1, b1), k2 = mt_key(a2, b2);
+  const uint32_t x1 = mt_bucket(k1, T.mt_shift), x2 = mt_bucket(k2, T.mt_shift);
+  const uint64_t w1 = (uint64_t(1) << (2 * MT_ID_BITS)) | k1;
+  const uint64_t w2 = (uint64_t(1) << (2 * MT_ID_BITS)) | k2;
+  uint64_t e1[MT_BUCKET] = {}, e2[MT_BUCKET] = {};
+  if (v1) mt_load(T, x1, e1);
+  if (v2) mt_load(T, x2, e2);
+  bool m1, m2;
+  r1 = mt_find(e1, w1, m1);
+  r2 = mt_find(e2, w2, m2);
+  if (v1 && m1) r1 = mt_rest(T, x1, w1);
+  if (v2 && m2) r2 = mt_rest(T, x2, w2);
+  if (!v1) r1 = RANK_NONE;
+  if (!v2) r2 = RANK_NONE;
+}
+
 // id of the special whose string is p[0..len)
 __device__ __forceinline__ int32_t special_id(const DevTables &T, const uint8_t *p, uint32_t len) {
   for (uint32_t k = 0; k < T.n_sp; ++k) {
@@ -224,42 +296,6 @@ __device__ __forceinline__ bool unit_rest_eq(const UnitBytes<SK> &u, uint32_t a,
   return true;
 }
 
-// Ranks of two keys of the unit, [a1, a1+l1) and [a2, a2+l2) (len 0 = none),
-// with the first probes of both issued together.
-template <int SK>
-__device__ __forceinline__ void unit_lookup2(const DevTables &T, const UnitBytes<SK> &u, uint32_t a1,
-                                             uint32_t l1, uint32_t a2, uint32_t l2, int32_t &r1,
-                                             int32_t &r2) {
-  const bool v1 = l1 > 0 && l1 <= T.max_key_len, v2 = l2 > 0 && l2 <= T.max_key_len;
-  uint64_t h1 = 0, k1 = 0, x1 = 0, h2 = 0, k2 = 0, x2 = 0;
-  if (v1) unit_hash(u, a1, l1, h1, k1, x1);
-  if (v2) unit_hash(u, a2, l2, h2, k2, x2);
-  const uint32_t i1 = uint32_t(h1) & T.slot_mask, i2 = uint32_t(h2) & T.slot_mask;
-  Slot s1{0, 0, -1}, s2{0, 0, -1};
-  uint64_t e1 = 0, e2 = 0;
-  if (v1) { s1 = T.slots[i1]; e1 = T.ext[i1]; }
-  if (v2) { s2 = T.slots[i2]; e2 = T.ext[i2]; }
-  uint32_t meta;
-  r1 = RANK_NONE;
-  r2 = RANK_NONE;
-  if (v1 && s1.rank >= 0) {
-    if (slot_match(T, s1, e1, k1, x1, l1) &&
-        (l1 <= 16 || unit_rest_eq(u, a1, l1, T.blob + (s1.meta >> META_OFF_SHIFT))))
-      r1 = s1.rank;
-    else
-      r1 = probe(T, h1 + 1, k1, x1, l1, meta,
-                 [&](const uint8_t *b) __attribute__((always_inline)) { return unit_rest_eq(u, a1, l1, b); });
-  }
-  if (v2 && s2.rank >= 0) {
-    if (slot_match(T, s2, e2, k2, x2, l2) &&
-        (l2 <= 16 || unit_rest_eq(u, a2, l2, T.blob + (s2.meta >> META_OFF_SHIFT))))
-      r2 = s2.rank;
-    else
-      r2 = probe(T, h2 + 1, k2, x2, l2, meta,
-                 [&](const uint8_t *b) __attribute__((always_inline)) { return unit_rest_eq(u, a2, l2, b); });
-  }
-}
-
 __device__ __forceinline__ uint32_t above32(int j) { return ~((2u << j) - 1u); }
 
 // Merge a unit of 2 <= m <= SK bytes held in registers: pair ranks r[j] and
@@ -290,13 +326,18 @@ __device__ __forceinline__ uint32_t merge_short(const DevTables &T, const UnitBy
     bnd &= ~(1u << k);
     const uint32_t after = bnd & above32(bj);
     const uint32_t k2 = after ? uint32_t(__ffs(after) - 1) : m;  // end of the merged part
-    const uint32_t rest = after & (after - 1);
-    const uint32_t end2 = rest ? uint32_t(__ffs(rest) - 1) : m;
     const uint32_t before = bnd & ((1u << bj) - 1u);
     const int q = before ? 31 - __clz(before) : -1;
+    // the merged part (id best) with its right and left neighbours
+    int32_t id2 = 0, idq = 0;
+#pragma unroll
+    for (int j = 0; j < SK; ++j) {
+      id2 = uint32_t(j) == k2 ? pr[j] : id2;
+      idq = j == q ? pr[j] : idq;
+    }
     int32_t nb, nq;
-    unit_lookup2(T, u, uint32_t(bj), after ? end2 - uint32_t(bj) : 0u, uint32_t(q < 0 ? 0 : q),
-                 q >= 0 ? k2 - uint32_t(q) : 0u, nb, nq);
+    merge_rank2(T, after != 0, uint32_t(best), uint32_t(id2), q >= 0, uint32_t(idq), uint32_t(best),
+                nb, nq);
 #pragma unroll
     for (int j = 0; j < SK; ++j) {
       r[j] = (j == k) ? RANK_NONE : r[j];
@@ -499,24 +540,28 @@ __device__ void merge_group(const EncodeArgs &a, const uint32_t *list, uint32_t 
       const uint64_t gb = (bal >> (g * G)) & A.full;
       bj = gb ? G * uint32_t(t) + uint32_t(__ffsll(static_cast<unsigned long long>(gb)) - 1) : bj;
     }
-    uint32_t k = m, k2 = m, end2 = m;
+    uint32_t k = m, k2 = m;
     int q = -1;
     if (act) {
       k = A.next(bj + 1, m);   // the part merged into bj
       k2 = A.next(k + 1, m);   // end of the merged part
-      end2 = k2 < m ? A.next(k2 + 1, m) : m;
       q = A.prev(bj);
     }
-    // group lane 0: the merged part with its right neighbour; lane 1: the
-    // left neighbour with the merged part
-    uint32_t ks = 0, kl = 0;
-    if (act && gl == 0 && k2 < m) { ks = bj; kl = end2 - bj; }
-    if (act && gl == 1 && q >= 0) { ks = uint32_t(q); kl = k2 - uint32_t(q); }
-    int32_t rv = RANK_NONE;
-    if (kl) {
-      uint32_t meta;
-      rv = lookup_text(T, p + ks, kl, meta);
+    // ids of the parts starting at k2 and q, read from the lanes holding them
+    const uint32_t uq = uint32_t(q);
+    int32_t v2 = 0, vq = 0;
+#pragma unroll
+    for (uint32_t t = 0; t < P; ++t) {
+      v2 = k2 / G == t ? pr[t] : v2;
+      vq = uq / G == t ? pr[t] : vq;
     }
+    const int32_t id2 = __shfl(v2, int(g * G + k2 % G), 64);
+    const int32_t idq = __shfl(vq, int(g * G + uq % G), 64);
+    // group lane 0: the merged part (id best) with its right neighbour; lane
+    // 1: the left neighbour with the merged part
+    int32_t rv = RANK_NONE;
+    if (act && gl == 0 && k2 < m) rv = merge_rank(T, uint32_t(best), uint32_t(id2));
+    if (act && gl == 1 && q >= 0) rv = merge_rank(T, uint32_t(idq), uint32_t(best));
     const int32_t nb = __shfl(rv, int(g * G), 64), nq = __shfl(rv, int(g * G + 1), 64);
     if (act) {
 #pragma unroll
@@ -716,16 +761,18 @@ __device__ void merge_long(const EncodeArgs &a, uint32_t i, int lane) {
         S &= S - 1;
         const uint32_t k = U.next(j + 1);
         const uint32_t k2 = U.next(k + 1);
-        const uint32_t k3 = k2 < m ? U.next(k2 + 1) : m;
         const int y = U.prev(j);
         int pf = y;
         if (y >= 0) {
           const int z = U.prev(uint32_t(y));
           if (z >= 0 && U.chosen(uint32_t(z))) pf = z;  // y merged into z
         }
-        uint32_t meta;
-        const int32_t nl = pf >= 0 ? lookup_text(T, p + pf, k2 - uint32_t(pf), meta) : RANK_NONE;
-        const int32_t nr = k2 < m ? lookup_text(T, p + j, k3 - j, meta) : RANK_NONE;
+        // the merged part (id R) with its neighbours; a left neighbour that
+        // merges in this batch too has id R as well
+        const uint32_t lid = pf >= 0 ? (pf != y ? uint32_t(R) : uint32_t(U.part(uint32_t(pf)))) : 0u;
+        const uint32_t rid = k2 < m ? uint32_t(U.part(k2)) : 0u;
+        int32_t nl, nr;
+        merge_rank2(T, pf >= 0, lid, uint32_t(R), k2 < m, uint32_t(R), rid, nl, nr);
         a.ws.lnl[s + j] = nl;
         a.ws.lnr[s + j] = nr;
         if (nl <= R || nr <= R) stop = min(stop, j);

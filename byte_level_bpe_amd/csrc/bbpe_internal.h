@@ -55,6 +55,23 @@ BBPE_HD uint64_t hash_seed(uint32_t len) { return (uint64_t(len) + 1) * 0x9E3779
 BBPE_HD uint64_t hash_step(uint64_t h, uint64_t w) { return fmix64(h ^ w); }
 
 // ---------------------------------------------------------------------------
+// Merge table: the rank of the key bytes(A) + bytes(B) for every pair of
+// keys (A, B) whose concatenation is a key, i.e. every split of a key into
+// two keys.  The parts of a piece are always keys, so every lookup the merge
+// loop makes after its first round is a lookup of such a pair, and it is
+// answered from the two part ids alone.  64-byte buckets of 8 entries:
+//   bit 63 valid | A << 42 | B << 21 | rank      (ids and ranks < 2^21)
+// A key hashes to one bucket; a full bucket continues into the next one.
+// ---------------------------------------------------------------------------
+constexpr uint32_t MT_ID_BITS = 21;
+constexpr uint32_t MT_ID_MASK = (1u << MT_ID_BITS) - 1;
+constexpr uint32_t MT_BUCKET = 8;
+BBPE_HD uint64_t mt_key(uint32_t a, uint32_t b) { return (uint64_t(a) << MT_ID_BITS) | b; }
+BBPE_HD uint32_t mt_bucket(uint64_t key, uint32_t shift) {
+  return uint32_t((key * 0x9E3779B97F4A7C15ull) >> shift);
+}
+
+// ---------------------------------------------------------------------------
 // Device view of the uploaded tables (passed to kernels by value).
 // ---------------------------------------------------------------------------
 struct DevTables {
@@ -69,6 +86,9 @@ struct DevTables {
   const uint32_t *sp_off;   // [n_sp+1]
   const int32_t *sp_id;     // [n_sp]
   const uint32_t *inner;    // [2048] bit (a*256+b): the byte pair (a,b) occurs inside some key
+  const uint64_t *mt;       // merge table, [mt_mask+1] buckets of MT_BUCKET entries
+  uint32_t mt_mask;
+  uint32_t mt_shift;        // 64 - log2(buckets)
   uint32_t slot_mask;
   uint32_t n_sp;
   uint32_t sp_first[8];     // bitmap of first bytes of specials
@@ -78,8 +98,9 @@ struct DevTables {
 
 // Byte offsets of each table inside the uploaded image.
 struct ImageLayout {
-  uint64_t slots, ext, blob, pair, atom, uni1, uni2, sp_bytes, sp_off, sp_id, inner, total;
+  uint64_t slots, ext, blob, pair, atom, uni1, uni2, sp_bytes, sp_off, sp_id, inner, mt, total;
   uint32_t n_slots;
+  uint32_t n_mt_buckets;
 };
 
 // ---------------------------------------------------------------------------

@@ -113,7 +113,9 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
   int32_t max_id = -1;
   uint32_t max_len = 0;
   for (uint32_t i = 0; i < n; ++i) {
-    if (keys[i].empty() || keys[i].size() > BBPE_MAX_KEY_BYTES || rk[i] < 0) return BBPE_E_TABLE;
+    if (keys[i].empty() || keys[i].size() > BBPE_MAX_KEY_BYTES || rk[i] < 0 ||
+        rk[i] > int32_t(BBPE_MAX_RANK))
+      return BBPE_E_TABLE;
     if (!ranks.emplace(keys[i], rk[i]).second || !seen.insert(rk[i]).second) return BBPE_E_TABLE;
     max_id = std::max(max_id, rk[i]);
     max_len = std::max<uint32_t>(max_len, uint32_t(keys[i].size()));
@@ -154,6 +156,23 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
   for (uint32_t i = 0; i < n; ++i) add_dec(keys[i], rk[i]);
   for (size_t i = 0; i < sp.size(); ++i) add_dec(sp[i], spid[i]);
 
+  // merge table entries: every split of a key into two keys
+  std::vector<uint64_t> mt_entries;
+  for (uint32_t i = 0; i < n; ++i) {
+    const std::string &k = keys[i];
+    for (size_t c = 1; c < k.size(); ++c) {
+      auto l = ranks.find(k.substr(0, c));
+      if (l == ranks.end()) continue;
+      auto r = ranks.find(k.substr(c));
+      if (r == ranks.end()) continue;
+      mt_entries.push_back((uint64_t(1) << 63) |
+                           (bbpe::mt_key(uint32_t(l->second), uint32_t(r->second)) << bbpe::MT_ID_BITS) |
+                           uint64_t(rk[i]));
+    }
+  }
+  uint32_t n_mt = 64, mt_log = 6;  // about 3 entries per bucket of 8
+  while (uint64_t(n_mt) * 3 < mt_entries.size()) n_mt <<= 1, ++mt_log;
+
   // image layout
   uint32_t n_slots = 1024;
   while (n_slots < 2 * n) n_slots <<= 1;
@@ -175,8 +194,10 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
   L.sp_bytes = o; o = align256(o + sp_bytes + 16);
   L.sp_off = o; o = align256(o + 4 * (sp.size() + 1));
   L.sp_id = o; o = align256(o + 4 * (sp.size() + 1));
+  L.mt = o; o = align256(o + uint64_t(n_mt) * bbpe::MT_BUCKET * 8);
   L.total = o;
   L.n_slots = n_slots;
+  L.n_mt_buckets = n_mt;
   t->layout = L;
   t->image.assign(L.total, 0);
   uint8_t *img = t->image.data();
@@ -237,10 +258,27 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
     spi[i] = spid[i];
   }
   spo[sp.size()] = so;
+  uint64_t *mt = reinterpret_cast<uint64_t *>(img + L.mt);
+  for (uint64_t e : mt_entries) {
+    const uint64_t key = (e >> bbpe::MT_ID_BITS) & ((uint64_t(1) << (2 * bbpe::MT_ID_BITS)) - 1);
+    uint32_t b = bbpe::mt_bucket(key, 64 - mt_log);
+    for (;;) {
+      uint64_t *bk = mt + uint64_t(b) * bbpe::MT_BUCKET;
+      uint32_t j = 0;
+      while (j < bbpe::MT_BUCKET && (bk[j] >> 63)) ++j;
+      if (j < bbpe::MT_BUCKET) {
+        bk[j] = e;
+        break;
+      }
+      b = (b + 1) & (n_mt - 1);
+    }
+  }
 
   bbpe::DevTables &d = t->dev;
   d = bbpe::DevTables{};
   d.slot_mask = n_slots - 1;
+  d.mt_mask = n_mt - 1;
+  d.mt_shift = 64 - mt_log;
   d.n_sp = uint32_t(sp.size());
   for (auto &s : sp) d.sp_first[uint8_t(s[0]) >> 5] |= 1u << (uint8_t(s[0]) & 31);
   d.grammar = t->grammar;

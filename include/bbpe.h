@@ -72,17 +72,20 @@ enum {
 /* Limits of this implementation. */
 #define BBPE_MAX_KEY_BYTES 128u      /* longest mergeable key (tiktoken deep-dive, "The byte floor") */
 #define BBPE_MAX_SPECIALS 1024u
+#define BBPE_MAX_RANK 2097151u       /* largest rank of a key, 2^21 - 1 (the merge
+                                        table packs two ids and a rank in 64 bits;
+                                        specials may use any id below 2^31) */
 #define BBPE_MAX_SPECIAL_BYTES 64u   /* longest special-token string */
 
 /* Build a tokenizer from a ranks table held in host memory.
  *
  *   key_bytes, key_off[n+1]: key i is key_bytes[key_off[i] .. key_off[i+1]);
- *   ranks[n]:                its rank (= token id), 0 <= rank < 2^31;
+ *   ranks[n]:                its rank (= token id), 0 <= rank <= BBPE_MAX_RANK;
  *   special_bytes, special_off[ns+1], special_ids[ns]: special tokens;
  *   grammar:                 BBPE_GRAMMAR_*.
  *
  * Rejected with BBPE_E_TABLE: n == 0, an empty key, a key longer than
- * BBPE_MAX_KEY_BYTES, a duplicate key or rank, a negative rank, or a missing
+ * BBPE_MAX_KEY_BYTES, a duplicate key or rank, a rank outside [0, BBPE_MAX_RANK], or a missing
  * single-byte key (all 256 must be present).  Rejected with BBPE_E_SPECIAL:
  * more than BBPE_MAX_SPECIALS specials, an empty special, one longer than
  * BBPE_MAX_SPECIAL_BYTES, one that is not valid UTF-8, a duplicate string or

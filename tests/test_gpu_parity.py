@@ -268,6 +268,23 @@ def test_group_tier_units_main_table():
         assert_ids(tok, orc, segs, safe=True, what="group tier %d units" % nw)
 
 
+def test_ranks_at_the_top_of_the_range():
+    """Keys whose ranks sit just below 2^21 (the merge table's 21-bit id
+    fields), merged through all three merge tiers."""
+    import itertools
+    r = random.Random(21)
+    tab = {bytes([b]): 2097151 - 300 + i for i, b in enumerate(r.sample(range(256), 256))}
+    keys = [bytes(k) for L in range(2, 6) for k in itertools.product(b"abc", repeat=L)]
+    r.shuffle(keys)
+    for k, rk in zip(keys[:120], r.sample(range(2097151 - 40000, 2097151 - 300), 120)):
+        tab[k] = rk
+    tab[b"ab"] = 2097151
+    tok, orc = make(tab, [], 0)
+    segs = [(bytes(r.choice(b"abc") for _ in range(n)), False) for n in (5, 20, 31, 100, 400, 2000)]
+    say("ranks near 2^21")
+    assert_ids(tok, orc, segs, safe=False, what="ranks near 2^21")
+
+
 def test_long_units_adversarial_tables():
     """Units over 512 bytes (the batched long tier) under random tables over
     {a, b}: keys of 2-6 bytes with random ranks, so that merges of equal rank

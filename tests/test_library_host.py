@@ -55,6 +55,14 @@ def test_table_validation():
     with pytest.raises(B.BBPEError) as e:
         B.load_ranks(long_key)
     assert e.value.status == B.E_TABLE
+    # ranks up to 2^21 - 1 are accepted (the merge table packs them in 21 bits)
+    big = dict(t)
+    big[b"xy"] = 2097151
+    B.load_ranks(big, [(b"<|s|>", 2**31 - 1)])
+    big[b"xy"] = 2097152
+    with pytest.raises(B.BBPEError) as e:
+        B.load_ranks(big)
+    assert e.value.status == B.E_TABLE
     for specials in ([(b"<|a|>", 7)], [(b"<|a", 300), (b"<|a|>", 301)], [(b"", 300)],
                      [(b"\xff", 300)], [(b"abab", 300)], [(b"ab", 300), (b"ba", 301)],
                      [(b"<|x|>", 300), (b"<|x|>", 301)], [(b"x" * 65, 300)]):
