@@ -4,7 +4,9 @@
 // words (the high bit of each byte lane carries the result), so the common
 // all-ASCII word needs no per-byte branches.  Bytes >= 0x80 are handled by a
 // slow path that decodes only the multi-byte characters, reading their bytes
-// from the text, validates UTF-8 and looks up the code point's class.
+// from the text, validates UTF-8 and looks up the code point's class, eight
+// characters at a time so that their loads overlap; its result is stored
+// per word and read back by later passes over the same text.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -64,23 +66,132 @@ __device__ __forceinline__ uint32_t decode_text(const uint8_t *__restrict__ text
   return cp;
 }
 
-// Set the class bits of one multi-byte character occupying bits `bits`.
-// (selects rather than branches, so that the masks stay in registers)
-__device__ __forceinline__ void add_class(WordMasks &m, uint32_t cls, uint64_t bits) {
-  m.LU |= (cls == CC_LU) ? bits : 0;
-  m.LL |= (cls == CC_LL) ? bits : 0;
-  m.LB |= (cls == CC_LO) ? bits : 0;
-  m.N |= (cls == CC_N) ? bits : 0;
-  m.WS |= (cls == CC_WS) ? bits : 0;
-  m.M |= (cls == CC_M) ? bits : 0;
+// What the multi-byte characters of a word add to its masks.  Computed once
+// per call (by the first front-end kernel, which stores it for every word
+// holding a byte >= 0x80) and read back by the later ones.
+struct SlowMasks {
+  uint64_t LU, LL, LB, N, WS, M, lead, ls0, ls1, err;
+};
+
+__device__ __forceinline__ void add_class(SlowMasks &r, uint32_t cls, uint64_t bits) {
+  r.LU |= (cls == CC_LU) ? bits : 0;
+  r.LL |= (cls == CC_LL) ? bits : 0;
+  r.LB |= (cls == CC_LO) ? bits : 0;
+  r.N |= (cls == CC_N) ? bits : 0;
+  r.WS |= (cls == CC_WS) ? bits : 0;
+  r.M |= (cls == CC_M) ? bits : 0;
+}
+
+// byte p of the text, 0 outside it (the load is issued either way)
+__device__ __forceinline__ uint32_t text_byte(const uint8_t *__restrict__ text, uint64_t n, int64_t p) {
+  const bool in = p >= 0 && uint64_t(p) < n;
+  const uint32_t v = text[in ? p : 0];
+  return in ? v : 0u;
+}
+
+// The multi-byte characters of the word at base: `hi2` marks its bytes >=
+// 0xC0, `non` its bytes >= 0x80.  Leads are decoded eight at a time with all
+// their byte loads, then all their class-table loads, issued together.
+__device__ __forceinline__ void classify_slow(const DevTables &T, const uint8_t *__restrict__ text,
+                                              const Window &win, int64_t base, uint64_t n,
+                                              uint64_t seg_lo, uint64_t seg_hi, uint64_t hi2,
+                                              uint64_t non, uint64_t valid, SlowMasks &r) {
+  r = SlowMasks{0, 0, 0, 0, 0, 0, 0, 0, 0, 64};
+  uint64_t covered = 0;
+  uint32_t err = 64;
+  // a character that began up to three bytes before the word
+  if (!(hi2 & 1) && (non & 1)) {
+    int kf = 0;
+    if ((win.at(-1) & 0xC0u) != 0x80u) kf = 1;
+    else if ((win.at(-2) & 0xC0u) != 0x80u) kf = 2;
+    else if ((win.at(-3) & 0xC0u) != 0x80u) kf = 3;
+    if (kf > 0 && base - kf >= 0) {
+      int len;
+      bool ok;
+      const uint32_t cp = decode_text(text, n, base, -kf, seg_lo, seg_hi, len, ok);
+      if (ok && len > kf) {
+        const uint64_t bits = bit_range(0, len - kf);
+        covered |= bits;
+        add_class(r, class_of(T, cp), bits);
+        if (cp == 0x17F) r.ls1 |= 1;  // its second byte
+      }
+    }
+  }
+  // invalid lead bytes (C0, C1, F5..FF) are >= 0xC0 too and fail to decode
+  uint64_t leads = hi2 & valid;
+  uint64_t lead = 0;
+  while (leads) {
+    constexpr int K = 8;
+    int ii[K];
+    uint32_t b[K][4];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      ii[k] = __ffsll(static_cast<unsigned long long>(leads)) - 1;  // -1 once none are left
+      leads &= leads - 1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[k][j] = text_byte(text, n, base + ii[k] + j);
+    }
+    uint32_t cp[K], blk[K];
+    int len[K];
+    bool ok[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int i = ii[k];
+      len[k] = utf8_len(b[k][0]);
+      uint32_t c = b[k][0] & (0x7Fu >> len[k]);
+      bool good = i >= 0 && len[k] >= 2;
+#pragma unroll
+      for (int j = 1; j < 4; ++j) {
+        const bool in = j < len[k];
+        good = good && (!in || (((b[k][j] & 0xC0u) == 0x80u) && !seg_start_at(seg_lo, seg_hi, i + j)));
+        c = in ? ((c << 6) | (b[k][j] & 0x3Fu)) : c;
+      }
+      if (len[k] == 3 && c < 0x800) good = false;
+      if (len[k] == 4 && (c < 0x10000 || c > 0x10FFFF)) good = false;
+      if (c >= 0xD800 && c <= 0xDFFF) good = false;
+      cp[k] = c;
+      ok[k] = good;
+      blk[k] = good ? T.uni1[c >> 8] : 0u;
+    }
+    uint32_t cls[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) cls[k] = ok[k] ? T.uni2[blk[k] * 256u + (cp[k] & 0xFFu)] : 0u;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int i = ii[k];
+      if (i < 0) continue;
+      lead |= bit(i);
+      if (!ok[k]) {
+        err = min(err, uint32_t(i));
+        continue;
+      }
+      const uint64_t bits = bit_range(i, len[k]);
+      covered |= bits & ~bit(i);
+      add_class(r, cls[k], bits);
+      if (cp[k] == 0x17F) {
+        r.ls0 |= bit(i);
+        if (i + 1 < 64) r.ls1 |= bit(i + 1);
+      }
+    }
+  }
+  // continuation bytes that no valid character claims are errors; they
+  // count as characters of their own (class "other")
+  const uint64_t cont = non & ~hi2;
+  const uint64_t stray = cont & ~covered;
+  if (stray) err = min(err, uint32_t(__ffsll(static_cast<unsigned long long>(stray)) - 1));
+  r.lead = lead | stray;
+  r.err = err;
 }
 
 // Classify the 64 bytes of the word at text offset base (window = bytes
 // [base-16, base+80)).  seg_lo/seg_hi: segment starts at window indices
-// -8..119 (bit j <-> index j-8).
+// -8..119 (bit j <-> index j-8).  The multi-byte part comes from slow_in
+// (the word's stored record) when given, else it is computed, and stored to
+// slow_out when given.
 __device__ __forceinline__ void classify_word(const DevTables &T, const uint8_t *__restrict__ text,
                                               const Window &win, int64_t base, uint64_t n,
-                                              uint64_t seg_lo, uint64_t seg_hi, WordMasks &m) {
+                                              uint64_t seg_lo, uint64_t seg_hi, WordMasks &m,
+                                              const uint64_t *slow_in, uint64_t *slow_out) {
   m.valid = 0;
   if (base >= 0 && uint64_t(base) < n) {
     const uint64_t left = n - uint64_t(base);
@@ -138,55 +249,32 @@ __device__ __forceinline__ void classify_word(const DevTables &T, const uint8_t 
   const uint64_t non = ~asc & m.valid;
   m.na = non;
   if (non) {
-    // multi-byte characters: continuation bytes are covered by a valid lead
-    uint64_t covered = 0;
-    uint32_t err = 64;
-    // a character that began up to three bytes before the word
-    if (!(hi2 & 1) && (non & 1)) {
-      int kf = 0;
-      if ((win.at(-1) & 0xC0u) != 0x80u) kf = 1;
-      else if ((win.at(-2) & 0xC0u) != 0x80u) kf = 2;
-      else if ((win.at(-3) & 0xC0u) != 0x80u) kf = 3;
-      if (kf > 0 && base - kf >= 0) {
-        int len;
-        bool ok;
-        const uint32_t cp = decode_text(text, n, base, -kf, seg_lo, seg_hi, len, ok);
-        if (ok && len > kf) {
-          const uint64_t bits = bit_range(0, len - kf);
-          covered |= bits;
-          add_class(m, class_of(T, cp), bits);
-          if (cp == 0x17F) m.c_ls1 |= 1;  // its second byte
-        }
+    SlowMasks r;
+    if (slow_in) {
+      const ulonglong2 *q = reinterpret_cast<const ulonglong2 *>(slow_in);
+      const ulonglong2 v0 = q[0], v1 = q[1], v2 = q[2], v3 = q[3], v4 = q[4];
+      r = SlowMasks{v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y, v4.x, v4.y};
+    } else {
+      classify_slow(T, text, win, base, n, seg_lo, seg_hi, hi2, non, m.valid, r);
+      if (slow_out) {
+        ulonglong2 *q = reinterpret_cast<ulonglong2 *>(slow_out);
+        q[0] = ulonglong2{r.LU, r.LL};
+        q[1] = ulonglong2{r.LB, r.N};
+        q[2] = ulonglong2{r.WS, r.M};
+        q[3] = ulonglong2{r.lead, r.ls0};
+        q[4] = ulonglong2{r.ls1, r.err};
       }
     }
-    uint64_t leads = hi2 & m.valid;
-    // invalid lead bytes (C0, C1, F5..FF) are >= 0xC0 too; decode_text rejects them
-    while (leads) {
-      const int i = __ffsll(static_cast<unsigned long long>(leads)) - 1;
-      leads &= leads - 1;
-      int len;
-      bool ok;
-      const uint32_t cp = decode_text(text, n, base, i, seg_lo, seg_hi, len, ok);
-      lead |= bit(i);
-      if (!ok) {
-        err = min(err, uint32_t(i));
-        continue;
-      }
-      const uint64_t bits = bit_range(i, len);
-      covered |= bits & ~bit(i);
-      add_class(m, class_of(T, cp), bits);
-      if (cp == 0x17F) {
-        m.c_ls0 |= bit(i);
-        if (i + 1 < 64) m.c_ls1 |= bit(i + 1);
-      }
-    }
-    // continuation bytes that no valid character claims are errors; they
-    // count as characters of their own (class "other")
-    const uint64_t cont = non & ~hi2;
-    const uint64_t stray = cont & ~covered;
-    if (stray) err = min(err, uint32_t(__ffsll(static_cast<unsigned long long>(stray)) - 1));
-    lead |= stray;
-    m.err = err;
+    m.LU |= r.LU;
+    m.LL |= r.LL;
+    m.LB |= r.LB;
+    m.N |= r.N;
+    m.WS |= r.WS;
+    m.M |= r.M;
+    m.c_ls0 |= r.ls0;
+    m.c_ls1 |= r.ls1;
+    lead |= r.lead;
+    m.err = uint32_t(r.err);
   }
   const uint64_t v = m.valid;
   m.L = m.LU | m.LL | m.LB;

@@ -21,7 +21,7 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 struct WsLayout {
   uint64_t status, tile_nchar, tile_lastchg, tile_charbase, tile_chgcarry, seg_local, seg_charstart,
       ss, spst, spc, ps, tile_fn, tile_carry, tile_np, piece_start, piece_cnt, piece_off,
-      tmp_ids, scan_part, l16, l32, g16, g32, g64, ll, lrank, lpart, lnl, lnr, lbits, lsel, lmin, ldirty, total;
+      tmp_ids, scan_part, l16, l32, g16, g32, g64, ll, lrank, lpart, lnl, lnr, lbits, lsel, lmin, ldirty, wslow, wseg, wseg_at, total;
   uint64_t n_words;
   uint32_t n_tiles;
 };
@@ -71,6 +71,9 @@ WsLayout layout_for(uint64_t n, uint32_t n_seg) {
   take(L.lsel, 8 * (n / 32 + 2));
   take(L.lmin, 4 * (n / 32 + 2));
   take(L.ldirty, 4 * (n / 32 + 2));
+  take(L.wslow, 8 * SLOW_WORDS * (W + 1));
+  take(L.wseg, 16 * (W + 1));
+  take(L.wseg_at, 4 * (W + 1));
   L.total = o;
   return L;
 }
@@ -260,6 +263,9 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
   a.ws.lsel = reinterpret_cast<unsigned long long *>(w + L.lsel);
   a.ws.lmin = reinterpret_cast<int32_t *>(w + L.lmin);
   a.ws.ldirty = reinterpret_cast<uint32_t *>(w + L.ldirty);
+  a.ws.wslow = reinterpret_cast<uint64_t *>(w + L.wslow);
+  a.ws.wseg = reinterpret_cast<uint64_t *>(w + L.wseg);
+  a.ws.wseg_at = reinterpret_cast<uint32_t *>(w + L.wseg_at);
   return BBPE_OK;
 }
 

@@ -7,6 +7,7 @@
 #include "bbpe_classify.h"
 #include "bbpe_device.h"
 #include "bbpe_kernels.h"
+#include "bbpe_word.h"
 
 namespace bbpe {
 
@@ -25,12 +26,10 @@ __global__ void __launch_bounds__(64) k_count(EncodeArgs a) {
   const bool owned = lane >= 1 && lane <= int(TILE_WORDS) && w < int64_t(a.n_words);
 
   Window win;
-  load_window(a.text, a.n, base, win);
   uint64_t seg_lo, seg_hi;
   uint32_t seg_at;
-  segment_marks(a.seg_off, a.n_seg, base, seg_lo, seg_hi, seg_at);
   WordMasks m;
-  classify_word(a.T, a.text, win, base, a.n, seg_lo, seg_hi, m);
+  word_setup<true>(a, w, owned, win, seg_lo, seg_hi, seg_at, m);
 
   const uint64_t segb = ((seg_lo >> 8) | (seg_hi << 56)) & m.valid;  // segment starts in [0,64)
   const uint64_t ws_prev = shfl_up64(m.WS, 1);
@@ -169,12 +168,10 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
   const bool live = lane >= 1 && w < int64_t(a.n_words);  // owned or the right halo
 
   Window win;
-  load_window(a.text, a.n, base, win);
   uint64_t seg_lo, seg_hi;
   uint32_t seg_at;
-  segment_marks(a.seg_off, a.n_seg, base, seg_lo, seg_hi, seg_at);
   WordMasks m;
-  classify_word(a.T, a.text, win, base, a.n, seg_lo, seg_hi, m);
+  word_setup<false>(a, w, owned, win, seg_lo, seg_hi, seg_at, m);
   const uint64_t segb = ((seg_lo >> 8) | (seg_hi << 56)) & m.valid;
   const uint64_t ws_prev = shfl_up64(m.WS, 1);
   const uint64_t chg = m.lead & (segb | (m.WS ^ shl(m.WS, ws_prev, 1)));

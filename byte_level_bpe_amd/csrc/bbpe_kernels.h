@@ -9,6 +9,9 @@
 
 namespace bbpe {
 
+// 64-bit words of a word's stored multi-byte class record
+constexpr uint32_t SLOW_WORDS = 10;
+
 // Device workspace, carved out of the caller's buffer by the host planner.
 struct WsPtrs {
   Status *status;
@@ -37,6 +40,12 @@ struct WsPtrs {
   unsigned long long *lbits, *lsel;
   int32_t *lmin;
   uint32_t *ldirty;
+  // per text word, stored by the first front-end kernel: the multi-byte part
+  // of its class masks (SLOW_WORDS each, words with a byte >= 0x80 only),
+  // and its segment marks (more than one segment only)
+  uint64_t *wslow;
+  uint64_t *wseg;                   // [W][2]
+  uint32_t *wseg_at;                // [W]
 };
 
 struct EncodeArgs {

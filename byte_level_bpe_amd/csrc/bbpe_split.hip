@@ -28,6 +28,7 @@
 #include "bbpe_classify.h"
 #include "bbpe_device.h"
 #include "bbpe_kernels.h"
+#include "bbpe_word.h"
 
 namespace bbpe {
 
@@ -461,12 +462,9 @@ __device__ __forceinline__ uint64_t split_finish(const SplitWord &o, uint64_t pC
 __device__ __forceinline__ void lane_setup(const EncodeArgs &a, int lane, uint32_t t, int64_t &w,
                                            WordMasks &m, Window &win) {
   w = int64_t(t) * TILE_WORDS + lane - 1;
-  const int64_t base = w * 64;
-  load_window(a.text, a.n, base, win);
   uint64_t seg_lo, seg_hi;
   uint32_t seg_at;
-  segment_marks(a.seg_off, a.n_seg, base, seg_lo, seg_hi, seg_at);
-  classify_word(a.T, a.text, win, base, a.n, seg_lo, seg_hi, m);
+  word_setup<false>(a, w, false, win, seg_lo, seg_hi, seg_at, m);
 }
 
 // previous-byte CR/LF within the span (needed by the emit pass)
