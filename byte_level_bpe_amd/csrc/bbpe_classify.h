@@ -151,11 +151,16 @@ __device__ __forceinline__ void classify_slow(const DevTables &T, const uint8_t 
       if (c >= 0xD800 && c <= 0xDFFF) good = false;
       cp[k] = c;
       ok[k] = good;
-      blk[k] = good ? T.uni1[c >> 8] : 0u;
+      // loads issued unconditionally (index 0 when unused): a load under a
+      // condition is waited for on its own
+      blk[k] = T.uni1[good ? (c >> 8) : 0u];
     }
     uint32_t cls[K];
 #pragma unroll
-    for (int k = 0; k < K; ++k) cls[k] = ok[k] ? T.uni2[blk[k] * 256u + (cp[k] & 0xFFu)] : 0u;
+    for (int k = 0; k < K; ++k) {
+      const uint32_t c = T.uni2[ok[k] ? blk[k] * 256u + (cp[k] & 0xFFu) : 0u];
+      cls[k] = ok[k] ? c : 0u;
+    }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const int i = ii[k];

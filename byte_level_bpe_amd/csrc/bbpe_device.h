@@ -80,16 +80,18 @@ __device__ __forceinline__ void load_window(const uint8_t *__restrict__ text, ui
       win.w[4 * q + 3] = v.w;
     }
   } else {
+    // Near the ends of the text: every dword load is issued unconditionally
+    // (from offset 0 when the dword lies outside the text) and masked after,
+    // so the 24 loads overlap.  A dword holding byte n-1 is read whole: the
+    // text is 16-byte aligned, so it lies in the same page as that byte.
 #pragma unroll
     for (int q = 0; q < 24; ++q) {
-      uint32_t v = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int64_t idx = base - 16 + 4 * q + j;
-        uint32_t b = (idx >= 0 && uint64_t(idx) < n) ? uint32_t(text[idx]) : 0u;
-        v |= b << (8 * j);
-      }
-      win.w[q] = v;
+      const int64_t addr = base - 16 + 4 * q;
+      const bool in = addr >= 0 && uint64_t(addr) < n;
+      const uint32_t raw = *reinterpret_cast<const uint32_t *>(text + (in ? addr : 0));
+      const int64_t left = int64_t(n) - addr;  // bytes of the dword inside the text
+      const uint32_t keep = !in ? 0u : (left >= 4 ? ~0u : ((1u << (8 * left)) - 1u));
+      win.w[q] = raw & keep;
     }
   }
 }

@@ -591,16 +591,25 @@ __device__ __forceinline__ void split_body(const EncodeArgs &a) {
     // cut there into independent units.  Checked where a non-ASCII byte is
     // involved, which is where long pieces come from; skipping a check only
     // leaves a unit longer, never changes the ids.
+    // The pair bitmap goes to LDS first (8 KB, only in waves that have a
+    // candidate), and every position is checked without a branch, so that
+    // the reads overlap.
+    __shared__ uint32_t s_inner[2048];
     const uint64_t na_prev = shfl_up64(m.na, 1);
     const uint64_t cand = o.IN & ~ps & ~o.SS & m.valid & (m.na | shl(m.na, na_prev, 1));
-    if (cand) {
+    if (__ballot(cand != 0)) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(a.T.inner);
+      uint4 *dst = reinterpret_cast<uint4 *>(s_inner);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) dst[k * 64 + lane] = src[k * 64 + lane];
+      __syncthreads();
+      uint64_t cut = 0;
 #pragma unroll
       for (int i = 0; i < 64; ++i) {
-        if ((cand >> i) & 1) {
-          const uint32_t pr = (win.at(i - 1) << 8) | win.at(i);
-          if (!((a.T.inner[pr >> 5] >> (pr & 31)) & 1)) ps |= bit(i);
-        }
+        const uint32_t pr = (win.at(i - 1) << 8) | win.at(i);
+        cut |= uint64_t(((s_inner[pr >> 5] >> (pr & 31)) & 1) ^ 1u) << i;
       }
+      ps |= cand & cut;
     }
   }
   const uint32_t np = owned ? uint32_t(__popcll(ps)) : 0u;
