@@ -34,24 +34,29 @@ WORKLOAD_DESC = {
 }
 
 
-def algorithmic_bytes(kernel: str, n: int, n_seg: int, n_ids: int, n_pieces: int,
-                      table_bytes_touched: int) -> int:
-    """Bytes a kernel must move by the definition of its step (one launch).
+ALG_BYTES = os.path.join(ROOT, "bench_alg_bytes.json")
 
-    k_merge: the pieces' bytes, their start offsets, the ids and the
-      per-piece id counts it writes, and the rank-table traffic of the
-      method's merge loop (key bytes + 4 per lookup, counted by the oracle).
-    front kernels (one pass over the text): the text bytes plus 64-bit masks
-      in and out (1/8 byte per text byte each).
+
+def algorithmic_bytes(kernel: str, w: dict) -> int:
+    """Bytes one launch of `kernel` must move by the definition of its step.
+
+    w is the workload's entry of bench_alg_bytes.json, counted once by the
+    oracle (oracle/alg_bytes.py): per merge kernel, the bytes of the units
+    it merges, their ids and counts, and the rank lookups of the merge loop
+    on those units (key bytes + 4 B each); for k_probe, every unit's bytes,
+    start and count, plus one lookup per unit of 2+ bytes that is a key.
+    Front-end kernels make one pass over the text: the text bytes plus
+    64-bit masks in and out (1/8 byte per text byte each).
     """
-    if kernel == "k_merge":
-        return n + 4 * n_pieces + 4 * n_ids + 4 * n_pieces + table_bytes_touched
+    n = w["bytes"]
+    if kernel in w["kernels"]:
+        return w["kernels"][kernel]["bytes"]
     if kernel in ("k_count", "k_spans", "k_split_agg", "k_split"):
         return n + n // 8 * (3 if kernel != "k_count" else 1)
     if kernel == "k_pieces":
-        return n // 8 + 4 * n_pieces
+        return n // 8 + 4 * w["pieces"]
     if kernel == "k_assemble":
-        return 4 * n_ids * 2 + 8 * n_pieces
+        return 4 * w["ids"] * 2 + 8 * w["pieces"]
     return n
 
 
@@ -140,18 +145,16 @@ def main():
     mbs = total * args.steps / wall / 1e6
     tps = n_ids * args.steps / wall
 
-    # algorithmic bytes of the whole call (oracle-instrumented table traffic)
-    from oracle import Oracle
-    orc = Oracle(w.tokens, w.specials, w.grammar)
-    orc.reset_counters()
-    oids, _ = orc.encode_segments(w.segments, w.tiktoken_safe)
-    cnt = orc.counters()
-    assert len(oids) == n_ids, "id count differs from the oracle"
-    b_alg = total + 4 * n_ids + 8 * (n_seg + 1) + cnt["lookup_bytes"]
+    # algorithmic bytes of the whole call and per kernel, counted once by the
+    # oracle and stored (oracle/alg_bytes.py)
+    with open(ALG_BYTES) as f:
+        alg = json.load(f)[args.workload]
+    assert alg["ids"] == n_ids and alg["bytes"] == total, "workload differs from the counted one"
+    b_alg = alg["call_bytes"]
     per_kernel = {k: v[0] / max(1, v[1]) for k, v in rep.items()}
     dom = max(rep, key=lambda k: rep[k][0])
     dom_ms = per_kernel[dom]
-    dom_bytes = algorithmic_bytes(dom, total, n_seg, n_ids, cnt["pieces"], cnt["lookup_bytes"])
+    dom_bytes = algorithmic_bytes(dom, alg)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -173,7 +176,7 @@ def main():
         "config": {"workload": WORKLOAD_DESC.get(args.workload, args.workload),
                    "bytes": total, "segments": n_seg, "ids": n_ids, "ranks": len(w.tokens)},
         "call_roofline": {"alg_bytes": b_alg, "frac_of_8TBs": round(b_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
-                          "pieces": cnt["pieces"], "table_bytes": cnt["lookup_bytes"]},
+                          "pieces": alg["pieces"], "table_bytes": alg["lookup_bytes"]},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
                      "traffic": None, "avg_ms": round(dom_ms, 5), "alg_bytes_per_launch": dom_bytes},

@@ -333,6 +333,8 @@ int bbpe_upload_tables(bbpe_tokenizer *t, void *d_mem, uint64_t bytes, void *str
   d.sp_id = reinterpret_cast<const int32_t *>(b + L.sp_id);
   d.inner = reinterpret_cast<const uint32_t *>(b + L.inner);
   d.mt = reinterpret_cast<const uint64_t *>(b + L.mt);
+  d.k3 = reinterpret_cast<const uint32_t *>(b + L.k3);
+  d.q4 = reinterpret_cast<const uint32_t *>(b + L.q4);
   t->d_image = b;
   return BBPE_OK;
 }

@@ -71,6 +71,9 @@ BBPE_HD uint32_t mt_bucket(uint64_t key, uint32_t shift) {
   return uint32_t((key * 0x9E3779B97F4A7C15ull) >> shift);
 }
 
+// Bit of a 4-byte string (little-endian) in the 4-gram bitmap.
+BBPE_HD uint32_t q4_index(uint32_t x) { return (x * 0x9E3779B1u) >> 8; }
+
 // ---------------------------------------------------------------------------
 // Device view of the uploaded tables (passed to kernels by value).
 // ---------------------------------------------------------------------------
@@ -87,6 +90,9 @@ struct DevTables {
   const int32_t *sp_id;     // [n_sp]
   const uint32_t *inner;    // [2048] bit (a*256+b): the byte pair (a,b) occurs inside some key
   const uint64_t *mt;       // merge table, [mt_mask+1] buckets of MT_BUCKET entries
+  const uint32_t *k3;       // [2^24 bits] bit (a<<16|b<<8|c): the 3-byte string abc is a key
+  const uint32_t *q4;       // [2^24 bits] bit q4_index(abcd): abcd may occur inside a key
+                            //   (every 4-byte substring of a key sets its bit)
   uint32_t mt_mask;
   uint32_t mt_shift;        // 64 - log2(buckets)
   uint32_t slot_mask;
@@ -98,7 +104,7 @@ struct DevTables {
 
 // Byte offsets of each table inside the uploaded image.
 struct ImageLayout {
-  uint64_t slots, ext, blob, pair, atom, uni1, uni2, sp_bytes, sp_off, sp_id, inner, mt, total;
+  uint64_t slots, ext, blob, pair, atom, uni1, uni2, sp_bytes, sp_off, sp_id, inner, mt, k3, q4, total;
   uint32_t n_slots;
   uint32_t n_mt_buckets;
 };

@@ -28,6 +28,7 @@
 #include "bbpe_classify.h"
 #include "bbpe_device.h"
 #include "bbpe_kernels.h"
+#include "bbpe_machines.h"
 #include "bbpe_word.h"
 
 namespace bbpe {
@@ -200,13 +201,7 @@ __device__ __forceinline__ void digit_v_fns(const SplitWord &o, const uint64_t N
     for (uint32_t s = 0; s < 3; ++s) fd |= ((s + cnt) % 3u) << (2 * s);
     fd |= ((cnt + 2u) % 3u) << 6;
   } else {
-    uint32_t ph = 3;
-    for (int i = 0; i < 64; ++i) {
-      const uint64_t b = bit(i);
-      if (o.N_ & o.LD & b) ph = (runstart & b) ? 0u : (ph == 3u ? 0u : (ph + 1u) % 3u);
-      else if (!(o.N_ & b)) ph = 3;
-    }
-    fd = ph * 0x55u;  // constant function
+    fd = digit_phase_out(o.N_, o.N_ & o.LD, runstart) * 0x55u;  // constant function
   }
   const uint64_t prop = o.NC & ~o.BRK;
   if (prop == ~uint64_t(0)) {
@@ -339,14 +334,8 @@ __device__ __forceinline__ void split_word(const EncodeArgs &a, int64_t w, const
     if ((CR_ & ~SS) == ~uint64_t(0)) {
       fc = ((pO & 1) ? 1u : 2u) | (1u << 2) | (2u << 4);
     } else {
-      uint32_t st = 0;
-      for (int i = 0; i < 64; ++i) {
-        const uint64_t b = bit(i);
-        if (!(IN & b)) st = 0;
-        else if (CR_ & b) st = (SS & b) ? 2u : (st == 0 ? ((pO & b) ? 1u : 2u) : st);
-        else st = 0;
-      }
-      fc = st * 0x15u;
+      uint64_t e2;
+      fc = cr_runs(CR_, IN, SS, pO, NC & LD, 0u, e2) * 0x15u;
     }
     o.f_cr = fc;
     o.f_let = 0;
@@ -399,7 +388,9 @@ __device__ __forceinline__ uint64_t split_finish(const SplitWord &o, uint64_t pC
   uint64_t PH0 = 0, E2b = 0, VN = 0, extra = 0;
   const uint64_t NLD = o.N_ & o.LD;
   const uint64_t runstart = NLD & (o.SS | ~o.pN);
-  if (o.N_) {
+  if (o.N_ == NLD) {  // single-byte digits only
+    PH0 = digit_phase0_ascii(NLD, runstart, ph);
+  } else {
     for (int i = 0; i < 64; ++i) {
       const uint64_t b = bit(i);
       if (NLD & b) {
@@ -411,20 +402,7 @@ __device__ __forceinline__ uint64_t split_finish(const SplitWord &o, uint64_t pC
     }
   }
   if (G == 0) {
-    uint32_t st = xs;
-    if (o.CR_ | (st != 0)) {
-      for (int i = 0; i < 64; ++i) {
-        const uint64_t b = bit(i);
-        if (!(o.IN & b)) {
-          st = 0;
-        } else if (o.CR_ & b) {
-          st = (o.SS & b) ? 2u : (st == 0 ? ((o.pO & b) ? 1u : 2u) : st);
-        } else {
-          if (st == 1 && (o.NC & o.LD & b) && !(o.SS & b)) E2b |= b;
-          st = 0;
-        }
-      }
-    }
+    (void)cr_runs(o.CR_, o.IN, o.SS, o.pO, o.NC & o.LD, xs, E2b);
   } else {
     uint32_t st = xs;
     uint64_t LS = 0, PQ = 0, F1m = 0;
@@ -446,15 +424,7 @@ __device__ __forceinline__ uint64_t split_finish(const SplitWord &o, uint64_t pC
     extra = LS | (o.WstCR & ~PQ);
   }
   const uint64_t Qcand = o.NC & o.LD & pCRmask;
-  if (Qcand) {
-    for (int i = 63; i >= 0; --i) {
-      const uint64_t b = bit(i);
-      if (v) VN |= b;
-      if (o.BRK & b) v = 0;
-      else if (o.NC & b) { /* propagate */ }
-      else v = (o.WS_ & b) ? 0u : 1u;
-    }
-  }
+  if (Qcand) VN = v_next(o.BRK, o.NC, o.WS_, v);
   const uint64_t startN = NLD & (o.SS | ~o.pN | PH0);
   return o.static_starts | startN | E2b | extra | (Qcand & VN);
 }
@@ -586,11 +556,17 @@ __device__ __forceinline__ void split_body(const EncodeArgs &a) {
   const uint64_t pCRm = prev_cr(o);
   uint64_t ps = split_finish<G>(o, pCRm, ph, xs, v) & m.valid;
   if (a.merge_units) {
-    // Merge units: a byte pair that occurs inside no key can never be merged
-    // across (the merged part would be a key containing it), so the piece is
-    // cut there into independent units.  Checked where a non-ASCII byte is
-    // involved, which is where long pieces come from; skipping a check only
-    // leaves a unit longer, never changes the ids.
+    // Merge units: where no key can occur across a position, no merge ever
+    // crosses it (every part is a key), so the piece is cut there into
+    // independent units.  A key occurrence across position j (between bytes
+    // j-1 and j) contains the byte pair there; if it is 2 or 3 bytes long it
+    // is one of the windows [j-1, j+1), [j-2, j+1), [j-1, j+2); if longer, it
+    // contains one of the 4-byte windows starting at j-3, j-2, j-1.  So j is
+    // a cut when the pair occurs inside no key, or else when neither short
+    // window is a key and no 4-byte window occurs inside a key (windows that
+    // reach outside the piece only make the test stricter).  Checked where a
+    // non-ASCII byte is involved, which is where long pieces come from;
+    // skipping a check only leaves a unit longer, never changes the ids.
     // The pair bitmap goes to LDS first (8 KB, only in waves that have a
     // candidate), and every position is checked without a branch, so that
     // the reads overlap.
@@ -610,6 +586,41 @@ __device__ __forceinline__ void split_body(const EncodeArgs &a) {
         cut |= uint64_t(((s_inner[pr >> 5] >> (pr & 31)) & 1) ^ 1u) << i;
       }
       ps |= cand & cut;
+      // pairs that occur inside keys: the longer windows, at character
+      // boundaries only, eight positions at a time with their loads issued
+      // together
+      uint64_t rest = cand & ~cut & m.lead;
+      const int64_t base = w * 64;
+      while (rest) {
+        constexpr int K = 8;
+        int ii[K];
+        uint32_t b[K][6];  // bytes j-3 .. j+2
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          ii[k] = __ffsll(static_cast<unsigned long long>(rest)) - 1;
+          rest &= rest - 1;
+#pragma unroll
+          for (int d = 0; d < 6; ++d) b[k][d] = text_byte(a.text, a.n, base + ii[k] - 3 + d);
+        }
+        uint32_t hit[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const uint32_t x3a = (b[k][1] << 16) | (b[k][2] << 8) | b[k][3];
+          const uint32_t x3b = (b[k][2] << 16) | (b[k][3] << 8) | b[k][4];
+          const uint32_t w0 = b[k][0] | (b[k][1] << 8) | (b[k][2] << 16) | (b[k][3] << 24);
+          const uint32_t w1 = b[k][1] | (b[k][2] << 8) | (b[k][3] << 16) | (b[k][4] << 24);
+          const uint32_t w2 = b[k][2] | (b[k][3] << 8) | (b[k][4] << 16) | (b[k][5] << 24);
+          const uint32_t q0 = q4_index(w0), q1 = q4_index(w1), q2 = q4_index(w2);
+          const bool pk = a.T.pair[(b[k][2] << 8) | b[k][3]] != RANK_NONE;
+          const uint32_t h = ((a.T.k3[x3a >> 5] >> (x3a & 31)) | (a.T.k3[x3b >> 5] >> (x3b & 31)) |
+                              (a.T.q4[q0 >> 5] >> (q0 & 31)) | (a.T.q4[q1 >> 5] >> (q1 & 31)) |
+                              (a.T.q4[q2 >> 5] >> (q2 & 31))) & 1u;
+          hit[k] = h | (pk ? 1u : 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+          if (ii[k] >= 0 && !hit[k]) ps |= bit(ii[k]);
+      }
     }
   }
   const uint32_t np = owned ? uint32_t(__popcll(ps)) : 0u;

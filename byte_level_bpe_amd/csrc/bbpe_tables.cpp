@@ -195,6 +195,8 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
   L.sp_off = o; o = align256(o + 4 * (sp.size() + 1));
   L.sp_id = o; o = align256(o + 4 * (sp.size() + 1));
   L.mt = o; o = align256(o + uint64_t(n_mt) * bbpe::MT_BUCKET * 8);
+  L.k3 = o; o = align256(o + (uint64_t(1) << 24) / 8);
+  L.q4 = o; o = align256(o + (uint64_t(1) << 24) / 8);
   L.total = o;
   L.n_slots = n_slots;
   L.n_mt_buckets = n_mt;
@@ -258,6 +260,23 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
     spi[i] = spid[i];
   }
   spo[sp.size()] = so;
+  // exact 3-byte keys, and the 4-byte substrings of keys (hashed)
+  uint32_t *k3 = reinterpret_cast<uint32_t *>(img + L.k3);
+  uint32_t *q4 = reinterpret_cast<uint32_t *>(img + L.q4);
+  for (uint32_t i = 0; i < n; ++i) {
+    const uint8_t *kp = reinterpret_cast<const uint8_t *>(keys[i].data());
+    const size_t len = keys[i].size();
+    if (len == 3) {
+      const uint32_t x = (uint32_t(kp[0]) << 16) | (uint32_t(kp[1]) << 8) | kp[2];
+      k3[x >> 5] |= 1u << (x & 31);
+    }
+    for (size_t j = 0; j + 4 <= len; ++j) {
+      const uint32_t x = uint32_t(kp[j]) | (uint32_t(kp[j + 1]) << 8) | (uint32_t(kp[j + 2]) << 16) |
+                         (uint32_t(kp[j + 3]) << 24);
+      const uint32_t b = bbpe::q4_index(x);
+      q4[b >> 5] |= 1u << (b & 31);
+    }
+  }
   uint64_t *mt = reinterpret_cast<uint64_t *>(img + L.mt);
   for (uint64_t e : mt_entries) {
     const uint64_t key = (e >> bbpe::MT_ID_BITS) & ((uint64_t(1) << (2 * bbpe::MT_ID_BITS)) - 1);

@@ -285,6 +285,41 @@ def test_ranks_at_the_top_of_the_range():
     assert_ids(tok, orc, segs, safe=False, what="ranks near 2^21")
 
 
+def test_unit_cuts_keys_across_characters():
+    """Merge units are cut between multi-byte characters where no key can
+    occur across the boundary.  Tables here hold keys that straddle
+    character boundaries (byte pairs, 3-byte windows, 4- to 6-byte windows
+    and two-character keys) with random ranks, so that a wrong cut shows up
+    as a wrong merge."""
+    r = random.Random(44)
+    chars = [c.encode() for c in "中文字符號碼ककिािं😀"]
+    for ti in range(8):
+        tab = dict(atoms_permuted(ti))
+        nxt = [256]
+
+        def add(k):
+            if k not in tab:
+                tab[k] = nxt[0]
+                nxt[0] += 1
+        for c in chars:
+            for L in range(2, len(c) + 1):
+                add(c[:L])
+        text = b"".join(r.choice(chars) for _ in range(400))
+        for _ in range(60):
+            a = r.randrange(len(text) - 8)
+            add(text[a:a + r.randint(2, 6)])
+        for _ in range(10):
+            add(r.choice(chars) + r.choice(chars))
+        keys = [k for k in tab if len(k) > 1]
+        for k, rk in zip(keys, r.sample(range(256, 256 + 4 * len(keys)), len(keys))):
+            tab[k] = rk
+        tok, orc = make(tab, [], ti % 2)
+        segs = [(b"".join(r.choice(chars) for _ in range(n)), False) for n in (3, 11, 40, 200, 900)]
+        segs.append((b"x" + text + b" " + text[::-1][:300].decode("utf-8", "ignore").encode(), False))
+        say("unit cuts, table", ti)
+        assert_ids(tok, orc, segs, safe=False, what="unit cuts table %d" % ti)
+
+
 def test_long_units_adversarial_tables():
     """Units over 512 bytes (the batched long tier) under random tables over
     {a, b}: keys of 2-6 bytes with random ranks, so that merges of equal rank
