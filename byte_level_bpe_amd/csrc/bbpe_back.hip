@@ -361,23 +361,22 @@ constexpr uint32_t WAVE_MAX = 64 * WNS;    // longest unit the group tiers hold
 constexpr uint32_t GROUP_PACK_MIN = 4096;  // group units above which several share a wave
 
 // Every unit: specials, single bytes and units that are keys whose own
-// merges rebuild them get their id here; the rest are listed for k_merge by
-// length.  Each block gathers its list entries in LDS and reserves room in
-// the global lists with one atomic per list (per-wave atomics on four
-// shared counters serialise at the L2).
-constexpr uint32_t PROBE_BLOCK = 256;
+// merges rebuild them get their id here; the rest are listed for the merge
+// kernels by length class.  Each block gathers its list entries in LDS and
+// reserves room in the global lists with one atomic per class: device-scope
+// atomics on a few shared counters serialise, so blocks are large (1024
+// units per block and pass).
 
 __global__ void __launch_bounds__(PROBE_BLOCK) k_probe(EncodeArgs a) {
   if (a.ws.status->pad2) return;
   Status *st = a.ws.status;
   const uint32_t P = uint32_t(st->n_pieces);
   const DevTables &T = a.T;
-  constexpr uint32_t NLIST = 6;
-  __shared__ unsigned int s_cnt[NLIST], s_base[NLIST];
-  __shared__ uint32_t s_list[NLIST][PROBE_BLOCK];
+  __shared__ unsigned int s_cnt[ML_COUNT], s_base[ML_COUNT];
+  __shared__ uint32_t s_list[ML_COUNT][PROBE_BLOCK];
   for (uint32_t b = blockIdx.x * PROBE_BLOCK; b < P; b += gridDim.x * PROBE_BLOCK) {
     const uint32_t i = b + threadIdx.x;
-    int tier = 0;  // list: 1 <= 16 bytes, 2 <= 32, 3 <= 128, 4 <= 256, 5 <= 512, 6 longer
+    int cls = -1;  // MergeList of a unit left to merge
     if (i < P) {
       const uint32_t s = a.ws.piece_start[i];
       const uint32_t m = a.ws.piece_start[i + 1] - s;
@@ -397,35 +396,28 @@ __global__ void __launch_bounds__(PROBE_BLOCK) k_probe(EncodeArgs a) {
                                       [&](const uint8_t *bb) __attribute__((always_inline)) { return unit_rest_eq(u, 0, m, bb); })
                               : RANK_NONE;
         if (r != RANK_NONE && (meta & META_SELF)) id = r;
-        else tier = m <= 16 ? 1 : 2;
+        else cls = m <= 4 ? ML_4 : m <= 8 ? ML_8 : m <= 16 ? ML_16 : ML_32;
       } else {
         uint32_t meta = 0;
         const int32_t r = m <= T.max_key_len ? lookup_text(T, a.text + s, m, meta) : RANK_NONE;
         if (r != RANK_NONE && (meta & META_SELF)) id = r;
-        else tier = m <= 128 ? 3 : m <= 256 ? 4 : m <= WAVE_MAX ? 5 : 6;
+        else cls = m <= 128 ? ML_G128 : m <= 256 ? ML_G256 : m <= WAVE_MAX ? ML_G512 : ML_LONG;
       }
       if (id >= 0) {
         a.ws.tmp_ids[s] = id;
         a.ws.piece_cnt[i] = 1;
       }
     }
-    if (threadIdx.x < NLIST) s_cnt[threadIdx.x] = 0;
+    if (threadIdx.x < ML_COUNT) s_cnt[threadIdx.x] = 0;
     __syncthreads();
-    if (tier) s_list[tier - 1][atomicAdd(&s_cnt[tier - 1], 1u)] = i;
+    if (cls >= 0) s_list[cls][atomicAdd(&s_cnt[cls], 1u)] = i;
     __syncthreads();
-    if (threadIdx.x < NLIST && s_cnt[threadIdx.x]) {
-      unsigned int *cnt = threadIdx.x == 0   ? &st->n_l16
-                          : threadIdx.x == 1 ? &st->n_l32
-                          : threadIdx.x == 2 ? &st->n_g16
-                          : threadIdx.x == 3 ? &st->n_g32
-                          : threadIdx.x == 4 ? &st->n_g64 : &st->n_ll;
-      s_base[threadIdx.x] = atomicAdd(cnt, s_cnt[threadIdx.x]);
-    }
+    if (threadIdx.x < ML_COUNT && s_cnt[threadIdx.x])
+      s_base[threadIdx.x] = atomicAdd(&st->n_list[threadIdx.x], s_cnt[threadIdx.x]);
     __syncthreads();
 #pragma unroll
-    for (uint32_t L = 0; L < NLIST; ++L) {
-      uint32_t *list = L == 0 ? a.ws.l16 : L == 1 ? a.ws.l32 : L == 2 ? a.ws.g16
-                       : L == 3 ? a.ws.g32 : L == 4 ? a.ws.g64 : a.ws.ll;
+    for (uint32_t L = 0; L < ML_COUNT; ++L) {
+      uint32_t *list = a.ws.lst[L];
       for (uint32_t k = threadIdx.x; k < s_cnt[L]; k += PROBE_BLOCK) list[s_base[L] + k] = s_list[L][k];
     }
     __syncthreads();
@@ -861,7 +853,9 @@ __device__ __forceinline__ void merge_short_unit(const EncodeArgs &a, uint32_t i
   a.ws.piece_cnt[i] = merge_short<SK>(a.T, u, m, a.ws.tmp_ids + s);
 }
 
-// Merge of the short units: chunks of 64 units (one lane each), 17-32 bytes
+// Merge of the short units: chunks of 64 units of one length class (one
+// lane each, positions in registers sized to the class, so that a wave's
+// rounds and its per-round work follow its longest unit), longest class
 // first.  Wave w takes items w, w + G, w + 2G, ... (G waves in the grid).
 // The item index is wave-uniform by construction: no lane-0 ticket and
 // broadcast, which lets the compiler split the loop per lane.  Three waves
@@ -870,15 +864,23 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
   if (a.ws.status->pad2) return;
   const Status *st = a.ws.status;
   const int lane = int(threadIdx.x);
-  const uint32_t n32 = st->n_l32, n16 = st->n_l16;
-  const uint32_t e_32 = (n32 + 63) / 64, e_16 = e_32 + (n16 + 63) / 64;
-  for (uint32_t item = blockIdx.x; item < e_16; item += gridDim.x) {
-    if (item < e_32) {
+  const uint32_t n32 = st->n_list[ML_32], n16 = st->n_list[ML_16], n8 = st->n_list[ML_8],
+                 n4 = st->n_list[ML_4];
+  const uint32_t e32 = (n32 + 63) / 64, e16 = e32 + (n16 + 63) / 64, e8 = e16 + (n8 + 63) / 64,
+                 e4 = e8 + (n4 + 63) / 64;
+  for (uint32_t item = blockIdx.x; item < e4; item += gridDim.x) {
+    if (item < e32) {
       const uint32_t x = item * 64 + uint32_t(lane);
-      if (x < n32) merge_short_unit<32>(a, a.ws.l32[x]);
+      if (x < n32) merge_short_unit<32>(a, a.ws.lst[ML_32][x]);
+    } else if (item < e16) {
+      const uint32_t x = (item - e32) * 64 + uint32_t(lane);
+      if (x < n16) merge_short_unit<16>(a, a.ws.lst[ML_16][x]);
+    } else if (item < e8) {
+      const uint32_t x = (item - e16) * 64 + uint32_t(lane);
+      if (x < n8) merge_short_unit<8>(a, a.ws.lst[ML_8][x]);
     } else {
-      const uint32_t x = (item - e_32) * 64 + uint32_t(lane);
-      if (x < n16) merge_short_unit<16>(a, a.ws.l16[x]);
+      const uint32_t x = (item - e8) * 64 + uint32_t(lane);
+      if (x < n4) merge_short_unit<4>(a, a.ws.lst[ML_4][x]);
     }
   }
 }
@@ -892,19 +894,19 @@ __global__ void __launch_bounds__(64) k_merge_group(EncodeArgs a) {
   if (a.ws.status->pad2) return;
   const Status *st = a.ws.status;
   const int lane = int(threadIdx.x);
-  const uint32_t n64 = st->n_g64, n32g = st->n_g32, n16g = st->n_g16;
+  const uint32_t n64 = st->n_list[ML_G512], n32g = st->n_list[ML_G256], n16g = st->n_list[ML_G128];
   const bool pack = n64 + n32g + n16g > GROUP_PACK_MIN;
   const uint32_t e64 = n64, e32g = e64 + (pack ? (n32g + 1) / 2 : n32g);
   const uint32_t e16g = e32g + (pack ? (n16g + 3) / 4 : n16g);
   for (uint32_t item = blockIdx.x; item < e16g; item += gridDim.x) {
     if (item < e64) {
-      merge_group<64, 8>(a, a.ws.g64, n64, item, lane);
+      merge_group<64, 8>(a, a.ws.lst[ML_G512], n64, item, lane);
     } else if (item < e32g) {
-      if (pack) merge_group<32, 8>(a, a.ws.g32, n32g, (item - e64) * 2, lane);
-      else merge_group<64, 4>(a, a.ws.g32, n32g, item - e64, lane);
+      if (pack) merge_group<32, 8>(a, a.ws.lst[ML_G256], n32g, (item - e64) * 2, lane);
+      else merge_group<64, 4>(a, a.ws.lst[ML_G256], n32g, item - e64, lane);
     } else {
-      if (pack) merge_group<16, 8>(a, a.ws.g16, n16g, (item - e32g) * 4, lane);
-      else merge_group<64, 2>(a, a.ws.g16, n16g, item - e32g, lane);
+      if (pack) merge_group<16, 8>(a, a.ws.lst[ML_G128], n16g, (item - e32g) * 4, lane);
+      else merge_group<64, 2>(a, a.ws.lst[ML_G128], n16g, item - e32g, lane);
     }
   }
 }
@@ -913,9 +915,9 @@ __global__ void __launch_bounds__(64) k_merge_group(EncodeArgs a) {
 // sharing one with the register tiers costs those their occupancy).
 __global__ void __launch_bounds__(64) k_merge_long(EncodeArgs a) {
   if (a.ws.status->pad2) return;
-  const uint32_t nll = a.ws.status->n_ll;
+  const uint32_t nll = a.ws.status->n_list[ML_LONG];
   for (uint32_t item = blockIdx.x; item < nll; item += gridDim.x)
-    merge_long(a, a.ws.ll[item], int(threadIdx.x));
+    merge_long(a, a.ws.lst[ML_LONG][item], int(threadIdx.x));
 }
 
 // ---------------------------------------------------------------------------

@@ -21,7 +21,7 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 struct WsLayout {
   uint64_t status, tile_nchar, tile_lastchg, tile_charbase, tile_chgcarry, seg_local, seg_charstart,
       ss, spst, spc, ps, tile_fn, tile_carry, tile_np, piece_start, piece_cnt, piece_off,
-      tmp_ids, scan_part, l16, l32, g16, g32, g64, ll, lrank, lpart, lnl, lnr, lbits, lsel, lmin, ldirty, wslow, wseg, wseg_at, total;
+      tmp_ids, scan_part, lst[ML_COUNT], lrank, lpart, lnl, lnr, lbits, lsel, lmin, ldirty, wslow, wseg, wseg_at, total;
   uint64_t n_words;
   uint32_t n_tiles;
 };
@@ -56,13 +56,7 @@ WsLayout layout_for(uint64_t n, uint32_t n_seg) {
   take(L.piece_off, 4 * (n + 1));
   take(L.tmp_ids, 4 * (n + 1));
   take(L.scan_part, 4 * ((n + 1) / 4096 + 2));
-  // units to merge have at least 2 / 17 / 33 / 513 bytes
-  take(L.l16, 4 * (n / 2 + 1));
-  take(L.l32, 4 * (n / 17 + 1));
-  take(L.g16, 4 * (n / 33 + 1));
-  take(L.g32, 4 * (n / 129 + 1));
-  take(L.g64, 4 * (n / 257 + 1));
-  take(L.ll, 4 * (n / 513 + 1));
+  for (uint32_t k = 0; k < ML_COUNT; ++k) take(L.lst[k], 4 * (n / ML_MIN_LEN[k] + 1));
   take(L.lrank, 4 * (n + 1));
   take(L.lpart, 4 * (n + 1));
   take(L.lnl, 4 * (n + 1));
@@ -84,12 +78,7 @@ __global__ void k_init(EncodeArgs a) {
     s->err_pos = ~0ull;
     s->n_pieces = 0;
     s->n_ids = 0;
-    s->n_ll = 0;
-    s->n_g16 = 0;
-    s->n_l32 = 0;
-    s->n_l16 = 0;
-    s->n_g32 = 0;
-    s->n_g64 = 0;
+    for (uint32_t k = 0; k < ML_COUNT; ++k) s->n_list[k] = 0;
     s->n_chars = 0;
     s->err_seg = 0;
     // offsets must start at 0 and end at the text length (monotonicity is
@@ -249,12 +238,7 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
   a.ws.piece_off = reinterpret_cast<uint32_t *>(w + L.piece_off);
   a.ws.tmp_ids = reinterpret_cast<int32_t *>(w + L.tmp_ids);
   a.ws.scan_part = reinterpret_cast<uint32_t *>(w + L.scan_part);
-  a.ws.l16 = reinterpret_cast<uint32_t *>(w + L.l16);
-  a.ws.l32 = reinterpret_cast<uint32_t *>(w + L.l32);
-  a.ws.g16 = reinterpret_cast<uint32_t *>(w + L.g16);
-  a.ws.g32 = reinterpret_cast<uint32_t *>(w + L.g32);
-  a.ws.g64 = reinterpret_cast<uint32_t *>(w + L.g64);
-  a.ws.ll = reinterpret_cast<uint32_t *>(w + L.ll);
+  for (uint32_t k = 0; k < ML_COUNT; ++k) a.ws.lst[k] = reinterpret_cast<uint32_t *>(w + L.lst[k]);
   a.ws.lrank = reinterpret_cast<int32_t *>(w + L.lrank);
   a.ws.lpart = reinterpret_cast<int32_t *>(w + L.lpart);
   a.ws.lnl = reinterpret_cast<int32_t *>(w + L.lnl);
@@ -367,8 +351,8 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
   if (n == 0) {
     go("k_zero_offsets", k_zero_offsets, dim3(seg_grid), dim3(256), a);
   } else {
-    const uint32_t probe_grid = uint32_t(std::min<uint64_t>((n + 1023) / 1024, 16384));
-    go("k_probe", k_probe, dim3(probe_grid), dim3(256), a);
+    const uint32_t probe_grid = uint32_t(std::min<uint64_t>((n + 4095) / 4096, 8192));
+    go("k_probe", k_probe, dim3(probe_grid), dim3(PROBE_BLOCK), a);
     // the group and long tiers (few units, long dependent chains) run on the
     // second stream beside the short tier
     hipStream_t aux = static_cast<hipStream_t>(t->aux_stream);

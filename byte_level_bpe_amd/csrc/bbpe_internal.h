@@ -122,15 +122,27 @@ struct Status {
   unsigned long long err_pos;     // first invalid UTF-8 byte (absolute), or ~0
   unsigned long long n_pieces;
   unsigned long long n_ids;
-  unsigned int n_ll;              // units to merge, longer than one wave holds
-  unsigned int n_g16;             // ... of 33-128 bytes
   unsigned long long n_chars;
   unsigned int err_seg;           // segment of err_pos
   unsigned int pad2;              // nonzero: invalid segment offsets, every kernel exits
-  unsigned int n_l32;             // ... of 17-32 bytes
-  unsigned int n_l16;             // ... of 2-16 bytes
-  unsigned int n_g32;             // ... of 129-256 bytes
-  unsigned int n_g64;             // ... of 257-512 bytes
+  unsigned int n_list[8];         // units to merge per length class (MergeList)
 };
+
+// Merge-unit lists by length class: the short tier (one lane per unit,
+// positions in registers sized to the class), the group tier (16, 32 or 64
+// lanes per unit) and the long tier.
+enum MergeList : uint32_t {
+  ML_4 = 0,    // 2-4 bytes
+  ML_8,        // 5-8
+  ML_16,       // 9-16
+  ML_32,       // 17-32
+  ML_G128,     // 33-128
+  ML_G256,     // 129-256
+  ML_G512,     // 257-512
+  ML_LONG,     // longer
+  ML_COUNT
+};
+// shortest unit of each class (list capacities are text bytes / this)
+constexpr uint32_t ML_MIN_LEN[ML_COUNT] = {2, 5, 9, 17, 33, 129, 257, 513};
 
 }  // namespace bbpe

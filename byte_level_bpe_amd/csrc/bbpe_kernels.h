@@ -31,7 +31,7 @@ struct WsPtrs {
   uint32_t *piece_off;              // [P+1] exclusive scan of the ids per unit
   int32_t *tmp_ids;                 // [N] ids of each piece, at the piece's byte offset
   uint32_t *scan_part;              // [N/4096+2] partial sums of the piece scan
-  uint32_t *l16, *l32, *g16, *g32, *g64, *ll;  // units to merge, by length
+  uint32_t *lst[ML_COUNT];          // units to merge, by length class
   // long tier, per text position: pair rank at each part start, id of the
   // part starting there, and the two created-pair ranks of a batch merge
   int32_t *lrank, *lpart, *lnl, *lnr;
@@ -47,6 +47,9 @@ struct WsPtrs {
   uint64_t *wseg;                   // [W][2]
   uint32_t *wseg_at;                // [W]
 };
+
+// threads per k_probe block (units per block and pass)
+constexpr uint32_t PROBE_BLOCK = 1024;
 
 struct EncodeArgs {
   DevTables T;
