@@ -579,7 +579,7 @@ __device__ void merge_group(const EncodeArgs &a, const uint32_t *list, uint32_t 
 }
 
 // ---------------------------------------------------------------------------
-// Long tier: one wave per unit longer than WAVE_MAX, state in global memory.
+// Long tier: one workgroup per unit longer than WAVE_MAX, state in global memory.
 // Per position j of the unit (text byte s + j): lrank = rank of the pair that
 // starts with the part starting at j, lpart = id of that part.  Per 64-position
 // block b of the unit, at index (s >> 5) + b (a unit of m > 64 bytes needs
@@ -598,7 +598,7 @@ __device__ void merge_group(const EncodeArgs &a, const uint32_t *list, uint32_t 
 // <= R.  The leftmost pair of rank R is always chosen, so every round merges.
 // Runs of one repeated character (tens of thousands of spaces) take a few
 // rounds per doubling of the part length instead of one round per merge.
-// Lanes own blocks; device-scope fences order the phases of a round.
+// Threads own blocks (or quarter blocks); barriers order the phases of a round.
 // ---------------------------------------------------------------------------
 struct LongUnit {
   const EncodeArgs &a;
@@ -662,186 +662,6 @@ struct LongUnit {
 __device__ __forceinline__ uint32_t chain_then(uint32_t f, uint32_t g) {
   if (g & 2) return g;
   return (f & 2) | ((f ^ g) & 1);
-}
-
-__device__ void merge_long(const EncodeArgs &a, uint32_t i, int lane) {
-  const DevTables &T = a.T;
-  const uint32_t s = a.ws.piece_start[i];
-  const uint32_t m = a.ws.piece_start[i + 1] - s;
-  const uint8_t *p = a.text + s;
-  const uint32_t base = s >> 5;
-  LongUnit U{a, s, m, (m + 63) / 64, a.ws.lbits + base, a.ws.lsel + base, a.ws.lmin + base,
-             a.ws.ldirty + base};
-  const uint32_t nb = U.nb;
-  for (uint32_t j = uint32_t(lane); j < m; j += 64) {
-    U.rank(j) = (j + 1 < m) ? T.pair[uint32_t(p[j]) * 256u + p[j + 1]] : RANK_NONE;
-    U.part(j) = T.atom[p[j]];
-  }
-  for (uint32_t b = uint32_t(lane); b < nb; b += 64) {
-    const uint32_t left = m - 64 * b;
-    U.bits[b] = left >= 64 ? ~0ull : ((1ull << left) - 1);
-    U.sel[b] = 0;
-    U.dirty[b] = 0;
-  }
-  __threadfence();
-  for (uint32_t b = uint32_t(lane); b < nb; b += 64) {
-    unsigned long long eq;
-    U.mn[b] = U.block_scan(b, U.bits[b], RANK_NONE, eq);
-  }
-  __threadfence();
-
-  for (;;) {
-    int32_t R = RANK_NONE;
-    for (uint32_t b = uint32_t(lane); b < nb; b += 64) R = min(R, U.mn[b]);
-    R = wave_min_i32(R);
-    if (R == RANK_NONE) break;
-
-    // 1. choose the pairs: chain parity scanned over blocks, 64 at a time
-    uint32_t carry = 0;
-    for (uint32_t b0 = 0; b0 < nb; b0 += 64) {
-      const uint32_t b = b0 + uint32_t(lane);
-      unsigned long long A = 0, C = 0;
-      if (b < nb) {
-        A = U.bits[b];
-        if (U.mn[b] == R) U.block_scan(b, A, R, C);
-      }
-      const unsigned long long N = A & ~C;
-      uint32_t f;
-      if (A == 0) {
-        f = 0;
-      } else if (N == 0) {
-        f = uint32_t(__popcll(C)) & 1u;
-      } else {
-        const int h = 63 - __clzll(static_cast<long long>(N));
-        const unsigned long long after = h == 63 ? 0ull : (C & (~0ull << (h + 1)));
-        f = 2u | (uint32_t(__popcll(after)) & 1u);
-      }
-      uint32_t inc = f;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = uint32_t(__shfl_up(int(inc), d, 64));
-        if (lane >= d) inc = chain_then(o, inc);
-      }
-      uint32_t ex = uint32_t(__shfl_up(int(inc), 1, 64));
-      if (lane == 0) ex = 0;  // identity
-      uint32_t st = (ex & 2) ? (ex & 1) : (carry ^ (ex & 1));
-      unsigned long long S = 0;
-      unsigned long long w = A;
-      while (w) {
-        const uint32_t t = uint32_t(__ffsll(w) - 1);
-        w &= w - 1;
-        if ((C >> t) & 1) {
-          if (st == 0) S |= 1ull << t;
-          st ^= 1u;
-        } else {
-          st = 0;
-        }
-      }
-      if (b < nb) U.sel[b] = S;
-      const uint32_t last = uint32_t(__shfl(int(inc), 63, 64));
-      carry = (last & 2) ? (last & 1) : (carry ^ (last & 1));
-    }
-    __threadfence();
-
-    // 2. the pairs each chosen merge creates, and the first merge after which
-    // the batch must stop
-    uint32_t stop = 0xFFFFFFFFu;
-    for (uint32_t b = uint32_t(lane); b < nb; b += 64) {
-      unsigned long long S = U.sel[b];
-      while (S) {
-        const uint32_t j = 64 * b + uint32_t(__ffsll(S) - 1);
-        S &= S - 1;
-        const uint32_t k = U.next(j + 1);
-        const uint32_t k2 = U.next(k + 1);
-        const int y = U.prev(j);
-        int pf = y;
-        if (y >= 0) {
-          const int z = U.prev(uint32_t(y));
-          if (z >= 0 && U.chosen(uint32_t(z))) pf = z;  // y merged into z
-        }
-        // the merged part (id R) with its neighbours; a left neighbour that
-        // merges in this batch too has id R as well
-        const uint32_t lid = pf >= 0 ? (pf != y ? uint32_t(R) : uint32_t(U.part(uint32_t(pf)))) : 0u;
-        const uint32_t rid = k2 < m ? uint32_t(U.part(k2)) : 0u;
-        int32_t nl, nr;
-        merge_rank2(T, pf >= 0, lid, uint32_t(R), k2 < m, uint32_t(R), rid, nl, nr);
-        a.ws.lnl[s + j] = nl;
-        a.ws.lnr[s + j] = nr;
-        if (nl <= R || nr <= R) stop = min(stop, j);
-      }
-    }
-    stop = uint32_t(wave_min_i32(int32_t(min(stop, 0x7FFFFFFFu))));
-    __threadfence();
-
-    // 3. apply the merges up to and including `stop`
-    for (uint32_t b = uint32_t(lane); b < nb && 64 * b <= stop; b += 64) {
-      unsigned long long S = U.sel[b];
-      while (S) {
-        const uint32_t j = 64 * b + uint32_t(__ffsll(S) - 1);
-        S &= S - 1;
-        if (j > stop) break;
-        const uint32_t k = U.next(j + 1);
-        const uint32_t k2 = U.next(k + 1);
-        const int y = U.prev(j);
-        int pf = y;
-        if (y >= 0) {
-          const int z = U.prev(uint32_t(y));
-          if (z >= 0 && U.chosen(uint32_t(z))) pf = z;
-        }
-        U.part(j) = R;
-        U.rank(k) = RANK_NONE;
-        if (pf >= 0) {
-          U.rank(uint32_t(pf)) = a.ws.lnl[s + j];
-          U.dirty[uint32_t(pf) >> 6] = 1;
-        }
-        // the pair to the right, unless the next part merges too (its own
-        // left pair is then this part's right pair)
-        if (!(k2 < m && k2 <= stop && U.chosen(k2))) U.rank(j) = a.ws.lnr[s + j];
-        U.dirty[j >> 6] = 1;
-        U.dirty[k >> 6] = 1;
-      }
-    }
-    __threadfence();
-    // the merged right parts stop being part starts
-    for (uint32_t b = uint32_t(lane); b < nb && 64 * b <= stop; b += 64) {
-      unsigned long long S = U.sel[b];
-      while (S) {
-        const uint32_t j = 64 * b + uint32_t(__ffsll(S) - 1);
-        S &= S - 1;
-        if (j > stop) break;
-        const uint32_t k = U.next(j + 1);
-        atomicAnd(&U.bits[k >> 6], ~(1ull << (k & 63)));
-      }
-    }
-    __threadfence();
-    for (uint32_t b = uint32_t(lane); b < nb; b += 64) {
-      U.sel[b] = 0;
-      if (U.dirty[b]) {
-        unsigned long long eq;
-        U.mn[b] = U.block_scan(b, U.bits[b], RANK_NONE, eq);
-        U.dirty[b] = 0;
-      }
-    }
-    __threadfence();
-  }
-
-  // output: ids in order; block counts scanned across lanes
-  uint32_t c = 0;
-  for (uint32_t b0 = 0; b0 < nb; b0 += 64) {
-    const uint32_t b = b0 + uint32_t(lane);
-    const unsigned long long A = b < nb ? U.bits[b] : 0ull;
-    const uint32_t cnt = uint32_t(__popcll(A));
-    const uint32_t incl = wave_incl_sum(cnt, lane);
-    uint32_t o = c + incl - cnt;
-    unsigned long long w = A;
-    while (w) {
-      const uint32_t t = uint32_t(__ffsll(w) - 1);
-      w &= w - 1;
-      a.ws.tmp_ids[s + o++] = U.part(64 * b + t);
-    }
-    c += uint32_t(__shfl(int(incl), 63, 64));
-  }
-  a.ws.piece_cnt[i] = c;  // c is the same in every lane
 }
 
 template <int SK>
@@ -911,13 +731,246 @@ __global__ void __launch_bounds__(64) k_merge_group(EncodeArgs a) {
   }
 }
 
-// Merge of the units longer than WAVE_MAX, one wave each (its own kernel:
-// sharing one with the register tiers costs those their occupancy).
-__global__ void __launch_bounds__(64) k_merge_long(EncodeArgs a) {
+// Block-wide helpers of the long tier (LONG_BLOCK threads, LDS scratch sh).
+constexpr uint32_t LONG_BLOCK = 1024;
+
+__device__ __forceinline__ int32_t block_min_i32(int32_t v, int32_t *sh) {
+  v = wave_min_i32(v);
+  const uint32_t wv = threadIdx.x / 64;
+  if ((threadIdx.x & 63) == 0) sh[wv] = v;
+  __syncthreads();
+  int32_t r = RANK_NONE;
+#pragma unroll
+  for (uint32_t k = 0; k < LONG_BLOCK / 64; ++k) r = min(r, sh[k]);
+  __syncthreads();
+  return r;
+}
+
+// inclusive scan of chain-parity functions over the threads, in thread order
+__device__ __forceinline__ uint32_t block_chain_scan(uint32_t f, uint32_t *sh) {
+  const uint32_t t = threadIdx.x;
+  sh[t] = f;
+  __syncthreads();
+  for (uint32_t d = 1; d < LONG_BLOCK; d <<= 1) {
+    const uint32_t v = t >= d ? chain_then(sh[t - d], sh[t]) : sh[t];
+    __syncthreads();
+    sh[t] = v;
+    __syncthreads();
+  }
+  const uint32_t r = sh[t];
+  __syncthreads();
+  return r;
+}
+
+// exclusive sum over the threads; total to every thread
+__device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t *sh, uint32_t &total) {
+  const uint32_t t = threadIdx.x;
+  sh[t] = v;
+  __syncthreads();
+  for (uint32_t d = 1; d < LONG_BLOCK; d <<= 1) {
+    const uint32_t o = t >= d ? sh[t - d] : 0u;
+    __syncthreads();
+    sh[t] += o;
+    __syncthreads();
+  }
+  total = sh[LONG_BLOCK - 1];
+  const uint32_t r = sh[t] - v;
+  __syncthreads();
+  return r;
+}
+
+// One workgroup per unit.  Blocks of 64 positions are owned by threads for
+// the scans; the chosen pairs of a round are handled per quarter block (16
+// positions), so that up to 4 * blocks threads merge side by side.
+__device__ void merge_long(const EncodeArgs &a, uint32_t i, uint32_t *sh) {
+  const DevTables &T = a.T;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t s = a.ws.piece_start[i];
+  const uint32_t m = a.ws.piece_start[i + 1] - s;
+  const uint8_t *p = a.text + s;
+  const uint32_t base = s >> 5;
+  LongUnit U{a, s, m, (m + 63) / 64, a.ws.lbits + base, a.ws.lsel + base, a.ws.lmin + base,
+             a.ws.ldirty + base};
+  const uint32_t nb = U.nb;
+  for (uint32_t j = tid; j < m; j += LONG_BLOCK) {
+    U.rank(j) = (j + 1 < m) ? T.pair[uint32_t(p[j]) * 256u + p[j + 1]] : RANK_NONE;
+    U.part(j) = T.atom[p[j]];
+  }
+  for (uint32_t b = tid; b < nb; b += LONG_BLOCK) {
+    const uint32_t left = m - 64 * b;
+    U.bits[b] = left >= 64 ? ~0ull : ((1ull << left) - 1);
+    U.sel[b] = 0;
+    U.dirty[b] = 0;
+  }
+  __syncthreads();
+  for (uint32_t b = tid; b < nb; b += LONG_BLOCK) {
+    unsigned long long eq;
+    U.mn[b] = U.block_scan(b, U.bits[b], RANK_NONE, eq);
+  }
+  __syncthreads();
+
+  for (;;) {
+    int32_t R = RANK_NONE;
+    for (uint32_t b = tid; b < nb; b += LONG_BLOCK) R = min(R, U.mn[b]);
+    R = block_min_i32(R, reinterpret_cast<int32_t *>(sh));
+    if (R == RANK_NONE) break;
+
+    // 1. choose the pairs: chain parity scanned over blocks, LONG_BLOCK at a time
+    uint32_t carry = 0;
+    for (uint32_t b0 = 0; b0 < nb; b0 += LONG_BLOCK) {
+      const uint32_t b = b0 + tid;
+      unsigned long long A = 0, C = 0;
+      if (b < nb) {
+        A = U.bits[b];
+        if (U.mn[b] == R) U.block_scan(b, A, R, C);
+      }
+      const unsigned long long N = A & ~C;
+      uint32_t f;
+      if (A == 0) {
+        f = 0;
+      } else if (N == 0) {
+        f = uint32_t(__popcll(C)) & 1u;
+      } else {
+        const int h = 63 - __clzll(static_cast<long long>(N));
+        const unsigned long long after = h == 63 ? 0ull : (C & (~0ull << (h + 1)));
+        f = 2u | (uint32_t(__popcll(after)) & 1u);
+      }
+      const uint32_t inc = block_chain_scan(f, sh);
+      sh[tid] = inc;
+      __syncthreads();
+      const uint32_t ex = tid ? sh[tid - 1] : 0u;  // 0 = identity
+      const uint32_t last = sh[LONG_BLOCK - 1];
+      __syncthreads();
+      uint32_t st = (ex & 2) ? (ex & 1) : (carry ^ (ex & 1));
+      unsigned long long S = 0;
+      unsigned long long w = A;
+      while (w) {
+        const uint32_t t = uint32_t(__ffsll(w) - 1);
+        w &= w - 1;
+        if ((C >> t) & 1) {
+          if (st == 0) S |= 1ull << t;
+          st ^= 1u;
+        } else {
+          st = 0;
+        }
+      }
+      if (b < nb) U.sel[b] = S;
+      carry = (last & 2) ? (last & 1) : (carry ^ (last & 1));
+    }
+    __syncthreads();
+
+    // 2. the pairs each chosen merge creates, and the first merge after which
+    // the batch must stop
+    uint32_t stop = 0xFFFFFFFFu;
+    for (uint32_t q = tid; q < 4 * nb; q += LONG_BLOCK) {
+      const uint32_t b = q >> 2;
+      unsigned long long S = U.sel[b] & (0xFFFFull << (16 * (q & 3)));
+      while (S) {
+        const uint32_t j = 64 * b + uint32_t(__ffsll(S) - 1);
+        S &= S - 1;
+        const uint32_t k = U.next(j + 1);
+        const uint32_t k2 = U.next(k + 1);
+        const int y = U.prev(j);
+        int pf = y;
+        if (y >= 0) {
+          const int z = U.prev(uint32_t(y));
+          if (z >= 0 && U.chosen(uint32_t(z))) pf = z;  // y merged into z
+        }
+        // the merged part (id R) with its neighbours; a left neighbour that
+        // merges in this batch too has id R as well
+        const uint32_t lid = pf >= 0 ? (pf != y ? uint32_t(R) : uint32_t(U.part(uint32_t(pf)))) : 0u;
+        const uint32_t rid = k2 < m ? uint32_t(U.part(k2)) : 0u;
+        int32_t nl, nr;
+        merge_rank2(T, pf >= 0, lid, uint32_t(R), k2 < m, uint32_t(R), rid, nl, nr);
+        a.ws.lnl[s + j] = nl;
+        a.ws.lnr[s + j] = nr;
+        if (nl <= R || nr <= R) stop = min(stop, j);
+      }
+    }
+    stop = uint32_t(block_min_i32(int32_t(min(stop, 0x7FFFFFFFu)), reinterpret_cast<int32_t *>(sh)));
+
+    // 3. apply the merges up to and including `stop`
+    for (uint32_t q = tid; q < 4 * nb && 16 * q <= stop; q += LONG_BLOCK) {
+      const uint32_t b = q >> 2;
+      unsigned long long S = U.sel[b] & (0xFFFFull << (16 * (q & 3)));
+      while (S) {
+        const uint32_t j = 64 * b + uint32_t(__ffsll(S) - 1);
+        S &= S - 1;
+        if (j > stop) break;
+        const uint32_t k = U.next(j + 1);
+        const uint32_t k2 = U.next(k + 1);
+        const int y = U.prev(j);
+        int pf = y;
+        if (y >= 0) {
+          const int z = U.prev(uint32_t(y));
+          if (z >= 0 && U.chosen(uint32_t(z))) pf = z;
+        }
+        U.part(j) = R;
+        U.rank(k) = RANK_NONE;
+        if (pf >= 0) {
+          U.rank(uint32_t(pf)) = a.ws.lnl[s + j];
+          U.dirty[uint32_t(pf) >> 6] = 1;
+        }
+        // the pair to the right, unless the next part merges too (its own
+        // left pair is then this part's right pair)
+        if (!(k2 < m && k2 <= stop && U.chosen(k2))) U.rank(j) = a.ws.lnr[s + j];
+        U.dirty[j >> 6] = 1;
+        U.dirty[k >> 6] = 1;
+      }
+    }
+    __syncthreads();
+    // the merged right parts stop being part starts
+    for (uint32_t q = tid; q < 4 * nb && 16 * q <= stop; q += LONG_BLOCK) {
+      const uint32_t b = q >> 2;
+      unsigned long long S = U.sel[b] & (0xFFFFull << (16 * (q & 3)));
+      while (S) {
+        const uint32_t j = 64 * b + uint32_t(__ffsll(S) - 1);
+        S &= S - 1;
+        if (j > stop) break;
+        const uint32_t k = U.next(j + 1);
+        atomicAnd(&U.bits[k >> 6], ~(1ull << (k & 63)));
+      }
+    }
+    __syncthreads();
+    for (uint32_t b = tid; b < nb; b += LONG_BLOCK) {
+      U.sel[b] = 0;
+      if (U.dirty[b]) {
+        unsigned long long eq;
+        U.mn[b] = U.block_scan(b, U.bits[b], RANK_NONE, eq);
+        U.dirty[b] = 0;
+      }
+    }
+    __syncthreads();
+  }
+
+  // output: ids in order; block counts scanned across threads
+  uint32_t c = 0;
+  for (uint32_t b0 = 0; b0 < nb; b0 += LONG_BLOCK) {
+    const uint32_t b = b0 + tid;
+    const unsigned long long A = b < nb ? U.bits[b] : 0ull;
+    const uint32_t cnt = uint32_t(__popcll(A));
+    uint32_t total;
+    uint32_t o = c + block_excl_sum(cnt, sh, total);
+    unsigned long long w = A;
+    while (w) {
+      const uint32_t t = uint32_t(__ffsll(w) - 1);
+      w &= w - 1;
+      a.ws.tmp_ids[s + o++] = U.part(64 * b + t);
+    }
+    c += total;
+  }
+  if (tid == 0) a.ws.piece_cnt[i] = c;
+  __syncthreads();
+}
+
+// Merge of the units longer than WAVE_MAX, one workgroup each (its own
+// kernel, on the second stream beside the short tier).
+__global__ void __launch_bounds__(LONG_BLOCK) k_merge_long(EncodeArgs a) {
   if (a.ws.status->pad2) return;
+  __shared__ uint32_t sh[LONG_BLOCK];
   const uint32_t nll = a.ws.status->n_list[ML_LONG];
   for (uint32_t item = blockIdx.x; item < nll; item += gridDim.x)
-    merge_long(a, a.ws.lst[ML_LONG][item], int(threadIdx.x));
+    merge_long(a, a.ws.lst[ML_LONG][item], sh);
 }
 
 // ---------------------------------------------------------------------------

@@ -359,8 +359,10 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
     HIP_OK(hipEventRecord(static_cast<hipEvent_t>(t->ev_fork), go.st));
     HIP_OK(hipStreamWaitEvent(aux, static_cast<hipEvent_t>(t->ev_fork), 0));
     go.use(aux);
-    const uint32_t long_grid = uint32_t(std::min<uint64_t>(n / 513 + 1, 2048));
-    go("k_merge_long", k_merge_long, dim3(long_grid), dim3(64), a);
+    // (grid-stride kernels: their units are few, and idle waves of the
+    // second stream take dispatch slots from the short tier)
+    const uint32_t long_grid = uint32_t(std::min<uint64_t>(n / 513 + 1, 64));
+    go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
     const uint32_t group_grid = uint32_t(std::min<uint64_t>(n / 33 + 1, 4096));
     go("k_merge_group", k_merge_group, dim3(group_grid), dim3(64), a);
     HIP_OK(hipEventRecord(static_cast<hipEvent_t>(t->ev_join), aux));
