@@ -257,7 +257,23 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
   }
   if (any_allow) {
     uint32_t s = seg_at;
+    // candidates: bytes equal to a special's first byte (an exact per-byte
+    // zero test of the window dwords xor the byte), when there are few
     uint64_t cand = m.lead;
+    if (a.T.sp_nfirst) {
+      uint64_t fm = 0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const uint32_t raw = win.w[4 + q];
+        uint32_t z = 0;
+        for (uint32_t f = 0; f < a.T.sp_nfirst; ++f) {
+          const uint32_t v = raw ^ (((a.T.sp_firsts >> (8 * f)) & 0xFFu) * 0x01010101u);
+          z |= ~(((v & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | v | 0x7F7F7F7Fu);  // 0x80 where v's byte is 0
+        }
+        fm |= gather4(z) << (4 * q);
+      }
+      cand &= fm;
+    }
     while (cand) {
       const int i = __ffsll(static_cast<unsigned long long>(cand)) - 1;
       cand &= cand - 1;

@@ -98,6 +98,8 @@ struct DevTables {
   uint32_t slot_mask;
   uint32_t n_sp;
   uint32_t sp_first[8];     // bitmap of first bytes of specials
+  uint32_t sp_nfirst;       // distinct first bytes of specials if at most 4, else 0
+  uint32_t sp_firsts;       // ... those bytes, one per byte lane
   int32_t grammar;
   uint32_t max_key_len;
 };

@@ -300,6 +300,15 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
   d.mt_shift = 64 - mt_log;
   d.n_sp = uint32_t(sp.size());
   for (auto &s : sp) d.sp_first[uint8_t(s[0]) >> 5] |= 1u << (uint8_t(s[0]) & 31);
+  {
+    std::vector<uint8_t> firsts;
+    for (auto &s : sp)
+      if (std::find(firsts.begin(), firsts.end(), uint8_t(s[0])) == firsts.end())
+        firsts.push_back(uint8_t(s[0]));
+    d.sp_nfirst = firsts.size() <= 4 ? uint32_t(firsts.size()) : 0u;
+    d.sp_firsts = 0;
+    for (size_t k = 0; k < firsts.size() && k < 4; ++k) d.sp_firsts |= uint32_t(firsts[k]) << (8 * k);
+  }
   d.grammar = t->grammar;
   d.max_key_len = max_len;
   return BBPE_OK;
