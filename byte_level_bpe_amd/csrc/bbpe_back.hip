@@ -301,15 +301,16 @@ __device__ __forceinline__ uint32_t above32(int j) { return ~((2u << j) - 1u); }
 // Merge a unit of 2 <= m <= SK bytes held in registers: pair ranks r[j] and
 // part ids pr[j] at every part start j, part starts as the bit mask bnd.
 // Writes the ids to out and returns their count.
+// atom: the 256 atom ranks (a copy in LDS).
 template <int SK>
-__device__ __forceinline__ uint32_t merge_short(const DevTables &T, const UnitBytes<SK> &u,
-                                                uint32_t m, int32_t *out) {
+__device__ __forceinline__ uint32_t merge_short(const DevTables &T, const int32_t *atom,
+                                                const UnitBytes<SK> &u, uint32_t m, int32_t *out) {
   int32_t r[SK], pr[SK];
 #pragma unroll
   for (int j = 0; j < SK; ++j) {
     const uint32_t b0 = u.byte(j), b1 = (j + 1 < SK) ? u.byte(j + 1) : 0u;
     r[j] = (uint32_t(j) + 1 < m) ? T.pair[b0 * 256u + b1] : RANK_NONE;
-    pr[j] = (uint32_t(j) < m) ? T.atom[b0] : 0;
+    pr[j] = (uint32_t(j) < m) ? atom[b0] : 0;
   }
   uint32_t bnd = (m >= 32) ? 0xFFFFFFFFu : ((1u << m) - 1u);
   for (uint32_t round = 0; round + 1 < m; ++round) {
@@ -665,12 +666,12 @@ __device__ __forceinline__ uint32_t chain_then(uint32_t f, uint32_t g) {
 }
 
 template <int SK>
-__device__ __forceinline__ void merge_short_unit(const EncodeArgs &a, uint32_t i) {
+__device__ __forceinline__ void merge_short_unit(const EncodeArgs &a, const int32_t *atom, uint32_t i) {
   const uint32_t s = a.ws.piece_start[i];
   const uint32_t m = a.ws.piece_start[i + 1] - s;
   UnitBytes<SK> u;
   load_unit(a.text, a.n, s, m, u);
-  a.ws.piece_cnt[i] = merge_short<SK>(a.T, u, m, a.ws.tmp_ids + s);
+  a.ws.piece_cnt[i] = merge_short<SK>(a.T, atom, u, m, a.ws.tmp_ids + s);
 }
 
 // Merge of the short units: chunks of 64 units of one length class (one
@@ -688,19 +689,23 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
                  n4 = st->n_list[ML_4];
   const uint32_t e32 = (n32 + 63) / 64, e16 = e32 + (n16 + 63) / 64, e8 = e16 + (n8 + 63) / 64,
                  e4 = e8 + (n4 + 63) / 64;
+  if (blockIdx.x >= e4) return;
+  __shared__ int32_t s_atom[256];
+  reinterpret_cast<int4 *>(s_atom)[lane] = reinterpret_cast<const int4 *>(a.T.atom)[lane];
+  __syncthreads();
   for (uint32_t item = blockIdx.x; item < e4; item += gridDim.x) {
     if (item < e32) {
       const uint32_t x = item * 64 + uint32_t(lane);
-      if (x < n32) merge_short_unit<32>(a, a.ws.lst[ML_32][x]);
+      if (x < n32) merge_short_unit<32>(a, s_atom, a.ws.lst[ML_32][x]);
     } else if (item < e16) {
       const uint32_t x = (item - e32) * 64 + uint32_t(lane);
-      if (x < n16) merge_short_unit<16>(a, a.ws.lst[ML_16][x]);
+      if (x < n16) merge_short_unit<16>(a, s_atom, a.ws.lst[ML_16][x]);
     } else if (item < e8) {
       const uint32_t x = (item - e16) * 64 + uint32_t(lane);
-      if (x < n8) merge_short_unit<8>(a, a.ws.lst[ML_8][x]);
+      if (x < n8) merge_short_unit<8>(a, s_atom, a.ws.lst[ML_8][x]);
     } else {
       const uint32_t x = (item - e8) * 64 + uint32_t(lane);
-      if (x < n4) merge_short_unit<4>(a, a.ws.lst[ML_4][x]);
+      if (x < n4) merge_short_unit<4>(a, s_atom, a.ws.lst[ML_4][x]);
     }
   }
 }

@@ -59,13 +59,14 @@ BBPE_HD uint64_t hash_step(uint64_t h, uint64_t w) { return fmix64(h ^ w); }
 // keys (A, B) whose concatenation is a key, i.e. every split of a key into
 // two keys.  The parts of a piece are always keys, so every lookup the merge
 // loop makes after its first round is a lookup of such a pair, and it is
-// answered from the two part ids alone.  64-byte buckets of 8 entries:
+// answered from the two part ids alone.  16-byte buckets of 2 entries (one
+// 16-byte load per probe), about a third of the slots used:
 //   bit 63 valid | A << 42 | B << 21 | rank      (ids and ranks < 2^21)
 // A key hashes to one bucket; a full bucket continues into the next one.
 // ---------------------------------------------------------------------------
 constexpr uint32_t MT_ID_BITS = 21;
 constexpr uint32_t MT_ID_MASK = (1u << MT_ID_BITS) - 1;
-constexpr uint32_t MT_BUCKET = 8;
+constexpr uint32_t MT_BUCKET = 2;
 BBPE_HD uint64_t mt_key(uint32_t a, uint32_t b) { return (uint64_t(a) << MT_ID_BITS) | b; }
 BBPE_HD uint32_t mt_bucket(uint64_t key, uint32_t shift) {
   return uint32_t((key * 0x9E3779B97F4A7C15ull) >> shift);

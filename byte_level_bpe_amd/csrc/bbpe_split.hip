@@ -565,14 +565,17 @@ __device__ __forceinline__ void split_body(const EncodeArgs &a) {
     // a cut when the pair occurs inside no key, or else when neither short
     // window is a key and no 4-byte window occurs inside a key (windows that
     // reach outside the piece only make the test stricter).  Checked where a
-    // non-ASCII byte is involved, which is where long pieces come from;
-    // skipping a check only leaves a unit longer, never changes the ids.
+    // non-ASCII byte is involved and where a lower-case letter is followed by
+    // an upper-case one (identifiers in code), which is where long pieces
+    // come from; skipping a check only leaves a unit longer, never changes
+    // the ids.
     // The pair bitmap goes to LDS first (8 KB, only in waves that have a
     // candidate), and every position is checked without a branch, so that
     // the reads overlap.
     __shared__ uint32_t s_inner[2048];
-    const uint64_t na_prev = shfl_up64(m.na, 1);
-    const uint64_t cand = o.IN & ~ps & ~o.SS & m.valid & (m.na | shl(m.na, na_prev, 1));
+    const uint64_t na_prev = shfl_up64(m.na, 1), ll_prev = shfl_up64(m.LL, 1);
+    const uint64_t cand = o.IN & ~ps & ~o.SS & m.valid &
+                          (m.na | shl(m.na, na_prev, 1) | (m.LU & shl(m.LL, ll_prev, 1)));
     if (__ballot(cand != 0)) {
       const uint4 *src = reinterpret_cast<const uint4 *>(a.T.inner);
       uint4 *dst = reinterpret_cast<uint4 *>(s_inner);

@@ -170,8 +170,8 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
                            uint64_t(rk[i]));
     }
   }
-  uint32_t n_mt = 64, mt_log = 6;  // about 3 entries per bucket of 8
-  while (uint64_t(n_mt) * 3 < mt_entries.size()) n_mt <<= 1, ++mt_log;
+  uint32_t n_mt = 64, mt_log = 6;  // at most 0.7 entries per bucket of 2
+  while (uint64_t(n_mt) * 7 < mt_entries.size() * 10) n_mt <<= 1, ++mt_log;
 
   // image layout
   uint32_t n_slots = 1024;

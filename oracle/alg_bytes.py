@@ -12,11 +12,11 @@ oracle's instrumented loop counts them).
 
 The same figures split by the GPU kernel that does the work, so that a
 kernel's achieved bandwidth can be stated.  Pieces are cut into merge units
-the way the GPU cuts them: at a position next to a byte >= 0x80 where no key
-can occur across it (the byte pair there occurs inside no key; or, at a
-character boundary, it is no 2-byte key, neither 3-byte window across it is a
-key and no 4-byte window across it has its bit set in the GPU's hashed
-4-gram bitmap).  Each unit goes
+the way the GPU cuts them: at a position next to a byte >= 0x80, or between
+an ASCII lower-case and upper-case letter, where no key can occur across it
+(the byte pair there occurs inside no key; or, at a character boundary, it
+is no 2-byte key, neither 3-byte window across it is a key and no 4-byte
+window across it has its bit set in the GPU's hashed 4-gram bitmap).  Each unit goes
 to the kernel of its length class:
 
     k_probe        every unit: its bytes, its start offset and its count
@@ -68,7 +68,8 @@ def count(name: str) -> dict:
         def byte(k):
             return text[k] if 0 <= k < len(text) else 0
         b = [byte(j + d) for d in range(-3, 3)]
-        if not (b[3] >= 0x80 or b[2] >= 0x80):
+        camel = 0x61 <= b[2] <= 0x7A and 0x41 <= b[3] <= 0x5A
+        if not (b[3] >= 0x80 or b[2] >= 0x80 or camel):
             return False
         if bytes(b[2:4]) not in inner:
             return True

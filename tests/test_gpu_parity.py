@@ -285,14 +285,17 @@ def test_ranks_at_the_top_of_the_range():
     assert_ids(tok, orc, segs, safe=False, what="ranks near 2^21")
 
 
-def test_unit_cuts_keys_across_characters():
-    """Merge units are cut between multi-byte characters where no key can
-    occur across the boundary.  Tables here hold keys that straddle
-    character boundaries (byte pairs, 3-byte windows, 4- to 6-byte windows
-    and two-character keys) with random ranks, so that a wrong cut shows up
-    as a wrong merge."""
+@pytest.mark.parametrize("alphabet", ["中文字符號碼ककिािं😀", "abcdeABCDEzZ"],
+                         ids=["multibyte", "camel"])
+def test_unit_cuts_keys_across_characters(alphabet):
+    """Merge units are cut between multi-byte characters, and between a
+    lower-case and an upper-case letter, where no key can occur across the
+    boundary.  Tables here hold keys that straddle character boundaries
+    (byte pairs, 3-byte windows, 4- to 6-byte windows and two-character
+    keys) with random ranks, so that a wrong cut shows up as a wrong
+    merge."""
     r = random.Random(44)
-    chars = [c.encode() for c in "中文字符號碼ककिािं😀"]
+    chars = [c.encode() for c in alphabet]
     for ti in range(8):
         tab = dict(atoms_permuted(ti))
         nxt = [256]
