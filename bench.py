@@ -35,6 +35,35 @@ WORKLOAD_DESC = {
 
 
 ALG_BYTES = os.path.join(ROOT, "bench_alg_bytes.json")
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scaled by a
+# plain copy of known size), valid for the kernel sources they were taken on
+TRAFFIC = os.path.join(ROOT, "profiles", "encode_%s_hbm_counters.json")
+CSRC = os.path.join(ROOT, "byte_level_bpe_amd", "csrc")
+
+
+def source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(CSRC)):
+        if fn.endswith((".hip", ".h", ".cpp", ".inc")):
+            h.update(fn.encode())
+            with open(os.path.join(CSRC, fn), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """Counted HBM bytes per launch of `kernel`, or None when none were taken
+    for this workload or the sources changed since."""
+    path = TRAFFIC % workload
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f).get(workload, {})
+    if t.get("source_sha256_16") != source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return k["bytes"] if k else None
 
 
 def algorithmic_bytes(kernel: str, w: dict) -> int:
@@ -191,7 +220,8 @@ def main():
                           "pieces": alg["pieces"], "table_bytes": alg["lookup_bytes"]},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
-                     "traffic": None, "avg_ms": round(dom_ms, 5), "alg_bytes_per_launch": dom_bytes},
+                     "traffic": measured_traffic(args.workload, dom), "avg_ms": round(dom_ms, 5),
+                     "alg_bytes_per_launch": dom_bytes},
         "kernels_avg_ms": {k: round(v, 5) for k, v in sorted(per_kernel.items(), key=lambda kv: -kv[1])},
     }
     if not args.no_cpu_baseline:
