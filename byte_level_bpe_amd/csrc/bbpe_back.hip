@@ -984,19 +984,19 @@ __global__ void __launch_bounds__(LONG_BLOCK) k_merge_long(EncodeArgs a) {
 constexpr uint32_t SCAN_BLOCK = 256, SCAN_ITEMS = 16, SCAN_TILE = SCAN_BLOCK * SCAN_ITEMS;
 
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *sh, uint32_t &total) {
-  const uint32_t tid = threadIdx.x;
-  sh[tid] = v;
+  const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x / 64;
+  const uint32_t incl = wave_incl_sum(v, int(lane));
+  if (lane == 63) sh[wv] = incl;
   __syncthreads();
-  for (uint32_t d = 1; d < SCAN_BLOCK; d <<= 1) {
-    const uint32_t o = tid >= d ? sh[tid - d] : 0;
-    __syncthreads();
-    sh[tid] += o;
-    __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < SCAN_BLOCK / 64; ++q) {
+    before += q < wv ? sh[q] : 0u;
+    all += sh[q];
   }
-  total = sh[SCAN_BLOCK - 1];
-  const uint32_t r = sh[tid] - v;
   __syncthreads();
-  return r;
+  total = all;
+  return before + incl - v;
 }
 
 __global__ void __launch_bounds__(SCAN_BLOCK) k_scan_reduce(EncodeArgs a) {
@@ -1015,32 +1015,6 @@ __global__ void __launch_bounds__(SCAN_BLOCK) k_scan_reduce(EncodeArgs a) {
   if (threadIdx.x == 0) a.ws.scan_part[blockIdx.x] = total;
 }
 
-__global__ void __launch_bounds__(1024) k_scan_partials(EncodeArgs a) {
-  if (a.ws.status->pad2) return;
-  __shared__ uint32_t sh[1024];
-  const uint32_t P = uint32_t(a.ws.status->n_pieces);
-  const uint32_t nb = (P + 1 + SCAN_TILE - 1) / SCAN_TILE;
-  const uint32_t tid = threadIdx.x;
-  const uint32_t per = (nb + 1023) / 1024;
-  const uint32_t t0 = tid * per, t1 = min(nb, t0 + per);
-  uint32_t sum = 0;
-  for (uint32_t t = t0; t < t1; ++t) sum += a.ws.scan_part[t];
-  sh[tid] = sum;
-  __syncthreads();
-  for (uint32_t d = 1; d < 1024; d <<= 1) {
-    const uint32_t o = tid >= d ? sh[tid - d] : 0;
-    __syncthreads();
-    sh[tid] += o;
-    __syncthreads();
-  }
-  uint32_t run = sh[tid] - sum;
-  for (uint32_t t = t0; t < t1; ++t) {
-    const uint32_t c = a.ws.scan_part[t];
-    a.ws.scan_part[t] = run;
-    run += c;
-  }
-}
-
 __global__ void __launch_bounds__(SCAN_BLOCK) k_scan_down(EncodeArgs a) {
   if (a.ws.status->pad2) return;
   __shared__ uint32_t sh[SCAN_BLOCK];
@@ -1054,8 +1028,13 @@ __global__ void __launch_bounds__(SCAN_BLOCK) k_scan_down(EncodeArgs a) {
     v[k] = i < P ? a.ws.piece_cnt[i] : 0u;
     sum += v[k];
   }
+  // this block's base: the totals of the blocks before it (k_scan_reduce)
+  uint32_t before = 0;
+  for (uint32_t q = threadIdx.x; q < blockIdx.x; q += SCAN_BLOCK) before += a.ws.scan_part[q];
+  uint32_t base_total;
+  (void)block_excl_scan(before, sh, base_total);
   uint32_t total;
-  uint32_t run = block_excl_scan(sum, sh, total) + a.ws.scan_part[blockIdx.x];
+  uint32_t run = block_excl_scan(sum, sh, total) + base_total;
   for (uint32_t k = 0; k < SCAN_ITEMS; ++k) {
     const uint32_t i = b0 + threadIdx.x * SCAN_ITEMS + k;
     if (i <= P) a.ws.piece_off[i] = run;  // piece_off[P] is the total
@@ -1098,13 +1077,8 @@ __global__ void __launch_bounds__(ASM_BLOCK) k_assemble(EncodeArgs a) {
     __syncthreads();
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) a.ws.status->n_ids = total;
-}
-
-// id offset of every segment, and the segment of the first UTF-8 error
-__global__ void __launch_bounds__(256) k_seg_offsets(EncodeArgs a) {
-  if (a.ws.status->pad2) return;
-  const uint32_t P = uint32_t(a.ws.status->n_pieces);
-  for (uint32_t s = blockIdx.x * 256 + threadIdx.x; s <= a.n_seg; s += gridDim.x * 256) {
+  // id offset of every segment, and the segment of the first UTF-8 error
+  for (uint32_t s = blockIdx.x * ASM_BLOCK + threadIdx.x; s <= a.n_seg; s += gridDim.x * ASM_BLOCK) {
     const uint64_t o = a.seg_off[s];
     // first unit starting at or after o
     uint32_t lo = 0, hi = P;
@@ -1128,5 +1102,7 @@ __global__ void __launch_bounds__(256) k_seg_offsets(EncodeArgs a) {
     }
   }
 }
+
+
 
 }  // namespace bbpe

@@ -82,7 +82,8 @@ __global__ void k_init(EncodeArgs a) {
     s->n_chars = 0;
     s->err_seg = 0;
     // offsets must start at 0 and end at the text length (monotonicity is
-    // checked by k_check_offsets); every later kernel exits when pad2 is set
+    // checked by k_count, or k_check_offsets for an empty text); every later
+    // kernel exits when pad2 is set
     const bool ok = a.seg_off[0] == 0 && a.seg_off[a.n_seg] == a.n;
     s->pad2 = ok ? 0u : 1u;
   }
@@ -256,10 +257,12 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
 // Steps up to the ordered list of piece starts.
 void launch_front(Launcher &go, const EncodeArgs &a, const WsLayout &L) {
   go("k_init", k_init, dim3(1), dim3(64), a);
-  if (a.n_seg)
-    go("k_check_offsets", k_check_offsets, dim3(std::min<uint32_t>(1024, (a.n_seg + 255) / 256)),
-       dim3(256), a);
-  if (a.n == 0) return;
+  if (a.n == 0) {
+    if (a.n_seg)
+      go("k_check_offsets", k_check_offsets, dim3(std::min<uint32_t>(1024, (a.n_seg + 255) / 256)),
+         dim3(256), a);
+    return;
+  }
   const uint32_t T = L.n_tiles;
   go("k_count", k_count, dim3(T), dim3(64), a);
   go("k_scan_chars", k_scan_chars, dim3(1), dim3(1024), a);
@@ -372,11 +375,9 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
     HIP_OK(hipStreamWaitEvent(go.st, static_cast<hipEvent_t>(t->ev_join), 0));
     const uint32_t nscan = uint32_t((n + 1 + 4095) / 4096);
     go("k_scan_reduce", k_scan_reduce, dim3(nscan), dim3(256), a);
-    go("k_scan_partials", k_scan_partials, dim3(1), dim3(1024), a);
     go("k_scan_down", k_scan_down, dim3(nscan), dim3(256), a);
     const uint32_t agrid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
     go("k_assemble", k_assemble, dim3(agrid), dim3(256), a);
-    go("k_seg_offsets", k_seg_offsets, dim3(seg_grid), dim3(256), a);
   }
   Status h{};
   rc = finish(t, go, a, h);

@@ -73,6 +73,10 @@ __global__ void __launch_bounds__(64) k_count(EncodeArgs a) {
     a.ws.spst[w] = 0;
     a.ws.spc[w] = 0;
   }
+  // segment offsets must not decrease: every later kernel exits otherwise
+  // (k_count itself only reads them to place bits and indexes, all bounded)
+  for (uint32_t s = t * 64u + uint32_t(lane); s < a.n_seg; s += gridDim.x * 64u)
+    if (a.seg_off[s + 1] < a.seg_off[s]) a.ws.status->pad2 = 1u;
 }
 
 // ---------------------------------------------------------------------------

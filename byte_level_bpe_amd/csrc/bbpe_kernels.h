@@ -84,9 +84,7 @@ __global__ void k_merge(EncodeArgs a);
 __global__ void k_merge_long(EncodeArgs a);
 __global__ void k_merge_group(EncodeArgs a);
 __global__ void k_scan_reduce(EncodeArgs a);
-__global__ void k_scan_partials(EncodeArgs a);
 __global__ void k_scan_down(EncodeArgs a);
 __global__ void k_assemble(EncodeArgs a);
-__global__ void k_seg_offsets(EncodeArgs a);
 
 }  // namespace bbpe

@@ -396,6 +396,25 @@ def test_utf8_char_split_across_segments(atoms):
     assert (e.value.segment, e.value.byte_offset) == (0, 1)
 
 
+@pytest.mark.parametrize("offs", [[0, 10, 5, 20], [0, 25, 20], [3, 20], [0, 19]],
+                         ids=["decreasing", "past-end-then-back", "not-from-zero", "short-of-end"])
+def test_invalid_segment_offsets(atoms, offs):
+    """Segment offsets that decrease, or do not run from 0 to the text
+    length, are rejected with BBPE_E_INVALID_ARG (no kernel acts on them)."""
+    tok, _ = atoms
+    text, _, _, total = B.to_device_segments([(b"abcdefghij0123456789", False)], "cuda")
+    seg_off = torch.tensor(offs, dtype=torch.int64, device="cuda")
+    allow = torch.zeros(len(offs) - 1, dtype=torch.uint8, device="cuda")
+    say("invalid offsets", offs)
+    with pytest.raises(B.BBPEError) as e:
+        tok.encode_device(text, seg_off, allow, total)
+    assert e.value.status == B.E_INVALID_ARG
+    # the handle still encodes valid input afterwards
+    ids, _, n = tok.encode_device(text, torch.tensor([0, total], dtype=torch.int64, device="cuda"),
+                                  torch.zeros(1, dtype=torch.uint8, device="cuda"), total)
+    assert n > 0
+
+
 def test_capacity_and_empty(atoms):
     tok, orc = atoms
     say("capacity and empty inputs")
