@@ -32,31 +32,24 @@ namespace bbpe {
 // one workgroup: exclusive scan of units per tile; the total becomes P
 __global__ void __launch_bounds__(1024) k_scan_tiles_np(EncodeArgs a) {
   if (a.ws.status->pad2) return;
-  __shared__ uint32_t s_sum[1024];
+  __shared__ uint32_t s_sum[33];
   const uint32_t T = a.n_tiles;
   const uint32_t tid = threadIdx.x;
   const uint32_t per = (T + 1023) / 1024;
   const uint32_t t0 = tid * per, t1 = min(T, t0 + per);
   uint32_t sum = 0;
   for (uint32_t t = t0; t < t1; ++t) sum += a.ws.tile_np[t];
-  s_sum[tid] = sum;
-  __syncthreads();
-  for (uint32_t d = 1; d < 1024; d <<= 1) {
-    uint32_t v = tid >= d ? s_sum[tid - d] : 0;
-    __syncthreads();
-    s_sum[tid] += v;
-    __syncthreads();
-  }
-  uint32_t run = s_sum[tid] - sum;
+  uint32_t total;
+  uint32_t run = block_incl_scan<1024>(sum, 0u, [](uint32_t x, uint32_t y) { return x + y; }, s_sum, total) - sum;
   for (uint32_t t = t0; t < t1; ++t) {
     const uint32_t c = a.ws.tile_np[t];
     a.ws.tile_np[t] = run;
     run += c;
   }
   if (tid == 1023) {
-    a.ws.tile_np[T] = s_sum[1023];
-    a.ws.status->n_pieces = s_sum[1023];
-    a.ws.piece_start[s_sum[1023]] = uint32_t(a.n);
+    a.ws.tile_np[T] = total;
+    a.ws.status->n_pieces = total;
+    a.ws.piece_start[total] = uint32_t(a.n);
   }
 }
 

@@ -46,6 +46,70 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
   for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
   return v;
 }
+// Inclusive scan of op (associative, identity id) over the threads of a
+// block of NT threads in thread order: a wave scan by shuffles, then the
+// first wave scans the wave totals (sh: 2 * NT/64 + 1 entries of LDS).
+// total: op over all threads.
+template <uint32_t NT, typename T, typename Op>
+__device__ __forceinline__ T block_incl_scan(T v, T id, Op op, T *sh, T &total) {
+  constexpr uint32_t NW = NT / 64;
+  const int lane = int(threadIdx.x & 63);
+  const uint32_t wv = threadIdx.x / 64;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const T o = __shfl_up(v, d, 64);
+    if (lane >= d) v = op(o, v);
+  }
+  if (lane == 63) sh[wv] = v;
+  __syncthreads();
+  if (wv == 0) {
+    T x = uint32_t(lane) < NW ? sh[lane] : id;
+#pragma unroll
+    for (int d = 1; d < int(NW); d <<= 1) {
+      const T o = __shfl_up(x, d, 64);
+      if (lane >= d) x = op(o, x);
+    }
+    T ex = __shfl_up(x, 1, 64);
+    if (lane == 0) ex = id;
+    if (uint32_t(lane) < NW) sh[NW + lane] = ex;
+    if (uint32_t(lane) == NW - 1) sh[2 * NW] = x;
+  }
+  __syncthreads();
+  const T pre = sh[NW + wv];
+  total = sh[2 * NW];
+  __syncthreads();
+  return op(pre, v);
+}
+// The same in reverse thread order (thread NT-1 first): op(later, earlier).
+template <uint32_t NT, typename T, typename Op>
+__device__ __forceinline__ T block_incl_scan_rev(T v, T id, Op op, T *sh) {
+  constexpr uint32_t NW = NT / 64;
+  const int lane = int(threadIdx.x & 63);
+  const uint32_t wv = threadIdx.x / 64;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const T o = __shfl_down(v, d, 64);
+    if (lane + d < 64) v = op(o, v);
+  }
+  if (lane == 0) sh[wv] = v;
+  __syncthreads();
+  if (wv == 0) {
+    T x = uint32_t(lane) < NW ? sh[lane] : id;
+#pragma unroll
+    for (int d = 1; d < int(NW); d <<= 1) {
+      const T o = __shfl_down(x, d, 64);
+      if (uint32_t(lane + d) < NW) x = op(o, x);
+    }
+    T ex = __shfl_down(x, 1, 64);
+    if (uint32_t(lane) + 1 >= NW) ex = id;
+    if (uint32_t(lane) < NW) sh[NW + lane] = ex;
+  }
+  __syncthreads();
+  const T pre = sh[NW + wv];
+  __syncthreads();
+  return op(pre, v);
+}
+
 __device__ __forceinline__ int64_t wave_incl_max(int64_t v, int lane) {
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {

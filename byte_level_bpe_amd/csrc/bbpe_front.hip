@@ -85,23 +85,18 @@ __global__ void __launch_bounds__(64) k_count(EncodeArgs a) {
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) k_scan_chars(EncodeArgs a) {
   if (a.ws.status->pad2) return;
-  __shared__ unsigned long long s_sum[1024];
-  __shared__ long long s_max[1024];
+  __shared__ unsigned long long s_sum[33];
+  __shared__ long long s_max[33];
   const uint32_t T = a.n_tiles;
   const uint32_t tid = threadIdx.x;
   const uint32_t per = (T + 1023) / 1024;
   const uint32_t t0 = tid * per, t1 = min(T, t0 + per);
   unsigned long long sum = 0;
   for (uint32_t t = t0; t < t1; ++t) sum += a.ws.tile_nchar[t];
-  s_sum[tid] = sum;
-  __syncthreads();
-  for (uint32_t d = 1; d < 1024; d <<= 1) {
-    unsigned long long v = tid >= d ? s_sum[tid - d] : 0;
-    __syncthreads();
-    s_sum[tid] += v;
-    __syncthreads();
-  }
-  unsigned long long run = s_sum[tid] - sum;  // exclusive
+  unsigned long long total;
+  unsigned long long run =
+      block_incl_scan<1024>(sum, 0ull, [](unsigned long long x, unsigned long long y) { return x + y; },
+                            s_sum, total) - sum;  // exclusive
   long long mx = -1;
   for (uint32_t t = t0; t < t1; ++t) {
     a.ws.tile_charbase[t] = run;
@@ -109,21 +104,20 @@ __global__ void __launch_bounds__(1024) k_scan_chars(EncodeArgs a) {
     if (lc >= 0) mx = max(mx, (long long)(run + uint32_t(lc)));
     run += a.ws.tile_nchar[t];
   }
-  s_max[tid] = mx;
+  long long mall;
+  const long long mincl =
+      block_incl_scan<1024>(mx, -1ll, [](long long x, long long y) { return x > y ? x : y; }, s_max, mall);
+  // exclusive: the inclusive max of the thread before
+  __shared__ long long s_incl[1024];
+  s_incl[tid] = mincl;
   __syncthreads();
-  for (uint32_t d = 1; d < 1024; d <<= 1) {
-    long long v = tid >= d ? s_max[tid - d] : -1;
-    __syncthreads();
-    s_max[tid] = max(s_max[tid], v);
-    __syncthreads();
-  }
-  long long carry = tid > 0 ? s_max[tid - 1] : -1;
+  long long carry = tid > 0 ? s_incl[tid - 1] : -1;
   for (uint32_t t = t0; t < t1; ++t) {
     a.ws.tile_chgcarry[t] = carry;
     const int32_t lc = a.ws.tile_lastchg[t];
     if (lc >= 0) carry = max(carry, (long long)(a.ws.tile_charbase[t] + uint32_t(lc)));
   }
-  const unsigned long long total = s_sum[1023];
+  __syncthreads();
   for (uint32_t s = tid; s <= a.n_seg; s += 1024) {
     const uint64_t o = a.seg_off[s];
     if (s == a.n_seg || o >= a.n) {

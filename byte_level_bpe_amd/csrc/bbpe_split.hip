@@ -493,18 +493,18 @@ __device__ __forceinline__ void scan_split_body(const EncodeArgs &a) {
   uint32_t gv = FV_ID;
   for (uint32_t t = t0; t < t1; ++t) f = ltr_then<G>(f, a.ws.tile_fn[t] & ~uint64_t(0x300));
   for (uint32_t t = t1; t > t0; --t) gv = fv_then(gv, uint32_t(a.ws.tile_fn[t - 1] >> 8) & 3u);
-  s_f[tid] = f;
-  s_g[tid] = gv;
+  // scans over threads: LTR for (digit, CR / letter), RTL for v
+  __shared__ uint64_t s_wf[33];
+  __shared__ uint32_t s_wg[33];
+  uint64_t all_f;
+  const uint64_t in_f = block_incl_scan<1024>(
+      f, ltr_id<G>(), [](uint64_t x, uint64_t y) { return ltr_then<G>(x, y); }, s_wf, all_f);
+  const uint32_t in_g = block_incl_scan_rev<1024>(
+      gv, FV_ID, [](uint32_t x, uint32_t y) { return fv_then(x, y); }, s_wg);
+  // exclusive: the inclusive value of the neighbouring thread
+  s_f[tid] = in_f;
+  s_g[tid] = in_g;
   __syncthreads();
-  // exclusive scans over threads: LTR for (digit, CR / letter), RTL for v
-  for (uint32_t d = 1; d < 1024; d <<= 1) {
-    const uint64_t lf = tid >= d ? s_f[tid - d] : ltr_id<G>();
-    const uint32_t rg = tid + d < 1024 ? s_g[tid + d] : FV_ID;
-    __syncthreads();
-    s_f[tid] = ltr_then<G>(lf, s_f[tid]);
-    s_g[tid] = fv_then(rg, s_g[tid]);
-    __syncthreads();
-  }
   const uint64_t ex_f = tid > 0 ? s_f[tid - 1] : ltr_id<G>();
   const uint32_t ex_g = tid + 1 < 1024 ? s_g[tid + 1] : FV_ID;
   // the text starts outside any digit run, with no CR run / in state F
