@@ -294,28 +294,31 @@ __device__ __forceinline__ uint32_t above32(int j) { return ~((2u << j) - 1u); }
 // Merge a unit of 2 <= m <= SK bytes held in registers: pair ranks r[j] and
 // part ids pr[j] at every part start j, part starts as the bit mask bnd.
 // Writes the ids to out and returns their count.
-// atom: the 256 atom ranks (a copy in LDS).
+// atom: the 256 atom ranks (a copy in LDS).  lp: this lane's column of an
+// LDS array [32][64] holding the id of the part starting at each position
+// (read and written at per-lane positions without select chains).  Pair
+// ranks stay in registers as keys (rank << 5 | position, or ~0 for none), so
+// the leftmost least rank is one unsigned minimum per position.
 template <int SK>
 __device__ __forceinline__ uint32_t merge_short(const DevTables &T, const int32_t *atom,
-                                                const UnitBytes<SK> &u, uint32_t m, int32_t *out) {
-  int32_t r[SK], pr[SK];
+                                                const UnitBytes<SK> &u, uint32_t m, int32_t *lp,
+                                                int32_t *out) {
+  uint32_t r[SK];
 #pragma unroll
   for (int j = 0; j < SK; ++j) {
     const uint32_t b0 = u.byte(j), b1 = (j + 1 < SK) ? u.byte(j + 1) : 0u;
-    r[j] = (uint32_t(j) + 1 < m) ? T.pair[b0 * 256u + b1] : RANK_NONE;
-    pr[j] = (uint32_t(j) < m) ? atom[b0] : 0;
+    const int32_t rk = (uint32_t(j) + 1 < m) ? T.pair[b0 * 256u + b1] : RANK_NONE;
+    r[j] = rk == RANK_NONE ? ~0u : (uint32_t(rk) << 5) | uint32_t(j);
+    if (uint32_t(j) < m) lp[64 * j] = atom[b0];
   }
   uint32_t bnd = (m >= 32) ? 0xFFFFFFFFu : ((1u << m) - 1u);
   for (uint32_t round = 0; round + 1 < m; ++round) {
-    int32_t best = RANK_NONE;
-    int bj = 0;
+    uint32_t key = ~0u;
 #pragma unroll
-    for (int j = 0; j < SK; ++j) {
-      const bool lt = r[j] < best;  // strict: the leftmost minimum wins
-      best = lt ? r[j] : best;
-      bj = lt ? j : bj;
-    }
-    if (best == RANK_NONE) break;
+    for (int j = 0; j < SK; ++j) key = min(key, r[j]);
+    if (key == ~0u) break;
+    const int bj = int(key & 31u);
+    const int32_t best = int32_t(key >> 5);
     const int k = __ffs(bnd & above32(bj)) - 1;  // the part merged into bj
     bnd &= ~(1u << k);
     const uint32_t after = bnd & above32(bj);
@@ -323,27 +326,25 @@ __device__ __forceinline__ uint32_t merge_short(const DevTables &T, const int32_
     const uint32_t before = bnd & ((1u << bj) - 1u);
     const int q = before ? 31 - __clz(before) : -1;
     // the merged part (id best) with its right and left neighbours
-    int32_t id2 = 0, idq = 0;
-#pragma unroll
-    for (int j = 0; j < SK; ++j) {
-      id2 = uint32_t(j) == k2 ? pr[j] : id2;
-      idq = j == q ? pr[j] : idq;
-    }
+    const int32_t id2 = after ? lp[64 * k2] : 0;
+    const int32_t idq = q >= 0 ? lp[64 * q] : 0;
     int32_t nb, nq;
     merge_rank2(T, after != 0, uint32_t(best), uint32_t(id2), q >= 0, uint32_t(idq), uint32_t(best),
                 nb, nq);
+    lp[64 * bj] = best;
+    const uint32_t kb = nb == RANK_NONE ? ~0u : (uint32_t(nb) << 5) | uint32_t(bj);
+    const uint32_t kq = nq == RANK_NONE ? ~0u : (uint32_t(nq) << 5) | uint32_t(q);
 #pragma unroll
     for (int j = 0; j < SK; ++j) {
-      r[j] = (j == k) ? RANK_NONE : r[j];
-      r[j] = (j == bj) ? nb : r[j];
-      pr[j] = (j == bj) ? best : pr[j];
-      r[j] = (j == q) ? nq : r[j];
+      r[j] = (j == k) ? ~0u : r[j];
+      r[j] = (j == bj) ? kb : r[j];
+      r[j] = (j == q) ? kq : r[j];
     }
   }
   uint32_t c = 0;
 #pragma unroll
   for (int j = 0; j < SK; ++j)
-    if ((bnd >> j) & 1u) out[c++] = pr[j];
+    if ((bnd >> j) & 1u) out[c++] = lp[64 * j];
   return c;
 }
 
@@ -659,12 +660,13 @@ __device__ __forceinline__ uint32_t chain_then(uint32_t f, uint32_t g) {
 }
 
 template <int SK>
-__device__ __forceinline__ void merge_short_unit(const EncodeArgs &a, const int32_t *atom, uint32_t i) {
+__device__ __forceinline__ void merge_short_unit(const EncodeArgs &a, const int32_t *atom, uint32_t i,
+                                                 int32_t *lp) {
   const uint32_t s = a.ws.piece_start[i];
   const uint32_t m = a.ws.piece_start[i + 1] - s;
   UnitBytes<SK> u;
   load_unit(a.text, a.n, s, m, u);
-  a.ws.piece_cnt[i] = merge_short<SK>(a.T, atom, u, m, a.ws.tmp_ids + s);
+  a.ws.piece_cnt[i] = merge_short<SK>(a.T, atom, u, m, lp, a.ws.tmp_ids + s);
 }
 
 // Merge of the short units: chunks of 64 units of one length class (one
@@ -684,21 +686,23 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
                  e4 = e8 + (n4 + 63) / 64;
   if (blockIdx.x >= e4) return;
   __shared__ int32_t s_atom[256];
+  __shared__ int32_t s_part[32 * 64];  // [position][lane]: part ids of each lane's unit
+  int32_t *lp = s_part + lane;
   reinterpret_cast<int4 *>(s_atom)[lane] = reinterpret_cast<const int4 *>(a.T.atom)[lane];
   __syncthreads();
   for (uint32_t item = blockIdx.x; item < e4; item += gridDim.x) {
     if (item < e32) {
       const uint32_t x = item * 64 + uint32_t(lane);
-      if (x < n32) merge_short_unit<32>(a, s_atom, a.ws.lst[ML_32][x]);
+      if (x < n32) merge_short_unit<32>(a, s_atom, a.ws.lst[ML_32][x], lp);
     } else if (item < e16) {
       const uint32_t x = (item - e32) * 64 + uint32_t(lane);
-      if (x < n16) merge_short_unit<16>(a, s_atom, a.ws.lst[ML_16][x]);
+      if (x < n16) merge_short_unit<16>(a, s_atom, a.ws.lst[ML_16][x], lp);
     } else if (item < e8) {
       const uint32_t x = (item - e16) * 64 + uint32_t(lane);
-      if (x < n8) merge_short_unit<8>(a, s_atom, a.ws.lst[ML_8][x]);
+      if (x < n8) merge_short_unit<8>(a, s_atom, a.ws.lst[ML_8][x], lp);
     } else {
       const uint32_t x = (item - e8) * 64 + uint32_t(lane);
-      if (x < n4) merge_short_unit<4>(a, s_atom, a.ws.lst[ML_4][x]);
+      if (x < n4) merge_short_unit<4>(a, s_atom, a.ws.lst[ML_4][x], lp);
     }
   }
 }
