@@ -151,11 +151,12 @@ __device__ __forceinline__ void classify_slow(const DevTables &T, const uint8_t 
       if (c >= 0xD800 && c <= 0xDFFF) good = false;
       cp[k] = c;
       ok[k] = good;
-      // loads issued unconditionally (index 0 when unused): a load under a
-      // condition is waited for on its own
-      blk[k] = T.uni1[good ? (c >> 8) : 0u];
     }
+    // class-table loads issued unconditionally (index 0 when unused: a load
+    // under a condition is waited for on its own)
     uint32_t cls[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) blk[k] = T.uni1[ok[k] ? (cp[k] >> 8) : 0u];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const uint32_t c = T.uni2[ok[k] ? blk[k] * 256u + (cp[k] & 0xFFu) : 0u];
@@ -190,9 +191,11 @@ __device__ __forceinline__ void classify_slow(const DevTables &T, const uint8_t 
 
 // Classify the 64 bytes of the word at text offset base (window = bytes
 // [base-16, base+80)).  seg_lo/seg_hi: segment starts at window indices
-// -8..119 (bit j <-> index j-8).  The multi-byte part comes from slow_in
-// (the word's stored record) when given, else it is computed, and stored to
-// slow_out when given.
+// -8..119 (bit j <-> index j-8).  COMPUTE: the multi-byte part is computed
+// (and stored to slow_out when given); else it is read from slow_in, the
+// word's stored record (kernels after the first never decode, which keeps
+// the decoder's registers out of them).
+template <bool COMPUTE>
 __device__ __forceinline__ void classify_word(const DevTables &T, const uint8_t *__restrict__ text,
                                               const Window &win, int64_t base, uint64_t n,
                                               uint64_t seg_lo, uint64_t seg_hi, WordMasks &m,
@@ -255,7 +258,7 @@ __device__ __forceinline__ void classify_word(const DevTables &T, const uint8_t 
   m.na = non;
   if (non) {
     SlowMasks r;
-    if (slow_in) {
+    if (!COMPUTE) {
       const ulonglong2 *q = reinterpret_cast<const ulonglong2 *>(slow_in);
       const ulonglong2 v0 = q[0], v1 = q[1], v2 = q[2], v3 = q[3], v4 = q[4];
       r = SlowMasks{v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y, v4.x, v4.y};

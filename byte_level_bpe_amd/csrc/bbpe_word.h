@@ -38,9 +38,12 @@ __device__ __forceinline__ void word_setup(const EncodeArgs &a, int64_t w, bool 
       a.ws.wseg_at[w] = seg_at;
     }
   }
+  // (a word outside [0, n_words) has no valid byte: classify_word returns
+  // before the multi-byte part, so later kernels read a record only for
+  // words that have one)
   uint64_t *rec = in ? a.ws.wslow + uint64_t(w) * SLOW_WORDS : nullptr;
-  classify_word(a.T, a.text, win, base, a.n, seg_lo, seg_hi, m, FIRST ? nullptr : rec,
-                (FIRST && owned) ? rec : nullptr);
+  classify_word<FIRST>(a.T, a.text, win, base, a.n, seg_lo, seg_hi, m, FIRST ? nullptr : rec,
+                       (FIRST && owned) ? rec : nullptr);
 }
 
 }  // namespace bbpe
