@@ -32,11 +32,12 @@ E_STATE = -9
 GRAMMAR_CL100K = 0
 GRAMMAR_O200K_STYLE = 1
 TIKTOKEN_SAFE = 1
+COUNT_ONLY = 2
 
 # every symbol include/bbpe.h declares
 EXPORTS = ["bbpe_load_ranks", "bbpe_load_ranks_tiktoken_file", "bbpe_upload_tables",
            "bbpe_workspace_bytes", "bbpe_encode_segments", "bbpe_pretokenize_segments",
-           "bbpe_decode", "bbpe_error_detail",
+           "bbpe_decode", "bbpe_decode_workspace_bytes", "bbpe_decode_device", "bbpe_error_detail",
            "bbpe_table_info", "bbpe_set_timing", "bbpe_timing_report", "bbpe_timing_reset",
            "bbpe_free", "bbpe_status_str"]
 
@@ -74,6 +75,11 @@ def _load():
                                                   C.POINTER(U64), P]
         lib.bbpe_decode.restype = I
         lib.bbpe_decode.argtypes = [P, P, U64, P, U64, C.POINTER(U64)]
+        lib.bbpe_decode_workspace_bytes.restype = I
+        lib.bbpe_decode_workspace_bytes.argtypes = [P, U64, C.POINTER(U64)]
+        lib.bbpe_decode_device.restype = I
+        lib.bbpe_decode_device.argtypes = [P, P, U64, P, U64, P, P, U64, C.POINTER(U64),
+                                           C.POINTER(U64), P]
         lib.bbpe_error_detail.restype = I
         lib.bbpe_error_detail.argtypes = [P, C.POINTER(U32), C.POINTER(U64)]
         lib.bbpe_table_info.restype = I
@@ -121,6 +127,7 @@ class Tokenizer:
         self.table_bytes = int(table_bytes)
         self._dev_table = None
         self._ws = None
+        self._dws = None
 
     def __del__(self):
         if getattr(self, "_h", None) and _lib is not None:
@@ -183,25 +190,29 @@ class Tokenizer:
         return self._ws
 
     def encode_device(self, text, seg_off, allow, total_bytes: int, tiktoken_safe: bool = True,
-                      ids=None, id_off=None, stream=None):
+                      ids=None, id_off=None, stream=None, count_only: bool = False):
         """Encode segments already resident on the device.
 
         text: uint8 tensor (16-byte aligned); seg_off: int64 tensor [n_seg+1]
         (read as uint64); allow: uint8 tensor [n_seg].  Returns (ids[:n],
-        id_off, n) with ids an int32 tensor."""
+        id_off, n) with ids an int32 tensor; with count_only, (None, id_off,
+        n) and no ids are written."""
         import torch
         self.upload(text.device)
         n_seg = int(seg_off.numel()) - 1
         ws = self.workspace(total_bytes, n_seg, text.device)
-        if ids is None:
+        if ids is None and not count_only:
             ids = torch.empty(max(1, total_bytes), dtype=torch.int32, device=text.device)
         if id_off is None:
             id_off = torch.empty(n_seg + 1, dtype=torch.int64, device=text.device)
+        flags = (TIKTOKEN_SAFE if tiktoken_safe else 0) | (COUNT_ONLY if count_only else 0)
+        ids_ptr = None if count_only else C.c_void_p(ids.data_ptr())
+        ids_cap = 0 if count_only else ids.numel()
         n = C.c_uint64(0)
         st = _load().bbpe_encode_segments(
             self._h, C.c_void_p(text.data_ptr()), int(total_bytes), C.c_void_p(seg_off.data_ptr()),
-            C.c_void_p(allow.data_ptr()), n_seg, TIKTOKEN_SAFE if tiktoken_safe else 0,
-            C.c_void_p(ws.data_ptr()), ws.numel(), C.c_void_p(ids.data_ptr()), ids.numel(),
+            C.c_void_p(allow.data_ptr()), n_seg, flags,
+            C.c_void_p(ws.data_ptr()), ws.numel(), ids_ptr, ids_cap,
             C.c_void_p(id_off.data_ptr()), C.byref(n), _stream_handle(stream))
         if st == E_UTF8:
             seg, off = C.c_uint32(), C.c_uint64()
@@ -211,6 +222,8 @@ class Tokenizer:
             raise err
         if st:
             raise BBPEError(st, "encode_segments")
+        if count_only:
+            return None, id_off, n.value
         return ids[:n.value], id_off, n.value
 
     def pretokenize_device(self, text, seg_off, allow, total_bytes: int, tiktoken_safe: bool = True,
@@ -244,6 +257,60 @@ class Tokenizer:
 
     def encode(self, text, allow_special: bool = False, tiktoken_safe: bool = True, device="cuda"):
         return self.encode_segments([(text, allow_special)], tiktoken_safe, device)[0]
+
+    def count_segments(self, segments, tiktoken_safe: bool = True, device="cuda", stream=None):
+        """segments: [(bytes | str, allow_special)] -> int64 tensor of per-segment token
+        counts (no ids are written)."""
+        text, seg_off, allow, total = to_device_segments(segments, device)
+        _, id_off, _ = self.encode_device(text, seg_off, allow, total, tiktoken_safe,
+                                          stream=stream, count_only=True)
+        return id_off[1:] - id_off[:-1]
+
+    def decode_workspace_bytes(self, n_ids: int) -> int:
+        out = C.c_uint64()
+        st = _load().bbpe_decode_workspace_bytes(self._h, int(n_ids), C.byref(out))
+        if st:
+            raise BBPEError(st, "decode_workspace_bytes")
+        return out.value
+
+    def decode_device(self, ids, out=None, offsets: bool = False, tok_off=None, stream=None):
+        """Decode an int32 id tensor on its device.
+
+        Returns (bytes as a uint8 tensor, per-token byte offsets as an int64
+        tensor or None, complete_len): complete_len is the length of the
+        longest prefix ending on a complete UTF-8 character.  Without `out`,
+        the output is sized 8 bytes per id and, when that is too small,
+        sized exactly and decoded again."""
+        import torch
+        dev = ids.device
+        self.upload(dev)
+        n_ids = int(ids.numel())
+        need = self.decode_workspace_bytes(n_ids)
+        if self._dws is None or self._dws.numel() < need:
+            self._dws = torch.empty(need, dtype=torch.uint8, device=dev)
+        if offsets and tok_off is None:
+            tok_off = torch.empty(max(1, n_ids), dtype=torch.int64, device=dev)
+        sized = out is not None
+        if out is None:
+            out = torch.empty(max(1, 8 * n_ids), dtype=torch.uint8, device=dev)
+        n, done = C.c_uint64(0), C.c_uint64(0)
+
+        def call(buf):
+            return _load().bbpe_decode_device(
+                self._h, C.c_void_p(ids.data_ptr()) if n_ids else None, n_ids,
+                C.c_void_p(buf.data_ptr()), buf.numel(),
+                C.c_void_p(tok_off.data_ptr()) if tok_off is not None else None,
+                C.c_void_p(self._dws.data_ptr()), self._dws.numel(), C.byref(n), C.byref(done),
+                _stream_handle(stream))
+        st = call(out)
+        if st == E_CAPACITY and not sized:
+            out = torch.empty(max(1, n.value), dtype=torch.uint8, device=dev)
+            st = call(out)
+        if st == E_BAD_ID:
+            raise BBPEError(st, "decode_device at index %d" % n.value)
+        if st:
+            raise BBPEError(st, "decode_device")
+        return out[:n.value], (tok_off[:n_ids] if tok_off is not None else None), done.value
 
     # ---- host side ----
     def decode(self, ids) -> bytes:

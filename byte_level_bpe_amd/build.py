@@ -15,7 +15,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("BBPE_ARCH", "gfx950")
 
 SOURCES = ["bbpe_tables.cpp", "bbpe_front.hip", "bbpe_split.hip", "bbpe_back.hip",
-           "bbpe_encode.hip"]
+           "bbpe_encode.hip", "bbpe_decode.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I" + os.path.join(HERE, "..", "include")]
 HIPFLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -10,6 +10,7 @@
 #include "../../include/bbpe.h"
 #include "bbpe_internal.h"
 #include "bbpe_kernels.h"
+#include "bbpe_launch.h"
 #include "bbpe_tokenizer.h"
 
 using namespace bbpe;
@@ -124,62 +125,6 @@ __global__ void k_err_seg(EncodeArgs a) {
   }
 }
 
-#define HIP_OK(x)                               \
-  do {                                          \
-    if ((x) != hipSuccess) return BBPE_E_HIP;   \
-  } while (0)
-
-// Launches kernels on the caller's stream `st` (or, after use(), another);
-// with timing enabled on the handle, every launch is bracketed by two events
-// from the handle's pool.
-struct Launcher {
-  bbpe_tokenizer *t;
-  hipStream_t st;
-  hipStream_t cur = st;
-  std::vector<std::pair<int, size_t>> recs;  // (kernel index, first event)
-  size_t next = 0;
-
-  int kernel_index(const char *name) {
-    for (size_t i = 0; i < t->t_names.size(); ++i)
-      if (t->t_names[i] == name) return int(i);
-    t->t_names.emplace_back(name);
-    t->t_ms.push_back(0.0);
-    t->t_launches.push_back(0);
-    return int(t->t_names.size() - 1);
-  }
-  hipEvent_t event(size_t i) {
-    while (t->t_events.size() <= i) {
-      hipEvent_t e = nullptr;
-      if (hipEventCreate(&e) != hipSuccess) e = nullptr;
-      t->t_events.push_back(e);
-    }
-    return static_cast<hipEvent_t>(t->t_events[i]);
-  }
-  template <typename K, typename... A>
-  void operator()(const char *name, K kernel, dim3 grid, dim3 block, A... args) {
-    const bool timed = t->timing;
-    if (timed) (void)hipEventRecord(event(next), cur);
-    hipLaunchKernelGGL(kernel, grid, block, 0, cur, args...);
-    if (timed) {
-      (void)hipEventRecord(event(next + 1), cur);
-      recs.emplace_back(kernel_index(name), next);
-      next += 2;
-    }
-  }
-  void use(hipStream_t s) { cur = s; }
-  // after the streams have been synchronised
-  void collect() {
-    for (auto &r : recs) {
-      float ms = 0.f;
-      if (hipEventElapsedTime(&ms, event(r.second), event(r.second + 1)) == hipSuccess) {
-        t->t_ms[size_t(r.first)] += ms;
-        t->t_launches[size_t(r.first)] += 1;
-      }
-    }
-    recs.clear();
-  }
-};
-
 // The handle's second stream and its fork/join events, created once.
 int ensure_aux(bbpe_tokenizer *t) {
   if (t->aux_stream) return BBPE_OK;
@@ -204,7 +149,8 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
             EncodeArgs &a, WsLayout &L) {
   if (!t || !d_seg_off || (n_seg && !d_allow)) return BBPE_E_INVALID_ARG;
   if (n && (!d_text || (reinterpret_cast<uintptr_t>(d_text) & 15))) return BBPE_E_INVALID_ARG;
-  if (n >= (uint64_t(1) << 32) - 64 || (flags & ~uint32_t(BBPE_TIKTOKEN_SAFE))) return BBPE_E_INVALID_ARG;
+  if (n >= (uint64_t(1) << 32) - 64 || (flags & ~uint32_t(BBPE_TIKTOKEN_SAFE | BBPE_COUNT_ONLY)))
+    return BBPE_E_INVALID_ARG;
   if (n_seg == 0 && n != 0) return BBPE_E_INVALID_ARG;
   if (!t->d_image) return BBPE_E_STATE;
   L = layout_for(n, n_seg);
@@ -321,6 +267,9 @@ int bbpe_upload_tables(bbpe_tokenizer *t, void *d_mem, uint64_t bytes, void *str
   d.inner = reinterpret_cast<const uint32_t *>(b + L.inner);
   d.mt = reinterpret_cast<const uint64_t *>(b + L.mt);
   d.k3 = reinterpret_cast<const uint32_t *>(b + L.k3);
+  d.dec = reinterpret_cast<const uint64_t *>(b + L.dec);
+  d.dblob = b + L.dblob;
+  d.dsp = reinterpret_cast<const uint64_t *>(b + L.dsp);
   d.q4 = reinterpret_cast<const uint32_t *>(b + L.q4);
   t->d_image = b;
   return BBPE_OK;
@@ -338,6 +287,8 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
                          uint32_t flags, void *d_ws, uint64_t ws_bytes, int32_t *d_ids,
                          uint64_t ids_cap, int64_t *d_id_off, uint64_t *n_ids, void *stream) {
   if (!d_id_off || !n_ids || (ids_cap && !d_ids)) return BBPE_E_INVALID_ARG;
+  const bool count_only = (flags & BBPE_COUNT_ONLY) != 0;
+  if (count_only) ids_cap = 0;  // k_assemble then copies no ids
   EncodeArgs a;
   WsLayout L;
   int rc = prepare(t, d_text, n, d_seg_off, d_allow, n_seg, flags, d_ws, ws_bytes, a, L);
@@ -383,7 +334,7 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
   rc = finish(t, go, a, h);
   if (rc) return rc;
   *n_ids = h.n_ids;
-  if (h.n_ids > ids_cap) return BBPE_E_CAPACITY;
+  if (h.n_ids > ids_cap && !count_only) return BBPE_E_CAPACITY;
   return BBPE_OK;
 }
 
@@ -392,7 +343,7 @@ int bbpe_pretokenize_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t
                               uint32_t flags, void *d_ws, uint64_t ws_bytes, uint32_t *d_starts,
                               uint64_t starts_cap, uint8_t *d_is_special, uint64_t *n_pieces,
                               void *stream) {
-  if (!n_pieces || (starts_cap && !d_starts)) return BBPE_E_INVALID_ARG;
+  if (!n_pieces || (starts_cap && !d_starts) || (flags & BBPE_COUNT_ONLY)) return BBPE_E_INVALID_ARG;
   EncodeArgs a;
   WsLayout L;
   int rc = prepare(t, d_text, n, d_seg_off, d_allow, n_seg, flags, d_ws, ws_bytes, a, L);

@@ -92,6 +92,10 @@ struct DevTables {
   const uint32_t *inner;    // [2048] bit (a*256+b): the byte pair (a,b) occurs inside some key
   const uint64_t *mt;       // merge table, [mt_mask+1] buckets of MT_BUCKET entries
   const uint32_t *k3;       // [2^24 bits] bit (a<<16|b<<8|c): the 3-byte string abc is a key
+  const uint64_t *dec;      // [dec_n] per rank: offset in dblob << 8 | length, or 0 (no such rank)
+  const uint8_t *dblob;     // bytes of every key and special, for decode
+  const uint64_t *dsp;      // [2 n_sp] specials sorted by id: id, then offset << 8 | length
+  uint32_t dec_n;           // largest rank + 1
   const uint32_t *q4;       // [2^24 bits] bit q4_index(abcd): abcd may occur inside a key
                             //   (every 4-byte substring of a key sets its bit)
   uint32_t mt_mask;
@@ -107,7 +111,8 @@ struct DevTables {
 
 // Byte offsets of each table inside the uploaded image.
 struct ImageLayout {
-  uint64_t slots, ext, blob, pair, atom, uni1, uni2, sp_bytes, sp_off, sp_id, inner, mt, k3, q4, total;
+  uint64_t slots, ext, blob, pair, atom, uni1, uni2, sp_bytes, sp_off, sp_id, inner, mt, k3, q4, dec,
+      dblob, dsp, total;
   uint32_t n_slots;
   uint32_t n_mt_buckets;
 };

@@ -197,6 +197,11 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
   L.mt = o; o = align256(o + uint64_t(n_mt) * bbpe::MT_BUCKET * 8);
   L.k3 = o; o = align256(o + (uint64_t(1) << 24) / 8);
   L.q4 = o; o = align256(o + (uint64_t(1) << 24) / 8);
+  int32_t max_rank = 0;
+  for (uint32_t i = 0; i < n; ++i) max_rank = std::max(max_rank, rk[i]);
+  L.dec = o; o = align256(o + 8 * (uint64_t(max_rank) + 1));
+  L.dblob = o; o = align256(o + t->dec_blob.size() + 16);
+  L.dsp = o; o = align256(o + 16 * (sp.size() + 1));
   L.total = o;
   L.n_slots = n_slots;
   L.n_mt_buckets = n_mt;
@@ -277,6 +282,24 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
       q4[b >> 5] |= 1u << (b & 31);
     }
   }
+  // decode: rank -> (offset, length) into the decode blob; specials by id
+  {
+    uint64_t *dec = reinterpret_cast<uint64_t *>(img + L.dec);
+    memcpy(img + L.dblob, t->dec_blob.data(), t->dec_blob.size());
+    auto entry = [&](int32_t id) -> uint64_t {
+      return t->dense ? t->dec_dense[size_t(id)] : t->dec_sparse.at(id);
+    };
+    for (uint32_t i = 0; i < n; ++i) dec[rk[i]] = entry(rk[i]);
+    std::vector<std::pair<uint64_t, uint64_t>> dsp;
+    for (size_t i = 0; i < sp.size(); ++i) dsp.emplace_back(uint64_t(spid[i]), entry(spid[i]));
+    std::sort(dsp.begin(), dsp.end());
+    uint64_t *dst = reinterpret_cast<uint64_t *>(img + L.dsp);
+    for (size_t i = 0; i < dsp.size(); ++i) {
+      dst[2 * i] = dsp[i].first;
+      dst[2 * i + 1] = dsp[i].second;
+    }
+    t->dev_dec_n = uint32_t(max_rank) + 1;
+  }
   uint64_t *mt = reinterpret_cast<uint64_t *>(img + L.mt);
   for (uint64_t e : mt_entries) {
     const uint64_t key = (e >> bbpe::MT_ID_BITS) & ((uint64_t(1) << (2 * bbpe::MT_ID_BITS)) - 1);
@@ -297,6 +320,7 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
   d = bbpe::DevTables{};
   d.slot_mask = n_slots - 1;
   d.mt_mask = n_mt - 1;
+  d.dec_n = t->dev_dec_n;
   d.mt_shift = 64 - mt_log;
   d.n_sp = uint32_t(sp.size());
   for (auto &s : sp) d.sp_first[uint8_t(s[0]) >> 5] |= 1u << (uint8_t(s[0]) & 31);

@@ -27,6 +27,7 @@ struct bbpe_tokenizer {
   const uint8_t *d_image = nullptr;
   bbpe::DevTables dev{};
   uint32_t max_key_len = 0;
+  uint32_t dev_dec_n = 0;  // largest rank + 1 (the device decode table's size)
   uint32_t n_self_consistent = 0;
   // per-kernel timing (diagnostics)
   bool timing = false;

@@ -66,7 +66,9 @@ enum { BBPE_GRAMMAR_CL100K = 0, BBPE_GRAMMAR_O200K_STYLE = 1 };
 
 /* encode flags */
 enum {
-  BBPE_TIKTOKEN_SAFE = 1u << 0 /* 400k-character windows, 25k-character run cuts */
+  BBPE_TIKTOKEN_SAFE = 1u << 0, /* 400k-character windows, 25k-character run cuts */
+  BBPE_COUNT_ONLY = 1u << 1     /* token counts only: d_id_off and *n_ids are written,
+                                   d_ids is not (it may be null, ids_capacity 0) */
 };
 
 /* Limits of this implementation. */
@@ -133,7 +135,8 @@ int bbpe_workspace_bytes(const bbpe_tokenizer *tok, uint64_t total_text_bytes, u
  *                     BBPE_E_INVALID_ARG otherwise);
  *   d_allow_special[n_seg]: device, 1 = match specials in this segment,
  *                     0 = specials are ordinary text;
- *   flags:            BBPE_TIKTOKEN_SAFE or 0;
+ *   flags:            BBPE_TIKTOKEN_SAFE, BBPE_COUNT_ONLY, both or 0 (count-only:
+ *                     per-segment token counts for token budgets, no ids);
  *   d_workspace:      device scratch of at least bbpe_workspace_bytes(),
  *                     256-byte aligned; its contents are not preserved;
  *   d_ids:            device output, int32, capacity ids_capacity;
@@ -148,7 +151,12 @@ int bbpe_workspace_bytes(const bbpe_tokenizer *tok, uint64_t total_text_bytes, u
  * leaves d_ids unspecified.  Invalid UTF-8 in any segment returns
  * BBPE_E_UTF8; bbpe_error_detail then reports the first offending segment and
  * byte.  The call synchronises the stream once, at its end, to read the
- * status and *n_ids; that is its only host synchronisation. */
+ * status and *n_ids; that is its only host synchronisation.
+ *
+ * With BBPE_COUNT_ONLY the call writes d_id_off and *n_ids only: the per-
+ * segment token counts are d_id_off[s+1] - d_id_off[s] (token budgets: the
+ * tiktoken deep-dive page, "Counting tokens for a budget"); d_ids may
+ * be null and no capacity error is returned. */
 int bbpe_encode_segments(bbpe_tokenizer *tok, const uint8_t *d_text, uint64_t total_bytes,
                          const uint64_t *d_seg_off, const uint8_t *d_allow_special,
                          uint32_t n_seg, uint32_t flags,
@@ -164,7 +172,8 @@ int bbpe_encode_segments(bbpe_tokenizer *tok, const uint8_t *d_text, uint64_t to
  * receives the count; BBPE_E_CAPACITY if it exceeds starts_cap.  Pieces
  * never cross a chunk cut, a special or a segment boundary (tiktoken
  * deep-dive page, "The split pattern": merges never cross a cut).  Same
- * arguments, errors and synchronisation as bbpe_encode_segments. */
+ * arguments, errors and synchronisation as bbpe_encode_segments
+ * (BBPE_COUNT_ONLY is not accepted here: BBPE_E_INVALID_ARG). */
 int bbpe_pretokenize_segments(bbpe_tokenizer *tok, const uint8_t *d_text, uint64_t total_bytes,
                               const uint64_t *d_seg_off, const uint8_t *d_allow_special,
                               uint32_t n_seg, uint32_t flags, void *d_workspace,
@@ -179,6 +188,27 @@ int bbpe_pretokenize_segments(bbpe_tokenizer *tok, const uint8_t *d_text, uint64
  * small (*out_len = bytes needed). */
 int bbpe_decode(const bbpe_tokenizer *tok, const int32_t *ids, uint64_t n, uint8_t *out,
                 uint64_t cap, uint64_t *out_len);
+
+/* Decode on the device.  d_ids[n_ids] (device, int32) -> d_out (device,
+ * capacity out_capacity): the concatenation of each token's bytes, specials
+ * decoded to their strings (tiktoken deep-dive page, "An encoding is three
+ * objects").  When d_tok_off (device, uint64[n_ids]) is not null it receives
+ * each token's byte offset in the output, which for the ids of one encode
+ * call is the token's byte offset in the text it came from.  *out_len (host)
+ * receives the output length; *complete_len (host, may be null) the length of
+ * the longest prefix that ends on a complete UTF-8 character, so that a
+ * streaming caller can hold back a partial character (a token may end inside
+ * one: tiktoken deep-dive page, "Pitfalls that bite in production").  d_workspace: device, at least
+ * bbpe_decode_workspace_bytes(), 256-byte aligned.  Returns BBPE_E_BAD_ID for
+ * an id that is neither a rank nor a special (*out_len = the index of the
+ * first), BBPE_E_CAPACITY when out_capacity is too small (*out_len = bytes
+ * needed; d_out is then not written, d_tok_off is).  Enqueues on hip_stream
+ * and synchronises it once, at the end. */
+int bbpe_decode_workspace_bytes(const bbpe_tokenizer *tok, uint64_t n_ids, uint64_t *out_bytes);
+int bbpe_decode_device(bbpe_tokenizer *tok, const int32_t *d_ids, uint64_t n_ids,
+                       uint8_t *d_out, uint64_t out_capacity, uint64_t *d_tok_off,
+                       void *d_workspace, uint64_t workspace_bytes, uint64_t *out_len,
+                       uint64_t *complete_len, void *hip_stream);
 
 /* Details of the last BBPE_E_UTF8 from bbpe_encode_segments on this handle:
  * the segment index and the absolute byte offset in d_text of the first

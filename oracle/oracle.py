@@ -181,6 +181,21 @@ class Oracle:
             raise OracleError(st, "at %d" % n.value)
         return out[:n.value].tobytes()
 
+    def token_offsets(self, ids) -> np.ndarray:
+        """Byte offset of every token in the decode of the sequence: the
+        length of the decode of the tokens before it (tiktoken deep-dive page,
+        "An encoding is three objects": decoding concatenates each token's
+        bytes).  Each distinct id is decoded once, alone; the offsets are the
+        running sum of those lengths."""
+        a = np.asarray(ids, dtype=np.int64).ravel()
+        uniq, inv = np.unique(a, return_inverse=True)
+        length = np.array([len(self.decode([int(t)])) for t in uniq], dtype=np.int64)
+        lens = length[inv] if a.size else np.zeros(0, dtype=np.int64)
+        off = np.zeros(a.size, dtype=np.int64)
+        if a.size > 1:
+            off[1:] = np.cumsum(lens[:-1])
+        return off
+
     def counters(self):
         lib = _load()
         a, b, c = C.c_uint64(0), C.c_uint64(0), C.c_uint64(0)
@@ -202,3 +217,38 @@ def chunk_cuts(text: bytes) -> list[int]:
     if st != 0:
         raise OracleError(st)
     return [int(x) for x in cuts[:n.value]]
+
+
+_PARTIAL = None
+
+
+def _partial_utf8_prefixes() -> frozenset:
+    """Every proper prefix of the UTF-8 encoding of every Unicode scalar value
+    (the code points U+0000..U+10FFFF other than the surrogates), found by
+    encoding each one with Python's codec."""
+    global _PARTIAL
+    if _PARTIAL is None:
+        out = set()
+        for cp in range(0x110000):
+            if 0xD800 <= cp <= 0xDFFF:
+                continue
+            b = chr(cp).encode("utf-8")
+            for k in range(1, len(b)):
+                out.add(b[:k])
+        _PARTIAL = frozenset(out)
+    return _PARTIAL
+
+
+def utf8_complete_len(data: bytes) -> int:
+    """Length of the longest prefix of `data` that does not end in a partial
+    UTF-8 character: when the last k bytes (k = 1..3) are a proper prefix of
+    some character's encoding, they are held back, since the next token may
+    complete them (tiktoken deep-dive page, "Pitfalls that bite in
+    production": a token can end inside a character, so a stream decodes
+    bytes and holds back a trailing partial sequence).  Bytes that can never
+    start or continue a character are not held back."""
+    p = _partial_utf8_prefixes()
+    for k in range(1, 4):
+        if len(data) >= k and data[-k:] in p:
+            return len(data) - k
+    return len(data)

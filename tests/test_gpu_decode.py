@@ -1,0 +1,208 @@
+"""GPU parity of device decode (ids to bytes, per-token byte offsets, the
+complete-character prefix length for streams) and of count-only encode,
+through the C ABI, against the CPU oracle.  Byte and index work: bit-exact."""
+import ctypes as C
+import itertools
+import random
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import byte_level_bpe_amd as B  # noqa: E402
+from oracle import Oracle, utf8_complete_len  # noqa: E402
+from tests.brute import atoms_permuted  # noqa: E402
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    from synth import configs
+    w = configs.tiny()
+    return w, B.load_ranks(w.tokens, w.specials, w.grammar), Oracle(w.tokens, w.specials, w.grammar)
+
+
+def dev_ids(ids):
+    return torch.tensor(np.asarray(ids, dtype=np.int32), dtype=torch.int32, device="cuda")
+
+
+def check_decode(tok, orc, ids, what):
+    out, off, done = tok.decode_device(dev_ids(ids), offsets=True)
+    got = out.cpu().numpy().tobytes()
+    ref = orc.decode(ids) if len(ids) else b""
+    assert got == ref, "%s: bytes differ (gpu %d, oracle %d)" % (what, len(got), len(ref))
+    assert np.array_equal(off.cpu().numpy(), orc.token_offsets(ids)), what
+    assert done == utf8_complete_len(ref), what
+
+
+@pytest.mark.parametrize("n", [0, 1, 5, 255, 4095, 4096, 4097, 3 * 4096 + 17, 100_000])
+def test_decode_random_ids(tiny, n):
+    """Random ranks and specials; sizes around the 4096-token block and a
+    ragged tail, several blocks, and empty."""
+    w, tok, orc = tiny
+    say("decode random ids n=%d" % n)
+    r = random.Random(n)
+    valid = list(range(len(w.tokens))) + [i for _, i in w.specials]
+    ids = [r.choice(valid) for _ in range(n)]
+    check_decode(tok, orc, ids, "random n=%d" % n)
+
+
+def test_decode_specials_only(tiny):
+    w, tok, orc = tiny
+    say("decode specials only")
+    ids = [i for _, i in w.specials] * 1000
+    check_decode(tok, orc, ids, "specials")
+
+
+@pytest.mark.parametrize("bad_at", [0, 3, 4095, 4096, 9000])
+def test_decode_bad_ids(tiny, bad_at):
+    """An id that is neither a rank nor a special (negative, in the gap
+    between ranks and specials, above every id): BBPE_E_BAD_ID with the
+    index of the first."""
+    w, tok, orc = tiny
+    say("decode bad id at %d" % bad_at)
+    r = random.Random(bad_at)
+    sp = {i for _, i in w.specials}
+    gap = next(i for i in range(len(w.tokens), 2 ** 31) if i not in sp)
+    for bad in (-1, gap, 2 ** 31 - 1):
+        ids = [r.randrange(len(w.tokens)) for _ in range(10_000)]
+        ids[bad_at] = bad
+        ids[bad_at + 1] = -5
+        with pytest.raises(B.BBPEError) as e:
+            tok.decode_device(dev_ids(ids))
+        assert e.value.status == B.E_BAD_ID
+        assert ("index %d:" % bad_at) in str(e.value)
+
+
+def test_decode_capacity_through_the_c_abi(tiny):
+    """Too small an output: BBPE_E_CAPACITY, *out_len = the bytes needed, the
+    output untouched and the offsets written; the exact size succeeds."""
+    w, tok, orc = tiny
+    say("decode capacity")
+    r = random.Random(11)
+    ids = [r.randrange(len(w.tokens)) for _ in range(5000)]
+    ref = orc.decode(ids)
+    d = dev_ids(ids)
+    tok.upload()
+    ws = torch.empty(tok.decode_workspace_bytes(len(ids)), dtype=torch.uint8, device="cuda")
+    off = torch.empty(len(ids), dtype=torch.int64, device="cuda")
+    lib = B._load()
+    for cap in (0, 1, len(ref) - 1, len(ref)):
+        out = torch.full((max(1, cap),), 0xA5, dtype=torch.uint8, device="cuda")
+        n, done = C.c_uint64(0), C.c_uint64(0)
+        off.fill_(-1)
+        st = lib.bbpe_decode_device(tok._h, C.c_void_p(d.data_ptr()), len(ids),
+                                    C.c_void_p(out.data_ptr()) if cap else None, cap,
+                                    C.c_void_p(off.data_ptr()), C.c_void_p(ws.data_ptr()), ws.numel(),
+                                    C.byref(n), C.byref(done),
+                                    C.c_void_p(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        assert n.value == len(ref)
+        assert np.array_equal(off.cpu().numpy(), orc.token_offsets(ids))
+        if cap < len(ref):
+            assert st == B.E_CAPACITY
+            assert bool((out == 0xA5).all())
+        else:
+            assert st == B.OK and out.cpu().numpy().tobytes() == ref
+    # workspace too small, misaligned
+    n = C.c_uint64(0)
+    st = lib.bbpe_decode_device(tok._h, C.c_void_p(d.data_ptr()), len(ids), None, 0, None,
+                                C.c_void_p(ws.data_ptr()), 16, C.byref(n), None, None)
+    assert st == B.E_WORKSPACE
+    st = lib.bbpe_decode_device(tok._h, C.c_void_p(d.data_ptr()), len(ids), None, 0, None,
+                                C.c_void_p(ws.data_ptr() + 64), ws.numel() - 64, C.byref(n), None,
+                                None)
+    assert st == B.E_WORKSPACE
+
+
+def test_decode_stream_prefixes(tiny):
+    """Every prefix of an encode's ids: the complete-character length equals
+    the oracle's, so a stream that emits only that prefix never shows a
+    partial character (Devanagari, CJK, emoji)."""
+    w, tok, orc = tiny
+    text = ("ाइ हिन्दी का 中文字符 😀😀 mixed é " * 8).encode()
+    ids = orc.encode(text)
+    say("decode stream prefixes: %d ids" % len(ids))
+    for k in range(len(ids) + 1):
+        out, _, done = tok.decode_device(dev_ids(ids[:k]))
+        data = out.cpu().numpy().tobytes()
+        assert data == orc.decode(ids[:k]) if k else data == b""
+        assert done == utf8_complete_len(data), k
+
+
+def test_decode_tail_byte_patterns():
+    """The held-back tail on every 1-, 2- and 3-byte ending built from the
+    boundary values of the UTF-8 byte ranges, after an ASCII byte and after a
+    complete 3-byte character (atoms-only table: one id per byte)."""
+    tokens = atoms_permuted(5)
+    tok = B.load_ranks(tokens)
+    id_of = {k[0]: v for k, v in tokens.items()}
+    vals = [0x41, 0x80, 0x9F, 0xA0, 0xBF, 0xC1, 0xC2, 0xDF, 0xE0, 0xED, 0xEF, 0xF0, 0xF4, 0xF5]
+    say("decode tail patterns")
+    for pre in (b"a", "中".encode()):
+        for n in (1, 2, 3):
+            for t in itertools.product(vals, repeat=n):
+                data = pre + bytes(t)
+                out, _, done = tok.decode_device(dev_ids([id_of[b] for b in data]))
+                assert out.cpu().numpy().tobytes() == data
+                assert done == utf8_complete_len(data), data.hex()
+
+
+# ------------------------------------------------------------ count only ----
+
+def test_count_only_matches_oracle_offsets(tiny):
+    w, tok, orc = tiny
+    say("count only, tiny workload")
+    segs = w.segments
+    counts = tok.count_segments(segs, w.tiktoken_safe).cpu().numpy()
+    _, ooff = orc.encode_segments(segs, w.tiktoken_safe)
+    assert np.array_equal(counts, np.diff(ooff))
+
+
+def test_count_only_needs_no_id_buffer(tiny):
+    """Null ids and capacity 0 with BBPE_COUNT_ONLY: no capacity error, the
+    offsets and the total are written; without the flag the same call is a
+    capacity error; invalid UTF-8 is still reported."""
+    w, tok, orc = tiny
+    say("count only without ids")
+    segs = [(b"hello world " * 50, False), (b"", True), ("中文 😀".encode() * 30, False)]
+    text, seg_off, allow, total = B.to_device_segments(segs)
+    _, id_off, n = tok.encode_device(text, seg_off, allow, total, count_only=True)
+    oids, ooff = orc.encode_segments(segs)
+    assert n == len(oids) and np.array_equal(id_off.cpu().numpy(), ooff)
+    ids = torch.empty(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(B.BBPEError) as e:
+        tok.encode_device(text, seg_off, allow, total, ids=ids[:0])
+    assert e.value.status == B.E_CAPACITY
+    bad = [(b"ok", False), (b"x\xc0\x80", False)]
+    text, seg_off, allow, total = B.to_device_segments(bad)
+    with pytest.raises(B.BBPEError) as e:
+        tok.encode_device(text, seg_off, allow, total, count_only=True)
+    assert e.value.status == B.E_UTF8 and e.value.segment == 1
+
+
+def test_pretokenize_rejects_count_only(tiny):
+    w, tok, orc = tiny
+    text, seg_off, allow, total = B.to_device_segments([(b"abc", False)])
+    tok.upload()
+    ws = tok.workspace(total, 1)
+    starts = torch.empty(4, dtype=torch.int32, device="cuda")
+    n = C.c_uint64(0)
+    st = B._load().bbpe_pretokenize_segments(
+        tok._h, C.c_void_p(text.data_ptr()), total, C.c_void_p(seg_off.data_ptr()),
+        C.c_void_p(allow.data_ptr()), 1, B.COUNT_ONLY, C.c_void_p(ws.data_ptr()), ws.numel(),
+        C.c_void_p(starts.data_ptr()), 4, None, C.byref(n), None)
+    assert st == B.E_INVALID_ARG

@@ -1,5 +1,7 @@
 """GPU parity on the full-size workloads: every id and every segment offset
-of the HIP path equals the oracle's, and decode restores the text."""
+of the HIP path equals the oracle's, count-only encode gives the same
+offsets, and device decode restores the text with the oracle's per-token
+byte offsets."""
 import sys
 
 import numpy as np
@@ -45,4 +47,13 @@ def test_workload_parity(name):
     text = b"".join(s for s, _ in w.segments)
     assert tok.decode(ids) == text
     assert len(ids) <= len(text)
+    say("count only", name)
+    _, c_off, c_n = tok.encode_device(*B.to_device_segments(w.segments), w.tiktoken_safe,
+                                      count_only=True)
+    assert c_n == len(oids) and np.array_equal(c_off.cpu().numpy(), ooff)
+    say("device decode", name)
+    out, tok_off, done = tok.decode_device(torch.from_numpy(ids).cuda(), offsets=True)
+    assert out.cpu().numpy().tobytes() == text
+    assert done == len(text)
+    assert np.array_equal(tok_off.cpu().numpy(), orc.token_offsets(oids))
 

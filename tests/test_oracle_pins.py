@@ -339,3 +339,80 @@ def test_table_validation():
         Oracle(t, [(b"", 300)])                       # empty special
     with pytest.raises(OracleError):
         Oracle(t, [(b"\xff", 300)])                   # not UTF-8
+
+
+# ------------------------------------------- decode offsets, stream tails ----
+
+@pytest.mark.parametrize("case", GOLDEN["stream_hold_back"], ids=lambda c: c["cite"][:30])
+def test_stream_hold_back_page_example(case):
+    """The page's two Devanagari tokens: after the first, its trailing partial
+    character is held back; after the second, everything is complete."""
+    from oracle import utf8_complete_len
+    data = b""
+    for hx, want in zip(case["tokens_hex"], case["complete_after"]):
+        data += bytes.fromhex(hx)
+        assert utf8_complete_len(data) == want
+    assert data.decode("utf-8") == "ाइ"
+
+
+def test_stream_hold_back_matches_incremental_codec():
+    """Against Python's incremental UTF-8 decoder on every string of 1 to 4
+    bytes drawn from the boundary values of the UTF-8 byte ranges.  The one
+    known difference: the codec also holds back ED A0..BF, the start of an
+    encoded surrogate, which the Unicode table of well-formed sequences
+    excludes (ED takes 80..9F); there the oracle holds nothing back."""
+    import codecs
+    import itertools
+    from oracle import utf8_complete_len
+    vals = [0x00, 0x41, 0x7F, 0x80, 0x8F, 0x90, 0x9F, 0xA0, 0xBF, 0xC0, 0xC1, 0xC2, 0xDF,
+            0xE0, 0xE1, 0xEC, 0xED, 0xEE, 0xEF, 0xF0, 0xF1, 0xF3, 0xF4, 0xF5, 0xFF]
+    surrogate_starts = 0
+    for n in range(1, 5):
+        for t in itertools.product(vals, repeat=n):
+            b = bytes(t)
+            d = codecs.getincrementaldecoder("utf-8")("replace")
+            d.decode(b, final=False)
+            held = len(d.getstate()[0])
+            if held >= 2 and b[-held] == 0xED and 0xA0 <= b[-held + 1] <= 0xBF:
+                surrogate_starts += 1
+                assert utf8_complete_len(b) == len(b)
+                continue
+            assert utf8_complete_len(b) == len(b) - held, b.hex()
+    assert surrogate_starts > 0
+
+
+def test_stream_hold_back_rebuilds_text_token_by_token(tiny_workload, tiny_oracle):
+    """Feeding an encode's tokens one at a time and emitting only the complete
+    prefix reproduces the text with no replacement characters, and every
+    emitted prefix is valid UTF-8."""
+    from oracle import utf8_complete_len
+    text = "ाइ हिन्दी 中文 😀 mixed ".encode() * 3 + tiny_workload.segments[0][0][:2000]
+    while text and (text[-1] & 0xC0) == 0x80:
+        text = text[:-1]
+    text = text[:len(text) - 1] if text and text[-1] >= 0xC0 else text
+    ids = tiny_oracle.encode(text)
+    data, shown = b"", 0
+    for t in ids:
+        data += tiny_oracle.decode([t])
+        c = utf8_complete_len(data)
+        assert c >= shown
+        data[:c].decode("utf-8")
+        shown = c
+    assert data == text and shown == len(text)
+
+
+def test_token_offsets_definition(tiny_workload, tiny_oracle):
+    """Offset of token i = length of the decode of tokens 0..i-1 (written out
+    for a few hundred tokens), and for an encode the offsets are the tokens'
+    positions in the text: text[off[i]:off[i+1]] decodes token i."""
+    r = random.Random(3)
+    valid = list(range(len(tiny_workload.tokens))) + [i for _, i in tiny_workload.specials]
+    ids = [r.choice(valid) for _ in range(300)]
+    off = tiny_oracle.token_offsets(ids)
+    assert [int(x) for x in off] == [len(tiny_oracle.decode(ids[:i])) for i in range(len(ids))]
+    text = tiny_workload.segments[0][0][:5000]
+    eids = tiny_oracle.encode(text)
+    eoff = list(tiny_oracle.token_offsets(eids)) + [len(text)]
+    for i, t in enumerate(eids):
+        assert text[eoff[i]:eoff[i + 1]] == tiny_oracle.decode([t])
+    assert len(tiny_oracle.token_offsets([])) == 0
