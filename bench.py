@@ -111,6 +111,89 @@ def cpu_baseline(w, budget_s: float = 10.0, max_reps: int = 200) -> dict:
                       % (w.name, nb, reps, total)}
 
 
+def decode_alg_bytes(kernel: str, n_ids: int, n_bytes: int) -> int:
+    """Bytes one decode launch must move: k_dec_len reads each id and its
+    8-byte table entry and writes a 4-byte length; k_dec_copy reads each id,
+    its length and its bytes, writes its 8-byte offset and its bytes."""
+    if kernel == "k_dec_len":
+        return n_ids * (4 + 8 + 4)
+    if kernel == "k_dec_copy":
+        return n_ids * (4 + 4 + 8) + 2 * n_bytes
+    return 0
+
+
+def bench_decode(args, w):
+    """Device decode of the workload's ids (encoded once on the device before
+    timing) into an output sized exactly, with per-token byte offsets."""
+    import torch
+    import byte_level_bpe_amd as B
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tok = B.load_ranks(w.tokens, w.specials, w.grammar)
+    ids, _ = tok.encode_segments(w.segments, w.tiktoken_safe, device=dev)
+    n_ids = int(ids.numel())
+    total = w.text_bytes
+    out = torch.empty(max(1, total), dtype=torch.uint8, device=dev)
+    tok_off = torch.empty(max(1, n_ids), dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        o, _, _ = tok.decode_device(ids, out=out, tok_off=tok_off, stream=stream)
+        return int(o.numel())
+
+    for _ in range(args.warmup):
+        nb = step()
+    assert nb == total
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tok.set_timing(True)
+    tok.timing_reset()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    rep = tok.timing_report()
+    tok.set_timing(False)
+    per_kernel = {k: v[0] / max(1, v[1]) for k, v in rep.items()}
+    dom = max(rep, key=lambda k: rep[k][0])
+    dom_bytes = decode_alg_bytes(dom, n_ids, total)
+    achieved = dom_bytes / (per_kernel[dom] * 1e-3) / 1e9
+    res = {
+        "metric": "decode output MB/s + tokens/s on 1 MI355X (ids to bytes with per-token offsets)",
+        "value": round(total * args.steps / wall / 1e6, 2),
+        "unit": "MB/s",
+        "tokens_per_s": round(n_ids * args.steps / wall, 1),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_DESC.get(w.name, w.name), "bytes": total, "ids": n_ids},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
+                     "traffic": None, "avg_ms": round(per_kernel[dom], 5),
+                     "alg_bytes_per_launch": dom_bytes},
+        "kernels_avg_ms": {k: round(v, 5) for k, v in sorted(per_kernel.items(), key=lambda kv: -kv[1])},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import Oracle
+        orc = Oracle(w.tokens, w.specials, w.grammar)
+        h = ids.cpu().numpy()
+        reps, spent = 0, 0.0
+        while spent < 10.0 and reps < 200:
+            t0 = time.perf_counter()
+            orc.decode(h)
+            spent += time.perf_counter() - t0
+            reps += 1
+        res["cpu_baseline"] = {"value": round(total * reps / spent / 1e6, 3), "unit": "MB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": "all %d ids of the %s workload decoded %d times "
+                                         "single-threaded, %.1f s" % (n_ids, w.name, reps, spent)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +201,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="main")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", choices=["encode", "decode"], default="encode",
+                    help="decode: device decode of the workload's ids with per-token offsets")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (5 times), "
                          "to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -142,6 +227,8 @@ def main():
     from synth import configs
 
     w = configs.ALL[args.workload]()
+    if args.op == "decode":
+        return bench_decode(args, w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tok = B.load_ranks(w.tokens, w.specials, w.grammar)

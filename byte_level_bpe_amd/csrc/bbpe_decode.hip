@@ -20,6 +20,8 @@ namespace bbpe {
 namespace {
 
 constexpr uint32_t DEC_BLOCK = 256, DEC_ITEMS = 16, DEC_TILE = DEC_BLOCK * DEC_ITEMS;
+// output bytes of one tile staged in LDS (more: written straight to HBM)
+constexpr uint32_t DEC_STAGE = 32768;
 
 struct DecStatus {
   unsigned long long first_bad;  // index of the first id that is neither rank nor special, or ~0
@@ -35,9 +37,10 @@ struct DecArgs {
   uint8_t *out;
   uint64_t cap;
   uint64_t *tok_off;
-  uint32_t *len;      // [n] byte length of each token
-  uint32_t *part;     // [blocks] bytes per block of DEC_TILE tokens
+  uint32_t *part;              // [blocks] bytes of each tile of DEC_TILE tokens
+  unsigned long long *bad;     // [blocks] first bad index of each tile, or ~0
   DecStatus *st;
+  uint32_t vec_ids, vec_off;   // ids / tok_off 16-byte aligned: vector loads / stores
 };
 
 // offset << 8 | length of an id's bytes in the decode blob, or 0 (bad id)
@@ -57,122 +60,196 @@ __device__ __forceinline__ uint64_t dec_entry(const DevTables &T, int32_t id) {
   return (lo < T.n_sp && T.dsp[2 * lo] == uint64_t(id)) ? T.dsp[2 * lo + 1] : 0ull;
 }
 
-__device__ __forceinline__ uint32_t dec_block_excl_scan(uint32_t v, uint32_t *sh, uint32_t &total) {
-  const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x / 64;
-  const uint32_t incl = wave_incl_sum(v, int(lane));
-  if (lane == 63) sh[wv] = incl;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
+__device__ __forceinline__ unsigned long long wave_sum64(unsigned long long v) {
 #pragma unroll
-  for (uint32_t q = 0; q < DEC_BLOCK / 64; ++q) {
-    before += q < wv ? sh[q] : 0u;
-    all += sh[q];
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+__device__ __forceinline__ unsigned long long wave_min64(unsigned long long v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const unsigned long long o = __shfl_xor(v, d, 64);
+    v = o < v ? o : v;
   }
-  __syncthreads();
-  total = all;
-  return before + incl - v;
+  return v;
 }
 
-__global__ void k_dec_init(DecArgs a) {
-  if (threadIdx.x == 0) {
-    a.st->first_bad = ~0ull;
-    a.st->total = 0;
-    a.st->complete = 0;
-  }
-}
-
-// lengths, the first bad id, and the bytes of every block of DEC_TILE tokens
+// Per tile: the bytes of its tokens and its first bad id (coalesced reads).
 __global__ void __launch_bounds__(DEC_BLOCK) k_dec_len(DecArgs a) {
-  __shared__ uint32_t sh[DEC_BLOCK / 64];
+  __shared__ unsigned long long s_sum[DEC_BLOCK / 64], s_bad[DEC_BLOCK / 64];
   const uint64_t b0 = uint64_t(blockIdx.x) * DEC_TILE;
   uint32_t sum = 0;
+  unsigned long long bad = ~0ull;
+#pragma unroll 4
   for (uint32_t k = 0; k < DEC_ITEMS; ++k) {
-    const uint64_t i = b0 + uint64_t(k) * DEC_BLOCK + threadIdx.x;  // coalesced
+    const uint64_t i = b0 + uint64_t(k) * DEC_BLOCK + threadIdx.x;
     if (i < a.n) {
       const uint64_t e = dec_entry(a.T, a.ids[i]);
-      if (!e) atomicMin(&a.st->first_bad, static_cast<unsigned long long>(i));
-      const uint32_t l = uint32_t(e & 0xFFu);
-      a.len[i] = l;
-      sum += l;
+      if (!e && i < bad) bad = i;
+      sum += uint32_t(e & 0xFFu);
     }
   }
-  uint32_t total;
-  (void)dec_block_excl_scan(sum, sh, total);
-  if (threadIdx.x == 0) a.part[blockIdx.x] = total;
+  const unsigned long long ws = wave_sum64(sum), wb = wave_min64(bad);
+  if ((threadIdx.x & 63) == 0) {
+    s_sum[threadIdx.x / 64] = ws;
+    s_bad[threadIdx.x / 64] = wb;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long t = 0, m = ~0ull;
+#pragma unroll
+    for (uint32_t q = 0; q < DEC_BLOCK / 64; ++q) {
+      t += s_sum[q];
+      m = s_bad[q] < m ? s_bad[q] : m;
+    }
+    a.part[blockIdx.x] = uint32_t(t);
+    a.bad[blockIdx.x] = m;
+  }
 }
 
-// offsets (base from the blocks before, scan inside the block), then the
-// bytes of every token when the output fits and every id is good
+// Per tile: its base (bytes of the tiles before), every token's offset (a
+// block scan over runs of DEC_ITEMS consecutive tokens per thread), then its
+// bytes: staged in LDS at the output's 16-byte phase and stored as aligned
+// 16-byte words.  The last tile also finds the end of the last complete
+// character from the last tokens' bytes.
 __global__ void __launch_bounds__(DEC_BLOCK) k_dec_copy(DecArgs a) {
-  __shared__ uint32_t sh[DEC_BLOCK / 64];
-  const uint64_t b0 = uint64_t(blockIdx.x) * DEC_TILE;
-  const uint32_t nblk = uint32_t((a.n + DEC_TILE - 1) / DEC_TILE);
-  uint64_t before = 0, every = 0;
+  __shared__ unsigned long long s_a[DEC_BLOCK / 64], s_b[DEC_BLOCK / 64], s_c[DEC_BLOCK / 64];
+  __shared__ uint32_t s_scan[2 * (DEC_BLOCK / 64) + 1];
+  __shared__ __align__(16) uint8_t stage[DEC_STAGE + 32];
+  const uint32_t nblk = gridDim.x;
+  const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x / 64;
+  // base, total and the first bad id over all tiles
+  unsigned long long before = 0, every = 0, bad = ~0ull;
   for (uint32_t q = threadIdx.x; q < nblk; q += DEC_BLOCK) {
-    const uint32_t t = a.part[q];
-    before += q < blockIdx.x ? t : 0u;
+    const unsigned long long t = a.part[q];
+    before += q < blockIdx.x ? t : 0ull;
     every += t;
+    const unsigned long long m = a.bad[q];
+    bad = m < bad ? m : bad;
   }
-  // (64-bit block sums: wave sums of the two halves)
-  __shared__ unsigned long long s_sum[2][DEC_BLOCK / 64];
-  {
-    unsigned long long x = before, y = every;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      x += __shfl_xor(x, d, 64);
-      y += __shfl_xor(y, d, 64);
-    }
-    if ((threadIdx.x & 63) == 0) {
-      s_sum[0][threadIdx.x / 64] = x;
-      s_sum[1][threadIdx.x / 64] = y;
-    }
+  before = wave_sum64(before);
+  every = wave_sum64(every);
+  bad = wave_min64(bad);
+  if (lane == 0) {
+    s_a[wv] = before;
+    s_b[wv] = every;
+    s_c[wv] = bad;
   }
   __syncthreads();
   uint64_t base = 0, total = 0;
+  unsigned long long first_bad = ~0ull;
 #pragma unroll
   for (uint32_t q = 0; q < DEC_BLOCK / 64; ++q) {
-    base += s_sum[0][q];
-    total += s_sum[1][q];
+    base += s_a[q];
+    total += s_b[q];
+    first_bad = s_c[q] < first_bad ? s_c[q] : first_bad;
   }
-  const bool write = total <= a.cap && a.st->first_bad == ~0ull;
-  // each thread: DEC_ITEMS consecutive tokens
-  uint32_t l[DEC_ITEMS];
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.st->total = total;
+    a.st->first_bad = first_bad;
+  }
+  if (first_bad != ~0ull) return;  // (uniform over the grid)
+
+  // this thread's DEC_ITEMS consecutive tokens
+  const uint64_t i0 = uint64_t(blockIdx.x) * DEC_TILE + uint64_t(threadIdx.x) * DEC_ITEMS;
+  uint64_t e[DEC_ITEMS];
   uint32_t sum = 0;
+  if (a.vec_ids && i0 + DEC_ITEMS <= a.n) {
+    const int4 *p = reinterpret_cast<const int4 *>(a.ids + i0);
 #pragma unroll
-  for (uint32_t k = 0; k < DEC_ITEMS; ++k) {
-    const uint64_t i = b0 + uint64_t(threadIdx.x) * DEC_ITEMS + k;
-    l[k] = i < a.n ? a.len[i] : 0u;
-    sum += l[k];
+    for (uint32_t v = 0; v < DEC_ITEMS / 4; ++v) {
+      const int4 x = p[v];
+      e[4 * v + 0] = dec_entry(a.T, x.x);
+      e[4 * v + 1] = dec_entry(a.T, x.y);
+      e[4 * v + 2] = dec_entry(a.T, x.z);
+      e[4 * v + 3] = dec_entry(a.T, x.w);
+    }
+  } else {
+#pragma unroll
+    for (uint32_t k = 0; k < DEC_ITEMS; ++k)
+      e[k] = i0 + k < a.n ? dec_entry(a.T, a.ids[i0 + k]) : 0ull;
   }
-  uint32_t blk;
-  uint64_t off = base + dec_block_excl_scan(sum, sh, blk);
 #pragma unroll
-  for (uint32_t k = 0; k < DEC_ITEMS; ++k) {
-    const uint64_t i = b0 + uint64_t(threadIdx.x) * DEC_ITEMS + k;
-    if (i < a.n) {
-      if (a.tok_off) a.tok_off[i] = off;
-      if (write) {
-        const uint64_t e = dec_entry(a.T, a.ids[i]);
-        const uint8_t *src = a.T.dblob + (e >> 8);
-        for (uint32_t j = 0; j < l[k]; ++j) a.out[off + j] = src[j];
+  for (uint32_t k = 0; k < DEC_ITEMS; ++k) sum += uint32_t(e[k] & 0xFFu);
+  uint32_t blk;
+  const uint32_t incl = block_incl_scan<DEC_BLOCK>(
+      sum, 0u, [](uint32_t x, uint32_t y) { return x + y; }, s_scan, blk);
+  const uint32_t mine = incl - sum;  // offset of this thread's first token in the tile
+
+  if (a.tok_off) {
+    uint64_t o = base + mine;
+    if (a.vec_off && i0 + DEC_ITEMS <= a.n) {
+      ulonglong2 *q = reinterpret_cast<ulonglong2 *>(a.tok_off + i0);
+#pragma unroll
+      for (uint32_t k = 0; k < DEC_ITEMS; k += 2) {
+        ulonglong2 v;
+        v.x = o;
+        o += e[k] & 0xFFu;
+        v.y = o;
+        o += e[k + 1] & 0xFFu;
+        q[k / 2] = v;
+      }
+    } else {
+#pragma unroll
+      for (uint32_t k = 0; k < DEC_ITEMS; ++k) {
+        if (i0 + k < a.n) a.tok_off[i0 + k] = o;
+        o += e[k] & 0xFFu;
       }
     }
-    off += l[k];
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.st->total = total;
-}
 
-// The output length without a trailing partial character: when the last k
-// bytes (k <= 3) are a proper prefix of a well-formed UTF-8 sequence (the
-// Unicode standard's table of well-formed byte sequences: lead C2-DF, E0-EF
-// or F0-F4, the second byte's range set by the lead), they are held back.
-__global__ void k_dec_tail(DecArgs a) {
-  if (threadIdx.x != 0) return;
-  const uint64_t total = a.st->total;
-  uint64_t complete = total;
-  if (total <= a.cap && a.st->first_bad == ~0ull) {
-    for (uint64_t k = 1; k <= 3 && k <= total; ++k) {
-      const uint32_t b = a.out[total - k];
+  if (total <= a.cap) {
+    if (blk <= DEC_STAGE) {
+      // LDS byte j <-> the output byte at address (out + base) rounded down
+      // to 16, plus j
+      const uint32_t phase = uint32_t((reinterpret_cast<uintptr_t>(a.out) + base) & 15);
+      uint32_t o = phase + mine;
+#pragma unroll
+      for (uint32_t k = 0; k < DEC_ITEMS; ++k) {
+        const uint32_t len = uint32_t(e[k] & 0xFFu);
+        const uint8_t *src = a.T.dblob + (e[k] >> 8);
+        for (uint32_t j = 0; j < len; ++j) stage[o + j] = src[j];
+        o += len;
+      }
+      __syncthreads();
+      uint8_t *dst = a.out + base - phase;
+      const uint32_t end = phase + blk, nchunk = (end + 15) / 16;
+      for (uint32_t c = threadIdx.x; c < nchunk; c += DEC_BLOCK) {
+        const uint32_t lo = c * 16, hi = lo + 16;
+        if (lo >= phase && hi <= end) {
+          *reinterpret_cast<uint4 *>(dst + lo) = *reinterpret_cast<const uint4 *>(stage + lo);
+        } else {
+          for (uint32_t j = lo < phase ? phase : lo; j < (hi < end ? hi : end); ++j) dst[j] = stage[j];
+        }
+      }
+    } else {
+      uint64_t o = base + mine;
+#pragma unroll
+      for (uint32_t k = 0; k < DEC_ITEMS; ++k) {
+        const uint32_t len = uint32_t(e[k] & 0xFFu);
+        const uint8_t *src = a.T.dblob + (e[k] >> 8);
+        for (uint32_t j = 0; j < len; ++j) a.out[o + j] = src[j];
+        o += len;
+      }
+    }
+  }
+
+  // The output length without a trailing partial character: when the last k
+  // bytes (k <= 3) are a proper prefix of a well-formed UTF-8 sequence (the
+  // Unicode standard's table of well-formed byte sequences: lead C2-DF,
+  // E0-EF or F0-F4, the second byte's range set by the lead), they are held
+  // back.  The last bytes are read from the last tokens (each has >= 1 byte).
+  if (blockIdx.x == nblk - 1 && threadIdx.x == 0) {
+    uint32_t tail[3] = {0, 0, 0};  // tail[k-1] = output byte total - k
+    uint32_t got = 0;
+    for (uint64_t t = a.n; t > 0 && got < 3; --t) {
+      const uint64_t et = dec_entry(a.T, a.ids[t - 1]);
+      const uint8_t *src = a.T.dblob + (et >> 8);
+      for (uint32_t j = uint32_t(et & 0xFFu); j > 0 && got < 3; --j) tail[got++] = src[j - 1];
+    }
+    uint64_t complete = total;
+    for (uint32_t k = 1; k <= got; ++k) {
+      const uint32_t b = tail[k - 1];
       if ((b & 0xC0u) == 0x80u) continue;
       // b is the last byte that is not a continuation byte
       const uint32_t need = (b >= 0xC2 && b <= 0xDF) ? 2u : (b >= 0xE0 && b <= 0xEF) ? 3u
@@ -180,7 +257,7 @@ __global__ void k_dec_tail(DecArgs a) {
       if (need > k) {
         bool ok = true;
         if (k >= 2) {
-          const uint32_t s = a.out[total - k + 1];
+          const uint32_t s = tail[k - 2];
           const uint32_t lo = b == 0xE0 ? 0xA0u : b == 0xF0 ? 0x90u : 0x80u;
           const uint32_t hi = b == 0xED ? 0x9Fu : b == 0xF4 ? 0x8Fu : 0xBFu;
           ok = s >= lo && s <= hi;
@@ -189,21 +266,22 @@ __global__ void k_dec_tail(DecArgs a) {
       }
       break;
     }
+    a.st->complete = complete;
   }
-  a.st->complete = complete;
 }
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 struct DecLayout {
-  uint64_t status, len, part, total;
+  uint64_t status, part, bad, total;
 };
 DecLayout dec_layout(uint64_t n) {
   DecLayout L{};
+  const uint64_t nb = n / DEC_TILE + 2;
   uint64_t o = 0;
   L.status = o; o = align256(o + sizeof(DecStatus));
-  L.len = o; o = align256(o + 4 * (n + 1));
-  L.part = o; o = align256(o + 4 * (n / DEC_TILE + 2));
+  L.part = o; o = align256(o + 4 * nb);
+  L.bad = o; o = align256(o + 8 * nb);
   L.total = o;
   return L;
 }
@@ -237,16 +315,21 @@ int bbpe_decode_device(bbpe_tokenizer *t, const int32_t *d_ids, uint64_t n_ids, 
   a.cap = out_capacity;
   a.tok_off = d_tok_off;
   a.st = reinterpret_cast<DecStatus *>(w + L.status);
-  a.len = reinterpret_cast<uint32_t *>(w + L.len);
   a.part = reinterpret_cast<uint32_t *>(w + L.part);
-  Launcher go{t, reinterpret_cast<hipStream_t>(stream)};
-  go("k_dec_init", k_dec_init, dim3(1), dim3(64), a);
-  if (n_ids) {
-    const uint32_t nb = uint32_t((n_ids + DEC_TILE - 1) / DEC_TILE);
-    go("k_dec_len", k_dec_len, dim3(nb), dim3(DEC_BLOCK), a);
-    go("k_dec_copy", k_dec_copy, dim3(nb), dim3(DEC_BLOCK), a);
-    go("k_dec_tail", k_dec_tail, dim3(1), dim3(64), a);
+  a.bad = reinterpret_cast<unsigned long long *>(w + L.bad);
+  if (n_ids == 0) {
+    *out_len = 0;
+    if (complete_len) *complete_len = 0;
+    return BBPE_OK;
   }
+  if (d_tok_off && (reinterpret_cast<uintptr_t>(d_tok_off) & 7)) return BBPE_E_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_ids) & 3) || n_ids >= (uint64_t(1) << 40)) return BBPE_E_INVALID_ARG;
+  a.vec_ids = (reinterpret_cast<uintptr_t>(d_ids) & 15) == 0;
+  a.vec_off = (reinterpret_cast<uintptr_t>(d_tok_off) & 15) == 0;
+  Launcher go{t, reinterpret_cast<hipStream_t>(stream)};
+  const uint32_t nb = uint32_t((n_ids + DEC_TILE - 1) / DEC_TILE);
+  go("k_dec_len", k_dec_len, dim3(nb), dim3(DEC_BLOCK), a);
+  go("k_dec_copy", k_dec_copy, dim3(nb), dim3(DEC_BLOCK), a);
   HIP_OK(hipGetLastError());
   DecStatus h{};
   HIP_OK(hipMemcpyAsync(&h, a.st, sizeof(DecStatus), hipMemcpyDeviceToHost, go.st));

@@ -203,7 +203,9 @@ int bbpe_decode(const bbpe_tokenizer *tok, const int32_t *ids, uint64_t n, uint8
  * an id that is neither a rank nor a special (*out_len = the index of the
  * first), BBPE_E_CAPACITY when out_capacity is too small (*out_len = bytes
  * needed; d_out is then not written, d_tok_off is).  Enqueues on hip_stream
- * and synchronises it once, at the end. */
+ * and synchronises it once, at the end.  d_ids must be 4-byte and d_tok_off
+ * 8-byte aligned (16-byte alignment of both is faster), n_ids below 2^40:
+ * BBPE_E_INVALID_ARG otherwise. */
 int bbpe_decode_workspace_bytes(const bbpe_tokenizer *tok, uint64_t n_ids, uint64_t *out_bytes);
 int bbpe_decode_device(bbpe_tokenizer *tok, const int32_t *d_ids, uint64_t n_ids,
                        uint8_t *d_out, uint64_t out_capacity, uint64_t *d_tok_off,

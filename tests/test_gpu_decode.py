@@ -206,3 +206,39 @@ def test_pretokenize_rejects_count_only(tiny):
         C.c_void_p(allow.data_ptr()), 1, B.COUNT_ONLY, C.c_void_p(ws.data_ptr()), ws.numel(),
         C.c_void_p(starts.data_ptr()), 4, None, C.byref(n), None)
     assert st == B.E_INVALID_ARG
+
+
+@pytest.mark.parametrize("pool", ["long_keys", "all"])
+def test_decode_alignments_and_long_tiles(tiny, pool):
+    """ids, offsets and output at 4-, 8- and 3-byte phases (scalar paths),
+    and tiles whose bytes exceed the LDS stage (only keys of 9+ bytes)."""
+    w, tok, orc = tiny
+    r = random.Random(17)
+    ids_pool = ([i for i, t in enumerate(w.tokens) if len(t) >= 9] if pool == "long_keys"
+                else list(range(len(w.tokens))))
+    n = 9000
+    ids = np.array([r.choice(ids_pool) for _ in range(n)], dtype=np.int32)
+    ref = orc.decode(ids)
+    ref_off = orc.token_offsets(ids)
+    tok.upload()
+    ws = torch.empty(tok.decode_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    lib = B._load()
+    for s_ids, s_off, s_out in [(0, 0, 0), (1, 1, 3), (2, 0, 1), (3, 1, 0)]:
+        say("decode alignment", pool, s_ids, s_off, s_out)
+        d_ids = torch.zeros(n + 4, dtype=torch.int32, device="cuda")
+        d_ids[s_ids:s_ids + n] = torch.from_numpy(ids).cuda()
+        d_off = torch.full((n + 2,), -1, dtype=torch.int64, device="cuda")
+        d_out = torch.zeros(len(ref) + 32, dtype=torch.uint8, device="cuda")
+        nn, done = C.c_uint64(0), C.c_uint64(0)
+        st = lib.bbpe_decode_device(tok._h, C.c_void_p(d_ids.data_ptr() + 4 * s_ids), n,
+                                    C.c_void_p(d_out.data_ptr() + s_out), len(ref),
+                                    C.c_void_p(d_off.data_ptr() + 8 * s_off),
+                                    C.c_void_p(ws.data_ptr()), ws.numel(), C.byref(nn),
+                                    C.byref(done), C.c_void_p(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        assert st == B.OK and nn.value == len(ref)
+        o = d_out.cpu().numpy()
+        assert o[s_out:s_out + len(ref)].tobytes() == ref
+        assert not o[:s_out].any() and not o[s_out + len(ref):].any()
+        assert np.array_equal(d_off.cpu().numpy()[s_off:s_off + n], ref_off)
+        assert done.value == utf8_complete_len(ref)
