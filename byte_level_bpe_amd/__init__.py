@@ -37,7 +37,8 @@ COUNT_ONLY = 2
 # every symbol include/bbpe.h declares
 EXPORTS = ["bbpe_load_ranks", "bbpe_load_ranks_tiktoken_file", "bbpe_upload_tables",
            "bbpe_workspace_bytes", "bbpe_encode_segments", "bbpe_pretokenize_segments",
-           "bbpe_decode", "bbpe_decode_workspace_bytes", "bbpe_decode_device", "bbpe_error_detail",
+           "bbpe_decode", "bbpe_decode_workspace_bytes", "bbpe_decode_device",
+           "bbpe_token_offsets_device", "bbpe_error_detail",
            "bbpe_table_info", "bbpe_set_timing", "bbpe_timing_report", "bbpe_timing_reset",
            "bbpe_free", "bbpe_status_str"]
 
@@ -80,6 +81,8 @@ def _load():
         lib.bbpe_decode_device.restype = I
         lib.bbpe_decode_device.argtypes = [P, P, U64, P, U64, P, P, U64, C.POINTER(U64),
                                            C.POINTER(U64), P]
+        lib.bbpe_token_offsets_device.restype = I
+        lib.bbpe_token_offsets_device.argtypes = [P, P, U64, P, P, U64, C.POINTER(U64), P]
         lib.bbpe_error_detail.restype = I
         lib.bbpe_error_detail.argtypes = [P, C.POINTER(U32), C.POINTER(U64)]
         lib.bbpe_table_info.restype = I
@@ -272,6 +275,29 @@ class Tokenizer:
         if st:
             raise BBPEError(st, "decode_workspace_bytes")
         return out.value
+
+    def token_offsets_device(self, ids, tok_off=None, stream=None):
+        """Byte offset of every token of an int32 id tensor (int64 tensor on its
+        device) and the total byte length, without decoding the bytes."""
+        import torch
+        dev = ids.device
+        self.upload(dev)
+        n_ids = int(ids.numel())
+        need = self.decode_workspace_bytes(n_ids)
+        if self._dws is None or self._dws.numel() < need:
+            self._dws = torch.empty(need, dtype=torch.uint8, device=dev)
+        if tok_off is None:
+            tok_off = torch.empty(max(1, n_ids), dtype=torch.int64, device=dev)
+        total = C.c_uint64(0)
+        st = _load().bbpe_token_offsets_device(
+            self._h, C.c_void_p(ids.data_ptr()) if n_ids else None, n_ids,
+            C.c_void_p(tok_off.data_ptr()), C.c_void_p(self._dws.data_ptr()), self._dws.numel(),
+            C.byref(total), _stream_handle(stream))
+        if st == E_BAD_ID:
+            raise BBPEError(st, "token_offsets_device at index %d" % total.value)
+        if st:
+            raise BBPEError(st, "token_offsets_device")
+        return tok_off[:n_ids], total.value
 
     def decode_device(self, ids, out=None, offsets: bool = False, tok_off=None, stream=None):
         """Decode an int32 id tensor on its device.

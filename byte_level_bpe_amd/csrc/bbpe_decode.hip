@@ -299,13 +299,17 @@ int bbpe_decode_workspace_bytes(const bbpe_tokenizer *t, uint64_t n_ids, uint64_
   return BBPE_OK;
 }
 
-int bbpe_decode_device(bbpe_tokenizer *t, const int32_t *d_ids, uint64_t n_ids, uint8_t *d_out,
-                       uint64_t out_capacity, uint64_t *d_tok_off, void *d_ws, uint64_t ws_bytes,
-                       uint64_t *out_len, uint64_t *complete_len, void *stream) {
-  if (!t || !out_len || (n_ids && !d_ids) || (out_capacity && !d_out)) return BBPE_E_INVALID_ARG;
+static int decode_run(bbpe_tokenizer *t, const int32_t *d_ids, uint64_t n_ids, uint8_t *d_out,
+                      uint64_t out_capacity, uint64_t *d_tok_off, void *d_ws, uint64_t ws_bytes,
+                      void *stream, DecStatus &h) {
   if (!t->d_image) return BBPE_E_STATE;
   const DecLayout L = dec_layout(n_ids);
   if (!d_ws || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(d_ws) & 255)) return BBPE_E_WORKSPACE;
+  h = DecStatus{};
+  h.first_bad = ~0ull;
+  if (n_ids == 0) return BBPE_OK;
+  if (d_tok_off && (reinterpret_cast<uintptr_t>(d_tok_off) & 7)) return BBPE_E_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_ids) & 3) || n_ids >= (uint64_t(1) << 40)) return BBPE_E_INVALID_ARG;
   uint8_t *w = static_cast<uint8_t *>(d_ws);
   DecArgs a{};
   a.T = t->dev;
@@ -317,13 +321,6 @@ int bbpe_decode_device(bbpe_tokenizer *t, const int32_t *d_ids, uint64_t n_ids, 
   a.st = reinterpret_cast<DecStatus *>(w + L.status);
   a.part = reinterpret_cast<uint32_t *>(w + L.part);
   a.bad = reinterpret_cast<unsigned long long *>(w + L.bad);
-  if (n_ids == 0) {
-    *out_len = 0;
-    if (complete_len) *complete_len = 0;
-    return BBPE_OK;
-  }
-  if (d_tok_off && (reinterpret_cast<uintptr_t>(d_tok_off) & 7)) return BBPE_E_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(d_ids) & 3) || n_ids >= (uint64_t(1) << 40)) return BBPE_E_INVALID_ARG;
   a.vec_ids = (reinterpret_cast<uintptr_t>(d_ids) & 15) == 0;
   a.vec_off = (reinterpret_cast<uintptr_t>(d_tok_off) & 15) == 0;
   Launcher go{t, reinterpret_cast<hipStream_t>(stream)};
@@ -331,10 +328,19 @@ int bbpe_decode_device(bbpe_tokenizer *t, const int32_t *d_ids, uint64_t n_ids, 
   go("k_dec_len", k_dec_len, dim3(nb), dim3(DEC_BLOCK), a);
   go("k_dec_copy", k_dec_copy, dim3(nb), dim3(DEC_BLOCK), a);
   HIP_OK(hipGetLastError());
-  DecStatus h{};
   HIP_OK(hipMemcpyAsync(&h, a.st, sizeof(DecStatus), hipMemcpyDeviceToHost, go.st));
   HIP_OK(hipStreamSynchronize(go.st));
   go.collect();
+  return BBPE_OK;
+}
+
+int bbpe_decode_device(bbpe_tokenizer *t, const int32_t *d_ids, uint64_t n_ids, uint8_t *d_out,
+                       uint64_t out_capacity, uint64_t *d_tok_off, void *d_ws, uint64_t ws_bytes,
+                       uint64_t *out_len, uint64_t *complete_len, void *stream) {
+  if (!t || !out_len || (n_ids && !d_ids) || (out_capacity && !d_out)) return BBPE_E_INVALID_ARG;
+  DecStatus h;
+  const int rc = decode_run(t, d_ids, n_ids, d_out, out_capacity, d_tok_off, d_ws, ws_bytes, stream, h);
+  if (rc) return rc;
   if (h.first_bad != ~0ull) {
     *out_len = h.first_bad;
     return BBPE_E_BAD_ID;
@@ -342,6 +348,21 @@ int bbpe_decode_device(bbpe_tokenizer *t, const int32_t *d_ids, uint64_t n_ids, 
   *out_len = h.total;
   if (complete_len) *complete_len = h.complete;
   return h.total > out_capacity ? BBPE_E_CAPACITY : BBPE_OK;
+}
+
+int bbpe_token_offsets_device(bbpe_tokenizer *t, const int32_t *d_ids, uint64_t n_ids,
+                              uint64_t *d_tok_off, void *d_ws, uint64_t ws_bytes,
+                              uint64_t *total_bytes, void *stream) {
+  if (!t || !total_bytes || (n_ids && (!d_ids || !d_tok_off))) return BBPE_E_INVALID_ARG;
+  DecStatus h;
+  const int rc = decode_run(t, d_ids, n_ids, nullptr, 0, d_tok_off, d_ws, ws_bytes, stream, h);
+  if (rc) return rc;
+  if (h.first_bad != ~0ull) {
+    *total_bytes = h.first_bad;
+    return BBPE_E_BAD_ID;
+  }
+  *total_bytes = h.total;
+  return BBPE_OK;
 }
 
 }  // extern "C"

@@ -212,6 +212,20 @@ int bbpe_decode_device(bbpe_tokenizer *tok, const int32_t *d_ids, uint64_t n_ids
                        void *d_workspace, uint64_t workspace_bytes, uint64_t *out_len,
                        uint64_t *complete_len, void *hip_stream);
 
+/* Per-token byte offsets without decoding: d_tok_off[i] (device, uint64,
+ * n_ids entries, 8-byte aligned) receives the byte offset of token i, that
+ * is the total length of the bytes of tokens 0..i-1; for the ids of one
+ * encode call it is the token's byte offset in the encoded text: a field of
+ * an encoding besides its ids, computed only when asked for (Kimi K3
+ * tokenization page, "Where the speed comes from": encodings are
+ * materialised when accessed).  *total_bytes (host) receives the length of the whole
+ * decode.  Same workspace (bbpe_decode_workspace_bytes), alignment rules,
+ * stream and synchronisation as bbpe_decode_device; BBPE_E_BAD_ID with
+ * *total_bytes = the index of the first bad id. */
+int bbpe_token_offsets_device(bbpe_tokenizer *tok, const int32_t *d_ids, uint64_t n_ids,
+                              uint64_t *d_tok_off, void *d_workspace, uint64_t workspace_bytes,
+                              uint64_t *total_bytes, void *hip_stream);
+
 /* Details of the last BBPE_E_UTF8 from bbpe_encode_segments on this handle:
  * the segment index and the absolute byte offset in d_text of the first
  * invalid sequence. */

@@ -242,3 +242,39 @@ def test_decode_alignments_and_long_tiles(tiny, pool):
         assert not o[:s_out].any() and not o[s_out + len(ref):].any()
         assert np.array_equal(d_off.cpu().numpy()[s_off:s_off + n], ref_off)
         assert done.value == utf8_complete_len(ref)
+
+
+# ---------------------------------------------------- per-token offsets ----
+
+@pytest.mark.parametrize("n", [0, 1, 4096, 4097, 50_000])
+def test_token_offsets_random_ids(tiny, n):
+    w, tok, orc = tiny
+    say("token offsets n=%d" % n)
+    r = random.Random(100 + n)
+    valid = list(range(len(w.tokens))) + [i for _, i in w.specials]
+    ids = [r.choice(valid) for _ in range(n)]
+    off, total = tok.token_offsets_device(dev_ids(ids))
+    assert total == (len(orc.decode(ids)) if n else 0)
+    assert np.array_equal(off.cpu().numpy(), orc.token_offsets(ids))
+
+
+def test_token_offsets_of_an_encode_are_text_positions(tiny):
+    """For the ids of one encode call, text[off[i]:off[i+1]] decodes token i."""
+    w, tok, orc = tiny
+    segs = [(w.segments[0][0][:30000], False), (b"<|endoftext|> tail", True)]
+    ids, _ = tok.encode_segments(segs)
+    off, total = tok.token_offsets_device(ids)
+    text = b"".join(s for s, _ in segs)
+    assert total == len(text)
+    o = off.cpu().numpy().tolist() + [len(text)]
+    h = ids.cpu().numpy()
+    for i in range(len(h)):
+        assert text[o[i]:o[i + 1]] == orc.decode([int(h[i])])
+
+
+def test_token_offsets_bad_id(tiny):
+    w, tok, orc = tiny
+    ids = list(range(100)) + [-3] + list(range(50))
+    with pytest.raises(B.BBPEError) as e:
+        tok.token_offsets_device(dev_ids(ids))
+    assert e.value.status == B.E_BAD_ID and "index 100:" in str(e.value)

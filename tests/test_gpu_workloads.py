@@ -55,5 +55,9 @@ def test_workload_parity(name):
     out, tok_off, done = tok.decode_device(torch.from_numpy(ids).cuda(), offsets=True)
     assert out.cpu().numpy().tobytes() == text
     assert done == len(text)
-    assert np.array_equal(tok_off.cpu().numpy(), orc.token_offsets(oids))
+    ref_off = orc.token_offsets(oids)
+    assert np.array_equal(tok_off.cpu().numpy(), ref_off)
+    say("token offsets", name)
+    off2, total = tok.token_offsets_device(torch.from_numpy(ids).cuda())
+    assert total == len(text) and np.array_equal(off2.cpu().numpy(), ref_off)
 
