@@ -19,8 +19,8 @@
 //     plans for");
 //   * each span between specials is cut by the split pattern, clause by
 //     clause, leftmost-first, with possessive quantifiers (tiktoken deep-dive
-//     page, "The split pattern"; the o200k-style letter clause from "r50k,
-//     cl100k, o200k");
+//     page, "The split pattern"; the o200k-style letter clause and the
+//     r50k digit clause from "r50k, cl100k, o200k");
 //   * each pre-token is merged with the parts-vector loop: ranks of adjacent
 //     pairs, take the lowest (leftmost on ties), merge, recompute only the two
 //     neighbours (tiktoken deep-dive page, "Inside encode");
@@ -183,6 +183,18 @@ size_t digits(const Span &s, size_t p) {
   return k - p;
 }
 
+// r50k-style digit clause:  ?\p{N}++  (an unbounded run of digits with an
+// optional leading space; the space is given back when no digit follows it).
+// Reading: the r50k-style grammar is cl100k's pattern with this clause in
+// place of \p{N}{1,3}+ (the page names only this change).
+size_t digits_r50k(const Span &s, size_t p) {
+  size_t j = p;
+  if (s.has(j) && s.at(j) == ' ' && s.has(j + 1) && is_number(s.at(j + 1))) ++j;
+  size_t k = j;
+  while (s.has(k) && is_number(s.at(k))) ++k;
+  return k > j ? k - p : 0;
+}
+
 bool is_punct(uint32_t c) { return !is_space(c) && !is_letter(c) && !is_number(c); }
 
 //  ?[^\s\p{L}\p{N}]++[\r\n]*+   (the leading " ?" is greedy but may give back)
@@ -239,13 +251,13 @@ size_t one_space(const Span &s, size_t p) { return (s.has(p) && is_space(s.at(p)
 // Length of the match at p, trying the clauses in the pattern's order.
 size_t match_at(const Span &s, size_t p, int grammar) {
   size_t m;
-  if (grammar == 0) {
+  if (grammar == 1) {
+    if ((m = letters_g2(s, p))) return m;
+  } else {  // cl100k and r50k-style
     if ((m = contraction(s, p))) return m;
     if ((m = letters_g1(s, p))) return m;
-  } else {
-    if ((m = letters_g2(s, p))) return m;
   }
-  if ((m = digits(s, p))) return m;
+  if ((m = grammar == 2 ? digits_r50k(s, p) : digits(s, p))) return m;
   if ((m = punct(s, p))) return m;
   if ((m = ws_to_end(s, p))) return m;
   if ((m = ws_then_newline(s, p))) return m;
@@ -405,7 +417,7 @@ void *oracle_new(const uint8_t *key_bytes, const uint64_t *key_off, const int32_
                  const int32_t *sp_ids, uint32_t ns, int grammar, int *status) {
   Oracle *o = new Oracle;
   o->grammar = grammar;
-  *status = 0;
+  *status = (grammar >= 0 && grammar <= 2) ? 0 : -2;
   std::unordered_set<int32_t> seen_rank;
   for (uint32_t i = 0; i < n; ++i) {
     std::string k(reinterpret_cast<const char *>(key_bytes + key_off[i]),

@@ -18,7 +18,8 @@ _W = r"[\p{Ll}\p{Lm}\p{Lo}\p{M}]"
 PATTERN_G2 = (_P + r"?+(?:" + _U + r"*+" + _W + r"++|" + _U + r"++" + _W + r"*+)"
               r"(?i:'[sdmt]|'ll|'ve|'re)?+|\p{N}{1,3}+| ?[^\s\p{L}\p{N}]++[\r\n]*+|"
               r"\s++\Z|\s*[\r\n]|\s+(?!\S)|\s")
-RX = {0: regex.compile(PATTERN_G1), 1: regex.compile(PATTERN_G2)}
+PATTERN_G3 = PATTERN_G1.replace(r"|\p{N}{1,3}+|", r"| ?\p{N}++|")
+RX = {0: regex.compile(PATTERN_G1), 1: regex.compile(PATTERN_G2), 2: regex.compile(PATTERN_G3)}
 
 
 def regex_split(text: bytes, grammar: int = 0) -> list[bytes]:

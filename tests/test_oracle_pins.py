@@ -35,6 +35,13 @@ def test_page_split_examples_cl100k(case):
     assert got == [p.encode() for p in case["pieces"]], case["cite"]
 
 
+@pytest.mark.parametrize("case", GOLDEN["split_r50k_style"], ids=lambda c: c["text"])
+def test_page_split_examples_r50k_style(case):
+    o, _ = atoms_only(2)
+    got = o.split(case["text"].encode())
+    assert got == [p.encode() for p in case["pieces"]], case["cite"]
+
+
 @pytest.mark.parametrize("case", GOLDEN["split_o200k_style"], ids=lambda c: c["text"])
 def test_page_split_examples_o200k_style(case):
     o, _ = atoms_only(1)
@@ -56,7 +63,7 @@ def _fuzz(seed, n, maxlen):
         yield "".join(r.choice(ALPHABET) for _ in range(r.randint(1, maxlen))).encode()
 
 
-@pytest.mark.parametrize("grammar", [0, 1])
+@pytest.mark.parametrize("grammar", [0, 1, 2])
 def test_split_matches_regex_library_fuzz(grammar):
     """The oracle's clause-by-clause matcher against the regex module running
     the printed pattern (a library routine with its own Unicode tables)."""
@@ -65,7 +72,7 @@ def test_split_matches_regex_library_fuzz(grammar):
         assert o.split(s) == regex_split(s, grammar), s
 
 
-@pytest.mark.parametrize("grammar", [0, 1])
+@pytest.mark.parametrize("grammar", [0, 1, 2])
 def test_split_tiles_input(grammar):
     o, _ = atoms_only(grammar)
     for s in _fuzz(200 + grammar, 2000, 30):
@@ -87,6 +94,18 @@ def test_split_regex_appendix_cases():
               "!!a", "!a", " !a", "x\t!abc", "!\n !", "a\r\n\r\n  b", "  123"]:
         b = s.encode()
         assert o.split(b) == regex_split(b, 0), s
+
+
+def test_split_r50k_style_digits():
+    """The leading space joins a digit run only when it is a single U+0020
+    right before the digits; other whitespace, CR/LF and span ends behave as
+    in cl100k."""
+    o, _ = atoms_only(2)
+    for s in ["a 123", "a  123", "a\t123", "x\n 12", " 1", "1 2 3", "१२३४५ ६", "x²³⁴⁵",
+              "12ab", "ab12", "'s 9", "  \n  42  "]:
+        b = s.encode()
+        assert o.split(b) == regex_split(b, 2), s
+    assert o.split(b"a  123") == [b"a", b" ", b" 123"]
 
 
 def test_split_o200k_style_readings():
