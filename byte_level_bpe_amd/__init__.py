@@ -31,6 +31,7 @@ E_WORKSPACE = -8
 E_STATE = -9
 GRAMMAR_CL100K = 0
 GRAMMAR_O200K_STYLE = 1
+GRAMMAR_R50K_STYLE = 2
 TIKTOKEN_SAFE = 1
 COUNT_ONLY = 2
 

@@ -1,5 +1,6 @@
 // Split of every span into pre-tokens, as piece-start bits, for the cl100k
-// grammar and the o200k-style grammar.
+// grammar, the o200k-style grammar and the r50k-style grammar (cl100k with
+// r50k's digit clause, run by the cl100k kernels).
 //
 // The printed patterns are applied leftmost-first with possessive
 // quantifiers (tiktoken deep-dive page, "The split pattern"; the o200k-style
@@ -9,7 +10,8 @@
 // characters a few bytes around it, except for quantities carried along the
 // text:
 //   * the position of a digit inside its digit run, modulo 3 (digit groups of
-//     at most three);                                            (both)
+//     at most three; not needed by the r50k-style digit clause, whose run
+//     is one match, led by a single space before it when there is one);
 //   * whether a run of non-CR/LF whitespace reaches a non-space character of
 //     the same span (the last CR/LF of a whitespace run ends a match only if
 //     the whitespace after it is followed by a non-space character); (both)
@@ -181,7 +183,7 @@ __device__ __forceinline__ void let_kind(uint32_t k, uint64_t &t, uint32_t &sm) 
 // Per-word split state.
 // ---------------------------------------------------------------------------
 struct SplitWord {
-  uint64_t SS, SPST, IN, BRK, LD, N_, CR_, NC, WS_, pN, pO;
+  uint64_t SS, SPST, IN, BRK, LD, N_, CR_, NC, WS_, pN, pO, pSP;
   uint64_t K0, K1, K2, K3;   // o200k-style: character kind bit planes
   uint64_t todo;             // o200k-style: bytes the automaton steps on
   uint64_t WstCR;            // o200k-style: CR/LF that begins a whitespace run
@@ -282,6 +284,7 @@ __device__ __forceinline__ void split_word(const EncodeArgs &a, int64_t w, const
   o.WS_ = WS_;
   o.pN = pN;
   o.pO = pO;
+  o.pSP = pSP;
 
   if (G == 0) {
     // punctuation (any non-letter, non-digit, non-space character): a match
@@ -384,11 +387,15 @@ __device__ __forceinline__ uint64_t pack_word_fn(const SplitWord &o) {
 // word.
 template <int G>
 __device__ __forceinline__ uint64_t split_finish(const SplitWord &o, uint64_t pCRmask, uint32_t ph,
-                                                 uint32_t xs, uint32_t v) {
+                                                 uint32_t xs, uint32_t v, bool r50k) {
   uint64_t PH0 = 0, E2b = 0, VN = 0, extra = 0;
   const uint64_t NLD = o.N_ & o.LD;
   const uint64_t runstart = NLD & (o.SS | ~o.pN);
-  if (o.N_ == NLD) {  // single-byte digits only
+  if (r50k) {
+    // one match per digit run; a U+0020 right before the run (in the same
+    // span) is always a match start under the whitespace rules, and here
+    // it leads the digits, so the run's own start goes
+  } else if (o.N_ == NLD) {  // single-byte digits only
     PH0 = digit_phase0_ascii(NLD, runstart, ph);
   } else {
     for (int i = 0; i < 64; ++i) {
@@ -425,7 +432,7 @@ __device__ __forceinline__ uint64_t split_finish(const SplitWord &o, uint64_t pC
   }
   const uint64_t Qcand = o.NC & o.LD & pCRmask;
   if (Qcand) VN = v_next(o.BRK, o.NC, o.WS_, v);
-  const uint64_t startN = NLD & (o.SS | ~o.pN | PH0);
+  const uint64_t startN = r50k ? (runstart & ~o.pSP) : (NLD & (o.SS | ~o.pN | PH0));
   return o.static_starts | startN | E2b | extra | (Qcand & VN);
 }
 
@@ -554,7 +561,8 @@ __device__ __forceinline__ void split_body(const EncodeArgs &a) {
   const uint32_t xs = ltr_apply_x<G>(exl, (carry >> 8) & 0xFFu);
   const uint32_t v = fv_apply(exv, (carry >> 16) & 1u);
   const uint64_t pCRm = prev_cr(o);
-  uint64_t ps = split_finish<G>(o, pCRm, ph, xs, v) & m.valid;
+  const bool r50k = G == 0 && a.T.grammar == BBPE_GRAMMAR_R50K_STYLE;
+  uint64_t ps = split_finish<G>(o, pCRm, ph, xs, v, r50k) & m.valid;
   if (a.merge_units) {
     // Merge units: where no key can occur across a position, no merge ever
     // crosses it (every part is a key), so the piece is cut there into

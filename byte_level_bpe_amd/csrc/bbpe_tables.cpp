@@ -387,7 +387,8 @@ int bbpe_load_ranks(const uint8_t *key_bytes, const uint64_t *key_off, const int
                     const int32_t *special_ids, uint32_t ns, int grammar,
                     bbpe_tokenizer **out, uint64_t *device_table_bytes) {
   if (!out || !device_table_bytes || !key_bytes || !key_off || !ranks) return BBPE_E_INVALID_ARG;
-  if (grammar != BBPE_GRAMMAR_CL100K && grammar != BBPE_GRAMMAR_O200K_STYLE)
+  if (grammar != BBPE_GRAMMAR_CL100K && grammar != BBPE_GRAMMAR_O200K_STYLE &&
+      grammar != BBPE_GRAMMAR_R50K_STYLE)
     return BBPE_E_INVALID_ARG;
   *out = nullptr;
   std::vector<std::string> keys;
@@ -416,7 +417,8 @@ int bbpe_load_ranks_tiktoken_file(const char *path, const uint8_t *special_bytes
                                   uint32_t ns, int grammar, bbpe_tokenizer **out,
                                   uint64_t *device_table_bytes) {
   if (!path || !out || !device_table_bytes) return BBPE_E_INVALID_ARG;
-  if (grammar != BBPE_GRAMMAR_CL100K && grammar != BBPE_GRAMMAR_O200K_STYLE)
+  if (grammar != BBPE_GRAMMAR_CL100K && grammar != BBPE_GRAMMAR_O200K_STYLE &&
+      grammar != BBPE_GRAMMAR_R50K_STYLE)
     return BBPE_E_INVALID_ARG;
   *out = nullptr;
   FILE *f = fopen(path, "rb");

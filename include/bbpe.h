@@ -61,8 +61,11 @@ enum {
  * categories with the contraction appended to the word ("r50k, cl100k,
  * o200k"):  [^\r\n\p{L}\p{N}]?+ (U*+ W++ | U++ W*+) (?i:'[sdmt]|'ll|'ve|'re)?+
  * with U = [\p{Lu}\p{Lt}\p{Lm}\p{Lo}\p{M}] and W = [\p{Ll}\p{Lm}\p{Lo}\p{M}],
- * followed by the cl100k clauses from the digit clause on. */
-enum { BBPE_GRAMMAR_CL100K = 0, BBPE_GRAMMAR_O200K_STYLE = 1 };
+ * followed by the cl100k clauses from the digit clause on.  R50K_STYLE is
+ * the cl100k pattern with r50k's digit clause " ?\p{N}++" (an unbounded
+ * digit run with an optional leading space, "r50k, cl100k, o200k") in place
+ * of \p{N}{1,3}+; the page names only that change. */
+enum { BBPE_GRAMMAR_CL100K = 0, BBPE_GRAMMAR_O200K_STYLE = 1, BBPE_GRAMMAR_R50K_STYLE = 2 };
 
 /* encode flags */
 enum {

@@ -74,7 +74,7 @@ def make(tokens, specials=(), grammar=0):
     return B.load_ranks(tokens, specials, grammar), Oracle(tokens, specials, grammar)
 
 
-@pytest.fixture(scope="module", params=[0, 1], ids=["cl100k", "o200k"])
+@pytest.fixture(scope="module", params=[0, 1, 2], ids=["cl100k", "o200k", "r50k"])
 def atoms(request):
     """Atoms-only table (ids = per-byte ranks) under each split grammar."""
     return make(atoms_permuted(1), SPECIALS, request.param)
@@ -204,6 +204,25 @@ def test_encode_fuzz_tiny_table(tiny):
     assert_ids(tok, orc, segs, what="tiny fuzz")
     text = b" ".join(_fuzz(7, 3000, 200, alpha))
     assert_ids(tok, orc, [(text, False)], what="tiny fuzz long")
+
+
+def test_r50k_style_digit_runs_tiny_table(tiny):
+    """The r50k-style grammar with the tiny table: digit runs of every length
+    with and without a leading space, across words and tiles, merged."""
+    w, _ = tiny
+    tok, orc = make(w.tokens, w.specials, 2)
+    r = random.Random(12)
+    parts = []
+    for _ in range(4000):
+        k = r.random()
+        d = "".join(r.choice("0123456789") for _ in range(r.choice([1, 2, 3, 4, 7, 63, 64, 65, 200])))
+        parts.append((" " if k < 0.5 else "  " if k < 0.6 else "\n " if k < 0.7 else "x") + d)
+    text = "".join(parts).encode()
+    say("r50k-style digit runs: %d bytes" % len(text))
+    assert_pieces(tok, orc, [(text, False)], what="r50k digits")
+    assert_ids(tok, orc, [(text, False)], what="r50k digits")
+    segs = [(s, False) for s in _fuzz(13, 3000, 40)]
+    assert_ids(tok, orc, segs, what="r50k fuzz")
 
 
 @pytest.fixture(scope="module")
