@@ -355,65 +355,129 @@ constexpr uint32_t WNS = 8;                // positions per lane in the group ti
 constexpr uint32_t WAVE_MAX = 64 * WNS;    // longest unit the group tiers hold
 constexpr uint32_t GROUP_PACK_MIN = 4096;  // group units above which several share a wave
 
+// Continue a probe whose first slot (sl, e at index idx) is already loaded.
+template <typename RestEq>
+__device__ __forceinline__ int32_t probe_from(const DevTables &T, uint32_t idx, Slot sl, uint64_t e,
+                                              uint64_t k8, uint64_t k8b, uint32_t len,
+                                              uint32_t &meta, RestEq rest_eq) {
+  for (;;) {
+    if (sl.rank < 0) return RANK_NONE;
+    if (slot_match(T, sl, e, k8, k8b, len) &&
+        (len <= 16 || rest_eq(T.blob + (sl.meta >> META_OFF_SHIFT)))) {
+      meta = sl.meta;
+      return sl.rank;
+    }
+    idx = (idx + 1) & T.slot_mask;
+    sl = T.slots[idx];
+    e = T.ext[idx];
+  }
+}
+
 // Every unit: specials, single bytes and units that are keys whose own
 // merges rebuild them get their id here; the rest are listed for the merge
-// kernels by length class.  Each block gathers its list entries in LDS and
-// reserves room in the global lists with one atomic per class: device-scope
-// atomics on a few shared counters serialise, so blocks are large (1024
-// units per block and pass).
+// kernels by length class.  Each thread takes PROBE_U units and issues the
+// loads of all of them (offsets, then bytes and special bits, then the
+// first hash slot) before it resolves any, so that one wave keeps several
+// units' memory chains in flight.  Each block gathers its list entries in
+// LDS (one array, grouped by class) and reserves room in the global lists
+// with one atomic per class.
+constexpr uint32_t PROBE_U = 4;
+constexpr uint32_t PROBE_CHUNK = PROBE_BLOCK * PROBE_U;
 
 __global__ void __launch_bounds__(PROBE_BLOCK) k_probe(EncodeArgs a) {
   if (a.ws.status->pad2) return;
   Status *st = a.ws.status;
   const uint32_t P = uint32_t(st->n_pieces);
   const DevTables &T = a.T;
-  __shared__ unsigned int s_cnt[ML_COUNT], s_base[ML_COUNT];
-  __shared__ uint32_t s_list[ML_COUNT][PROBE_BLOCK];
-  for (uint32_t b = blockIdx.x * PROBE_BLOCK; b < P; b += gridDim.x * PROBE_BLOCK) {
-    const uint32_t i = b + threadIdx.x;
-    int cls = -1;  // MergeList of a unit left to merge
-    if (i < P) {
-      const uint32_t s = a.ws.piece_start[i];
-      const uint32_t m = a.ws.piece_start[i + 1] - s;
+  __shared__ unsigned int s_cnt[ML_COUNT], s_base[ML_COUNT], s_off[ML_COUNT], s_cur[ML_COUNT];
+  __shared__ uint32_t s_list[PROBE_CHUNK];
+  __shared__ int32_t s_atom[256];
+  if (threadIdx.x < 256) s_atom[threadIdx.x] = T.atom[threadIdx.x];
+  __syncthreads();
+  for (uint32_t b = blockIdx.x * PROBE_CHUNK; b < P; b += gridDim.x * PROBE_CHUNK) {
+    uint32_t idx[PROBE_U], s0[PROBE_U], m[PROBE_U];
+#pragma unroll
+    for (uint32_t u = 0; u < PROBE_U; ++u) {
+      idx[u] = b + u * PROBE_BLOCK + threadIdx.x;
+      const bool in = idx[u] < P;
+      s0[u] = in ? a.ws.piece_start[idx[u]] : 0u;
+      m[u] = in ? a.ws.piece_start[idx[u] + 1] - s0[u] : 0u;
+    }
+    uint64_t spw[PROBE_U];
+    UnitBytes<32> ub[PROBE_U];
+#pragma unroll
+    for (uint32_t u = 0; u < PROBE_U; ++u) {
+      spw[u] = m[u] ? a.ws.spst[s0[u] >> 6] : 0ull;
+      load_unit(a.text, a.n, s0[u], min(m[u], 32u), ub[u]);
+    }
+    uint64_t h[PROBE_U], k8[PROBE_U], k8b[PROBE_U];
+    uint32_t slot[PROBE_U];
+    Slot sl[PROBE_U];
+    uint64_t ex[PROBE_U];
+#pragma unroll
+    for (uint32_t u = 0; u < PROBE_U; ++u) {
+      const uint32_t len = min(max(m[u], 1u), 32u);
+      unit_hash(ub[u], 0, len, h[u], k8[u], k8b[u]);
+      slot[u] = uint32_t(h[u]) & T.slot_mask;
+      sl[u] = T.slots[slot[u]];
+      ex[u] = T.ext[slot[u]];
+    }
+    int cls[PROBE_U];
+#pragma unroll
+    for (uint32_t u = 0; u < PROBE_U; ++u) {
+      cls[u] = -1;  // MergeList of a unit left to merge
+      const uint32_t mm = m[u], s = s0[u];
+      if (mm == 0) continue;
       int32_t id = -1;
-      if ((a.ws.spst[s >> 6] >> (s & 63)) & 1) {
-        id = special_id(T, a.text + s, m);
-      } else if (m == 1) {
-        id = T.atom[a.text[s]];
-      } else if (m <= 32) {
-        UnitBytes<32> u;
-        load_unit(a.text, a.n, s, m, u);
-        uint64_t h, k8, k8b;
-        unit_hash(u, 0, m, h, k8, k8b);
+      if ((spw[u] >> (s & 63)) & 1) {
+        id = special_id(T, a.text + s, mm);
+      } else if (mm == 1) {
+        id = s_atom[ub[u].byte(0)];
+      } else if (mm <= 32) {
         uint32_t meta = 0;
-        const int32_t r = m <= T.max_key_len
-                              ? probe(T, h, k8, k8b, m, meta,
-                                      [&](const uint8_t *bb) __attribute__((always_inline)) { return unit_rest_eq(u, 0, m, bb); })
+        const UnitBytes<32> &uu = ub[u];
+        const int32_t r = mm <= T.max_key_len
+                              ? probe_from(T, slot[u], sl[u], ex[u], k8[u], k8b[u], mm, meta,
+                                           [&](const uint8_t *bb) __attribute__((always_inline)) { return unit_rest_eq(uu, 0, mm, bb); })
                               : RANK_NONE;
         if (r != RANK_NONE && (meta & META_SELF)) id = r;
-        else cls = m <= 4 ? ML_4 : m <= 8 ? ML_8 : m <= 16 ? ML_16 : ML_32;
+        else cls[u] = mm <= 4 ? ML_4 : mm <= 8 ? ML_8 : mm <= 16 ? ML_16 : ML_32;
       } else {
         uint32_t meta = 0;
-        const int32_t r = m <= T.max_key_len ? lookup_text(T, a.text + s, m, meta) : RANK_NONE;
+        const int32_t r = mm <= T.max_key_len ? lookup_text(T, a.text + s, mm, meta) : RANK_NONE;
         if (r != RANK_NONE && (meta & META_SELF)) id = r;
-        else cls = m <= 128 ? ML_G128 : m <= 256 ? ML_G256 : m <= WAVE_MAX ? ML_G512 : ML_LONG;
+        else cls[u] = mm <= 128 ? ML_G128 : mm <= 256 ? ML_G256 : mm <= WAVE_MAX ? ML_G512 : ML_LONG;
       }
       if (id >= 0) {
         a.ws.tmp_ids[s] = id;
-        a.ws.piece_cnt[i] = 1;
+        a.ws.piece_cnt[idx[u]] = 1;
       }
     }
-    if (threadIdx.x < ML_COUNT) s_cnt[threadIdx.x] = 0;
+    if (threadIdx.x < ML_COUNT) {
+      s_cnt[threadIdx.x] = 0;
+      s_cur[threadIdx.x] = 0;
+    }
     __syncthreads();
-    if (cls >= 0) s_list[cls][atomicAdd(&s_cnt[cls], 1u)] = i;
+#pragma unroll
+    for (uint32_t u = 0; u < PROBE_U; ++u)
+      if (cls[u] >= 0) atomicAdd(&s_cnt[cls[u]], 1u);
     __syncthreads();
-    if (threadIdx.x < ML_COUNT && s_cnt[threadIdx.x])
-      s_base[threadIdx.x] = atomicAdd(&st->n_list[threadIdx.x], s_cnt[threadIdx.x]);
+    if (threadIdx.x < ML_COUNT) {
+      uint32_t o = 0;
+      for (uint32_t L = 0; L < threadIdx.x; ++L) o += s_cnt[L];
+      s_off[threadIdx.x] = o;
+      if (s_cnt[threadIdx.x]) s_base[threadIdx.x] = atomicAdd(&st->n_list[threadIdx.x], s_cnt[threadIdx.x]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (uint32_t u = 0; u < PROBE_U; ++u)
+      if (cls[u] >= 0) s_list[s_off[cls[u]] + atomicAdd(&s_cur[cls[u]], 1u)] = idx[u];
     __syncthreads();
 #pragma unroll
     for (uint32_t L = 0; L < ML_COUNT; ++L) {
       uint32_t *list = a.ws.lst[L];
-      for (uint32_t k = threadIdx.x; k < s_cnt[L]; k += PROBE_BLOCK) list[s_base[L] + k] = s_list[L][k];
+      const uint32_t o = s_off[L];
+      for (uint32_t k = threadIdx.x; k < s_cnt[L]; k += PROBE_BLOCK) list[s_base[L] + k] = s_list[o + k];
     }
     __syncthreads();
   }

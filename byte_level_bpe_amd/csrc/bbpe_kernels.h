@@ -49,7 +49,7 @@ struct WsPtrs {
 };
 
 // threads per k_probe block (units per block and pass)
-constexpr uint32_t PROBE_BLOCK = 1024;
+constexpr uint32_t PROBE_BLOCK = 512;
 
 struct EncodeArgs {
   DevTables T;
