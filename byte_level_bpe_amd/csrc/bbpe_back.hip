@@ -638,13 +638,15 @@ __device__ void merge_group(const EncodeArgs &a, const uint32_t *list, uint32_t 
 }
 
 // ---------------------------------------------------------------------------
-// Long tier: one workgroup per unit longer than WAVE_MAX, state in global memory.
-// Per position j of the unit (text byte s + j): lrank = rank of the pair that
-// starts with the part starting at j, lpart = id of that part.  Per 64-position
-// block b of the unit, at index (s >> 5) + b (a unit of m > 64 bytes needs
-// ceil(m/64) <= floor(m/32) entries, so units never share one): lbits = part
-// starts, lsel = pairs chosen this round, lmin = least pair rank, ldirty =
-// lmin stale.
+// Long tier: one workgroup per unit longer than WAVE_MAX.  Per position j of
+// the unit (text byte s + j), in global memory: lrank = rank of the pair that
+// starts with the part starting at j, lpart = id of that part.  Per
+// 64-position block b of the unit: part starts, pairs chosen this round,
+// the part starts whose pair has the block's least rank, that least rank,
+// least rank stale; in LDS for units of up to
+// 64 * LONG_LDS_BLOCKS bytes, else in global memory at index (s >> 5) + b (a
+// unit of m > 64 bytes needs ceil(m/64) <= floor(m/32) entries, so units
+// never share one): lbits, lsel, leqm, lmin, ldirty.
 //
 // Each round takes the least rank R and merges in one batch the leftmost
 // non-overlapping pairs of rank R: in every run of consecutive parts whose
@@ -662,7 +664,7 @@ __device__ void merge_group(const EncodeArgs &a, const uint32_t *list, uint32_t 
 struct LongUnit {
   const EncodeArgs &a;
   uint32_t s, m, nb;
-  unsigned long long *bits, *sel;
+  unsigned long long *bits, *sel, *eqm;
   int32_t *mn;
   uint32_t *dirty;
   __device__ __forceinline__ int32_t &rank(uint32_t j) const { return a.ws.lrank[s + j]; }
@@ -692,9 +694,10 @@ struct LongUnit {
   }
   __device__ __forceinline__ bool chosen(uint32_t j) const { return (sel[j >> 6] >> (j & 63)) & 1; }
   // Pair ranks of the part starts of block b: the least one, and the mask of
-  // those equal to R.  All 64 loads are issued without branches (addresses
-  // clamped into the unit) so that they overlap.
-  __device__ __forceinline__ int32_t block_scan(uint32_t b, unsigned long long A, int32_t R,
+  // the starts whose pair has it (empty when no pair has a rank).  All 64
+  // loads are issued without branches (addresses clamped into the unit) so
+  // that they overlap.
+  __device__ __forceinline__ int32_t block_scan(uint32_t b, unsigned long long A,
                                                 unsigned long long &eq) const {
     int32_t r = RANK_NONE;
     eq = 0;
@@ -706,12 +709,17 @@ struct LongUnit {
       for (uint32_t t = 0; t < 8; ++t) v[t] = rank(min(j0 + q + t, m - 1));
 #pragma unroll
       for (uint32_t t = 0; t < 8; ++t) {
-        const bool on = (A >> (q + t)) & 1;
-        r = on ? min(r, v[t]) : r;
-        eq |= (on && v[t] == R) ? (1ull << (q + t)) : 0ull;
+        const int32_t x = ((A >> (q + t)) & 1) ? v[t] : RANK_NONE;
+        eq = x < r ? (1ull << (q + t)) : (x == r ? eq | (1ull << (q + t)) : eq);
+        r = min(r, x);
       }
     }
-    return r;
+    return r == RANK_NONE ? (eq = 0, r) : r;
+  }
+  __device__ __forceinline__ void rescan(uint32_t b) const {
+    unsigned long long e;
+    mn[b] = block_scan(b, bits[b], e);
+    eqm[b] = e;
   }
 };
 
@@ -812,20 +820,23 @@ __device__ __forceinline__ int32_t block_min_i32(int32_t v, int32_t *sh) {
   return r;
 }
 
-// inclusive scan of chain-parity functions over the threads, in thread order
+// inclusive scan of chain-parity functions over the threads, in thread order:
+// wave scans by shuffles, then each wave folds in the totals of the waves
+// before it (0 is the identity)
 __device__ __forceinline__ uint32_t block_chain_scan(uint32_t f, uint32_t *sh) {
-  const uint32_t t = threadIdx.x;
-  sh[t] = f;
-  __syncthreads();
-  for (uint32_t d = 1; d < LONG_BLOCK; d <<= 1) {
-    const uint32_t v = t >= d ? chain_then(sh[t - d], sh[t]) : sh[t];
-    __syncthreads();
-    sh[t] = v;
-    __syncthreads();
+  const int lane = int(threadIdx.x & 63);
+  const uint32_t wv = threadIdx.x / 64;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(f, d, 64);
+    if (lane >= d) f = chain_then(o, f);
   }
-  const uint32_t r = sh[t];
+  if (lane == 63) sh[wv] = f;
   __syncthreads();
-  return r;
+  uint32_t pre = 0;
+  for (uint32_t q = 0; q < wv; ++q) pre = chain_then(pre, sh[q]);
+  __syncthreads();
+  return chain_then(pre, f);
 }
 
 // exclusive sum over the threads; total to every thread
@@ -848,19 +859,51 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t *sh, uin
 // One workgroup per unit.  Blocks of 64 positions are owned by threads for
 // the scans; the chosen pairs of a round are handled per quarter block (16
 // positions), so that up to 4 * blocks threads merge side by side.
-__device__ void merge_long(const EncodeArgs &a, uint32_t i, uint32_t *sh) {
+constexpr uint32_t LONG_LDS_BLOCKS = 2048;
+struct LongLds {
+  unsigned long long bits[LONG_LDS_BLOCKS], sel[LONG_LDS_BLOCKS], eqm[LONG_LDS_BLOCKS];
+  int32_t mn[LONG_LDS_BLOCKS];
+  uint32_t dirty[LONG_LDS_BLOCKS];
+};
+
+__device__ void merge_long(const EncodeArgs &a, uint32_t i, uint32_t *sh, LongLds &ld) {
   const DevTables &T = a.T;
   const uint32_t tid = threadIdx.x;
   const uint32_t s = a.ws.piece_start[i];
   const uint32_t m = a.ws.piece_start[i + 1] - s;
   const uint8_t *p = a.text + s;
   const uint32_t base = s >> 5;
-  LongUnit U{a, s, m, (m + 63) / 64, a.ws.lbits + base, a.ws.lsel + base, a.ws.lmin + base,
-             a.ws.ldirty + base};
+  const uint32_t nbk = (m + 63) / 64;
+  const bool in_lds = nbk <= LONG_LDS_BLOCKS;
+  LongUnit U{a, s, m, nbk, in_lds ? ld.bits : a.ws.lbits + base, in_lds ? ld.sel : a.ws.lsel + base,
+             in_lds ? ld.eqm : a.ws.leqm + base, in_lds ? ld.mn : a.ws.lmin + base,
+             in_lds ? ld.dirty : a.ws.ldirty + base};
   const uint32_t nb = U.nb;
-  for (uint32_t j = tid; j < m; j += LONG_BLOCK) {
-    U.rank(j) = (j + 1 < m) ? T.pair[uint32_t(p[j]) * 256u + p[j + 1]] : RANK_NONE;
-    U.part(j) = T.atom[p[j]];
+  // initial pair ranks and atoms, eight positions per thread with their
+  // loads issued before the stores
+  for (uint32_t j0 = tid; j0 < m; j0 += 8 * LONG_BLOCK) {
+    uint32_t c0[8], c1[8];
+#pragma unroll
+    for (uint32_t k = 0; k < 8; ++k) {
+      const uint32_t j = j0 + k * LONG_BLOCK;
+      c0[k] = j < m ? p[j] : 0u;
+      c1[k] = j + 1 < m ? p[j + 1] : 0u;
+    }
+    int32_t rk[8], at[8];
+#pragma unroll
+    for (uint32_t k = 0; k < 8; ++k) {
+      const uint32_t j = j0 + k * LONG_BLOCK;
+      rk[k] = (j + 1 < m) ? T.pair[c0[k] * 256u + c1[k]] : RANK_NONE;
+      at[k] = T.atom[c0[k]];
+    }
+#pragma unroll
+    for (uint32_t k = 0; k < 8; ++k) {
+      const uint32_t j = j0 + k * LONG_BLOCK;
+      if (j < m) {
+        U.rank(j) = rk[k];
+        U.part(j) = at[k];
+      }
+    }
   }
   for (uint32_t b = tid; b < nb; b += LONG_BLOCK) {
     const uint32_t left = m - 64 * b;
@@ -869,10 +912,7 @@ __device__ void merge_long(const EncodeArgs &a, uint32_t i, uint32_t *sh) {
     U.dirty[b] = 0;
   }
   __syncthreads();
-  for (uint32_t b = tid; b < nb; b += LONG_BLOCK) {
-    unsigned long long eq;
-    U.mn[b] = U.block_scan(b, U.bits[b], RANK_NONE, eq);
-  }
+  for (uint32_t b = tid; b < nb; b += LONG_BLOCK) U.rescan(b);
   __syncthreads();
 
   for (;;) {
@@ -888,7 +928,7 @@ __device__ void merge_long(const EncodeArgs &a, uint32_t i, uint32_t *sh) {
       unsigned long long A = 0, C = 0;
       if (b < nb) {
         A = U.bits[b];
-        if (U.mn[b] == R) U.block_scan(b, A, R, C);
+        if (U.mn[b] == R) C = U.eqm[b];
       }
       const unsigned long long N = A & ~C;
       uint32_t f;
@@ -1001,8 +1041,7 @@ __device__ void merge_long(const EncodeArgs &a, uint32_t i, uint32_t *sh) {
     for (uint32_t b = tid; b < nb; b += LONG_BLOCK) {
       U.sel[b] = 0;
       if (U.dirty[b]) {
-        unsigned long long eq;
-        U.mn[b] = U.block_scan(b, U.bits[b], RANK_NONE, eq);
+        U.rescan(b);
         U.dirty[b] = 0;
       }
     }
@@ -1034,9 +1073,10 @@ __device__ void merge_long(const EncodeArgs &a, uint32_t i, uint32_t *sh) {
 __global__ void __launch_bounds__(LONG_BLOCK) k_merge_long(EncodeArgs a) {
   if (a.ws.status->pad2) return;
   __shared__ uint32_t sh[LONG_BLOCK];
+  __shared__ LongLds ld;
   const uint32_t nll = a.ws.status->n_list[ML_LONG];
   for (uint32_t item = blockIdx.x; item < nll; item += gridDim.x)
-    merge_long(a, a.ws.lst[ML_LONG][item], sh);
+    merge_long(a, a.ws.lst[ML_LONG][item], sh, ld);
 }
 
 // ---------------------------------------------------------------------------

@@ -22,7 +22,7 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 struct WsLayout {
   uint64_t status, tile_nchar, tile_lastchg, tile_charbase, tile_chgcarry, seg_local, seg_charstart,
       ss, spst, spc, ps, tile_fn, tile_carry, tile_np, piece_start, piece_cnt, piece_off,
-      tmp_ids, scan_part, lst[ML_COUNT], lrank, lpart, lnl, lnr, lbits, lsel, lmin, ldirty, wslow, wseg, wseg_at, total;
+      tmp_ids, scan_part, lst[ML_COUNT], lrank, lpart, lnl, lnr, lbits, lsel, leqm, lmin, ldirty, wslow, wseg, wseg_at, total;
   uint64_t n_words;
   uint32_t n_tiles;
 };
@@ -64,6 +64,7 @@ WsLayout layout_for(uint64_t n, uint32_t n_seg) {
   take(L.lnr, 4 * (n + 1));
   take(L.lbits, 8 * (n / 32 + 2));
   take(L.lsel, 8 * (n / 32 + 2));
+  take(L.leqm, 8 * (n / 32 + 2));
   take(L.lmin, 4 * (n / 32 + 2));
   take(L.ldirty, 4 * (n / 32 + 2));
   take(L.wslow, 8 * SLOW_WORDS * (W + 1));
@@ -192,6 +193,7 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
   a.ws.lnr = reinterpret_cast<int32_t *>(w + L.lnr);
   a.ws.lbits = reinterpret_cast<unsigned long long *>(w + L.lbits);
   a.ws.lsel = reinterpret_cast<unsigned long long *>(w + L.lsel);
+  a.ws.leqm = reinterpret_cast<unsigned long long *>(w + L.leqm);
   a.ws.lmin = reinterpret_cast<int32_t *>(w + L.lmin);
   a.ws.ldirty = reinterpret_cast<uint32_t *>(w + L.ldirty);
   a.ws.wslow = reinterpret_cast<uint64_t *>(w + L.wslow);

@@ -37,7 +37,7 @@ struct WsPtrs {
   int32_t *lrank, *lpart, *lnl, *lnr;
   // long tier, per 64-position block of a unit (index (s >> 5) + block):
   // part starts, selected pair starts, least pair rank, stale-minimum flag
-  unsigned long long *lbits, *lsel;
+  unsigned long long *lbits, *lsel, *leqm;
   int32_t *lmin;
   uint32_t *ldirty;
   // per text word, stored by the first front-end kernel: the multi-byte part
