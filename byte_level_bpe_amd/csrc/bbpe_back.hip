@@ -968,12 +968,13 @@ __device__ void merge_long(const EncodeArgs &a, uint32_t i, uint32_t *sh, LongLd
     // 2. the pairs each chosen merge creates, and the first merge after which
     // the batch must stop
     uint32_t stop = 0xFFFFFFFFu;
-    for (uint32_t q = tid; q < 4 * nb; q += LONG_BLOCK) {
-      const uint32_t b = q >> 2;
-      unsigned long long S = U.sel[b] & (0xFFFFull << (16 * (q & 3)));
-      while (S) {
-        const uint32_t j = 64 * b + uint32_t(__ffsll(S) - 1);
-        S &= S - 1;
+    // (thread x takes positions 2x and 2x+1, at most one of which begins a
+    // chosen pair, so that neighbouring lanes touch neighbouring positions)
+    for (uint32_t x = tid; x < 32 * nb; x += LONG_BLOCK) {
+      const uint32_t b = x >> 5;
+      const uint32_t two = uint32_t(U.sel[b] >> (2 * (x & 31))) & 3u;
+      if (two) {
+        const uint32_t j = 64 * b + 2 * (x & 31) + ((two & 1) ? 0u : 1u);
         const uint32_t k = U.next(j + 1);
         const uint32_t k2 = U.next(k + 1);
         const int y = U.prev(j);
@@ -996,13 +997,11 @@ __device__ void merge_long(const EncodeArgs &a, uint32_t i, uint32_t *sh, LongLd
     stop = uint32_t(block_min_i32(int32_t(min(stop, 0x7FFFFFFFu)), reinterpret_cast<int32_t *>(sh)));
 
     // 3. apply the merges up to and including `stop`
-    for (uint32_t q = tid; q < 4 * nb && 16 * q <= stop; q += LONG_BLOCK) {
-      const uint32_t b = q >> 2;
-      unsigned long long S = U.sel[b] & (0xFFFFull << (16 * (q & 3)));
-      while (S) {
-        const uint32_t j = 64 * b + uint32_t(__ffsll(S) - 1);
-        S &= S - 1;
-        if (j > stop) break;
+    for (uint32_t x = tid; x < 32 * nb && 2 * x <= stop; x += LONG_BLOCK) {
+      const uint32_t b = x >> 5;
+      const uint32_t two = uint32_t(U.sel[b] >> (2 * (x & 31))) & 3u;
+      const uint32_t j = 64 * b + 2 * (x & 31) + ((two & 1) ? 0u : 1u);
+      if (two && j <= stop) {
         const uint32_t k = U.next(j + 1);
         const uint32_t k2 = U.next(k + 1);
         const int y = U.prev(j);
@@ -1026,13 +1025,11 @@ __device__ void merge_long(const EncodeArgs &a, uint32_t i, uint32_t *sh, LongLd
     }
     __syncthreads();
     // the merged right parts stop being part starts
-    for (uint32_t q = tid; q < 4 * nb && 16 * q <= stop; q += LONG_BLOCK) {
-      const uint32_t b = q >> 2;
-      unsigned long long S = U.sel[b] & (0xFFFFull << (16 * (q & 3)));
-      while (S) {
-        const uint32_t j = 64 * b + uint32_t(__ffsll(S) - 1);
-        S &= S - 1;
-        if (j > stop) break;
+    for (uint32_t x = tid; x < 32 * nb && 2 * x <= stop; x += LONG_BLOCK) {
+      const uint32_t b = x >> 5;
+      const uint32_t two = uint32_t(U.sel[b] >> (2 * (x & 31))) & 3u;
+      const uint32_t j = 64 * b + 2 * (x & 31) + ((two & 1) ? 0u : 1u);
+      if (two && j <= stop) {
         const uint32_t k = U.next(j + 1);
         atomicAnd(&U.bits[k >> 6], ~(1ull << (k & 63)));
       }
