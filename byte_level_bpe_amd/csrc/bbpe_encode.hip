@@ -20,7 +20,7 @@ namespace {
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 struct WsLayout {
-  uint64_t status, tile_nchar, tile_lastchg, tile_charbase, tile_chgcarry, seg_local, seg_charstart,
+  uint64_t status, tile_nchar, tile_err, tile_bad, tile_lastchg, tile_charbase, tile_chgcarry, seg_local, seg_charstart,
       ss, spst, spc, ps, tile_fn, tile_carry, tile_np, piece_start, piece_cnt, piece_off,
       tmp_ids, scan_part, lst[ML_COUNT], lrank, lpart, lnl, lnr, lbits, lsel, leqm, lmin, ldirty, wslow, wseg, wseg_at, total;
   uint64_t n_words;
@@ -40,6 +40,8 @@ WsLayout layout_for(uint64_t n, uint32_t n_seg) {
   };
   take(L.status, sizeof(Status));
   take(L.tile_nchar, 4 * (T + 1));
+  take(L.tile_err, 8 * (T + 1));
+  take(L.tile_bad, 4 * (T + 1));
   take(L.tile_lastchg, 4 * (T + 1));
   take(L.tile_charbase, 8 * (T + 1));
   take(L.tile_chgcarry, 8 * (T + 1));
@@ -169,6 +171,8 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
   a.n_tiles = L.n_tiles;
   a.ws.status = reinterpret_cast<Status *>(w + L.status);
   a.ws.tile_nchar = reinterpret_cast<uint32_t *>(w + L.tile_nchar);
+  a.ws.tile_err = reinterpret_cast<unsigned long long *>(w + L.tile_err);
+  a.ws.tile_bad = reinterpret_cast<uint32_t *>(w + L.tile_bad);
   a.ws.tile_lastchg = reinterpret_cast<int32_t *>(w + L.tile_lastchg);
   a.ws.tile_charbase = reinterpret_cast<unsigned long long *>(w + L.tile_charbase);
   a.ws.tile_chgcarry = reinterpret_cast<long long *>(w + L.tile_chgcarry);
@@ -204,8 +208,10 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
 
 // Steps up to the ordered list of piece starts.
 void launch_front(Launcher &go, const EncodeArgs &a, const WsLayout &L) {
-  go("k_init", k_init, dim3(1), dim3(64), a);
+  // (a non-empty text has its status initialised by k_scan_chars, from the
+  // per-tile results of k_count, which reads no status)
   if (a.n == 0) {
+    go("k_init", k_init, dim3(1), dim3(64), a);
     if (a.n_seg)
       go("k_check_offsets", k_check_offsets, dim3(std::min<uint32_t>(1024, (a.n_seg + 255) / 256)),
          dim3(256), a);

@@ -15,10 +15,11 @@ namespace bbpe {
 // Step 1: classify every byte, report the first invalid UTF-8 sequence, count
 // characters per tile, record the last whitespace/non-whitespace change of
 // each tile (for the 25,000-character run cuts) and where each segment starts
-// in character terms.  Also clears the span masks written by step 3.
+// in character terms.  Also clears the span masks written by step 3.  Runs
+// before the status block is initialised: its error and offset checks go to
+// per-tile slots, reduced by step 2.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(64) k_count(EncodeArgs a) {
-  if (a.ws.status->pad2) return;
   const int lane = threadIdx.x;
   const uint32_t t = blockIdx.x;
   const int64_t w = int64_t(t) * TILE_WORDS + lane - 1;
@@ -55,8 +56,16 @@ __global__ void __launch_bounds__(64) k_count(EncodeArgs a) {
   }
   if (lane == 0) a.ws.tile_lastchg[t] = last;
 
+  {
+    unsigned long long e = (owned && m.err < 64) ? (unsigned long long)(base + m.err) : ~0ull;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const unsigned long long o = __shfl_xor(e, d, 64);
+      e = o < e ? o : e;
+    }
+    if (lane == 0) a.ws.tile_err[t] = e;
+  }
   if (owned) {
-    if (m.err < 64) atomicMin(&a.ws.status->err_pos, (unsigned long long)(base + m.err));
     // segment starts inside this word: their local character index
     uint64_t sb = segb;
     if (sb) {
@@ -75,8 +84,11 @@ __global__ void __launch_bounds__(64) k_count(EncodeArgs a) {
   }
   // segment offsets must not decrease: every later kernel exits otherwise
   // (k_count itself only reads them to place bits and indexes, all bounded)
+  bool bad = false;
   for (uint32_t s = t * 64u + uint32_t(lane); s < a.n_seg; s += gridDim.x * 64u)
-    if (a.seg_off[s + 1] < a.seg_off[s]) a.ws.status->pad2 = 1u;
+    bad = bad || a.seg_off[s + 1] < a.seg_off[s];
+  const bool any_bad = __ballot(bad) != 0;
+  if (lane == 0) a.ws.tile_bad[t] = any_bad ? 1u : 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -84,15 +96,53 @@ __global__ void __launch_bounds__(64) k_count(EncodeArgs a) {
 // every segment start, and the last run change before every tile.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) k_scan_chars(EncodeArgs a) {
-  if (a.ws.status->pad2) return;
   __shared__ unsigned long long s_sum[33];
   __shared__ long long s_max[33];
   const uint32_t T = a.n_tiles;
   const uint32_t tid = threadIdx.x;
   const uint32_t per = (T + 1023) / 1024;
   const uint32_t t0 = tid * per, t1 = min(T, t0 + per);
-  unsigned long long sum = 0;
-  for (uint32_t t = t0; t < t1; ++t) sum += a.ws.tile_nchar[t];
+  unsigned long long sum = 0, err = ~0ull;
+  uint32_t bad = 0;
+  for (uint32_t t = t0; t < t1; ++t) {
+    sum += a.ws.tile_nchar[t];
+    err = min(err, a.ws.tile_err[t]);
+    bad |= a.ws.tile_bad[t];
+  }
+  // the status block: first invalid byte, offsets check, counters cleared
+  {
+    __shared__ unsigned long long s_err[16];
+    __shared__ uint32_t s_bad[16];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const unsigned long long o = __shfl_xor(err, d, 64);
+      err = o < err ? o : err;
+    }
+    const bool wbad = __ballot(bad != 0) != 0;
+    if ((tid & 63) == 0) {
+      s_err[tid / 64] = err;
+      s_bad[tid / 64] = wbad ? 1u : 0u;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long e = ~0ull;
+      uint32_t b = 0;
+      for (uint32_t q = 0; q < 16; ++q) {
+        e = min(e, s_err[q]);
+        b |= s_bad[q];
+      }
+      Status *s = a.ws.status;
+      s->err_pos = e;
+      s->n_pieces = 0;
+      s->n_ids = 0;
+      for (uint32_t k = 0; k < ML_COUNT; ++k) s->n_list[k] = 0;
+      s->err_seg = 0;
+      // offsets start at 0, end at the text length and never decrease;
+      // every later kernel exits when pad2 is set
+      const bool ok = b == 0 && a.seg_off[0] == 0 && a.seg_off[a.n_seg] == a.n;
+      s->pad2 = ok ? 0u : 1u;
+    }
+  }
   unsigned long long total;
   unsigned long long run =
       block_incl_scan<1024>(sum, 0ull, [](unsigned long long x, unsigned long long y) { return x + y; },

@@ -16,6 +16,8 @@ constexpr uint32_t SLOW_WORDS = 10;
 struct WsPtrs {
   Status *status;
   uint32_t *tile_nchar;             // [T] characters per tile
+  unsigned long long *tile_err;     // [T] first invalid UTF-8 byte of the tile, or ~0
+  uint32_t *tile_bad;               // [T] 1: a decreasing segment offset was seen
   int32_t *tile_lastchg;            // [T] tile-local index of the last run change, or -1
   unsigned long long *tile_charbase;  // [T] index of the tile's first character
   long long *tile_chgcarry;         // [T] last run change before the tile, or -1
