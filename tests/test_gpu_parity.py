@@ -342,6 +342,27 @@ def test_unit_cuts_keys_across_characters(alphabet):
         assert_ids(tok, orc, segs, safe=False, what="unit cuts table %d" % ti)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_short_units_adversarial_tables(seed):
+    """Short units (2-32 bytes, one lane each) under random tables whose keys
+    overlap heavily ({a, b, c} strings of 2-5 bytes at random ranks): every
+    order of neighbouring merges, adjacent and apart, in the rounds that take
+    two merges at a time."""
+    import itertools
+    r = random.Random(500 + seed)
+    tab = dict(atoms_permuted(2))
+    keys = [bytes(k) for L in range(2, 6) for k in itertools.product(b"abc", repeat=L)]
+    r.shuffle(keys)
+    chosen = keys[:r.randint(10, 120)]
+    for k, rk in zip(chosen, r.sample(range(256, 2000), len(chosen))):
+        tab[k] = rk
+    tok, orc = make(tab)
+    segs = [(b" ".join(bytes(r.choice(b"abc") for _ in range(r.randint(2, 32)))
+                       for _ in range(3000)), False)]
+    say("short units, adversarial table %d" % seed)
+    assert_ids(tok, orc, segs, safe=False, what="short adversarial %d" % seed)
+
+
 def test_long_units_adversarial_tables():
     """Units over 512 bytes (the batched long tier) under random tables over
     {a, b}: keys of 2-6 bytes with random ranks, so that merges of equal rank
