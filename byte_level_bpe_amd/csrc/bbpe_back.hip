@@ -1140,37 +1140,39 @@ __global__ void __launch_bounds__(SCAN_BLOCK) k_scan_down(EncodeArgs a) {
   }
 }
 
-// ids in order: unit i's ids go to [piece_off[i], piece_off[i+1]).  A
-// thread copies the ids of its unit; units with many ids (long runs the
-// merge left unmerged) are copied by the whole block afterwards.
-constexpr uint32_t ASM_BLOCK = 256, ASM_SMALL = 16;
+// ids in order: unit i's ids go to [piece_off[i], piece_off[i+1]).  A block
+// takes ASM_BLOCK units and fills their output range in output order:
+// thread x writes ids o = base + x, base + x + ASM_BLOCK, ..., finding the
+// unit of o by a binary search over the block's unit offsets in LDS, so
+// that the writes are contiguous across lanes and the reads follow the
+// units' scratch slots.
+constexpr uint32_t ASM_BLOCK = 256;
 
 __global__ void __launch_bounds__(ASM_BLOCK) k_assemble(EncodeArgs a) {
   if (a.ws.status->pad2) return;
   const uint32_t P = uint32_t(a.ws.status->n_pieces);
   const uint32_t total = P ? a.ws.piece_off[P] : 0u;
-  __shared__ unsigned int s_nbig;
-  __shared__ uint32_t s_big[ASM_BLOCK];
+  __shared__ uint32_t s_off[ASM_BLOCK + 1], s_start[ASM_BLOCK];
   const bool fits = total <= a.ids_cap;
-  for (uint32_t b = blockIdx.x * ASM_BLOCK; b < P; b += gridDim.x * ASM_BLOCK) {
-    if (threadIdx.x == 0) s_nbig = 0;
-    __syncthreads();
+  for (uint32_t b = blockIdx.x * ASM_BLOCK; b < P && fits; b += gridDim.x * ASM_BLOCK) {
+    const uint32_t nu = min(ASM_BLOCK, P - b);
     const uint32_t i = b + threadIdx.x;
-    if (i < P && fits) {
-      const uint32_t o = a.ws.piece_off[i], e = a.ws.piece_off[i + 1];
-      const uint32_t s = a.ws.piece_start[i];
-      if (e - o <= ASM_SMALL) {
-        for (uint32_t j = 0; j < e - o; ++j) a.ids[o + j] = a.ws.tmp_ids[s + j];
-      } else {
-        s_big[atomicAdd(&s_nbig, 1u)] = i;
-      }
+    if (threadIdx.x < nu) {
+      s_off[threadIdx.x] = a.ws.piece_off[i];
+      s_start[threadIdx.x] = a.ws.piece_start[i];
     }
+    if (threadIdx.x == 0) s_off[nu] = a.ws.piece_off[b + nu];
     __syncthreads();
-    for (uint32_t k = 0; k < s_nbig; ++k) {
-      const uint32_t u = s_big[k];
-      const uint32_t o = a.ws.piece_off[u], e = a.ws.piece_off[u + 1];
-      const uint32_t s = a.ws.piece_start[u];
-      for (uint32_t j = threadIdx.x; j < e - o; j += ASM_BLOCK) a.ids[o + j] = a.ws.tmp_ids[s + j];
+    const uint32_t o0 = s_off[0], o1 = s_off[nu];
+    for (uint32_t o = o0 + threadIdx.x; o < o1; o += ASM_BLOCK) {
+      // last unit u with s_off[u] <= o
+      uint32_t lo = 0, hi = nu;
+      while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (s_off[mid] <= o) lo = mid;
+        else hi = mid;
+      }
+      a.ids[o] = a.ws.tmp_ids[s_start[lo] + (o - s_off[lo])];
     }
     __syncthreads();
   }
