@@ -346,24 +346,31 @@ __device__ __forceinline__ void split_word(const EncodeArgs &a, int64_t w, const
     // the automaton over the word from every entry state; once all entry
     // states agree (after a space, a digit, a span start, ...) one state is
     // enough
+    // (characters only, not every byte; and a kind whose step left the
+    // function unchanged is skipped until the function changes again: runs
+    // of letters and marks settle after a character or two)
     uint64_t f = FLET_ID;
     bool konst = false;
     uint32_t cst = 0;
-    for (int i = 0; i < 64; ++i) {
-      if (!((o.todo >> i) & 1)) continue;
+    uint32_t settled = 0;  // kinds whose step is known to leave f unchanged
+    for (uint64_t todo = o.todo; todo; todo &= todo - 1) {
+      const int i = __ffsll(static_cast<unsigned long long>(todo)) - 1;
       const uint32_t k = uint32_t((o.K0 >> i) & 1) | (uint32_t((o.K1 >> i) & 1) << 1) |
                          (uint32_t((o.K2 >> i) & 1) << 2) | (uint32_t((o.K3 >> i) & 1) << 3);
-      uint64_t t;
-      uint32_t sm;
-      let_kind(k, t, sm);
       if ((SS >> i) & 1) {
         konst = true;
         cst = S_F;
       }
+      if (!konst && ((settled >> k) & 1)) continue;
+      uint64_t t;
+      uint32_t sm;
+      let_kind(k, t, sm);
       if (konst) {
         cst = flet_apply(t, cst);
       } else {
-        f = flet_then(f, t);
+        const uint64_t g = flet_then(f, t);
+        settled = g == f ? (settled | (1u << k)) : 0u;
+        f = g;
         if ((f & 15u) * FLET_ONES == f) {
           konst = true;
           cst = uint32_t(f & 15u);
@@ -413,8 +420,8 @@ __device__ __forceinline__ uint64_t split_finish(const SplitWord &o, uint64_t pC
   } else {
     uint32_t st = xs;
     uint64_t LS = 0, PQ = 0, F1m = 0;
-    for (int i = 0; i < 64; ++i) {
-      if (!((o.todo >> i) & 1)) continue;
+    for (uint64_t todo = o.todo; todo; todo &= todo - 1) {
+      const int i = __ffsll(static_cast<unsigned long long>(todo)) - 1;
       const uint64_t b = bit(i);
       if (o.SS & b) st = S_F;
       const uint32_t k = uint32_t((o.K0 >> i) & 1) | (uint32_t((o.K1 >> i) & 1) << 1) |
