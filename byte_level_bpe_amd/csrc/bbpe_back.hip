@@ -63,7 +63,21 @@ __global__ void __launch_bounds__(64) k_pieces(EncodeArgs a) {
   uint64_t ps = owned ? a.ws.ps[w] : 0;
   const uint32_t c = uint32_t(__popcll(ps));
   const uint32_t incl = wave_incl_sum(c, lane);
-  uint32_t idx = a.ws.tile_np[t] + incl - c;
+  uint32_t tbase;
+  if (a.n_tiles <= FUSE_TILES) {
+    // units of the tiles before this one (their counts, unscanned)
+    uint32_t acc = 0;
+    for (uint32_t q = uint32_t(lane); q < t; q += 64) acc += a.ws.tile_np[q];
+    tbase = wave_sum(acc);
+    if (t + 1 == a.n_tiles && lane == 63) {
+      const uint32_t total = tbase + incl;
+      a.ws.status->n_pieces = total;
+      a.ws.piece_start[total] = uint32_t(a.n);
+    }
+  } else {
+    tbase = a.ws.tile_np[t];
+  }
+  uint32_t idx = tbase + incl - c;
   const uint32_t base = uint32_t(w * 64);
   while (ps) {
     const int i = __ffsll(static_cast<unsigned long long>(ps)) - 1;

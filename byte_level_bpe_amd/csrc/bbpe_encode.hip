@@ -223,14 +223,14 @@ void launch_front(Launcher &go, const EncodeArgs &a, const WsLayout &L) {
   go("k_spans", k_spans, dim3(T), dim3(64), a);
   if (a.T.grammar == BBPE_GRAMMAR_O200K_STYLE) {
     go("k_split_agg_o200k", k_split_agg_o200k, dim3(T), dim3(64), a);
-    go("k_scan_split_o200k", k_scan_split_o200k, dim3(1), dim3(1024), a);
+    if (T > FUSE_TILES) go("k_scan_split_o200k", k_scan_split_o200k, dim3(1), dim3(1024), a);
     go("k_split_o200k", k_split_o200k, dim3(T), dim3(64), a);
   } else {
     go("k_split_agg", k_split_agg, dim3(T), dim3(64), a);
-    go("k_scan_split", k_scan_split, dim3(1), dim3(1024), a);
+    if (T > FUSE_TILES) go("k_scan_split", k_scan_split, dim3(1), dim3(1024), a);
     go("k_split", k_split, dim3(T), dim3(64), a);
   }
-  go("k_scan_tiles_np", k_scan_tiles_np, dim3(1), dim3(1024), a);
+  if (T > FUSE_TILES) go("k_scan_tiles_np", k_scan_tiles_np, dim3(1), dim3(1024), a);
   go("k_pieces", k_pieces, dim3(T), dim3(64), a);
 }
 

@@ -52,6 +52,10 @@ struct WsPtrs {
 
 // threads per k_probe block (units per block and pass)
 constexpr uint32_t PROBE_BLOCK = 512;
+// Texts of at most FUSE_TILES tiles skip the one-workgroup tile scans of the
+// split functions and of the unit counts: every block of k_split / k_pieces
+// folds the tiles before (and, for the lookahead, after) it itself.
+constexpr uint32_t FUSE_TILES = 2048;
 
 struct EncodeArgs {
   DevTables T;

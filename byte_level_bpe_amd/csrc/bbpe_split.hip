@@ -540,6 +540,31 @@ __device__ __forceinline__ void scan_split_body(const EncodeArgs &a) {
 __global__ void __launch_bounds__(1024) k_scan_split(EncodeArgs a) { scan_split_body<0>(a); }
 __global__ void __launch_bounds__(1024) k_scan_split_o200k(EncodeArgs a) { scan_split_body<1>(a); }
 
+// The state entering tile t, folded from the tile functions directly (for
+// texts of at most FUSE_TILES tiles, in place of the tile scan): the
+// left-to-right parts over tiles [0, t) from the text start (outside any
+// digit run, no CR run / state F), the lookahead over tiles (t, T) from past
+// the text end (a break).  Lane l folds a contiguous run of tiles; the runs
+// compose in lane order by wave shuffles.  Must be called by all 64 lanes.
+template <int G>
+__device__ __forceinline__ uint32_t carry_direct(const EncodeArgs &a, uint32_t t, int lane) {
+  const uint32_t T = a.n_tiles;
+  const uint32_t per_l = (t + 63) / 64, per_r = (T - 1 - t + 63) / 64;
+  uint64_t f = ltr_id<G>();
+  const uint32_t l0 = min(t, uint32_t(lane) * per_l), l1 = min(t, l0 + per_l);
+  for (uint32_t q = l0; q < l1; ++q) f = ltr_then<G>(f, a.ws.tile_fn[q] & ~uint64_t(0x300));
+  uint32_t gv = FV_ID;
+  const uint32_t r0 = min(T, t + 1 + uint32_t(lane) * per_r), r1 = min(T, r0 + per_r);
+  for (uint32_t q = r1; q > r0; --q) gv = fv_then(gv, uint32_t(a.ws.tile_fn[q - 1] >> 8) & 3u);
+  wave_scan_fns<G>(f, gv, lane);
+  const uint64_t all_f = __shfl(static_cast<unsigned long long>(f), 63, 64);
+  const uint32_t all_g = __shfl(gv, 0, 64);
+  const uint32_t dig = fdig_apply(uint32_t(all_f & 0xFFu), 3u);
+  const uint32_t x = ltr_apply_x<G>(all_f, 0u);
+  const uint32_t v = fv_apply(all_g, 0u);
+  return dig | (x << 8) | (v << 16);
+}
+
 // Step 6: piece-start bits of every word and the number of pieces per tile.
 template <int G>
 __device__ __forceinline__ void split_body(const EncodeArgs &a) {
@@ -563,7 +588,7 @@ __device__ __forceinline__ void split_body(const EncodeArgs &a) {
   uint32_t exv = __shfl_down(fv, 1, 64);
   if (lane == 0) exl = ltr_id<G>();
   if (lane == 63) exv = FV_ID;
-  const uint32_t carry = a.ws.tile_carry[t];
+  const uint32_t carry = a.n_tiles <= FUSE_TILES ? carry_direct<G>(a, t, lane) : a.ws.tile_carry[t];
   const uint32_t ph = fdig_apply(uint32_t(exl & 0xFFu), carry & 0xFFu);
   const uint32_t xs = ltr_apply_x<G>(exl, (carry >> 8) & 0xFFu);
   const uint32_t v = fv_apply(exv, (carry >> 16) & 1u);

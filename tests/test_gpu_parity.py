@@ -363,6 +363,22 @@ def test_short_units_adversarial_tables(seed):
     assert_ids(tok, orc, segs, safe=False, what="short adversarial %d" % seed)
 
 
+@pytest.mark.parametrize("extra", [0, 1])
+def test_tile_scans_folded_and_not(extra):
+    """Texts of exactly 2,048 tiles (the split and unit-count scans folded
+    into the per-tile kernels) and one byte more (the one-workgroup scans)."""
+    from synth import configs
+    w = configs.main()
+    tok, orc = make(w.tokens, w.specials, w.grammar)
+    base = w.segments[0][0]
+    n = 2048 * 62 * 64 + extra
+    text = (base * (n // len(base) + 1))[:n]
+    while (text[-1] & 0xC0) == 0x80 or text[-1] >= 0xC0:  # end on a whole character
+        text = text[:-1] + b"x"
+    say("tile scans, %d bytes" % len(text))
+    assert_ids(tok, orc, [(text, False)], what="tiles %d" % len(text))
+
+
 def test_long_units_adversarial_tables():
     """Units over 512 bytes (the batched long tier) under random tables over
     {a, b}: keys of 2-6 bytes with random ranks, so that merges of equal rank
