@@ -1178,13 +1178,17 @@ __global__ void __launch_bounds__(ASM_BLOCK) k_assemble(EncodeArgs a) {
     if (threadIdx.x == 0) s_off[nu] = a.ws.piece_off[b + nu];
     __syncthreads();
     const uint32_t o0 = s_off[0], o1 = s_off[nu];
+    uint32_t lo = 0, lo_end = 0;  // the unit of the thread's last id and its end
     for (uint32_t o = o0 + threadIdx.x; o < o1; o += ASM_BLOCK) {
-      // last unit u with s_off[u] <= o
-      uint32_t lo = 0, hi = nu;
-      while (hi - lo > 1) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (s_off[mid] <= o) lo = mid;
-        else hi = mid;
+      if (o >= lo_end) {
+        // last unit u with s_off[u] <= o (units after the previous one)
+        uint32_t hi = nu;
+        while (hi - lo > 1) {
+          const uint32_t mid = (lo + hi) >> 1;
+          if (s_off[mid] <= o) lo = mid;
+          else hi = mid;
+        }
+        lo_end = s_off[lo + 1];
       }
       a.ids[o] = a.ws.tmp_ids[s_start[lo] + (o - s_off[lo])];
     }
