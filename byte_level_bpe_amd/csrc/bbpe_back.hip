@@ -653,14 +653,15 @@ __device__ void merge_group(const EncodeArgs &a, const uint32_t *list, uint32_t 
 
 // ---------------------------------------------------------------------------
 // Long tier: one workgroup per unit longer than WAVE_MAX.  Per position j of
-// the unit (text byte s + j), in global memory: lrank = rank of the pair that
-// starts with the part starting at j, lpart = id of that part.  Per
-// 64-position block b of the unit: part starts, pairs chosen this round,
-// the part starts whose pair has the block's least rank, that least rank,
-// least rank stale; in LDS for units of up to
-// 64 * LONG_LDS_BLOCKS bytes, else in global memory at index (s >> 5) + b (a
-// unit of m > 64 bytes needs ceil(m/64) <= floor(m/32) entries, so units
-// never share one): lbits, lsel, leqm, lmin, ldirty.
+// the unit (text byte s + j): lrank = rank of the pair that starts with the
+// part starting at j, in global memory; lpart = id of that part, in LDS for
+// units of up to LONG_LDS_POS bytes, else in global memory.  Per 64-position
+// block b of the unit: part starts, pairs chosen this round, the part starts
+// whose pair has the block's least rank, that least rank, least rank stale;
+// in LDS for units of up to 64 * LONG_LDS_BLOCKS bytes, else in global
+// memory at index (s >> 5) + b (a unit of m > 64 bytes needs ceil(m/64) <=
+// floor(m/32) entries, so units never share one): lbits, lsel, leqm, lmin,
+// ldirty.  (gfx950 gives one workgroup up to 160 KB of LDS.)
 //
 // Each round takes the least rank R and merges in one batch the leftmost
 // non-overlapping pairs of rank R: in every run of consecutive parts whose
@@ -681,8 +682,9 @@ struct LongUnit {
   unsigned long long *bits, *sel, *eqm;
   int32_t *mn;
   uint32_t *dirty;
+  int32_t *pt;  // part ids, position 0 of the unit
   __device__ __forceinline__ int32_t &rank(uint32_t j) const { return a.ws.lrank[s + j]; }
-  __device__ __forceinline__ int32_t &part(uint32_t j) const { return a.ws.lpart[s + j]; }
+  __device__ __forceinline__ int32_t &part(uint32_t j) const { return pt[j]; }
   // first part start >= x, or m
   __device__ __forceinline__ uint32_t next(uint32_t x) const {
     if (x >= m) return m;
@@ -873,11 +875,12 @@ __device__ __forceinline__ uint32_t block_excl_sum(uint32_t v, uint32_t *sh, uin
 // One workgroup per unit.  Blocks of 64 positions are owned by threads for
 // the scans; the chosen pairs of a round are handled per quarter block (16
 // positions), so that up to 4 * blocks threads merge side by side.
-constexpr uint32_t LONG_LDS_BLOCKS = 2048;
+constexpr uint32_t LONG_LDS_BLOCKS = 512, LONG_LDS_POS = 25600;
 struct LongLds {
   unsigned long long bits[LONG_LDS_BLOCKS], sel[LONG_LDS_BLOCKS], eqm[LONG_LDS_BLOCKS];
   int32_t mn[LONG_LDS_BLOCKS];
   uint32_t dirty[LONG_LDS_BLOCKS];
+  int32_t part[LONG_LDS_POS];
 };
 
 __device__ void merge_long(const EncodeArgs &a, uint32_t i, uint32_t *sh, LongLds &ld) {
@@ -891,7 +894,7 @@ __device__ void merge_long(const EncodeArgs &a, uint32_t i, uint32_t *sh, LongLd
   const bool in_lds = nbk <= LONG_LDS_BLOCKS;
   LongUnit U{a, s, m, nbk, in_lds ? ld.bits : a.ws.lbits + base, in_lds ? ld.sel : a.ws.lsel + base,
              in_lds ? ld.eqm : a.ws.leqm + base, in_lds ? ld.mn : a.ws.lmin + base,
-             in_lds ? ld.dirty : a.ws.ldirty + base};
+             in_lds ? ld.dirty : a.ws.ldirty + base, m <= LONG_LDS_POS ? ld.part : a.ws.lpart + s};
   const uint32_t nb = U.nb;
   // initial pair ranks and atoms, eight positions per thread with their
   // loads issued before the stores

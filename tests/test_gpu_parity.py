@@ -420,7 +420,7 @@ def test_long_runs_main_table():
             ("".join(r.choice("abcdeinorst") for _ in range(1500)).encode(), False),
             (("\t" * 900 + " " * 700 + "\n" * 600 + "z").encode(), False),
             ((" " * 60001).encode(), False), (("*" * 800 + "/" * 700).encode(), False),
-            # units beyond the long tier's LDS state (over 131,072 bytes) unchunked
+            # units beyond the long tier's LDS state (over 32,768 bytes) unchunked
             ((" " * 140001 + "y").encode(), False), (("ab" * 70001).encode(), False)]
     say("long runs, main table")
     assert_ids(tok, orc, segs, safe=False, what="runs unchunked")
