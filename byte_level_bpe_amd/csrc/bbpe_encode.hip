@@ -219,7 +219,7 @@ void launch_front(Launcher &go, const EncodeArgs &a, const WsLayout &L) {
   }
   const uint32_t T = L.n_tiles;
   go("k_count", k_count, dim3(T), dim3(64), a);
-  go("k_scan_chars", k_scan_chars, dim3(1), dim3(1024), a);
+  if (T > FUSE_TILES) go("k_scan_chars", k_scan_chars, dim3(1), dim3(1024), a);
   go("k_spans", k_spans, dim3(T), dim3(64), a);
   if (a.T.grammar == BBPE_GRAMMAR_O200K_STYLE) {
     go("k_split_agg_o200k", k_split_agg_o200k, dim3(T), dim3(64), a);

@@ -95,6 +95,23 @@ __global__ void __launch_bounds__(64) k_count(EncodeArgs a) {
 // Step 2 (one workgroup): character base of every tile, character index of
 // every segment start, and the last run change before every tile.
 // ---------------------------------------------------------------------------
+// The status block of a non-empty text (first invalid byte, offsets check,
+// counters cleared); one thread.
+__device__ __forceinline__ void init_status(const EncodeArgs &a, unsigned long long err, bool bad,
+                                            unsigned long long n_chars) {
+  Status *s = a.ws.status;
+  s->err_pos = err;
+  s->n_pieces = 0;
+  s->n_ids = 0;
+  for (uint32_t k = 0; k < ML_COUNT; ++k) s->n_list[k] = 0;
+  s->err_seg = 0;
+  s->n_chars = n_chars;
+  // offsets start at 0, end at the text length and never decrease; every
+  // later kernel exits when pad2 is set
+  const bool ok = !bad && a.seg_off[0] == 0 && a.seg_off[a.n_seg] == a.n;
+  s->pad2 = ok ? 0u : 1u;
+}
+
 __global__ void __launch_bounds__(1024) k_scan_chars(EncodeArgs a) {
   __shared__ unsigned long long s_sum[33];
   __shared__ long long s_max[33];
@@ -131,16 +148,7 @@ __global__ void __launch_bounds__(1024) k_scan_chars(EncodeArgs a) {
         e = min(e, s_err[q]);
         b |= s_bad[q];
       }
-      Status *s = a.ws.status;
-      s->err_pos = e;
-      s->n_pieces = 0;
-      s->n_ids = 0;
-      for (uint32_t k = 0; k < ML_COUNT; ++k) s->n_list[k] = 0;
-      s->err_seg = 0;
-      // offsets start at 0, end at the text length and never decrease;
-      // every later kernel exits when pad2 is set
-      const bool ok = b == 0 && a.seg_off[0] == 0 && a.seg_off[a.n_seg] == a.n;
-      s->pad2 = ok ? 0u : 1u;
+      init_status(a, e, b != 0, 0);
     }
   }
   unsigned long long total;
@@ -206,10 +214,75 @@ __device__ __forceinline__ bool special_at(const EncodeArgs &a, uint64_t p, uint
   return false;
 }
 
+__device__ __forceinline__ unsigned long long wave_incl_sum64(unsigned long long v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const unsigned long long o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
 __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
-  if (a.ws.status->pad2) return;
   const int lane = threadIdx.x;
   const uint32_t t = blockIdx.x;
+  const uint32_t T = a.n_tiles;
+  // the character base of this tile, the last run change before it, and
+  // (folded) the character base at the start of each tile before it: from
+  // step 2's outputs, or, for texts of at most FUSE_TILES tiles, folded here
+  // from step 1's per-tile counts (lane l a contiguous run of tiles)
+  const bool fold = T <= FUSE_TILES;
+  uint64_t tile_base;
+  int64_t chg_carry;
+  unsigned long long run_excl = 0;  // (fold) characters before lane's first tile
+  uint32_t per = 0;
+  if (fold) {
+    per = (t + 63) / 64;
+    const uint32_t q0 = min(t, uint32_t(lane) * per), q1 = min(t, q0 + per);
+    unsigned long long sum = 0;
+    for (uint32_t q = q0; q < q1; ++q) sum += a.ws.tile_nchar[q];
+    const unsigned long long incl_s = wave_incl_sum64(sum, lane);
+    run_excl = incl_s - sum;
+    unsigned long long run = run_excl;
+    long long mx = -1;
+    for (uint32_t q = q0; q < q1; ++q) {
+      const int32_t lc = a.ws.tile_lastchg[q];
+      if (lc >= 0) mx = max(mx, (long long)(run + uint32_t(lc)));
+      run += a.ws.tile_nchar[q];
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const long long o = __shfl_xor(mx, d, 64);
+      mx = o > mx ? o : mx;
+    }
+    tile_base = __shfl(incl_s, 63, 64);
+    chg_carry = mx;
+    // the offsets check over every tile; block 0 also writes the status
+    uint32_t bad = 0;
+    unsigned long long err = ~0ull, nch = 0;
+    for (uint32_t q = uint32_t(lane); q < T; q += 64) {
+      bad |= a.ws.tile_bad[q];
+      if (t == 0) {
+        err = min(err, a.ws.tile_err[q]);
+        nch += a.ws.tile_nchar[q];
+      }
+    }
+    const bool any_bad = __ballot(bad != 0) != 0;
+    if (t == 0) {
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) {
+        const unsigned long long o = __shfl_xor(err, d, 64);
+        err = o < err ? o : err;
+        nch += __shfl_xor(nch, d, 64);
+      }
+      if (lane == 0) init_status(a, err, any_bad, nch);
+    }
+    if (any_bad || a.seg_off[0] != 0 || a.seg_off[a.n_seg] != a.n) return;
+  } else {
+    if (a.ws.status->pad2) return;
+    tile_base = a.ws.tile_charbase[t];
+    chg_carry = a.ws.tile_chgcarry[t];
+  }
   const int64_t w = int64_t(t) * TILE_WORDS + lane - 1;
   const int64_t base = w * 64;
   const bool owned = lane >= 1 && lane <= int(TILE_WORDS) && w < int64_t(a.n_words);
@@ -228,7 +301,6 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
   // before it (lanes 1..63 are contiguous with the tile's character base)
   const uint32_t nch = (lane >= 1) ? uint32_t(__popcll(m.lead)) : 0u;
   const uint32_t incl = wave_incl_sum(nch, lane);
-  const uint64_t tile_base = a.ws.tile_charbase[t];
   const uint64_t c0 = tile_base + (incl - nch);
   int64_t lastchg = -1;
   if (lane >= 1 && chg) {
@@ -238,13 +310,31 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
   const int64_t incl_chg = wave_incl_max(lastchg, lane);
   int64_t chg_before = __shfl_up(static_cast<long long>(incl_chg), 1, 64);
   if (lane <= 1) chg_before = -1;
-  chg_before = max(chg_before, (int64_t)a.ws.tile_chgcarry[t]);
+  chg_before = max(chg_before, chg_carry);
+  // (fold) character index of the start of this lane's segment, for the
+  // lanes that place window cuts: its tile's base plus its index there
+  uint64_t segcs_fold = 0;
+  if (fold) {
+    const uint32_t s = seg_at;
+    const uint64_t o = a.seg_off[s];
+    const uint32_t tq = o < a.n ? uint32_t((o >> 6) / TILE_WORDS) : t;
+    const uint32_t owner = per ? min(63u, tq / per) : 0u;
+    const unsigned long long ex = __shfl(run_excl, int(owner), 64);
+    if (tq >= t) {
+      segcs_fold = tile_base;
+    } else {
+      unsigned long long b = ex;
+      for (uint32_t q = owner * per; q < tq; ++q) b += a.ws.tile_nchar[q];
+      segcs_fold = b;
+    }
+    segcs_fold += (o < a.n) ? a.ws.seg_local[s] : 0u;
+  }
 
   uint64_t cut = 0;
   if (live && (a.flags & BBPE_TIKTOKEN_SAFE) && m.valid) {
     // state at the first character of the word
     uint32_t s = seg_at;
-    uint64_t segcs = a.ws.seg_charstart[s];
+    uint64_t segcs = fold ? segcs_fold : a.ws.seg_charstart[s];
     uint64_t c = c0;
     uint64_t nw, rs, nr;
     {
