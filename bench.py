@@ -273,12 +273,41 @@ def main():
     mbs = total * args.steps / wall / 1e6
     tps = n_ids * args.steps / wall
 
+    # context, outside the timed region: (1) the PCIe-inclusive rate, text
+    # copied in from pinned host memory and ids copied back per call; (2) a
+    # plain device-to-device copy of 256 MiB, the bandwidth one kernel can
+    # actually move on this machine
+    host_text = torch.empty(text.numel(), dtype=torch.uint8, pin_memory=True)
+    host_text.copy_(text)
+    host_ids = torch.empty(max(1, n_ids), dtype=torch.int32, pin_memory=True)
+    e2e_steps = min(args.steps, 10)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(e2e_steps):
+        text.copy_(host_text, non_blocking=True)
+        step()
+        host_ids[:n_ids].copy_(ids[:n_ids], non_blocking=True)
+        torch.cuda.synchronize()
+    e2e_ms = (time.perf_counter() - t0) * 1e3 / e2e_steps
+    cp_src = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    cp_dst.copy_(cp_src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        cp_dst.copy_(cp_src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * 5 * cp_src.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del cp_src, cp_dst
+
     # algorithmic bytes of the whole call and per kernel, counted once by the
     # oracle and stored (oracle/alg_bytes.py)
     with open(ALG_BYTES) as f:
         alg = json.load(f)[args.workload]
     assert alg["ids"] == n_ids and alg["bytes"] == total, "workload differs from the counted one"
     b_alg = alg["call_bytes"]
+    floor_bytes = total + 4 * n_ids + 8 * (n_seg + 1) + tok.table_bytes
     per_kernel = {k: v[0] / max(1, v[1]) for k, v in rep.items()}
     dom = max(rep, key=lambda k: rep[k][0])
     dom_ms = per_kernel[dom]
@@ -304,7 +333,15 @@ def main():
         "config": {"workload": WORKLOAD_DESC.get(args.workload, args.workload),
                    "bytes": total, "segments": n_seg, "ids": n_ids, "ranks": len(w.tokens)},
         "call_roofline": {"alg_bytes": b_alg, "frac_of_8TBs": round(b_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
-                          "pieces": alg["pieces"], "table_bytes": alg["lookup_bytes"]},
+                          "pieces": alg["pieces"], "table_bytes": alg["lookup_bytes"],
+                          # compulsory bytes only: text in, ids and offsets out, the table read once
+                          "floor_bytes": floor_bytes,
+                          "floor_frac_of_8TBs": round(floor_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+                          "copy_GBs": round(copy_gbs, 1),
+                          "alg_frac_of_copy": round(b_alg / (ms_per_step * 1e-3) / 1e9 / copy_gbs, 5)},
+        "pcie_inclusive": {"ms_per_step": round(e2e_ms, 4), "MBs": round(total / (e2e_ms * 1e-3) / 1e6, 2),
+                           "steps": e2e_steps,
+                           "what": "text host-to-device from pinned memory, encode, ids device-to-host"},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
                      "traffic": measured_traffic(args.workload, dom), "avg_ms": round(dom_ms, 5),
