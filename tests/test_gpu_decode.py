@@ -278,3 +278,22 @@ def test_token_offsets_bad_id(tiny):
     with pytest.raises(B.BBPEError) as e:
         tok.token_offsets_device(dev_ids(ids))
     assert e.value.status == B.E_BAD_ID and "index 100:" in str(e.value)
+
+
+def test_count_only_with_specials_and_empty_segments(tiny):
+    """Count-only over typed segments: specials allowed and not, empty
+    segments, a special at the very end, a 64-byte run of one character."""
+    w, _, _ = tiny
+    specials = [(b"<|endoftext|>", len(w.tokens) + 7), (b"<|fim_middle|>", len(w.tokens) + 9)]
+    tok = B.load_ranks(w.tokens, specials, w.grammar)
+    orc = Oracle(w.tokens, specials, w.grammar)
+    sp = specials[0][0]
+    segs = [(b"", True), (b"a" + sp + b"b", True), (sp, False), (b"", False),
+            (b"x" * 64, False), (b"hello " + sp, True), (sp + sp, True), (b"", True)]
+    say("count only, typed segments")
+    counts = tok.count_segments(segs).cpu().numpy()
+    _, ooff = orc.encode_segments(segs)
+    assert np.array_equal(counts, np.diff(ooff))
+    ids, _ = tok.encode_segments(segs)
+    out, off, done = tok.decode_device(ids, offsets=True)
+    assert out.cpu().numpy().tobytes() == b"".join(s for s, _ in segs)

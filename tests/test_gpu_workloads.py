@@ -61,3 +61,37 @@ def test_workload_parity(name):
     off2, total = tok.token_offsets_device(torch.from_numpy(ids).cuda())
     assert total == len(text) and np.array_equal(off2.cpu().numpy(), ref_off)
 
+
+
+@pytest.mark.parametrize("grammar", [1, 2], ids=["o200k_style", "r50k_style"])
+def test_main_text_other_grammars(grammar):
+    """The main workload's text and table under the o200k-style and the
+    r50k-style split (one 4.2 MB segment, tiktoken-safe): every id and the
+    round trip."""
+    w = configs.main()
+    tok = B.load_ranks(w.tokens, w.specials, grammar)
+    orc = Oracle(w.tokens, w.specials, grammar)
+    say("main text, grammar", grammar)
+    ids, id_off = tok.encode_segments(w.segments, True)
+    ids = ids.cpu().numpy()
+    oids, ooff = orc.encode_segments(w.segments, True)
+    if not np.array_equal(ids, oids):
+        n = min(len(ids), len(oids))
+        d = np.nonzero(ids[:n] != oids[:n])[0]
+        k = int(d[0]) if len(d) else n
+        raise AssertionError("grammar %d: %d vs %d ids, first difference at %d" % (grammar, len(ids), len(oids), k))
+    assert np.array_equal(id_off.cpu().numpy(), ooff)
+    assert tok.decode(ids) == b"".join(s for s, _ in w.segments)
+
+
+def test_main_text_unchunked():
+    """The main workload without tiktoken-safe chunking (no window or run
+    cuts: pieces may be longer)."""
+    w = configs.main()
+    tok = B.load_ranks(w.tokens, w.specials, w.grammar)
+    orc = Oracle(w.tokens, w.specials, w.grammar)
+    say("main text, unchunked")
+    ids, id_off = tok.encode_segments(w.segments, False)
+    oids, ooff = orc.encode_segments(w.segments, False)
+    assert np.array_equal(ids.cpu().numpy(), oids)
+    assert np.array_equal(id_off.cpu().numpy(), ooff)
