@@ -389,16 +389,17 @@ __device__ __forceinline__ int32_t probe_from(const DevTables &T, uint32_t idx, 
 
 // Every unit: specials, single bytes and units that are keys whose own
 // merges rebuild them get their id here; the rest are listed for the merge
-// kernels by length class.  Each thread takes PROBE_U units and issues the
+// kernels by length class.  Each thread takes PROBE_U (4) units and issues the
 // loads of all of them (offsets, then bytes and special bits, then the
 // first hash slot) before it resolves any, so that one wave keeps several
 // units' memory chains in flight.  Each block gathers its list entries in
 // LDS (one array, grouped by class) and reserves room in the global lists
 // with one atomic per class.
-constexpr uint32_t PROBE_U = 4;
-constexpr uint32_t PROBE_CHUNK = PROBE_BLOCK * PROBE_U;
-
-__global__ void __launch_bounds__(PROBE_BLOCK) k_probe(EncodeArgs a) {
+// (Texts under PROBE_SMALL bytes take one unit per thread instead: with few
+// units, the four serial resolutions of a thread are the kernel's length.)
+template <uint32_t PROBE_U>
+__device__ __forceinline__ void probe_body(const EncodeArgs &a) {
+  constexpr uint32_t PROBE_CHUNK = PROBE_BLOCK * PROBE_U;
   if (a.ws.status->pad2) return;
   Status *st = a.ws.status;
   const uint32_t P = uint32_t(st->n_pieces);
@@ -496,6 +497,8 @@ __global__ void __launch_bounds__(PROBE_BLOCK) k_probe(EncodeArgs a) {
     __syncthreads();
   }
 }
+__global__ void __launch_bounds__(PROBE_BLOCK) k_probe(EncodeArgs a) { probe_body<4>(a); }
+__global__ void __launch_bounds__(PROBE_BLOCK) k_probe1(EncodeArgs a) { probe_body<1>(a); }
 
 // ---------------------------------------------------------------------------
 // Group tier: units of 33..WAVE_MAX bytes, a group of G lanes per unit (64/G

@@ -313,8 +313,13 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
   if (n == 0) {
     go("k_zero_offsets", k_zero_offsets, dim3(seg_grid), dim3(256), a);
   } else {
-    const uint32_t probe_grid = uint32_t(std::min<uint64_t>((n + 8191) / 8192, 8192));
-    go("k_probe", k_probe, dim3(probe_grid), dim3(PROBE_BLOCK), a);
+    if (n < PROBE_SMALL) {
+      const uint32_t probe_grid = uint32_t((n + 2047) / 2048);
+      go("k_probe", k_probe1, dim3(probe_grid), dim3(PROBE_BLOCK), a);
+    } else {
+      const uint32_t probe_grid = uint32_t(std::min<uint64_t>((n + 8191) / 8192, 8192));
+      go("k_probe", k_probe, dim3(probe_grid), dim3(PROBE_BLOCK), a);
+    }
     // the group and long tiers (few units, long dependent chains) run on the
     // second stream beside the short tier
     hipStream_t aux = static_cast<hipStream_t>(t->aux_stream);

@@ -56,6 +56,7 @@ constexpr uint32_t PROBE_BLOCK = 512;
 // split functions and of the unit counts: every block of k_split / k_pieces
 // folds the tiles before (and, for the lookahead, after) it itself.
 constexpr uint32_t FUSE_TILES = 2048;
+constexpr uint64_t PROBE_SMALL = 1u << 20;  // texts below this: one unit per probe thread
 
 struct EncodeArgs {
   DevTables T;
@@ -86,6 +87,7 @@ __global__ void k_split_o200k(EncodeArgs a);
 __global__ void k_scan_tiles_np(EncodeArgs a);
 __global__ void k_pieces(EncodeArgs a);
 __global__ void k_probe(EncodeArgs a);
+__global__ void k_probe1(EncodeArgs a);
 __global__ void k_merge(EncodeArgs a);
 __global__ void k_merge_long(EncodeArgs a);
 __global__ void k_merge_group(EncodeArgs a);
