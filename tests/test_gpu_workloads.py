@@ -95,3 +95,26 @@ def test_main_text_unchunked():
     oids, ooff = orc.encode_segments(w.segments, False)
     assert np.array_equal(ids.cpu().numpy(), oids)
     assert np.array_equal(id_off.cpu().numpy(), ooff)
+
+
+def test_one_gigabyte_call():
+    """One call over 1 GiB: the large workload's 64 MiB text as 16 segments.
+    Each segment is encoded as its own text, so every segment's ids equal
+    the oracle's ids of one 64 MiB text; decode restores all 1 GiB."""
+    w = configs.large()
+    text = w.segments[0][0]
+    tok = B.load_ranks(w.tokens, w.specials, w.grammar)
+    orc = Oracle(w.tokens, w.specials, w.grammar)
+    oids, _ = orc.encode_segments([(text, False)], True)
+    segs = [(text, False)] * 16
+    say("one call over %d bytes" % (16 * len(text)))
+    ids, id_off = tok.encode_segments(segs, True)
+    off = id_off.cpu().numpy()
+    assert np.array_equal(np.diff(off), np.full(16, len(oids)))
+    h = ids.cpu().numpy()
+    for k in range(16):
+        assert np.array_equal(h[off[k]:off[k + 1]], oids), "segment %d" % k
+    out, _, done = tok.decode_device(ids)
+    dev_text = torch.from_numpy(np.frombuffer(text, dtype=np.uint8).copy()).cuda()
+    o = out.view(16, len(text))
+    assert bool((o == dev_text.unsqueeze(0)).all()) and done == 16 * len(text)
