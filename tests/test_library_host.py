@@ -128,3 +128,46 @@ def test_encode_before_upload_is_rejected_without_gpu():
     st = lib.bbpe_encode_segments(tok._h, None, 0, None, None, 0, 1, None, 0, None, 0, None,
                                   ctypes.byref(n), None)
     assert st == B.E_INVALID_ARG
+
+
+def test_decode_entry_points_reject_without_gpu():
+    """Device decode and per-token offsets: argument checks and the
+    tables-not-uploaded state, all answered on the host."""
+    tok = B.load_ranks(atoms_permuted(0))
+    lib = B._load()
+    a = tok.decode_workspace_bytes(0)
+    b = tok.decode_workspace_bytes(1 << 20)
+    c = tok.decode_workspace_bytes(1 << 24)
+    assert 0 < a <= b < c and b % 256 == 0 and c % 256 == 0
+    n, done = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: the call returns first
+    # no output length pointer / ids missing / output missing with capacity
+    assert lib.bbpe_decode_device(tok._h, fake, 4, fake, 16, None, fake, 1 << 20, None, None,
+                                  None) == B.E_INVALID_ARG
+    assert lib.bbpe_decode_device(tok._h, None, 4, fake, 16, None, fake, 1 << 20, ctypes.byref(n),
+                                  None, None) == B.E_INVALID_ARG
+    assert lib.bbpe_decode_device(tok._h, fake, 4, None, 16, None, fake, 1 << 20, ctypes.byref(n),
+                                  None, None) == B.E_INVALID_ARG
+    # tables not uploaded
+    assert lib.bbpe_decode_device(tok._h, fake, 4, fake, 16, None, fake, 1 << 20, ctypes.byref(n),
+                                  ctypes.byref(done), None) == B.E_STATE
+    assert lib.bbpe_token_offsets_device(tok._h, fake, 4, None, fake, 1 << 20, ctypes.byref(n),
+                                         None) == B.E_INVALID_ARG
+    assert lib.bbpe_token_offsets_device(tok._h, fake, 4, fake, fake, 1 << 20, ctypes.byref(n),
+                                         None) == B.E_STATE
+
+
+def test_count_only_flag_rules_without_gpu():
+    """BBPE_COUNT_ONLY is a known encode flag (the call gets as far as the
+    missing tables) and pretokenize rejects it before anything else."""
+    tok = B.load_ranks(atoms_permuted(0))
+    lib = B._load()
+    n = ctypes.c_uint64(0)
+    buf = (ctypes.c_uint64 * 2)(0, 0)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    assert lib.bbpe_encode_segments(tok._h, None, 0, p, p, 1, B.COUNT_ONLY, None, 0, None, 0, p,
+                                    ctypes.byref(n), None) == B.E_STATE
+    assert lib.bbpe_encode_segments(tok._h, None, 0, p, p, 1, 1 << 5, None, 0, None, 0, p,
+                                    ctypes.byref(n), None) == B.E_INVALID_ARG
+    assert lib.bbpe_pretokenize_segments(tok._h, None, 0, p, p, 1, B.COUNT_ONLY, None, 0, None, 0,
+                                         None, ctypes.byref(n), None) == B.E_INVALID_ARG
