@@ -204,12 +204,31 @@ __global__ void __launch_bounds__(DEC_BLOCK) k_dec_copy(DecArgs a) {
       // to 16, plus j
       const uint32_t phase = uint32_t((reinterpret_cast<uintptr_t>(a.out) + base) & 15);
       uint32_t o = phase + mine;
+      // four tokens at a time: the first 8 bytes of each from three aligned
+      // dwords of the blob (padded, so the reads stay inside it), all twelve
+      // loads issued before any byte is stored; longer tokens copy the rest
 #pragma unroll
-      for (uint32_t k = 0; k < DEC_ITEMS; ++k) {
-        const uint32_t len = uint32_t(e[k] & 0xFFu);
-        const uint8_t *src = a.T.dblob + (e[k] >> 8);
-        for (uint32_t j = 0; j < len; ++j) stage[o + j] = src[j];
-        o += len;
+      for (uint32_t k0 = 0; k0 < DEC_ITEMS; k0 += 4) {
+        uint32_t wd[4][3];
+#pragma unroll
+        for (uint32_t c = 0; c < 4; ++c) {
+          const uint32_t *q = reinterpret_cast<const uint32_t *>(a.T.dblob + ((e[k0 + c] >> 8) & ~uint64_t(3)));
+          wd[c][0] = q[0];
+          wd[c][1] = q[1];
+          wd[c][2] = q[2];
+        }
+#pragma unroll
+        for (uint32_t c = 0; c < 4; ++c) {
+          const uint64_t ek = e[k0 + c];
+          const uint32_t len = uint32_t(ek & 0xFFu), sh = uint32_t((ek >> 8) & 3u);
+          const uint64_t v = uint64_t(__builtin_amdgcn_alignbyte(wd[c][1], wd[c][0], sh)) |
+                             (uint64_t(__builtin_amdgcn_alignbyte(wd[c][2], wd[c][1], sh)) << 32);
+          const uint32_t head = min(len, 8u);
+          for (uint32_t j = 0; j < head; ++j) stage[o + j] = uint8_t(v >> (8 * j));
+          const uint8_t *src = a.T.dblob + (ek >> 8);
+          for (uint32_t j = 8; j < len; ++j) stage[o + j] = src[j];
+          o += len;
+        }
       }
       __syncthreads();
       uint8_t *dst = a.out + base - phase;
