@@ -19,9 +19,13 @@
 namespace bbpe {
 namespace {
 
-constexpr uint32_t DEC_BLOCK = 256, DEC_ITEMS = 16, DEC_TILE = DEC_BLOCK * DEC_ITEMS;
+constexpr uint32_t DEC_BLOCK = 256, DEC_ITEMS = 8, DEC_TILE = DEC_BLOCK * DEC_ITEMS;
 // output bytes of one tile staged in LDS (more: written straight to HBM)
 constexpr uint32_t DEC_STAGE = 32768;
+// up to this many tiles, every tile sums the byte counts of the tiles before
+// it itself; beyond, a one-workgroup scan does it once (the per-tile sums
+// grow with the square of the tile count)
+constexpr uint32_t DEC_FOLD = 2048;
 
 struct DecStatus {
   unsigned long long first_bad;  // index of the first id that is neither rank nor special, or ~0
@@ -38,6 +42,7 @@ struct DecArgs {
   uint64_t cap;
   uint64_t *tok_off;
   uint32_t *part;              // [blocks] bytes of each tile of DEC_TILE tokens
+  unsigned long long *pre;     // [blocks] bytes before each tile (more than DEC_FOLD tiles)
   unsigned long long *bad;     // [blocks] first bad index of each tile, or ~0
   DecStatus *st;
   uint32_t vec_ids, vec_off;   // ids / tok_off 16-byte aligned: vector loads / stores
@@ -112,12 +117,50 @@ __global__ void __launch_bounds__(DEC_BLOCK) k_dec_len(DecArgs a) {
 // bytes: staged in LDS at the output's 16-byte phase and stored as aligned
 // 16-byte words.  The last tile also finds the end of the last complete
 // character from the last tokens' bytes.
+// (more than DEC_FOLD tiles, one workgroup) bytes before every tile, the
+// total and the first bad id, into pre[] and the status
+__global__ void __launch_bounds__(1024) k_dec_scan(DecArgs a, uint32_t nblk) {
+  __shared__ unsigned long long s_sum[2 * 16 + 1];
+  __shared__ unsigned long long s_bad[16];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t per = (nblk + 1023) / 1024;
+  const uint32_t q0 = min(nblk, tid * per), q1 = min(nblk, q0 + per);
+  unsigned long long sum = 0, bad = ~0ull;
+  for (uint32_t q = q0; q < q1; ++q) {
+    sum += a.part[q];
+    bad = min(bad, a.bad[q]);
+  }
+  unsigned long long total;
+  unsigned long long run = block_incl_scan<1024>(
+      sum, 0ull, [](unsigned long long x, unsigned long long y) { return x + y; }, s_sum, total) - sum;
+  for (uint32_t q = q0; q < q1; ++q) {
+    a.pre[q] = run;
+    run += a.part[q];
+  }
+  bad = wave_min64(bad);
+  if ((tid & 63) == 0) s_bad[tid / 64] = bad;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long b = ~0ull;
+    for (uint32_t w = 0; w < 16; ++w) b = min(b, s_bad[w]);
+    a.st->total = total;
+    a.st->first_bad = b;
+  }
+}
+
 __global__ void __launch_bounds__(DEC_BLOCK) k_dec_copy(DecArgs a) {
   __shared__ unsigned long long s_a[DEC_BLOCK / 64], s_b[DEC_BLOCK / 64], s_c[DEC_BLOCK / 64];
   __shared__ uint32_t s_scan[2 * (DEC_BLOCK / 64) + 1];
   __shared__ __align__(16) uint8_t stage[DEC_STAGE + 32];
   const uint32_t nblk = gridDim.x;
   const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x / 64;
+  uint64_t base = 0, total = 0;
+  unsigned long long first_bad = ~0ull;
+  if (nblk > DEC_FOLD) {
+    base = a.pre[blockIdx.x];
+    total = a.st->total;
+    first_bad = a.st->first_bad;
+  } else {
   // base, total and the first bad id over all tiles
   unsigned long long before = 0, every = 0, bad = ~0ull;
   for (uint32_t q = threadIdx.x; q < nblk; q += DEC_BLOCK) {
@@ -136,8 +179,6 @@ __global__ void __launch_bounds__(DEC_BLOCK) k_dec_copy(DecArgs a) {
     s_c[wv] = bad;
   }
   __syncthreads();
-  uint64_t base = 0, total = 0;
-  unsigned long long first_bad = ~0ull;
 #pragma unroll
   for (uint32_t q = 0; q < DEC_BLOCK / 64; ++q) {
     base += s_a[q];
@@ -147,6 +188,7 @@ __global__ void __launch_bounds__(DEC_BLOCK) k_dec_copy(DecArgs a) {
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     a.st->total = total;
     a.st->first_bad = first_bad;
+  }
   }
   if (first_bad != ~0ull) return;  // (uniform over the grid)
 
@@ -292,7 +334,7 @@ __global__ void __launch_bounds__(DEC_BLOCK) k_dec_copy(DecArgs a) {
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 struct DecLayout {
-  uint64_t status, part, bad, total;
+  uint64_t status, part, bad, pre, total;
 };
 DecLayout dec_layout(uint64_t n) {
   DecLayout L{};
@@ -301,6 +343,7 @@ DecLayout dec_layout(uint64_t n) {
   L.status = o; o = align256(o + sizeof(DecStatus));
   L.part = o; o = align256(o + 4 * nb);
   L.bad = o; o = align256(o + 8 * nb);
+  L.pre = o; o = align256(o + 8 * nb);
   L.total = o;
   return L;
 }
@@ -340,11 +383,13 @@ static int decode_run(bbpe_tokenizer *t, const int32_t *d_ids, uint64_t n_ids, u
   a.st = reinterpret_cast<DecStatus *>(w + L.status);
   a.part = reinterpret_cast<uint32_t *>(w + L.part);
   a.bad = reinterpret_cast<unsigned long long *>(w + L.bad);
+  a.pre = reinterpret_cast<unsigned long long *>(w + L.pre);
   a.vec_ids = (reinterpret_cast<uintptr_t>(d_ids) & 15) == 0;
   a.vec_off = (reinterpret_cast<uintptr_t>(d_tok_off) & 15) == 0;
   Launcher go{t, reinterpret_cast<hipStream_t>(stream)};
   const uint32_t nb = uint32_t((n_ids + DEC_TILE - 1) / DEC_TILE);
   go("k_dec_len", k_dec_len, dim3(nb), dim3(DEC_BLOCK), a);
+  if (nb > DEC_FOLD) go("k_dec_scan", k_dec_scan, dim3(1), dim3(1024), a, nb);
   go("k_dec_copy", k_dec_copy, dim3(nb), dim3(DEC_BLOCK), a);
   HIP_OK(hipGetLastError());
   HIP_OK(hipMemcpyAsync(&h, a.st, sizeof(DecStatus), hipMemcpyDeviceToHost, go.st));
