@@ -89,13 +89,43 @@ __device__ __forceinline__ uint32_t text_byte(const uint8_t *__restrict__ text, 
   return in ? v : 0u;
 }
 
+// The bytes of one wave's 64 windows, copied to LDS, and the first stage of
+// the class table for the Basic Multilingual Plane (code points >> 8 below
+// 256), so that the multi-byte decoder's byte reads and first-stage lookups
+// go to LDS instead of memory.
+struct SlowStage {
+  uint4 bytes[(64 * 64 + 32) / 16];  // text bytes [lo, lo + 4128), 0 outside the text
+  uint16_t u1[256];
+};
+
+// Fill the stage: every lane of the wave calls this with its own window (the
+// word at lane_base, lane = threadIdx.x < 64, consecutive lanes at
+// consecutive words).
+__device__ __forceinline__ void stage_fill(SlowStage &st, const DevTables &T, const Window &win, int lane) {
+  const uint2 u = reinterpret_cast<const uint2 *>(T.uni1)[lane];
+  reinterpret_cast<uint2 *>(st.u1)[lane] = u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    st.bytes[1 + 4 * lane + q] = uint4{win.w[4 + 4 * q], win.w[5 + 4 * q], win.w[6 + 4 * q], win.w[7 + 4 * q]};
+  if (lane == 0) st.bytes[0] = uint4{win.w[0], win.w[1], win.w[2], win.w[3]};
+  if (lane == 63) st.bytes[257] = uint4{win.w[20], win.w[21], win.w[22], win.w[23]};
+  __syncthreads();
+}
+
+// byte p of the text from the stage (p in [lo, lo + 4128); the windows hold 0
+// outside the text)
+__device__ __forceinline__ uint32_t stage_byte(const SlowStage &st, int64_t lo, int64_t p) {
+  return reinterpret_cast<const uint8_t *>(st.bytes)[p - lo];
+}
+
 // The multi-byte characters of the word at base: `hi2` marks its bytes >=
 // 0xC0, `non` its bytes >= 0x80.  Leads are decoded eight at a time with all
 // their byte loads, then all their class-table loads, issued together.
 __device__ __forceinline__ void classify_slow(const DevTables &T, const uint8_t *__restrict__ text,
                                               const Window &win, int64_t base, uint64_t n,
                                               uint64_t seg_lo, uint64_t seg_hi, uint64_t hi2,
-                                              uint64_t non, uint64_t valid, SlowMasks &r) {
+                                              uint64_t non, uint64_t valid, const SlowStage &st,
+                                              int64_t lo, SlowMasks &r) {
   r = SlowMasks{0, 0, 0, 0, 0, 0, 0, 0, 0, 64};
   uint64_t covered = 0;
   uint32_t err = 64;
@@ -129,7 +159,7 @@ __device__ __forceinline__ void classify_slow(const DevTables &T, const uint8_t 
       ii[k] = __ffsll(static_cast<unsigned long long>(leads)) - 1;  // -1 once none are left
       leads &= leads - 1;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[k][j] = text_byte(text, n, base + ii[k] + j);
+      for (int j = 0; j < 4; ++j) b[k][j] = stage_byte(st, lo, base + ii[k] + j);
     }
     uint32_t cp[K], blk[K];
     int len[K];
@@ -152,11 +182,21 @@ __device__ __forceinline__ void classify_slow(const DevTables &T, const uint8_t 
       cp[k] = c;
       ok[k] = good;
     }
-    // class-table loads issued unconditionally (index 0 when unused: a load
-    // under a condition is waited for on its own)
+    // second-stage loads issued unconditionally (index 0 when unused: a load
+    // under a condition is waited for on its own); the first stage is read
+    // from LDS, and from memory only for code points beyond U+FFFF
     uint32_t cls[K];
+    bool astral = false;
 #pragma unroll
-    for (int k = 0; k < K; ++k) blk[k] = T.uni1[ok[k] ? (cp[k] >> 8) : 0u];
+    for (int k = 0; k < K; ++k) {
+      blk[k] = st.u1[ok[k] ? ((cp[k] >> 8) & 0xFFu) : 0u];
+      astral = astral || (ok[k] && cp[k] > 0xFFFFu);
+    }
+    if (astral) {
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        if (ok[k] && cp[k] > 0xFFFFu) blk[k] = T.uni1[cp[k] >> 8];
+    }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const uint32_t c = T.uni2[ok[k] ? blk[k] * 256u + (cp[k] & 0xFFu) : 0u];
@@ -199,7 +239,8 @@ template <bool COMPUTE>
 __device__ __forceinline__ void classify_word(const DevTables &T, const uint8_t *__restrict__ text,
                                               const Window &win, int64_t base, uint64_t n,
                                               uint64_t seg_lo, uint64_t seg_hi, WordMasks &m,
-                                              const uint64_t *slow_in, uint64_t *slow_out) {
+                                              const uint64_t *slow_in, uint64_t *slow_out,
+                                              const SlowStage *st, int64_t lo) {
   m.valid = 0;
   if (base >= 0 && uint64_t(base) < n) {
     const uint64_t left = n - uint64_t(base);
@@ -263,7 +304,7 @@ __device__ __forceinline__ void classify_word(const DevTables &T, const uint8_t 
       const ulonglong2 v0 = q[0], v1 = q[1], v2 = q[2], v3 = q[3], v4 = q[4];
       r = SlowMasks{v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y, v4.x, v4.y};
     } else {
-      classify_slow(T, text, win, base, n, seg_lo, seg_hi, hi2, non, m.valid, r);
+      classify_slow(T, text, win, base, n, seg_lo, seg_hi, hi2, non, m.valid, *st, lo, r);
       if (slow_out) {
         ulonglong2 *q = reinterpret_cast<ulonglong2 *>(slow_out);
         q[0] = ulonglong2{r.LU, r.LL};

@@ -26,6 +26,16 @@ __device__ __forceinline__ void word_setup(const EncodeArgs &a, int64_t w, bool 
   const int64_t base = w * 64;
   const bool in = w >= 0 && w < int64_t(a.n_words);
   load_window(a.text, a.n, base, win);
+  // the first kernel stages the wave's bytes in LDS for the multi-byte
+  // decoder (one wave per workgroup, lane = threadIdx.x at consecutive words)
+  const SlowStage *st = nullptr;
+  int64_t lo = 0;
+  if (FIRST) {
+    __shared__ SlowStage stage;
+    stage_fill(stage, a.T, win, int(threadIdx.x));
+    st = &stage;
+    lo = base - int64_t(threadIdx.x) * 64 - 16;
+  }
   if (a.n_seg > 1 && in && !FIRST) {
     const ulonglong2 v = reinterpret_cast<const ulonglong2 *>(a.ws.wseg)[w];
     seg_lo = v.x;
@@ -43,7 +53,7 @@ __device__ __forceinline__ void word_setup(const EncodeArgs &a, int64_t w, bool 
   // words that have one)
   uint64_t *rec = in ? a.ws.wslow + uint64_t(w) * SLOW_WORDS : nullptr;
   classify_word<FIRST>(a.T, a.text, win, base, a.n, seg_lo, seg_hi, m, FIRST ? nullptr : rec,
-                       (FIRST && owned) ? rec : nullptr);
+                       (FIRST && owned) ? rec : nullptr, st, lo);
 }
 
 }  // namespace bbpe
