@@ -67,7 +67,7 @@ __global__ void __launch_bounds__(64) k_pieces(EncodeArgs a) {
   if (a.n_tiles <= FUSE_TILES) {
     // units of the tiles before this one (their counts, unscanned)
     uint32_t acc = 0;
-    for (uint32_t q = uint32_t(lane); q < t; q += 64) acc += a.ws.tile_np[q];
+    fold_strided(a.ws.tile_np, uint32_t(lane), t, 64u, [&](uint32_t, uint32_t v) { acc += v; });
     tbase = wave_sum(acc);
     if (t + 1 == a.n_tiles && lane == 63) {
       const uint32_t total = tbase + incl;

@@ -82,40 +82,38 @@ __device__ __forceinline__ void add_class(SlowMasks &r, uint32_t cls, uint64_t b
   r.M |= (cls == CC_M) ? bits : 0;
 }
 
-// byte p of the text, 0 outside it (the load is issued either way)
-__device__ __forceinline__ uint32_t text_byte(const uint8_t *__restrict__ text, uint64_t n, int64_t p) {
-  const bool in = p >= 0 && uint64_t(p) < n;
-  const uint32_t v = text[in ? p : 0];
-  return in ? v : 0u;
+// The text bytes of one wave's 64 windows in LDS: bytes [lo, lo + 4128),
+// where lo is 16 bytes before lane 0's word (the windows hold 0 outside the
+// text), so that per-character byte reads go to LDS instead of memory.
+constexpr uint32_t STAGE_BYTES = 64 * 64 + 32;
+
+// Every lane of the wave calls this with its own window (lane = threadIdx.x
+// < 64, consecutive lanes at consecutive words); no barrier.
+__device__ __forceinline__ void stage_window(uint4 *bytes, const Window &win, int lane) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    bytes[1 + 4 * lane + q] = uint4{win.w[4 + 4 * q], win.w[5 + 4 * q], win.w[6 + 4 * q], win.w[7 + 4 * q]};
+  if (lane == 0) bytes[0] = uint4{win.w[0], win.w[1], win.w[2], win.w[3]};
+  if (lane == 63) bytes[STAGE_BYTES / 16 - 1] = uint4{win.w[20], win.w[21], win.w[22], win.w[23]};
 }
 
-// The bytes of one wave's 64 windows, copied to LDS, and the first stage of
-// the class table for the Basic Multilingual Plane (code points >> 8 below
-// 256), so that the multi-byte decoder's byte reads and first-stage lookups
-// go to LDS instead of memory.
+// byte p of the text from a staged tile (p in [lo, lo + STAGE_BYTES))
+__device__ __forceinline__ uint32_t staged_byte(const uint4 *bytes, int64_t lo, int64_t p) {
+  return reinterpret_cast<const uint8_t *>(bytes)[p - lo];
+}
+
+// The staged bytes and the first stage of the class table for the Basic
+// Multilingual Plane (code points >> 8 below 256), for the multi-byte decoder.
 struct SlowStage {
-  uint4 bytes[(64 * 64 + 32) / 16];  // text bytes [lo, lo + 4128), 0 outside the text
+  uint4 bytes[STAGE_BYTES / 16];
   uint16_t u1[256];
 };
 
-// Fill the stage: every lane of the wave calls this with its own window (the
-// word at lane_base, lane = threadIdx.x < 64, consecutive lanes at
-// consecutive words).
 __device__ __forceinline__ void stage_fill(SlowStage &st, const DevTables &T, const Window &win, int lane) {
   const uint2 u = reinterpret_cast<const uint2 *>(T.uni1)[lane];
   reinterpret_cast<uint2 *>(st.u1)[lane] = u;
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    st.bytes[1 + 4 * lane + q] = uint4{win.w[4 + 4 * q], win.w[5 + 4 * q], win.w[6 + 4 * q], win.w[7 + 4 * q]};
-  if (lane == 0) st.bytes[0] = uint4{win.w[0], win.w[1], win.w[2], win.w[3]};
-  if (lane == 63) st.bytes[257] = uint4{win.w[20], win.w[21], win.w[22], win.w[23]};
+  stage_window(st.bytes, win, lane);
   __syncthreads();
-}
-
-// byte p of the text from the stage (p in [lo, lo + 4128); the windows hold 0
-// outside the text)
-__device__ __forceinline__ uint32_t stage_byte(const SlowStage &st, int64_t lo, int64_t p) {
-  return reinterpret_cast<const uint8_t *>(st.bytes)[p - lo];
 }
 
 // The multi-byte characters of the word at base: `hi2` marks its bytes >=
@@ -159,7 +157,7 @@ __device__ __forceinline__ void classify_slow(const DevTables &T, const uint8_t 
       ii[k] = __ffsll(static_cast<unsigned long long>(leads)) - 1;  // -1 once none are left
       leads &= leads - 1;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[k][j] = stage_byte(st, lo, base + ii[k] + j);
+      for (int j = 0; j < 4; ++j) b[k][j] = staged_byte(st.bytes, lo, base + ii[k] + j);
     }
     uint32_t cp[K], blk[K];
     int len[K];

@@ -240,4 +240,66 @@ __device__ __forceinline__ void segment_marks(const uint64_t *__restrict__ seg_o
   seg_at_base = a > 0 ? a - 1 : 0;
 }
 
+// Position of the k-th (from 0) set bit of x, for k < popcount(x): a binary
+// search over halves by population count.
+__device__ __forceinline__ int nth_set_bit(uint64_t x, uint32_t k) {
+  int pos = 0;
+#pragma unroll
+  for (int wdt = 32; wdt >= 1; wdt >>= 1) {
+    const uint32_t lo = uint32_t(__popcll(x & ((uint64_t(1) << wdt) - 1)));
+    if (k >= lo) {
+      k -= lo;
+      x >>= wdt;
+      pos += wdt;
+    }
+  }
+  return pos;
+}
+
+// ---------------------------------------------------------------------------
+// Per-lane folds over short runs of per-tile values (the tile scans folded
+// into the per-tile kernels).  Loads are issued eight at a time before any is
+// used, so a run of up to 32 values costs four memory round trips, not 32.
+// ---------------------------------------------------------------------------
+constexpr uint32_t FOLD_BATCH = 8;
+
+// f(q, p[q]) for q = q0, q0 + 1, ..., q1 - 1, in that order
+template <typename V, typename F>
+__device__ __forceinline__ void fold_run(const V *p, uint32_t q0, uint32_t q1, F f) {
+  for (uint32_t q = q0; q < q1; q += FOLD_BATCH) {
+    V v[FOLD_BATCH];
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j) v[j] = (q + j < q1) ? p[q + j] : V(0);
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j)
+      if (q + j < q1) f(q + j, v[j]);
+  }
+}
+
+// f(q, p[q]) for q = q1 - 1, q1 - 2, ..., q0, in that order
+template <typename V, typename F>
+__device__ __forceinline__ void fold_run_rev(const V *p, uint32_t q0, uint32_t q1, F f) {
+  for (uint32_t q = q1; q > q0; q -= min(q - q0, FOLD_BATCH)) {
+    V v[FOLD_BATCH];
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j) v[j] = (q - q0 > j) ? p[q - 1 - j] : V(0);
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j)
+      if (q - q0 > j) f(q - 1 - j, v[j]);
+  }
+}
+
+// f(q, p[q]) for q = q0, q0 + step, ... below q1
+template <typename V, typename F>
+__device__ __forceinline__ void fold_strided(const V *p, uint32_t q0, uint32_t q1, uint32_t step, F f) {
+  for (uint32_t q = q0; q < q1; q += FOLD_BATCH * step) {
+    V v[FOLD_BATCH];
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j) v[j] = (q + j * step < q1) ? p[q + j * step] : V(0);
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j)
+      if (q + j * step < q1) f(q + j * step, v[j]);
+  }
+}
+
 }  // namespace bbpe

@@ -239,17 +239,28 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
   if (fold) {
     per = (t + 63) / 64;
     const uint32_t q0 = min(t, uint32_t(lane) * per), q1 = min(t, q0 + per);
+    // one pass over the lane's run: its character count and its last run
+    // change relative to the run's start
     unsigned long long sum = 0;
-    for (uint32_t q = q0; q < q1; ++q) sum += a.ws.tile_nchar[q];
+    long long mx_rel = -1;
+    for (uint32_t q = q0; q < q1; q += FOLD_BATCH) {  // loads issued a batch at a time
+      int32_t lc[FOLD_BATCH];
+      uint32_t nc[FOLD_BATCH];
+#pragma unroll
+      for (uint32_t j = 0; j < FOLD_BATCH; ++j) {
+        const bool in = q + j < q1;
+        lc[j] = in ? a.ws.tile_lastchg[q + j] : -1;
+        nc[j] = in ? a.ws.tile_nchar[q + j] : 0u;
+      }
+#pragma unroll
+      for (uint32_t j = 0; j < FOLD_BATCH; ++j) {
+        if (lc[j] >= 0) mx_rel = max(mx_rel, (long long)(sum + uint32_t(lc[j])));
+        sum += nc[j];
+      }
+    }
     const unsigned long long incl_s = wave_incl_sum64(sum, lane);
     run_excl = incl_s - sum;
-    unsigned long long run = run_excl;
-    long long mx = -1;
-    for (uint32_t q = q0; q < q1; ++q) {
-      const int32_t lc = a.ws.tile_lastchg[q];
-      if (lc >= 0) mx = max(mx, (long long)(run + uint32_t(lc)));
-      run += a.ws.tile_nchar[q];
-    }
+    long long mx = mx_rel >= 0 ? (long long)run_excl + mx_rel : -1;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
       const long long o = __shfl_xor(mx, d, 64);
@@ -260,11 +271,25 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
     // the offsets check over every tile; block 0 also writes the status
     uint32_t bad = 0;
     unsigned long long err = ~0ull, nch = 0;
-    for (uint32_t q = uint32_t(lane); q < T; q += 64) {
-      bad |= a.ws.tile_bad[q];
-      if (t == 0) {
-        err = min(err, a.ws.tile_err[q]);
-        nch += a.ws.tile_nchar[q];
+    if (t != 0) {
+      fold_strided(a.ws.tile_bad, uint32_t(lane), T, 64u, [&](uint32_t, uint32_t v) { bad |= v; });
+    } else {
+      for (uint32_t q = uint32_t(lane); q < T; q += 64 * FOLD_BATCH) {  // three loads per tile, batched
+        uint32_t bv[FOLD_BATCH], nv[FOLD_BATCH];
+        unsigned long long ev[FOLD_BATCH];
+#pragma unroll
+        for (uint32_t j = 0; j < FOLD_BATCH; ++j) {
+          const bool in = q + 64 * j < T;
+          bv[j] = in ? a.ws.tile_bad[q + 64 * j] : 0u;
+          ev[j] = in ? a.ws.tile_err[q + 64 * j] : ~0ull;
+          nv[j] = in ? a.ws.tile_nchar[q + 64 * j] : 0u;
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < FOLD_BATCH; ++j) {
+          bad |= bv[j];
+          err = min(err, ev[j]);
+          nch += nv[j];
+        }
       }
     }
     const bool any_bad = __ballot(bad != 0) != 0;
@@ -349,34 +374,31 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
       if (kk == 0) kk = 1;
       nr = rs + 25000ull * kk;                      // next run cut >= c
     }
-    // a run change only moves the next run cut later, so with no segment
-    // start in the word and both boundaries beyond its last character there
-    // is no cut here
-    const uint64_t c_end = c + uint64_t(__popcll(m.lead));
-    uint64_t leads = (segb == 0 && nw >= c_end && nr >= c_end) ? 0ull : m.lead;
-    while (leads) {
-      const int i = __ffsll(static_cast<unsigned long long>(leads)) - 1;
-      leads &= leads - 1;
-      if ((segb >> i) & 1) {
-        while (s + 1 < a.n_seg && a.seg_off[s + 1] <= uint64_t(base + i)) ++s;
-        segcs = c;
-        nw = c + 400000ull;
-        rs = c;
-        nr = c + 25000ull;
-      } else if (c == nw) {
-        cut |= bit(i);
-        rs = c;
-        nw += 400000ull;
-        nr = c + 25000ull;
-      } else if ((chg >> i) & 1) {
-        rs = c;
-        nr = c + 25000ull;
-      } else if (c == nr) {
-        cut |= bit(i);
-        nr += 25000ull;
-      }
-      ++c;
+    // Walking the word's characters in order: a segment start restarts
+    // both counts; else the character at nw is a window cut (which restarts
+    // the run count); else a run change restarts the run count; else the
+    // character at nr is a run cut.  A restart puts the next boundary of
+    // its kind at least 25,000 characters on, past the word's end (a word
+    // holds at most 64 characters), so each kind of cut falls at most once
+    // in a word, at a character found from the counts directly:
+    //  * the window cut at character nw, unless a segment starts at or
+    //    before it in the word;
+    //  * the run cut at character nr, unless a segment start, a run change
+    //    or the window cut falls at or before it in the word.
+    const uint64_t nlead = uint64_t(__popcll(m.lead));
+    const uint64_t segl = segb & m.lead;
+    const uint64_t upto_seg = segl ? bit(__ffsll(static_cast<unsigned long long>(segl)) - 1) - 1 : ~0ull;
+    uint64_t wcut = 0;
+    if (nw - c < nlead) {
+      const uint64_t b = bit(nth_set_bit(m.lead, uint32_t(nw - c)));
+      wcut = b & upto_seg;  // strictly before the first segment start
     }
+    if (nr - c < nlead) {
+      const int i = nth_set_bit(m.lead, uint32_t(nr - c));
+      const uint64_t through = (i == 63) ? ~0ull : (bit(i + 1) - 1);
+      if (((segl | chg | wcut) & through) == 0) cut |= bit(i);
+    }
+    cut |= wcut;
   }
   const uint64_t brk = segb | cut;                   // span starts known so far
   const uint64_t brk_next = shfl_down64(brk, 1);

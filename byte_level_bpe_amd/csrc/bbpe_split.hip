@@ -578,10 +578,10 @@ __device__ __forceinline__ uint32_t carry_direct(const EncodeArgs &a, uint32_t t
   const uint32_t per_l = (t + 63) / 64, per_r = (T - 1 - t + 63) / 64;
   uint64_t f = ltr_id<G>();
   const uint32_t l0 = min(t, uint32_t(lane) * per_l), l1 = min(t, l0 + per_l);
-  for (uint32_t q = l0; q < l1; ++q) f = ltr_then<G>(f, a.ws.tile_fn[q] & ~uint64_t(0x300));
+  fold_run(a.ws.tile_fn, l0, l1, [&](uint32_t, uint64_t x) { f = ltr_then<G>(f, x & ~uint64_t(0x300)); });
   uint32_t gv = FV_ID;
   const uint32_t r0 = min(T, t + 1 + uint32_t(lane) * per_r), r1 = min(T, r0 + per_r);
-  for (uint32_t q = r1; q > r0; --q) gv = fv_then(gv, uint32_t(a.ws.tile_fn[q - 1] >> 8) & 3u);
+  fold_run_rev(a.ws.tile_fn, r0, r1, [&](uint32_t, uint64_t x) { gv = fv_then(gv, uint32_t(x >> 8) & 3u); });
   wave_scan_fns<G>(f, gv, lane);
   const uint64_t all_f = __shfl(static_cast<unsigned long long>(f), 63, 64);
   const uint32_t all_g = __shfl(gv, 0, 64);
@@ -639,6 +639,7 @@ __device__ __forceinline__ void split_body(const EncodeArgs &a) {
     // candidate), and every position is checked without a branch, so that
     // the reads overlap.
     __shared__ uint32_t s_inner[2048];
+    __shared__ uint4 s_bytes[STAGE_BYTES / 16];
     const uint64_t na_prev = shfl_up64(m.na, 1), ll_prev = shfl_up64(m.LL, 1);
     const uint64_t cand = o.IN & ~ps & ~o.SS & m.valid &
                           (m.na | shl(m.na, na_prev, 1) | (m.LU & shl(m.LL, ll_prev, 1)));
@@ -647,6 +648,7 @@ __device__ __forceinline__ void split_body(const EncodeArgs &a) {
       uint4 *dst = reinterpret_cast<uint4 *>(s_inner);
 #pragma unroll
       for (int k = 0; k < 8; ++k) dst[k * 64 + lane] = src[k * 64 + lane];
+      stage_window(s_bytes, win, lane);
       __syncthreads();
       uint64_t cut = 0;
 #pragma unroll
@@ -660,6 +662,7 @@ __device__ __forceinline__ void split_body(const EncodeArgs &a) {
       // together
       uint64_t rest = cand & ~cut & m.lead;
       const int64_t base = w * 64;
+      const int64_t lo = base - int64_t(lane) * 64 - 16;  // first staged byte
       while (rest) {
         constexpr int K = 8;
         int ii[K];
@@ -669,7 +672,7 @@ __device__ __forceinline__ void split_body(const EncodeArgs &a) {
           ii[k] = __ffsll(static_cast<unsigned long long>(rest)) - 1;
           rest &= rest - 1;
 #pragma unroll
-          for (int d = 0; d < 6; ++d) b[k][d] = text_byte(a.text, a.n, base + ii[k] - 3 + d);
+          for (int d = 0; d < 6; ++d) b[k][d] = staged_byte(s_bytes, lo, base + ii[k] - 3 + d);
         }
         uint32_t hit[K];
 #pragma unroll
