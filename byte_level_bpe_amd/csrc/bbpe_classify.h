@@ -43,29 +43,6 @@ __device__ __forceinline__ bool seg_start_at(uint64_t seg_lo, uint64_t seg_hi, i
   return s < 64 ? ((seg_lo >> s) & 1) : ((seg_hi >> (s - 64)) & 1);
 }
 
-// Decode the sequence whose lead byte is at text offset base + i (i may be
-// negative down to -3), reading bytes from the text.  ok = complete, minimal,
-// no surrogate, <= U+10FFFF, inside the text and crossing no segment start.
-__device__ __forceinline__ uint32_t decode_text(const uint8_t *__restrict__ text, uint64_t n,
-                                                int64_t base, int i, uint64_t seg_lo,
-                                                uint64_t seg_hi, int &len, bool &ok) {
-  const int64_t p = base + i;
-  const uint32_t b0 = text[p];
-  len = utf8_len(b0);
-  ok = len > 0 && uint64_t(p) + uint64_t(len) <= n;
-  if (!ok || len == 1) return b0;
-  uint32_t cp = b0 & (0x7Fu >> len);
-  for (int j = 1; j < len; ++j) {
-    const uint32_t b = text[p + j];
-    ok = ok && ((b & 0xC0u) == 0x80u) && !seg_start_at(seg_lo, seg_hi, i + j);
-    cp = (cp << 6) | (b & 0x3Fu);
-  }
-  if (len == 3 && cp < 0x800) ok = false;
-  if (len == 4 && (cp < 0x10000 || cp > 0x10FFFF)) ok = false;
-  if (cp >= 0xD800 && cp <= 0xDFFF) ok = false;
-  return cp;
-}
-
 // What the multi-byte characters of a word add to its masks.  Computed once
 // per call (by the first front-end kernel, which stores it for every word
 // holding a byte >= 0x80) and read back by the later ones.
@@ -134,13 +111,28 @@ __device__ __forceinline__ void classify_slow(const DevTables &T, const uint8_t 
     else if ((win.at(-2) & 0xC0u) != 0x80u) kf = 2;
     else if ((win.at(-3) & 0xC0u) != 0x80u) kf = 3;
     if (kf > 0 && base - kf >= 0) {
-      int len;
-      bool ok;
-      const uint32_t cp = decode_text(text, n, base, -kf, seg_lo, seg_hi, len, ok);
+      // its bytes from the window (fixed indices, selected by kf)
+      uint32_t b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = kf == 1 ? win.at(j - 1) : (kf == 2 ? win.at(j - 2) : win.at(j - 3));
+      const int len = utf8_len(b[0]);
+      bool ok = len >= 2 && uint64_t(base - kf) + uint64_t(len) <= n;
+      uint32_t cp = b[0] & (0x7Fu >> len);
+#pragma unroll
+      for (int j = 1; j < 4; ++j) {
+        const bool in = j < len;
+        ok = ok && (!in || (((b[j] & 0xC0u) == 0x80u) && !seg_start_at(seg_lo, seg_hi, j - kf)));
+        cp = in ? ((cp << 6) | (b[j] & 0x3Fu)) : cp;
+      }
+      if (len == 3 && cp < 0x800) ok = false;
+      if (len == 4 && (cp < 0x10000 || cp > 0x10FFFF)) ok = false;
+      if (cp >= 0xD800 && cp <= 0xDFFF) ok = false;
       if (ok && len > kf) {
+        const uint32_t blk = cp <= 0xFFFFu ? uint32_t(st.u1[cp >> 8]) : uint32_t(T.uni1[cp >> 8]);
         const uint64_t bits = bit_range(0, len - kf);
         covered |= bits;
-        add_class(r, class_of(T, cp), bits);
+        add_class(r, T.uni2[blk * 256u + (cp & 0xFFu)], bits);
         if (cp == 0x17F) r.ls1 |= 1;  // its second byte
       }
     }
@@ -148,37 +140,49 @@ __device__ __forceinline__ void classify_slow(const DevTables &T, const uint8_t 
   // invalid lead bytes (C0, C1, F5..FF) are >= 0xC0 too and fail to decode
   uint64_t leads = hi2 & valid;
   uint64_t lead = 0;
+  // segment starts at word positions 0..63, and 64..66 in bits 0..2
+  const uint64_t segw = (seg_lo >> 8) | (seg_hi << 56);
+  const uint32_t segx = uint32_t(seg_hi >> 8) & 7u;
+  // class code planes of the batch loop's characters (bit b of the code)
+  uint64_t pl0 = 0, pl1 = 0, pl2 = 0;
+  const uint32_t *b32 = reinterpret_cast<const uint32_t *>(st.bytes);
+  const uint32_t a0 = uint32_t(base - lo);  // the word's first byte in the stage
   while (leads) {
     constexpr int K = 8;
     int ii[K];
-    uint32_t b[K][4];
+    uint32_t v[K];  // the four bytes from each lead, little endian
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       ii[k] = __ffsll(static_cast<unsigned long long>(leads)) - 1;  // -1 once none are left
       leads &= leads - 1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[k][j] = staged_byte(st.bytes, lo, base + ii[k] + j);
+      const uint32_t ad = uint32_t(int(a0) + ii[k]);
+      v[k] = __builtin_amdgcn_alignbyte(b32[(ad >> 2) + 1], b32[ad >> 2], ad & 3u);
     }
     uint32_t cp[K], blk[K];
     int len[K];
     bool ok[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int i = ii[k];
-      len[k] = utf8_len(b[k][0]);
-      uint32_t c = b[k][0] & (0x7Fu >> len[k]);
-      bool good = i >= 0 && len[k] >= 2;
-#pragma unroll
-      for (int j = 1; j < 4; ++j) {
-        const bool in = j < len[k];
-        good = good && (!in || (((b[k][j] & 0xC0u) == 0x80u) && !seg_start_at(seg_lo, seg_hi, i + j)));
-        c = in ? ((c << 6) | (b[k][j] & 0x3Fu)) : c;
-      }
-      if (len[k] == 3 && c < 0x800) good = false;
-      if (len[k] == 4 && (c < 0x10000 || c > 0x10FFFF)) good = false;
+      const uint32_t w = v[k], b0 = w & 0xFFu;
+      const int Ln = b0 < 0xC2u ? 0 : (b0 < 0xE0u ? 2 : (b0 < 0xF0u ? 3 : (b0 < 0xF5u ? 4 : 0)));
+      // continuation bytes 1 .. Ln-1 of the form 10xxxxxx
+      const uint32_t cm = Ln == 2 ? 0xC000u : (Ln == 3 ? 0xC0C000u : 0xC0C0C000u);
+      bool good = ii[k] >= 0 && Ln >= 2 && (w & cm) == (cm & 0x80808080u);
+      const uint32_t f1 = (w >> 8) & 0x3Fu, f2 = (w >> 16) & 0x3Fu, f3 = (w >> 24) & 0x3Fu;
+      const uint32_t c = Ln == 2 ? (((b0 & 0x1Fu) << 6) | f1)
+                       : Ln == 3 ? (((b0 & 0x0Fu) << 12) | (f1 << 6) | f2)
+                                 : (((b0 & 0x07u) << 18) | (f1 << 12) | (f2 << 6) | f3);
+      if (Ln == 3 && c < 0x800) good = false;
+      if (Ln == 4 && (c < 0x10000 || c > 0x10FFFF)) good = false;
       if (c >= 0xD800 && c <= 0xDFFF) good = false;
+      // no segment starts at a continuation byte
+      const int i = ii[k] < 0 ? 0 : ii[k];
+      const uint64_t cont = bit_range(i + 1, Ln - 1);
+      const int ext = i + Ln - 64;  // continuation bytes past the word
+      const bool segbad = (segw & cont) != 0 || (ext > 0 && (segx & ((1u << ext) - 1u)) != 0);
       cp[k] = c;
-      ok[k] = good;
+      len[k] = Ln;
+      ok[k] = good && !segbad;
     }
     // second-stage loads issued unconditionally (index 0 when unused: a load
     // under a condition is waited for on its own); the first stage is read
@@ -211,13 +215,22 @@ __device__ __forceinline__ void classify_slow(const DevTables &T, const uint8_t 
       }
       const uint64_t bits = bit_range(i, len[k]);
       covered |= bits & ~bit(i);
-      add_class(r, cls[k], bits);
+      pl0 |= (cls[k] & 1u) ? bits : 0;
+      pl1 |= (cls[k] & 2u) ? bits : 0;
+      pl2 |= (cls[k] & 4u) ? bits : 0;
       if (cp[k] == 0x17F) {
         r.ls0 |= bit(i);
         if (i + 1 < 64) r.ls1 |= bit(i + 1);
       }
     }
   }
+  // planes to class masks (class codes 1..6; 0, "other", sets no plane)
+  r.LU |= pl0 & ~pl1 & ~pl2;
+  r.LL |= ~pl0 & pl1 & ~pl2;
+  r.LB |= pl0 & pl1 & ~pl2;
+  r.N |= ~pl0 & ~pl1 & pl2;
+  r.WS |= pl0 & ~pl1 & pl2;
+  r.M |= ~pl0 & pl1 & pl2;
   // continuation bytes that no valid character claims are errors; they
   // count as characters of their own (class "other")
   const uint64_t cont = non & ~hi2;
