@@ -484,3 +484,24 @@ def test_capacity_and_empty(atoms):
     ids, id_off = tok.encode_segments([(b"", False), (b"", True)])
     assert ids.numel() == 0 and id_off.cpu().tolist() == [0, 0, 0]
     assert_ids(tok, orc, [(b"", False), (b"a", False), (b"", False)], what="empty")
+
+
+def test_chunk_cuts_coinciding(atoms):
+    """Window and run cuts where they meet each other, run changes and
+    segment starts inside one 64-byte word: a run whose 16th run cut falls on
+    the 400,000-character window boundary (the window cut takes it), a run
+    change on the character where a run cut is due, a segment that starts
+    a few bytes after the previous segment's window boundary, and run cuts
+    shifted through every byte phase by multi-byte prefixes."""
+    tok, orc = atoms
+    segs = [(b"x" * 450000, False),                      # run cut on the window boundary
+            (b"x" * 25000 + b" y" + b"x" * 30000, False),  # run change where a cut is due
+            (b"ab " * 133336 + b"c", False),              # 400,009 bytes: the next segment
+            (b"z" * 30000, False)]                        # starts in the boundary's word
+    r = random.Random(1234)
+    for k in range(0, 64, 3):  # multi-byte prefixes move the run cuts through the word
+        pre = "é" * r.randint(0, 40) + "中" * k
+        segs.append(((pre + "q" * (25000 + r.randint(-70, 70)) + " " * r.randint(0, 3)
+                      + "w" * r.randint(24900, 25100)).encode(), r.random() < 0.5))
+    say("coinciding chunk cuts: %d bytes" % sum(len(s) for s, _ in segs))
+    assert_pieces(tok, orc, segs, safe=True, what="coinciding cuts")
