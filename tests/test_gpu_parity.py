@@ -505,3 +505,32 @@ def test_chunk_cuts_coinciding(atoms):
                       + "w" * r.randint(24900, 25100)).encode(), r.random() < 0.5))
     say("coinciding chunk cuts: %d bytes" % sum(len(s) for s, _ in segs))
     assert_pieces(tok, orc, segs, safe=True, what="coinciding cuts")
+
+
+def test_multibyte_at_word_edges(atoms):
+    """Multi-byte characters that start at every byte phase around a 64-byte
+    word's end (so that they straddle into the next word, or begin in the
+    word before), valid ones against the oracle's ids and truncated ones
+    against the first invalid byte."""
+    tok, orc = atoms
+    chars = ["é", "中", "😀"]
+    text = bytearray()
+    for c in chars:
+        cb = c.encode()
+        for phase in range(56, 72):
+            pad = (phase - len(text)) % 64
+            text += b"a" * pad + cb + b" "
+    say("multi-byte characters at word edges: %d bytes" % len(text))
+    assert_ids(tok, orc, [(bytes(text), False)], what="word edges")
+    for c in ["中", "😀"]:
+        cb = c.encode()
+        for phase in range(58, 68):
+            bad = b"a" * phase + cb[:-1] + b"b" * 70  # truncated: the lead is the first bad byte
+            with pytest.raises(B.BBPEError) as e:
+                tok.encode_segments([(bad, False)])
+            assert e.value.status == B.E_UTF8
+            assert (e.value.segment, e.value.byte_offset) == (0, phase), (c, phase)
+    c = "中".encode()
+    with pytest.raises(B.BBPEError) as e:  # a character split by a segment start at a word edge
+        tok.encode_segments([(b"x" * 63 + c[:1], False), (c[1:] + b"y", False)])
+    assert (e.value.segment, e.value.byte_offset) == (0, 63)
