@@ -305,6 +305,21 @@ __device__ __forceinline__ bool unit_rest_eq(const UnitBytes<SK> &u, uint32_t a,
 
 __device__ __forceinline__ uint32_t above32(int j) { return ~((2u << j) - 1u); }
 
+// One lane's column of the LDS part-id array [32 positions][64 lanes]: ids
+// are below 2^21, kept as a 16-bit low part and an 8-bit high part (6 KB per
+// wave instead of 8 KB, which lets more merge waves share a CU).
+struct PartCol {
+  uint16_t *lo;
+  uint8_t *hi;
+  __device__ __forceinline__ int32_t get(int j) const {
+    return int32_t(uint32_t(lo[64 * j]) | (uint32_t(hi[64 * j]) << 16));
+  }
+  __device__ __forceinline__ void set(int j, int32_t v) const {
+    lo[64 * j] = uint16_t(uint32_t(v));
+    hi[64 * j] = uint8_t(uint32_t(v) >> 16);
+  }
+};
+
 // Merge a unit of 2 <= m <= SK bytes held in registers: pair ranks r[j] and
 // part ids pr[j] at every part start j, part starts as the bit mask bnd.
 // Writes the ids to out and returns their count.
@@ -315,7 +330,7 @@ __device__ __forceinline__ uint32_t above32(int j) { return ~((2u << j) - 1u); }
 // the leftmost least rank is one unsigned minimum per position.
 template <int SK>
 __device__ __forceinline__ uint32_t merge_short(const DevTables &T, const int32_t *atom,
-                                                const UnitBytes<SK> &u, uint32_t m, int32_t *lp,
+                                                const UnitBytes<SK> &u, uint32_t m, const PartCol &lp,
                                                 int32_t *out) {
   uint32_t r[SK];
 #pragma unroll
@@ -323,7 +338,7 @@ __device__ __forceinline__ uint32_t merge_short(const DevTables &T, const int32_
     const uint32_t b0 = u.byte(j), b1 = (j + 1 < SK) ? u.byte(j + 1) : 0u;
     const int32_t rk = (uint32_t(j) + 1 < m) ? T.pair[b0 * 256u + b1] : RANK_NONE;
     r[j] = rk == RANK_NONE ? ~0u : (uint32_t(rk) << 5) | uint32_t(j);
-    if (uint32_t(j) < m) lp[64 * j] = atom[b0];
+    if (uint32_t(j) < m) lp.set(j, atom[b0]);
   }
   uint32_t bnd = (m >= 32) ? 0xFFFFFFFFu : ((1u << m) - 1u);
   for (uint32_t round = 0; round + 1 < m; ++round) {
@@ -340,12 +355,12 @@ __device__ __forceinline__ uint32_t merge_short(const DevTables &T, const int32_
     const uint32_t before = bnd & ((1u << bj) - 1u);
     const int q = before ? 31 - __clz(before) : -1;
     // the merged part (id best) with its right and left neighbours
-    const int32_t id2 = after ? lp[64 * k2] : 0;
-    const int32_t idq = q >= 0 ? lp[64 * q] : 0;
+    const int32_t id2 = after ? lp.get(int(k2)) : 0;
+    const int32_t idq = q >= 0 ? lp.get(q) : 0;
     int32_t nb, nq;
     merge_rank2(T, after != 0, uint32_t(best), uint32_t(id2), q >= 0, uint32_t(idq), uint32_t(best),
                 nb, nq);
-    lp[64 * bj] = best;
+    lp.set(bj, best);
     const uint32_t kb = nb == RANK_NONE ? ~0u : (uint32_t(nb) << 5) | uint32_t(bj);
     const uint32_t kq = nq == RANK_NONE ? ~0u : (uint32_t(nq) << 5) | uint32_t(q);
 #pragma unroll
@@ -358,7 +373,7 @@ __device__ __forceinline__ uint32_t merge_short(const DevTables &T, const int32_
   uint32_t c = 0;
 #pragma unroll
   for (int j = 0; j < SK; ++j)
-    if ((bnd >> j) & 1u) out[c++] = lp[64 * j];
+    if ((bnd >> j) & 1u) out[c++] = lp.get(j);
   return c;
 }
 
@@ -752,7 +767,7 @@ __device__ __forceinline__ uint32_t chain_then(uint32_t f, uint32_t g) {
 
 template <int SK>
 __device__ __forceinline__ void merge_short_unit(const EncodeArgs &a, const int32_t *atom, uint32_t i,
-                                                 int32_t *lp) {
+                                                 const PartCol &lp) {
   const uint32_t s = a.ws.piece_start[i];
   const uint32_t m = a.ws.piece_start[i + 1] - s;
   UnitBytes<SK> u;
@@ -777,8 +792,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
                  e4 = e8 + (n4 + 63) / 64;
   if (blockIdx.x >= e4) return;
   __shared__ int32_t s_atom[256];
-  __shared__ int32_t s_part[32 * 64];  // [position][lane]: part ids of each lane's unit
-  int32_t *lp = s_part + lane;
+  __shared__ uint16_t s_part_lo[32 * 64];  // [position][lane]: part ids of each lane's unit
+  __shared__ uint8_t s_part_hi[32 * 64];
+  const PartCol lp{s_part_lo + lane, s_part_hi + lane};
   reinterpret_cast<int4 *>(s_atom)[lane] = reinterpret_cast<const int4 *>(a.T.atom)[lane];
   __syncthreads();
   for (uint32_t item = blockIdx.x; item < e4; item += gridDim.x) {
