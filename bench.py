@@ -34,7 +34,7 @@ WORKLOAD_DESC = {
 }
 
 
-ALG_BYTES = os.path.join(ROOT, "bench_alg_bytes.json")
+ALG_BYTES = os.path.join(ROOT, "tests", "golden", "alg_bytes.json")
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scaled by a
 # plain copy of known size), valid for the kernel sources they were taken on
 TRAFFIC = os.path.join(ROOT, "profiles", "encode_%s_hbm_counters.json")
@@ -69,11 +69,10 @@ def measured_traffic(workload: str, kernel: str):
 def algorithmic_bytes(kernel: str, w: dict) -> int:
     """Bytes one launch of `kernel` must move by the definition of its step.
 
-    w is the workload's entry of bench_alg_bytes.json, counted once by the
-    oracle (oracle/alg_bytes.py): per merge kernel, the bytes of the units
-    it merges, their ids and counts, and the rank lookups of the merge loop
-    on those units (key bytes + 4 B each); for k_probe, every unit's bytes,
-    start and count, plus one lookup per unit of 2+ bytes that is a key.
+    w is the workload's entry of tests/golden/alg_bytes.json, counted once by
+    the oracle (tests/golden/alg_bytes.py).  For k_probe and the merge
+    kernels: the units the kernel settles, each with its bytes (once), 4 B
+    per id and the merge loop's rank lookups on it (key bytes + 4 B each).
     Front-end kernels make one pass over the text: the text bytes plus
     64-bit masks in and out (1/8 byte per text byte each).
     """
@@ -302,7 +301,7 @@ def main():
     del cp_src, cp_dst
 
     # algorithmic bytes of the whole call and per kernel, counted once by the
-    # oracle and stored (oracle/alg_bytes.py)
+    # oracle and stored (tests/golden/alg_bytes.py)
     with open(ALG_BYTES) as f:
         alg = json.load(f)[args.workload]
     assert alg["ids"] == n_ids and alg["bytes"] == total, "workload differs from the counted one"

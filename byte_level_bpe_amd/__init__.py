@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import ctypes as C
 import os
+import threading
 
 import numpy as np
 
@@ -132,6 +133,10 @@ class Tokenizer:
         self._dev_table = None
         self._ws = None
         self._dws = None
+        # guards the cached table, workspace and decode workspace when
+        # several threads share this object (the library itself runs calls
+        # on one handle one after the other)
+        self._lock = threading.RLock()
 
     def __del__(self):
         if getattr(self, "_h", None) and _lib is not None:
@@ -170,6 +175,11 @@ class Tokenizer:
     # ---- device side ----
     def upload(self, device="cuda", stream=None):
         import torch
+        with self._lock:
+            return self._upload(device, stream)
+
+    def _upload(self, device, stream):
+        import torch
         if self._dev_table is None:
             t = torch.empty(self.table_bytes + 256, dtype=torch.uint8, device=device)
             st = _load().bbpe_upload_tables(self._h, C.c_void_p(t.data_ptr()), self.table_bytes,
@@ -189,9 +199,18 @@ class Tokenizer:
     def workspace(self, total_bytes: int, n_seg: int, device="cuda"):
         import torch
         need = self.workspace_bytes(total_bytes, n_seg)
-        if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(need, dtype=torch.uint8, device=device)
-        return self._ws
+        with self._lock:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty(need, dtype=torch.uint8, device=device)
+            return self._ws
+
+    def _decode_workspace(self, n_ids: int, dev):
+        import torch
+        need = self.decode_workspace_bytes(n_ids)
+        with self._lock:
+            if self._dws is None or self._dws.numel() < need:
+                self._dws = torch.empty(need, dtype=torch.uint8, device=dev)
+            return self._dws
 
     def encode_device(self, text, seg_off, allow, total_bytes: int, tiktoken_safe: bool = True,
                       ids=None, id_off=None, stream=None, count_only: bool = False):
@@ -284,15 +303,13 @@ class Tokenizer:
         dev = ids.device
         self.upload(dev)
         n_ids = int(ids.numel())
-        need = self.decode_workspace_bytes(n_ids)
-        if self._dws is None or self._dws.numel() < need:
-            self._dws = torch.empty(need, dtype=torch.uint8, device=dev)
+        dws = self._decode_workspace(n_ids, dev)
         if tok_off is None:
             tok_off = torch.empty(max(1, n_ids), dtype=torch.int64, device=dev)
         total = C.c_uint64(0)
         st = _load().bbpe_token_offsets_device(
             self._h, C.c_void_p(ids.data_ptr()) if n_ids else None, n_ids,
-            C.c_void_p(tok_off.data_ptr()), C.c_void_p(self._dws.data_ptr()), self._dws.numel(),
+            C.c_void_p(tok_off.data_ptr()), C.c_void_p(dws.data_ptr()), dws.numel(),
             C.byref(total), _stream_handle(stream))
         if st == E_BAD_ID:
             raise BBPEError(st, "token_offsets_device at index %d" % total.value)
@@ -312,9 +329,7 @@ class Tokenizer:
         dev = ids.device
         self.upload(dev)
         n_ids = int(ids.numel())
-        need = self.decode_workspace_bytes(n_ids)
-        if self._dws is None or self._dws.numel() < need:
-            self._dws = torch.empty(need, dtype=torch.uint8, device=dev)
+        dws = self._decode_workspace(n_ids, dev)
         if offsets and tok_off is None:
             tok_off = torch.empty(max(1, n_ids), dtype=torch.int64, device=dev)
         sized = out is not None
@@ -327,7 +342,7 @@ class Tokenizer:
                 self._h, C.c_void_p(ids.data_ptr()) if n_ids else None, n_ids,
                 C.c_void_p(buf.data_ptr()), buf.numel(),
                 C.c_void_p(tok_off.data_ptr()) if tok_off is not None else None,
-                C.c_void_p(self._dws.data_ptr()), self._dws.numel(), C.byref(n), C.byref(done),
+                C.c_void_p(dws.data_ptr()), dws.numel(), C.byref(n), C.byref(done),
                 _stream_handle(stream))
         st = call(out)
         if st == E_CAPACITY and not sized:

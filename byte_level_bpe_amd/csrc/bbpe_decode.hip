@@ -8,6 +8,8 @@
 // caller can hold the rest back (a token may end inside a character).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include <algorithm>
 
 #include "../../include/bbpe.h"
@@ -402,6 +404,7 @@ int bbpe_decode_device(bbpe_tokenizer *t, const int32_t *d_ids, uint64_t n_ids, 
                        uint64_t out_capacity, uint64_t *d_tok_off, void *d_ws, uint64_t ws_bytes,
                        uint64_t *out_len, uint64_t *complete_len, void *stream) {
   if (!t || !out_len || (n_ids && !d_ids) || (out_capacity && !d_out)) return BBPE_E_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(t->mu);
   DecStatus h;
   const int rc = decode_run(t, d_ids, n_ids, d_out, out_capacity, d_tok_off, d_ws, ws_bytes, stream, h);
   if (rc) return rc;
@@ -418,6 +421,7 @@ int bbpe_token_offsets_device(bbpe_tokenizer *t, const int32_t *d_ids, uint64_t 
                               uint64_t *d_tok_off, void *d_ws, uint64_t ws_bytes,
                               uint64_t *total_bytes, void *stream) {
   if (!t || !total_bytes || (n_ids && (!d_ids || !d_tok_off))) return BBPE_E_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(t->mu);
   DecStatus h;
   const int rc = decode_run(t, d_ids, n_ids, nullptr, 0, d_tok_off, d_ws, ws_bytes, stream, h);
   if (rc) return rc;

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -242,8 +243,7 @@ int finish(bbpe_tokenizer *t, Launcher &go, const EncodeArgs &a, Status &h) {
   go.collect();
   if (h.pad2) return BBPE_E_INVALID_ARG;
   if (h.err_pos != ~0ull) {
-    t->err_seg = h.err_seg;
-    t->err_byte = h.err_pos;
+    set_last_utf8_error(t, h.err_seg, h.err_pos);
     return BBPE_E_UTF8;
   }
   return BBPE_OK;
@@ -255,6 +255,7 @@ extern "C" {
 
 int bbpe_upload_tables(bbpe_tokenizer *t, void *d_mem, uint64_t bytes, void *stream) {
   if (!t || !d_mem) return BBPE_E_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(t->mu);
   if (bytes < t->layout.total || (reinterpret_cast<uintptr_t>(d_mem) & 255)) return BBPE_E_INVALID_ARG;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   HIP_OK(hipMemcpyAsync(d_mem, t->image.data(), t->layout.total, hipMemcpyHostToDevice, st));
@@ -297,6 +298,8 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
   if (!d_id_off || !n_ids || (ids_cap && !d_ids)) return BBPE_E_INVALID_ARG;
   const bool count_only = (flags & BBPE_COUNT_ONLY) != 0;
   if (count_only) ids_cap = 0;  // k_assemble then copies no ids
+  if (!t) return BBPE_E_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(t->mu);
   EncodeArgs a;
   WsLayout L;
   int rc = prepare(t, d_text, n, d_seg_off, d_allow, n_seg, flags, d_ws, ws_bytes, a, L);
@@ -327,11 +330,15 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
     HIP_OK(hipStreamWaitEvent(aux, static_cast<hipEvent_t>(t->ev_fork), 0));
     go.use(aux);
     // (grid-stride kernels: their units are few, and idle waves of the
-    // second stream take dispatch slots from the short tier)
-    const uint32_t long_grid = uint32_t(std::min<uint64_t>(n / 513 + 1, 64));
-    go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
+    // second stream take dispatch slots from the short tier.)  The group
+    // tier goes first: its one-wave workgroups are placed beside the short
+    // tier's waves at once, while a long-tier workgroup needs a whole CU's
+    // LDS and so waits for the short tier to drain even when it finds no
+    // unit to merge.
     const uint32_t group_grid = uint32_t(std::min<uint64_t>(n / 33 + 1, 4096));
     go("k_merge_group", k_merge_group, dim3(group_grid), dim3(64), a);
+    const uint32_t long_grid = uint32_t(std::min<uint64_t>(n / 513 + 1, 64));
+    go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
     HIP_OK(hipEventRecord(static_cast<hipEvent_t>(t->ev_join), aux));
     go.use(go.st);
     const uint32_t merge_grid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
@@ -356,7 +363,9 @@ int bbpe_pretokenize_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t
                               uint32_t flags, void *d_ws, uint64_t ws_bytes, uint32_t *d_starts,
                               uint64_t starts_cap, uint8_t *d_is_special, uint64_t *n_pieces,
                               void *stream) {
-  if (!n_pieces || (starts_cap && !d_starts) || (flags & BBPE_COUNT_ONLY)) return BBPE_E_INVALID_ARG;
+  if (!t || !n_pieces || (starts_cap && !d_starts) || (flags & BBPE_COUNT_ONLY))
+    return BBPE_E_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(t->mu);
   EncodeArgs a;
   WsLayout L;
   int rc = prepare(t, d_text, n, d_seg_off, d_allow, n_seg, flags, d_ws, ws_bytes, a, L);
@@ -378,13 +387,16 @@ int bbpe_pretokenize_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t
 
 int bbpe_set_timing(bbpe_tokenizer *t, int enable) {
   if (!t) return BBPE_E_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(t->mu);
   t->timing = enable != 0;
   return BBPE_OK;
 }
 
 int bbpe_timing_report(const bbpe_tokenizer *t, uint32_t idx, const char **name, double *total_ms,
                        uint64_t *launches) {
-  if (!t || idx >= t->t_names.size()) return BBPE_E_INVALID_ARG;
+  if (!t) return BBPE_E_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(const_cast<bbpe_tokenizer *>(t)->mu);
+  if (idx >= t->t_names.size()) return BBPE_E_INVALID_ARG;
   if (name) *name = t->t_names[idx].c_str();
   if (total_ms) *total_ms = t->t_ms[idx];
   if (launches) *launches = t->t_launches[idx];
@@ -406,6 +418,7 @@ void bbpe_free(bbpe_tokenizer *t) {
 
 int bbpe_timing_reset(bbpe_tokenizer *t) {
   if (!t) return BBPE_E_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(t->mu);
   for (auto &v : t->t_ms) v = 0.0;
   for (auto &v : t->t_launches) v = 0;
   return BBPE_OK;

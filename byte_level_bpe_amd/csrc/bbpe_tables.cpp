@@ -380,6 +380,22 @@ int collect_specials(const uint8_t *special_bytes, const uint64_t *special_off,
 
 }  // namespace
 
+namespace {
+// per host thread: the handle, segment and byte of its last UTF-8 error
+struct LastUtf8Error {
+  const bbpe_tokenizer *tok = nullptr;
+  uint32_t seg = 0;
+  uint64_t byte = 0;
+};
+thread_local LastUtf8Error t_last_err;
+}  // namespace
+
+void bbpe::set_last_utf8_error(const bbpe_tokenizer *t, uint32_t seg, uint64_t byte) {
+  t_last_err.tok = t;
+  t_last_err.seg = seg;
+  t_last_err.byte = byte;
+}
+
 extern "C" {
 
 int bbpe_load_ranks(const uint8_t *key_bytes, const uint64_t *key_off, const int32_t *ranks,
@@ -479,8 +495,9 @@ int bbpe_decode(const bbpe_tokenizer *t, const int32_t *ids, uint64_t n, uint8_t
 
 int bbpe_error_detail(const bbpe_tokenizer *t, uint32_t *segment, uint64_t *byte_offset) {
   if (!t || !segment || !byte_offset) return BBPE_E_INVALID_ARG;
-  *segment = t->err_seg;
-  *byte_offset = t->err_byte;
+  const bool mine = t_last_err.tok == t;
+  *segment = mine ? t_last_err.seg : 0;
+  *byte_offset = mine ? t_last_err.byte : 0;
   return BBPE_OK;
 }
 

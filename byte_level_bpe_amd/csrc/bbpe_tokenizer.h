@@ -3,6 +3,7 @@
 
 #include <stdint.h>
 
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -40,12 +41,17 @@ struct bbpe_tokenizer {
   // (created at the first encode, on the device current then)
   void *aux_stream = nullptr;
   void *ev_fork = nullptr, *ev_join = nullptr;
-  // last UTF-8 error
-  uint32_t err_seg = 0;
-  uint64_t err_byte = 0;
+  // Every entry point that enqueues work or touches the mutable state above
+  // (second stream, fork/join events, timing records) holds this lock for
+  // the whole call, so that host threads sharing a handle never interleave
+  // their fork/join events or timing records; such calls run one after the
+  // other.
+  std::mutex mu;
 };
 
 namespace bbpe {
+// The calling thread's last BBPE_E_UTF8 on a handle (bbpe_error_detail).
+void set_last_utf8_error(const bbpe_tokenizer *t, uint32_t seg, uint64_t byte);
 // Hash of a host key (same function the kernels apply to text slices).
 uint64_t hash_key(const uint8_t *p, uint32_t len);
 }  // namespace bbpe

@@ -40,7 +40,13 @@
 extern "C" {
 #endif
 
-typedef struct bbpe_tokenizer bbpe_tokenizer; /* opaque; immutable once uploaded */
+/* Opaque handle.  Its tables are immutable once uploaded.  Host threads may
+ * share a handle: every call that enqueues device work or reads or writes
+ * its per-handle state (the second stream and its fork/join events, the
+ * timing records) holds the handle's lock for its whole duration, so such
+ * calls on one handle run one after the other.  For concurrent encodes on
+ * one GPU, give each thread its own handle. */
+typedef struct bbpe_tokenizer bbpe_tokenizer;
 
 enum {
   BBPE_OK = 0,
@@ -62,9 +68,10 @@ enum {
  * o200k"):  [^\r\n\p{L}\p{N}]?+ (U*+ W++ | U++ W*+) (?i:'[sdmt]|'ll|'ve|'re)?+
  * with U = [\p{Lu}\p{Lt}\p{Lm}\p{Lo}\p{M}] and W = [\p{Ll}\p{Lm}\p{Lo}\p{M}],
  * followed by the cl100k clauses from the digit clause on.  R50K_STYLE is
- * the cl100k pattern with r50k's digit clause " ?\p{N}++" (an unbounded
- * digit run with an optional leading space, "r50k, cl100k, o200k") in place
- * of \p{N}{1,3}+; the page names only that change. */
+ * the cl100k pattern with r50k's digit clause " ?\p{N}++" in place of
+ * \p{N}{1,3}+: all the digits of a run form one piece, with no cap on its
+ * length, and a single space right before the run joins it (the same page
+ * and section give only this clause of r50k's pattern). */
 enum { BBPE_GRAMMAR_CL100K = 0, BBPE_GRAMMAR_O200K_STYLE = 1, BBPE_GRAMMAR_R50K_STYLE = 2 };
 
 /* encode flags */
@@ -229,9 +236,10 @@ int bbpe_token_offsets_device(bbpe_tokenizer *tok, const int32_t *d_ids, uint64_
                               uint64_t *d_tok_off, void *d_workspace, uint64_t workspace_bytes,
                               uint64_t *total_bytes, void *hip_stream);
 
-/* Details of the last BBPE_E_UTF8 from bbpe_encode_segments on this handle:
+/* Details of the last BBPE_E_UTF8 that bbpe_encode_segments or
+ * bbpe_pretokenize_segments returned to the calling thread on this handle:
  * the segment index and the absolute byte offset in d_text of the first
- * invalid sequence. */
+ * invalid sequence (0 and 0 when there was none). */
 int bbpe_error_detail(const bbpe_tokenizer *tok, uint32_t *segment, uint64_t *byte_offset);
 
 /* Number of ranks and the largest id (rank or special) of the table. */

@@ -1,32 +1,27 @@
 """Algorithmic bytes of each encode workload, counted by the oracle.
 
-Test infrastructure: run once per workload definition; writes
-``bench_alg_bytes.json`` at the repository root, which bench.py reads.
+Writes ``tests/golden/alg_bytes.json`` (read by bench.py for its roofline
+numbers).  Calls only the oracle; nothing here comes from the GPU.
 
-    python -m oracle.alg_bytes [workload ...]
+    python -m tests.golden.alg_bytes [workload ...]
 
 The method's bytes for one call (tiktoken deep-dive page, "Inside encode"):
-the text, the ids out (4 B each), the segment offsets out (8 B each) and the
-rank lookups of the merge loop (key bytes + a 4-byte rank per lookup, as the
-oracle's instrumented loop counts them).
+the text in, the ids out (4 B each), the segment offsets out (8 B each) and
+the rank lookups of the merge loop, each moving its key bytes and a 4-byte
+rank, as the oracle's instrumented loop counts them over every pre-token.
 
-The same figures split by the GPU kernel that does the work, so that a
-kernel's achieved bandwidth can be stated.  Pieces are cut into merge units
-the way the GPU cuts them: at a position next to a byte >= 0x80, or between
-an ASCII lower-case and upper-case letter, where no key can occur across it
-(the byte pair there occurs inside no key; or, at a character boundary, it
-is no 2-byte key, neither 3-byte window across it is a key and no 4-byte
-window across it has its bit set in the GPU's hashed 4-gram bitmap).  Each unit goes
-to the kernel of its length class:
-
-    k_probe        every unit: its bytes, its start offset and its count
-                   (8 B); a unit of one byte, or a key that merges back to
-                   itself, is settled there with one lookup (key + 4 B).
-    k_merge        units of 2-32 bytes left to merge
-    k_merge_group  units of 33-512 bytes
-    k_merge_long   longer units
-                   each: its bytes, its ids (4 B each) and count (4 B), and
-                   the loop's lookups on the unit.
+The per-kernel figures attribute the same terms to the kernel that settles
+each unit: its bytes (once), 4 B per id it yields and the lookups the merge
+loop makes on it (none for a special).  Units are the pieces cut the way the
+GPU cuts them into independent merge units (a bench-side model of that rule,
+not part of the oracle): at a position next to a byte >= 0x80, or between an
+ASCII lower-case and upper-case letter, where no key can occur across it (the
+byte pair there occurs inside no key; or, at a character boundary, it is no
+2-byte key, neither 3-byte window across it is a key and no 4-byte window
+across it has its bit set in the GPU's hashed 4-gram bitmap).  A unit that is
+a special, a single byte, or a key that the loop merges back into itself is
+settled by k_probe; every other unit goes to the merge kernel of its length
+class (k_merge 2-32 bytes, k_merge_group 33-512, k_merge_long longer).
 """
 from __future__ import annotations
 
@@ -34,17 +29,21 @@ import json
 import os
 import sys
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 sys.path.insert(0, ROOT)
 
 from oracle import Oracle  # noqa: E402
 
-OUT = os.path.join(ROOT, "bench_alg_bytes.json")
+OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "alg_bytes.json")
+
+# the GPU's hash of a 4-byte string into its 2^24-bit 4-gram bitmap
+# (multiplicative hashing with the 32-bit golden-ratio constant)
+_Q4_MUL = 2654435761
 
 
 def q4_index(w4: bytes) -> int:
     x = int.from_bytes(w4, "little")
-    return ((x * 0x9E3779B1) & 0xFFFFFFFF) >> 8
+    return ((x * _Q4_MUL) & 0xFFFFFFFF) >> 8
 
 
 def tier_of(m: int) -> str:
@@ -85,8 +84,9 @@ def count(name: str) -> dict:
     n = w.text_bytes
     n_seg = len(w.segments)
 
-    per = {k: {"units": 0, "bytes": 0} for k in ("k_probe", "k_merge", "k_merge_group", "k_merge_long")}
-    memo = {}  # unit bytes -> (n ids, lookup bytes of the merge loop)
+    per = {k: {"units": 0, "bytes": 0, "ids": 0, "lookup_bytes": 0}
+           for k in ("k_probe", "k_merge", "k_merge_group", "k_merge_long")}
+    memo = {}  # unit bytes -> (ids, lookup bytes of the merge loop)
 
     def merge_cost(u: bytes):
         c = memo.get(u)
@@ -102,9 +102,7 @@ def count(name: str) -> dict:
     bounds = [int(x) for x in starts] + [len(text)]
     for i in range(len(starts)):
         p = text[bounds[i]:bounds[i + 1]]
-        if spec[i]:
-            units = [p]
-        elif p.isascii():
+        if spec[i] or p.isascii():
             units = [p]
         else:
             units, a = [], 0
@@ -115,20 +113,16 @@ def count(name: str) -> dict:
             units.append(p[a:])
         for u in units:
             m = len(u)
-            pr = per["k_probe"]
-            pr["units"] += 1
-            pr["bytes"] += m + 8
-            if spec[i] or m == 1:
-                continue
-            if u in ranks:
-                pr["bytes"] += m + 4
+            if spec[i]:
+                k, lb, where = 1, 0, "k_probe"
+            else:
                 k, lb = merge_cost(u)
-                if k == 1:
-                    continue
-            k, lb = merge_cost(u)
-            t = per[tier_of(m)]
+                where = "k_probe" if k == 1 else tier_of(m)
+            t = per[where]
             t["units"] += 1
-            t["bytes"] += m + 4 * k + 4 + lb
+            t["ids"] += k
+            t["lookup_bytes"] += lb
+            t["bytes"] += m + 4 * k + lb
     return {"bytes": n, "segments": n_seg, "ids": int(len(ids)), "pieces": whole["pieces"],
             "lookups": whole["lookups"], "lookup_bytes": whole["lookup_bytes"],
             "call_bytes": n + 4 * int(len(ids)) + 8 * (n_seg + 1) + whole["lookup_bytes"],

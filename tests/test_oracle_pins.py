@@ -208,6 +208,69 @@ def test_merge_counters_count_pair_lookups():
     assert c["lookups"] == 5 and c["lookup_bytes"] == 5 * 6 and c["pieces"] == 1
 
 
+def _counted(o, piece):
+    o.reset_counters()
+    ids = o.merge(piece)
+    c = o.counters()
+    return ids, c["lookups"], c["lookup_bytes"]
+
+
+# Lookup counts of the "Inside encode" loop worked by hand: m-1 two-byte
+# lookups in the first round, then after each merge the pair to the right of
+# the merged part (when a part follows it) and the pair to its left (when a
+# part precedes it); each lookup moves its key bytes and a 4-byte rank.
+def test_merge_counters_neighbour_recomputes_by_hand():
+    t = atoms_permuted(5)
+    t.update({b"bc": 300, b"ab": 301, b"cd": 302, b"abcd": 303})
+    o = Oracle(t)
+    # ab bc cd (3 x 6 B); merge bc -> a|bc|d: right "bcd" and left "abc"
+    # (2 x 7 B), both absent, stop
+    assert _counted(o, b"abcd") == ([t[b"a"], 300, t[b"d"]], 5, 18 + 14)
+
+    t2 = atoms_permuted(5)
+    t2[b"aa"] = 300
+    o2 = Oracle(t2)
+    # aa aa aa (3 x 6 B); merge at 0 -> aa|a|a: right "aaa" (7 B), no left;
+    # merge at 2 -> aa|aa: no right part, left "aaaa" (8 B)
+    assert _counted(o2, b"aaaa") == ([300, 300], 5, 18 + 7 + 8)
+    # aa aa (2 x 6 B); merge at 0 -> aa|a: right "aaa" (7 B); stop
+    assert _counted(o2, b"aaa") == ([300, t2[b"a"]], 3, 12 + 7)
+
+    t3 = atoms_permuted(5)
+    t3.update({b"ab": 300, b"cd": 301, b"abcd": 302})
+    o3 = Oracle(t3)
+    # ab bc cd (3 x 6 B); merge ab -> ab|c|d: right "abc" (7 B); merge cd ->
+    # ab|cd: no right part, left "abcd" (8 B) = 302; merge -> abcd: no
+    # neighbours, no lookup
+    assert _counted(o3, b"abcd") == ([302], 5, 18 + 7 + 8)
+    # a merge in the middle looks up both neighbours: xaby: xa ab by (3 x 6),
+    # merge ab -> x|ab|y: right "aby" (7), left "xab" (7)
+    assert _counted(o3, b"xaby") == ([t3[b"x"], 300, t3[b"y"]], 5, 18 + 7 + 7)
+    # single bytes and empty pieces perform no lookup
+    assert _counted(o3, b"a")[1:] == (0, 0)
+    assert _counted(o3, b"")[1:] == (0, 0)
+
+
+def test_merge_counters_sum_over_pieces_of_an_encode():
+    """An encode's counters are the sum of its pieces' counters (no lookups for
+    specials, none for the final read-out of each piece)."""
+    t = atoms_permuted(5)
+    t.update({b"ab": 300, b"cd": 301, b"abcd": 302, b" a": 303})
+    o = Oracle(t, [(b"<|x|>", 1000)], 0)
+    text = b"abcd<|x|>xaby abcd"
+    o.reset_counters()
+    o.encode(text, True)
+    c = o.counters()
+    # pieces "abcd", the special, "xaby", " abcd".  " abcd" by hand: " a" ab
+    # bc cd (4 x 6 B); merge ab (300): right "abc", left " ab" (2 x 7 B);
+    # merge cd (301): no right part, left "abcd" (8 B) = 302; merge abcd:
+    # no right part, left " abcd" (9 B); stop: 8 lookups, 55 B
+    assert _counted(o, b"abcd")[1:] == (5, 33)
+    assert _counted(o, b"xaby")[1:] == (5, 32)
+    assert _counted(o, b" abcd") == ([t[b" "], 302], 8, 24 + 14 + 8 + 9)
+    assert (c["lookups"], c["lookup_bytes"], c["pieces"]) == (5 + 5 + 8, 33 + 32 + 55, 3)
+
+
 # -------------------------------------------------------------- specials ----
 
 def test_specials_allowed_and_not(tiny_workload):
