@@ -88,26 +88,72 @@ def algorithmic_bytes(kernel: str, w: dict) -> int:
     return n
 
 
+def host_cpu() -> dict:
+    """The host the oracle runs on: logical CPUs, the CPUs this process may
+    use, and the CPU model."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "usable": len(os.sched_getaffinity(0)), "model": model}
+
+
+def ids_sha256(ids) -> str:
+    import hashlib
+    return hashlib.sha256(np.ascontiguousarray(ids, dtype=np.int32).tobytes()).hexdigest()
+
+
 def cpu_baseline(w, budget_s: float = 10.0, max_reps: int = 200) -> dict:
-    """The oracle (plain single-threaded C++) over the whole workload,
-    repeated until about budget_s seconds of CPU work."""
+    """The oracle (plain C++, -O2) on the host cores, reported beside the GPU.
+
+    Row 1: single-threaded, pinned to one core (sched_setaffinity, as
+    taskset does), over the whole workload, repeated until about budget_s
+    seconds.  Row 2: the same oracle over the workload's independent units
+    (segments and 400,000-character windows) on K std::threads, K = the
+    usable cores (at most 16), repeated until about budget_s / 2 seconds.
+    Each row gives the SHA-256 of its ids."""
     from oracle import Oracle
+    from oracle.oracle import encode_parallel, window_units
     orc = Oracle(w.tokens, w.specials, w.grammar)
-    reps = 0
-    total = 0.0
-    n_ids = 0
-    while reps < max_reps and (total < budget_s or reps == 0):
-        t0 = time.perf_counter()
-        ids, _ = orc.encode_segments(w.segments, w.tiktoken_safe)
-        total += time.perf_counter() - t0
-        n_ids = len(ids)
-        reps += 1
+    cpus = sorted(os.sched_getaffinity(0))
+    reps, total, ids = 0, 0.0, None
+    os.sched_setaffinity(0, {cpus[-1]})
+    try:
+        while reps < max_reps and (total < budget_s or reps == 0):
+            t0 = time.perf_counter()
+            ids, _ = orc.encode_segments(w.segments, w.tiktoken_safe)
+            total += time.perf_counter() - t0
+            reps += 1
+    finally:
+        os.sched_setaffinity(0, set(cpus))
     nb = w.text_bytes
+    k = min(16, len(cpus))
+    pool = [Oracle(w.tokens, w.specials, w.grammar) for _ in range(k)]
+    preps, ptotal, pids = 0, 0.0, None
+    while preps < max_reps and (ptotal < budget_s / 2 or preps == 0):
+        pids, sec = encode_parallel(pool, w.segments, w.tiktoken_safe)
+        ptotal += sec
+        preps += 1
+    n_units = len(window_units(w.segments, w.tiktoken_safe)[0]) - 1
+    host = host_cpu()
     return {"value": round(nb * reps / total / 1e6, 3), "unit": "MB/s", "cores": 1,
             "kind": "oracle",
-            "tokens_per_s": round(n_ids * reps / total, 1),
-            "sample": "whole %s workload (%d bytes) encoded %d times single-threaded, %.1f s"
-                      % (w.name, nb, reps, total)}
+            "tokens_per_s": round(len(ids) * reps / total, 1),
+            "ids_sha256": ids_sha256(ids),
+            "sample": "whole %s workload (%d bytes) encoded %d times on one pinned core, %.1f s"
+                      % (w.name, nb, reps, total),
+            "host": host,
+            "all_cores": {"value": round(nb * preps / ptotal / 1e6, 3), "unit": "MB/s",
+                          "cores": k, "units": n_units,
+                          "tokens_per_s": round(len(pids) * preps / ptotal, 1),
+                          "ids_sha256": ids_sha256(pids),
+                          "sample": "whole workload as %d independent units on %d std::threads, "
+                                    "%d times, %.1f s" % (n_units, k, preps, ptotal)}}
 
 
 def decode_alg_bytes(kernel: str, n_ids: int, n_bytes: int) -> int:
@@ -268,6 +314,10 @@ def main():
     rep = tok.timing_report()
     tok.set_timing(False)
 
+    # ids of the last timed call, checked outside the timed region against
+    # the oracle's (SHA-256 stored by tests/golden/alg_bytes.py)
+    gpu_sha = ids_sha256(ids[:n_ids].cpu().numpy())
+
     ms_per_step = wall * 1e3 / args.steps
     mbs = total * args.steps / wall / 1e6
     tps = n_ids * args.steps / wall
@@ -346,9 +396,13 @@ def main():
                      "traffic": measured_traffic(args.workload, dom), "avg_ms": round(dom_ms, 5),
                      "alg_bytes_per_launch": dom_bytes},
         "kernels_avg_ms": {k: round(v, 5) for k, v in sorted(per_kernel.items(), key=lambda kv: -kv[1])},
+        "ids_sha256": gpu_sha,
+        "ids_match_oracle": gpu_sha == alg.get("ids_sha256"),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
+        out["ids_match_oracle"] = (out["ids_match_oracle"] and
+                                   out["cpu_baseline"]["ids_sha256"] == gpu_sha)
     print(json.dumps(out), flush=True)
 
 

@@ -11,13 +11,17 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 SRC = os.path.join(HERE, "bbpe_oracle.cpp")
+# the CPU baseline's multi-core driver (std::thread over independent units);
+# it only calls oracle_encode
+SRC_MT = os.path.join(HERE, "parallel_runner.cpp")
 
 
 def build() -> str:
-    """Compile the oracle with g++ -O2 (single-threaded, plain C++17)."""
+    """Compile the oracle with g++ -O2 (plain C++17; each encode call is
+    single-threaded), with the multi-core baseline driver beside it."""
     tmp = LIB_PATH + ".tmp"
-    subprocess.check_call(["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-o", tmp, SRC],
-                          cwd=HERE)
+    subprocess.check_call(["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-pthread", "-o", tmp,
+                           SRC, SRC_MT], cwd=HERE)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
@@ -50,6 +54,9 @@ def _load():
         lib.oracle_merge.argtypes = [P, P, C.c_uint64, P, C.c_uint64, P]
         lib.oracle_decode.restype = C.c_int
         lib.oracle_decode.argtypes = [P, P, C.c_uint64, P, C.c_uint64, P]
+        lib.oracle_encode_units_mt.restype = C.c_int
+        lib.oracle_encode_units_mt.argtypes = [P, C.c_int, P, P, P, C.c_uint32, C.c_int, P,
+                                               C.c_uint64, P, P]
         _lib = lib
     return _lib
 
@@ -252,3 +259,44 @@ def utf8_complete_len(data: bytes) -> int:
         if len(data) >= k and data[-k:] in p:
             return len(data) - k
     return len(data)
+
+
+def window_units(segments, tiktoken_safe: bool = True, window_chars: int = 400_000):
+    """Independent units of a workload: each segment, cut (with tiktoken-safe
+    chunking) at every 400,000th character, since each such window is
+    encoded as its own text.  Returns (unit byte offsets into the
+    concatenated text, allow flag per unit)."""
+    offs, allow = [0], []
+    base = 0
+    for seg, a in segments:
+        cuts = []
+        if tiktoken_safe and len(seg) > window_chars:
+            b = np.frombuffer(seg, dtype=np.uint8)
+            lead = np.nonzero((b & 0xC0) != 0x80)[0]  # first byte of every character
+            cuts = [int(lead[k]) for k in range(window_chars, len(lead), window_chars)]
+        for c in cuts + [len(seg)]:
+            offs.append(base + c)
+            allow.append(1 if a else 0)
+        base += len(seg)
+    return np.array(offs, dtype=np.uint64), np.array(allow or [0], dtype=np.uint8)
+
+
+def encode_parallel(oracles, segments, tiktoken_safe: bool = True):
+    """The oracle over the workload's independent units on len(oracles)
+    std::threads (one oracle each).  Returns (ids, seconds of the threaded
+    section)."""
+    lib = _load()
+    text = b"".join(s for s, _ in segments)
+    tarr = np.frombuffer(text or b"\0", dtype=np.uint8)
+    off, allow = window_units(segments, tiktoken_safe)
+    hs = (C.c_void_p * len(oracles))(*[o._h for o in oracles])
+    cap = max(1, len(text))
+    ids = np.empty(cap, dtype=np.int32)
+    n = C.c_uint64(0)
+    sec = C.c_double(0.0)
+    st = lib.oracle_encode_units_mt(hs, len(oracles), _ptr(tarr), _ptr(off), _ptr(allow),
+                                    len(off) - 1, 1 if tiktoken_safe else 0, _ptr(ids), cap,
+                                    C.byref(n), C.byref(sec))
+    if st != 0:
+        raise OracleError(st, "parallel encode")
+    return ids[:n.value].copy(), sec.value

@@ -123,7 +123,10 @@ def count(name: str) -> dict:
             t["ids"] += k
             t["lookup_bytes"] += lb
             t["bytes"] += m + 4 * k + lb
-    return {"bytes": n, "segments": n_seg, "ids": int(len(ids)), "pieces": whole["pieces"],
+    import hashlib
+    sha = hashlib.sha256(ids.astype("<i4").tobytes()).hexdigest()
+    return {"bytes": n, "segments": n_seg, "ids": int(len(ids)), "ids_sha256": sha,
+            "pieces": whole["pieces"],
             "lookups": whole["lookups"], "lookup_bytes": whole["lookup_bytes"],
             "call_bytes": n + 4 * int(len(ids)) + 8 * (n_seg + 1) + whole["lookup_bytes"],
             "kernels": per}
