@@ -249,6 +249,83 @@ int finish(bbpe_tokenizer *t, Launcher &go, const EncodeArgs &a, Status &h) {
   return BBPE_OK;
 }
 
+// The encode sequence of both encode entry points.  fork: run the group and
+// long tiers on the handle's second stream beside the short tier (creating
+// it on first use); otherwise everything goes on the caller's stream, and
+// no stream, event or memory is created.
+int encode_impl(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t *d_seg_off,
+                const uint8_t *d_allow, uint32_t n_seg, uint32_t flags, void *d_ws,
+                uint64_t ws_bytes, int32_t *d_ids, uint64_t ids_cap, int64_t *d_id_off,
+                uint64_t *n_ids, void *stream, bool fork) {
+  const bool count_only = (flags & BBPE_COUNT_ONLY) != 0;
+  if (count_only) ids_cap = 0;  // k_assemble then copies no ids
+  EncodeArgs a;
+  WsLayout L;
+  int rc = prepare(t, d_text, n, d_seg_off, d_allow, n_seg, flags, d_ws, ws_bytes, a, L);
+  if (rc) return rc;
+  a.ids = d_ids;
+  a.ids_cap = ids_cap;
+  a.id_off = d_id_off;
+  a.merge_units = 1;
+  if (fork) {
+    rc = ensure_aux(t);
+    if (rc) return rc;
+  }
+  Launcher go{t, reinterpret_cast<hipStream_t>(stream)};
+  go.allow_timing = fork;
+  launch_front(go, a, L);
+  const uint32_t seg_grid = std::min<uint32_t>(1024, (n_seg + 256) / 256);
+  if (n == 0) {
+    go("k_zero_offsets", k_zero_offsets, dim3(seg_grid), dim3(256), a);
+  } else {
+    if (n < PROBE_SMALL) {
+      const uint32_t probe_grid = uint32_t((n + 2047) / 2048);
+      go("k_probe", k_probe1, dim3(probe_grid), dim3(PROBE_BLOCK), a);
+    } else {
+      const uint32_t probe_grid = uint32_t(std::min<uint64_t>((n + 8191) / 8192, 8192));
+      go("k_probe", k_probe, dim3(probe_grid), dim3(PROBE_BLOCK), a);
+    }
+    // (grid-stride kernels: their units are few, and idle waves of the
+    // second stream take dispatch slots from the short tier.)
+    const uint32_t group_grid = uint32_t(std::min<uint64_t>(n / 33 + 1, 4096));
+    const uint32_t long_grid = uint32_t(std::min<uint64_t>(n / 513 + 1, 64));
+    const uint32_t merge_grid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
+    if (fork) {
+      // the group and long tiers (few units, long dependent chains) run on
+      // the second stream beside the short tier.  The group tier goes
+      // first: its one-wave workgroups are placed beside the short tier's
+      // waves at once, while a long-tier workgroup needs a whole CU's LDS
+      // and so waits for the short tier to drain even when it finds no unit
+      // to merge.
+      hipStream_t aux = static_cast<hipStream_t>(t->aux_stream);
+      HIP_OK(hipEventRecord(static_cast<hipEvent_t>(t->ev_fork), go.st));
+      HIP_OK(hipStreamWaitEvent(aux, static_cast<hipEvent_t>(t->ev_fork), 0));
+      go.use(aux);
+      go("k_merge_group", k_merge_group, dim3(group_grid), dim3(64), a);
+      go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
+      HIP_OK(hipEventRecord(static_cast<hipEvent_t>(t->ev_join), aux));
+      go.use(go.st);
+      go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
+      HIP_OK(hipStreamWaitEvent(go.st, static_cast<hipEvent_t>(t->ev_join), 0));
+    } else {
+      go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
+      go("k_merge_group", k_merge_group, dim3(group_grid), dim3(64), a);
+      go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
+    }
+    const uint32_t nscan = uint32_t((n + 1 + 4095) / 4096);
+    go("k_scan_reduce", k_scan_reduce, dim3(nscan), dim3(256), a);
+    go("k_scan_down", k_scan_down, dim3(nscan), dim3(256), a);
+    const uint32_t agrid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
+    go("k_assemble", k_assemble, dim3(agrid), dim3(256), a);
+  }
+  Status h{};
+  rc = finish(t, go, a, h);
+  if (rc) return rc;
+  *n_ids = h.n_ids;
+  if (h.n_ids > ids_cap && !count_only) return BBPE_E_CAPACITY;
+  return BBPE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,67 +372,10 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
                          const uint64_t *d_seg_off, const uint8_t *d_allow, uint32_t n_seg,
                          uint32_t flags, void *d_ws, uint64_t ws_bytes, int32_t *d_ids,
                          uint64_t ids_cap, int64_t *d_id_off, uint64_t *n_ids, void *stream) {
-  if (!d_id_off || !n_ids || (ids_cap && !d_ids)) return BBPE_E_INVALID_ARG;
-  const bool count_only = (flags & BBPE_COUNT_ONLY) != 0;
-  if (count_only) ids_cap = 0;  // k_assemble then copies no ids
-  if (!t) return BBPE_E_INVALID_ARG;
+  if (!t || !d_id_off || !n_ids || (ids_cap && !d_ids)) return BBPE_E_INVALID_ARG;
   std::lock_guard<std::mutex> lock(t->mu);
-  EncodeArgs a;
-  WsLayout L;
-  int rc = prepare(t, d_text, n, d_seg_off, d_allow, n_seg, flags, d_ws, ws_bytes, a, L);
-  if (rc) return rc;
-  a.ids = d_ids;
-  a.ids_cap = ids_cap;
-  a.id_off = d_id_off;
-  a.merge_units = 1;
-  rc = ensure_aux(t);
-  if (rc) return rc;
-  Launcher go{t, reinterpret_cast<hipStream_t>(stream)};
-  launch_front(go, a, L);
-  const uint32_t seg_grid = std::min<uint32_t>(1024, (n_seg + 256) / 256);
-  if (n == 0) {
-    go("k_zero_offsets", k_zero_offsets, dim3(seg_grid), dim3(256), a);
-  } else {
-    if (n < PROBE_SMALL) {
-      const uint32_t probe_grid = uint32_t((n + 2047) / 2048);
-      go("k_probe", k_probe1, dim3(probe_grid), dim3(PROBE_BLOCK), a);
-    } else {
-      const uint32_t probe_grid = uint32_t(std::min<uint64_t>((n + 8191) / 8192, 8192));
-      go("k_probe", k_probe, dim3(probe_grid), dim3(PROBE_BLOCK), a);
-    }
-    // the group and long tiers (few units, long dependent chains) run on the
-    // second stream beside the short tier
-    hipStream_t aux = static_cast<hipStream_t>(t->aux_stream);
-    HIP_OK(hipEventRecord(static_cast<hipEvent_t>(t->ev_fork), go.st));
-    HIP_OK(hipStreamWaitEvent(aux, static_cast<hipEvent_t>(t->ev_fork), 0));
-    go.use(aux);
-    // (grid-stride kernels: their units are few, and idle waves of the
-    // second stream take dispatch slots from the short tier.)  The group
-    // tier goes first: its one-wave workgroups are placed beside the short
-    // tier's waves at once, while a long-tier workgroup needs a whole CU's
-    // LDS and so waits for the short tier to drain even when it finds no
-    // unit to merge.
-    const uint32_t group_grid = uint32_t(std::min<uint64_t>(n / 33 + 1, 4096));
-    go("k_merge_group", k_merge_group, dim3(group_grid), dim3(64), a);
-    const uint32_t long_grid = uint32_t(std::min<uint64_t>(n / 513 + 1, 64));
-    go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
-    HIP_OK(hipEventRecord(static_cast<hipEvent_t>(t->ev_join), aux));
-    go.use(go.st);
-    const uint32_t merge_grid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
-    go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
-    HIP_OK(hipStreamWaitEvent(go.st, static_cast<hipEvent_t>(t->ev_join), 0));
-    const uint32_t nscan = uint32_t((n + 1 + 4095) / 4096);
-    go("k_scan_reduce", k_scan_reduce, dim3(nscan), dim3(256), a);
-    go("k_scan_down", k_scan_down, dim3(nscan), dim3(256), a);
-    const uint32_t agrid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
-    go("k_assemble", k_assemble, dim3(agrid), dim3(256), a);
-  }
-  Status h{};
-  rc = finish(t, go, a, h);
-  if (rc) return rc;
-  *n_ids = h.n_ids;
-  if (h.n_ids > ids_cap && !count_only) return BBPE_E_CAPACITY;
-  return BBPE_OK;
+  return encode_impl(t, d_text, n, d_seg_off, d_allow, n_seg, flags, d_ws, ws_bytes, d_ids,
+                     ids_cap, d_id_off, n_ids, stream, true);
 }
 
 int bbpe_pretokenize_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,

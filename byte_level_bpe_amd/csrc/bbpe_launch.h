@@ -23,6 +23,7 @@ struct Launcher {
   bbpe_tokenizer *t;
   hipStream_t st;
   hipStream_t cur = st;
+  bool allow_timing = true;  // false: never record events, even with timing on
   std::vector<std::pair<int, size_t>> recs;  // (kernel index, first event)
   size_t next = 0;
 
@@ -44,7 +45,7 @@ struct Launcher {
   }
   template <typename K, typename... A>
   void operator()(const char *name, K kernel, dim3 grid, dim3 block, A... args) {
-    const bool timed = t->timing;
+    const bool timed = t->timing && allow_timing;
     if (timed) (void)hipEventRecord(event(next), cur);
     hipLaunchKernelGGL(kernel, grid, block, 0, cur, args...);
     if (timed) {
