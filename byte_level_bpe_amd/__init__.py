@@ -35,10 +35,12 @@ GRAMMAR_O200K_STYLE = 1
 GRAMMAR_R50K_STYLE = 2
 TIKTOKEN_SAFE = 1
 COUNT_ONLY = 2
+NOALLOC_SCRATCH_BYTES = 48 << 20  # BBPE_NOALLOC_SCRATCH_BYTES
 
 # every symbol include/bbpe.h declares
 EXPORTS = ["bbpe_load_ranks", "bbpe_load_ranks_tiktoken_file", "bbpe_upload_tables",
-           "bbpe_workspace_bytes", "bbpe_encode_segments", "bbpe_pretokenize_segments",
+           "bbpe_workspace_bytes", "bbpe_encode_segments", "bbpe_encode_segments_noalloc",
+           "bbpe_pretokenize_segments",
            "bbpe_decode", "bbpe_decode_workspace_bytes", "bbpe_decode_device",
            "bbpe_token_offsets_device", "bbpe_error_detail",
            "bbpe_table_info", "bbpe_set_timing", "bbpe_timing_report", "bbpe_timing_reset",
@@ -73,6 +75,9 @@ def _load():
         lib.bbpe_encode_segments.restype = I
         lib.bbpe_encode_segments.argtypes = [P, P, U64, P, P, U32, U32, P, U64, P, U64, P,
                                              C.POINTER(U64), P]
+        lib.bbpe_encode_segments_noalloc.restype = I
+        lib.bbpe_encode_segments_noalloc.argtypes = [P, P, U64, P, P, U32, U32, P, U64, P,
+                                                     C.POINTER(U64), P]
         lib.bbpe_pretokenize_segments.restype = I
         lib.bbpe_pretokenize_segments.argtypes = [P, P, U64, P, P, U32, U32, P, U64, P, U64, P,
                                                   C.POINTER(U64), P]
@@ -245,6 +250,32 @@ class Tokenizer:
             raise err
         if st:
             raise BBPEError(st, "encode_segments")
+        if count_only:
+            return None, id_off, n.value
+        return ids[:n.value], id_off, n.value
+
+    def encode_device_noalloc(self, text, seg_off, allow, total_bytes: int,
+                              tiktoken_safe: bool = True, ids=None, id_off=None, stream=None,
+                              count_only: bool = False):
+        """encode_device through bbpe_encode_segments_noalloc: no workspace
+        (the library's static device array is used).  ids and id_off should
+        be given by callers that must not allocate."""
+        import torch
+        self.upload(text.device)
+        n_seg = int(seg_off.numel()) - 1
+        if ids is None and not count_only:
+            ids = torch.empty(max(1, total_bytes), dtype=torch.int32, device=text.device)
+        if id_off is None:
+            id_off = torch.empty(n_seg + 1, dtype=torch.int64, device=text.device)
+        flags = (TIKTOKEN_SAFE if tiktoken_safe else 0) | (COUNT_ONLY if count_only else 0)
+        n = C.c_uint64(0)
+        st = _load().bbpe_encode_segments_noalloc(
+            self._h, C.c_void_p(text.data_ptr()), int(total_bytes), C.c_void_p(seg_off.data_ptr()),
+            C.c_void_p(allow.data_ptr()), n_seg, flags,
+            None if count_only else C.c_void_p(ids.data_ptr()), 0 if count_only else ids.numel(),
+            C.c_void_p(id_off.data_ptr()), C.byref(n), _stream_handle(stream))
+        if st:
+            raise BBPEError(st, "encode_segments_noalloc")
         if count_only:
             return None, id_off, n.value
         return ids[:n.value], id_off, n.value

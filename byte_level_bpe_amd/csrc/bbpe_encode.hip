@@ -16,6 +16,13 @@
 
 using namespace bbpe;
 
+// Device scratch of bbpe_encode_segments_noalloc: the workspace of that
+// entry point, a file-scope array of BBPE_NOALLOC_SCRATCH_BYTES bytes.  Each
+// GPU the library runs on holds its own copy until the process ends.  Host
+// code never uses this name as an address: the device address of each
+// GPU's copy comes from hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) uint8_t scratch[BBPE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -326,6 +333,26 @@ int encode_impl(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint
   return BBPE_OK;
 }
 
+constexpr int kMaxDevices = 64;
+// One no-alloc encode at a time in this process: the calls share each GPU's
+// scratch array (a call on another device waits too; it is short).
+std::mutex g_noalloc_mu;
+void *g_scratch_addr[kMaxDevices] = {};  // device address of `scratch`, per device
+
+// The current device's address of `scratch`, looked up once per device
+// (with that device current) and kept.  Caller holds g_noalloc_mu.
+int scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BBPE_E_HIP;
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BBPE_E_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return BBPE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -376,6 +403,25 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
   std::lock_guard<std::mutex> lock(t->mu);
   return encode_impl(t, d_text, n, d_seg_off, d_allow, n_seg, flags, d_ws, ws_bytes, d_ids,
                      ids_cap, d_id_off, n_ids, stream, true);
+}
+
+int bbpe_encode_segments_noalloc(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
+                                 const uint64_t *d_seg_off, const uint8_t *d_allow,
+                                 uint32_t n_seg, uint32_t flags, int32_t *d_ids, uint64_t ids_cap,
+                                 int64_t *d_id_off, uint64_t *n_ids, void *stream) {
+  if (!t || !d_id_off || !n_ids || (ids_cap && !d_ids)) return BBPE_E_INVALID_ARG;
+  if (n >= (uint64_t(1) << 32) - 64) return BBPE_E_INVALID_ARG;
+  // every workspace region is written before it is read within a call, so
+  // the array needs no clearing between calls
+  const uint64_t need = layout_for(n, n_seg).total;
+  if (need > BBPE_NOALLOC_SCRATCH_BYTES) return BBPE_E_WORKSPACE;
+  std::lock_guard<std::mutex> g(g_noalloc_mu);
+  void *ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lock(t->mu);
+  return encode_impl(t, d_text, n, d_seg_off, d_allow, n_seg, flags, ws,
+                     BBPE_NOALLOC_SCRATCH_BYTES, d_ids, ids_cap, d_id_off, n_ids, stream, false);
 }
 
 int bbpe_pretokenize_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,

@@ -174,6 +174,26 @@ int bbpe_encode_segments(bbpe_tokenizer *tok, const uint8_t *d_text, uint64_t to
                          uint64_t ids_capacity, int64_t *d_id_off, uint64_t *n_ids,
                          void *hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * bbpe_encode_segments without a workspace argument.  Same arguments
+ * (d_workspace and workspace_bytes aside), results, errors and
+ * synchronisation.  Its workspace is a static device array of
+ * BBPE_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held
+ * from the library's first use of that GPU until the process ends; the
+ * call allocates nothing and creates no stream or event, and runs every
+ * kernel on hip_stream (which must belong to the current device).  Texts
+ * whose workspace (bbpe_workspace_bytes) exceeds the array -- about
+ * 1.2 MB of text -- return BBPE_E_WORKSPACE.  All calls of this entry
+ * point in one process share the array and run one at a time (a lock);
+ * calls from other processes use their own copy. */
+#define BBPE_NOALLOC_SCRATCH_BYTES (48ull << 20)
+int bbpe_encode_segments_noalloc(bbpe_tokenizer *tok, const uint8_t *d_text,
+                                 uint64_t total_bytes, const uint64_t *d_seg_off,
+                                 const uint8_t *d_allow_special, uint32_t n_seg, uint32_t flags,
+                                 int32_t *d_ids, uint64_t ids_capacity, int64_t *d_id_off,
+                                 uint64_t *n_ids, void *hip_stream);
+
 /* Pre-tokenization only: the same segment handling, chunking, special pass
  * and split as bbpe_encode_segments, without merging.  Writes the byte offset
  * (into d_text) of every piece in text order to d_starts (device, uint32,
