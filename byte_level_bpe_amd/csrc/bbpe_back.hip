@@ -378,6 +378,23 @@ __device__ __forceinline__ uint32_t merge_short(const DevTables &T, const int32_
 }
 
 // ---------------------------------------------------------------------------
+// Word cache of one call.  Units with equal bytes merge to equal ids (the
+// merge of a unit depends on its bytes alone), so of all the units of 2-16
+// bytes with one byte string only one, its leader, runs the merge loop; the
+// others follow it.  k_probe stores each such unit's index in the slot
+// chosen by a hash of its bytes (plain stores: the last one wins).  The
+// leader of a byte string is the unit its slot holds if that unit has the
+// same bytes; otherwise every unit with the string leads itself.  Every
+// unit of one byte string reads the same slot, so they all agree on it, and
+// the leader finds itself there.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t owner_slot(uint64_t h, uint32_t mask) {
+  return uint32_t(h >> 40) & mask;
+}
+// largest unit index a follower can record (UID_FOLLOW - j must be an int32)
+constexpr uint32_t FOLLOW_MAX = uint32_t(UID_FOLLOW - INT32_MIN);
+
+// ---------------------------------------------------------------------------
 // Probe pass: one thread per unit.
 // ---------------------------------------------------------------------------
 constexpr uint32_t WNS = 8;                // positions per lane in the group tiers
@@ -423,6 +440,9 @@ __device__ __forceinline__ void probe_body(const EncodeArgs &a) {
   __shared__ uint32_t s_list[PROBE_CHUNK];
   __shared__ int32_t s_atom[256];
   if (threadIdx.x < 256) s_atom[threadIdx.x] = T.atom[threadIdx.x];
+  // the tile states of k_assemble's scan start unpublished
+  for (uint32_t k = blockIdx.x * PROBE_BLOCK + threadIdx.x; k <= P / ASM_UNITS; k += gridDim.x * PROBE_BLOCK)
+    a.ws.scan_state[k] = 0ull;
   __syncthreads();
   for (uint32_t b = blockIdx.x * PROBE_CHUNK; b < P; b += gridDim.x * PROBE_CHUNK) {
     uint32_t idx[PROBE_U], s0[PROBE_U], m[PROBE_U];
@@ -478,10 +498,9 @@ __device__ __forceinline__ void probe_body(const EncodeArgs &a) {
         if (r != RANK_NONE && (meta & META_SELF)) id = r;
         else cls[u] = mm <= 128 ? ML_G128 : mm <= 256 ? ML_G256 : mm <= WAVE_MAX ? ML_G512 : ML_LONG;
       }
-      if (id >= 0) {
-        a.ws.tmp_ids[s] = id;
-        a.ws.piece_cnt[idx[u]] = 1;
-      }
+      a.ws.uid[idx[u]] = id >= 0 ? id : UID_MERGED;
+      if (a.word_cache && cls[u] >= 0 && cls[u] <= int(ML_16))  // this unit under its hash
+        a.ws.owner[owner_slot(h[u], a.owner_mask)] = idx[u];
     }
     if (threadIdx.x < ML_COUNT) {
       s_cnt[threadIdx.x] = 0;
@@ -775,42 +794,142 @@ __device__ __forceinline__ void merge_short_unit(const EncodeArgs &a, const int3
   a.ws.piece_cnt[i] = merge_short<SK>(a.T, atom, u, m, lp, a.ws.tmp_ids + s);
 }
 
-// Merge of the short units: chunks of 64 units of one length class (one
-// lane each, positions in registers sized to the class, so that a wave's
-// rounds and its per-round work follow its longest unit), longest class
-// first.  Wave w takes items w, w + G, w + 2G, ... (G waves in the grid).
-// The item index is wave-uniform by construction: no lane-0 ticket and
-// broadcast, which lets the compiler split the loop per lane.  Three waves
-// per SIMD: the register tiers fit in 168 VGPRs without spilling.
+// Short-tier work item with the word cache: list entries first .. first +
+// 64 K - 1 of one class of 2-16 bytes, K per lane.  The election of all K
+// entries runs with their loads issued side by side (the entries, their
+// offsets and bytes, their slots, the slot units' offsets and bytes); a unit
+// that follows another records it (uid) and is done; the leaders are packed
+// into a queue in LDS and merged 64 at a time, one lane each.
+template <int SK, uint32_t K, bool ELECT>
+__device__ __forceinline__ void merge_short_item(const EncodeArgs &a, uint32_t P, const int32_t *atom,
+                                                 const PartCol &lp, uint32_t *queue,
+                                                 const uint32_t *list, uint32_t count,
+                                                 uint32_t first, int lane) {
+  if (!ELECT) {  // every entry merges itself, one lane each
+#pragma unroll
+    for (uint32_t k = 0; k < K; ++k) {
+      const uint32_t x = first + 64 * k + uint32_t(lane);
+      if (x < count) merge_short_unit<SK>(a, atom, list[x], lp);
+    }
+    return;
+  }
+  uint32_t idx[K], s0[K], m[K], own[K], js[K], jm[K];
+  bool in[K], other[K];
+  UnitBytes<SK> u[K], v[K];
+#pragma unroll
+  for (uint32_t k = 0; k < K; ++k) {
+    const uint32_t x = first + 64 * k + uint32_t(lane);
+    in[k] = x < count;
+    idx[k] = in[k] ? list[x] : 0u;
+  }
+#pragma unroll
+  for (uint32_t k = 0; k < K; ++k) {
+    s0[k] = in[k] ? a.ws.piece_start[idx[k]] : 0u;
+    m[k] = in[k] ? a.ws.piece_start[idx[k] + 1] - s0[k] : 0u;
+  }
+#pragma unroll
+  for (uint32_t k = 0; k < K; ++k) load_unit(a.text, a.n, s0[k], m[k], u[k]);
+#pragma unroll
+  for (uint32_t k = 0; k < K; ++k) {
+    uint64_t h, k8, k8b;
+    unit_hash(u[k], 0, max(m[k], 1u), h, k8, k8b);
+    own[k] = in[k] ? a.ws.owner[owner_slot(h, a.owner_mask)] : 0u;
+  }
+#pragma unroll
+  for (uint32_t k = 0; k < K; ++k) {
+    other[k] = in[k] && own[k] != idx[k] && own[k] < P && own[k] <= FOLLOW_MAX;
+    js[k] = other[k] ? a.ws.piece_start[own[k]] : 0u;
+    jm[k] = other[k] ? a.ws.piece_start[own[k] + 1] - js[k] : 0u;
+  }
+#pragma unroll
+  for (uint32_t k = 0; k < K; ++k) {
+    other[k] = other[k] && jm[k] == m[k];
+    load_unit(a.text, a.n, js[k], other[k] ? m[k] : 0u, v[k]);
+  }
+  uint32_t nq = 0;  // leaders queued (the same in every lane)
+#pragma unroll
+  for (uint32_t k = 0; k < K; ++k) {
+    const bool follow = other[k] && v[k] == u[k];
+    if (follow) a.ws.uid[idx[k]] = UID_FOLLOW - int32_t(own[k]);
+    const bool lead = in[k] && !follow;
+    const unsigned long long b = __ballot(lead);
+    if (lead) queue[nq + uint32_t(__popcll(b & ((1ull << lane) - 1)))] = idx[k];
+    nq += uint32_t(__popcll(b));
+  }
+  __syncthreads();  // (one wave: orders the queue's writes before its reads)
+  for (uint32_t q = 0; q < nq; q += 64) {
+    const uint32_t x = q + uint32_t(lane);
+    if (x < nq) merge_short_unit<SK>(a, atom, queue[x], lp);
+  }
+  __syncthreads();  // the queue is rewritten by the next item
+}
+
+// Merge of the units of 2-16 bytes: work items of list entries of one
+// length class (256 with the word cache, else 64), longest class first; the register
+// tiers follow the class, so that a wave's rounds and its per-round work
+// follow its longest unit.  Wave w takes items w, w + G, w + 2G, ... (G
+// waves in the grid).  The item index is wave-uniform by construction: no
+// lane-0 ticket and broadcast, which lets the compiler split the loop per
+// lane.
+constexpr uint32_t SHORT_K = 4;  // chunks of 64 entries per item
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge(EncodeArgs a) {
   if (a.ws.status->pad2) return;
   const Status *st = a.ws.status;
   const int lane = int(threadIdx.x);
-  const uint32_t n32 = st->n_list[ML_32], n16 = st->n_list[ML_16], n8 = st->n_list[ML_8],
-                 n4 = st->n_list[ML_4];
-  const uint32_t e32 = (n32 + 63) / 64, e16 = e32 + (n16 + 63) / 64, e8 = e16 + (n8 + 63) / 64,
-                 e4 = e8 + (n4 + 63) / 64;
+  const uint32_t P = uint32_t(st->n_pieces);
+  const uint32_t n16 = st->n_list[ML_16], n8 = st->n_list[ML_8], n4 = st->n_list[ML_4];
+  // entries per item: 256 with the word cache (elected together), else 64
+  const uint32_t C = a.word_cache ? 64 * SHORT_K : 64;
+  const uint32_t e16 = (n16 + C - 1) / C, e8 = e16 + (n8 + C - 1) / C, e4 = e8 + (n4 + C - 1) / C;
   if (blockIdx.x >= e4) return;
   __shared__ int32_t s_atom[256];
   __shared__ uint16_t s_part_lo[32 * 64];  // [position][lane]: part ids of each lane's unit
   __shared__ uint8_t s_part_hi[32 * 64];
+  __shared__ uint32_t s_queue[64 * SHORT_K];
   const PartCol lp{s_part_lo + lane, s_part_hi + lane};
   reinterpret_cast<int4 *>(s_atom)[lane] = reinterpret_cast<const int4 *>(a.T.atom)[lane];
   __syncthreads();
   for (uint32_t item = blockIdx.x; item < e4; item += gridDim.x) {
-    if (item < e32) {
-      const uint32_t x = item * 64 + uint32_t(lane);
-      if (x < n32) merge_short_unit<32>(a, s_atom, a.ws.lst[ML_32][x], lp);
-    } else if (item < e16) {
-      const uint32_t x = (item - e32) * 64 + uint32_t(lane);
-      if (x < n16) merge_short_unit<16>(a, s_atom, a.ws.lst[ML_16][x], lp);
-    } else if (item < e8) {
-      const uint32_t x = (item - e16) * 64 + uint32_t(lane);
-      if (x < n8) merge_short_unit<8>(a, s_atom, a.ws.lst[ML_8][x], lp);
+    const bool in16 = item < e16, in8 = !in16 && item < e8;
+    const uint32_t first = (item - (in16 ? 0u : in8 ? e16 : e8)) * C;
+    if (a.word_cache) {
+      if (in16)
+        merge_short_item<16, SHORT_K, true>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_16], n16, first, lane);
+      else if (in8)
+        merge_short_item<8, SHORT_K, true>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_8], n8, first, lane);
+      else
+        merge_short_item<4, SHORT_K, true>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_4], n4, first, lane);
     } else {
-      const uint32_t x = (item - e8) * 64 + uint32_t(lane);
-      if (x < n4) merge_short_unit<4>(a, s_atom, a.ws.lst[ML_4][x], lp);
+      if (in16)
+        merge_short_item<16, 1, false>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_16], n16, first, lane);
+      else if (in8)
+        merge_short_item<8, 1, false>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_8], n8, first, lane);
+      else
+        merge_short_item<4, 1, false>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_4], n4, first, lane);
     }
+  }
+}
+
+// Merge of the units of 17-32 bytes, one lane each, 64 per item (second
+// stream, beside k_merge: their chains of up to 31 dependent rounds are the
+// short tier's longest, and running them apart lets them start with the
+// rest).  Nearly every such unit is a byte string of its own, so they skip
+// the word cache.
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge32(EncodeArgs a) {
+  if (a.ws.status->pad2) return;
+  const uint32_t n32 = a.ws.status->n_list[ML_32];
+  const int lane = int(threadIdx.x);
+  const uint32_t e32 = (n32 + 63) / 64;
+  if (blockIdx.x >= e32) return;
+  __shared__ int32_t s_atom[256];
+  __shared__ uint16_t s_part_lo[32 * 64];
+  __shared__ uint8_t s_part_hi[32 * 64];
+  const PartCol lp{s_part_lo + lane, s_part_hi + lane};
+  reinterpret_cast<int4 *>(s_atom)[lane] = reinterpret_cast<const int4 *>(a.T.atom)[lane];
+  __syncthreads();
+  for (uint32_t item = blockIdx.x; item < e32; item += gridDim.x) {
+    const uint32_t x = item * 64 + uint32_t(lane);
+    if (x < n32) merge_short_unit<32>(a, s_atom, a.ws.lst[ML_32][x], lp);
   }
 }
 
@@ -1113,136 +1232,311 @@ __global__ void __launch_bounds__(LONG_BLOCK) k_merge_long(EncodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Exclusive scan of ids per unit (three phases, 4096 units per block).
+// Ordered assembly: the exclusive scan of the units' id counts and the ids
+// in output order, in one pass.  Each workgroup takes the next tile of
+// ASM_UNITS units from a ticket counter (so a tile only ever waits for tiles
+// whose workgroups are already running), publishes its own count, then
+// reads its predecessors' published states from the nearest one back
+// (decoupled look-back): a predecessor's prefix ends the walk, its count
+// alone adds and moves on.  A state is one 64-bit word (flag and value
+// together), written and read with agent-scope atomics, so no fence orders
+// it.  Every wait is bounded: past SCAN_SPIN_MAX polls the call fails
+// (status scan_fail) rather than wait on.
 // ---------------------------------------------------------------------------
-constexpr uint32_t SCAN_BLOCK = 256, SCAN_ITEMS = 16, SCAN_TILE = SCAN_BLOCK * SCAN_ITEMS;
+constexpr uint32_t ASM_BLOCK = 1024, ASM_PER = ASM_UNITS / ASM_BLOCK;  // 4 units per thread
+constexpr unsigned long long SCAN_AGG = 1ull << 62, SCAN_PREFIX = 2ull << 62;
+constexpr unsigned long long SCAN_VALUE = (1ull << 62) - 1;
+constexpr uint32_t SCAN_SPIN_MAX = 1u << 22;
 
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *sh, uint32_t &total) {
-  const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x / 64;
-  const uint32_t incl = wave_incl_sum(v, int(lane));
-  if (lane == 63) sh[wv] = incl;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
+// ids of unit i: 1 for a unit settled by k_probe, else the count of the unit
+// that merged its bytes (itself or its leader)
+__device__ __forceinline__ uint32_t unit_count(const EncodeArgs &a, uint32_t i) {
+  const int32_t u = a.ws.uid[i];
+  if (u >= 0) return 1u;
+  return a.ws.piece_cnt[u == UID_MERGED ? i : uint32_t(UID_FOLLOW - u)];
+}
+
+__device__ __forceinline__ void scan_publish(unsigned long long *p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long scan_read(unsigned long long *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The status block to pinned host memory (the call's result), all but
+// scan_fail, which a failing tile sets there itself (the host clears it
+// before each call).
+__device__ __forceinline__ void publish_status(const EncodeArgs &a, Status *host) {
+  const Status &d = *a.ws.status;
+  host->err_pos = d.err_pos;
+  host->n_pieces = d.n_pieces;
+  host->n_ids = d.n_ids;
+  host->n_chars = d.n_chars;
+  host->err_seg = d.err_seg;
+  host->pad2 = d.pad2;
+  for (uint32_t k = 0; k < ML_COUNT; ++k) host->n_list[k] = d.n_list[k];
+  host->scan_ticket = d.scan_ticket;
+  __threadfence_system();
+}
+
+// Texts above ASM_SINGLE_MAX bytes have more scan tiles than stay resident at
+// once, and the look-back's waits grow with them; their tiles' sums are
+// scanned apart instead: k_scan_sums (the sum of every tile), k_scan_bases
+// (one workgroup: the exclusive scan of the sums), then k_assemble reads its
+// base.
+__global__ void __launch_bounds__(ASM_BLOCK) k_scan_sums(EncodeArgs a) {
+  if (a.ws.status->pad2) return;
+  const uint32_t P = uint32_t(a.ws.status->n_pieces);
+  const uint32_t t = blockIdx.x;
+  if (t > P / ASM_UNITS) return;
+  const uint32_t i0 = t * ASM_UNITS, nu = min(ASM_UNITS, P - i0);
+  uint32_t sum = 0;
 #pragma unroll
-  for (uint32_t q = 0; q < SCAN_BLOCK / 64; ++q) {
-    before += q < wv ? sh[q] : 0u;
-    all += sh[q];
+  for (uint32_t k = 0; k < ASM_PER; ++k) {
+    const uint32_t j = k * ASM_BLOCK + threadIdx.x;
+    if (j < nu) sum += unit_count(a, i0 + j);
+  }
+  __shared__ uint32_t s_w[ASM_BLOCK / 64];
+  const uint32_t w = wave_sum(sum);
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x / 64] = w;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t tot = 0;
+    for (uint32_t q = 0; q < ASM_BLOCK / 64; ++q) tot += s_w[q];
+    a.ws.scan_state[t] = tot;
+  }
+}
+
+__global__ void __launch_bounds__(1024) k_scan_bases(EncodeArgs a) {
+  if (a.ws.status->pad2) return;
+  const uint32_t P = uint32_t(a.ws.status->n_pieces);
+  const uint32_t T = P / ASM_UNITS + 1;
+  const uint32_t tid = threadIdx.x, per = (T + 1023) / 1024;
+  const uint32_t t0 = min(T, tid * per), t1 = min(T, t0 + per);
+  unsigned long long sum = 0;
+  for (uint32_t t = t0; t < t1; ++t) sum += a.ws.scan_state[t];
+  __shared__ unsigned long long s_sum[33];
+  unsigned long long total;
+  unsigned long long run =
+      block_incl_scan<1024>(sum, 0ull, [](unsigned long long x, unsigned long long y) { return x + y; },
+                            s_sum, total) - sum;
+  for (uint32_t t = t0; t < t1; ++t) {
+    const unsigned long long v = a.ws.scan_state[t];
+    a.ws.scan_state[t] = run;  // now the ids before tile t
+    run += v;
+  }
+}
+
+// single_pass: the tiles' bases by the look-back; else read from scan_state
+// (k_scan_sums and k_scan_bases ran before).
+__global__ void __launch_bounds__(ASM_BLOCK) k_assemble(EncodeArgs a, Status *host, int single_pass) {
+  Status *st = a.ws.status;
+  if (st->pad2) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) publish_status(a, host);
+    return;
+  }
+  const uint32_t P = uint32_t(st->n_pieces);
+  const uint32_t nt = P / ASM_UNITS + 1;  // tiles over unit indices 0..P (P: the end)
+  __shared__ uint32_t s_tile, s_excl, s_fail;
+  __shared__ uint32_t s_off[ASM_UNITS + 1], s_start[ASM_UNITS];
+  __shared__ int32_t s_uid[ASM_UNITS];
+  __shared__ uint32_t s_wsum[ASM_BLOCK / 64];
+  if (threadIdx.x == 0) s_tile = single_pass ? atomicAdd(&st->scan_ticket, 1u) : blockIdx.x;
+  __syncthreads();
+  const uint32_t t = s_tile;
+  if (t >= nt) return;
+  const uint32_t i0 = t * ASM_UNITS;
+  const uint32_t nu = min(ASM_UNITS, P - i0);  // units of this tile (the last may have 0)
+  // counts: thread x takes units i0 + 4 x .. i0 + 4 x + 3; a unit's uid, its
+  // count and its start load side by side (a follower of the word cache
+  // needs its leader's count and start after)
+  const uint32_t tid = threadIdx.x;
+  int32_t uv[ASM_PER];
+  uint32_t cnt[ASM_PER], sst[ASM_PER];
+#pragma unroll
+  for (uint32_t k = 0; k < ASM_PER; ++k) {
+    const uint32_t j = tid * ASM_PER + k;
+    const bool in = j < nu;
+    uv[k] = in ? a.ws.uid[i0 + j] : 0;
+    cnt[k] = in ? a.ws.piece_cnt[i0 + j] : 0u;
+    sst[k] = in ? a.ws.piece_start[i0 + j] : 0u;
+  }
+#pragma unroll
+  for (uint32_t k = 0; k < ASM_PER; ++k) {
+    const int32_t u = uv[k];
+    if (tid * ASM_PER + k >= nu) cnt[k] = 0u;
+    else if (u >= 0) cnt[k] = 1u;
+    else if (u != UID_MERGED) {
+      const uint32_t src = uint32_t(UID_FOLLOW - u);
+      cnt[k] = a.ws.piece_cnt[src];
+      sst[k] = a.ws.piece_start[src];
+    }
+  }
+  uint32_t sum = 0;
+#pragma unroll
+  for (uint32_t k = 0; k < ASM_PER; ++k) sum += cnt[k];
+  // block scan of the per-thread sums
+  const int lane = int(tid & 63);
+  const uint32_t incl = wave_incl_sum(sum, lane);
+  if (lane == 63) s_wsum[tid / 64] = incl;
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < ASM_BLOCK / 64; ++q) {
+    before += q < tid / 64 ? s_wsum[q] : 0u;
+    total += s_wsum[q];
+  }
+  // the tile's place in the output: look-back by the first wave, 64
+  // predecessors per step (lane l reads tile base - l); the nearest prefix
+  // in the window ends the walk, else the window's counts add and it moves
+  // 64 tiles back.  Before tile 0 reads as a prefix of 0.
+  if (!single_pass) {
+    if (tid == 0) {
+      s_excl = uint32_t(a.ws.scan_state[t]);
+      s_fail = 0;
+    }
+  } else if (tid < 64) {
+    unsigned long long *state = a.ws.scan_state;
+    if (tid == 0) scan_publish(&state[t], (t == 0 ? SCAN_PREFIX : SCAN_AGG) | total);
+    unsigned long long acc = 0;
+    uint32_t fail = 0;
+    int64_t base = int64_t(t) - 1;
+    for (;;) {  // wave-uniform
+      const int64_t p = base - lane;
+      unsigned long long v = p >= 0 ? scan_read(&state[p]) : SCAN_PREFIX;
+      for (uint32_t spins = 0; __ballot(v == 0); ++spins) {
+        if (spins >= SCAN_SPIN_MAX) {
+          fail = 1;
+          break;
+        }
+        if (v == 0) v = scan_read(&state[p]);
+      }
+      if (fail) break;
+      const unsigned long long pm = __ballot((v & SCAN_PREFIX) != 0);
+      const int f = pm ? __ffsll(pm) - 1 : 63;  // the nearest prefix, or the whole window
+      unsigned long long x = lane <= f ? (v & SCAN_VALUE) : 0ull;
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+      acc += x;
+      if (pm) break;
+      base -= 64;
+    }
+    if (tid == 0) {
+      if (!fail && t > 0) scan_publish(&state[t], SCAN_PREFIX | (acc + total));
+      s_excl = uint32_t(acc);
+      s_fail = fail;
+    }
   }
   __syncthreads();
-  total = all;
-  return before + incl - v;
-}
-
-__global__ void __launch_bounds__(SCAN_BLOCK) k_scan_reduce(EncodeArgs a) {
-  if (a.ws.status->pad2) return;
-  __shared__ uint32_t sh[SCAN_BLOCK];
-  const uint32_t P = uint32_t(a.ws.status->n_pieces);
-  const uint32_t b0 = blockIdx.x * SCAN_TILE;
-  if (b0 >= P + 1) return;
-  uint32_t sum = 0;
-  for (uint32_t k = 0; k < SCAN_ITEMS; ++k) {
-    const uint32_t i = b0 + threadIdx.x * SCAN_ITEMS + k;
-    if (i < P) sum += a.ws.piece_cnt[i];
-  }
-  uint32_t total;
-  block_excl_scan(sum, sh, total);
-  if (threadIdx.x == 0) a.ws.scan_part[blockIdx.x] = total;
-}
-
-__global__ void __launch_bounds__(SCAN_BLOCK) k_scan_down(EncodeArgs a) {
-  if (a.ws.status->pad2) return;
-  __shared__ uint32_t sh[SCAN_BLOCK];
-  const uint32_t P = uint32_t(a.ws.status->n_pieces);
-  const uint32_t b0 = blockIdx.x * SCAN_TILE;
-  if (b0 >= P + 1) return;
-  uint32_t v[SCAN_ITEMS];
-  uint32_t sum = 0;
-  for (uint32_t k = 0; k < SCAN_ITEMS; ++k) {
-    const uint32_t i = b0 + threadIdx.x * SCAN_ITEMS + k;
-    v[k] = i < P ? a.ws.piece_cnt[i] : 0u;
-    sum += v[k];
-  }
-  // this block's base: the totals of the blocks before it (k_scan_reduce)
-  uint32_t before = 0;
-  for (uint32_t q = threadIdx.x; q < blockIdx.x; q += SCAN_BLOCK) before += a.ws.scan_part[q];
-  uint32_t base_total;
-  (void)block_excl_scan(before, sh, base_total);
-  uint32_t total;
-  uint32_t run = block_excl_scan(sum, sh, total) + base_total;
-  for (uint32_t k = 0; k < SCAN_ITEMS; ++k) {
-    const uint32_t i = b0 + threadIdx.x * SCAN_ITEMS + k;
-    if (i <= P) a.ws.piece_off[i] = run;  // piece_off[P] is the total
-    run += v[k];
-  }
-}
-
-// ids in order: unit i's ids go to [piece_off[i], piece_off[i+1]).  A block
-// takes ASM_BLOCK units and fills their output range in output order:
-// thread x writes ids o = base + x, base + x + ASM_BLOCK, ..., finding the
-// unit of o by a binary search over the block's unit offsets in LDS, so
-// that the writes are contiguous across lanes and the reads follow the
-// units' scratch slots.
-constexpr uint32_t ASM_BLOCK = 256;
-
-__global__ void __launch_bounds__(ASM_BLOCK) k_assemble(EncodeArgs a) {
-  if (a.ws.status->pad2) return;
-  const uint32_t P = uint32_t(a.ws.status->n_pieces);
-  const uint32_t total = P ? a.ws.piece_off[P] : 0u;
-  __shared__ uint32_t s_off[ASM_BLOCK + 1], s_start[ASM_BLOCK];
-  const bool fits = total <= a.ids_cap;
-  for (uint32_t b = blockIdx.x * ASM_BLOCK; b < P && fits; b += gridDim.x * ASM_BLOCK) {
-    const uint32_t nu = min(ASM_BLOCK, P - b);
-    const uint32_t i = b + threadIdx.x;
-    if (threadIdx.x < nu) {
-      s_off[threadIdx.x] = a.ws.piece_off[i];
-      s_start[threadIdx.x] = a.ws.piece_start[i];
+  if (s_fail) {
+    if (tid == 0) {
+      host->scan_fail = 1u;
+      __threadfence_system();
     }
-    if (threadIdx.x == 0) s_off[nu] = a.ws.piece_off[b + nu];
-    __syncthreads();
-    const uint32_t o0 = s_off[0], o1 = s_off[nu];
-    uint32_t lo = 0, lo_end = 0;  // the unit of the thread's last id and its end
-    for (uint32_t o = o0 + threadIdx.x; o < o1; o += ASM_BLOCK) {
-      if (o >= lo_end) {
-        // last unit u with s_off[u] <= o (units after the previous one)
-        uint32_t hi = nu;
-        while (hi - lo > 1) {
-          const uint32_t mid = (lo + hi) >> 1;
-          if (s_off[mid] <= o) lo = mid;
-          else hi = mid;
+    return;
+  }
+  const uint32_t excl = s_excl;
+  // unit offsets and sources into LDS
+  uint32_t run = excl + before + incl - sum;
+#pragma unroll
+  for (uint32_t k = 0; k < ASM_PER; ++k) {
+    const uint32_t j = tid * ASM_PER + k;
+    if (j < nu) {
+      s_off[j] = run;
+      s_uid[j] = uv[k];
+      s_start[j] = sst[k];
+    }
+    run += cnt[k];
+  }
+  if (tid == 0) s_off[nu] = excl + total;
+  __syncthreads();
+  // ids in output order: thread x writes ids o0 + x, o0 + x + 256, ..., each
+  // finding its unit by a binary search over the tile's offsets (skipped
+  // while the next id is in the same unit); nothing at or past the capacity
+  const uint32_t o0 = excl, o1 = excl + total;
+  const uint32_t cap = uint32_t(min<uint64_t>(a.ids_cap, 0xFFFFFFFFull));
+  const uint32_t o1c = min(o1, cap);
+  // (eight ids per round trip: their units found in LDS, then their loads
+  // issued together, then their stores)
+  constexpr uint32_t B = 8;
+  uint32_t lo = 0, lo_end = 0;
+  for (uint32_t ob = o0 + tid; ob < o1c; ob += B * ASM_BLOCK) {
+    int32_t val[B];
+    uint32_t src[B];
+#pragma unroll
+    for (uint32_t k = 0; k < B; ++k) {
+      const uint32_t o = ob + k * ASM_BLOCK;
+      src[k] = ~0u;
+      val[k] = 0;
+      if (o < o1c) {
+        if (o >= lo_end) {
+          uint32_t hi = nu;
+          while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (s_off[mid] <= o) lo = mid;
+            else hi = mid;
+          }
+          lo_end = s_off[lo + 1];
         }
-        lo_end = s_off[lo + 1];
+        const int32_t u = s_uid[lo];
+        if (u >= 0) val[k] = u;
+        else src[k] = s_start[lo] + (o - s_off[lo]);
       }
-      a.ids[o] = a.ws.tmp_ids[s_start[lo] + (o - s_off[lo])];
     }
-    __syncthreads();
+#pragma unroll
+    for (uint32_t k = 0; k < B; ++k)
+      if (src[k] != ~0u) val[k] = a.ws.tmp_ids[src[k]];
+#pragma unroll
+    for (uint32_t k = 0; k < B; ++k) {
+      const uint32_t o = ob + k * ASM_BLOCK;
+      if (o < o1c) a.ids[o] = val[k];
+    }
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.ws.status->n_ids = total;
-  // id offset of every segment, and the segment of the first UTF-8 error
-  for (uint32_t s = blockIdx.x * ASM_BLOCK + threadIdx.x; s <= a.n_seg; s += gridDim.x * ASM_BLOCK) {
-    const uint64_t o = a.seg_off[s];
-    // first unit starting at or after o
-    uint32_t lo = 0, hi = P;
-    while (lo < hi) {
-      const uint32_t mid = (lo + hi) >> 1;
-      if (a.ws.piece_start[mid] < o) lo = mid + 1;
+  // id offset of every segment whose first unit (the first starting at or
+  // after the segment's offset; index P for segments at the text's end) is
+  // in this tile: segments with offsets in (start of unit i0 - 1, start of
+  // the tile's last unit index]
+  {
+    const uint32_t iend = t + 1 == nt ? P : i0 + ASM_UNITS - 1;  // last unit index of the tile
+    const uint64_t above = i0 == 0 ? 0ull : uint64_t(a.ws.piece_start[i0 - 1]) + 1;
+    const uint64_t upto = iend >= P ? ~0ull : uint64_t(a.ws.piece_start[iend]);
+    // first segment with offset >= above
+    uint32_t s_lo = 0, hi = a.n_seg + 1;
+    while (s_lo < hi) {
+      const uint32_t mid = (s_lo + hi) >> 1;
+      if (a.seg_off[mid] < above) s_lo = mid + 1;
       else hi = mid;
     }
-    a.id_off[s] = P ? int64_t(a.ws.piece_off[lo]) : 0;
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    const unsigned long long e = a.ws.status->err_pos;
-    if (e != ~0ull) {
-      uint32_t lo = 0, hi = a.n_seg;
-      while (lo < hi) {
-        const uint32_t mid = (lo + hi) >> 1;
-        if (a.seg_off[mid] <= e) lo = mid + 1;
-        else hi = mid;
+    for (uint32_t s = s_lo + tid; s <= a.n_seg; s += ASM_BLOCK) {
+      const uint64_t o = a.seg_off[s];
+      if (o > upto) break;
+      // first unit of the tile starting at or after o
+      uint32_t l = 0, h = nu;
+      while (l < h) {
+        const uint32_t mid = (l + h) >> 1;
+        if (a.ws.piece_start[i0 + mid] < o) l = mid + 1;
+        else h = mid;
       }
-      a.ws.status->err_seg = lo > 0 ? lo - 1 : 0;
+      a.id_off[s] = int64_t(s_off[l]);
     }
   }
+  if (t + 1 == nt && tid == 0) {
+    // the last tile: the id total, the segment of the first UTF-8 error, and
+    // the status block to the host
+    st->n_ids = o1;
+    const unsigned long long e = st->err_pos;
+    if (e != ~0ull) {
+      uint32_t l = 0, h = a.n_seg;
+      while (l < h) {
+        const uint32_t mid = (l + h) >> 1;
+        if (a.seg_off[mid] <= e) l = mid + 1;
+        else h = mid;
+      }
+      st->err_seg = l > 0 ? l - 1 : 0;
+    }
+    publish_status(a, host);
+  }
 }
-
 
 
 }  // namespace bbpe

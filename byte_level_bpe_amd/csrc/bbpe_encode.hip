@@ -29,11 +29,22 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 struct WsLayout {
   uint64_t status, tile_nchar, tile_err, tile_bad, tile_lastchg, tile_charbase, tile_chgcarry, seg_local, seg_charstart,
-      ss, spst, spc, ps, tile_fn, tile_carry, tile_np, piece_start, piece_cnt, piece_off,
-      tmp_ids, scan_part, lst[ML_COUNT], lrank, lpart, lnl, lnr, lbits, lsel, leqm, lmin, ldirty, wslow, wseg, wseg_at, total;
+      ss, spst, spc, ps, tile_fn, tile_carry, tile_np, piece_start, piece_cnt,
+      tmp_ids, uid, owner, scan_state, lst[ML_COUNT], lrank, lpart, lnl, lnr, lbits, lsel, leqm, lmin, ldirty, wslow, wseg, wseg_at, total;
   uint64_t n_words;
   uint32_t n_tiles;
+  uint32_t owner_slots;
 };
+
+// Word-cache slots for a text of n bytes: a power of two of at least n/4
+// (at most one unit per two bytes, and far fewer distinct ones, so that
+// few byte strings share a slot), 2^12..2^23.
+uint32_t owner_slots_for(uint64_t n) {
+  uint64_t want = std::max<uint64_t>(n / 4, uint64_t(1) << 12);
+  uint32_t s = 1u << 12;
+  while (s < want && s < (1u << 23)) s <<= 1;
+  return s;
+}
 
 WsLayout layout_for(uint64_t n, uint32_t n_seg) {
   WsLayout L{};
@@ -64,9 +75,11 @@ WsLayout layout_for(uint64_t n, uint32_t n_seg) {
   take(L.tile_np, 4 * (T + 1));
   take(L.piece_start, 4 * (n + 1));
   take(L.piece_cnt, 4 * (n + 1));
-  take(L.piece_off, 4 * (n + 1));
   take(L.tmp_ids, 4 * (n + 1));
-  take(L.scan_part, 4 * ((n + 1) / 4096 + 2));
+  take(L.uid, 4 * (n + 1));
+  L.owner_slots = owner_slots_for(n);
+  take(L.owner, 4ull * L.owner_slots);
+  take(L.scan_state, 8 * ((n + 1) / ASM_UNITS + 2));
   for (uint32_t k = 0; k < ML_COUNT; ++k) take(L.lst[k], 4 * (n / ML_MIN_LEN[k] + 1));
   take(L.lrank, 4 * (n + 1));
   take(L.lpart, 4 * (n + 1));
@@ -91,6 +104,8 @@ __global__ void k_init(EncodeArgs a) {
     s->n_pieces = 0;
     s->n_ids = 0;
     for (uint32_t k = 0; k < ML_COUNT; ++k) s->n_list[k] = 0;
+  s->scan_ticket = 0;
+  s->scan_fail = 0;
     s->n_chars = 0;
     s->err_seg = 0;
     // offsets must start at 0 and end at the text length (monotonicity is
@@ -136,6 +151,16 @@ __global__ void k_err_seg(EncodeArgs a) {
   }
 }
 
+static_assert(sizeof(Status) <= 256, "the host copy of the status block is 256 bytes");
+
+// The last kernel of every sequence: the status block into pinned host memory.
+__global__ void k_publish(EncodeArgs a, Status *host) {
+  if (threadIdx.x == 0) {
+    *host = *a.ws.status;
+    __threadfence_system();
+  }
+}
+
 // The handle's second stream and its fork/join events, created once.
 int ensure_aux(bbpe_tokenizer *t) {
   if (t->aux_stream) return BBPE_OK;
@@ -163,7 +188,7 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
   if (n >= (uint64_t(1) << 32) - 64 || (flags & ~uint32_t(BBPE_TIKTOKEN_SAFE | BBPE_COUNT_ONLY)))
     return BBPE_E_INVALID_ARG;
   if (n_seg == 0 && n != 0) return BBPE_E_INVALID_ARG;
-  if (!t->d_image) return BBPE_E_STATE;
+  if (!t->d_image || !t->host_status) return BBPE_E_STATE;
   L = layout_for(n, n_seg);
   if (!d_ws || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(d_ws) & 255)) return BBPE_E_WORKSPACE;
   uint8_t *w = static_cast<uint8_t *>(d_ws);
@@ -195,9 +220,12 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
   a.ws.tile_np = reinterpret_cast<uint32_t *>(w + L.tile_np);
   a.ws.piece_start = reinterpret_cast<uint32_t *>(w + L.piece_start);
   a.ws.piece_cnt = reinterpret_cast<uint32_t *>(w + L.piece_cnt);
-  a.ws.piece_off = reinterpret_cast<uint32_t *>(w + L.piece_off);
   a.ws.tmp_ids = reinterpret_cast<int32_t *>(w + L.tmp_ids);
-  a.ws.scan_part = reinterpret_cast<uint32_t *>(w + L.scan_part);
+  a.ws.uid = reinterpret_cast<int32_t *>(w + L.uid);
+  a.ws.owner = reinterpret_cast<uint32_t *>(w + L.owner);
+  a.owner_mask = L.owner_slots - 1;
+  a.word_cache = n >= WORD_CACHE_MIN ? 1u : 0u;
+  a.ws.scan_state = reinterpret_cast<unsigned long long *>(w + L.scan_state);
   for (uint32_t k = 0; k < ML_COUNT; ++k) a.ws.lst[k] = reinterpret_cast<uint32_t *>(w + L.lst[k]);
   a.ws.lrank = reinterpret_cast<int32_t *>(w + L.lrank);
   a.ws.lpart = reinterpret_cast<int32_t *>(w + L.lpart);
@@ -242,13 +270,21 @@ void launch_front(Launcher &go, const EncodeArgs &a, const WsLayout &L) {
   go("k_pieces", k_pieces, dim3(T), dim3(64), a);
 }
 
-// Reads the status block (the call's one host synchronisation).
-int finish(bbpe_tokenizer *t, Launcher &go, const EncodeArgs &a, Status &h) {
+// Publishes the status block to the host (k_publish, the sequence's last
+// kernel) unless the sequence already did.
+void publish(bbpe_tokenizer *t, Launcher &go, const EncodeArgs &a) {
+  go("k_publish", k_publish, dim3(1), dim3(64), a, static_cast<Status *>(t->host_status_dev));
+}
+
+// Waits for the call (its one host synchronisation) and reads the status
+// block that k_publish wrote.
+int finish(bbpe_tokenizer *t, Launcher &go, Status &h) {
   HIP_OK(hipGetLastError());
-  HIP_OK(hipMemcpyAsync(&h, a.ws.status, sizeof(Status), hipMemcpyDeviceToHost, go.st));
   HIP_OK(hipStreamSynchronize(go.st));
   go.collect();
+  memcpy(&h, t->host_status, sizeof(Status));
   if (h.pad2) return BBPE_E_INVALID_ARG;
+  if (h.scan_fail) return BBPE_E_HIP;
   if (h.err_pos != ~0ull) {
     set_last_utf8_error(t, h.err_seg, h.err_pos);
     return BBPE_E_UTF8;
@@ -256,10 +292,139 @@ int finish(bbpe_tokenizer *t, Launcher &go, const EncodeArgs &a, Status &h) {
   return BBPE_OK;
 }
 
-// The encode sequence of both encode entry points.  fork: run the group and
-// long tiers on the handle's second stream beside the short tier (creating
-// it on first use); otherwise everything goes on the caller's stream, and
-// no stream, event or memory is created.
+// The encode kernels of `a` on go.st, and with fork the group and long
+// tiers on the handle's second stream beside the short tier (joined back
+// before the scan), ending with k_publish.
+int enqueue_encode(bbpe_tokenizer *t, Launcher &go, const EncodeArgs &a, const WsLayout &L,
+                   bool fork) {
+  const uint64_t n = a.n;
+  launch_front(go, a, L);
+  const uint32_t seg_grid = std::min<uint32_t>(1024, (a.n_seg + 256) / 256);
+  if (n == 0) {
+    go("k_zero_offsets", k_zero_offsets, dim3(seg_grid), dim3(256), a);
+  } else {
+    if (n < PROBE_SMALL) {
+      const uint32_t probe_grid = uint32_t((n + 2047) / 2048);
+      go("k_probe", k_probe1, dim3(probe_grid), dim3(PROBE_BLOCK), a);
+    } else {
+      const uint32_t probe_grid = uint32_t(std::min<uint64_t>((n + 8191) / 8192, 8192));
+      go("k_probe", k_probe, dim3(probe_grid), dim3(PROBE_BLOCK), a);
+    }
+    // (grid-stride kernels: their units are few, and idle waves of the
+    // second stream take dispatch slots from the short tier.)
+    const uint32_t group_grid = uint32_t(std::min<uint64_t>(n / 33 + 1, 4096));
+    const uint32_t long_grid = uint32_t(std::min<uint64_t>(n / 513 + 1, 64));
+    const uint32_t merge_grid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
+    const uint32_t merge32_grid = uint32_t(std::min<uint64_t>(n / 1088 + 1, 4096));
+    if (fork) {
+      // the 17-32-byte units and the group and long tiers (few units, long
+      // dependent chains) run on the second stream beside the rest of the
+      // short tier.  The long tier goes last: a long-tier workgroup needs a
+      // whole CU's LDS and so waits for the short tier to drain even when
+      // it finds no unit to merge.
+      hipStream_t aux = static_cast<hipStream_t>(t->aux_stream);
+      HIP_OK(hipEventRecord(static_cast<hipEvent_t>(t->ev_fork), go.st));
+      HIP_OK(hipStreamWaitEvent(aux, static_cast<hipEvent_t>(t->ev_fork), 0));
+      go.use(aux);
+      go("k_merge32", k_merge32, dim3(merge32_grid), dim3(64), a);
+      go("k_merge_group", k_merge_group, dim3(group_grid), dim3(64), a);
+      go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
+      HIP_OK(hipEventRecord(static_cast<hipEvent_t>(t->ev_join), aux));
+      go.use(go.st);
+      go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
+      HIP_OK(hipStreamWaitEvent(go.st, static_cast<hipEvent_t>(t->ev_join), 0));
+    } else {
+      go("k_merge32", k_merge32, dim3(merge32_grid), dim3(64), a);
+      go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
+      go("k_merge_group", k_merge_group, dim3(group_grid), dim3(64), a);
+      go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
+    }
+    // one workgroup per scan tile (the unit count is at most n), the last
+    // one publishing the status block
+    const uint32_t agrid = uint32_t((n + 1 + ASM_UNITS - 1) / ASM_UNITS);
+    const int single = n <= ASM_SINGLE_MAX ? 1 : 0;
+    if (!single) {
+      go("k_scan_sums", k_scan_sums, dim3(agrid), dim3(1024), a);
+      go("k_scan_bases", k_scan_bases, dim3(1), dim3(1024), a);
+    }
+    go("k_assemble", k_assemble, dim3(agrid), dim3(1024), a, static_cast<Status *>(t->host_status_dev),
+       single);
+    return BBPE_OK;
+  }
+  publish(t, go, a);
+  return BBPE_OK;
+}
+
+// What an encode's kernel sequence depends on besides the handle's tables:
+// a captured graph is replayed only for a call with the same values.
+struct GraphKey {
+  const void *image, *text, *seg_off, *allow, *ws, *ids, *id_off;
+  uint64_t n, ids_cap;
+  uint32_t n_seg, flags;
+};
+
+// Replays the handle's graph of this sequence, capturing it first (on the
+// handle's capture stream) when the last one was captured with other
+// arguments.  BBPE_E_STATE when capturing is not possible here; the caller
+// then enqueues the kernels directly.
+int run_graph(bbpe_tokenizer *t, const EncodeArgs &a, const WsLayout &L, hipStream_t st) {
+  GraphKey k;
+  memset(&k, 0, sizeof k);
+  k.image = t->d_image;
+  k.text = a.text;
+  k.seg_off = a.seg_off;
+  k.allow = a.allow;
+  k.ws = a.ws.status;
+  k.ids = a.ids;
+  k.id_off = a.id_off;
+  k.n = a.n;
+  k.ids_cap = a.ids_cap;
+  k.n_seg = a.n_seg;
+  k.flags = a.flags;
+  const uint8_t *kb = reinterpret_cast<const uint8_t *>(&k);
+  const bool hit = t->graph_exec && t->graph_key.size() == sizeof k &&
+                   memcmp(t->graph_key.data(), kb, sizeof k) == 0;
+  if (!hit) {
+    if (t->graph_exec) {
+      (void)hipGraphExecDestroy(static_cast<hipGraphExec_t>(t->graph_exec));
+      t->graph_exec = nullptr;
+      t->graph_key.clear();
+    }
+    if (!t->capture_stream) {
+      hipStream_t cs = nullptr;
+      if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return BBPE_E_STATE;
+      t->capture_stream = cs;
+    }
+    hipStream_t cs = static_cast<hipStream_t>(t->capture_stream);
+    if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) return BBPE_E_STATE;
+    Launcher go{t, cs};
+    go.allow_timing = false;
+    const int rc = enqueue_encode(t, go, a, L, true);
+    hipGraph_t g = nullptr;
+    const hipError_t e = hipStreamEndCapture(cs, &g);
+    if (rc || e != hipSuccess || !g) {
+      if (g) (void)hipGraphDestroy(g);
+      (void)hipGetLastError();
+      return BBPE_E_STATE;
+    }
+    hipGraphExec_t x = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (ei != hipSuccess || !x) {
+      (void)hipGetLastError();
+      return BBPE_E_STATE;
+    }
+    t->graph_exec = x;
+    t->graph_key.assign(kb, kb + sizeof k);
+  }
+  HIP_OK(hipGraphLaunch(static_cast<hipGraphExec_t>(t->graph_exec), st));
+  return BBPE_OK;
+}
+
+// The encode of both encode entry points.  fork: the second stream beside
+// the short tier (created on first use), and the whole sequence replayed as
+// one HIP graph when possible; otherwise every kernel is launched directly
+// on the caller's stream, and no stream, event, graph or memory is created.
 int encode_impl(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t *d_seg_off,
                 const uint8_t *d_allow, uint32_t n_seg, uint32_t flags, void *d_ws,
                 uint64_t ws_bytes, int32_t *d_ids, uint64_t ids_cap, int64_t *d_id_off,
@@ -280,53 +445,21 @@ int encode_impl(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint
   }
   Launcher go{t, reinterpret_cast<hipStream_t>(stream)};
   go.allow_timing = fork;
-  launch_front(go, a, L);
-  const uint32_t seg_grid = std::min<uint32_t>(1024, (n_seg + 256) / 256);
-  if (n == 0) {
-    go("k_zero_offsets", k_zero_offsets, dim3(seg_grid), dim3(256), a);
-  } else {
-    if (n < PROBE_SMALL) {
-      const uint32_t probe_grid = uint32_t((n + 2047) / 2048);
-      go("k_probe", k_probe1, dim3(probe_grid), dim3(PROBE_BLOCK), a);
-    } else {
-      const uint32_t probe_grid = uint32_t(std::min<uint64_t>((n + 8191) / 8192, 8192));
-      go("k_probe", k_probe, dim3(probe_grid), dim3(PROBE_BLOCK), a);
-    }
-    // (grid-stride kernels: their units are few, and idle waves of the
-    // second stream take dispatch slots from the short tier.)
-    const uint32_t group_grid = uint32_t(std::min<uint64_t>(n / 33 + 1, 4096));
-    const uint32_t long_grid = uint32_t(std::min<uint64_t>(n / 513 + 1, 64));
-    const uint32_t merge_grid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
-    if (fork) {
-      // the group and long tiers (few units, long dependent chains) run on
-      // the second stream beside the short tier.  The group tier goes
-      // first: its one-wave workgroups are placed beside the short tier's
-      // waves at once, while a long-tier workgroup needs a whole CU's LDS
-      // and so waits for the short tier to drain even when it finds no unit
-      // to merge.
-      hipStream_t aux = static_cast<hipStream_t>(t->aux_stream);
-      HIP_OK(hipEventRecord(static_cast<hipEvent_t>(t->ev_fork), go.st));
-      HIP_OK(hipStreamWaitEvent(aux, static_cast<hipEvent_t>(t->ev_fork), 0));
-      go.use(aux);
-      go("k_merge_group", k_merge_group, dim3(group_grid), dim3(64), a);
-      go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
-      HIP_OK(hipEventRecord(static_cast<hipEvent_t>(t->ev_join), aux));
-      go.use(go.st);
-      go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
-      HIP_OK(hipStreamWaitEvent(go.st, static_cast<hipEvent_t>(t->ev_join), 0));
-    } else {
-      go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
-      go("k_merge_group", k_merge_group, dim3(group_grid), dim3(64), a);
-      go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
-    }
-    const uint32_t nscan = uint32_t((n + 1 + 4095) / 4096);
-    go("k_scan_reduce", k_scan_reduce, dim3(nscan), dim3(256), a);
-    go("k_scan_down", k_scan_down, dim3(nscan), dim3(256), a);
-    const uint32_t agrid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
-    go("k_assemble", k_assemble, dim3(agrid), dim3(256), a);
+  // (the previous call has completed: its stream was synchronised)
+  static_cast<volatile Status *>(t->host_status)->scan_fail = 0u;
+  bool done = false;
+  if (fork && !t->timing && !t->graph_broken) {
+    rc = run_graph(t, a, L, go.st);
+    if (rc == BBPE_E_STATE) t->graph_broken = true;
+    else if (rc) return rc;
+    else done = true;
+  }
+  if (!done) {
+    rc = enqueue_encode(t, go, a, L, fork);
+    if (rc) return rc;
   }
   Status h{};
-  rc = finish(t, go, a, h);
+  rc = finish(t, go, h);
   if (rc) return rc;
   *n_ids = h.n_ids;
   if (h.n_ids > ids_cap && !count_only) return BBPE_E_CAPACITY;
@@ -362,6 +495,23 @@ int bbpe_upload_tables(bbpe_tokenizer *t, void *d_mem, uint64_t bytes, void *str
   std::lock_guard<std::mutex> lock(t->mu);
   if (bytes < t->layout.total || (reinterpret_cast<uintptr_t>(d_mem) & 255)) return BBPE_E_INVALID_ARG;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!t->host_status) {
+    void *h = nullptr, *d = nullptr;
+    HIP_OK(hipHostMalloc(&h, 256, hipHostMallocMapped | hipHostMallocCoherent));
+    if (hipHostGetDevicePointer(&d, h, 0) != hipSuccess) {
+      (void)hipHostFree(h);
+      return BBPE_E_HIP;
+    }
+    memset(h, 0, 256);
+    t->host_status = h;
+    t->host_status_dev = d;
+  }
+  // a replayed graph holds the old table addresses
+  if (t->graph_exec) {
+    (void)hipGraphExecDestroy(static_cast<hipGraphExec_t>(t->graph_exec));
+    t->graph_exec = nullptr;
+    t->graph_key.clear();
+  }
   HIP_OK(hipMemcpyAsync(d_mem, t->image.data(), t->layout.total, hipMemcpyHostToDevice, st));
   HIP_OK(hipStreamSynchronize(st));
   const uint8_t *b = static_cast<const uint8_t *>(d_mem);
@@ -443,8 +593,9 @@ int bbpe_pretokenize_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t
     go("k_copy_pieces", k_copy_pieces, dim3(g), dim3(256), a, d_starts, starts_cap, d_is_special);
     go("k_err_seg", k_err_seg, dim3(1), dim3(64), a);
   }
+  publish(t, go, a);
   Status h{};
-  rc = finish(t, go, a, h);
+  rc = finish(t, go, h);
   if (rc) return rc;
   *n_pieces = h.n_pieces;
   if (h.n_pieces > starts_cap) return BBPE_E_CAPACITY;
@@ -473,6 +624,9 @@ void bbpe_free(bbpe_tokenizer *t) {
   if (!t) return;
   for (void *e : t->t_events)
     if (e) (void)hipEventDestroy(static_cast<hipEvent_t>(e));
+  if (t->graph_exec) (void)hipGraphExecDestroy(static_cast<hipGraphExec_t>(t->graph_exec));
+  if (t->capture_stream) (void)hipStreamDestroy(static_cast<hipStream_t>(t->capture_stream));
+  if (t->host_status) (void)hipHostFree(t->host_status);
   if (t->aux_stream) {
     (void)hipStreamSynchronize(static_cast<hipStream_t>(t->aux_stream));
     (void)hipEventDestroy(static_cast<hipEvent_t>(t->ev_fork));

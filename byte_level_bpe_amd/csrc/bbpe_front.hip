@@ -104,6 +104,8 @@ __device__ __forceinline__ void init_status(const EncodeArgs &a, unsigned long l
   s->n_pieces = 0;
   s->n_ids = 0;
   for (uint32_t k = 0; k < ML_COUNT; ++k) s->n_list[k] = 0;
+  s->scan_ticket = 0;
+  s->scan_fail = 0;
   s->err_seg = 0;
   s->n_chars = n_chars;
   // offsets start at 0, end at the text length and never decrease; every

@@ -134,6 +134,8 @@ struct Status {
   unsigned int err_seg;           // segment of err_pos
   unsigned int pad2;              // nonzero: invalid segment offsets, every kernel exits
   unsigned int n_list[8];         // units to merge per length class (MergeList)
+  unsigned int scan_ticket;       // next tile of the id-count scan (k_assemble)
+  unsigned int scan_fail;         // nonzero: a scan tile's wait for its predecessors gave up
 };
 
 // Merge-unit lists by length class: the short tier (one lane per unit,

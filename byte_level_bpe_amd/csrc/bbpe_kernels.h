@@ -30,9 +30,19 @@ struct WsPtrs {
   uint32_t *tile_np;                // [T+1] pieces per tile, then their exclusive scan
   uint32_t *piece_start;            // [P+1]
   uint32_t *piece_cnt;              // [P] ids per unit
-  uint32_t *piece_off;              // [P+1] exclusive scan of the ids per unit
-  int32_t *tmp_ids;                 // [N] ids of each piece, at the piece's byte offset
-  uint32_t *scan_part;              // [N/4096+2] partial sums of the piece scan
+  int32_t *tmp_ids;                 // [N] ids of each merged unit, at the unit's byte offset
+  // per unit: its one id (>= 0: a special, a single byte or a key that
+  // merges back to itself), UID_MERGED (its ids are at tmp_ids + its start,
+  // piece_cnt of them), or UID_FOLLOW - j for a unit whose bytes equal those
+  // of unit j, which merged for both (the word cache of one call)
+  int32_t *uid;
+  // word cache: unit index stored under a hash of each 2-16-byte unit's
+  // bytes (the last store wins); [owner_mask + 1]
+  uint32_t *owner;
+  // per scan tile of ASM_UNITS units (k_assemble): 0 (not yet published),
+  // or a flag in bits 62-63 (SCAN_AGG: the tile's own id count; SCAN_PREFIX:
+  // the ids of every unit up to the tile's end) over the value
+  unsigned long long *scan_state;
   uint32_t *lst[ML_COUNT];          // units to merge, by length class
   // long tier, per text position: pair rank at each part start, id of the
   // part starting there, and the two created-pair ranks of a batch merge
@@ -50,6 +60,12 @@ struct WsPtrs {
   uint32_t *wseg_at;                // [W]
 };
 
+// units per tile of the id-count scan in k_assemble
+constexpr uint32_t ASM_UNITS = 4096;
+// texts up to this size scan the tiles' id counts in k_assemble itself
+// (look-back between tiles); larger ones scan the tile sums apart first
+constexpr uint64_t ASM_SINGLE_MAX = 6000000;
+
 // threads per k_probe block (units per block and pass)
 constexpr uint32_t PROBE_BLOCK = 512;
 // Texts of at most FUSE_TILES tiles skip the one-workgroup tile scans of the
@@ -57,6 +73,13 @@ constexpr uint32_t PROBE_BLOCK = 512;
 // folds the tiles before (and, for the lookahead, after) it itself.
 constexpr uint32_t FUSE_TILES = 2048;
 constexpr uint64_t PROBE_SMALL = 1u << 20;  // texts below this: one unit per probe thread
+// Texts from this size on use the word cache.  Below it the short tier's
+// units fit in about one generation of resident waves, so its length is
+// its longest chain of merge rounds, which the cache's election only delays.
+constexpr uint64_t WORD_CACHE_MIN = 16u << 20;
+
+constexpr int32_t UID_MERGED = -1;
+constexpr int32_t UID_FOLLOW = -2;  // UID_FOLLOW - j: follows unit j
 
 struct EncodeArgs {
   DevTables T;
@@ -69,6 +92,9 @@ struct EncodeArgs {
   uint64_t n_words;
   uint32_t n_tiles;
   int32_t merge_units;   // 1: cut pieces into merge units (encode); 0: pieces (pre-tokenize)
+  uint32_t owner_mask;   // word-cache slots - 1 (a power of two minus one)
+  uint32_t word_cache;   // 1: units of 2-16 bytes merge once per byte string (texts of at
+                         //    least WORD_CACHE_MIN bytes)
   int32_t *ids;
   uint64_t ids_cap;
   int64_t *id_off;
@@ -88,11 +114,12 @@ __global__ void k_scan_tiles_np(EncodeArgs a);
 __global__ void k_pieces(EncodeArgs a);
 __global__ void k_probe(EncodeArgs a);
 __global__ void k_probe1(EncodeArgs a);
+__global__ void k_merge32(EncodeArgs a);
 __global__ void k_merge(EncodeArgs a);
 __global__ void k_merge_long(EncodeArgs a);
 __global__ void k_merge_group(EncodeArgs a);
-__global__ void k_scan_reduce(EncodeArgs a);
-__global__ void k_scan_down(EncodeArgs a);
-__global__ void k_assemble(EncodeArgs a);
+__global__ void k_scan_sums(EncodeArgs a);
+__global__ void k_scan_bases(EncodeArgs a);
+__global__ void k_assemble(EncodeArgs a, Status *host_status, int single_pass);
 
 }  // namespace bbpe

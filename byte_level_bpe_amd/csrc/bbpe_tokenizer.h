@@ -41,6 +41,18 @@ struct bbpe_tokenizer {
   // (created at the first encode, on the device current then)
   void *aux_stream = nullptr;
   void *ev_fork = nullptr, *ev_join = nullptr;
+  // The status block of the last call, written by its last kernel into
+  // pinned host memory (allocated by bbpe_upload_tables): read after the
+  // call's one stream synchronisation.  host_status_dev is its device
+  // address.
+  void *host_status = nullptr, *host_status_dev = nullptr;
+  // The last encode's kernel sequence (both streams) as an instantiated HIP
+  // graph, captured on capture_stream, and the arguments it was captured
+  // with: a call with the same arguments replays it with one launch.
+  void *capture_stream = nullptr;
+  void *graph_exec = nullptr;
+  std::vector<uint8_t> graph_key;
+  bool graph_broken = false;  // a capture failed: encode without graphs
   // Every entry point that enqueues work or touches the mutable state above
   // (second stream, fork/join events, timing records) holds this lock for
   // the whole call, so that host threads sharing a handle never interleave

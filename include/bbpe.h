@@ -183,10 +183,11 @@ int bbpe_encode_segments(bbpe_tokenizer *tok, const uint8_t *d_text, uint64_t to
  * from the library's first use of that GPU until the process ends; the
  * call allocates nothing and creates no stream or event, and runs every
  * kernel on hip_stream (which must belong to the current device).  Texts
- * whose workspace (bbpe_workspace_bytes) exceeds the array -- about
- * 1.2 MB of text -- return BBPE_E_WORKSPACE.  All calls of this entry
- * point in one process share the array and run one at a time (a lock);
- * calls from other processes use their own copy. */
+ * whose workspace (bbpe_workspace_bytes, some 50 bytes per text byte)
+ * exceeds the array -- about a megabyte of text -- return
+ * BBPE_E_WORKSPACE.  All calls of this entry point in one process share the
+ * array and run one at a time (a lock); calls from other processes use
+ * their own copy. */
 #define BBPE_NOALLOC_SCRATCH_BYTES (48ull << 20)
 int bbpe_encode_segments_noalloc(bbpe_tokenizer *tok, const uint8_t *d_text,
                                  uint64_t total_bytes, const uint64_t *d_seg_off,

@@ -62,8 +62,15 @@ def test_noalloc_matches_workspace_entry_point():
     text = w.segments[0][0]
     limit = B.NOALLOC_SCRATCH_BYTES
     # first call: the largest slice of the main text that fits the array
-    n1 = 1_150_000
-    assert tok.workspace_bytes(n1, 1) <= limit
+    lo, hi = 1, len(text)
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if tok.workspace_bytes(mid, 1) <= limit:
+            lo = mid
+        else:
+            hi = mid - 1
+    n1 = lo
+    assert 500_000 < n1 < len(text)
     say("noalloc call 1", n1, "bytes")
     k1 = _both(tok, [(_cut(text, 0, n1), False)])
     assert k1 > 100_000
@@ -79,8 +86,8 @@ def test_noalloc_matches_workspace_entry_point():
     say("noalloc unchunked")
     _both(tok, [(_cut(text, 0, 70_000), False)], safe=False)
     # too large for the array
-    big = 1_400_000
-    assert tok.workspace_bytes(big, 1) > limit
+    big = n1 + 200_000
+    assert tok.workspace_bytes(big - 3, 1) > limit
     d = torch.device("cuda:0")
     t_big, o_big, a_big, n_big = B.to_device_segments([(_cut(text, 0, big), False)], d)
     with pytest.raises(B.BBPEError) as ei:
