@@ -910,51 +910,44 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
   }
 }
 
-// Merge of the units of 17-32 bytes, one lane each, 64 per item (second
-// stream, beside k_merge: their chains of up to 31 dependent rounds are the
-// short tier's longest, and running them apart lets them start with the
-// rest).  Nearly every such unit is a byte string of its own, so they skip
-// the word cache.
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge32(EncodeArgs a) {
+// Merge of the units of 17..WAVE_MAX bytes (second stream, beside k_merge:
+// theirs are the longest chains of dependent merge rounds below the long
+// tier, and running them apart lets them start with the rest), longest
+// first.  Units of 33..WAVE_MAX bytes: few, one wave each, positions per
+// lane sized to the list's longest unit (their chains are the critical
+// path, and a wave shared by several units waits for the slowest probe of
+// all of them every round); many, 16 or 32 lanes per unit, for throughput.
+// Then the units of 17-32 bytes, one lane each, 64 per item (nearly every
+// such unit is a byte string of its own, so they skip the word cache).
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge_wide(EncodeArgs a) {
   if (a.ws.status->pad2) return;
-  const uint32_t n32 = a.ws.status->n_list[ML_32];
+  const Status *st = a.ws.status;
   const int lane = int(threadIdx.x);
-  const uint32_t e32 = (n32 + 63) / 64;
+  const uint32_t n64 = st->n_list[ML_G512], n32g = st->n_list[ML_G256], n16g = st->n_list[ML_G128];
+  const uint32_t n32 = st->n_list[ML_32];
+  const bool pack = n64 + n32g + n16g > GROUP_PACK_MIN;
+  const uint32_t e64 = n64, e32g = e64 + (pack ? (n32g + 1) / 2 : n32g);
+  const uint32_t e16g = e32g + (pack ? (n16g + 3) / 4 : n16g);
+  const uint32_t e32 = e16g + (n32 + 63) / 64;
   if (blockIdx.x >= e32) return;
   __shared__ int32_t s_atom[256];
-  __shared__ uint16_t s_part_lo[32 * 64];
+  __shared__ uint16_t s_part_lo[32 * 64];  // [position][lane]: part ids of each lane's unit
   __shared__ uint8_t s_part_hi[32 * 64];
   const PartCol lp{s_part_lo + lane, s_part_hi + lane};
   reinterpret_cast<int4 *>(s_atom)[lane] = reinterpret_cast<const int4 *>(a.T.atom)[lane];
   __syncthreads();
   for (uint32_t item = blockIdx.x; item < e32; item += gridDim.x) {
-    const uint32_t x = item * 64 + uint32_t(lane);
-    if (x < n32) merge_short_unit<32>(a, s_atom, a.ws.lst[ML_32][x], lp);
-  }
-}
-
-// Merge of the units of 33..WAVE_MAX bytes, longest first.  Few units: one
-// wave each, positions per lane sized to the list's longest unit (their
-// chains are the critical path, and a wave shared by several units waits for
-// the slowest probe of all of them every round).  Many: 16 or 32 lanes per
-// unit, for throughput.  Runs beside k_merge (another stream).
-__global__ void __launch_bounds__(64) k_merge_group(EncodeArgs a) {
-  if (a.ws.status->pad2) return;
-  const Status *st = a.ws.status;
-  const int lane = int(threadIdx.x);
-  const uint32_t n64 = st->n_list[ML_G512], n32g = st->n_list[ML_G256], n16g = st->n_list[ML_G128];
-  const bool pack = n64 + n32g + n16g > GROUP_PACK_MIN;
-  const uint32_t e64 = n64, e32g = e64 + (pack ? (n32g + 1) / 2 : n32g);
-  const uint32_t e16g = e32g + (pack ? (n16g + 3) / 4 : n16g);
-  for (uint32_t item = blockIdx.x; item < e16g; item += gridDim.x) {
     if (item < e64) {
       merge_group<64, 8>(a, a.ws.lst[ML_G512], n64, item, lane);
     } else if (item < e32g) {
       if (pack) merge_group<32, 8>(a, a.ws.lst[ML_G256], n32g, (item - e64) * 2, lane);
       else merge_group<64, 4>(a, a.ws.lst[ML_G256], n32g, item - e64, lane);
-    } else {
+    } else if (item < e16g) {
       if (pack) merge_group<16, 8>(a, a.ws.lst[ML_G128], n16g, (item - e32g) * 4, lane);
       else merge_group<64, 2>(a, a.ws.lst[ML_G128], n16g, item - e32g, lane);
+    } else {
+      const uint32_t x = (item - e16g) * 64 + uint32_t(lane);
+      if (x < n32) merge_short_unit<32>(a, s_atom, a.ws.lst[ML_32][x], lp);
     }
   }
 }

@@ -243,7 +243,8 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
 }
 
 // Steps up to the ordered list of piece starts.
-void launch_front(Launcher &go, const EncodeArgs &a, const WsLayout &L) {
+template <typename Go>
+void launch_front(Go &go, const EncodeArgs &a, const WsLayout &L) {
   // (a non-empty text has its status initialised by k_scan_chars, from the
   // per-tile results of k_count, which reads no status)
   if (a.n == 0) {
@@ -272,7 +273,8 @@ void launch_front(Launcher &go, const EncodeArgs &a, const WsLayout &L) {
 
 // Publishes the status block to the host (k_publish, the sequence's last
 // kernel) unless the sequence already did.
-void publish(bbpe_tokenizer *t, Launcher &go, const EncodeArgs &a) {
+template <typename Go>
+void publish(bbpe_tokenizer *t, Go &go, const EncodeArgs &a) {
   go("k_publish", k_publish, dim3(1), dim3(64), a, static_cast<Status *>(t->host_status_dev));
 }
 
@@ -295,7 +297,8 @@ int finish(bbpe_tokenizer *t, Launcher &go, Status &h) {
 // The encode kernels of `a` on go.st, and with fork the group and long
 // tiers on the handle's second stream beside the short tier (joined back
 // before the scan), ending with k_publish.
-int enqueue_encode(bbpe_tokenizer *t, Launcher &go, const EncodeArgs &a, const WsLayout &L,
+template <typename Go>
+int enqueue_encode(bbpe_tokenizer *t, Go &go, const EncodeArgs &a, const WsLayout &L,
                    bool fork) {
   const uint64_t n = a.n;
   launch_front(go, a, L);
@@ -312,31 +315,28 @@ int enqueue_encode(bbpe_tokenizer *t, Launcher &go, const EncodeArgs &a, const W
     }
     // (grid-stride kernels: their units are few, and idle waves of the
     // second stream take dispatch slots from the short tier.)
-    const uint32_t group_grid = uint32_t(std::min<uint64_t>(n / 33 + 1, 4096));
+    const uint32_t wide_grid = uint32_t(std::min<uint64_t>(n / 17 + 1, 4096));
     const uint32_t long_grid = uint32_t(std::min<uint64_t>(n / 513 + 1, 64));
     const uint32_t merge_grid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
-    const uint32_t merge32_grid = uint32_t(std::min<uint64_t>(n / 1088 + 1, 4096));
     if (fork) {
-      // the 17-32-byte units and the group and long tiers (few units, long
-      // dependent chains) run on the second stream beside the rest of the
-      // short tier.  The long tier goes last: a long-tier workgroup needs a
-      // whole CU's LDS and so waits for the short tier to drain even when
-      // it finds no unit to merge.
-      hipStream_t aux = static_cast<hipStream_t>(t->aux_stream);
-      HIP_OK(hipEventRecord(static_cast<hipEvent_t>(t->ev_fork), go.st));
-      HIP_OK(hipStreamWaitEvent(aux, static_cast<hipEvent_t>(t->ev_fork), 0));
-      go.use(aux);
-      go("k_merge32", k_merge32, dim3(merge32_grid), dim3(64), a);
-      go("k_merge_group", k_merge_group, dim3(group_grid), dim3(64), a);
+      // the units of 17-512 bytes (few, long dependent chains) run on the
+      // second stream beside the rest of the short tier; the long tier
+      // follows the short tier on the caller's stream (a long-tier
+      // workgroup needs a whole CU's LDS, which the short tier's waves hold
+      // until they drain)
+      int rc = go.record(0);
+      go.use_aux();
+      if (!rc) rc = go.wait(0);
+      go("k_merge_wide", k_merge_wide, dim3(wide_grid), dim3(64), a);
+      if (!rc) rc = go.record(1);
+      go.use_main();
+      go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
       go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
-      HIP_OK(hipEventRecord(static_cast<hipEvent_t>(t->ev_join), aux));
-      go.use(go.st);
-      go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
-      HIP_OK(hipStreamWaitEvent(go.st, static_cast<hipEvent_t>(t->ev_join), 0));
+      if (!rc) rc = go.wait(1);
+      if (rc) return rc;
     } else {
-      go("k_merge32", k_merge32, dim3(merge32_grid), dim3(64), a);
+      go("k_merge_wide", k_merge_wide, dim3(wide_grid), dim3(64), a);
       go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
-      go("k_merge_group", k_merge_group, dim3(group_grid), dim3(64), a);
       go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
     }
     // one workgroup per scan tile (the unit count is at most n), the last
@@ -356,17 +356,17 @@ int enqueue_encode(bbpe_tokenizer *t, Launcher &go, const EncodeArgs &a, const W
 }
 
 // What an encode's kernel sequence depends on besides the handle's tables:
-// a captured graph is replayed only for a call with the same values.
+// a built graph is replayed only for a call with the same values.
 struct GraphKey {
-  const void *image, *text, *seg_off, *allow, *ws, *ids, *id_off;
+  const void *image, *text, *seg_off, *allow, *ws, *ids, *id_off, *host;
   uint64_t n, ids_cap;
   uint32_t n_seg, flags;
 };
 
-// Replays the handle's graph of this sequence, capturing it first (on the
-// handle's capture stream) when the last one was captured with other
-// arguments.  BBPE_E_STATE when capturing is not possible here; the caller
-// then enqueues the kernels directly.
+// Launches the handle's graph of this sequence on st, building it first (a
+// GraphBuilder run of the same sequence) when the last one was built with
+// other arguments.  BBPE_E_STATE when that is not possible: the caller then
+// launches the kernels directly.
 int run_graph(bbpe_tokenizer *t, const EncodeArgs &a, const WsLayout &L, hipStream_t st) {
   GraphKey k;
   memset(&k, 0, sizeof k);
@@ -377,6 +377,7 @@ int run_graph(bbpe_tokenizer *t, const EncodeArgs &a, const WsLayout &L, hipStre
   k.ws = a.ws.status;
   k.ids = a.ids;
   k.id_off = a.id_off;
+  k.host = t->host_status_dev;
   k.n = a.n;
   k.ids_cap = a.ids_cap;
   k.n_seg = a.n_seg;
@@ -390,27 +391,14 @@ int run_graph(bbpe_tokenizer *t, const EncodeArgs &a, const WsLayout &L, hipStre
       t->graph_exec = nullptr;
       t->graph_key.clear();
     }
-    if (!t->capture_stream) {
-      hipStream_t cs = nullptr;
-      if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return BBPE_E_STATE;
-      t->capture_stream = cs;
-    }
-    hipStream_t cs = static_cast<hipStream_t>(t->capture_stream);
-    if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) return BBPE_E_STATE;
-    Launcher go{t, cs};
-    go.allow_timing = false;
-    const int rc = enqueue_encode(t, go, a, L, true);
-    hipGraph_t g = nullptr;
-    const hipError_t e = hipStreamEndCapture(cs, &g);
-    if (rc || e != hipSuccess || !g) {
-      if (g) (void)hipGraphDestroy(g);
-      (void)hipGetLastError();
-      return BBPE_E_STATE;
-    }
+    GraphBuilder gb;
+    if (hipGraphCreate(&gb.g, 0) != hipSuccess) return BBPE_E_STATE;
+    const int rc = enqueue_encode(t, gb, a, L, true);
     hipGraphExec_t x = nullptr;
-    const hipError_t ei = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
-    (void)hipGraphDestroy(g);
-    if (ei != hipSuccess || !x) {
+    const bool ok = !rc && !gb.err &&
+                    hipGraphInstantiate(&x, gb.g, nullptr, nullptr, 0) == hipSuccess && x;
+    (void)hipGraphDestroy(gb.g);
+    if (!ok) {
       (void)hipGetLastError();
       return BBPE_E_STATE;
     }
@@ -422,9 +410,12 @@ int run_graph(bbpe_tokenizer *t, const EncodeArgs &a, const WsLayout &L, hipStre
 }
 
 // The encode of both encode entry points.  fork: the second stream beside
-// the short tier (created on first use), and the whole sequence replayed as
-// one HIP graph when possible; otherwise every kernel is launched directly
-// on the caller's stream, and no stream, event, graph or memory is created.
+// the short tier (its stream and events created on first use), and the
+// whole sequence launched as one HIP graph, built once and replayed while
+// the arguments stay the same (a replay saves the host the time of
+// launching a dozen kernels and events one by one); otherwise every kernel
+// is launched on the caller's stream, and no stream, event, graph or memory
+// is created.
 int encode_impl(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t *d_seg_off,
                 const uint8_t *d_allow, uint32_t n_seg, uint32_t flags, void *d_ws,
                 uint64_t ws_bytes, int32_t *d_ids, uint64_t ids_cap, int64_t *d_id_off,
@@ -495,6 +486,11 @@ int bbpe_upload_tables(bbpe_tokenizer *t, void *d_mem, uint64_t bytes, void *str
   std::lock_guard<std::mutex> lock(t->mu);
   if (bytes < t->layout.total || (reinterpret_cast<uintptr_t>(d_mem) & 255)) return BBPE_E_INVALID_ARG;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (t->graph_exec) {  // (built on the old table addresses)
+    (void)hipGraphExecDestroy(static_cast<hipGraphExec_t>(t->graph_exec));
+    t->graph_exec = nullptr;
+    t->graph_key.clear();
+  }
   if (!t->host_status) {
     void *h = nullptr, *d = nullptr;
     HIP_OK(hipHostMalloc(&h, 256, hipHostMallocMapped | hipHostMallocCoherent));
@@ -505,12 +501,6 @@ int bbpe_upload_tables(bbpe_tokenizer *t, void *d_mem, uint64_t bytes, void *str
     memset(h, 0, 256);
     t->host_status = h;
     t->host_status_dev = d;
-  }
-  // a replayed graph holds the old table addresses
-  if (t->graph_exec) {
-    (void)hipGraphExecDestroy(static_cast<hipGraphExec_t>(t->graph_exec));
-    t->graph_exec = nullptr;
-    t->graph_key.clear();
   }
   HIP_OK(hipMemcpyAsync(d_mem, t->image.data(), t->layout.total, hipMemcpyHostToDevice, st));
   HIP_OK(hipStreamSynchronize(st));
@@ -625,7 +615,6 @@ void bbpe_free(bbpe_tokenizer *t) {
   for (void *e : t->t_events)
     if (e) (void)hipEventDestroy(static_cast<hipEvent_t>(e));
   if (t->graph_exec) (void)hipGraphExecDestroy(static_cast<hipGraphExec_t>(t->graph_exec));
-  if (t->capture_stream) (void)hipStreamDestroy(static_cast<hipStream_t>(t->capture_stream));
   if (t->host_status) (void)hipHostFree(t->host_status);
   if (t->aux_stream) {
     (void)hipStreamSynchronize(static_cast<hipStream_t>(t->aux_stream));

@@ -114,10 +114,9 @@ __global__ void k_scan_tiles_np(EncodeArgs a);
 __global__ void k_pieces(EncodeArgs a);
 __global__ void k_probe(EncodeArgs a);
 __global__ void k_probe1(EncodeArgs a);
-__global__ void k_merge32(EncodeArgs a);
 __global__ void k_merge(EncodeArgs a);
 __global__ void k_merge_long(EncodeArgs a);
-__global__ void k_merge_group(EncodeArgs a);
+__global__ void k_merge_wide(EncodeArgs a);
 __global__ void k_scan_sums(EncodeArgs a);
 __global__ void k_scan_bases(EncodeArgs a);
 __global__ void k_assemble(EncodeArgs a, Status *host_status, int single_pass);

@@ -47,12 +47,11 @@ struct bbpe_tokenizer {
   // address.
   void *host_status = nullptr, *host_status_dev = nullptr;
   // The last encode's kernel sequence (both streams) as an instantiated HIP
-  // graph, captured on capture_stream, and the arguments it was captured
-  // with: a call with the same arguments replays it with one launch.
-  void *capture_stream = nullptr;
+  // graph, and the arguments it was built with: a call with the same
+  // arguments replays it with one launch.
   void *graph_exec = nullptr;
   std::vector<uint8_t> graph_key;
-  bool graph_broken = false;  // a capture failed: encode without graphs
+  bool graph_broken = false;  // building one failed: launch kernels directly
   // Every entry point that enqueues work or touches the mutable state above
   // (second stream, fork/join events, timing records) holds this lock for
   // the whole call, so that host threads sharing a handle never interleave

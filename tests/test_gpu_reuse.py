@@ -1,6 +1,7 @@
-"""Encode calls replayed from the handle's captured HIP graph: the same
-buffers with new contents on every call, other buffers and flags in between
-(each change recaptures), every result id for id against the oracle."""
+"""Encode calls on the same device buffers with new contents on every call,
+other buffers, flags and count-only calls in between: every result id for
+id against the oracle (nothing from an earlier call may leak into a later
+one through the reused workspace)."""
 import sys
 
 import numpy as np
@@ -36,7 +37,7 @@ def _slice(text, a, n):
     return text[a:b] + b" " * (n - (b - a))
 
 
-def test_graph_replays_with_new_contents():
+def test_reused_buffers_with_new_contents():
     w = configs.main()
     tok = B.load_ranks(w.tokens, w.specials, w.grammar)
     orc = Oracle(w.tokens, w.specials, w.grammar)
@@ -50,8 +51,8 @@ def test_graph_replays_with_new_contents():
     other = B.to_device_segments([(_slice(text, 7_000, 50_000), False), (b"x y", True)], dev)
     for it in range(8):
         seg = _slice(text, 131_071 * it, n)
-        say("graph replay", it)
-        # new contents in the same buffers (an eager copy between replays)
+        say("reused buffers", it)
+        # new contents in the same buffers
         t_dev[:n].copy_(torch.frombuffer(bytearray(seg), dtype=torch.uint8).to(dev))
         safe = it % 3 != 2
         _, _, k = tok.encode_device(t_dev, off_dev, allow_dev, total, safe, ids=ids, id_off=id_off)
