@@ -29,7 +29,7 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 struct WsLayout {
   uint64_t status, tile_nchar, tile_err, tile_bad, tile_lastchg, tile_charbase, tile_chgcarry, seg_local, seg_charstart,
-      ss, spst, spc, ps, tile_fn, tile_carry, tile_np, piece_start, piece_cnt,
+      ss, spst, spc, ps, tile_sp_eout, tile_sp_unres, tile_fn, tile_carry, tile_np, piece_start, piece_cnt,
       tmp_ids, uid, owner, scan_state, lst[ML_COUNT], lrank, lpart, lnl, lnr, lbits, lsel, leqm, lmin, ldirty, wslow, wseg, wseg_at, total;
   uint64_t n_words;
   uint32_t n_tiles;
@@ -70,6 +70,8 @@ WsLayout layout_for(uint64_t n, uint32_t n_seg) {
   take(L.spst, 8 * (W + 1));
   take(L.spc, 8 * (W + 1));
   take(L.ps, 8 * (W + 1));
+  take(L.tile_sp_eout, 4 * (T + 1));
+  take(L.tile_sp_unres, 4 * (T + 1));
   take(L.tile_fn, 8 * (T + 1));
   take(L.tile_carry, 4 * (T + 1));
   take(L.tile_np, 4 * (T + 1));
@@ -106,6 +108,7 @@ __global__ void k_init(EncodeArgs a) {
     for (uint32_t k = 0; k < ML_COUNT; ++k) s->n_list[k] = 0;
   s->scan_ticket = 0;
   s->scan_fail = 0;
+  s->sp_fix = 0;
     s->n_chars = 0;
     s->err_seg = 0;
     // offsets must start at 0 and end at the text length (monotonicity is
@@ -215,6 +218,8 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
   a.ws.spst = reinterpret_cast<uint64_t *>(w + L.spst);
   a.ws.spc = reinterpret_cast<uint64_t *>(w + L.spc);
   a.ws.ps = reinterpret_cast<uint64_t *>(w + L.ps);
+  a.ws.tile_sp_eout = reinterpret_cast<uint32_t *>(w + L.tile_sp_eout);
+  a.ws.tile_sp_unres = reinterpret_cast<uint32_t *>(w + L.tile_sp_unres);
   a.ws.tile_fn = reinterpret_cast<uint64_t *>(w + L.tile_fn);
   a.ws.tile_carry = reinterpret_cast<uint32_t *>(w + L.tile_carry);
   a.ws.tile_np = reinterpret_cast<uint32_t *>(w + L.tile_np);
@@ -258,6 +263,10 @@ void launch_front(Go &go, const EncodeArgs &a, const WsLayout &L) {
   go("k_count", k_count, dim3(T), dim3(64), a);
   if (T > FUSE_TILES) go("k_scan_chars", k_scan_chars, dim3(1), dim3(1024), a);
   go("k_spans", k_spans, dim3(T), dim3(64), a);
+  if (a.T.sp_overlap) {
+    go("k_specials", k_specials, dim3(T), dim3(64), a);
+    go("k_specials_fix", k_specials_fix, dim3(1), dim3(64), a);
+  }
   if (a.T.grammar == BBPE_GRAMMAR_O200K_STYLE) {
     go("k_split_agg_o200k", k_split_agg_o200k, dim3(T), dim3(64), a);
     if (T > FUSE_TILES) go("k_scan_split_o200k", k_scan_split_o200k, dim3(1), dim3(1024), a);

@@ -106,6 +106,7 @@ __device__ __forceinline__ void init_status(const EncodeArgs &a, unsigned long l
   for (uint32_t k = 0; k < ML_COUNT; ++k) s->n_list[k] = 0;
   s->scan_ticket = 0;
   s->scan_fail = 0;
+  s->sp_fix = 0;
   s->err_seg = 0;
   s->n_chars = n_chars;
   // offsets start at 0, end at the text length and never decrease; every
@@ -417,7 +418,7 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
       any_allow = a.allow[s] != 0;
     }
   }
-  if (any_allow) {
+  if (any_allow && !a.T.sp_overlap) {
     uint32_t s = seg_at;
     // candidates: bytes equal to a special's first byte (an exact per-byte
     // zero test of the window dwords xor the byte), when there are few
@@ -471,6 +472,208 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
       if (sp_in_next) atomicOr(reinterpret_cast<unsigned long long *>(&a.ws.spc[w + 1]), sp_in_next);
       if (ss_end_next) atomicOr(reinterpret_cast<unsigned long long *>(&a.ws.ss[w + 1]), ss_end_next);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Step 3b (special sets whose occurrences can overlap, e.g. "xyx", or
+// "<|a|>" with "|>b"): the special pass as the leftmost-first scan of the
+// tiktoken page ("Special tokens"): in each chunk of an allow_special
+// segment, the leftmost position where a special occurs entirely inside the
+// chunk starts one, and the scan resumes after it.  k_spans has written the
+// chunk cuts and segment starts (SS) and no specials.  A word's choices
+// depend on how far a special chosen in the word before covers it; each
+// lane of a tile runs the scan over its word for an incoming coverage, and
+// the coverages pass from lane to lane until none changes (one step per
+// lane of a chain at most).  The coverage entering a tile comes from a walk
+// back from its start to a position that no occurrence covers (its state is
+// known there), then the scan forward from that position; a tile whose walk
+// back passes SP_WALK_MAX bytes is left to k_specials_fix, which resolves
+// such tiles in text order from their predecessors' outgoing coverage.
+// (Only long unbroken runs of overlapping occurrences, such as "xyxyxy..."
+// for a special "xyx", come near the limit; tiktoken-safe chunking cuts
+// them at 25,000 characters.)
+// ---------------------------------------------------------------------------
+constexpr uint64_t SP_WALK_MAX = 16384;
+
+// Bytes of the 64-byte word at wi that are the first byte of some special.
+__device__ __forceinline__ uint64_t sp_first_mask(const EncodeArgs &a, uint64_t wi) {
+  uint64_t m = 0;
+  const uint64_t b0 = wi * 64;
+  for (uint32_t q = 0; q < 16; ++q) {
+    const uint64_t addr = b0 + 4 * q;
+    if (addr >= a.n) break;
+    uint32_t v = 0;
+    if (addr + 4 <= a.n) {
+      v = *reinterpret_cast<const uint32_t *>(a.text + addr);
+    } else {
+      for (uint32_t j = 0; addr + j < a.n; ++j) v |= uint32_t(a.text[addr + j]) << (8 * j);
+    }
+    for (uint32_t j = 0; j < 4 && addr + j < a.n; ++j) {
+      const uint32_t b = (v >> (8 * j)) & 0xFFu;
+      if ((a.T.sp_first[b >> 5] >> (b & 31)) & 1) m |= uint64_t(1) << (4 * q + j);
+    }
+  }
+  return m;
+}
+
+// Length of the special occurring at byte p, or 0: in an allow_special
+// segment, entirely inside it, with no chunk cut or segment start strictly
+// inside.  (The specials are prefix-free: at most one occurs at p.)
+__device__ uint32_t sp_match_len(const EncodeArgs &a, uint64_t p) {
+  const uint32_t b0 = a.text[p];
+  if (!((a.T.sp_first[b0 >> 5] >> (b0 & 31)) & 1)) return 0;
+  uint32_t lo = 0, hi = a.n_seg;  // the segment holding p: the last starting at or before it
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (a.seg_off[mid] <= p) lo = mid + 1;
+    else hi = mid;
+  }
+  const uint32_t seg = lo > 0 ? lo - 1 : 0;
+  if (!a.allow[seg]) return 0;
+  const uint64_t end = min(a.seg_off[seg + 1], a.n);
+  for (uint32_t k = 0; k < a.T.n_sp; ++k) {
+    const uint32_t o = a.T.sp_off[k], L = a.T.sp_off[k + 1] - o;
+    if (p + L > end) continue;
+    bool eq = true;
+    for (uint32_t j = 0; j < L && eq; ++j) eq = a.text[p + j] == a.T.sp_bytes[o + j];
+    if (!eq) continue;
+    for (uint64_t q = p + 1; q < p + L; ++q)
+      if ((a.ws.ss[q >> 6] >> (q & 63)) & 1) return 0;
+    return L;
+  }
+  return 0;
+}
+
+// The coverage entering byte x: bytes from x on that a special chosen before
+// x covers (0: none).  One lane; false when the walk back passes
+// SP_WALK_MAX bytes.
+__device__ bool sp_cover_into(const EncodeArgs &a, uint64_t x, uint32_t &cov_out) {
+  uint64_t s = x;
+  for (;;) {
+    // an occurrence starting in [s - 63, s) that covers s?
+    const uint64_t lo = s >= 63 ? s - 63 : 0;
+    uint64_t best = s;
+    for (uint64_t wi = lo >> 6; wi * 64 < s; ++wi) {
+      uint64_t m = sp_first_mask(a, wi);
+      while (m) {
+        const uint64_t p = wi * 64 + uint64_t(__ffsll(static_cast<unsigned long long>(m)) - 1);
+        m &= m - 1;
+        if (p < lo || p >= s || p >= best) continue;
+        const uint32_t L = sp_match_len(a, p);
+        if (L && p + L > s) best = p;
+      }
+    }
+    if (best == s) break;  // no occurrence covers s: nothing chosen before covers it either
+    if (x - best > SP_WALK_MAX) return false;
+    s = best;
+  }
+  uint64_t cov = s;  // the scan forward from s to x
+  for (uint64_t wi = s >> 6; wi * 64 < x; ++wi) {
+    uint64_t m = sp_first_mask(a, wi);
+    while (m) {
+      const uint64_t p = wi * 64 + uint64_t(__ffsll(static_cast<unsigned long long>(m)) - 1);
+      m &= m - 1;
+      if (p < cov || p >= x) continue;
+      const uint32_t L = sp_match_len(a, p);
+      if (L) cov = p + L;
+    }
+  }
+  cov_out = cov > x ? uint32_t(cov - x) : 0u;
+  return true;
+}
+
+// The scan over one word entering with `cov` bytes covered: vm marks the
+// bytes where a special occurs, lp[b] bit i is bit b of that special's
+// length - 1.  Returns the coverage passed on; st, in_lo / in_hi: the
+// starts chosen and the bytes inside them in this word / the next.
+__device__ __forceinline__ uint32_t sp_scan_word(uint64_t vm, const uint64_t (&lp)[6], uint32_t cov,
+                                                 uint64_t &st, uint64_t &in_lo, uint64_t &in_hi) {
+  st = in_lo = in_hi = 0;
+  uint64_t c = cov >= 64 ? 0 : (vm & ~((uint64_t(1) << cov) - 1));
+  while (c) {
+    const int i = __ffsll(static_cast<unsigned long long>(c)) - 1;
+    uint32_t L = 1;
+#pragma unroll
+    for (int b = 0; b < 6; ++b) L += uint32_t((lp[b] >> i) & 1) << b;
+    const int e = i + int(L);  // in [i + 1, i + 64]
+    st |= uint64_t(1) << i;
+    const uint64_t from_i = ~((uint64_t(1) << i) - 1);
+    in_lo |= e >= 64 ? from_i : (from_i & ((uint64_t(1) << e) - 1));
+    if (e > 64) in_hi |= e - 64 >= 64 ? ~0ull : ((uint64_t(1) << (e - 64)) - 1);
+    cov = uint32_t(e);
+    c = e >= 64 ? 0 : (c & ~((uint64_t(1) << e) - 1));
+  }
+  return cov > 64 ? cov - 64 : 0u;
+}
+
+// The special pass of tile t, given the coverage entering its first owned
+// word; writes SPST / SPC and the coverage leaving the tile.  All lanes.
+__device__ void sp_tile(const EncodeArgs &a, uint32_t t, int lane, uint32_t cov_first) {
+  const int64_t w = int64_t(t) * TILE_WORDS + lane - 1;
+  const bool owned = lane >= 1 && lane <= int(TILE_WORDS) && w < int64_t(a.n_words);
+  const uint64_t base = owned ? uint64_t(w) * 64 : 0;
+  // the word's occurrences, found once
+  uint64_t vm = 0, lp[6] = {0, 0, 0, 0, 0, 0};
+  if (owned) {
+    for (uint64_t c = sp_first_mask(a, uint64_t(w)); c; c &= c - 1) {
+      const int i = __ffsll(static_cast<unsigned long long>(c)) - 1;
+      const uint32_t L = sp_match_len(a, base + uint64_t(i));
+      if (!L) continue;
+      vm |= uint64_t(1) << i;
+#pragma unroll
+      for (int b = 0; b < 6; ++b) lp[b] |= uint64_t(((L - 1) >> b) & 1) << i;
+    }
+  }
+  uint32_t cin = lane == 1 ? cov_first : 0u;
+  uint64_t st = 0, in_lo = 0, in_hi = 0;
+  uint32_t out = 0;
+  for (int it = 0; it < 64; ++it) {  // a chain passes one more lane per step
+    out = sp_scan_word(vm, lp, cin, st, in_lo, in_hi);
+    uint32_t nin = __shfl_up(out, 1, 64);
+    if (lane == 1) nin = cov_first;
+    if (lane == 0 || !owned) nin = 0;
+    if (!__ballot(nin != cin)) break;
+    cin = nin;
+  }
+  if (owned) {
+    if (st) atomicOr(reinterpret_cast<unsigned long long *>(&a.ws.spst[w]), st);
+    if (in_lo) atomicOr(reinterpret_cast<unsigned long long *>(&a.ws.spc[w]), in_lo);
+    if (in_hi && w + 1 < int64_t(a.n_words))
+      atomicOr(reinterpret_cast<unsigned long long *>(&a.ws.spc[w + 1]), in_hi);
+  }
+  const uint32_t last = __shfl(out, int(TILE_WORDS), 64);
+  if (lane == 0) a.ws.tile_sp_eout[t] = last;
+}
+
+__global__ void __launch_bounds__(64) k_specials(EncodeArgs a) {
+  if (a.ws.status->pad2) return;
+  const int lane = threadIdx.x;
+  const uint32_t t = blockIdx.x;
+  uint32_t cov = 0, ok = 1;
+  if (lane == 0 && t > 0) ok = sp_cover_into(a, uint64_t(t) * TILE_BYTES, cov) ? 1u : 0u;
+  ok = __shfl(ok, 0, 64);
+  cov = __shfl(cov, 0, 64);
+  if (lane == 0) a.ws.tile_sp_unres[t] = ok ? 0u : 1u;
+  if (!ok) {
+    if (lane == 0) atomicOr(&a.ws.status->sp_fix, 1u);
+    return;
+  }
+  sp_tile(a, t, lane, cov);
+}
+
+// The tiles k_specials left, in text order, each from the coverage leaving
+// the tile before it (one wave; nothing to do unless sp_fix is set).
+__global__ void __launch_bounds__(64) k_specials_fix(EncodeArgs a) {
+  if (a.ws.status->pad2 || !a.ws.status->sp_fix) return;
+  const int lane = threadIdx.x;
+  uint32_t prev = 0;  // coverage leaving tile t - 1
+  for (uint32_t t = 0; t < a.n_tiles; ++t) {
+    if (a.ws.tile_sp_unres[t]) {
+      sp_tile(a, t, lane, prev);
+      __syncthreads();  // (lane 0's store of the tile's coverage, then everyone's load)
+    }
+    prev = a.ws.tile_sp_eout[t];
   }
 }
 

@@ -107,6 +107,8 @@ struct DevTables {
   uint32_t sp_firsts;       // ... those bytes, one per byte lane
   int32_t grammar;
   uint32_t max_key_len;
+  uint32_t sp_overlap;      // 1: two occurrences of specials can overlap (the special pass
+                            //    then runs in k_specials)
 };
 
 // Byte offsets of each table inside the uploaded image.
@@ -136,6 +138,7 @@ struct Status {
   unsigned int n_list[8];         // units to merge per length class (MergeList)
   unsigned int scan_ticket;       // next tile of the id-count scan (k_assemble)
   unsigned int scan_fail;         // nonzero: a scan tile's wait for its predecessors gave up
+  unsigned int sp_fix;            // nonzero: k_specials left tiles to k_specials_fix
 };
 
 // Merge-unit lists by length class: the short tier (one lane per unit,

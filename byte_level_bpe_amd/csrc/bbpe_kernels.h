@@ -25,6 +25,9 @@ struct WsPtrs {
   unsigned long long *seg_charstart;  // [S+1]
   uint64_t *ss, *spst, *spc;        // [W] span start / special start / inside special
   uint64_t *ps;                     // [W] piece starts
+  uint32_t *tile_sp_eout;           // [T] (specials that can overlap) bytes of the next tile
+                                    //     that the tile's last special covers
+  uint32_t *tile_sp_unres;          // [T] 1: the tile's special pass is left to k_specials_fix
   uint64_t *tile_fn;                // [T] split transfer functions
   uint32_t *tile_carry;             // [T] split state entering each tile
   uint32_t *tile_np;                // [T+1] pieces per tile, then their exclusive scan
@@ -104,6 +107,8 @@ struct EncodeArgs {
 __global__ void k_count(EncodeArgs a);
 __global__ void k_scan_chars(EncodeArgs a);
 __global__ void k_spans(EncodeArgs a);
+__global__ void k_specials(EncodeArgs a);
+__global__ void k_specials_fix(EncodeArgs a);
 __global__ void k_split_agg(EncodeArgs a);
 __global__ void k_scan_split(EncodeArgs a);
 __global__ void k_split(EncodeArgs a);

@@ -249,9 +249,12 @@ template <int G>
 __device__ __forceinline__ void split_word(const EncodeArgs &a, int64_t w, const WordMasks &m,
                                            SplitWord &o) {
   const bool inrange = w >= 0 && w < int64_t(a.n_words);
-  const uint64_t SS = inrange ? a.ws.ss[w] : 0;
   const uint64_t SPST = inrange ? a.ws.spst[w] : 0;
   const uint64_t SPC = inrange ? a.ws.spc[w] : 0;
+  // a span also starts right after every special (the first byte outside
+  // one after a byte inside), whichever pass chose the special
+  const uint64_t SPCq = shfl_up64(SPC, 1);
+  const uint64_t SS = (inrange ? a.ws.ss[w] : 0) | (shl(SPC, SPCq, 1) & ~SPC & m.valid);
   const uint64_t IN = m.valid & ~SPC;
   const uint64_t BRK = SS | SPST | ~m.valid;
   const uint64_t L_ = m.L & IN, N_ = m.N & IN, WS_ = m.WS & IN, CR_ = m.CR & IN, SP_ = m.SP & IN;

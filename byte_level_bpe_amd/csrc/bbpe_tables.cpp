@@ -131,11 +131,12 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
     seen.insert(spid[i]);
     max_id = std::max(max_id, spid[i]);
   }
+  bool overlap = false;
   for (size_t i = 0; i < sp.size(); ++i)
     for (size_t j = 0; j < sp.size(); ++j) {
       if (i != j && sp[j].size() >= sp[i].size() && sp[j].compare(0, sp[i].size(), sp[i]) == 0)
         return BBPE_E_SPECIAL;  // prefix
-      if (can_overlap(sp[i], sp[j])) return BBPE_E_SPECIAL;
+      overlap = overlap || can_overlap(sp[i], sp[j]);
     }
 
   t->n_ranks = n;
@@ -335,6 +336,7 @@ int build(bbpe_tokenizer *t, std::vector<std::string> &keys, std::vector<int32_t
   }
   d.grammar = t->grammar;
   d.max_key_len = max_len;
+  d.sp_overlap = overlap ? 1u : 0u;
   return BBPE_OK;
 }
 

@@ -101,9 +101,13 @@ enum {
  * single-byte key (all 256 must be present).  Rejected with BBPE_E_SPECIAL:
  * more than BBPE_MAX_SPECIALS specials, an empty special, one longer than
  * BBPE_MAX_SPECIAL_BYTES, one that is not valid UTF-8, a duplicate string or
- * id, an id that is also a rank, one special that is a prefix of another, or
- * two specials that can overlap in some text (a proper suffix of one equal to
- * a proper prefix of another, or one inside another).
+ * id, an id that is also a rank, or one special that is a prefix of another
+ * (so at most one special can start at any byte).  Specials whose occurrences
+ * can overlap in a text (a proper suffix of one equal to a proper prefix of
+ * another, as "<|a|>" and "|>b", or one inside another not at its start) are
+ * accepted: the encoder takes the leftmost occurrence, resumes the search
+ * after its end, and never matches across a segment boundary (tiktoken
+ * deep-dive page, "Special tokens").
  * On success *out receives the handle and *device_table_bytes the size of the
  * device memory that bbpe_upload_tables needs.  The library copies what it
  * needs; the caller keeps ownership of every input. */

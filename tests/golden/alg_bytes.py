@@ -21,7 +21,7 @@ byte pair there occurs inside no key; or, at a character boundary, it is no
 across it has its bit set in the GPU's hashed 4-gram bitmap).  A unit that is
 a special, a single byte, or a key that the loop merges back into itself is
 settled by k_probe; every other unit goes to the merge kernel of its length
-class (k_merge 2-32 bytes, k_merge_group 33-512, k_merge_long longer).
+class (k_merge 2-16 bytes, k_merge_wide 17-512, k_merge_long longer).
 """
 from __future__ import annotations
 
@@ -47,7 +47,7 @@ def q4_index(w4: bytes) -> int:
 
 
 def tier_of(m: int) -> str:
-    return "k_merge" if m <= 32 else "k_merge_group" if m <= 512 else "k_merge_long"
+    return "k_merge" if m <= 16 else "k_merge_wide" if m <= 512 else "k_merge_long"
 
 
 def count(name: str) -> dict:
@@ -85,7 +85,7 @@ def count(name: str) -> dict:
     n_seg = len(w.segments)
 
     per = {k: {"units": 0, "bytes": 0, "ids": 0, "lookup_bytes": 0}
-           for k in ("k_probe", "k_merge", "k_merge_group", "k_merge_long")}
+           for k in ("k_probe", "k_merge", "k_merge_wide", "k_merge_long")}
     memo = {}  # unit bytes -> (ids, lookup bytes of the merge loop)
 
     def merge_cost(u: bytes):
@@ -102,7 +102,7 @@ def count(name: str) -> dict:
     bounds = [int(x) for x in starts] + [len(text)]
     for i in range(len(starts)):
         p = text[bounds[i]:bounds[i + 1]]
-        if spec[i] or p.isascii():
+        if spec[i]:
             units = [p]
         else:
             units, a = [], 0

@@ -167,6 +167,64 @@ def test_specials_fuzz(atoms):
     assert_ids(tok, orc, segs, what="specials")
 
 
+# Special sets whose occurrences can overlap: a suffix of one is a prefix of
+# another, one overlaps itself, one sits inside another.  The special pass
+# takes the leftmost occurrence and resumes after it (tiktoken deep-dive
+# page, "Special tokens"); the oracle defines the ids.
+OVERLAP_SETS = [
+    [(b"<|a|>", 300000), (b"|>b", 300001)],
+    [(b"xyx", 300000)],
+    [(b"xyx", 300000), (b"yxy", 300001), (b"<|e|>", 300002)],
+    [(b"ab", 300000), (b"ba", 300001), (b"<|ab|>", 300002)],
+]
+
+
+@pytest.mark.parametrize("k", range(len(OVERLAP_SETS)))
+def test_overlapping_specials(k):
+    specials = OVERLAP_SETS[k]
+    tok, orc = make(atoms_permuted(1), specials, 0)
+    r = random.Random(40 + k)
+    sp = [x for x, _ in specials]
+    alpha = sorted(set(b"".join(sp))) + [ord(" "), ord("\n"), ord("q")]
+    segs = []
+    for _ in range(600):
+        parts = []
+        for _ in range(r.randint(0, 10)):
+            x = r.random()
+            if x < 0.35:
+                parts.append(r.choice(sp))
+            elif x < 0.5:
+                parts.append(r.choice(sp)[r.randint(1, 3):])  # a suffix starts an overlap
+            else:
+                parts.append(bytes(r.choice(alpha) for _ in range(r.randint(0, 12))))
+        segs.append((b"".join(parts), r.random() < 0.7))
+    say("overlapping specials, set", k, "dense segments")
+    assert_pieces(tok, orc, segs, what="overlap %d" % k)
+    assert_ids(tok, orc, segs, what="overlap %d" % k)
+    # long runs of overlapping occurrences across words and tiles (the
+    # coverage entering a tile found by the walk back), under chunking and
+    # without it, between ordinary text and at segment edges
+    run = (sp[0] * 3000)[:9001] if k != 1 else b"xy" * 5000 + b"x"
+    long_segs = [(b"lead " + run + b" tail", True), (run, False), (b"q" + run[:4097], True),
+                 (run[1:], True)]
+    for safe in (True, False):
+        say("overlapping specials, set", k, "long runs, chunked", safe)
+        assert_pieces(tok, orc, long_segs, safe, what="overlap runs %d" % k)
+        assert_ids(tok, orc, long_segs, safe, what="overlap runs %d" % k)
+
+
+def test_overlapping_specials_chain_past_walk_limit():
+    """A chain of overlapping occurrences longer than the walk back from a
+    tile's start may take (unchunked): those tiles resolve in text order."""
+    specials = [(b"xyx", 300000)]
+    tok, orc = make(atoms_permuted(1), specials, 0)
+    run = b"xy" * 20_000 + b"x"  # 40 KB, one chain
+    segs = [(b"a " + run + b" b", True), (run[:20_001], True)]
+    say("overlapping specials, chain of 40 KB, unchunked")
+    assert_ids(tok, orc, segs, False, what="long chain")
+    assert_pieces(tok, orc, segs, False, what="long chain")
+
+
 # -------------------------------------------------------------- chunking ----
 
 def test_chunking_space_run_and_windows(atoms):
