@@ -30,6 +30,7 @@ E_BAD_ID = -6
 E_HIP = -7
 E_WORKSPACE = -8
 E_STATE = -9
+E_NOMEM = -10
 GRAMMAR_CL100K = 0
 GRAMMAR_O200K_STYLE = 1
 GRAMMAR_R50K_STYLE = 2
@@ -42,7 +43,8 @@ EXPORTS = ["bbpe_load_ranks", "bbpe_load_ranks_tiktoken_file", "bbpe_upload_tabl
            "bbpe_workspace_bytes", "bbpe_encode_segments", "bbpe_encode_segments_noalloc",
            "bbpe_pretokenize_segments",
            "bbpe_decode", "bbpe_decode_workspace_bytes", "bbpe_decode_device",
-           "bbpe_token_offsets_device", "bbpe_error_detail",
+           "bbpe_token_offsets_device", "bbpe_stream_decoder_create", "bbpe_stream_decoder_free",
+           "bbpe_stream_decoder_reset", "bbpe_stream_decode_device", "bbpe_error_detail",
            "bbpe_table_info", "bbpe_set_timing", "bbpe_timing_report", "bbpe_timing_reset",
            "bbpe_free", "bbpe_status_str"]
 
@@ -90,6 +92,14 @@ def _load():
                                            C.POINTER(U64), P]
         lib.bbpe_token_offsets_device.restype = I
         lib.bbpe_token_offsets_device.argtypes = [P, P, U64, P, P, U64, C.POINTER(U64), P]
+        lib.bbpe_stream_decoder_create.restype = I
+        lib.bbpe_stream_decoder_create.argtypes = [P, C.POINTER(P)]
+        lib.bbpe_stream_decoder_free.restype = I
+        lib.bbpe_stream_decoder_free.argtypes = [P]
+        lib.bbpe_stream_decoder_reset.restype = I
+        lib.bbpe_stream_decoder_reset.argtypes = [P]
+        lib.bbpe_stream_decode_device.restype = I
+        lib.bbpe_stream_decode_device.argtypes = [P, P, U64, I, P, U64, P, U64, C.POINTER(U64), P]
         lib.bbpe_error_detail.restype = I
         lib.bbpe_error_detail.argtypes = [P, C.POINTER(U32), C.POINTER(U64)]
         lib.bbpe_table_info.restype = I
@@ -402,6 +412,63 @@ class Tokenizer:
         if st:
             raise BBPEError(st, "decode")
         return out[:n.value].tobytes()
+
+
+class StreamDecoder:
+    """Incremental decode on the device that holds back a trailing partial
+    UTF-8 character between calls (bbpe_stream_decode_device)."""
+
+    def __init__(self, tok: "Tokenizer"):
+        self._tok = tok  # the tokenizer must outlive the decoder
+        h = C.c_void_p()
+        st = _load().bbpe_stream_decoder_create(tok._h, C.byref(h))
+        if st:
+            raise BBPEError(st, "stream_decoder_create")
+        self._h = h
+
+    def feed(self, ids, final: bool = False, out=None, stream=None):
+        """Decode an int32 id tensor; returns the emitted bytes as a uint8
+        tensor (a view of `out`, sized 8 bytes per id + 3 when not given)."""
+        import torch
+        dev = ids.device
+        tok = self._tok
+        tok.upload(dev)
+        n_ids = int(ids.numel())
+        dws = tok._decode_workspace(n_ids, dev)
+        sized = out is not None
+        if out is None:
+            out = torch.empty(8 * n_ids + 3, dtype=torch.uint8, device=dev)
+        n = C.c_uint64(0)
+
+        def call(buf):
+            return _load().bbpe_stream_decode_device(
+                self._h, C.c_void_p(ids.data_ptr()) if n_ids else None, n_ids, 1 if final else 0,
+                C.c_void_p(buf.data_ptr()), buf.numel(), C.c_void_p(dws.data_ptr()), dws.numel(),
+                C.byref(n), _stream_handle(stream))
+        with tok._lock:
+            st = call(out)
+            if st == E_CAPACITY and not sized:
+                out = torch.empty(n.value + 3, dtype=torch.uint8, device=dev)
+                st = call(out)
+        if st == E_BAD_ID:
+            raise BBPEError(st, "stream_decode_device at index %d" % n.value)
+        if st:
+            raise BBPEError(st, "stream_decode_device")
+        return out[:n.value]
+
+    def reset(self):
+        _load().bbpe_stream_decoder_reset(self._h)
+
+    def close(self):
+        if self._h:
+            _load().bbpe_stream_decoder_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def to_device_segments(segments, device="cuda"):

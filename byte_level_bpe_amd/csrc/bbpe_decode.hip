@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <new>
 
 #include <algorithm>
 
@@ -33,7 +34,9 @@ struct DecStatus {
   unsigned long long first_bad;  // index of the first id that is neither rank nor special, or ~0
   unsigned long long total;      // output bytes
   unsigned long long complete;   // bytes up to the end of the last complete character
-  unsigned long long pad;
+                                 // (carried bytes included)
+  unsigned long long tail;       // the last three bytes (carried bytes included), the
+                                 // last in bits 0-7
 };
 
 struct DecArgs {
@@ -48,6 +51,8 @@ struct DecArgs {
   unsigned long long *bad;     // [blocks] first bad index of each tile, or ~0
   DecStatus *st;
   uint32_t vec_ids, vec_off;   // ids / tok_off 16-byte aligned: vector loads / stores
+  uint32_t carry, n_carry;     // bytes a stream decoder held back (n_carry <= 3, the first
+                               // in bits 0-7), placed just before out
 };
 
 // offset << 8 | length of an id's bytes in the decode blob, or 0 (bad id)
@@ -301,7 +306,11 @@ __global__ void __launch_bounds__(DEC_BLOCK) k_dec_copy(DecArgs a) {
   // bytes (k <= 3) are a proper prefix of a well-formed UTF-8 sequence (the
   // Unicode standard's table of well-formed byte sequences: lead C2-DF,
   // E0-EF or F0-F4, the second byte's range set by the lead), they are held
-  // back.  The last bytes are read from the last tokens (each has >= 1 byte).
+  // back.  The last bytes are read from the last tokens (each has >= 1 byte),
+  // then from the carried bytes before them.  Block 0 writes the carried
+  // bytes.
+  if (blockIdx.x == 0 && threadIdx.x == 0 && total <= a.cap)
+    for (uint32_t j = 0; j < a.n_carry; ++j) a.out[int64_t(j) - int64_t(a.n_carry)] = uint8_t(a.carry >> (8 * j));
   if (blockIdx.x == nblk - 1 && threadIdx.x == 0) {
     uint32_t tail[3] = {0, 0, 0};  // tail[k-1] = output byte total - k
     uint32_t got = 0;
@@ -310,7 +319,9 @@ __global__ void __launch_bounds__(DEC_BLOCK) k_dec_copy(DecArgs a) {
       const uint8_t *src = a.T.dblob + (et >> 8);
       for (uint32_t j = uint32_t(et & 0xFFu); j > 0 && got < 3; --j) tail[got++] = src[j - 1];
     }
-    uint64_t complete = total;
+    for (uint32_t j = a.n_carry; j > 0 && got < 3; --j) tail[got++] = (a.carry >> (8 * (j - 1))) & 0xFFu;
+    const uint64_t all = total + a.n_carry;
+    uint64_t complete = all;
     for (uint32_t k = 1; k <= got; ++k) {
       const uint32_t b = tail[k - 1];
       if ((b & 0xC0u) == 0x80u) continue;
@@ -325,12 +336,18 @@ __global__ void __launch_bounds__(DEC_BLOCK) k_dec_copy(DecArgs a) {
           const uint32_t hi = b == 0xED ? 0x9Fu : b == 0xF4 ? 0x8Fu : 0xBFu;
           ok = s >= lo && s <= hi;
         }
-        if (ok) complete = total - k;
+        if (ok) complete = all - k;
       }
       break;
     }
     a.st->complete = complete;
+    a.st->tail = tail[0] | (tail[1] << 8) | (tail[2] << 16);
   }
+}
+
+// The carried bytes alone (a stream decoder's final call with no ids).
+__global__ void k_dec_carry(uint8_t *out, uint32_t carry, uint32_t n_carry) {
+  for (uint32_t j = 0; j < n_carry; ++j) out[j] = uint8_t(carry >> (8 * j));
 }
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -363,9 +380,11 @@ int bbpe_decode_workspace_bytes(const bbpe_tokenizer *t, uint64_t n_ids, uint64_
   return BBPE_OK;
 }
 
+// d_out / out_capacity: where the ids' bytes go; n_carry carried bytes are
+// written just before d_out.
 static int decode_run(bbpe_tokenizer *t, const int32_t *d_ids, uint64_t n_ids, uint8_t *d_out,
                       uint64_t out_capacity, uint64_t *d_tok_off, void *d_ws, uint64_t ws_bytes,
-                      void *stream, DecStatus &h) {
+                      void *stream, DecStatus &h, uint32_t carry = 0, uint32_t n_carry = 0) {
   if (!t->d_image) return BBPE_E_STATE;
   const DecLayout L = dec_layout(n_ids);
   if (!d_ws || ws_bytes < L.total || (reinterpret_cast<uintptr_t>(d_ws) & 255)) return BBPE_E_WORKSPACE;
@@ -388,6 +407,8 @@ static int decode_run(bbpe_tokenizer *t, const int32_t *d_ids, uint64_t n_ids, u
   a.pre = reinterpret_cast<unsigned long long *>(w + L.pre);
   a.vec_ids = (reinterpret_cast<uintptr_t>(d_ids) & 15) == 0;
   a.vec_off = (reinterpret_cast<uintptr_t>(d_tok_off) & 15) == 0;
+  a.carry = carry;
+  a.n_carry = n_carry;
   Launcher go{t, reinterpret_cast<hipStream_t>(stream)};
   const uint32_t nb = uint32_t((n_ids + DEC_TILE - 1) / DEC_TILE);
   go("k_dec_len", k_dec_len, dim3(nb), dim3(DEC_BLOCK), a);
@@ -415,6 +436,86 @@ int bbpe_decode_device(bbpe_tokenizer *t, const int32_t *d_ids, uint64_t n_ids, 
   *out_len = h.total;
   if (complete_len) *complete_len = h.complete;
   return h.total > out_capacity ? BBPE_E_CAPACITY : BBPE_OK;
+}
+
+}  // extern "C"
+
+// A stream decoder: the bytes held back at the end of the last call.
+struct bbpe_stream_decoder {
+  bbpe_tokenizer *tok;
+  uint32_t held, n_held;  // n_held <= 3 bytes, the first in bits 0-7
+};
+
+extern "C" {
+
+int bbpe_stream_decoder_create(bbpe_tokenizer *tok, bbpe_stream_decoder **out) {
+  if (!tok || !out) return BBPE_E_INVALID_ARG;
+  *out = new (std::nothrow) bbpe_stream_decoder{tok, 0, 0};
+  return *out ? BBPE_OK : BBPE_E_NOMEM;
+}
+
+int bbpe_stream_decoder_free(bbpe_stream_decoder *dec) {
+  delete dec;
+  return BBPE_OK;
+}
+
+int bbpe_stream_decoder_reset(bbpe_stream_decoder *dec) {
+  if (!dec) return BBPE_E_INVALID_ARG;
+  dec->held = dec->n_held = 0;
+  return BBPE_OK;
+}
+
+int bbpe_stream_decode_device(bbpe_stream_decoder *dec, const int32_t *d_ids, uint64_t n_ids, int final,
+                              uint8_t *d_out, uint64_t out_capacity, void *d_ws, uint64_t ws_bytes,
+                              uint64_t *out_len, void *stream) {
+  if (!dec || !out_len || (n_ids && !d_ids) || (out_capacity && !d_out)) return BBPE_E_INVALID_ARG;
+  bbpe_tokenizer *t = dec->tok;
+  const uint32_t nh = dec->n_held;
+  if (n_ids == 0) {  // only the held bytes: emitted when final, else still held
+    if (!final) {
+      *out_len = 0;
+      return BBPE_OK;
+    }
+    if (out_capacity < nh) {
+      *out_len = nh;
+      return BBPE_E_CAPACITY;
+    }
+    if (nh) {
+      std::lock_guard<std::mutex> lock(t->mu);
+      const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+      k_dec_carry<<<1, 1, 0, st>>>(d_out, dec->held, nh);
+      HIP_OK(hipGetLastError());
+      HIP_OK(hipStreamSynchronize(st));
+    }
+    *out_len = nh;
+    dec->held = dec->n_held = 0;
+    return BBPE_OK;
+  }
+  DecStatus h;
+  {
+    std::lock_guard<std::mutex> lock(t->mu);
+    const uint64_t cap = out_capacity >= nh ? out_capacity - nh : 0;
+    const int rc = decode_run(t, d_ids, n_ids, out_capacity >= nh ? d_out + nh : d_out, cap, nullptr, d_ws,
+                              ws_bytes, stream, h, dec->held, out_capacity >= nh ? nh : 0);
+    if (rc) return rc;
+    if (h.first_bad != ~0ull) {
+      *out_len = h.first_bad;
+      return BBPE_E_BAD_ID;
+    }
+    if (out_capacity < nh || h.total > cap) {
+      *out_len = h.total + nh;
+      return BBPE_E_CAPACITY;
+    }
+  }
+  const uint64_t all = h.total + nh;
+  const uint64_t emit = final ? all : h.complete;
+  const uint32_t k = uint32_t(all - emit);  // <= 3: a proper prefix of one character
+  uint32_t held = 0;
+  for (uint32_t j = 0; j < k; ++j) held |= ((uint32_t(h.tail) >> (8 * (k - 1 - j))) & 0xFFu) << (8 * j);
+  dec->held = held;
+  dec->n_held = k;
+  *out_len = emit;
+  return BBPE_OK;
 }
 
 int bbpe_token_offsets_device(bbpe_tokenizer *t, const int32_t *d_ids, uint64_t n_ids,

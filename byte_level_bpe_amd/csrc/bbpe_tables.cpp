@@ -525,6 +525,7 @@ const char *bbpe_status_str(int s) {
     case BBPE_E_HIP: return "HIP runtime error";
     case BBPE_E_WORKSPACE: return "workspace missing or too small";
     case BBPE_E_STATE: return "tables not uploaded";
+    case BBPE_E_NOMEM: return "host allocation failed";
     default: return "unknown status";
   }
 }

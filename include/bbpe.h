@@ -58,7 +58,8 @@ enum {
   BBPE_E_BAD_ID = -6,      /* decode met an id that is neither rank nor special */
   BBPE_E_HIP = -7,         /* a HIP runtime call failed */
   BBPE_E_WORKSPACE = -8,   /* workspace missing or smaller than required */
-  BBPE_E_STATE = -9        /* tables not uploaded yet */
+  BBPE_E_STATE = -9,       /* tables not uploaded yet */
+  BBPE_E_NOMEM = -10       /* a host allocation failed */
 };
 
 /* Split grammars.  CL100K is the pattern printed on the tiktoken deep-dive
@@ -246,6 +247,34 @@ int bbpe_decode_device(bbpe_tokenizer *tok, const int32_t *d_ids, uint64_t n_ids
                        uint8_t *d_out, uint64_t out_capacity, uint64_t *d_tok_off,
                        void *d_workspace, uint64_t workspace_bytes, uint64_t *out_len,
                        uint64_t *complete_len, void *hip_stream);
+
+/* Stateful streaming decode (tiktoken deep-dive page, "Pitfalls that bite
+ * in production": a token can end inside a UTF-8 character, so text that is
+ * shown as it is generated must hold back a trailing partial character until
+ * the tokens that complete it arrive).  A stream decoder keeps, between
+ * calls, the bytes of the trailing partial character of everything it has
+ * decoded (at most 3).  Each call decodes d_ids[n_ids] (device, int32) on
+ * the device and writes to d_out (device, capacity out_capacity) the held
+ * bytes followed by the ids' bytes; *out_len (host) receives how many of
+ * them are emitted: all of them when final != 0 (the decoder is then empty),
+ * else the longest prefix that ends on a complete UTF-8 character, the rest
+ * being held for the next call (bytes that cannot start or continue a
+ * well-formed character are emitted as they are).  Concatenating the
+ * emitted bytes of a sequence of calls, the last one final, gives the decode
+ * of all of their ids.  d_out receives up to out_len + 3 bytes.  Workspace,
+ * alignment, stream and synchronisation as bbpe_decode_device.  Errors leave
+ * the held bytes unchanged: BBPE_E_BAD_ID (*out_len = index of the first bad
+ * id in this call), BBPE_E_CAPACITY (*out_len = bytes needed).  A decoder
+ * belongs to one caller at a time (calls on one decoder must not overlap);
+ * it keeps a pointer to tok, which must outlive it.  bbpe_stream_decoder_reset
+ * drops the held bytes. */
+typedef struct bbpe_stream_decoder bbpe_stream_decoder;
+int bbpe_stream_decoder_create(bbpe_tokenizer *tok, bbpe_stream_decoder **out);
+int bbpe_stream_decoder_free(bbpe_stream_decoder *dec);
+int bbpe_stream_decoder_reset(bbpe_stream_decoder *dec);
+int bbpe_stream_decode_device(bbpe_stream_decoder *dec, const int32_t *d_ids, uint64_t n_ids, int final,
+                              uint8_t *d_out, uint64_t out_capacity, void *d_workspace,
+                              uint64_t workspace_bytes, uint64_t *out_len, void *hip_stream);
 
 /* Per-token byte offsets without decoding: d_tok_off[i] (device, uint64,
  * n_ids entries, 8-byte aligned) receives the byte offset of token i, that

@@ -161,6 +161,94 @@ def test_decode_tail_byte_patterns():
                 assert done == utf8_complete_len(data), data.hex()
 
 
+# --------------------------------------------------------- stream decode ----
+def stream_feed(dec, ids, final=False):
+    return dec.feed(dev_ids(ids), final=final).cpu().numpy().tobytes()
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_stream_decoder_random_chunks(tiny, seed):
+    """An encode's ids fed in random chunks (empty ones included): after each
+    call the bytes emitted so far are the decode of the ids fed so far up to
+    the oracle's complete-character length, and after the final call they
+    are the whole decode."""
+    w, tok, orc = tiny
+    text = ("ाइ हिन्दी का 中文字符 😀😀 mixed é \u00a0" * 6).encode()
+    ids = list(orc.encode(text))
+    r = random.Random(seed)
+    dec = B.StreamDecoder(tok)
+    say("stream decode random chunks seed=%d, %d ids" % (seed, len(ids)))
+    got, k = b"", 0
+    while k < len(ids):
+        c = r.choice([0, 1, 1, 2, 3, 5])
+        got += stream_feed(dec, ids[k:k + c])
+        k = min(len(ids), k + c)
+        ref = orc.decode(ids[:k]) if k else b""
+        assert got == ref[:utf8_complete_len(ref)], k
+    got += stream_feed(dec, [], final=True)
+    assert got == orc.decode(ids)
+    # the decoder is empty again: a second stream starts clean
+    assert stream_feed(dec, ids[:3], final=True) == orc.decode(ids[:3])
+
+
+def test_stream_decoder_byte_tails():
+    """One byte per call (atoms-only table): partial characters carried over
+    one, two and three calls, completed, or broken by a byte that cannot
+    continue them; the emitted length always equals the oracle's
+    complete-character length of everything fed."""
+    tokens = atoms_permuted(7)
+    tok = B.load_ranks(tokens)
+    id_of = {k[0]: v for k, v in tokens.items()}
+    vals = [0x41, 0x80, 0x9F, 0xA0, 0xBF, 0xC2, 0xE0, 0xED, 0xEF, 0xF0, 0xF4, 0xF5]
+    say("stream decode byte tails")
+    for pre in (b"a", "中".encode()):
+        for t in itertools.product(vals, repeat=3):
+            data = pre + bytes(t) + "é".encode()
+            dec = B.StreamDecoder(tok)
+            got = b""
+            for j in range(len(data)):
+                got += stream_feed(dec, [id_of[data[j]]])
+                assert got == data[:utf8_complete_len(data[:j + 1])], (data.hex(), j)
+            got += stream_feed(dec, [], final=True)
+            assert got == data, data.hex()
+
+
+def test_stream_decoder_errors_keep_the_held_bytes(tiny):
+    """A bad id or a too-small output leaves the held bytes as they were; an
+    empty non-final call emits nothing; reset drops the held bytes."""
+    w, tok, orc = tiny
+    text = "x中文".encode()
+    ids = list(orc.encode(text))
+    data = orc.decode(ids)
+    # find a prefix of ids that ends inside a character, if the table gives one
+    cut = next((k for k in range(1, len(ids)) if utf8_complete_len(orc.decode(ids[:k])) < len(orc.decode(ids[:k]))), None)
+    dec = B.StreamDecoder(tok)
+    first = stream_feed(dec, ids[:cut] if cut else ids[:1])
+    n0 = len(first)
+    with pytest.raises(B.BBPEError) as ei:
+        dec.feed(dev_ids([ids[0], 10 ** 9]))
+    assert ei.value.status == B.E_BAD_ID
+    assert stream_feed(dec, []) == b""
+    # too small through the C ABI: needs the held bytes plus the ids' bytes
+    rest = ids[cut:] if cut else ids[1:]
+    d = dev_ids(rest)
+    ws = torch.empty(tok.decode_workspace_bytes(len(rest)), dtype=torch.uint8, device="cuda")
+    out = torch.empty(len(data) + 8, dtype=torch.uint8, device="cuda")
+    n = C.c_uint64(0)
+    lib = B._load()
+    st = lib.bbpe_stream_decode_device(dec._h, C.c_void_p(d.data_ptr()), len(rest), 1,
+                                       C.c_void_p(out.data_ptr()), 1, C.c_void_p(ws.data_ptr()),
+                                       ws.numel(), C.byref(n), None)
+    assert st == B.E_CAPACITY and n.value == len(data) - n0
+    got = first + stream_feed(dec, rest, final=True)
+    assert got == data
+    # reset drops what is held
+    if cut:
+        dec.feed(dev_ids(ids[:cut]))
+        dec.reset()
+        assert stream_feed(dec, [], final=True) == b""
+
+
 # ------------------------------------------------------------ count only ----
 
 def test_count_only_matches_oracle_offsets(tiny):
