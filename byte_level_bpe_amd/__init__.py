@@ -36,6 +36,7 @@ GRAMMAR_O200K_STYLE = 1
 GRAMMAR_R50K_STYLE = 2
 TIKTOKEN_SAFE = 1
 COUNT_ONLY = 2
+KEEP_WORD_CACHE = 4
 NOALLOC_SCRATCH_BYTES = 48 << 20  # BBPE_NOALLOC_SCRATCH_BYTES
 
 # every symbol include/bbpe.h declares
@@ -44,7 +45,8 @@ EXPORTS = ["bbpe_load_ranks", "bbpe_load_ranks_tiktoken_file", "bbpe_upload_tabl
            "bbpe_pretokenize_segments",
            "bbpe_decode", "bbpe_decode_workspace_bytes", "bbpe_decode_device",
            "bbpe_token_offsets_device", "bbpe_stream_decoder_create", "bbpe_stream_decoder_free",
-           "bbpe_stream_decoder_reset", "bbpe_stream_decode_device", "bbpe_error_detail",
+           "bbpe_stream_decoder_reset", "bbpe_stream_decode_device", "bbpe_word_cache_clear",
+           "bbpe_word_cache_info", "bbpe_error_detail",
            "bbpe_table_info", "bbpe_set_timing", "bbpe_timing_report", "bbpe_timing_reset",
            "bbpe_free", "bbpe_status_str"]
 
@@ -100,6 +102,10 @@ def _load():
         lib.bbpe_stream_decoder_reset.argtypes = [P]
         lib.bbpe_stream_decode_device.restype = I
         lib.bbpe_stream_decode_device.argtypes = [P, P, U64, I, P, U64, P, U64, C.POINTER(U64), P]
+        lib.bbpe_word_cache_clear.restype = I
+        lib.bbpe_word_cache_clear.argtypes = [P, P]
+        lib.bbpe_word_cache_info.restype = I
+        lib.bbpe_word_cache_info.argtypes = [P, C.POINTER(U64), C.POINTER(U64)]
         lib.bbpe_error_detail.restype = I
         lib.bbpe_error_detail.argtypes = [P, C.POINTER(U32), C.POINTER(U64)]
         lib.bbpe_table_info.restype = I
@@ -228,13 +234,15 @@ class Tokenizer:
             return self._dws
 
     def encode_device(self, text, seg_off, allow, total_bytes: int, tiktoken_safe: bool = True,
-                      ids=None, id_off=None, stream=None, count_only: bool = False):
+                      ids=None, id_off=None, stream=None, count_only: bool = False,
+                      keep_word_cache: bool = False):
         """Encode segments already resident on the device.
 
         text: uint8 tensor (16-byte aligned); seg_off: int64 tensor [n_seg+1]
         (read as uint64); allow: uint8 tensor [n_seg].  Returns (ids[:n],
         id_off, n) with ids an int32 tensor; with count_only, (None, id_off,
-        n) and no ids are written."""
+        n) and no ids are written.  keep_word_cache: look units up in, and
+        add them to, the handle's word cache kept across calls."""
         import torch
         self.upload(text.device)
         n_seg = int(seg_off.numel()) - 1
@@ -243,7 +251,8 @@ class Tokenizer:
             ids = torch.empty(max(1, total_bytes), dtype=torch.int32, device=text.device)
         if id_off is None:
             id_off = torch.empty(n_seg + 1, dtype=torch.int64, device=text.device)
-        flags = (TIKTOKEN_SAFE if tiktoken_safe else 0) | (COUNT_ONLY if count_only else 0)
+        flags = ((TIKTOKEN_SAFE if tiktoken_safe else 0) | (COUNT_ONLY if count_only else 0) |
+                 (KEEP_WORD_CACHE if keep_word_cache else 0))
         ids_ptr = None if count_only else C.c_void_p(ids.data_ptr())
         ids_cap = 0 if count_only else ids.numel()
         n = C.c_uint64(0)
@@ -329,6 +338,21 @@ class Tokenizer:
         _, id_off, _ = self.encode_device(text, seg_off, allow, total, tiktoken_safe,
                                           stream=stream, count_only=True)
         return id_off[1:] - id_off[:-1]
+
+    def word_cache_clear(self, stream=None):
+        """Empty the word cache kept across calls."""
+        st = _load().bbpe_word_cache_clear(self._h, _stream_handle(stream))
+        if st:
+            raise BBPEError(st, "word_cache_clear")
+
+    def word_cache_info(self):
+        """(capacity in entries, 0 before the first keep_word_cache call;
+        units the last keep_word_cache call took from the cache)."""
+        ent, hits = C.c_uint64(0), C.c_uint64(0)
+        st = _load().bbpe_word_cache_info(self._h, C.byref(ent), C.byref(hits))
+        if st:
+            raise BBPEError(st, "word_cache_info")
+        return ent.value, hits.value
 
     def decode_workspace_bytes(self, n_ids: int) -> int:
         out = C.c_uint64()

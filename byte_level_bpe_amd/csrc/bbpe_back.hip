@@ -395,6 +395,84 @@ __device__ __forceinline__ uint32_t owner_slot(uint64_t h, uint32_t mask) {
 constexpr uint32_t FOLLOW_MAX = uint32_t(UID_FOLLOW - INT32_MIN);
 
 // ---------------------------------------------------------------------------
+// Word cache kept across calls (BBPE_KEEP_WORD_CACHE): the ids of units of
+// 2-32 bytes that went through the merge loop, by their bytes, for the
+// calls that follow (a serving process meets the same words in request
+// after request; the per-call cache above only spans one call).  Entries of
+// 32 dwords: the unit's bytes zero padded (0-7), meta (8: WC_FULL | length
+// << 8 | id count; 0 = empty, WC_BUSY = being written), ids (9-31).  An
+// entry sits at most WC_PROBES slots past the slot of its bytes' hash;
+// entries are never removed (bbpe_word_cache_clear empties the cache), so
+// a probe ends at the first empty slot.  k_probe reads the cache; k_merge
+// adds the units it merges (claiming an empty slot with a compare-and-swap,
+// then writing it, then marking it full), which later calls see.
+// Best-effort: a unit whose slots are busy or taken is not added.
+// ---------------------------------------------------------------------------
+constexpr uint32_t WC_WORDS = 32, WC_MAX_IDS = 23, WC_PROBES = 4;
+constexpr uint32_t WC_FULL = 1u << 31, WC_BUSY = 1u << 30;
+__device__ __forceinline__ uint32_t wc_slot(uint64_t h, uint32_t mask) { return uint32_t(h >> 20) & mask; }
+
+template <int SK>
+__device__ __forceinline__ bool wc_key_eq(const uint32_t *e, const UnitBytes<SK> &u) {
+  const uint4 k0 = reinterpret_cast<const uint4 *>(e)[0], k1 = reinterpret_cast<const uint4 *>(e)[1];
+  const uint32_t k[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+  bool eq = true;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) eq = eq && k[q] == (q < UnitBytes<SK>::NB ? u.d[q] : 0u);
+  return eq;
+}
+
+// The cached ids of unit i (bytes u, m of them, hash h, text offset s), if
+// any: written to tmp_ids and piece_cnt as the merge would.
+template <int SK>
+__device__ __forceinline__ bool wc_find(const EncodeArgs &a, const UnitBytes<SK> &u, uint32_t m,
+                                        uint64_t h, uint32_t s, uint32_t i, uint32_t p0 = 0) {
+  const uint32_t home = wc_slot(h, a.wc_mask);
+  for (uint32_t p = p0; p < WC_PROBES; ++p) {
+    const uint32_t *e = a.wcache + uint64_t((home + p) & a.wc_mask) * WC_WORDS;
+    const uint32_t meta = e[8];
+    if (!(meta & WC_FULL)) return false;
+    if (((meta >> 8) & 63u) != m || !wc_key_eq(e, u)) continue;
+    const uint32_t cnt = meta & 63u;
+    for (uint32_t j = 0; j < cnt; ++j) a.ws.tmp_ids[s + j] = int32_t(e[9 + j]);
+    a.ws.piece_cnt[i] = cnt;
+    return true;
+  }
+  return false;
+}
+
+// Add a merged unit (its cnt ids at tmp_ids + s) to the cache.
+template <int SK>
+__device__ __forceinline__ void wc_put(const EncodeArgs &a, const UnitBytes<SK> &u, uint32_t m,
+                                       uint32_t s, uint32_t cnt) {
+  if (cnt > WC_MAX_IDS) return;
+  uint64_t h, k8, k8b;
+  unit_hash(u, 0, m, h, k8, k8b);
+  const uint32_t home = wc_slot(h, a.wc_mask);
+  for (uint32_t p = 0; p < WC_PROBES; ++p) {
+    uint32_t *e = a.wcache + uint64_t((home + p) & a.wc_mask) * WC_WORDS;
+    // a plain read first: a repeated word finds itself without an atomic
+    const uint32_t cur = e[8];
+    if (cur & WC_BUSY) return;
+    if (cur & WC_FULL) {
+      if (((cur >> 8) & 63u) == m && wc_key_eq(e, u)) return;
+      continue;
+    }
+    const uint32_t old = atomicCAS(e + 8, 0u, WC_BUSY);
+    if (old == 0) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) e[q] = q < UnitBytes<SK>::NB ? u.d[q] : 0u;
+      for (uint32_t j = 0; j < cnt; ++j) e[9 + j] = uint32_t(a.ws.tmp_ids[s + j]);
+      __threadfence();
+      atomicExch(e + 8, WC_FULL | (m << 8) | cnt);
+      return;
+    }
+    if (old & WC_BUSY) return;                                  // another unit is writing here
+    if (((old >> 8) & 63u) == m && wc_key_eq(e, u)) return;    // already cached
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Probe pass: one thread per unit.
 // ---------------------------------------------------------------------------
 constexpr uint32_t WNS = 8;                // positions per lane in the group tiers
@@ -429,7 +507,7 @@ __device__ __forceinline__ int32_t probe_from(const DevTables &T, uint32_t idx, 
 // with one atomic per class.
 // (Texts under PROBE_SMALL bytes take one unit per thread instead: with few
 // units, the four serial resolutions of a thread are the kernel's length.)
-template <uint32_t PROBE_U>
+template <uint32_t PROBE_U, bool WC>
 __device__ __forceinline__ void probe_body(const EncodeArgs &a) {
   constexpr uint32_t PROBE_CHUNK = PROBE_BLOCK * PROBE_U;
   if (a.ws.status->pad2) return;
@@ -444,6 +522,7 @@ __device__ __forceinline__ void probe_body(const EncodeArgs &a) {
   for (uint32_t k = blockIdx.x * PROBE_BLOCK + threadIdx.x; k <= P / ASM_UNITS; k += gridDim.x * PROBE_BLOCK)
     a.ws.scan_state[k] = 0ull;
   __syncthreads();
+  uint32_t wc_hits = 0;
   for (uint32_t b = blockIdx.x * PROBE_CHUNK; b < P; b += gridDim.x * PROBE_CHUNK) {
     uint32_t idx[PROBE_U], s0[PROBE_U], m[PROBE_U];
 #pragma unroll
@@ -502,6 +581,51 @@ __device__ __forceinline__ void probe_body(const EncodeArgs &a) {
       if (a.word_cache && cls[u] >= 0 && cls[u] <= int(ML_16))  // this unit under its hash
         a.ws.owner[owner_slot(h[u], a.owner_mask)] = idx[u];
     }
+    if (WC) {
+      // the kept word cache: the first 64 bytes of every unit's home entry
+      // (its bytes, meta and first 7 ids) loaded together, then resolved;
+      // a home entry holding other bytes sends the unit on to the next slots
+      uint4 eq[PROBE_U][4];
+      bool want[PROBE_U];
+#pragma unroll
+      for (uint32_t u = 0; u < PROBE_U; ++u) {
+        want[u] = cls[u] >= 0 && cls[u] <= int(ML_32);
+        const uint4 *e = reinterpret_cast<const uint4 *>(
+            a.wcache + uint64_t(wc_slot(h[u], a.wc_mask)) * WC_WORDS);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) eq[u][q] = want[u] ? e[q] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (uint32_t u = 0; u < PROBE_U; ++u) {
+        if (!want[u]) continue;
+        const uint32_t meta = eq[u][2].x, mm = m[u], s = s0[u];
+        if (!(meta & WC_FULL)) continue;  // empty home slot: not cached
+        const uint32_t k[8] = {eq[u][0].x, eq[u][0].y, eq[u][0].z, eq[u][0].w,
+                               eq[u][1].x, eq[u][1].y, eq[u][1].z, eq[u][1].w};
+        bool same = ((meta >> 8) & 63u) == mm;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) same = same && k[q] == ub[u].d[q];
+        bool hit = false;
+        if (same) {
+          const uint32_t cnt = meta & 63u;
+          const uint32_t first[7] = {eq[u][2].y, eq[u][2].z, eq[u][2].w, eq[u][3].x,
+                                     eq[u][3].y, eq[u][3].z, eq[u][3].w};
+          const uint32_t *e = a.wcache + uint64_t(wc_slot(h[u], a.wc_mask)) * WC_WORDS;
+#pragma unroll
+          for (uint32_t j = 0; j < 7; ++j)
+            if (j < cnt) a.ws.tmp_ids[s + j] = int32_t(first[j]);
+          for (uint32_t j = 7; j < cnt; ++j) a.ws.tmp_ids[s + j] = int32_t(e[9 + j]);
+          a.ws.piece_cnt[idx[u]] = cnt;
+          hit = true;
+        } else {
+          hit = wc_find(a, ub[u], mm, h[u], s, idx[u], 1);
+        }
+        if (hit) {
+          cls[u] = -1;  // settled from the kept word cache
+          ++wc_hits;
+        }
+      }
+    }
     if (threadIdx.x < ML_COUNT) {
       s_cnt[threadIdx.x] = 0;
       s_cur[threadIdx.x] = 0;
@@ -530,9 +654,16 @@ __device__ __forceinline__ void probe_body(const EncodeArgs &a) {
     }
     __syncthreads();
   }
+  if (WC) {
+    wc_hits = wave_sum(wc_hits);
+    if ((threadIdx.x & 63) == 0 && wc_hits) atomicAdd(&st->wc_hits, (unsigned long long)wc_hits);
+  }
 }
-__global__ void __launch_bounds__(PROBE_BLOCK) k_probe(EncodeArgs a) { probe_body<4>(a); }
-__global__ void __launch_bounds__(PROBE_BLOCK) k_probe1(EncodeArgs a) { probe_body<1>(a); }
+__global__ void __launch_bounds__(PROBE_BLOCK) k_probe(EncodeArgs a) { probe_body<4, false>(a); }
+__global__ void __launch_bounds__(PROBE_BLOCK) k_probe1(EncodeArgs a) { probe_body<1, false>(a); }
+// the same with the kept word cache
+__global__ void __launch_bounds__(PROBE_BLOCK) k_probe_wc(EncodeArgs a) { probe_body<4, true>(a); }
+__global__ void __launch_bounds__(PROBE_BLOCK) k_probe1_wc(EncodeArgs a) { probe_body<1, true>(a); }
 
 // ---------------------------------------------------------------------------
 // Group tier: units of 33..WAVE_MAX bytes, a group of G lanes per unit (64/G
@@ -784,14 +915,16 @@ __device__ __forceinline__ uint32_t chain_then(uint32_t f, uint32_t g) {
   return (f & 2) | ((f ^ g) & 1);
 }
 
-template <int SK>
+template <int SK, bool WC>
 __device__ __forceinline__ void merge_short_unit(const EncodeArgs &a, const int32_t *atom, uint32_t i,
                                                  const PartCol &lp) {
   const uint32_t s = a.ws.piece_start[i];
   const uint32_t m = a.ws.piece_start[i + 1] - s;
   UnitBytes<SK> u;
   load_unit(a.text, a.n, s, m, u);
-  a.ws.piece_cnt[i] = merge_short<SK>(a.T, atom, u, m, lp, a.ws.tmp_ids + s);
+  const uint32_t cnt = merge_short<SK>(a.T, atom, u, m, lp, a.ws.tmp_ids + s);
+  a.ws.piece_cnt[i] = cnt;
+  if (WC) wc_put(a, u, m, s, cnt);
 }
 
 // Short-tier work item with the word cache: list entries first .. first +
@@ -800,7 +933,7 @@ __device__ __forceinline__ void merge_short_unit(const EncodeArgs &a, const int3
 // offsets and bytes, their slots, the slot units' offsets and bytes); a unit
 // that follows another records it (uid) and is done; the leaders are packed
 // into a queue in LDS and merged 64 at a time, one lane each.
-template <int SK, uint32_t K, bool ELECT>
+template <int SK, uint32_t K, bool ELECT, bool WC>
 __device__ __forceinline__ void merge_short_item(const EncodeArgs &a, uint32_t P, const int32_t *atom,
                                                  const PartCol &lp, uint32_t *queue,
                                                  const uint32_t *list, uint32_t count,
@@ -809,7 +942,7 @@ __device__ __forceinline__ void merge_short_item(const EncodeArgs &a, uint32_t P
 #pragma unroll
     for (uint32_t k = 0; k < K; ++k) {
       const uint32_t x = first + 64 * k + uint32_t(lane);
-      if (x < count) merge_short_unit<SK>(a, atom, list[x], lp);
+      if (x < count) merge_short_unit<SK, WC>(a, atom, list[x], lp);
     }
     return;
   }
@@ -859,7 +992,7 @@ __device__ __forceinline__ void merge_short_item(const EncodeArgs &a, uint32_t P
   __syncthreads();  // (one wave: orders the queue's writes before its reads)
   for (uint32_t q = 0; q < nq; q += 64) {
     const uint32_t x = q + uint32_t(lane);
-    if (x < nq) merge_short_unit<SK>(a, atom, queue[x], lp);
+    if (x < nq) merge_short_unit<SK, WC>(a, atom, queue[x], lp);
   }
   __syncthreads();  // the queue is rewritten by the next item
 }
@@ -872,7 +1005,8 @@ __device__ __forceinline__ void merge_short_item(const EncodeArgs &a, uint32_t P
 // lane-0 ticket and broadcast, which lets the compiler split the loop per
 // lane.
 constexpr uint32_t SHORT_K = 4;  // chunks of 64 entries per item
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge(EncodeArgs a) {
+template <bool WC>
+__device__ __forceinline__ void merge_body(const EncodeArgs &a) {
   if (a.ws.status->pad2) return;
   const Status *st = a.ws.status;
   const int lane = int(threadIdx.x);
@@ -894,20 +1028,27 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
     const uint32_t first = (item - (in16 ? 0u : in8 ? e16 : e8)) * C;
     if (a.word_cache) {
       if (in16)
-        merge_short_item<16, SHORT_K, true>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_16], n16, first, lane);
+        merge_short_item<16, SHORT_K, true, WC>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_16], n16, first, lane);
       else if (in8)
-        merge_short_item<8, SHORT_K, true>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_8], n8, first, lane);
+        merge_short_item<8, SHORT_K, true, WC>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_8], n8, first, lane);
       else
-        merge_short_item<4, SHORT_K, true>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_4], n4, first, lane);
+        merge_short_item<4, SHORT_K, true, WC>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_4], n4, first, lane);
     } else {
       if (in16)
-        merge_short_item<16, 1, false>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_16], n16, first, lane);
+        merge_short_item<16, 1, false, WC>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_16], n16, first, lane);
       else if (in8)
-        merge_short_item<8, 1, false>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_8], n8, first, lane);
+        merge_short_item<8, 1, false, WC>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_8], n8, first, lane);
       else
-        merge_short_item<4, 1, false>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_4], n4, first, lane);
+        merge_short_item<4, 1, false, WC>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_4], n4, first, lane);
     }
   }
+}
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge(EncodeArgs a) {
+  merge_body<false>(a);
+}
+// the same with the kept word cache
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge_wc(EncodeArgs a) {
+  merge_body<true>(a);
 }
 
 // Merge of the units of 17..WAVE_MAX bytes (second stream, beside k_merge:
@@ -919,7 +1060,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
 // all of them every round); many, 16 or 32 lanes per unit, for throughput.
 // Then the units of 17-32 bytes, one lane each, 64 per item (nearly every
 // such unit is a byte string of its own, so they skip the word cache).
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge_wide(EncodeArgs a) {
+template <bool WC>
+__device__ __forceinline__ void merge_wide_body(const EncodeArgs &a) {
   if (a.ws.status->pad2) return;
   const Status *st = a.ws.status;
   const int lane = int(threadIdx.x);
@@ -947,9 +1089,16 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
       else merge_group<64, 2>(a, a.ws.lst[ML_G128], n16g, item - e32g, lane);
     } else {
       const uint32_t x = (item - e16g) * 64 + uint32_t(lane);
-      if (x < n32) merge_short_unit<32>(a, s_atom, a.ws.lst[ML_32][x], lp);
+      if (x < n32) merge_short_unit<32, WC>(a, s_atom, a.ws.lst[ML_32][x], lp);
     }
   }
+}
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge_wide(EncodeArgs a) {
+  merge_wide_body<false>(a);
+}
+// the same with the kept word cache
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge_wide_wc(EncodeArgs a) {
+  merge_wide_body<true>(a);
 }
 
 // Block-wide helpers of the long tier (LONG_BLOCK threads, LDS scratch sh).
@@ -1269,6 +1418,7 @@ __device__ __forceinline__ void publish_status(const EncodeArgs &a, Status *host
   host->pad2 = d.pad2;
   for (uint32_t k = 0; k < ML_COUNT; ++k) host->n_list[k] = d.n_list[k];
   host->scan_ticket = d.scan_ticket;
+  host->wc_hits = d.wc_hits;
   __threadfence_system();
 }
 

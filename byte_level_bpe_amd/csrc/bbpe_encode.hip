@@ -188,7 +188,8 @@ int prepare(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t
             EncodeArgs &a, WsLayout &L) {
   if (!t || !d_seg_off || (n_seg && !d_allow)) return BBPE_E_INVALID_ARG;
   if (n && (!d_text || (reinterpret_cast<uintptr_t>(d_text) & 15))) return BBPE_E_INVALID_ARG;
-  if (n >= (uint64_t(1) << 32) - 64 || (flags & ~uint32_t(BBPE_TIKTOKEN_SAFE | BBPE_COUNT_ONLY)))
+  if (n >= (uint64_t(1) << 32) - 64 ||
+      (flags & ~uint32_t(BBPE_TIKTOKEN_SAFE | BBPE_COUNT_ONLY | BBPE_KEEP_WORD_CACHE)))
     return BBPE_E_INVALID_ARG;
   if (n_seg == 0 && n != 0) return BBPE_E_INVALID_ARG;
   if (!t->d_image || !t->host_status) return BBPE_E_STATE;
@@ -317,16 +318,20 @@ int enqueue_encode(bbpe_tokenizer *t, Go &go, const EncodeArgs &a, const WsLayou
   } else {
     if (n < PROBE_SMALL) {
       const uint32_t probe_grid = uint32_t((n + 2047) / 2048);
-      go("k_probe", k_probe1, dim3(probe_grid), dim3(PROBE_BLOCK), a);
+      go("k_probe", a.wcache ? k_probe1_wc : k_probe1, dim3(probe_grid), dim3(PROBE_BLOCK), a);
     } else {
       const uint32_t probe_grid = uint32_t(std::min<uint64_t>((n + 8191) / 8192, 8192));
-      go("k_probe", k_probe, dim3(probe_grid), dim3(PROBE_BLOCK), a);
+      go("k_probe", a.wcache ? k_probe_wc : k_probe, dim3(probe_grid), dim3(PROBE_BLOCK), a);
     }
     // (grid-stride kernels: their units are few, and idle waves of the
     // second stream take dispatch slots from the short tier.)
     const uint32_t wide_grid = uint32_t(std::min<uint64_t>(n / 17 + 1, 4096));
     const uint32_t long_grid = uint32_t(std::min<uint64_t>(n / 513 + 1, 64));
     const uint32_t merge_grid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
+    // (the kept word cache has kernels of its own, so that the others carry
+    // none of its code)
+    auto *const merge_k = a.wcache ? k_merge_wc : k_merge;
+    auto *const wide_k = a.wcache ? k_merge_wide_wc : k_merge_wide;
     if (fork) {
       // the units of 17-512 bytes (few, long dependent chains) run on the
       // second stream beside the rest of the short tier; the long tier
@@ -336,16 +341,16 @@ int enqueue_encode(bbpe_tokenizer *t, Go &go, const EncodeArgs &a, const WsLayou
       int rc = go.record(0);
       go.use_aux();
       if (!rc) rc = go.wait(0);
-      go("k_merge_wide", k_merge_wide, dim3(wide_grid), dim3(64), a);
+      go("k_merge_wide", wide_k, dim3(wide_grid), dim3(64), a);
       if (!rc) rc = go.record(1);
       go.use_main();
-      go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
+      go("k_merge", merge_k, dim3(merge_grid), dim3(64), a);
       go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
       if (!rc) rc = go.wait(1);
       if (rc) return rc;
     } else {
-      go("k_merge_wide", k_merge_wide, dim3(wide_grid), dim3(64), a);
-      go("k_merge", k_merge, dim3(merge_grid), dim3(64), a);
+      go("k_merge_wide", wide_k, dim3(wide_grid), dim3(64), a);
+      go("k_merge", merge_k, dim3(merge_grid), dim3(64), a);
       go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
     }
     // one workgroup per scan tile (the unit count is at most n), the last
@@ -367,7 +372,7 @@ int enqueue_encode(bbpe_tokenizer *t, Go &go, const EncodeArgs &a, const WsLayou
 // What an encode's kernel sequence depends on besides the handle's tables:
 // a built graph is replayed only for a call with the same values.
 struct GraphKey {
-  const void *image, *text, *seg_off, *allow, *ws, *ids, *id_off, *host;
+  const void *image, *text, *seg_off, *allow, *ws, *ids, *id_off, *host, *wcache;
   uint64_t n, ids_cap;
   uint32_t n_seg, flags;
 };
@@ -387,6 +392,7 @@ int run_graph(bbpe_tokenizer *t, const EncodeArgs &a, const WsLayout &L, hipStre
   k.ids = a.ids;
   k.id_off = a.id_off;
   k.host = t->host_status_dev;
+  k.wcache = a.wcache;
   k.n = a.n;
   k.ids_cap = a.ids_cap;
   k.n_seg = a.n_seg;
@@ -439,6 +445,22 @@ int encode_impl(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint
   a.ids_cap = ids_cap;
   a.id_off = d_id_off;
   a.merge_units = 1;
+  const bool keep = (flags & BBPE_KEEP_WORD_CACHE) != 0;
+  if (keep) {
+    if (!fork) return BBPE_E_INVALID_ARG;  // the no-alloc entry point keeps no cache
+    if (!t->wcache) {
+      void *p = nullptr;
+      const uint64_t bytes = uint64_t(BBPE_WORD_CACHE_ENTRIES) * WC_ENTRY_BYTES;
+      HIP_OK(hipMalloc(&p, bytes));
+      if (hipMemset(p, 0, bytes) != hipSuccess) {
+        (void)hipFree(p);
+        return BBPE_E_HIP;
+      }
+      t->wcache = p;
+    }
+    a.wcache = static_cast<uint32_t *>(t->wcache);
+    a.wc_mask = BBPE_WORD_CACHE_ENTRIES - 1;
+  }
   if (fork) {
     rc = ensure_aux(t);
     if (rc) return rc;
@@ -462,6 +484,7 @@ int encode_impl(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint
   rc = finish(t, go, h);
   if (rc) return rc;
   *n_ids = h.n_ids;
+  if (keep) t->wc_last_hits = h.wc_hits;
   if (h.n_ids > ids_cap && !count_only) return BBPE_E_CAPACITY;
   return BBPE_OK;
 }
@@ -625,6 +648,7 @@ void bbpe_free(bbpe_tokenizer *t) {
     if (e) (void)hipEventDestroy(static_cast<hipEvent_t>(e));
   if (t->graph_exec) (void)hipGraphExecDestroy(static_cast<hipGraphExec_t>(t->graph_exec));
   if (t->host_status) (void)hipHostFree(t->host_status);
+  if (t->wcache) (void)hipFree(t->wcache);
   if (t->aux_stream) {
     (void)hipStreamSynchronize(static_cast<hipStream_t>(t->aux_stream));
     (void)hipEventDestroy(static_cast<hipEvent_t>(t->ev_fork));
@@ -632,6 +656,25 @@ void bbpe_free(bbpe_tokenizer *t) {
     (void)hipStreamDestroy(static_cast<hipStream_t>(t->aux_stream));
   }
   delete t;
+}
+
+int bbpe_word_cache_clear(bbpe_tokenizer *t, void *stream) {
+  if (!t) return BBPE_E_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(t->mu);
+  t->wc_last_hits = 0;
+  if (!t->wcache) return BBPE_OK;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  HIP_OK(hipMemsetAsync(t->wcache, 0, uint64_t(BBPE_WORD_CACHE_ENTRIES) * WC_ENTRY_BYTES, st));
+  HIP_OK(hipStreamSynchronize(st));
+  return BBPE_OK;
+}
+
+int bbpe_word_cache_info(bbpe_tokenizer *t, uint64_t *entries, uint64_t *last_hits) {
+  if (!t) return BBPE_E_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(t->mu);
+  if (entries) *entries = t->wcache ? BBPE_WORD_CACHE_ENTRIES : 0;
+  if (last_hits) *last_hits = t->wc_last_hits;
+  return BBPE_OK;
 }
 
 int bbpe_timing_reset(bbpe_tokenizer *t) {

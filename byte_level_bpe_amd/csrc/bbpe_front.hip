@@ -107,6 +107,7 @@ __device__ __forceinline__ void init_status(const EncodeArgs &a, unsigned long l
   s->scan_ticket = 0;
   s->scan_fail = 0;
   s->sp_fix = 0;
+  s->wc_hits = 0;
   s->err_seg = 0;
   s->n_chars = n_chars;
   // offsets start at 0, end at the text length and never decrease; every

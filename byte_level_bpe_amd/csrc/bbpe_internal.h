@@ -139,6 +139,8 @@ struct Status {
   unsigned int scan_ticket;       // next tile of the id-count scan (k_assemble)
   unsigned int scan_fail;         // nonzero: a scan tile's wait for its predecessors gave up
   unsigned int sp_fix;            // nonzero: k_specials left tiles to k_specials_fix
+  unsigned int pad3;
+  unsigned long long wc_hits;     // units settled from the kept word cache (k_probe)
 };
 
 // Merge-unit lists by length class: the short tier (one lane per unit,

@@ -84,6 +84,8 @@ constexpr uint64_t WORD_CACHE_MIN = 16u << 20;
 constexpr int32_t UID_MERGED = -1;
 constexpr int32_t UID_FOLLOW = -2;  // UID_FOLLOW - j: follows unit j
 
+constexpr uint64_t WC_ENTRY_BYTES = 128;  // one kept-word-cache entry (32 dwords)
+
 struct EncodeArgs {
   DevTables T;
   const uint8_t *text;
@@ -98,6 +100,9 @@ struct EncodeArgs {
   uint32_t owner_mask;   // word-cache slots - 1 (a power of two minus one)
   uint32_t word_cache;   // 1: units of 2-16 bytes merge once per byte string (texts of at
                          //    least WORD_CACHE_MIN bytes)
+  uint32_t *wcache;      // word cache kept across calls (BBPE_KEEP_WORD_CACHE), or null
+                         // (WC_ENTRY_BYTES per entry)
+  uint32_t wc_mask;      // its entries - 1 (a power of two minus one)
   int32_t *ids;
   uint64_t ids_cap;
   int64_t *id_off;
@@ -122,6 +127,10 @@ __global__ void k_probe1(EncodeArgs a);
 __global__ void k_merge(EncodeArgs a);
 __global__ void k_merge_long(EncodeArgs a);
 __global__ void k_merge_wide(EncodeArgs a);
+__global__ void k_probe_wc(EncodeArgs a);
+__global__ void k_probe1_wc(EncodeArgs a);
+__global__ void k_merge_wc(EncodeArgs a);
+__global__ void k_merge_wide_wc(EncodeArgs a);
 __global__ void k_scan_sums(EncodeArgs a);
 __global__ void k_scan_bases(EncodeArgs a);
 __global__ void k_assemble(EncodeArgs a, Status *host_status, int single_pass);

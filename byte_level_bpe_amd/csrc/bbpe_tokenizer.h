@@ -52,6 +52,10 @@ struct bbpe_tokenizer {
   void *graph_exec = nullptr;
   std::vector<uint8_t> graph_key;
   bool graph_broken = false;  // building one failed: launch kernels directly
+  // The word cache kept across calls (BBPE_KEEP_WORD_CACHE): allocated on the
+  // device current at the first call that asks for it, freed by bbpe_free.
+  void *wcache = nullptr;
+  uint64_t wc_last_hits = 0;  // units the last such call settled from it
   // Every entry point that enqueues work or touches the mutable state above
   // (second stream, fork/join events, timing records) holds this lock for
   // the whole call, so that host threads sharing a handle never interleave

@@ -77,9 +77,11 @@ enum { BBPE_GRAMMAR_CL100K = 0, BBPE_GRAMMAR_O200K_STYLE = 1, BBPE_GRAMMAR_R50K_
 
 /* encode flags */
 enum {
-  BBPE_TIKTOKEN_SAFE = 1u << 0, /* 400k-character windows, 25k-character run cuts */
-  BBPE_COUNT_ONLY = 1u << 1     /* token counts only: d_id_off and *n_ids are written,
-                                   d_ids is not (it may be null, ids_capacity 0) */
+  BBPE_TIKTOKEN_SAFE = 1u << 0,  /* 400k-character windows, 25k-character run cuts */
+  BBPE_COUNT_ONLY = 1u << 1,     /* token counts only: d_id_off and *n_ids are written,
+                                    d_ids is not (it may be null, ids_capacity 0) */
+  BBPE_KEEP_WORD_CACHE = 1u << 2 /* look units up in, and add them to, the handle's
+                                    word cache (see bbpe_word_cache_info) */
 };
 
 /* Limits of this implementation. */
@@ -289,6 +291,25 @@ int bbpe_stream_decode_device(bbpe_stream_decoder *dec, const int32_t *d_ids, ui
 int bbpe_token_offsets_device(bbpe_tokenizer *tok, const int32_t *d_ids, uint64_t n_ids,
                               uint64_t *d_tok_off, void *d_workspace, uint64_t workspace_bytes,
                               uint64_t *total_bytes, void *hip_stream);
+
+/* The word cache kept across calls (tokenizers v1 page, "Key Technical
+ * Improvements": a cache of the ids of words already merged).  Units of 2-32
+ * bytes that need the merge loop are looked up by their bytes in a device
+ * hash table held by the handle; the ones found take their ids from it, and
+ * the ones merged are added to it, for the calls that follow.  Only calls of
+ * bbpe_encode_segments with BBPE_KEEP_WORD_CACHE use it (the first such call
+ * allocates it, BBPE_WORD_CACHE_ENTRIES entries of 128 bytes, on the current
+ * device; bbpe_encode_segments_noalloc rejects the flag with
+ * BBPE_E_INVALID_ARG).  The cache holds the merge results of this handle's
+ * table only, so its answers are exact; it is best-effort in what it holds
+ * (a unit whose slots are taken is not added; nothing is evicted).
+ * bbpe_word_cache_clear empties it (on hip_stream, synchronised);
+ * bbpe_word_cache_info gives its capacity in entries (0 before it is
+ * allocated) and how many units the last BBPE_KEEP_WORD_CACHE call took
+ * from it. */
+#define BBPE_WORD_CACHE_ENTRIES (1u << 18)
+int bbpe_word_cache_clear(bbpe_tokenizer *tok, void *hip_stream);
+int bbpe_word_cache_info(bbpe_tokenizer *tok, uint64_t *entries, uint64_t *last_hits);
 
 /* Details of the last BBPE_E_UTF8 that bbpe_encode_segments or
  * bbpe_pretokenize_segments returned to the calling thread on this handle:
