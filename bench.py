@@ -479,6 +479,13 @@ def main():
                      "traffic": measured_traffic(args.workload, dom), "avg_ms": round(dom_ms, 5),
                      "alg_bytes_per_launch": dom_bytes},
         "kernels_avg_ms": {k: round(v, 5) for k, v in sorted(per_kernel.items(), key=lambda kv: -kv[1])},
+        # every kernel's algorithmic rate against the same peak (the dominant
+        # kernel by time above can be a latency-bound one carrying few bytes)
+        "roofline_by_kernel": {k: {"alg_bytes": algorithmic_bytes(k, alg),
+                                   "avg_ms": round(v, 5),
+                                   "frac": round(algorithmic_bytes(k, alg) / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+                                   "traffic": measured_traffic(args.workload, k)}
+                               for k, v in sorted(per_kernel.items(), key=lambda kv: -kv[1])},
         "ids_sha256": gpu_sha,
         "ids_match_oracle": gpu_sha == alg.get("ids_sha256"),
     }
