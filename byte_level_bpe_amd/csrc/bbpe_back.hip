@@ -1472,22 +1472,21 @@ __global__ void __launch_bounds__(1024) k_scan_bases(EncodeArgs a) {
 
 // single_pass: the tiles' bases by the look-back; else read from scan_state
 // (k_scan_sums and k_scan_bases ran before).
-__global__ void __launch_bounds__(ASM_BLOCK) k_assemble(EncodeArgs a, Status *host, int single_pass) {
+struct AsmLds {
+  uint32_t tile, excl, fail;
+  uint32_t off[ASM_UNITS + 1], start[ASM_UNITS];
+  int32_t uid[ASM_UNITS];
+  uint32_t wsum[ASM_BLOCK / 64];
+};
+
+// One tile of the assembly; false when the look-back gave up (the call then
+// reports a failure).
+__device__ __forceinline__ bool assemble_tile(const EncodeArgs &a, Status *host, int single_pass,
+                                              uint32_t t, uint32_t P, uint32_t nt, AsmLds &L) {
   Status *st = a.ws.status;
-  if (st->pad2) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) publish_status(a, host);
-    return;
-  }
-  const uint32_t P = uint32_t(st->n_pieces);
-  const uint32_t nt = P / ASM_UNITS + 1;  // tiles over unit indices 0..P (P: the end)
-  __shared__ uint32_t s_tile, s_excl, s_fail;
-  __shared__ uint32_t s_off[ASM_UNITS + 1], s_start[ASM_UNITS];
-  __shared__ int32_t s_uid[ASM_UNITS];
-  __shared__ uint32_t s_wsum[ASM_BLOCK / 64];
-  if (threadIdx.x == 0) s_tile = single_pass ? atomicAdd(&st->scan_ticket, 1u) : blockIdx.x;
-  __syncthreads();
-  const uint32_t t = s_tile;
-  if (t >= nt) return;
+  uint32_t &s_excl = L.excl, &s_fail = L.fail;
+  uint32_t *s_off = L.off, *s_start = L.start, *s_wsum = L.wsum;
+  int32_t *s_uid = L.uid;
   const uint32_t i0 = t * ASM_UNITS;
   const uint32_t nu = min(ASM_UNITS, P - i0);  // units of this tile (the last may have 0)
   // counts: thread x takes units i0 + 4 x .. i0 + 4 x + 3; a unit's uid, its
@@ -1576,7 +1575,7 @@ __global__ void __launch_bounds__(ASM_BLOCK) k_assemble(EncodeArgs a, Status *ho
       host->scan_fail = 1u;
       __threadfence_system();
     }
-    return;
+    return false;
   }
   const uint32_t excl = s_excl;
   // unit offsets and sources into LDS
@@ -1679,6 +1678,46 @@ __global__ void __launch_bounds__(ASM_BLOCK) k_assemble(EncodeArgs a, Status *ho
     }
     publish_status(a, host);
   }
+  return true;
+}
+
+// Ordered assembly, single pass: each workgroup takes tiles from the ticket
+// counter until none is left (a grid of a few workgroups per CU, not one per
+// possible tile: the unit count is only known on the device, and a grid
+// sized for the worst case spent most of its workgroups on exiting).
+__global__ void __launch_bounds__(ASM_BLOCK) k_assemble(EncodeArgs a, Status *host) {
+  Status *st = a.ws.status;
+  if (st->pad2) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) publish_status(a, host);
+    return;
+  }
+  const uint32_t P = uint32_t(st->n_pieces);
+  const uint32_t nt = P / ASM_UNITS + 1;  // tiles over unit indices 0..P (P: the end)
+  __shared__ AsmLds L;
+  for (;;) {
+    if (threadIdx.x == 0) L.tile = atomicAdd(&st->scan_ticket, 1u);
+    __syncthreads();
+    const uint32_t t = L.tile;
+    if (t >= nt) return;
+    if (!assemble_tile(a, host, 1, t, P, nt, L)) return;
+    __syncthreads();  // the tile's LDS is read before the next tile writes it
+  }
+}
+
+// The same after k_scan_sums and k_scan_bases (texts above ASM_SINGLE_MAX
+// bytes): one tile per workgroup, its base read from the scan.
+__global__ void __launch_bounds__(ASM_BLOCK) k_assemble_based(EncodeArgs a, Status *host) {
+  Status *st = a.ws.status;
+  if (st->pad2) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) publish_status(a, host);
+    return;
+  }
+  const uint32_t P = uint32_t(st->n_pieces);
+  const uint32_t nt = P / ASM_UNITS + 1;
+  __shared__ AsmLds L;
+  const uint32_t t = blockIdx.x;
+  if (t >= nt) return;
+  (void)assemble_tile(a, host, 0, t, P, nt, L);
 }
 
 

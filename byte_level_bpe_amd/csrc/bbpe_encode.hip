@@ -353,16 +353,22 @@ int enqueue_encode(bbpe_tokenizer *t, Go &go, const EncodeArgs &a, const WsLayou
       go("k_merge", merge_k, dim3(merge_grid), dim3(64), a);
       go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
     }
-    // one workgroup per scan tile (the unit count is at most n), the last
-    // one publishing the status block
+    // at most one scan tile per ASM_UNITS bytes (the unit count is at most
+    // n); the single pass takes its tiles from a ticket counter on a grid of
+    // at most ASM_GRID workgroups, the three-phase path one tile per
+    // workgroup; the last tile publishes the status block
     const uint32_t agrid = uint32_t((n + 1 + ASM_UNITS - 1) / ASM_UNITS);
     const int single = n <= ASM_SINGLE_MAX ? 1 : 0;
     if (!single) {
       go("k_scan_sums", k_scan_sums, dim3(agrid), dim3(1024), a);
       go("k_scan_bases", k_scan_bases, dim3(1), dim3(1024), a);
     }
-    go("k_assemble", k_assemble, dim3(agrid), dim3(1024), a, static_cast<Status *>(t->host_status_dev),
-       single);
+    if (single)
+      go("k_assemble", k_assemble, dim3(std::min(agrid, ASM_GRID)), dim3(1024), a,
+         static_cast<Status *>(t->host_status_dev));
+    else
+      go("k_assemble", k_assemble_based, dim3(agrid), dim3(1024), a,
+         static_cast<Status *>(t->host_status_dev));
     return BBPE_OK;
   }
   publish(t, go, a);

@@ -68,6 +68,7 @@ constexpr uint32_t ASM_UNITS = 4096;
 // texts up to this size scan the tiles' id counts in k_assemble itself
 // (look-back between tiles); larger ones scan the tile sums apart first
 constexpr uint64_t ASM_SINGLE_MAX = 6000000;
+constexpr uint32_t ASM_GRID = 256;  // workgroups of the single-pass assembly at most
 
 // threads per k_probe block (units per block and pass)
 constexpr uint32_t PROBE_BLOCK = 512;
@@ -133,6 +134,7 @@ __global__ void k_merge_wc(EncodeArgs a);
 __global__ void k_merge_wide_wc(EncodeArgs a);
 __global__ void k_scan_sums(EncodeArgs a);
 __global__ void k_scan_bases(EncodeArgs a);
-__global__ void k_assemble(EncodeArgs a, Status *host_status, int single_pass);
+__global__ void k_assemble(EncodeArgs a, Status *host);
+__global__ void k_assemble_based(EncodeArgs a, Status *host);
 
 }  // namespace bbpe
