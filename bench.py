@@ -10,6 +10,7 @@ resident in device memory.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -189,12 +190,15 @@ def bench_decode(args, w):
     for _ in range(args.warmup):
         nb = step()
     assert nb == total
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     tok.set_timing(True)
     tok.timing_reset()
     for _ in range(args.steps):
@@ -376,7 +380,11 @@ def main():
         n_ids = step()
     torch.cuda.synchronize()
     # timed region: K whole calls, one event pair per call on the launch stream
+    # (the interpreter's collector is held off meanwhile: each call waits for
+    # its status on the host, so a collection would stall the device too)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     evs[0].record(stream)
@@ -385,6 +393,7 @@ def main():
         evs[k + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     step_ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps))
     dev_ms = evs[0].elapsed_time(evs[-1])
     # per-kernel durations: the same K calls again with an event pair around
