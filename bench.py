@@ -313,6 +313,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="main")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--blocking", action="store_true",
+                    help="time the entry point that waits for each call (default: calls queued "
+                         "back to back and settled by one wait)")
     ap.add_argument("--no-warm-cache", action="store_true",
                     help="skip the kept-word-cache leg (main workload only)")
     ap.add_argument("--op", choices=["encode", "decode"], default="encode",
@@ -376,12 +379,22 @@ def main():
                   "what": "host wall time on a fresh handle: table build, table upload + workspace "
                           "allocation, the first encode (graph built, kernels loaded) and the second"}
 
+    def step_queued():
+        tok.encode_device_async(text, seg_off, allow, total, ids, id_off,
+                                tiktoken_safe=w.tiktoken_safe, stream=stream)
+
     for _ in range(args.warmup):
         n_ids = step()
+    if not args.blocking:
+        step_queued()
+        n_ids = tok.encode_wait(stream)
     torch.cuda.synchronize()
-    # timed region: K whole calls, one event pair per call on the launch stream
-    # (the interpreter's collector is held off meanwhile: each call waits for
-    # its status on the host, so a collection would stall the device too)
+    # timed region: K whole calls, one event pair per call on the launch
+    # stream.  By default the calls are queued back to back
+    # (bbpe_encode_segments_async, the way a serving loop issues batches) and
+    # settled by one wait inside the region, which also checks every call's
+    # status; --blocking times the entry point that waits for each call.
+    # (The interpreter's collector is held off meanwhile.)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     gc.collect()
     gc.disable()
@@ -389,10 +402,30 @@ def main():
     t0 = time.perf_counter()
     evs[0].record(stream)
     for k in range(args.steps):
-        n_ids = step()
+        if args.blocking:
+            n_ids = step()
+        else:
+            step_queued()
         evs[k + 1].record(stream)
     torch.cuda.synchronize()
+    if not args.blocking:
+        n_ids = tok.encode_wait(stream)
     wall = time.perf_counter() - t0
+    gc.enable()
+    # the other way of calling, the same K calls, outside the timed region
+    gc.collect()
+    gc.disable()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        if args.blocking:
+            step_queued()
+        else:
+            step()
+    torch.cuda.synchronize()
+    if args.blocking:
+        tok.encode_wait(stream)
+    other_wall = time.perf_counter() - t0
     gc.enable()
     step_ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps))
     dev_ms = evs[0].elapsed_time(evs[-1])
@@ -480,6 +513,12 @@ def main():
                           "floor_frac_of_8TBs": round(floor_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
                           "copy_GBs": round(copy_gbs, 1),
                           "alg_frac_of_copy": round(b_alg / (ms_per_step * 1e-3) / 1e9 / copy_gbs, 5)},
+        "calls": "blocking" if args.blocking else "queued",
+        ("queued_calls" if args.blocking else "blocking_calls"): {
+            "ms_per_step": round(other_wall * 1e3 / args.steps, 4),
+            "MBs": round(total * args.steps / other_wall / 1e6, 2),
+            "what": ("the same calls queued back to back, one wait at the end" if args.blocking else
+                     "the same calls through the entry point that waits for each call's result")},
         "pcie_inclusive": {"ms_per_step": round(e2e_ms, 4), "MBs": round(total / (e2e_ms * 1e-3) / 1e6, 2),
                            "steps": e2e_steps,
                            "what": "text host-to-device from pinned memory, encode, ids device-to-host"},

@@ -41,8 +41,8 @@ NOALLOC_SCRATCH_BYTES = 48 << 20  # BBPE_NOALLOC_SCRATCH_BYTES
 
 # every symbol include/bbpe.h declares
 EXPORTS = ["bbpe_load_ranks", "bbpe_load_ranks_tiktoken_file", "bbpe_upload_tables",
-           "bbpe_workspace_bytes", "bbpe_encode_segments", "bbpe_encode_segments_noalloc",
-           "bbpe_pretokenize_segments",
+           "bbpe_workspace_bytes", "bbpe_encode_segments", "bbpe_encode_segments_async",
+           "bbpe_encode_wait", "bbpe_encode_segments_noalloc", "bbpe_pretokenize_segments",
            "bbpe_decode", "bbpe_decode_workspace_bytes", "bbpe_decode_device",
            "bbpe_token_offsets_device", "bbpe_stream_decoder_create", "bbpe_stream_decoder_free",
            "bbpe_stream_decoder_reset", "bbpe_stream_decode_device", "bbpe_word_cache_clear",
@@ -79,6 +79,10 @@ def _load():
         lib.bbpe_encode_segments.restype = I
         lib.bbpe_encode_segments.argtypes = [P, P, U64, P, P, U32, U32, P, U64, P, U64, P,
                                              C.POINTER(U64), P]
+        lib.bbpe_encode_segments_async.restype = I
+        lib.bbpe_encode_segments_async.argtypes = [P, P, U64, P, P, U32, U32, P, U64, P, U64, P, P]
+        lib.bbpe_encode_wait.restype = I
+        lib.bbpe_encode_wait.argtypes = [P, P, C.POINTER(U64)]
         lib.bbpe_encode_segments_noalloc.restype = I
         lib.bbpe_encode_segments_noalloc.argtypes = [P, P, U64, P, P, U32, U32, P, U64, P,
                                                      C.POINTER(U64), P]
@@ -154,6 +158,9 @@ class Tokenizer:
         self._dev_table = None
         self._ws = None
         self._dws = None
+        # tensors of asynchronous encodes not yet waited for, kept alive
+        # until the wait
+        self._pending = {}
         # guards the cached table, workspace and decode workspace when
         # several threads share this object (the library itself runs calls
         # on one handle one after the other)
@@ -261,17 +268,56 @@ class Tokenizer:
             C.c_void_p(allow.data_ptr()), n_seg, flags,
             C.c_void_p(ws.data_ptr()), ws.numel(), ids_ptr, ids_cap,
             C.c_void_p(id_off.data_ptr()), C.byref(n), _stream_handle(stream))
-        if st == E_UTF8:
-            seg, off = C.c_uint32(), C.c_uint64()
-            _load().bbpe_error_detail(self._h, C.byref(seg), C.byref(off))
-            err = BBPEError(st, "encode_segments: segment %d byte %d" % (seg.value, off.value))
-            err.segment, err.byte_offset = seg.value, off.value
-            raise err
         if st:
-            raise BBPEError(st, "encode_segments")
+            self._raise(st, "encode_segments")
         if count_only:
             return None, id_off, n.value
         return ids[:n.value], id_off, n.value
+
+    def _raise(self, st: int, what: str):
+        if st == E_UTF8:
+            seg, off = C.c_uint32(), C.c_uint64()
+            _load().bbpe_error_detail(self._h, C.byref(seg), C.byref(off))
+            err = BBPEError(st, "%s: segment %d byte %d" % (what, seg.value, off.value))
+            err.segment, err.byte_offset = seg.value, off.value
+            raise err
+        raise BBPEError(st, what)
+
+    def encode_device_async(self, text, seg_off, allow, total_bytes: int, ids, id_off,
+                            tiktoken_safe: bool = True, stream=None, count_only: bool = False,
+                            keep_word_cache: bool = False):
+        """encode_device without the wait (bbpe_encode_segments_async): the
+        work is enqueued on the stream and the call returns.  ids (unless
+        count_only) and id_off are the caller's; the call's id count is
+        id_off[-1] on the device.  encode_wait settles every such call."""
+        self.upload(text.device)
+        n_seg = int(seg_off.numel()) - 1
+        ws = self.workspace(total_bytes, n_seg, text.device)
+        flags = ((TIKTOKEN_SAFE if tiktoken_safe else 0) | (COUNT_ONLY if count_only else 0) |
+                 (KEEP_WORD_CACHE if keep_word_cache else 0))
+        st = _load().bbpe_encode_segments_async(
+            self._h, C.c_void_p(text.data_ptr()), int(total_bytes), C.c_void_p(seg_off.data_ptr()),
+            C.c_void_p(allow.data_ptr()), n_seg, flags, C.c_void_p(ws.data_ptr()), ws.numel(),
+            None if count_only else C.c_void_p(ids.data_ptr()), 0 if count_only else ids.numel(),
+            C.c_void_p(id_off.data_ptr()), _stream_handle(stream))
+        if st:
+            raise BBPEError(st, "encode_segments_async")
+        with self._lock:
+            for x in (text, seg_off, allow, ws, ids, id_off):
+                if x is not None:
+                    self._pending[id(x)] = x
+
+    def encode_wait(self, stream=None) -> int:
+        """Waits for every encode_device_async call not yet waited for;
+        returns the last one's id count, or raises the first error any of
+        them met."""
+        n = C.c_uint64(0)
+        st = _load().bbpe_encode_wait(self._h, _stream_handle(stream), C.byref(n))
+        with self._lock:
+            self._pending.clear()
+        if st:
+            self._raise(st, "encode_wait")
+        return n.value
 
     def encode_device_noalloc(self, text, seg_off, allow, total_bytes: int,
                               tiktoken_safe: bool = True, ids=None, id_off=None, stream=None,

@@ -1409,17 +1409,7 @@ __device__ __forceinline__ unsigned long long scan_read(unsigned long long *p) {
 // scan_fail, which a failing tile sets there itself (the host clears it
 // before each call).
 __device__ __forceinline__ void publish_status(const EncodeArgs &a, Status *host) {
-  const Status &d = *a.ws.status;
-  host->err_pos = d.err_pos;
-  host->n_pieces = d.n_pieces;
-  host->n_ids = d.n_ids;
-  host->n_chars = d.n_chars;
-  host->err_seg = d.err_seg;
-  host->pad2 = d.pad2;
-  for (uint32_t k = 0; k < ML_COUNT; ++k) host->n_list[k] = d.n_list[k];
-  host->scan_ticket = d.scan_ticket;
-  host->wc_hits = d.wc_hits;
-  __threadfence_system();
+  publish_record(a, host, true);
 }
 
 // Texts above ASM_SINGLE_MAX bytes have more scan tiles than stay resident at

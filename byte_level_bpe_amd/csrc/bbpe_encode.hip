@@ -158,10 +158,7 @@ static_assert(sizeof(Status) <= 256, "the host copy of the status block is 256 b
 
 // The last kernel of every sequence: the status block into pinned host memory.
 __global__ void k_publish(EncodeArgs a, Status *host) {
-  if (threadIdx.x == 0) {
-    *host = *a.ws.status;
-    __threadfence_system();
-  }
+  if (threadIdx.x == 0) publish_record(a, host, false);
 }
 
 // The handle's second stream and its fork/join events, created once.
@@ -288,20 +285,49 @@ void publish(bbpe_tokenizer *t, Go &go, const EncodeArgs &a) {
   go("k_publish", k_publish, dim3(1), dim3(64), a, static_cast<Status *>(t->host_status_dev));
 }
 
-// Waits for the call (its one host synchronisation) and reads the status
-// block that k_publish wrote.
-int finish(bbpe_tokenizer *t, Launcher &go, Status &h) {
-  HIP_OK(hipGetLastError());
-  HIP_OK(hipStreamSynchronize(go.st));
-  go.collect();
-  memcpy(&h, t->host_status, sizeof(Status));
+// Clears the error fields of the host record before a call, unless calls
+// enqueued without a wait are outstanding: their errors stay for the wait.
+void clear_record(bbpe_tokenizer *t) {
+  if (t->inflight) return;
+  volatile Status *h = static_cast<volatile Status *>(t->host_status);
+  h->err_pos = ~0ull;
+  h->err_seg = 0u;
+  h->pad2 = 0u;
+  h->scan_fail = 0u;
+  h->over_cap = 0u;
+}
+
+// While asynchronous encodes are outstanding, every call of the handle must
+// use their stream (a wait on it then covers them all).
+int check_pipeline(const bbpe_tokenizer *t, void *stream) {
+  return t->inflight && stream != t->async_stream ? BBPE_E_INVALID_ARG : BBPE_OK;
+}
+
+// The first error the record holds: bad offsets, a scan that gave up
+// waiting, invalid UTF-8 (its place kept for bbpe_error_detail), ids beyond
+// a capacity.
+int record_error(const bbpe_tokenizer *t, const Status &h) {
   if (h.pad2) return BBPE_E_INVALID_ARG;
   if (h.scan_fail) return BBPE_E_HIP;
   if (h.err_pos != ~0ull) {
     set_last_utf8_error(t, h.err_seg, h.err_pos);
     return BBPE_E_UTF8;
   }
+  if (h.over_cap) return BBPE_E_CAPACITY;
   return BBPE_OK;
+}
+
+// Waits for the call (its one host synchronisation) and reads the status
+// block that its last kernel wrote; this also settles every asynchronous
+// call before it.
+int finish(bbpe_tokenizer *t, Launcher &go, Status &h) {
+  const hipError_t e0 = hipGetLastError();
+  const hipError_t e1 = hipStreamSynchronize(go.st);
+  t->inflight = 0;
+  if (e0 != hipSuccess || e1 != hipSuccess) return BBPE_E_HIP;
+  go.collect();
+  memcpy(&h, t->host_status, sizeof(Status));
+  return record_error(t, h);
 }
 
 // The encode kernels of `a` on go.st, and with fork the group and long
@@ -408,6 +434,7 @@ int run_graph(bbpe_tokenizer *t, const EncodeArgs &a, const WsLayout &L, hipStre
                    memcmp(t->graph_key.data(), kb, sizeof k) == 0;
   if (!hit) {
     if (t->graph_exec) {
+      if (t->inflight) HIP_OK(hipStreamSynchronize(st));  // (replays of it may still run)
       (void)hipGraphExecDestroy(static_cast<hipGraphExec_t>(t->graph_exec));
       t->graph_exec = nullptr;
       t->graph_key.clear();
@@ -430,22 +457,24 @@ int run_graph(bbpe_tokenizer *t, const EncodeArgs &a, const WsLayout &L, hipStre
   return BBPE_OK;
 }
 
-// The encode of both encode entry points.  fork: the second stream beside
+// The encode of the encode entry points.  fork: the second stream beside
 // the short tier (its stream and events created on first use), and the
 // whole sequence launched as one HIP graph, built once and replayed while
 // the arguments stay the same (a replay saves the host the time of
 // launching a dozen kernels and events one by one); otherwise every kernel
 // is launched on the caller's stream, and no stream, event, graph or memory
-// is created.
+// is created.  async: return once the work is enqueued (n_ids unused).
 int encode_impl(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint64_t *d_seg_off,
                 const uint8_t *d_allow, uint32_t n_seg, uint32_t flags, void *d_ws,
                 uint64_t ws_bytes, int32_t *d_ids, uint64_t ids_cap, int64_t *d_id_off,
-                uint64_t *n_ids, void *stream, bool fork) {
+                uint64_t *n_ids, void *stream, bool fork, bool async = false) {
   const bool count_only = (flags & BBPE_COUNT_ONLY) != 0;
   if (count_only) ids_cap = 0;  // k_assemble then copies no ids
+  int rc = check_pipeline(t, stream);
+  if (rc) return rc;
   EncodeArgs a;
   WsLayout L;
-  int rc = prepare(t, d_text, n, d_seg_off, d_allow, n_seg, flags, d_ws, ws_bytes, a, L);
+  rc = prepare(t, d_text, n, d_seg_off, d_allow, n_seg, flags, d_ws, ws_bytes, a, L);
   if (rc) return rc;
   a.ids = d_ids;
   a.ids_cap = ids_cap;
@@ -473,8 +502,9 @@ int encode_impl(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint
   }
   Launcher go{t, reinterpret_cast<hipStream_t>(stream)};
   go.allow_timing = fork;
-  // (the previous call has completed: its stream was synchronised)
-  static_cast<volatile Status *>(t->host_status)->scan_fail = 0u;
+  // (the previous call has completed, its stream synchronised, unless it
+  // was enqueued without a wait on this same stream)
+  clear_record(t);
   bool done = false;
   if (fork && !t->timing && !t->graph_broken) {
     rc = run_graph(t, a, L, go.st);
@@ -486,11 +516,18 @@ int encode_impl(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n, const uint
     rc = enqueue_encode(t, go, a, L, fork);
     if (rc) return rc;
   }
+  if (async) {
+    ++t->inflight;
+    t->async_stream = stream;
+    t->async_keep = keep;
+    return BBPE_OK;
+  }
   Status h{};
   rc = finish(t, go, h);
-  if (rc) return rc;
+  if (rc && rc != BBPE_E_CAPACITY) return rc;
   *n_ids = h.n_ids;
   if (keep) t->wc_last_hits = h.wc_hits;
+  if (rc) return rc;
   if (h.n_ids > ids_cap && !count_only) return BBPE_E_CAPACITY;
   return BBPE_OK;
 }
@@ -524,6 +561,8 @@ int bbpe_upload_tables(bbpe_tokenizer *t, void *d_mem, uint64_t bytes, void *str
   std::lock_guard<std::mutex> lock(t->mu);
   if (bytes < t->layout.total || (reinterpret_cast<uintptr_t>(d_mem) & 255)) return BBPE_E_INVALID_ARG;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (t->inflight)  // (outstanding encodes read the old tables; the wait reports them)
+    HIP_OK(hipStreamSynchronize(static_cast<hipStream_t>(t->async_stream)));
   if (t->graph_exec) {  // (built on the old table addresses)
     (void)hipGraphExecDestroy(static_cast<hipGraphExec_t>(t->graph_exec));
     t->graph_exec = nullptr;
@@ -583,6 +622,32 @@ int bbpe_encode_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
                      ids_cap, d_id_off, n_ids, stream, true);
 }
 
+int bbpe_encode_segments_async(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
+                               const uint64_t *d_seg_off, const uint8_t *d_allow, uint32_t n_seg,
+                               uint32_t flags, void *d_ws, uint64_t ws_bytes, int32_t *d_ids,
+                               uint64_t ids_cap, int64_t *d_id_off, void *stream) {
+  if (!t || !d_id_off || (ids_cap && !d_ids)) return BBPE_E_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(t->mu);
+  if (t->timing) return BBPE_E_STATE;  // (per-kernel events are read at the call's end)
+  return encode_impl(t, d_text, n, d_seg_off, d_allow, n_seg, flags, d_ws, ws_bytes, d_ids,
+                     ids_cap, d_id_off, nullptr, stream, true, true);
+}
+
+int bbpe_encode_wait(bbpe_tokenizer *t, void *stream, uint64_t *n_ids) {
+  if (!t || !n_ids) return BBPE_E_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(t->mu);
+  if (!t->inflight) return BBPE_E_STATE;
+  if (stream != t->async_stream) return BBPE_E_INVALID_ARG;
+  const hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  t->inflight = 0;
+  if (e != hipSuccess) return BBPE_E_HIP;
+  Status h;
+  memcpy(&h, t->host_status, sizeof h);
+  *n_ids = h.n_ids;
+  if (t->async_keep) t->wc_last_hits = h.wc_hits;
+  return record_error(t, h);
+}
+
 int bbpe_encode_segments_noalloc(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t n,
                                  const uint64_t *d_seg_off, const uint8_t *d_allow,
                                  uint32_t n_seg, uint32_t flags, int32_t *d_ids, uint64_t ids_cap,
@@ -610,11 +675,14 @@ int bbpe_pretokenize_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t
   if (!t || !n_pieces || (starts_cap && !d_starts) || (flags & BBPE_COUNT_ONLY))
     return BBPE_E_INVALID_ARG;
   std::lock_guard<std::mutex> lock(t->mu);
+  int rc = check_pipeline(t, stream);
+  if (rc) return rc;
   EncodeArgs a;
   WsLayout L;
-  int rc = prepare(t, d_text, n, d_seg_off, d_allow, n_seg, flags, d_ws, ws_bytes, a, L);
+  rc = prepare(t, d_text, n, d_seg_off, d_allow, n_seg, flags, d_ws, ws_bytes, a, L);
   if (rc) return rc;
   Launcher go{t, reinterpret_cast<hipStream_t>(stream)};
+  clear_record(t);
   launch_front(go, a, L);
   if (n) {
     const uint32_t g = uint32_t(std::min<uint64_t>((n + 255) / 256, 4096));
@@ -624,8 +692,9 @@ int bbpe_pretokenize_segments(bbpe_tokenizer *t, const uint8_t *d_text, uint64_t
   publish(t, go, a);
   Status h{};
   rc = finish(t, go, h);
-  if (rc) return rc;
+  if (rc && rc != BBPE_E_CAPACITY) return rc;
   *n_pieces = h.n_pieces;
+  if (rc) return rc;
   if (h.n_pieces > starts_cap) return BBPE_E_CAPACITY;
   return BBPE_OK;
 }
@@ -650,6 +719,7 @@ int bbpe_timing_report(const bbpe_tokenizer *t, uint32_t idx, const char **name,
 
 void bbpe_free(bbpe_tokenizer *t) {
   if (!t) return;
+  if (t->inflight) (void)hipStreamSynchronize(static_cast<hipStream_t>(t->async_stream));
   for (void *e : t->t_events)
     if (e) (void)hipEventDestroy(static_cast<hipEvent_t>(e));
   if (t->graph_exec) (void)hipGraphExecDestroy(static_cast<hipGraphExec_t>(t->graph_exec));
@@ -667,6 +737,7 @@ void bbpe_free(bbpe_tokenizer *t) {
 int bbpe_word_cache_clear(bbpe_tokenizer *t, void *stream) {
   if (!t) return BBPE_E_INVALID_ARG;
   std::lock_guard<std::mutex> lock(t->mu);
+  if (check_pipeline(t, stream)) return BBPE_E_INVALID_ARG;
   t->wc_last_hits = 0;
   if (!t->wcache) return BBPE_OK;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);

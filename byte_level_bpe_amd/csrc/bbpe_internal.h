@@ -139,7 +139,7 @@ struct Status {
   unsigned int scan_ticket;       // next tile of the id-count scan (k_assemble)
   unsigned int scan_fail;         // nonzero: a scan tile's wait for its predecessors gave up
   unsigned int sp_fix;            // nonzero: k_specials left tiles to k_specials_fix
-  unsigned int pad3;
+  unsigned int over_cap;          // nonzero: a call's ids exceeded its capacity (host record only)
   unsigned long long wc_hits;     // units settled from the kept word cache (k_probe)
 };
 

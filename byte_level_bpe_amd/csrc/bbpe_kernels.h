@@ -110,6 +110,29 @@ struct EncodeArgs {
   WsPtrs ws;
 };
 
+// The call's status block into the host's pinned record (one thread, the
+// sequence's last step).  Counts are the call's own; the error fields only
+// ever go from clear to set here (the host clears them before a call when no
+// other call is outstanding), so that after several calls enqueued without a
+// wait the record still shows whether any of them failed: the first invalid
+// UTF-8 byte met, bad offsets, ids beyond a call's capacity.
+__device__ __forceinline__ void publish_record(const EncodeArgs &a, Status *host, bool ids_out) {
+  const Status &d = *a.ws.status;
+  host->n_pieces = d.n_pieces;
+  host->n_ids = d.n_ids;
+  host->n_chars = d.n_chars;
+  for (uint32_t k = 0; k < ML_COUNT; ++k) host->n_list[k] = d.n_list[k];
+  host->scan_ticket = d.scan_ticket;
+  host->wc_hits = d.wc_hits;
+  if (d.pad2) host->pad2 = d.pad2;
+  if (d.err_pos != ~0ull && host->err_pos == ~0ull) {
+    host->err_seg = d.err_seg;
+    host->err_pos = d.err_pos;
+  }
+  if (ids_out && !(a.flags & BBPE_COUNT_ONLY) && d.n_ids > a.ids_cap) host->over_cap = 1u;
+  __threadfence_system();
+}
+
 __global__ void k_count(EncodeArgs a);
 __global__ void k_scan_chars(EncodeArgs a);
 __global__ void k_spans(EncodeArgs a);

@@ -56,6 +56,12 @@ struct bbpe_tokenizer {
   // device current at the first call that asks for it, freed by bbpe_free.
   void *wcache = nullptr;
   uint64_t wc_last_hits = 0;  // units the last such call settled from it
+  // Encodes enqueued by bbpe_encode_segments_async and not yet waited for,
+  // the stream they are on (every call of the handle uses it until the
+  // wait), and whether the last of them kept the word cache.
+  uint32_t inflight = 0;
+  void *async_stream = nullptr;
+  bool async_keep = false;
   // Every entry point that enqueues work or touches the mutable state above
   // (second stream, fork/join events, timing records) holds this lock for
   // the whole call, so that host threads sharing a handle never interleave

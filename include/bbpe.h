@@ -181,6 +181,35 @@ int bbpe_encode_segments(bbpe_tokenizer *tok, const uint8_t *d_text, uint64_t to
                          uint64_t ids_capacity, int64_t *d_id_off, uint64_t *n_ids,
                          void *hip_stream);
 
+/* bbpe_encode_segments without the wait: the same arguments but n_ids, and
+ * the same work, enqueued on hip_stream; returns once it is enqueued, so a
+ * serving loop can queue the next batch while this one runs (the Baseten
+ * page, "One native call for the whole serving path": every crossing of the
+ * native boundary costs, and here each blocking call also costs a host round
+ * trip between batches).  The call's id count is d_id_off[n_seg] on the
+ * device.  Calls enqueued this way and not yet waited for are outstanding;
+ * while any is, every encode or pre-tokenize call on the handle must use the
+ * same stream (BBPE_E_INVALID_ARG otherwise), and they run in stream order,
+ * so they may share a workspace.  Errors come from bbpe_encode_wait (or from
+ * the next synchronous call on the handle, which settles the outstanding
+ * ones too).  Arguments checked on the host return their error at once, and
+ * nothing is enqueued.  BBPE_E_STATE while per-kernel timing is on. */
+int bbpe_encode_segments_async(bbpe_tokenizer *tok, const uint8_t *d_text, uint64_t total_bytes,
+                               const uint64_t *d_seg_off, const uint8_t *d_allow_special,
+                               uint32_t n_seg, uint32_t flags, void *d_workspace,
+                               uint64_t workspace_bytes, int32_t *d_ids, uint64_t ids_capacity,
+                               int64_t *d_id_off, void *hip_stream);
+
+/* Waits for every outstanding bbpe_encode_segments_async call of the handle
+ * (hip_stream must be theirs: BBPE_E_INVALID_ARG otherwise; BBPE_E_STATE if
+ * none is outstanding).  *n_ids (host) receives the last call's id count.
+ * The result is the first error any of them met, in this order: bad segment
+ * offsets (BBPE_E_INVALID_ARG), a device-side wait of the ordered assembly
+ * that gave up (BBPE_E_HIP), invalid UTF-8 (BBPE_E_UTF8, the first such
+ * byte met kept for bbpe_error_detail), ids beyond a call's capacity
+ * (BBPE_E_CAPACITY), else BBPE_OK. */
+int bbpe_encode_wait(bbpe_tokenizer *tok, void *hip_stream, uint64_t *n_ids);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * bbpe_encode_segments without a workspace argument.  Same arguments
