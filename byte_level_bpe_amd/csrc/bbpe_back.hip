@@ -539,17 +539,23 @@ __device__ __forceinline__ void probe_body(const EncodeArgs &a) {
       spw[u] = m[u] ? a.ws.spst[s0[u] >> 6] : 0ull;
       load_unit(a.text, a.n, s0[u], min(m[u], 32u), ub[u]);
     }
+    // (a unit of two bytes is one key or two atoms: the pair table says
+    // which; longer units probe the key table, whose second word holds key
+    // bytes 8-15 and is read for units longer than 8 bytes only; the loads a
+    // unit does not need go to entry 0, so that they cost no extra lines)
     uint64_t h[PROBE_U], k8[PROBE_U], k8b[PROBE_U];
     uint32_t slot[PROBE_U];
     Slot sl[PROBE_U];
     uint64_t ex[PROBE_U];
+    int32_t pr[PROBE_U];
 #pragma unroll
     for (uint32_t u = 0; u < PROBE_U; ++u) {
       const uint32_t len = min(max(m[u], 1u), 32u);
       unit_hash(ub[u], 0, len, h[u], k8[u], k8b[u]);
-      slot[u] = uint32_t(h[u]) & T.slot_mask;
+      slot[u] = m[u] > 2 ? uint32_t(h[u]) & T.slot_mask : 0u;
       sl[u] = T.slots[slot[u]];
-      ex[u] = T.ext[slot[u]];
+      ex[u] = T.ext[m[u] > 8 ? slot[u] : 0u];
+      pr[u] = T.pair[m[u] == 2 ? (ub[u].byte(0) << 8) | ub[u].byte(1) : 0u];
     }
     int cls[PROBE_U];
 #pragma unroll
@@ -562,6 +568,14 @@ __device__ __forceinline__ void probe_body(const EncodeArgs &a) {
         id = special_id(T, a.text + s, mm);
       } else if (mm == 1) {
         id = s_atom[ub[u].byte(0)];
+      } else if (mm == 2) {
+        if (pr[u] != RANK_NONE) {
+          id = pr[u];
+        } else {  // no merge: its two atoms, as the merge would write them
+          a.ws.tmp_ids[s] = s_atom[ub[u].byte(0)];
+          a.ws.tmp_ids[s + 1] = s_atom[ub[u].byte(1)];
+          a.ws.piece_cnt[idx[u]] = 2u;
+        }
       } else if (mm <= 32) {
         uint32_t meta = 0;
         const UnitBytes<32> &uu = ub[u];

@@ -19,9 +19,10 @@ ASCII lower-case and upper-case letter, where no key can occur across it (the
 byte pair there occurs inside no key; or, at a character boundary, it is no
 2-byte key, neither 3-byte window across it is a key and no 4-byte window
 across it has its bit set in the GPU's hashed 4-gram bitmap).  A unit that is
-a special, a single byte, or a key that the loop merges back into itself is
-settled by k_probe; every other unit goes to the merge kernel of its length
-class (k_merge 2-16 bytes, k_merge_wide 17-512, k_merge_long longer).
+a special, a single byte, two bytes (one key or two atoms, from the pair
+table), or a key that the loop merges back into itself is settled by
+k_probe; every other unit goes to the merge kernel of its length class
+(k_merge 3-16 bytes, k_merge_wide 17-512, k_merge_long longer).
 """
 from __future__ import annotations
 
@@ -117,7 +118,7 @@ def count(name: str) -> dict:
                 k, lb, where = 1, 0, "k_probe"
             else:
                 k, lb = merge_cost(u)
-                where = "k_probe" if k == 1 else tier_of(m)
+                where = "k_probe" if k == 1 or m <= 2 else tier_of(m)
             t = per[where]
             t["units"] += 1
             t["ids"] += k
