@@ -1177,12 +1177,202 @@ struct LongLds {
   int32_t part[LONG_LDS_POS];
 };
 
+// Units made of at most RLE_RUNS runs of one repeated byte (long runs of
+// spaces, dashes, '=' ...) are merged in run-length form, one run of equal
+// part ids (id, count) per lane of the first wave.  The pairs inside a run
+// all have the rank of (id, id); the pair between two runs is one of a
+// kind.  Each step takes the least rank R and the leftmost pair that has
+// it, as the one-at-a-time loop does.  A pair between two runs merges
+// alone: (x, c), (y, d) become (x, c - 1), (R, 1), (y, d - 1).  A pair
+// inside a run (x, c) starts a batch: the loop merges the run's parts two
+// by two, left to right, into parts R for as long as every pair these
+// merges create ranks above R (the first creates (left neighbour, R) and
+// (R, x), later ones (R, R) and again (R, x)); once one ranks at or below R
+// the loop takes it next, so the batch stops after the first merge, or the
+// second, or runs through the whole run: (x, c) becomes (R, k),
+// (x, c - 2k).  Runs with equal neighbours are joined.  Returns false, with
+// nothing written, when the runs do not fit in a wave or the steps exceed
+// RLE_STEPS; the unit is then merged position by position.  (Merging a run
+// of n equal bytes takes a few steps per doubling of the part length.)
+constexpr uint32_t RLE_RUNS = 64, RLE_STEPS = 4096;
+
+__device__ bool merge_long_runs(const EncodeArgs &a, uint32_t i, uint32_t s, uint32_t m,
+                                int32_t *scratch) {
+  const DevTables &T = a.T;
+  const uint32_t tid = threadIdx.x;
+  const uint8_t *p = a.text + s;
+  // runs of equal bytes: their starts, in no order, at most RLE_RUNS of them
+  // kept (positions tid, tid + LONG_BLOCK, ..., eight loads in flight)
+  uint32_t *nst = reinterpret_cast<uint32_t *>(scratch + 4 * RLE_RUNS);
+  if (tid == 0) *nst = 0u;
+  __syncthreads();
+  for (uint32_t k0 = 0; k0 * LONG_BLOCK < m; k0 += 8) {
+    uint32_t b[8], pb[8];
+#pragma unroll
+    for (uint32_t q = 0; q < 8; ++q) {
+      const uint32_t j = tid + (k0 + q) * LONG_BLOCK;
+      b[q] = j < m ? uint32_t(p[j]) : 0u;
+      pb[q] = (j < m && j > 0) ? uint32_t(p[j - 1]) : 0x100u;
+    }
+#pragma unroll
+    for (uint32_t q = 0; q < 8; ++q) {
+      const uint32_t j = tid + (k0 + q) * LONG_BLOCK;
+      if (j < m && b[q] != pb[q]) {
+        const uint32_t o = atomicAdd(nst, 1u);
+        if (o < RLE_RUNS) scratch[o] = int32_t(j);
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t nruns = *nst;
+  if (nruns > RLE_RUNS) return false;
+  int32_t *fid = scratch + RLE_RUNS;
+  uint32_t *fcnt = reinterpret_cast<uint32_t *>(scratch + 2 * RLE_RUNS);
+  uint32_t *fres = reinterpret_cast<uint32_t *>(scratch + 3 * RLE_RUNS);  // [runs, ok]
+  if (tid < 64) {
+    const int lane = int(tid);
+    int nr = int(nruns);
+    // the starts in text order: lane l sends its start to the lane of its
+    // rank among them
+    const int32_t v = lane < nr ? scratch[lane] : 0x7FFFFFFF;
+    int rk = 0;
+    for (int q = 0; q < nr; ++q) rk += __shfl(v, q, 64) < v ? 1 : 0;
+    const int32_t st_sorted = __builtin_amdgcn_ds_permute((lane < nr ? rk : lane) * 4, v);
+    const int32_t en_sorted = __shfl(st_sorted, min(lane + 1, 63), 64);
+    int32_t id = 0, ra = RANK_NONE, rb = RANK_NONE;
+    uint32_t cnt = 0;
+    if (lane < nr) {
+      const uint32_t st = uint32_t(st_sorted);
+      const uint32_t en = lane + 1 < nr ? uint32_t(en_sorted) : m;
+      const uint32_t b = p[st];
+      const uint32_t nb = lane + 1 < nr ? uint32_t(p[en]) : 0u;
+      id = T.atom[b];
+      cnt = en - st;
+      ra = T.pair[b * 256u + b];
+      rb = lane + 1 < nr ? T.pair[b * 256u + nb] : RANK_NONE;
+    }
+    bool ok = true;
+    for (uint32_t step = 0;; ++step) {  // wave-uniform
+      const bool live = lane < nr;
+      const int32_t va = (live && cnt >= 2) ? ra : RANK_NONE;
+      const int32_t vb = (live && lane + 1 < nr) ? rb : RANK_NONE;
+      const int32_t R = wave_min_i32(min(va, vb));
+      if (R == RANK_NONE) break;
+      if (step >= RLE_STEPS) {
+        ok = false;
+        break;
+      }
+      const unsigned long long ba = __ballot(va == R), bb = __ballot(vb == R);
+      const int L = __ffsll(ba | bb) - 1;
+      const bool inner = (ba >> L) & 1;
+      const int32_t idL = __shfl(id, L, 64), idL1 = __shfl(id, min(L + 1, 63), 64);
+      const int32_t idLm = __shfl(id, max(L - 1, 0), 64);
+      const uint32_t cL = __shfl(cnt, L, 64), cL1 = __shfl(cnt, min(L + 1, 63), 64);
+      // the runs that replace run L (inner) or runs L and L+1 (between)
+      int32_t nid0, nid1, nid2;
+      uint32_t nc0, nc1, nc2;
+      int consumed;
+      if (inner) {
+        int32_t look = RANK_NONE;
+        if (lane == 0 && L > 0) look = merge_rank(T, uint32_t(idLm), uint32_t(R));
+        if (lane == 1 && cL >= 3) look = merge_rank(T, uint32_t(R), uint32_t(idL));
+        if (lane == 2 && cL >= 4) look = merge_rank(T, uint32_t(R), uint32_t(R));
+        const int32_t nl = __shfl(look, 0, 64), nx = __shfl(look, 1, 64), pp = __shfl(look, 2, 64);
+        uint32_t k;
+        if (cL < 4 || (L > 0 && nl <= R) || nx <= R) k = 1;
+        else if (pp <= R) k = 2;
+        else k = cL / 2;
+        nid0 = R, nc0 = k;
+        nid1 = idL, nc1 = cL - 2 * k;
+        nid2 = 0, nc2 = 0;
+        consumed = 1;
+      } else {
+        nid0 = idL, nc0 = cL - 1;
+        nid1 = R, nc1 = 1;
+        nid2 = idL1, nc2 = cL1 - 1;
+        consumed = 2;
+      }
+      // the non-empty ones of the three, in order: e0, e1, e2
+      const bool h0 = nc0 != 0, h1 = nc1 != 0, h2 = nc2 != 0;
+      const int nn = int(h0) + int(h1) + int(h2);
+      const int e0 = h0 ? 0 : (h1 ? 1 : 2), e1 = (h0 && h1) ? 1 : 2;
+      const int shift = nn - consumed;
+      if (nr + shift > int(RLE_RUNS)) {
+        ok = false;
+        break;
+      }
+      // lanes before L keep their run, L .. L+nn-1 take the new runs, the
+      // rest take the run `shift` lanes before them
+      const int src = min(max(lane - shift, 0), 63);
+      const int32_t sid = __shfl(id, src, 64);
+      const uint32_t scnt = __shfl(cnt, src, 64);
+      if (lane >= L) {
+        if (lane < L + nn) {
+          const int t = lane - L;
+          const int e = t == 0 ? e0 : (t == 1 ? e1 : 2);
+          id = e == 0 ? nid0 : (e == 1 ? nid1 : nid2);
+          cnt = e == 0 ? nc0 : (e == 1 ? nc1 : nc2);
+        } else {
+          id = sid;
+          cnt = scnt;
+        }
+      }
+      nr += shift;
+      // join runs with equal neighbours
+      for (;;) {
+        const int32_t pid = __shfl_up(id, 1, 64);
+        const unsigned long long eq = __ballot(lane > 0 && lane < nr && id == pid);
+        if (!eq) break;
+        const int f = __ffsll(eq) - 1;
+        const uint32_t cf = __shfl(cnt, f, 64);
+        if (lane == f - 1) cnt += cf;
+        const int32_t nid = __shfl(id, min(lane + 1, 63), 64);
+        const uint32_t ncnt = __shfl(cnt, min(lane + 1, 63), 64);
+        if (lane >= f) {
+          id = nid;
+          cnt = ncnt;
+        }
+        --nr;
+      }
+      // ranks of every run: inside it and with the next run
+      const int32_t nxt = __shfl(id, min(lane + 1, 63), 64);
+      merge_rank2(T, lane < nr, uint32_t(id), uint32_t(id), lane + 1 < nr, uint32_t(id), uint32_t(nxt), ra, rb);
+      if (lane >= nr) ra = RANK_NONE;
+      if (lane + 1 >= nr) rb = RANK_NONE;
+    }
+    if (lane < nr) {
+      fid[lane] = id;
+      fcnt[lane] = cnt;
+    }
+    if (lane == 0) {
+      fres[0] = uint32_t(nr);
+      fres[1] = ok ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  const uint32_t nr = fres[0];
+  const bool ok = fres[1] != 0;
+  if (ok) {
+    uint32_t o = 0;
+    for (uint32_t r = 0; r < nr; ++r) {
+      const uint32_t cr = fcnt[r];
+      const int32_t ir = fid[r];
+      for (uint32_t x = tid; x < cr; x += LONG_BLOCK) a.ws.tmp_ids[s + o + x] = ir;
+      o += cr;
+    }
+    if (tid == 0) a.ws.piece_cnt[i] = o;
+  }
+  __syncthreads();
+  return ok;
+}
+
 __device__ void merge_long(const EncodeArgs &a, uint32_t i, uint32_t *sh, LongLds &ld) {
   const DevTables &T = a.T;
   const uint32_t tid = threadIdx.x;
   const uint32_t s = a.ws.piece_start[i];
   const uint32_t m = a.ws.piece_start[i + 1] - s;
   const uint8_t *p = a.text + s;
+  if (merge_long_runs(a, i, s, m, ld.part)) return;
   const uint32_t base = s >> 5;
   const uint32_t nbk = (m + 63) / 64;
   const bool in_lds = nbk <= LONG_LDS_BLOCKS;

@@ -466,6 +466,38 @@ def test_long_units_adversarial_tables():
         assert_ids(tok, orc, segs, safe=False, what="adversarial table %d" % ti)
 
 
+def test_long_units_of_few_byte_runs():
+    """Units over 512 bytes made of a few runs of one repeated byte (merged
+    in run-length form when there are at most 64 runs, position by position
+    above that): 1-64 runs, 64 and 65 runs exactly, under random tables over
+    {a, b, c} whose ranks let merges create pairs of lower or equal rank."""
+    import itertools
+    for ti in range(12):
+        r = random.Random(700 + ti)
+        tab = dict(atoms_permuted(1))
+        keys = [bytes(k) for L in range(2, 7) for k in itertools.product(b"abc", repeat=L)]
+        r.shuffle(keys)
+        chosen = keys[:r.randint(10, 80)]
+        for k, rk in zip(chosen, r.sample(range(256, 856), len(chosen))):
+            tab[k] = rk
+        tok, orc = make(tab, [], 0)
+        segs = []
+        for nruns in (1, 2, 3, r.randint(4, 20), 64, 65):
+            runs, last = [], None
+            while len(runs) < nruns:
+                c = r.choice(b"abc")
+                if c == last:
+                    continue
+                runs.append(bytes([c]) * r.randint(1, 80 if nruns > 20 else 900))
+                last = c
+            seg = b"".join(runs)
+            if len(seg) < 520:
+                seg = seg + bytes([b"abc"[(b"abc".index(seg[-1:]) + 1) % 3]]) * (520 - len(seg))
+            segs.append((seg, False))
+        say("few-run long units, table", ti)
+        assert_ids(tok, orc, segs, safe=False, what="few-run table %d" % ti)
+
+
 def test_long_runs_main_table():
     """Runs of one character and repeated patterns with the 100,256-rank
     table, chunked and unchunked."""
