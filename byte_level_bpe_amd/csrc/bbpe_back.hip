@@ -478,6 +478,7 @@ __device__ __forceinline__ void wc_put(const EncodeArgs &a, const UnitBytes<SK> 
 constexpr uint32_t WNS = 8;                // positions per lane in the group tiers
 constexpr uint32_t WAVE_MAX = 64 * WNS;    // longest unit the group tiers hold
 constexpr uint32_t GROUP_PACK_MIN = 4096;  // group units above which several share a wave
+constexpr uint32_t FEW32_MAX = 256;        // 17-32-byte units taken 32 lanes each up to this
 
 // Continue a probe whose first slot (sl, e at index idx) is already loaded.
 template <typename RestEq>
@@ -1019,7 +1020,10 @@ __device__ __forceinline__ void merge_short_item(const EncodeArgs &a, uint32_t P
 // lane-0 ticket and broadcast, which lets the compiler split the loop per
 // lane.
 constexpr uint32_t SHORT_K = 4;  // chunks of 64 entries per item
-template <bool WC>
+// (ELECT: the per-call word cache, texts from WORD_CACHE_MIN bytes.  The LDS
+// of a wave -- atoms, part ids of up to 16 positions per lane, the leaders'
+// queue only with the cache -- sets how many merge waves share a CU.)
+template <bool WC, bool ELECT>
 __device__ __forceinline__ void merge_body(const EncodeArgs &a) {
   if (a.ws.status->pad2) return;
   const Status *st = a.ws.status;
@@ -1027,20 +1031,20 @@ __device__ __forceinline__ void merge_body(const EncodeArgs &a) {
   const uint32_t P = uint32_t(st->n_pieces);
   const uint32_t n16 = st->n_list[ML_16], n8 = st->n_list[ML_8], n4 = st->n_list[ML_4];
   // entries per item: 256 with the word cache (elected together), else 64
-  const uint32_t C = a.word_cache ? 64 * SHORT_K : 64;
+  const uint32_t C = ELECT ? 64 * SHORT_K : 64;
   const uint32_t e16 = (n16 + C - 1) / C, e8 = e16 + (n8 + C - 1) / C, e4 = e8 + (n4 + C - 1) / C;
   if (blockIdx.x >= e4) return;
   __shared__ int32_t s_atom[256];
-  __shared__ uint16_t s_part_lo[32 * 64];  // [position][lane]: part ids of each lane's unit
-  __shared__ uint8_t s_part_hi[32 * 64];
-  __shared__ uint32_t s_queue[64 * SHORT_K];
+  __shared__ uint16_t s_part_lo[16 * 64];  // [position][lane]: part ids of each lane's unit
+  __shared__ uint8_t s_part_hi[16 * 64];
+  __shared__ uint32_t s_queue[ELECT ? 64 * SHORT_K : 1];
   const PartCol lp{s_part_lo + lane, s_part_hi + lane};
   reinterpret_cast<int4 *>(s_atom)[lane] = reinterpret_cast<const int4 *>(a.T.atom)[lane];
   __syncthreads();
   for (uint32_t item = blockIdx.x; item < e4; item += gridDim.x) {
     const bool in16 = item < e16, in8 = !in16 && item < e8;
     const uint32_t first = (item - (in16 ? 0u : in8 ? e16 : e8)) * C;
-    if (a.word_cache) {
+    if constexpr (ELECT) {
       if (in16)
         merge_short_item<16, SHORT_K, true, WC>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_16], n16, first, lane);
       else if (in8)
@@ -1058,11 +1062,17 @@ __device__ __forceinline__ void merge_body(const EncodeArgs &a) {
   }
 }
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge(EncodeArgs a) {
-  merge_body<false>(a);
+  merge_body<false, false>(a);
+}
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge_elect(EncodeArgs a) {
+  merge_body<false, true>(a);
 }
 // the same with the kept word cache
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge_wc(EncodeArgs a) {
-  merge_body<true>(a);
+  merge_body<true, false>(a);
+}
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge_elect_wc(EncodeArgs a) {
+  merge_body<true, true>(a);
 }
 
 // Merge of the units of 17..WAVE_MAX bytes (second stream, beside k_merge:
@@ -1074,7 +1084,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
 // all of them every round); many, 16 or 32 lanes per unit, for throughput.
 // Then the units of 17-32 bytes, one lane each, 64 per item (nearly every
 // such unit is a byte string of its own, so they skip the word cache).
-template <bool WC>
+template <bool WC, bool FEW32>
 __device__ __forceinline__ void merge_wide_body(const EncodeArgs &a) {
   if (a.ws.status->pad2) return;
   const Status *st = a.ws.status;
@@ -1084,7 +1094,11 @@ __device__ __forceinline__ void merge_wide_body(const EncodeArgs &a) {
   const bool pack = n64 + n32g + n16g > GROUP_PACK_MIN;
   const uint32_t e64 = n64, e32g = e64 + (pack ? (n32g + 1) / 2 : n32g);
   const uint32_t e16g = e32g + (pack ? (n16g + 3) / 4 : n16g);
-  const uint32_t e32 = e16g + (n32 + 63) / 64;
+  // (FEW32, few units of 17-32 bytes: 32 lanes each, one position per lane,
+  // as in the group tier; else one lane each, positions in registers.  A
+  // kernel of its own: its registers slowed the group tier of large texts.)
+  const bool few32 = FEW32 && n32 <= FEW32_MAX;
+  const uint32_t e32 = e16g + (few32 ? (n32 + 1) / 2 : (n32 + 63) / 64);
   if (blockIdx.x >= e32) return;
   __shared__ int32_t s_atom[256];
   __shared__ uint16_t s_part_lo[32 * 64];  // [position][lane]: part ids of each lane's unit
@@ -1101,6 +1115,8 @@ __device__ __forceinline__ void merge_wide_body(const EncodeArgs &a) {
     } else if (item < e16g) {
       if (pack) merge_group<16, 8>(a, a.ws.lst[ML_G128], n16g, (item - e32g) * 4, lane);
       else merge_group<64, 2>(a, a.ws.lst[ML_G128], n16g, item - e32g, lane);
+    } else if (few32) {
+      merge_group<32, 1>(a, a.ws.lst[ML_32], n32, (item - e16g) * 2, lane);
     } else {
       const uint32_t x = (item - e16g) * 64 + uint32_t(lane);
       if (x < n32) merge_short_unit<32, WC>(a, s_atom, a.ws.lst[ML_32][x], lp);
@@ -1108,11 +1124,14 @@ __device__ __forceinline__ void merge_wide_body(const EncodeArgs &a) {
   }
 }
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge_wide(EncodeArgs a) {
-  merge_wide_body<false>(a);
+  merge_wide_body<false, false>(a);
+}
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge_wide_few32(EncodeArgs a) {
+  merge_wide_body<false, true>(a);
 }
 // the same with the kept word cache
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge_wide_wc(EncodeArgs a) {
-  merge_wide_body<true>(a);
+  merge_wide_body<true, false>(a);
 }
 
 // Block-wide helpers of the long tier (LONG_BLOCK threads, LDS scratch sh).

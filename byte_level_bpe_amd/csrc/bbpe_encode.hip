@@ -356,22 +356,34 @@ int enqueue_encode(bbpe_tokenizer *t, Go &go, const EncodeArgs &a, const WsLayou
     const uint32_t merge_grid = uint32_t(std::min<uint64_t>((n + 255) / 256, 8192));
     // (the kept word cache has kernels of its own, so that the others carry
     // none of its code)
-    auto *const merge_k = a.wcache ? k_merge_wc : k_merge;
-    auto *const wide_k = a.wcache ? k_merge_wide_wc : k_merge_wide;
+    auto *const merge_k = a.word_cache ? (a.wcache ? k_merge_elect_wc : k_merge_elect)
+                                       : (a.wcache ? k_merge_wc : k_merge);
+    auto *const wide_k = a.wcache ? k_merge_wide_wc : (a.word_cache ? k_merge_wide : k_merge_wide_few32);
     if (fork) {
       // the units of 17-512 bytes (few, long dependent chains) run on the
       // second stream beside the rest of the short tier; the long tier
       // follows the short tier on the caller's stream (a long-tier
       // workgroup needs a whole CU's LDS, which the short tier's waves hold
       // until they drain)
+      // (which branch is enqueued first matters for the graph: its first
+      // kernel starts about 5 us after the fork, the other's about 10.
+      // Below WORD_CACHE_MIN bytes the short and long tiers come first and
+      // the group tier, short there, runs beside them; from it the group
+      // tier is the longest chain and comes first.)
       int rc = go.record(0);
+      if (!a.word_cache) {
+        go("k_merge", merge_k, dim3(merge_grid), dim3(64), a);
+        go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
+      }
       go.use_aux();
       if (!rc) rc = go.wait(0);
       go("k_merge_wide", wide_k, dim3(wide_grid), dim3(64), a);
       if (!rc) rc = go.record(1);
       go.use_main();
-      go("k_merge", merge_k, dim3(merge_grid), dim3(64), a);
-      go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
+      if (a.word_cache) {
+        go("k_merge", merge_k, dim3(merge_grid), dim3(64), a);
+        go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
+      }
       if (!rc) rc = go.wait(1);
       if (rc) return rc;
     } else {

@@ -149,8 +149,11 @@ __global__ void k_pieces(EncodeArgs a);
 __global__ void k_probe(EncodeArgs a);
 __global__ void k_probe1(EncodeArgs a);
 __global__ void k_merge(EncodeArgs a);
+__global__ void k_merge_elect(EncodeArgs a);
+__global__ void k_merge_elect_wc(EncodeArgs a);
 __global__ void k_merge_long(EncodeArgs a);
 __global__ void k_merge_wide(EncodeArgs a);
+__global__ void k_merge_wide_few32(EncodeArgs a);
 __global__ void k_probe_wc(EncodeArgs a);
 __global__ void k_probe1_wc(EncodeArgs a);
 __global__ void k_merge_wc(EncodeArgs a);
