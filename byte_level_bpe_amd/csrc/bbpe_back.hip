@@ -1022,17 +1022,22 @@ __device__ __forceinline__ void merge_short_item(const EncodeArgs &a, uint32_t P
 constexpr uint32_t SHORT_K = 4;  // chunks of 64 entries per item
 // (ELECT: the per-call word cache, texts from WORD_CACHE_MIN bytes.  The LDS
 // of a wave -- atoms, part ids of up to 16 positions per lane, the leaders'
-// queue only with the cache -- sets how many merge waves share a CU.)
-template <bool WC, bool ELECT>
+// queue only with the cache -- sets how many merge waves share a CU.
+// FEW32: up to FEW32_MAX units of 17-32 bytes are taken here too, 32 lanes
+// each with one position per lane, as the first items, so that their long
+// chains start first; k_merge_wide then leaves them out.)
+template <bool WC, bool ELECT, bool FEW32>
 __device__ __forceinline__ void merge_body(const EncodeArgs &a) {
   if (a.ws.status->pad2) return;
   const Status *st = a.ws.status;
   const int lane = int(threadIdx.x);
   const uint32_t P = uint32_t(st->n_pieces);
   const uint32_t n16 = st->n_list[ML_16], n8 = st->n_list[ML_8], n4 = st->n_list[ML_4];
+  const uint32_t n32 = st->n_list[ML_32];
+  const uint32_t f32 = (FEW32 && n32 <= FEW32_MAX) ? (n32 + 1) / 2 : 0u;
   // entries per item: 256 with the word cache (elected together), else 64
   const uint32_t C = ELECT ? 64 * SHORT_K : 64;
-  const uint32_t e16 = (n16 + C - 1) / C, e8 = e16 + (n8 + C - 1) / C, e4 = e8 + (n4 + C - 1) / C;
+  const uint32_t e16 = f32 + (n16 + C - 1) / C, e8 = e16 + (n8 + C - 1) / C, e4 = e8 + (n4 + C - 1) / C;
   if (blockIdx.x >= e4) return;
   __shared__ int32_t s_atom[256];
   __shared__ uint16_t s_part_lo[16 * 64];  // [position][lane]: part ids of each lane's unit
@@ -1042,8 +1047,12 @@ __device__ __forceinline__ void merge_body(const EncodeArgs &a) {
   reinterpret_cast<int4 *>(s_atom)[lane] = reinterpret_cast<const int4 *>(a.T.atom)[lane];
   __syncthreads();
   for (uint32_t item = blockIdx.x; item < e4; item += gridDim.x) {
+    if (FEW32 && item < f32) {
+      merge_group<32, 1>(a, a.ws.lst[ML_32], n32, item * 2, lane);
+      continue;
+    }
     const bool in16 = item < e16, in8 = !in16 && item < e8;
-    const uint32_t first = (item - (in16 ? 0u : in8 ? e16 : e8)) * C;
+    const uint32_t first = (item - (in16 ? f32 : in8 ? e16 : e8)) * C;
     if constexpr (ELECT) {
       if (in16)
         merge_short_item<16, SHORT_K, true, WC>(a, P, s_atom, lp, s_queue, a.ws.lst[ML_16], n16, first, lane);
@@ -1062,17 +1071,17 @@ __device__ __forceinline__ void merge_body(const EncodeArgs &a) {
   }
 }
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge(EncodeArgs a) {
-  merge_body<false, false>(a);
+  merge_body<false, false, true>(a);
 }
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge_elect(EncodeArgs a) {
-  merge_body<false, true>(a);
+  merge_body<false, true, false>(a);
 }
 // the same with the kept word cache
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge_wc(EncodeArgs a) {
-  merge_body<true, false>(a);
+  merge_body<true, false, false>(a);
 }
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) k_merge_elect_wc(EncodeArgs a) {
-  merge_body<true, true>(a);
+  merge_body<true, true, false>(a);
 }
 
 // Merge of the units of 17..WAVE_MAX bytes (second stream, beside k_merge:
@@ -1094,11 +1103,10 @@ __device__ __forceinline__ void merge_wide_body(const EncodeArgs &a) {
   const bool pack = n64 + n32g + n16g > GROUP_PACK_MIN;
   const uint32_t e64 = n64, e32g = e64 + (pack ? (n32g + 1) / 2 : n32g);
   const uint32_t e16g = e32g + (pack ? (n16g + 3) / 4 : n16g);
-  // (FEW32, few units of 17-32 bytes: 32 lanes each, one position per lane,
-  // as in the group tier; else one lane each, positions in registers.  A
-  // kernel of its own: its registers slowed the group tier of large texts.)
+  // (FEW32: up to FEW32_MAX units of 17-32 bytes are k_merge's; else they
+  // are taken here, one lane each, positions in registers)
   const bool few32 = FEW32 && n32 <= FEW32_MAX;
-  const uint32_t e32 = e16g + (few32 ? (n32 + 1) / 2 : (n32 + 63) / 64);
+  const uint32_t e32 = e16g + (few32 ? 0u : (n32 + 63) / 64);
   if (blockIdx.x >= e32) return;
   __shared__ int32_t s_atom[256];
   __shared__ uint16_t s_part_lo[32 * 64];  // [position][lane]: part ids of each lane's unit
@@ -1115,8 +1123,6 @@ __device__ __forceinline__ void merge_wide_body(const EncodeArgs &a) {
     } else if (item < e16g) {
       if (pack) merge_group<16, 8>(a, a.ws.lst[ML_G128], n16g, (item - e32g) * 4, lane);
       else merge_group<64, 2>(a, a.ws.lst[ML_G128], n16g, item - e32g, lane);
-    } else if (few32) {
-      merge_group<32, 1>(a, a.ws.lst[ML_32], n32, (item - e16g) * 2, lane);
     } else {
       const uint32_t x = (item - e16g) * 64 + uint32_t(lane);
       if (x < n32) merge_short_unit<32, WC>(a, s_atom, a.ws.lst[ML_32][x], lp);
