@@ -367,17 +367,16 @@ int enqueue_encode(bbpe_tokenizer *t, Go &go, const EncodeArgs &a, const WsLayou
       // until they drain)
       // (which branch is enqueued first matters for the graph: its first
       // kernel starts about 5 us after the fork, the other's about 10.
-      // Below WORD_CACHE_MIN bytes the short and long tiers come first and
-      // the group tier, short there, runs beside them; from it the group
-      // tier is the longest chain and comes first.)
+      // Below WORD_CACHE_MIN bytes the short tier comes first, and the
+      // group tier, short there, runs beside it followed by the long tier;
+      // from it the group tier is the longest chain and comes first, and
+      // the long tier follows the short tier.)
       int rc = go.record(0);
-      if (!a.word_cache) {
-        go("k_merge", merge_k, dim3(merge_grid), dim3(64), a);
-        go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
-      }
+      if (!a.word_cache) go("k_merge", merge_k, dim3(merge_grid), dim3(64), a);
       go.use_aux();
       if (!rc) rc = go.wait(0);
       go("k_merge_wide", wide_k, dim3(wide_grid), dim3(64), a);
+      if (!a.word_cache) go("k_merge_long", k_merge_long, dim3(long_grid), dim3(1024), a);
       if (!rc) rc = go.record(1);
       go.use_main();
       if (a.word_cache) {
