@@ -243,6 +243,50 @@ def bench_decode(args, w):
     print(json.dumps(res), flush=True)
 
 
+def two_requests_in_flight_ms(tok, tok2, text, seg_off, allow, total, bufs, streams, steps, safe):
+    """K calls alternated between two handles on two streams (the second
+    handle with its own workspace and outputs), settled by one wait each."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        h, (ids, id_off), st = (tok, bufs[0], streams[0]) if k % 2 == 0 else (tok2, bufs[1], streams[1])
+        h.encode_device_async(text, seg_off, allow, total, ids, id_off, tiktoken_safe=safe, stream=st)
+    torch.cuda.synchronize()
+    tok.encode_wait(streams[0])
+    if steps > 1:
+        tok2.encode_wait(streams[1])
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def two_requests_leg(tok, w, text, seg_off, allow, total, n_seg, ids, id_off, stream, steps):
+    """Context, outside the timed region: the same workload as two requests
+    in flight at once (two handles, two streams), the way a server overlaps
+    requests; every call still runs the whole path."""
+    import torch
+    import byte_level_bpe_amd as B
+    tok2 = B.load_ranks(w.tokens, w.specials, w.grammar)
+    tok2.upload(text.device)
+    tok2.workspace(total, n_seg, text.device)
+    ids2 = torch.empty_like(ids)
+    id_off2 = torch.empty_like(id_off)
+    s2 = torch.cuda.Stream(device=text.device)
+    bufs, streams = [(ids, id_off), (ids2, id_off2)], [stream, s2]
+    gc.collect()
+    gc.disable()
+    two_requests_in_flight_ms(tok, tok2, text, seg_off, allow, total, bufs, streams, 4, w.tiktoken_safe)
+    ms = two_requests_in_flight_ms(tok, tok2, text, seg_off, allow, total, bufs, streams, steps,
+                                   w.tiktoken_safe)
+    gc.enable()
+    ok = bool(torch.equal(ids2[:int(id_off2[-1])], ids[:int(id_off[-1])]))
+    del tok2
+    return {"ms_per_step": round(ms, 4), "MBs": round(total / (ms * 1e-3) / 1e6, 2),
+            "ids_equal": ok,
+            "what": "the same calls alternated between two handles on two streams, two requests "
+                    "in flight (context: every call runs the whole path; value is one request "
+                    "at a time)"}
+
+
 def warm_cache_leg(tok, w, text, seg_off, allow, total, ids, id_off, stream, want_sha, reps=5):
     """The word cache kept across calls (BBPE_KEEP_WORD_CACHE), outside the
     timed region of the headline number: one call's device time (events on
@@ -427,6 +471,7 @@ def main():
         tok.encode_wait(stream)
     other_wall = time.perf_counter() - t0
     gc.enable()
+    two = two_requests_leg(tok, w, text, seg_off, allow, total, n_seg, ids, id_off, stream, args.steps)
     step_ms = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps))
     dev_ms = evs[0].elapsed_time(evs[-1])
     # per-kernel durations: the same K calls again with an event pair around
@@ -519,6 +564,7 @@ def main():
             "MBs": round(total * args.steps / other_wall / 1e6, 2),
             "what": ("the same calls queued back to back, one wait at the end" if args.blocking else
                      "the same calls through the entry point that waits for each call's result")},
+        "two_requests_in_flight": two,
         "pcie_inclusive": {"ms_per_step": round(e2e_ms, 4), "MBs": round(total / (e2e_ms * 1e-3) / 1e6, 2),
                            "steps": e2e_steps,
                            "what": "text host-to-device from pinned memory, encode, ids device-to-host"},

@@ -345,9 +345,12 @@ int enqueue_encode(bbpe_tokenizer *t, Go &go, const EncodeArgs &a, const WsLayou
     if (n < PROBE_SMALL) {
       const uint32_t probe_grid = uint32_t((n + 2047) / 2048);
       go("k_probe", a.wcache ? k_probe1_wc : k_probe1, dim3(probe_grid), dim3(PROBE_BLOCK), a);
-    } else {
+    } else if (n < PROBE_MID || a.wcache) {
       const uint32_t probe_grid = uint32_t(std::min<uint64_t>((n + 8191) / 8192, 8192));
       go("k_probe", a.wcache ? k_probe_wc : k_probe, dim3(probe_grid), dim3(PROBE_BLOCK), a);
+    } else {
+      const uint32_t probe_grid = uint32_t(std::min<uint64_t>((n + 4095) / 4096, 8192));
+      go("k_probe", k_probe2, dim3(probe_grid), dim3(PROBE_BLOCK), a);
     }
     // (grid-stride kernels: their units are few, and idle waves of the
     // second stream take dispatch slots from the short tier.)

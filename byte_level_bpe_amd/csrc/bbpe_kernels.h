@@ -77,6 +77,7 @@ constexpr uint32_t PROBE_BLOCK = 512;
 // folds the tiles before (and, for the lookahead, after) it itself.
 constexpr uint32_t FUSE_TILES = 2048;
 constexpr uint64_t PROBE_SMALL = 1u << 20;  // texts below this: one unit per probe thread
+constexpr uint64_t PROBE_MID = 1u << 23;    // texts from this: two units per probe thread
 // Texts from this size on use the word cache.  Below it the short tier's
 // units fit in about one generation of resident waves, so its length is
 // its longest chain of merge rounds, which the cache's election only delays.
@@ -147,6 +148,7 @@ __global__ void k_split_o200k(EncodeArgs a);
 __global__ void k_scan_tiles_np(EncodeArgs a);
 __global__ void k_pieces(EncodeArgs a);
 __global__ void k_probe(EncodeArgs a);
+__global__ void k_probe2(EncodeArgs a);
 __global__ void k_probe1(EncodeArgs a);
 __global__ void k_merge(EncodeArgs a);
 __global__ void k_merge_elect(EncodeArgs a);
