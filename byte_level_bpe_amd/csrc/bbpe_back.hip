@@ -259,19 +259,43 @@ __device__ __forceinline__ uint32_t text_dword(const uint8_t *__restrict__ text,
   return v;
 }
 
-// bytes [s, s+m) of the text, zero beyond m (m <= SK)
+// bytes [s, s+m) of the text, zero beyond m (m <= SK).  The aligned 16-byte
+// chunks that hold them are loaded whole (a chunk holding a byte of the
+// text lies in that byte's page: the text is 16-byte aligned), at most
+// SK/16 + 1 of them, then shifted into place: a few wide loads per unit
+// instead of one per dword.
 template <int SK>
 __device__ __forceinline__ void load_unit(const uint8_t *__restrict__ text, uint64_t n, uint32_t s,
                                           uint32_t m, UnitBytes<SK> &u) {
   constexpr int NB = UnitBytes<SK>::NB;
-  const uint64_t a0 = s & ~3u;
-  const uint32_t off = s & 3u;
-  uint32_t raw[NB + 1];
+  constexpr int NC = (SK + 14) / 16 + 1;  // chunks over [s, s + SK) at any offset
+  constexpr int NQ = SK / 4;  // dwords that can hold unit bytes
+  static_assert(4 * NC >= NQ + 4, "chunks cover the shifted dwords");
+  const uint32_t off = s & 15u, sh = off >> 2, ob = off & 3u;
+  const uint4 *c = reinterpret_cast<const uint4 *>(text) + (s >> 4);
+  uint32_t raw[4 * NC];
 #pragma unroll
-  for (int q = 0; q <= NB; ++q) raw[q] = (4u * q < off + m) ? text_dword(text, n, a0 + 4u * q) : 0u;
+  for (int j = 0; j < NC; ++j) {
+    const bool in = 16u * j < off + m && (uint64_t(s >> 4) + j) * 16 < n;
+    const uint4 v = in ? c[j] : make_uint4(0, 0, 0, 0);
+    raw[4 * j] = v.x;
+    raw[4 * j + 1] = v.y;
+    raw[4 * j + 2] = v.z;
+    raw[4 * j + 3] = v.w;
+  }
+  // shift by sh dwords: by 2, then by 1
+  uint32_t r1[4 * NC], r2[4 * NC];
+#pragma unroll
+  for (int q = 0; q < 4 * NC; ++q) r1[q] = (sh & 2u) ? (q + 2 < 4 * NC ? raw[q + 2] : 0u) : raw[q];
+#pragma unroll
+  for (int q = 0; q < 4 * NC; ++q) r2[q] = (sh & 1u) ? (q + 1 < 4 * NC ? r1[q + 1] : 0u) : r1[q];
 #pragma unroll
   for (int q = 0; q < NB; ++q) {
-    const uint32_t v = __builtin_amdgcn_alignbyte(raw[q + 1], raw[q], off);
+    if (q > NQ) {
+      u.d[q] = 0u;
+      continue;
+    }
+    const uint32_t v = __builtin_amdgcn_alignbyte(q + 1 < 4 * NC ? r2[q + 1] : 0u, r2[q], ob);
     const int lim = int(m) - 4 * q;
     const uint32_t keep = lim >= 4 ? 0xFFFFFFFFu : (lim <= 0 ? 0u : ((1u << (8 * lim)) - 1));
     u.d[q] = v & keep;
