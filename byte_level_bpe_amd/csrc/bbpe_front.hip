@@ -201,15 +201,44 @@ __global__ void __launch_bounds__(1024) k_scan_chars(EncodeArgs a) {
 // SS (a span starts here: segment start, cut or end of a special), SPST (a
 // special starts here) and SPC (byte inside a special).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool special_at(const EncodeArgs &a, uint64_t p, uint64_t seg_end,
-                                           uint32_t &len) {
-  const uint32_t b = a.text[p];
+// Whether a special starts at text position p (inside the lane's word) and
+// ends by seg_end, and its length: the first special whose bytes match.
+// The text comes from the wave's bytes staged in LDS (bytes [lo, lo +
+// STAGE_BYTES)) and the specials' strings from their copy in LDS (sp_lds,
+// when they fit), four bytes at a time; memory is read only past the stage.
+// (Compared byte by byte from memory, a match after two near misses cost a
+// chain of some twenty dependent loads, 20-25 us for a wave.)
+constexpr uint32_t SP_LDS_BYTES = 1024;
+__device__ __forceinline__ uint32_t lds_dword_at(const uint32_t *b32, uint32_t q) {
+  return __builtin_amdgcn_alignbyte(b32[(q >> 2) + 1], b32[q >> 2], q & 3u);
+}
+__device__ __forceinline__ bool special_at_staged(const EncodeArgs &a, const uint4 *bytes, int64_t lo,
+                                                  const uint32_t *sp_lds, bool sp_in_lds, uint64_t p,
+                                                  uint64_t seg_end, uint32_t &len) {
+  const uint32_t *b32 = reinterpret_cast<const uint32_t *>(bytes);
+  const uint32_t b = reinterpret_cast<const uint8_t *>(bytes)[int64_t(p) - lo];
   if (!((a.T.sp_first[b >> 5] >> (b & 31)) & 1)) return false;
   for (uint32_t k = 0; k < a.T.n_sp; ++k) {
     const uint32_t o = a.T.sp_off[k], L = a.T.sp_off[k + 1] - o;
     if (p + L > seg_end) continue;
     bool eq = true;
-    for (uint32_t j = 0; j < L && eq; ++j) eq = a.text[p + j] == a.T.sp_bytes[o + j];
+    for (uint32_t j = 0; j < L && eq; j += 4) {
+      const uint64_t q = p + j;
+      const uint32_t nb = min(4u, L - j);
+      uint32_t tv = 0, sv = 0;
+      if (int64_t(q) + 8 <= lo + int64_t(STAGE_BYTES)) {
+        tv = lds_dword_at(b32, uint32_t(int64_t(q) - lo));
+      } else {
+        for (uint32_t x = 0; x < nb; ++x) tv |= uint32_t(a.text[q + x]) << (8 * x);
+      }
+      if (sp_in_lds) {
+        sv = lds_dword_at(sp_lds, o + j);
+      } else {
+        for (uint32_t x = 0; x < nb; ++x) sv |= uint32_t(a.T.sp_bytes[o + j + x]) << (8 * x);
+      }
+      const uint32_t mask = nb == 4 ? 0xFFFFFFFFu : ((1u << (8 * nb)) - 1u);
+      eq = ((tv ^ sv) & mask) == 0;
+    }
     if (eq) {
       len = L;
       return true;
@@ -272,12 +301,13 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
     }
     tile_base = __shfl(incl_s, 63, 64);
     chg_carry = mx;
-    // the offsets check over every tile; block 0 also writes the status
+    // the offsets check over every tile and the status, by block 0 alone:
+    // with offsets that decrease somewhere the other blocks' results are
+    // never read (every later kernel exits on the status' flag), and every
+    // index they form from the offsets is bounded
     uint32_t bad = 0;
     unsigned long long err = ~0ull, nch = 0;
-    if (t != 0) {
-      fold_strided(a.ws.tile_bad, uint32_t(lane), T, 64u, [&](uint32_t, uint32_t v) { bad |= v; });
-    } else {
+    if (t == 0) {
       for (uint32_t q = uint32_t(lane); q < T; q += 64 * FOLD_BATCH) {  // three loads per tile, batched
         uint32_t bv[FOLD_BATCH], nv[FOLD_BATCH];
         unsigned long long ev[FOLD_BATCH];
@@ -419,11 +449,11 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
       any_allow = a.allow[s] != 0;
     }
   }
+  uint64_t cand = 0;
   if (any_allow && !a.T.sp_overlap) {
-    uint32_t s = seg_at;
     // candidates: bytes equal to a special's first byte (an exact per-byte
     // zero test of the window dwords xor the byte), when there are few
-    uint64_t cand = m.lead;
+    cand = m.lead;
     if (a.T.sp_nfirst) {
       uint64_t fm = 0;
 #pragma unroll
@@ -438,6 +468,21 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
       }
       cand &= fm;
     }
+  }
+  // a wave with candidates stages its bytes and the specials' strings in LDS
+  if (__ballot(cand != 0)) {
+    __shared__ uint4 s_bytes[STAGE_BYTES / 16];
+    __shared__ uint32_t s_sp[SP_LDS_BYTES / 4 + 2];
+    const int64_t lo = base - int64_t(lane) * 64 - 16;
+    stage_window(s_bytes, win, lane);
+    const uint32_t sp_len = a.T.sp_off[a.T.n_sp];
+    const bool sp_in_lds = sp_len <= SP_LDS_BYTES;
+    if (sp_in_lds) {  // (the blob is padded by 16 bytes)
+      const uint32_t *src = reinterpret_cast<const uint32_t *>(a.T.sp_bytes);
+      for (uint32_t k = uint32_t(lane); k < sp_len / 4 + 2; k += 64) s_sp[k] = src[k];
+    }
+    __syncthreads();
+    uint32_t s = seg_at;
     while (cand) {
       const int i = __ffsll(static_cast<unsigned long long>(cand)) - 1;
       cand &= cand - 1;
@@ -445,7 +490,7 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
       while (s + 1 < a.n_seg && a.seg_off[s + 1] <= p) ++s;
       if (!a.allow[s]) continue;
       uint32_t L;
-      if (!special_at(a, p, min(a.seg_off[s + 1], a.n), L)) continue;
+      if (!special_at_staged(a, s_bytes, lo, s_sp, sp_in_lds, p, min(a.seg_off[s + 1], a.n), L)) continue;
       // no chunk cut strictly inside the special
       const int e = i + int(L);  // end, exclusive, in [i+1, i+64]
       uint64_t inner_lo = 0, inner_hi = 0;  // bits i+1 .. e-1 over this and the next word
