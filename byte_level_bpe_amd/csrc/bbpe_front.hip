@@ -208,18 +208,20 @@ __global__ void __launch_bounds__(1024) k_scan_chars(EncodeArgs a) {
 // when they fit), four bytes at a time; memory is read only past the stage.
 // (Compared byte by byte from memory, a match after two near misses cost a
 // chain of some twenty dependent loads, 20-25 us for a wave.)
-constexpr uint32_t SP_LDS_BYTES = 1024;
+constexpr uint32_t SP_LDS_BYTES = 1024, SP_LDS_MAX = 255;  // strings' bytes, specials
 __device__ __forceinline__ uint32_t lds_dword_at(const uint32_t *b32, uint32_t q) {
   return __builtin_amdgcn_alignbyte(b32[(q >> 2) + 1], b32[q >> 2], q & 3u);
 }
 __device__ __forceinline__ bool special_at_staged(const EncodeArgs &a, const uint4 *bytes, int64_t lo,
-                                                  const uint32_t *sp_lds, bool sp_in_lds, uint64_t p,
-                                                  uint64_t seg_end, uint32_t &len) {
+                                                  const uint32_t *sp_lds, const uint32_t *off_lds,
+                                                  bool sp_in_lds, uint64_t p, uint64_t seg_end,
+                                                  uint32_t &len) {
   const uint32_t *b32 = reinterpret_cast<const uint32_t *>(bytes);
   const uint32_t b = reinterpret_cast<const uint8_t *>(bytes)[int64_t(p) - lo];
   if (!((a.T.sp_first[b >> 5] >> (b & 31)) & 1)) return false;
   for (uint32_t k = 0; k < a.T.n_sp; ++k) {
-    const uint32_t o = a.T.sp_off[k], L = a.T.sp_off[k + 1] - o;
+    const uint32_t o = sp_in_lds ? off_lds[k] : a.T.sp_off[k];
+    const uint32_t L = (sp_in_lds ? off_lds[k + 1] : a.T.sp_off[k + 1]) - o;
     if (p + L > seg_end) continue;
     bool eq = true;
     for (uint32_t j = 0; j < L && eq; j += 4) {
@@ -473,24 +475,34 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
   if (__ballot(cand != 0)) {
     __shared__ uint4 s_bytes[STAGE_BYTES / 16];
     __shared__ uint32_t s_sp[SP_LDS_BYTES / 4 + 2];
+    __shared__ uint32_t s_spo[SP_LDS_MAX + 1];
     const int64_t lo = base - int64_t(lane) * 64 - 16;
     stage_window(s_bytes, win, lane);
     const uint32_t sp_len = a.T.sp_off[a.T.n_sp];
-    const bool sp_in_lds = sp_len <= SP_LDS_BYTES;
+    const bool sp_in_lds = sp_len <= SP_LDS_BYTES && a.T.n_sp <= SP_LDS_MAX;
     if (sp_in_lds) {  // (the blob is padded by 16 bytes)
       const uint32_t *src = reinterpret_cast<const uint32_t *>(a.T.sp_bytes);
       for (uint32_t k = uint32_t(lane); k < sp_len / 4 + 2; k += 64) s_sp[k] = src[k];
+      for (uint32_t k = uint32_t(lane); k <= a.T.n_sp; k += 64) s_spo[k] = a.T.sp_off[k];
     }
     __syncthreads();
+    // this lane's segment: its end and allow flag, read again only when a
+    // candidate lies in a later segment
     uint32_t s = seg_at;
+    uint64_t seg_next = a.seg_off[s + 1];
+    bool allow_s = a.allow[s] != 0;
     while (cand) {
       const int i = __ffsll(static_cast<unsigned long long>(cand)) - 1;
       cand &= cand - 1;
       const uint64_t p = uint64_t(base) + uint64_t(i);
-      while (s + 1 < a.n_seg && a.seg_off[s + 1] <= p) ++s;
-      if (!a.allow[s]) continue;
+      while (s + 1 < a.n_seg && seg_next <= p) {
+        ++s;
+        seg_next = a.seg_off[s + 1];
+        allow_s = a.allow[s] != 0;
+      }
+      if (!allow_s) continue;
       uint32_t L;
-      if (!special_at_staged(a, s_bytes, lo, s_sp, sp_in_lds, p, min(a.seg_off[s + 1], a.n), L)) continue;
+      if (!special_at_staged(a, s_bytes, lo, s_sp, s_spo, sp_in_lds, p, min(seg_next, a.n), L)) continue;
       // no chunk cut strictly inside the special
       const int e = i + int(L);  // end, exclusive, in [i+1, i+64]
       uint64_t inner_lo = 0, inner_hi = 0;  // bits i+1 .. e-1 over this and the next word
