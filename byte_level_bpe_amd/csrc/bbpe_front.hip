@@ -214,17 +214,26 @@ __device__ __forceinline__ uint32_t lds_dword_at(const uint32_t *b32, uint32_t q
 }
 __device__ __forceinline__ bool special_at_staged(const EncodeArgs &a, const uint4 *bytes, int64_t lo,
                                                   const uint32_t *sp_lds, const uint32_t *off_lds,
-                                                  bool sp_in_lds, uint64_t p, uint64_t seg_end,
-                                                  uint32_t &len) {
+                                                  const uint32_t *head_lds, bool sp_in_lds, uint64_t p,
+                                                  uint64_t seg_end, uint32_t &len) {
   const uint32_t *b32 = reinterpret_cast<const uint32_t *>(bytes);
   const uint32_t b = reinterpret_cast<const uint8_t *>(bytes)[int64_t(p) - lo];
   if (!((a.T.sp_first[b >> 5] >> (b & 31)) & 1)) return false;
+  // the text's first four bytes at p, read once and held against each
+  // special's first four (head_lds, zero past the special's end) before any
+  // longer compare
+  const bool head = sp_in_lds && int64_t(p) + 8 <= lo + int64_t(STAGE_BYTES);
+  const uint32_t tv0 = head ? lds_dword_at(b32, uint32_t(int64_t(p) - lo)) : 0u;
   for (uint32_t k = 0; k < a.T.n_sp; ++k) {
     const uint32_t o = sp_in_lds ? off_lds[k] : a.T.sp_off[k];
     const uint32_t L = (sp_in_lds ? off_lds[k + 1] : a.T.sp_off[k + 1]) - o;
+    if (head) {
+      const uint32_t hm = L >= 4 ? 0xFFFFFFFFu : ((1u << (8 * L)) - 1u);
+      if ((tv0 ^ head_lds[k]) & hm) continue;
+    }
     if (p + L > seg_end) continue;
     bool eq = true;
-    for (uint32_t j = 0; j < L && eq; j += 4) {
+    for (uint32_t j = head ? 4u : 0u; j < L && eq; j += 4) {
       const uint64_t q = p + j;
       const uint32_t nb = min(4u, L - j);
       uint32_t tv = 0, sv = 0;
@@ -247,6 +256,11 @@ __device__ __forceinline__ bool special_at_staged(const EncodeArgs &a, const uin
     }
   }
   return false;
+}
+
+// bits [x, 64) of a word that holds positions 0..63; x may be out of range
+__device__ __forceinline__ uint64_t from_bit(int x) {
+  return x <= 0 ? ~0ull : (x >= 64 ? 0ull : ~(bit(x) - 1));
 }
 
 __device__ __forceinline__ unsigned long long wave_incl_sum64(unsigned long long v, int lane) {
@@ -476,6 +490,7 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
     __shared__ uint4 s_bytes[STAGE_BYTES / 16];
     __shared__ uint32_t s_sp[SP_LDS_BYTES / 4 + 2];
     __shared__ uint32_t s_spo[SP_LDS_MAX + 1];
+    __shared__ uint32_t s_head[SP_LDS_MAX];
     const int64_t lo = base - int64_t(lane) * 64 - 16;
     stage_window(s_bytes, win, lane);
     const uint32_t sp_len = a.T.sp_off[a.T.n_sp];
@@ -486,6 +501,13 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
       for (uint32_t k = uint32_t(lane); k <= a.T.n_sp; k += 64) s_spo[k] = a.T.sp_off[k];
     }
     __syncthreads();
+    if (sp_in_lds) {  // each special's first four bytes, zero past its end
+      for (uint32_t k = uint32_t(lane); k < a.T.n_sp; k += 64) {
+        const uint32_t L = s_spo[k + 1] - s_spo[k];
+        s_head[k] = lds_dword_at(s_sp, s_spo[k]) & (L >= 4 ? 0xFFFFFFFFu : ((1u << (8 * L)) - 1u));
+      }
+      __syncthreads();
+    }
     // this lane's segment: its end and allow flag, read again only when a
     // candidate lies in a later segment
     uint32_t s = seg_at;
@@ -502,20 +524,15 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
       }
       if (!allow_s) continue;
       uint32_t L;
-      if (!special_at_staged(a, s_bytes, lo, s_sp, s_spo, sp_in_lds, p, min(seg_next, a.n), L)) continue;
-      // no chunk cut strictly inside the special
+      if (!special_at_staged(a, s_bytes, lo, s_sp, s_spo, s_head, sp_in_lds, p, min(seg_next, a.n), L)) continue;
+      // no chunk cut strictly inside the special: bits i+1 .. e-1 over this
+      // word and the next
       const int e = i + int(L);  // end, exclusive, in [i+1, i+64]
-      uint64_t inner_lo = 0, inner_hi = 0;  // bits i+1 .. e-1 over this and the next word
-      for (int j = i + 1; j < e; ++j) {
-        if (j < 64) inner_lo |= bit(j);
-        else inner_hi |= bit(j - 64);
-      }
-      if ((inner_lo & brk) || (inner_hi & brk_next)) continue;
+      const uint64_t lo_in = from_bit(i + 1) & ~from_bit(e), hi_in = ~from_bit(e - 64);
+      if ((lo_in & brk) || (hi_in & brk_next)) continue;
       sp_st |= bit(i);
-      for (int j = i; j < e; ++j) {
-        if (j < 64) sp_in |= bit(j);
-        else sp_in_next |= bit(j - 64);
-      }
+      sp_in |= from_bit(i) & ~from_bit(e);
+      sp_in_next |= hi_in;
       if (e < 64) ss_end |= bit(e);
       else ss_end_next |= bit(e - 64);
       cand &= (e >= 64) ? 0 : ~(bit(e) - 1);  // continue after the special
