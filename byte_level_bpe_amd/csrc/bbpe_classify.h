@@ -3,10 +3,11 @@
 // ASCII bytes are classified four at a time with SWAR range tests on 32-bit
 // words (the high bit of each byte lane carries the result), so the common
 // all-ASCII word needs no per-byte branches.  Bytes >= 0x80 are handled by a
-// slow path that decodes only the multi-byte characters, reading their bytes
-// from the text, validates UTF-8 and looks up the code point's class, eight
-// characters at a time so that their loads overlap; its result is stored
-// per word and read back by later passes over the same text.
+// slow path that decodes only the multi-byte characters: the wave lists the
+// leads of all its words and its 64 lanes share them out, each validating
+// UTF-8 and looking up the code point's class for every 64th lead, eight at
+// a time so that their loads overlap.  The result is stored per word and
+// read back by later passes over the same text.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -81,9 +82,22 @@ __device__ __forceinline__ uint32_t staged_byte(const uint4 *bytes, int64_t lo, 
 
 // The staged bytes and the first stage of the class table for the Basic
 // Multilingual Plane (code points >> 8 below 256), for the multi-byte decoder.
+// The wave's multi-byte characters are decoded by all 64 lanes together:
+// their lead positions go to a list, each lane decodes every 64th entry, and
+// a per-byte code array carries the results back to the words.
+constexpr uint32_t LEAD_LIST = 1024;
 struct SlowStage {
+  uint64_t seg[65];  // segment starts at stage positions (bit q & 63 of seg[q >> 6])
   uint4 bytes[STAGE_BYTES / 16];
+  uint4 code[STAGE_BYTES / 16];  // per stage byte: what the decoder found there
   uint16_t u1[256];
+  union {
+    uint16_t list[LEAD_LIST];  // stage positions of the leads
+    struct {                   // (before that) the segment-start search:
+      uint64_t sm[2][64];      // each lane's window bits
+      uint32_t sh[64];         // segment starts counted from each lane on
+    } sq;
+  };
 };
 
 __device__ __forceinline__ void stage_fill(SlowStage &st, const DevTables &T, const Window &win, int lane) {
@@ -93,81 +107,44 @@ __device__ __forceinline__ void stage_fill(SlowStage &st, const DevTables &T, co
   __syncthreads();
 }
 
-// The multi-byte characters of the word at base: `hi2` marks its bytes >=
-// 0xC0, `non` its bytes >= 0x80.  Leads are decoded eight at a time with all
-// their byte loads, then all their class-table loads, issued together.
-__device__ __forceinline__ void classify_slow(const DevTables &T, const uint8_t *__restrict__ text,
-                                              const Window &win, int64_t base, uint64_t n,
-                                              uint64_t seg_lo, uint64_t seg_hi, uint64_t hi2,
-                                              uint64_t non, uint64_t valid, const SlowStage &st,
-                                              int64_t lo, SlowMasks &r) {
-  r = SlowMasks{0, 0, 0, 0, 0, 0, 0, 0, 0, 64};
-  uint64_t covered = 0;
-  uint32_t err = 64;
-  // a character that began up to three bytes before the word
-  if (!(hi2 & 1) && (non & 1)) {
-    int kf = 0;
-    if ((win.at(-1) & 0xC0u) != 0x80u) kf = 1;
-    else if ((win.at(-2) & 0xC0u) != 0x80u) kf = 2;
-    else if ((win.at(-3) & 0xC0u) != 0x80u) kf = 3;
-    if (kf > 0 && base - kf >= 0) {
-      // its bytes from the window (fixed indices, selected by kf)
-      uint32_t b[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = kf == 1 ? win.at(j - 1) : (kf == 2 ? win.at(j - 2) : win.at(j - 3));
-      const int len = utf8_len(b[0]);
-      bool ok = len >= 2 && uint64_t(base - kf) + uint64_t(len) <= n;
-      uint32_t cp = b[0] & (0x7Fu >> len);
-#pragma unroll
-      for (int j = 1; j < 4; ++j) {
-        const bool in = j < len;
-        ok = ok && (!in || (((b[j] & 0xC0u) == 0x80u) && !seg_start_at(seg_lo, seg_hi, j - kf)));
-        cp = in ? ((cp << 6) | (b[j] & 0x3Fu)) : cp;
-      }
-      if (len == 3 && cp < 0x800) ok = false;
-      if (len == 4 && (cp < 0x10000 || cp > 0x10FFFF)) ok = false;
-      if (cp >= 0xD800 && cp <= 0xDFFF) ok = false;
-      if (ok && len > kf) {
-        const uint32_t blk = cp <= 0xFFFFu ? uint32_t(st.u1[cp >> 8]) : uint32_t(T.uni1[cp >> 8]);
-        const uint64_t bits = bit_range(0, len - kf);
-        covered |= bits;
-        add_class(r, T.uni2[blk * 256u + (cp & 0xFFu)], bits);
-        if (cp == 0x17F) r.ls1 |= 1;  // its second byte
-      }
-    }
-  }
-  // invalid lead bytes (C0, C1, F5..FF) are >= 0xC0 too and fail to decode
-  uint64_t leads = hi2 & valid;
-  uint64_t lead = 0;
-  // segment starts at word positions 0..63, and 64..66 in bits 0..2
-  const uint64_t segw = (seg_lo >> 8) | (seg_hi << 56);
-  const uint32_t segx = uint32_t(seg_hi >> 8) & 7u;
-  // class code planes of the batch loop's characters (bit b of the code)
-  uint64_t pl0 = 0, pl1 = 0, pl2 = 0;
-  const uint32_t *b32 = reinterpret_cast<const uint32_t *>(st.bytes);
-  const uint32_t a0 = uint32_t(base - lo);  // the word's first byte in the stage
-  while (leads) {
+// Per-byte codes of the wave decoder: the class code of a valid character
+// on each of its bytes (bits 0..2), a continuation byte it claims (3), a
+// lead (4), a lead that does not start a valid character (5), the lead and
+// the second byte of U+017F (6, 7).
+constexpr uint32_t CODE_CONT = 0x08, CODE_LEAD = 0x10, CODE_BAD = 0x20, CODE_LS0 = 0x40, CODE_LS1 = 0x80;
+
+// bits [i, i + len) of a 128-bit mask held as two words, i < 64, len <= 4
+__device__ __forceinline__ bool any_in128(uint64_t w0, uint64_t w1, int i, int len) {
+  const uint64_t m0 = bit_range(i, len);
+  const int over = i + len - 64;
+  const uint64_t m1 = over > 0 ? (bit(over) - 1) : 0;
+  return ((w0 & m0) | (w1 & m1)) != 0;
+}
+
+// Decodes list entries [0, count) of the stage (every 64th from this lane,
+// eight at a time: their byte reads, then their class-table reads, issued
+// together) and writes their codes.
+__device__ __forceinline__ void decode_listed(const DevTables &T, const SlowStage &st, const uint32_t *b32,
+                                              uint8_t *code, uint32_t count, int lane) {
+  for (uint32_t g0 = 0; g0 < count; g0 += 64u * 8u) {
     constexpr int K = 8;
-    int ii[K];
-    uint32_t v[K];  // the four bytes from each lead, little endian
+    uint32_t q[K], v[K], cp[K], blk[K], cls[K];
+    int len[K];
+    bool ok[K], has[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      ii[k] = __ffsll(static_cast<unsigned long long>(leads)) - 1;  // -1 once none are left
-      leads &= leads - 1;
-      const uint32_t ad = uint32_t(int(a0) + ii[k]);
-      v[k] = __builtin_amdgcn_alignbyte(b32[(ad >> 2) + 1], b32[ad >> 2], ad & 3u);
+      const uint32_t g = g0 + uint32_t(lane) + 64u * uint32_t(k);
+      has[k] = g < count;
+      q[k] = st.list[has[k] ? g : 0u];
     }
-    uint32_t cp[K], blk[K];
-    int len[K];
-    bool ok[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = __builtin_amdgcn_alignbyte(b32[(q[k] >> 2) + 1], b32[q[k] >> 2], q[k] & 3u);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const uint32_t w = v[k], b0 = w & 0xFFu;
       const int Ln = b0 < 0xC2u ? 0 : (b0 < 0xE0u ? 2 : (b0 < 0xF0u ? 3 : (b0 < 0xF5u ? 4 : 0)));
-      // continuation bytes 1 .. Ln-1 of the form 10xxxxxx
       const uint32_t cm = Ln == 2 ? 0xC000u : (Ln == 3 ? 0xC0C000u : 0xC0C0C000u);
-      bool good = ii[k] >= 0 && Ln >= 2 && (w & cm) == (cm & 0x80808080u);
+      bool good = has[k] && Ln >= 2 && (w & cm) == (cm & 0x80808080u);
       const uint32_t f1 = (w >> 8) & 0x3Fu, f2 = (w >> 16) & 0x3Fu, f3 = (w >> 24) & 0x3Fu;
       const uint32_t c = Ln == 2 ? (((b0 & 0x1Fu) << 6) | f1)
                        : Ln == 3 ? (((b0 & 0x0Fu) << 12) | (f1 << 6) | f2)
@@ -175,19 +152,17 @@ __device__ __forceinline__ void classify_slow(const DevTables &T, const uint8_t 
       if (Ln == 3 && c < 0x800) good = false;
       if (Ln == 4 && (c < 0x10000 || c > 0x10FFFF)) good = false;
       if (c >= 0xD800 && c <= 0xDFFF) good = false;
-      // no segment starts at a continuation byte
-      const int i = ii[k] < 0 ? 0 : ii[k];
-      const uint64_t cont = bit_range(i + 1, Ln - 1);
-      const int ext = i + Ln - 64;  // continuation bytes past the word
-      const bool segbad = (segw & cont) != 0 || (ext > 0 && (segx & ((1u << ext) - 1u)) != 0);
+      // no segment starts at a continuation byte (q + Ln - 1 < 64 * 65)
+      if (good) {
+        const uint32_t e = q[k] >> 6;
+        const int b = int(q[k] & 63u);
+        const uint64_t s1 = (b + Ln > 64) ? st.seg[e + 1] : 0ull;
+        good = !any_in128(st.seg[e], s1, b + 1, Ln - 1);
+      }
       cp[k] = c;
       len[k] = Ln;
-      ok[k] = good && !segbad;
+      ok[k] = good;
     }
-    // second-stage loads issued unconditionally (index 0 when unused: a load
-    // under a condition is waited for on its own); the first stage is read
-    // from LDS, and from memory only for code points beyond U+FFFF
-    uint32_t cls[K];
     bool astral = false;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -206,38 +181,102 @@ __device__ __forceinline__ void classify_slow(const DevTables &T, const uint8_t 
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int i = ii[k];
-      if (i < 0) continue;
-      lead |= bit(i);
+      if (!has[k]) continue;
       if (!ok[k]) {
-        err = min(err, uint32_t(i));
+        code[q[k]] = uint8_t(CODE_LEAD | CODE_BAD);
         continue;
       }
-      const uint64_t bits = bit_range(i, len[k]);
-      covered |= bits & ~bit(i);
-      pl0 |= (cls[k] & 1u) ? bits : 0;
-      pl1 |= (cls[k] & 2u) ? bits : 0;
-      pl2 |= (cls[k] & 4u) ? bits : 0;
-      if (cp[k] == 0x17F) {
-        r.ls0 |= bit(i);
-        if (i + 1 < 64) r.ls1 |= bit(i + 1);
-      }
+      const bool ls = cp[k] == 0x17F;
+      code[q[k]] = uint8_t(cls[k] | CODE_LEAD | (ls ? CODE_LS0 : 0u));
+      code[q[k] + 1] = uint8_t(cls[k] | CODE_CONT | (ls ? CODE_LS1 : 0u));
+      if (len[k] > 2) code[q[k] + 2] = uint8_t(cls[k] | CODE_CONT);
+      if (len[k] > 3) code[q[k] + 3] = uint8_t(cls[k] | CODE_CONT);
     }
   }
-  // planes to class masks (class codes 1..6; 0, "other", sets no plane)
-  r.LU |= pl0 & ~pl1 & ~pl2;
-  r.LL |= ~pl0 & pl1 & ~pl2;
-  r.LB |= pl0 & pl1 & ~pl2;
-  r.N |= ~pl0 & ~pl1 & pl2;
-  r.WS |= pl0 & ~pl1 & pl2;
-  r.M |= ~pl0 & pl1 & pl2;
-  // continuation bytes that no valid character claims are errors; they
-  // count as characters of their own (class "other")
-  const uint64_t cont = non & ~hi2;
-  const uint64_t stray = cont & ~covered;
-  if (stray) err = min(err, uint32_t(__ffsll(static_cast<unsigned long long>(stray)) - 1));
-  r.lead = lead | stray;
-  r.err = err;
+}
+
+// The multi-byte part of every lane's word, the wave's characters decoded by
+// all lanes together.  Every lane of the wave calls this (lane = threadIdx.x,
+// consecutive lanes at consecutive words, lo = stage start); r is set for
+// lanes whose word holds a byte >= 0x80.
+__device__ __forceinline__ void classify_slow_wave(const DevTables &T, const uint8_t *__restrict__ text,
+                                                   const Window &win, int64_t base, uint64_t n,
+                                                   uint64_t seg_lo, uint64_t seg_hi, uint64_t hi2,
+                                                   uint64_t non, uint64_t valid, SlowStage &st,
+                                                   int64_t lo, int lane, SlowMasks &r) {
+  uint64_t leads = hi2 & valid;
+  // a character that began up to three bytes before lane 0's word (later
+  // lanes' such characters start in the previous lane's word)
+  int pre = -1;
+  if (lane == 0 && !(hi2 & 1) && (non & 1)) {
+    int kf = 0;
+    if ((win.at(-1) & 0xC0u) != 0x80u) kf = 1;
+    else if ((win.at(-2) & 0xC0u) != 0x80u) kf = 2;
+    else if ((win.at(-3) & 0xC0u) != 0x80u) kf = 3;
+    if (kf > 0 && base - kf >= 0 && win.at(-kf) >= 0xC0u) pre = 16 - kf;
+  }
+  const uint32_t cnt = uint32_t(__popcll(leads)) + (pre >= 0 ? 1u : 0u);
+  const uint32_t incl = wave_incl_sum(cnt, lane);
+  const uint32_t total = __shfl(incl, 63, 64);
+  for (uint32_t j = uint32_t(lane); j < STAGE_BYTES / 16; j += 64) st.code[j] = uint4{0, 0, 0, 0};
+  // stage positions 64(l+1) .. 64(l+2)-1 are window indices 56..119 of lane l
+  st.seg[lane + 1] = (seg_lo >> 56) | (seg_hi << 8);
+  if (lane == 0) st.seg[0] = seg_lo << 8;
+  __syncthreads();
+  const uint32_t *b32 = reinterpret_cast<const uint32_t *>(st.bytes);
+  uint8_t *code = reinterpret_cast<uint8_t *>(st.code);
+  // the list in pieces of LEAD_LIST entries
+  for (uint32_t c0 = 0; c0 < total; c0 += LEAD_LIST) {
+    const uint32_t c1 = min(total, c0 + LEAD_LIST);
+    {
+      uint32_t k = incl - cnt;
+      const uint32_t w0 = 16u + 64u * uint32_t(lane);  // the word's first byte in the stage
+      if (pre >= 0) {
+        if (k >= c0 && k < c1) st.list[k - c0] = uint16_t(pre);
+        ++k;
+      }
+      for (uint64_t x = leads; x && k < c1; x &= x - 1, ++k)
+        if (k >= c0) st.list[k - c0] = uint16_t(w0 + uint32_t(__ffsll(static_cast<unsigned long long>(x)) - 1));
+    }
+    __syncthreads();
+    decode_listed(T, st, b32, code, c1 - c0, lane);
+    __syncthreads();
+  }
+  if (!non) return;
+  // this word's 64 codes, one bit per byte and field
+  uint64_t pl0 = 0, pl1 = 0, pl2 = 0, cov = 0, ld = 0, bad = 0, l0 = 0, l1 = 0;
+  const uint4 *cw = st.code + 1 + 4 * lane;
+#pragma unroll
+  for (int qd = 0; qd < 4; ++qd) {
+    const uint4 c4 = cw[qd];
+    const uint32_t f4[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t f = f4[j];
+      const int sh = 4 * (4 * qd + j);
+      pl0 |= gather4((f << 7) & 0x80808080u) << sh;
+      pl1 |= gather4((f << 6) & 0x80808080u) << sh;
+      pl2 |= gather4((f << 5) & 0x80808080u) << sh;
+      cov |= gather4((f << 4) & 0x80808080u) << sh;
+      ld |= gather4((f << 3) & 0x80808080u) << sh;
+      bad |= gather4((f << 2) & 0x80808080u) << sh;
+      l0 |= gather4((f << 1) & 0x80808080u) << sh;
+      l1 |= gather4(f & 0x80808080u) << sh;
+    }
+  }
+  r = SlowMasks{0, 0, 0, 0, 0, 0, 0, 0, 0, 64};
+  r.LU = pl0 & ~pl1 & ~pl2;
+  r.LL = ~pl0 & pl1 & ~pl2;
+  r.LB = pl0 & pl1 & ~pl2;
+  r.N = ~pl0 & ~pl1 & pl2;
+  r.WS = pl0 & ~pl1 & pl2;
+  r.M = ~pl0 & pl1 & pl2;
+  const uint64_t stray = non & ~hi2 & ~cov;
+  const uint64_t errs = (bad & valid) | stray;
+  r.err = errs ? uint64_t(__ffsll(static_cast<unsigned long long>(errs)) - 1) : 64u;
+  r.lead = ld | stray;
+  r.ls0 = l0;
+  r.ls1 = l1;
 }
 
 // Classify the 64 bytes of the word at text offset base (window = bytes
@@ -251,7 +290,7 @@ __device__ __forceinline__ void classify_word(const DevTables &T, const uint8_t 
                                               const Window &win, int64_t base, uint64_t n,
                                               uint64_t seg_lo, uint64_t seg_hi, WordMasks &m,
                                               const uint64_t *slow_in, uint64_t *slow_out,
-                                              const SlowStage *st, int64_t lo) {
+                                              SlowStage *st, int64_t lo) {
   m.valid = 0;
   if (base >= 0 && uint64_t(base) < n) {
     const uint64_t left = n - uint64_t(base);
@@ -261,7 +300,9 @@ __device__ __forceinline__ void classify_word(const DevTables &T, const uint8_t 
   m.c_sdmt = m.c_l = m.c_v = m.c_e = m.c_r = m.c_ls0 = m.c_ls1 = 0;
   m.err = 64;
   m.na = 0;
-  if (!m.valid) return;
+  // (the decoding kernel goes on with every lane: the wave decodes together;
+  // a word outside the text has a zero window and no valid byte)
+  if (!COMPUTE && !m.valid) return;
 
   uint64_t asc = 0, hi2 = 0;  // ASCII bytes; bytes >= 0xC0 (lead bytes of multi-byte chars)
   uint32_t ap_near = 0;
@@ -308,15 +349,14 @@ __device__ __forceinline__ void classify_word(const DevTables &T, const uint8_t 
 
   const uint64_t non = ~asc & m.valid;
   m.na = non;
-  if (non) {
-    SlowMasks r;
-    if (!COMPUTE) {
-      const ulonglong2 *q = reinterpret_cast<const ulonglong2 *>(slow_in);
-      const ulonglong2 v0 = q[0], v1 = q[1], v2 = q[2], v3 = q[3], v4 = q[4];
-      r = SlowMasks{v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y, v4.x, v4.y};
-    } else {
-      classify_slow(T, text, win, base, n, seg_lo, seg_hi, hi2, non, m.valid, *st, lo, r);
-      if (slow_out) {
+  SlowMasks r;
+  bool have = false;
+  if (COMPUTE) {
+    if (__ballot(non != 0)) {  // wave-uniform: every lane takes part
+      classify_slow_wave(T, text, win, base, n, seg_lo, seg_hi, hi2, non, m.valid, *st, lo,
+                         int(threadIdx.x), r);
+      have = non != 0;
+      if (have && slow_out) {
         ulonglong2 *q = reinterpret_cast<ulonglong2 *>(slow_out);
         q[0] = ulonglong2{r.LU, r.LL};
         q[1] = ulonglong2{r.LB, r.N};
@@ -325,6 +365,13 @@ __device__ __forceinline__ void classify_word(const DevTables &T, const uint8_t 
         q[4] = ulonglong2{r.ls1, r.err};
       }
     }
+  } else if (non) {
+    const ulonglong2 *q = reinterpret_cast<const ulonglong2 *>(slow_in);
+    const ulonglong2 v0 = q[0], v1 = q[1], v2 = q[2], v3 = q[3], v4 = q[4];
+    r = SlowMasks{v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y, v4.x, v4.y};
+    have = true;
+  }
+  if (have) {
     m.LU |= r.LU;
     m.LL |= r.LL;
     m.LB |= r.LB;
