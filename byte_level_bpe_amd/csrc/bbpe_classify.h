@@ -80,17 +80,18 @@ __device__ __forceinline__ uint32_t staged_byte(const uint4 *bytes, int64_t lo, 
   return reinterpret_cast<const uint8_t *>(bytes)[p - lo];
 }
 
-// The staged bytes and the first stage of the class table for the Basic
-// Multilingual Plane (code points >> 8 below 256), for the multi-byte decoder.
 // The wave's multi-byte characters are decoded by all 64 lanes together:
 // their lead positions go to a list, each lane decodes every 64th entry, and
-// a per-byte code array carries the results back to the words.
+// a per-byte code array carries the results back to the words.  The stage
+// also holds the wave's bytes and the first class-table stage for the Basic
+// Multilingual Plane (code points >> 8 below 256).
 constexpr uint32_t LEAD_LIST = 1024;
 struct SlowStage {
   uint64_t seg[65];  // segment starts at stage positions (bit q & 63 of seg[q >> 6])
   uint4 bytes[STAGE_BYTES / 16];
   uint4 code[STAGE_BYTES / 16];  // per stage byte: what the decoder found there
   uint16_t u1[256];
+  uint32_t ls;                   // some character decoded is U+017F
   union {
     uint16_t list[LEAD_LIST];  // stage positions of the leads
     struct {                   // (before that) the segment-start search:
@@ -100,18 +101,10 @@ struct SlowStage {
   };
 };
 
-__device__ __forceinline__ void stage_fill(SlowStage &st, const DevTables &T, const Window &win, int lane) {
-  const uint2 u = reinterpret_cast<const uint2 *>(T.uni1)[lane];
-  reinterpret_cast<uint2 *>(st.u1)[lane] = u;
-  stage_window(st.bytes, win, lane);
-  __syncthreads();
-}
-
-// Per-byte codes of the wave decoder: the class code of a valid character
-// on each of its bytes (bits 0..2), a continuation byte it claims (3), a
-// lead (4), a lead that does not start a valid character (5), the lead and
-// the second byte of U+017F (6, 7).
-constexpr uint32_t CODE_CONT = 0x08, CODE_LEAD = 0x10, CODE_BAD = 0x20, CODE_LS0 = 0x40, CODE_LS1 = 0x80;
+// Per-byte codes of the wave decoder: on every byte of a valid character its
+// class code plus one (bits 0..2; 0 where no valid character claims the
+// byte), and on the lead and the second byte of U+017F bits 3 and 4.
+constexpr uint32_t CODE_LS0 = 0x08, CODE_LS1 = 0x10;
 
 // bits [i, i + len) of a 128-bit mask held as two words, i < 64, len <= 4
 __device__ __forceinline__ bool any_in128(uint64_t w0, uint64_t w1, int i, int len) {
@@ -123,9 +116,12 @@ __device__ __forceinline__ bool any_in128(uint64_t w0, uint64_t w1, int i, int l
 
 // Decodes list entries [0, count) of the stage (every 64th from this lane,
 // eight at a time: their byte reads, then their class-table reads, issued
-// together) and writes their codes.
-__device__ __forceinline__ void decode_listed(const DevTables &T, const SlowStage &st, const uint32_t *b32,
-                                              uint8_t *code, uint32_t count, int lane) {
+// together) and writes their codes.  segs: the stage holds a segment start
+// (none may fall on a continuation byte).
+__device__ __forceinline__ void decode_listed(const DevTables &T, SlowStage &st, uint32_t count, int lane,
+                                              bool segs) {
+  const uint32_t *b32 = reinterpret_cast<const uint32_t *>(st.bytes);
+  uint8_t *code = reinterpret_cast<uint8_t *>(st.code);
   for (uint32_t g0 = 0; g0 < count; g0 += 64u * 8u) {
     constexpr int K = 8;
     uint32_t q[K], v[K], cp[K], blk[K], cls[K];
@@ -153,7 +149,7 @@ __device__ __forceinline__ void decode_listed(const DevTables &T, const SlowStag
       if (Ln == 4 && (c < 0x10000 || c > 0x10FFFF)) good = false;
       if (c >= 0xD800 && c <= 0xDFFF) good = false;
       // no segment starts at a continuation byte (q + Ln - 1 < 64 * 65)
-      if (good) {
+      if (segs && good) {
         const uint32_t e = q[k] >> 6;
         const int b = int(q[k] & 63u);
         const uint64_t s1 = (b + Ln > 64) ? st.seg[e + 1] : 0ull;
@@ -175,36 +171,33 @@ __device__ __forceinline__ void decode_listed(const DevTables &T, const SlowStag
         if (ok[k] && cp[k] > 0xFFFFu) blk[k] = T.uni1[cp[k] >> 8];
     }
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const uint32_t c = T.uni2[ok[k] ? blk[k] * 256u + (cp[k] & 0xFFu) : 0u];
-      cls[k] = ok[k] ? c : 0u;
-    }
+    for (int k = 0; k < K; ++k) cls[k] = T.uni2[ok[k] ? blk[k] * 256u + (cp[k] & 0xFFu) : 0u];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      if (!has[k]) continue;
-      if (!ok[k]) {
-        code[q[k]] = uint8_t(CODE_LEAD | CODE_BAD);
-        continue;
-      }
+      if (!ok[k]) continue;  // an invalid lead keeps code 0
+      const uint32_t cv = (cls[k] & 7u) + 1u;
       const bool ls = cp[k] == 0x17F;
-      code[q[k]] = uint8_t(cls[k] | CODE_LEAD | (ls ? CODE_LS0 : 0u));
-      code[q[k] + 1] = uint8_t(cls[k] | CODE_CONT | (ls ? CODE_LS1 : 0u));
-      if (len[k] > 2) code[q[k] + 2] = uint8_t(cls[k] | CODE_CONT);
-      if (len[k] > 3) code[q[k] + 3] = uint8_t(cls[k] | CODE_CONT);
+      code[q[k]] = uint8_t(cv | (ls ? CODE_LS0 : 0u));
+      code[q[k] + 1] = uint8_t(cv | (ls ? CODE_LS1 : 0u));
+      if (len[k] > 2) code[q[k] + 2] = uint8_t(cv);
+      if (len[k] > 3) code[q[k] + 3] = uint8_t(cv);
+      if (ls) st.ls = 1;
     }
   }
 }
 
 // The multi-byte part of every lane's word, the wave's characters decoded by
 // all lanes together.  Every lane of the wave calls this (lane = threadIdx.x,
-// consecutive lanes at consecutive words, lo = stage start); r is set for
-// lanes whose word holds a byte >= 0x80.
-__device__ __forceinline__ void classify_slow_wave(const DevTables &T, const uint8_t *__restrict__ text,
-                                                   const Window &win, int64_t base, uint64_t n,
+// consecutive lanes at consecutive words); r is set for lanes whose word
+// holds a byte >= 0x80.  Stages the wave's bytes and the first class-table
+// stage in st.
+__device__ __forceinline__ void classify_slow_wave(const DevTables &T, const Window &win, int64_t base,
                                                    uint64_t seg_lo, uint64_t seg_hi, uint64_t hi2,
-                                                   uint64_t non, uint64_t valid, SlowStage &st,
-                                                   int64_t lo, int lane, SlowMasks &r) {
-  uint64_t leads = hi2 & valid;
+                                                   uint64_t non, uint64_t valid, SlowStage &st, int lane,
+                                                   SlowMasks &r) {
+  const uint2 u1v = reinterpret_cast<const uint2 *>(T.uni1)[lane];  // stored once it is needed
+  stage_window(st.bytes, win, lane);
+  const uint64_t leads = hi2 & valid;
   // a character that began up to three bytes before lane 0's word (later
   // lanes' such characters start in the previous lane's word)
   int pre = -1;
@@ -220,61 +213,96 @@ __device__ __forceinline__ void classify_slow_wave(const DevTables &T, const uin
   const uint32_t total = __shfl(incl, 63, 64);
   for (uint32_t j = uint32_t(lane); j < STAGE_BYTES / 16; j += 64) st.code[j] = uint4{0, 0, 0, 0};
   // stage positions 64(l+1) .. 64(l+2)-1 are window indices 56..119 of lane l
-  st.seg[lane + 1] = (seg_lo >> 56) | (seg_hi << 8);
-  if (lane == 0) st.seg[0] = seg_lo << 8;
+  const uint64_t sg = (seg_lo >> 56) | (seg_hi << 8);
+  st.seg[lane + 1] = sg;
+  const uint64_t sg0 = lane == 0 ? (seg_lo << 8) : 0ull;
+  if (lane == 0) {
+    st.seg[0] = sg0;
+    st.ls = 0;
+  }
+  const bool segs = __ballot((sg | sg0) != 0) != 0;
   __syncthreads();
-  const uint32_t *b32 = reinterpret_cast<const uint32_t *>(st.bytes);
-  uint8_t *code = reinterpret_cast<uint8_t *>(st.code);
-  // the list in pieces of LEAD_LIST entries
-  for (uint32_t c0 = 0; c0 < total; c0 += LEAD_LIST) {
-    const uint32_t c1 = min(total, c0 + LEAD_LIST);
-    {
+  const uint32_t w0 = 16u + 64u * uint32_t(lane);  // the word's first byte in the stage
+  if (total <= LEAD_LIST) {
+    // the word's leads from both halves at once (the list's order is free)
+    uint32_t k = incl - cnt;
+    if (pre >= 0) st.list[k++] = uint16_t(pre);
+    uint32_t xl = uint32_t(leads), xh = uint32_t(leads >> 32);
+    uint32_t kh = k + uint32_t(__popc(xl));
+    while (xl | xh) {
+      if (xl) {
+        st.list[k++] = uint16_t(w0 + uint32_t(__ffs(xl) - 1));
+        xl &= xl - 1;
+      }
+      if (xh) {
+        st.list[kh++] = uint16_t(w0 + 32u + uint32_t(__ffs(xh) - 1));
+        xh &= xh - 1;
+      }
+    }
+    reinterpret_cast<uint2 *>(st.u1)[lane] = u1v;
+    __syncthreads();
+    decode_listed(T, st, total, lane, segs);
+    __syncthreads();
+  } else {
+    // in pieces of LEAD_LIST entries
+    for (uint32_t c0 = 0; c0 < total; c0 += LEAD_LIST) {
+      const uint32_t c1 = min(total, c0 + LEAD_LIST);
       uint32_t k = incl - cnt;
-      const uint32_t w0 = 16u + 64u * uint32_t(lane);  // the word's first byte in the stage
       if (pre >= 0) {
         if (k >= c0 && k < c1) st.list[k - c0] = uint16_t(pre);
         ++k;
       }
       for (uint64_t x = leads; x && k < c1; x &= x - 1, ++k)
         if (k >= c0) st.list[k - c0] = uint16_t(w0 + uint32_t(__ffsll(static_cast<unsigned long long>(x)) - 1));
+      if (c0 == 0) reinterpret_cast<uint2 *>(st.u1)[lane] = u1v;
+      __syncthreads();
+      decode_listed(T, st, c1 - c0, lane, segs);
+      __syncthreads();
     }
-    __syncthreads();
-    decode_listed(T, st, b32, code, c1 - c0, lane);
-    __syncthreads();
   }
   if (!non) return;
   // this word's 64 codes, one bit per byte and field
-  uint64_t pl0 = 0, pl1 = 0, pl2 = 0, cov = 0, ld = 0, bad = 0, l0 = 0, l1 = 0;
   const uint4 *cw = st.code + 1 + 4 * lane;
+  uint64_t p0 = 0, p1 = 0, p2 = 0;
 #pragma unroll
   for (int qd = 0; qd < 4; ++qd) {
     const uint4 c4 = cw[qd];
     const uint32_t f4[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t f = f4[j];
       const int sh = 4 * (4 * qd + j);
-      pl0 |= gather4((f << 7) & 0x80808080u) << sh;
-      pl1 |= gather4((f << 6) & 0x80808080u) << sh;
-      pl2 |= gather4((f << 5) & 0x80808080u) << sh;
-      cov |= gather4((f << 4) & 0x80808080u) << sh;
-      ld |= gather4((f << 3) & 0x80808080u) << sh;
-      bad |= gather4((f << 2) & 0x80808080u) << sh;
-      l0 |= gather4((f << 1) & 0x80808080u) << sh;
-      l1 |= gather4(f & 0x80808080u) << sh;
+      p0 |= gather4((f4[j] << 7) & 0x80808080u) << sh;
+      p1 |= gather4((f4[j] << 6) & 0x80808080u) << sh;
+      p2 |= gather4((f4[j] << 5) & 0x80808080u) << sh;
     }
   }
+  uint64_t l0 = 0, l1 = 0;
+  if (st.ls) {  // (wave-uniform)
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const uint4 c4 = cw[qd];
+      const uint32_t f4[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int sh = 4 * (4 * qd + j);
+        l0 |= gather4((f4[j] << 4) & 0x80808080u) << sh;
+        l1 |= gather4((f4[j] << 3) & 0x80808080u) << sh;
+      }
+    }
+  }
+  // class code plus one: 1 other, 2 Lu/Lt, 3 Ll, 4 Lm/Lo, 5 N, 6 White_Space, 7 M
   r = SlowMasks{0, 0, 0, 0, 0, 0, 0, 0, 0, 64};
-  r.LU = pl0 & ~pl1 & ~pl2;
-  r.LL = ~pl0 & pl1 & ~pl2;
-  r.LB = pl0 & pl1 & ~pl2;
-  r.N = ~pl0 & ~pl1 & pl2;
-  r.WS = pl0 & ~pl1 & pl2;
-  r.M = ~pl0 & pl1 & pl2;
-  const uint64_t stray = non & ~hi2 & ~cov;
-  const uint64_t errs = (bad & valid) | stray;
+  r.LU = ~p0 & p1 & ~p2;
+  r.LL = p0 & p1 & ~p2;
+  r.LB = ~p0 & ~p1 & p2;
+  r.N = p0 & ~p1 & p2;
+  r.WS = ~p0 & p1 & p2;
+  r.M = p0 & p1 & p2;
+  const uint64_t claimed = p0 | p1 | p2;
+  const uint64_t stray = non & ~hi2 & ~claimed;  // continuation bytes no character claims
+  const uint64_t errs = (leads & ~claimed) | stray;
   r.err = errs ? uint64_t(__ffsll(static_cast<unsigned long long>(errs)) - 1) : 64u;
-  r.lead = ld | stray;
+  r.lead = leads | stray;
   r.ls0 = l0;
   r.ls1 = l1;
 }
@@ -290,7 +318,7 @@ __device__ __forceinline__ void classify_word(const DevTables &T, const uint8_t 
                                               const Window &win, int64_t base, uint64_t n,
                                               uint64_t seg_lo, uint64_t seg_hi, WordMasks &m,
                                               const uint64_t *slow_in, uint64_t *slow_out,
-                                              SlowStage *st, int64_t lo) {
+                                              SlowStage *st) {
   m.valid = 0;
   if (base >= 0 && uint64_t(base) < n) {
     const uint64_t left = n - uint64_t(base);
@@ -353,8 +381,7 @@ __device__ __forceinline__ void classify_word(const DevTables &T, const uint8_t 
   bool have = false;
   if (COMPUTE) {
     if (__ballot(non != 0)) {  // wave-uniform: every lane takes part
-      classify_slow_wave(T, text, win, base, n, seg_lo, seg_hi, hi2, non, m.valid, *st, lo,
-                         int(threadIdx.x), r);
+      classify_slow_wave(T, win, base, seg_lo, seg_hi, hi2, non, m.valid, *st, int(threadIdx.x), r);
       have = non != 0;
       if (have && slow_out) {
         ulonglong2 *q = reinterpret_cast<ulonglong2 *>(slow_out);

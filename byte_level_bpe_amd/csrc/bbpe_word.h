@@ -89,17 +89,13 @@ __device__ __forceinline__ void word_setup(const EncodeArgs &a, int64_t w, bool 
   const int64_t base = w * 64;
   const bool in = w >= 0 && w < int64_t(a.n_words);
   load_window(a.text, a.n, base, win);
-  // the first kernel stages the wave's bytes in LDS for the multi-byte
-  // decoder (one wave per workgroup, lane = threadIdx.x at consecutive words)
+  // the first kernel's wave works together (one wave per workgroup, lane =
+  // threadIdx.x at consecutive words) in LDS: the segment-start search and
+  // the multi-byte decoder
   SlowStage *st = nullptr;
-  int64_t lo = 0;
   if (FIRST) {
     __shared__ SlowStage stage;
-    stage_fill(stage, a.T, win, int(threadIdx.x));
     st = &stage;
-    lo = base - int64_t(threadIdx.x) * 64 - 16;
-  }
-  if (FIRST) {
     wave_segment_marks(a.seg_off, a.n_seg, base, int(threadIdx.x), *st, seg_lo, seg_hi, seg_at);
     if (a.n_seg > 1 && owned) {
       reinterpret_cast<ulonglong2 *>(a.ws.wseg)[w] = ulonglong2{seg_lo, seg_hi};
@@ -118,7 +114,7 @@ __device__ __forceinline__ void word_setup(const EncodeArgs &a, int64_t w, bool 
   // words that have one)
   uint64_t *rec = in ? a.ws.wslow + uint64_t(w) * SLOW_WORDS : nullptr;
   classify_word<FIRST>(a.T, a.text, win, base, a.n, seg_lo, seg_hi, m, FIRST ? nullptr : rec,
-                       (FIRST && owned) ? rec : nullptr, st, lo);
+                       (FIRST && owned) ? rec : nullptr, st);
 }
 
 }  // namespace bbpe
