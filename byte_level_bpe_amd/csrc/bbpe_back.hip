@@ -55,7 +55,6 @@ __global__ void __launch_bounds__(1024) k_scan_tiles_np(EncodeArgs a) {
 
 // unit start offsets, in text order
 __global__ void __launch_bounds__(64) k_pieces(EncodeArgs a) {
-  if (a.ws.status->pad2) return;
   const int lane = threadIdx.x;
   const uint32_t t = blockIdx.x;
   const int64_t w = int64_t(t) * TILE_WORDS + lane - 1;
@@ -69,6 +68,7 @@ __global__ void __launch_bounds__(64) k_pieces(EncodeArgs a) {
     uint32_t acc = 0;
     fold_strided(a.ws.tile_np, uint32_t(lane), t, 64u, [&](uint32_t, uint32_t v) { acc += v; });
     tbase = wave_sum(acc);
+    if (a.ws.status->pad2) return;  // (checked once the reads above are issued)
     if (t + 1 == a.n_tiles && lane == 63) {
       const uint32_t total = tbase + incl;
       a.ws.status->n_pieces = total;
@@ -76,6 +76,7 @@ __global__ void __launch_bounds__(64) k_pieces(EncodeArgs a) {
     }
   } else {
     tbase = a.ws.tile_np[t];
+    if (a.ws.status->pad2) return;
   }
   uint32_t idx = tbase + incl - c;
   const uint32_t base = uint32_t(w * 64);

@@ -27,6 +27,7 @@ __global__ void __launch_bounds__(64) k_count(EncodeArgs a) {
   const bool owned = lane >= 1 && lane <= int(TILE_WORDS) && w < int64_t(a.n_words);
 
   Window win;
+  load_window(a.text, a.n, base, win);
   uint64_t seg_lo, seg_hi;
   uint32_t seg_at;
   WordMasks m;
@@ -276,6 +277,7 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
   const int lane = threadIdx.x;
   const uint32_t t = blockIdx.x;
   const uint32_t T = a.n_tiles;
+
   // the character base of this tile, the last run change before it, and
   // (folded) the character base at the start of each tile before it: from
   // step 2's outputs, or, for texts of at most FUSE_TILES tiles, folded here
@@ -364,6 +366,7 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
   const bool live = lane >= 1 && w < int64_t(a.n_words);  // owned or the right halo
 
   Window win;
+  load_window(a.text, a.n, base, win);
   uint64_t seg_lo, seg_hi;
   uint32_t seg_at;
   WordMasks m;

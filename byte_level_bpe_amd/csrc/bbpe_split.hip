@@ -475,6 +475,7 @@ __device__ __forceinline__ uint64_t split_finish(const SplitWord &o, uint64_t pC
 __device__ __forceinline__ void lane_setup(const EncodeArgs &a, int lane, uint32_t t, int64_t &w,
                                            WordMasks &m, Window &win) {
   w = int64_t(t) * TILE_WORDS + lane - 1;
+  load_window(a.text, a.n, w * 64, win);
   uint64_t seg_lo, seg_hi;
   uint32_t seg_at;
   word_setup<false>(a, w, false, win, seg_lo, seg_hi, seg_at, m);
@@ -502,13 +503,13 @@ __device__ __forceinline__ void wave_scan_fns(uint64_t &ltr, uint32_t &fv, int l
 // Step 4: per-tile transfer functions.
 template <int G>
 __device__ __forceinline__ void split_agg_body(const EncodeArgs &a) {
-  if (a.ws.status->pad2) return;
   const int lane = threadIdx.x;
   const uint32_t t = blockIdx.x;
   int64_t w;
   WordMasks m;
   Window win;
-  lane_setup(a, lane, t, w, m, win);
+  lane_setup(a, lane, t, w, m, win);  // (its reads are bounded whatever the offsets)
+  if (a.ws.status->pad2) return;      // checked once the word's loads are issued
   SplitWord o;
   split_word<G>(a, w, m, o);
   const bool owned = lane >= 1 && lane <= int(TILE_WORDS);
@@ -594,16 +595,55 @@ __device__ __forceinline__ uint32_t carry_direct(const EncodeArgs &a, uint32_t t
   return dig | (x << 8) | (v << 16);
 }
 
+// Entries of the list of merge-unit positions that a wave checks at once.
+constexpr uint32_t REST_LIST = 1024;
+
+// Merge-unit cuts among K positions j (stage indexes, >= 16, of the wave's
+// staged bytes b32), for positions whose byte pair occurs inside a key: j is
+// a cut when neither 3-byte window across it is a key, the pair itself is
+// not one, and no 4-byte window across it may occur inside a key.  Bit k of
+// the result: position k (with has[k]) is a cut.  The table loads of all K
+// positions are issued together.
+template <int K>
+__device__ __forceinline__ uint32_t unit_cuts(const DevTables &T, const uint32_t *b32, const uint32_t *pos,
+                                              const bool *has) {
+  uint32_t hit[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    // bytes j-3 .. j+4
+    const uint32_t q = pos[k] - 3u, d = q >> 2, sh = q & 3u;
+    const uint32_t x0 = b32[d], x1 = b32[d + 1], x2 = b32[d + 2];
+    const uint32_t lo4 = __builtin_amdgcn_alignbyte(x1, x0, sh);
+    const uint32_t hi4 = __builtin_amdgcn_alignbyte(x2, x1, sh);
+    const uint32_t v0 = lo4;                                      // j-3 .. j
+    const uint32_t v1 = __builtin_amdgcn_alignbyte(hi4, lo4, 1);  // j-2 .. j+1
+    const uint32_t v2 = __builtin_amdgcn_alignbyte(hi4, lo4, 2);  // j-1 .. j+2
+    const uint32_t x3a = __builtin_bswap32(v1) >> 8;  // bytes j-2, j-1, j, first byte high
+    const uint32_t x3b = __builtin_bswap32(v2) >> 8;  // bytes j-1, j, j+1
+    const uint32_t pr = ((v2 & 0xFFu) << 8) | ((v2 >> 8) & 0xFFu);  // bytes j-1, j
+    const uint32_t q0 = q4_index(v0), q1 = q4_index(v1), q2 = q4_index(v2);
+    const bool pk = T.pair[pr] != RANK_NONE;
+    const uint32_t h = ((T.k3[x3a >> 5] >> (x3a & 31)) | (T.k3[x3b >> 5] >> (x3b & 31)) |
+                        (T.q4[q0 >> 5] >> (q0 & 31)) | (T.q4[q1 >> 5] >> (q1 & 31)) |
+                        (T.q4[q2 >> 5] >> (q2 & 31))) & 1u;
+    hit[k] = h | (pk ? 1u : 0u);
+  }
+  uint32_t cuts = 0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) cuts |= (has[k] && !hit[k]) ? (1u << k) : 0u;
+  return cuts;
+}
+
 // Step 6: piece-start bits of every word and the number of pieces per tile.
 template <int G>
 __device__ __forceinline__ void split_body(const EncodeArgs &a) {
-  if (a.ws.status->pad2) return;
   const int lane = threadIdx.x;
   const uint32_t t = blockIdx.x;
   int64_t w;
   WordMasks m;
   Window win;
-  lane_setup(a, lane, t, w, m, win);
+  lane_setup(a, lane, t, w, m, win);  // (its reads are bounded whatever the offsets)
+  if (a.ws.status->pad2) return;      // checked once the word's loads are issued
   SplitWord o;
   split_word<G>(a, w, m, o);
   const bool owned = lane >= 1 && lane <= int(TILE_WORDS) && w < int64_t(a.n_words);
@@ -641,7 +681,7 @@ __device__ __forceinline__ void split_body(const EncodeArgs &a) {
     // The pair bitmap goes to LDS first (8 KB, only in waves that have a
     // candidate), and every position is checked without a branch, so that
     // the reads overlap.
-    __shared__ uint32_t s_inner[2048];
+    __shared__ __align__(16) uint32_t s_inner[2048];
     __shared__ uint4 s_bytes[STAGE_BYTES / 16];
     const uint64_t na_prev = shfl_up64(m.na, 1), ll_prev = shfl_up64(m.LL, 1);
     const uint64_t cand = o.IN & ~ps & ~o.SS & m.valid &
@@ -662,39 +702,69 @@ __device__ __forceinline__ void split_body(const EncodeArgs &a) {
       ps |= cand & cut;
       // pairs that occur inside keys: the longer windows, at character
       // boundaries only, eight positions at a time with their loads issued
-      // together
-      uint64_t rest = cand & ~cut & m.lead;
-      const int64_t base = w * 64;
-      const int64_t lo = base - int64_t(lane) * 64 - 16;  // first staged byte
-      while (rest) {
-        constexpr int K = 8;
-        int ii[K];
-        uint32_t b[K][6];  // bytes j-3 .. j+2
+      // together.  Where one lane has many more positions than the wave's
+      // average (so more rounds of loads), the wave's positions go to a
+      // list shared out over its lanes (every 64th entry each) and a cut
+      // found goes back to its word in LDS; else each lane takes its own.
+      const uint64_t rest = owned ? (cand & ~cut & m.lead) : 0ull;
+      const uint32_t cnt = uint32_t(__popcll(rest));
+      const uint32_t incl = wave_incl_sum(cnt, lane);
+      const uint32_t total = __shfl(incl, 63, 64);
+      uint32_t most = cnt;
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          ii[k] = __ffsll(static_cast<unsigned long long>(rest)) - 1;
-          rest &= rest - 1;
+      for (int d = 32; d >= 1; d >>= 1) most = max(most, uint32_t(__shfl_xor(most, d, 64)));
+      const uint32_t *b32 = reinterpret_cast<const uint32_t *>(s_bytes);
+      if ((most + 7) / 8 > (total + 511) / 512) {  // (wave-uniform)
+        // the list and the cuts take the pair bitmap's place
+        static_assert(REST_LIST * 2 + 64 * 8 <= sizeof(s_inner), "list space");
+        uint16_t *s_list = reinterpret_cast<uint16_t *>(s_inner);
+        unsigned long long *s_cut = reinterpret_cast<unsigned long long *>(s_inner + REST_LIST / 2);
+        __syncthreads();
+        s_cut[lane] = 0;
+        const uint32_t w0 = 16u + 64u * uint32_t(lane);  // the word's first byte in the stage
+        for (uint32_t c0 = 0; c0 < total; c0 += REST_LIST) {
+          const uint32_t c1 = min(total, c0 + REST_LIST);
+          uint32_t k = incl - cnt;
+          for (uint64_t x = rest; x && k < c1; x &= x - 1, ++k)
+            if (k >= c0) s_list[k - c0] = uint16_t(w0 + uint32_t(__ffsll(static_cast<unsigned long long>(x)) - 1));
+          __syncthreads();
+          for (uint32_t g0 = 0; g0 < c1 - c0; g0 += 64u * 8u) {
+            constexpr int K = 8;
+            uint32_t pos[K];
+            bool has[K];
 #pragma unroll
-          for (int d = 0; d < 6; ++d) b[k][d] = staged_byte(s_bytes, lo, base + ii[k] - 3 + d);
+            for (int k2 = 0; k2 < K; ++k2) {
+              const uint32_t g = g0 + uint32_t(lane) + 64u * uint32_t(k2);
+              has[k2] = g < c1 - c0;
+              pos[k2] = s_list[has[k2] ? g : 0u];
+            }
+            const uint32_t cuts = unit_cuts<K>(a.T, b32, pos, has);
+#pragma unroll
+            for (int k2 = 0; k2 < K; ++k2)
+              if ((cuts >> k2) & 1u) atomicOr(&s_cut[(pos[k2] - 16u) >> 6], 1ull << ((pos[k2] - 16u) & 63u));
+          }
+          __syncthreads();
         }
-        uint32_t hit[K];
+        ps |= s_cut[lane];
+      } else {
+        const uint32_t w0 = 16u + 64u * uint32_t(lane);
+        for (uint64_t x = rest; x;) {
+          constexpr int K = 8;
+          uint32_t pos[K];
+          bool has[K];
+          int ii[K];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          const uint32_t x3a = (b[k][1] << 16) | (b[k][2] << 8) | b[k][3];
-          const uint32_t x3b = (b[k][2] << 16) | (b[k][3] << 8) | b[k][4];
-          const uint32_t w0 = b[k][0] | (b[k][1] << 8) | (b[k][2] << 16) | (b[k][3] << 24);
-          const uint32_t w1 = b[k][1] | (b[k][2] << 8) | (b[k][3] << 16) | (b[k][4] << 24);
-          const uint32_t w2 = b[k][2] | (b[k][3] << 8) | (b[k][4] << 16) | (b[k][5] << 24);
-          const uint32_t q0 = q4_index(w0), q1 = q4_index(w1), q2 = q4_index(w2);
-          const bool pk = a.T.pair[(b[k][2] << 8) | b[k][3]] != RANK_NONE;
-          const uint32_t h = ((a.T.k3[x3a >> 5] >> (x3a & 31)) | (a.T.k3[x3b >> 5] >> (x3b & 31)) |
-                              (a.T.q4[q0 >> 5] >> (q0 & 31)) | (a.T.q4[q1 >> 5] >> (q1 & 31)) |
-                              (a.T.q4[q2 >> 5] >> (q2 & 31))) & 1u;
-          hit[k] = h | (pk ? 1u : 0u);
+          for (int k2 = 0; k2 < K; ++k2) {
+            ii[k2] = __ffsll(static_cast<unsigned long long>(x)) - 1;  // -1 once none are left
+            x &= x - 1;
+            has[k2] = ii[k2] >= 0;
+            pos[k2] = w0 + uint32_t(has[k2] ? ii[k2] : 0);
+          }
+          const uint32_t cuts = unit_cuts<K>(a.T, b32, pos, has);
+#pragma unroll
+          for (int k2 = 0; k2 < K; ++k2)
+            if ((cuts >> k2) & 1u) ps |= bit(ii[k2]);
         }
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-          if (ii[k] >= 0 && !hit[k]) ps |= bit(ii[k]);
       }
     }
   }

@@ -80,7 +80,8 @@ __device__ __forceinline__ void wave_segment_marks(const uint64_t *__restrict__ 
   seg_at = cum > 0 ? cum - 1 : 0;
 }
 
-// FIRST: compute and store (owners only); else read back.  Words outside
+// The window `win` is loaded by the caller (load_window at w * 64), as early
+// as it can be.  FIRST: compute and store (owners only); else read back.  Words outside
 // [0, n_words) (halo lanes at the ends of the text) always compute.
 template <bool FIRST>
 __device__ __forceinline__ void word_setup(const EncodeArgs &a, int64_t w, bool owned, Window &win,
@@ -88,7 +89,6 @@ __device__ __forceinline__ void word_setup(const EncodeArgs &a, int64_t w, bool 
                                            WordMasks &m) {
   const int64_t base = w * 64;
   const bool in = w >= 0 && w < int64_t(a.n_words);
-  load_window(a.text, a.n, base, win);
   // the first kernel's wave works together (one wave per workgroup, lane =
   // threadIdx.x at consecutive words) in LDS: the segment-start search and
   // the multi-byte decoder
