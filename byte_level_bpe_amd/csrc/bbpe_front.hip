@@ -213,21 +213,27 @@ constexpr uint32_t SP_LDS_BYTES = 1024, SP_LDS_MAX = 255;  // strings' bytes, sp
 __device__ __forceinline__ uint32_t lds_dword_at(const uint32_t *b32, uint32_t q) {
   return __builtin_amdgcn_alignbyte(b32[(q >> 2) + 1], b32[q >> 2], q & 3u);
 }
+// SP_LDS: the specials' strings, offsets and heads are in LDS (two
+// instances, so that their reads compile to LDS reads rather than to
+// generic ones that could address either).
+template <bool SP_LDS>
 __device__ __forceinline__ bool special_at_staged(const EncodeArgs &a, const uint4 *bytes, int64_t lo,
                                                   const uint32_t *sp_lds, const uint32_t *off_lds,
-                                                  const uint32_t *head_lds, bool sp_in_lds, uint64_t p,
-                                                  uint64_t seg_end, uint32_t &len) {
+                                                  const uint32_t *head_lds, const uint32_t *spf_lds,
+                                                  uint64_t p, uint64_t seg_end, uint32_t &len) {
   const uint32_t *b32 = reinterpret_cast<const uint32_t *>(bytes);
-  const uint32_t b = reinterpret_cast<const uint8_t *>(bytes)[int64_t(p) - lo];
-  if (!((a.T.sp_first[b >> 5] >> (b & 31)) & 1)) return false;
+  if (!a.T.sp_nfirst) {  // (else the candidates are exactly the specials' first bytes)
+    const uint32_t b = reinterpret_cast<const uint8_t *>(bytes)[int64_t(p) - lo];
+    if (!((spf_lds[b >> 5] >> (b & 31)) & 1)) return false;
+  }
   // the text's first four bytes at p, read once and held against each
   // special's first four (head_lds, zero past the special's end) before any
   // longer compare
-  const bool head = sp_in_lds && int64_t(p) + 8 <= lo + int64_t(STAGE_BYTES);
+  const bool head = SP_LDS && int64_t(p) + 8 <= lo + int64_t(STAGE_BYTES);
   const uint32_t tv0 = head ? lds_dword_at(b32, uint32_t(int64_t(p) - lo)) : 0u;
   for (uint32_t k = 0; k < a.T.n_sp; ++k) {
-    const uint32_t o = sp_in_lds ? off_lds[k] : a.T.sp_off[k];
-    const uint32_t L = (sp_in_lds ? off_lds[k + 1] : a.T.sp_off[k + 1]) - o;
+    const uint32_t o = SP_LDS ? off_lds[k] : a.T.sp_off[k];
+    const uint32_t L = (SP_LDS ? off_lds[k + 1] : a.T.sp_off[k + 1]) - o;
     if (head) {
       const uint32_t hm = L >= 4 ? 0xFFFFFFFFu : ((1u << (8 * L)) - 1u);
       if ((tv0 ^ head_lds[k]) & hm) continue;
@@ -243,7 +249,7 @@ __device__ __forceinline__ bool special_at_staged(const EncodeArgs &a, const uin
       } else {
         for (uint32_t x = 0; x < nb; ++x) tv |= uint32_t(a.text[q + x]) << (8 * x);
       }
-      if (sp_in_lds) {
+      if (SP_LDS) {
         sv = lds_dword_at(sp_lds, o + j);
       } else {
         for (uint32_t x = 0; x < nb; ++x) sv |= uint32_t(a.T.sp_bytes[o + j + x]) << (8 * x);
@@ -494,8 +500,10 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
     __shared__ uint32_t s_sp[SP_LDS_BYTES / 4 + 2];
     __shared__ uint32_t s_spo[SP_LDS_MAX + 1];
     __shared__ uint32_t s_head[SP_LDS_MAX];
+    __shared__ uint32_t s_spf[8];  // the specials' first bytes, a bitmap
     const int64_t lo = base - int64_t(lane) * 64 - 16;
     stage_window(s_bytes, win, lane);
+    if (lane < 8) s_spf[lane] = a.T.sp_first[lane];
     const uint32_t sp_len = a.T.sp_off[a.T.n_sp];
     const bool sp_in_lds = sp_len <= SP_LDS_BYTES && a.T.n_sp <= SP_LDS_MAX;
     if (sp_in_lds) {  // (the blob is padded by 16 bytes)
@@ -527,7 +535,10 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
       }
       if (!allow_s) continue;
       uint32_t L;
-      if (!special_at_staged(a, s_bytes, lo, s_sp, s_spo, s_head, sp_in_lds, p, min(seg_next, a.n), L)) continue;
+      const uint64_t seg_end = min(seg_next, a.n);
+      if (!(sp_in_lds ? special_at_staged<true>(a, s_bytes, lo, s_sp, s_spo, s_head, s_spf, p, seg_end, L)
+                      : special_at_staged<false>(a, s_bytes, lo, s_sp, s_spo, s_head, s_spf, p, seg_end, L)))
+        continue;
       // no chunk cut strictly inside the special: bits i+1 .. e-1 over this
       // word and the next
       const int e = i + int(L);  // end, exclusive, in [i+1, i+64]
