@@ -624,3 +624,51 @@ def test_multibyte_at_word_edges(atoms):
     with pytest.raises(B.BBPEError) as e:  # a character split by a segment start at a word edge
         tok.encode_segments([(b"x" * 63 + c[:1], False), (c[1:] + b"y", False)])
     assert (e.value.segment, e.value.byte_offset) == (0, 63)
+
+
+def test_dense_multibyte_waves(atoms):
+    """Waves whose words hold more character leads than the decoder's list
+    takes at once (a 64-word wave of 2-byte characters has 2,048 leads; of
+    invalid lead bytes, up to 4,096), so that the list is decoded in pieces:
+    dense 2-, 3- and 4-byte text against the oracle's pieces and ids, and
+    dense invalid lead bytes after valid ones against the first bad byte."""
+    tok, orc = atoms
+    r = random.Random(77)
+    two = "".join(r.choice("абвгдежзийклмнопрстуфхцчшщыэюяΩαβγδéüñ") for _ in range(9000))
+    three = "".join(r.choice("中文字符测试भारत") for _ in range(3000))
+    four = "😀😁🚀🌍" * 600
+    for name, s in (("2-byte", two), ("3-byte", three), ("4-byte", four),
+                    ("mixed", two[:3000] + " " + three[:1000] + four[:300] + "ab ſ's ſ")):
+        segs = [(s.encode(), False)]
+        say("dense multi-byte text:", name, len(segs[0][0]))
+        assert_pieces(tok, orc, segs, what=name)
+        assert_ids(tok, orc, segs, what=name)
+    for lead in (b"\xc0", b"\xff", b"\xc3"):
+        ok = ("é" * 1500).encode()           # 3,000 bytes, 1,500 valid leads
+        bad = ok + lead * 1200 + b" tail"   # then 1,200 lead bytes that start nothing valid
+        say("dense invalid leads", lead)
+        with pytest.raises(B.BBPEError) as e:
+            tok.encode_segments([(b"x", False), (bad, False)])
+        assert e.value.status == B.E_UTF8
+        assert (e.value.segment, e.value.byte_offset) == (1, 1 + 3000)
+        with pytest.raises(OracleError):
+            orc.encode_segments([(b"x", False), (bad, False)])
+
+
+def test_many_segment_starts_in_a_wave(atoms):
+    """More segment starts inside one wave's 4 KB than a wave reads at once
+    (64): thousands of empty and one- to three-byte segments, some of them
+    splitting words and multi-byte runs, between longer ones; pieces, ids
+    and every segment's id offset against the oracle."""
+    tok, orc = atoms
+    r = random.Random(4242)
+    segs = []
+    for k in range(6000):
+        n = r.choice([0, 0, 1, 2, 3, 1, 2])
+        if k % 997 == 0:
+            n = r.randint(100, 3000)
+        s = "".join(r.choice("ab cd\n12é中") for _ in range(n)).encode()
+        segs.append((s, r.random() < 0.3))
+    say("many segment starts: %d segments, %d bytes" % (len(segs), sum(len(s) for s, _ in segs)))
+    assert_pieces(tok, orc, segs, what="many segments")
+    assert_ids(tok, orc, segs, what="many segments")
