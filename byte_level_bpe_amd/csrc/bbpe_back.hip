@@ -251,15 +251,6 @@ struct UnitBytes {
   }
 };
 
-__device__ __forceinline__ uint32_t text_dword(const uint8_t *__restrict__ text, uint64_t n,
-                                               uint64_t addr) {
-  if (addr + 4 <= n) return *reinterpret_cast<const uint32_t *>(text + addr);
-  uint32_t v = 0;
-  for (uint32_t j = 0; j < 4; ++j)
-    if (addr + j < n) v |= uint32_t(text[addr + j]) << (8 * j);
-  return v;
-}
-
 // bytes [s, s+m) of the text, zero beyond m (m <= SK).  The aligned 16-byte
 // chunks that hold them are loaded whole (a chunk holding a byte of the
 // text lies in that byte's page: the text is 16-byte aligned), at most

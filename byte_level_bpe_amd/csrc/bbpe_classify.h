@@ -38,27 +38,12 @@ __device__ __forceinline__ uint64_t bit_range(int i, int len) {
   return hi & ~(bit(i) - 1);
 }
 
-__device__ __forceinline__ bool seg_start_at(uint64_t seg_lo, uint64_t seg_hi, int k) {
-  const int s = k + 8;  // window index k -> segment-mask bit k + 8
-  if (s < 0 || s >= 128) return false;
-  return s < 64 ? ((seg_lo >> s) & 1) : ((seg_hi >> (s - 64)) & 1);
-}
-
 // What the multi-byte characters of a word add to its masks.  Computed once
 // per call (by the first front-end kernel, which stores it for every word
 // holding a byte >= 0x80) and read back by the later ones.
 struct SlowMasks {
   uint64_t LU, LL, LB, N, WS, M, lead, ls0, ls1, err;
 };
-
-__device__ __forceinline__ void add_class(SlowMasks &r, uint32_t cls, uint64_t bits) {
-  r.LU |= (cls == CC_LU) ? bits : 0;
-  r.LL |= (cls == CC_LL) ? bits : 0;
-  r.LB |= (cls == CC_LO) ? bits : 0;
-  r.N |= (cls == CC_N) ? bits : 0;
-  r.WS |= (cls == CC_WS) ? bits : 0;
-  r.M |= (cls == CC_M) ? bits : 0;
-}
 
 // The text bytes of one wave's 64 windows in LDS: bytes [lo, lo + 4128),
 // where lo is 16 bytes before lane 0's word (the windows hold 0 outside the
@@ -73,11 +58,6 @@ __device__ __forceinline__ void stage_window(uint4 *bytes, const Window &win, in
     bytes[1 + 4 * lane + q] = uint4{win.w[4 + 4 * q], win.w[5 + 4 * q], win.w[6 + 4 * q], win.w[7 + 4 * q]};
   if (lane == 0) bytes[0] = uint4{win.w[0], win.w[1], win.w[2], win.w[3]};
   if (lane == 63) bytes[STAGE_BYTES / 16 - 1] = uint4{win.w[20], win.w[21], win.w[22], win.w[23]};
-}
-
-// byte p of the text from a staged tile (p in [lo, lo + STAGE_BYTES))
-__device__ __forceinline__ uint32_t staged_byte(const uint4 *bytes, int64_t lo, int64_t p) {
-  return reinterpret_cast<const uint8_t *>(bytes)[p - lo];
 }
 
 // The wave's multi-byte characters are decoded by all 64 lanes together:

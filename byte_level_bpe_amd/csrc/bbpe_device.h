@@ -183,30 +183,6 @@ struct WordMasks {
   uint32_t err;    // first invalid-sequence byte in [0,64), or 64
 };
 
-__device__ __forceinline__ uint32_t class_of(const DevTables &T, uint32_t cp) {
-  if (cp < 0x80) {
-    const uint32_t lc = cp | 0x20u;
-    if (cp >= 'A' && cp <= 'Z') return CC_LU;
-    if (lc >= 'a' && lc <= 'z') return CC_LL;
-    if (cp >= '0' && cp <= '9') return CC_N;
-    if (cp == ' ' || (cp >= 9 && cp <= 13)) return CC_WS;
-    return CC_OTHER;
-  }
-  const uint32_t blk = T.uni1[cp >> 8];
-  return T.uni2[blk * 256u + (cp & 0xFFu)];
-}
-
-// Length of the UTF-8 sequence announced by a lead byte, 0 if the byte
-// cannot start a sequence.
-__device__ __forceinline__ int utf8_len(uint32_t b) {
-  if (b < 0x80) return 1;
-  if (b < 0xC2) return 0;
-  if (b < 0xE0) return 2;
-  if (b < 0xF0) return 3;
-  if (b < 0xF5) return 4;
-  return 0;
-}
-
 // Segment starts at window indices -8..119 of a lane (bit j <-> index j-8),
 // found by binary search in seg_off[0..n_seg].  Also returns the index of the
 // last non-empty... segment containing byte `base` (or the first segment).
