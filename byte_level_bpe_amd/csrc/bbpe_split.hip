@@ -44,18 +44,16 @@ namespace bbpe {
 //   letter:      the o200k-style automaton, 11 entries of 4 bits.
 //   v (RTL):     state = "the non-CR/LF whitespace continuing here ends at a
 //                non-space character of the span"; 2 entries of 1 bit.
-// A word's or tile's functions are packed in 64 bits: digit in bits 0-7,
-// v in bits 8-9, CR run / letter from bit 16.
+// A word's or tile's functions are packed in 64 bits (the layout per
+// grammar is given with ltr_then below).
 // ---------------------------------------------------------------------------
 constexpr uint32_t FDIG_ID = 0xE4u;  // 3,2,1,0
-constexpr uint32_t FCR_ID = 0x24u;   // 2,1,0
 constexpr uint32_t FV_ID = 0x2u;     // 1,0
 constexpr uint32_t NLET = 11;
 constexpr uint64_t FLET_ID = 0xA9876543210ull;
 constexpr uint64_t FLET_ONES = 0x11111111111ull;
 
 __device__ __forceinline__ uint32_t fdig_apply(uint32_t f, uint32_t s) { return (f >> (2 * s)) & 3u; }
-__device__ __forceinline__ uint32_t fcr_apply(uint32_t f, uint32_t s) { return (f >> (2 * s)) & 3u; }
 __device__ __forceinline__ uint32_t flet_apply(uint64_t f, uint32_t s) { return uint32_t(f >> (4 * s)) & 15u; }
 __device__ __forceinline__ uint32_t fv_apply(uint32_t f, uint32_t s) { return (f >> s) & 1u; }
 // f first, then g
@@ -63,12 +61,6 @@ __device__ __forceinline__ uint32_t fdig_then(uint32_t f, uint32_t g) {
   uint32_t h = 0;
 #pragma unroll
   for (uint32_t s = 0; s < 4; ++s) h |= fdig_apply(g, fdig_apply(f, s)) << (2 * s);
-  return h;
-}
-__device__ __forceinline__ uint32_t fcr_then(uint32_t f, uint32_t g) {
-  uint32_t h = 0;
-#pragma unroll
-  for (uint32_t s = 0; s < 3; ++s) h |= fcr_apply(g, fcr_apply(f, s)) << (2 * s);
   return h;
 }
 __device__ __forceinline__ uint64_t flet_then(uint64_t f, uint64_t g) {
@@ -84,21 +76,46 @@ __device__ __forceinline__ uint32_t fv_then(uint32_t f, uint32_t g) {
   return h;
 }
 
-// The left-to-right part of a packed function (digit + CR run or letter).
+// The left-to-right part of a packed function (digit + CR run or letter)
+// and the lookahead function beside it.  cl100k (G == 0): the digit
+// function's images of states 0..3 in bytes 0..3 and the CR function's of
+// states 0..2 in bytes 4..6, so that composing is one byte permute per
+// part; the lookahead function in bits 56-57 (the CR part's unused byte).
+// o200k-style (G == 1): 2-bit digit images in bits 0-7, the lookahead in
+// bits 8-9, the letter automaton's 4-bit images from bit 16.
 template <int G>
 __device__ __forceinline__ uint64_t ltr_id() {
-  return uint64_t(FDIG_ID) | ((G == 0 ? uint64_t(FCR_ID) : FLET_ID) << 16);
+  return G == 0 ? 0x0302010003020100ull : (uint64_t(FDIG_ID) | (FLET_ID << 16));
 }
 template <int G>
 __device__ __forceinline__ uint64_t ltr_then(uint64_t f, uint64_t g) {
-  const uint64_t d = fdig_then(uint32_t(f & 0xFFu), uint32_t(g & 0xFFu));
-  const uint64_t x = G == 0 ? uint64_t(fcr_then(uint32_t(f >> 16) & 0x3Fu, uint32_t(g >> 16) & 0x3Fu))
-                            : flet_then(f >> 16, g >> 16);
-  return d | (x << 16);
+  if (G == 0) {  // h(s) = g(f(s)): f's bytes select g's (selectors 0..3 pick the second source's bytes)
+    const uint32_t lo = __builtin_amdgcn_perm(0u, uint32_t(g), uint32_t(f));
+    const uint32_t hi = __builtin_amdgcn_perm(0u, uint32_t(g >> 32), uint32_t(f >> 32));
+    return uint64_t(lo) | (uint64_t(hi) << 32);
+  }
+  return fdig_then(uint32_t(f & 0xFFu), uint32_t(g & 0xFFu)) | (flet_then(f >> 16, g >> 16) << 16);
+}
+template <int G>
+__device__ __forceinline__ uint32_t ltr_apply_dig(uint64_t f, uint32_t s) {
+  return G == 0 ? uint32_t(f >> (8 * s)) & 0xFFu : fdig_apply(uint32_t(f & 0xFFu), s);
 }
 template <int G>
 __device__ __forceinline__ uint32_t ltr_apply_x(uint64_t f, uint32_t s) {
-  return G == 0 ? fcr_apply(uint32_t(f >> 16) & 0x3Fu, s) : flet_apply(f >> 16, s);
+  return G == 0 ? uint32_t(f >> (32 + 8 * s)) & 0xFFu : flet_apply(f >> 16, s);
+}
+// the lookahead part, and the packed function without it
+template <int G>
+__device__ __forceinline__ uint32_t fn_v(uint64_t f) {
+  return uint32_t(f >> (G == 0 ? 56 : 8)) & 3u;
+}
+template <int G>
+__device__ __forceinline__ uint64_t fn_ltr(uint64_t f) {
+  return G == 0 ? (f & 0x00FFFFFFFFFFFFFFull) | (uint64_t(3) << 56) : (f & ~uint64_t(0x300));
+}
+template <int G>
+__device__ __forceinline__ uint64_t fn_with_v(uint64_t ltr, uint32_t v) {
+  return G == 0 ? (ltr & 0x00FFFFFFFFFFFFFFull) | (uint64_t(v) << 56) : (ltr | (uint64_t(v) << 8));
 }
 
 // ---------------------------------------------------------------------------
@@ -411,10 +428,15 @@ __device__ __forceinline__ void split_word(const EncodeArgs &a, int64_t w, const
   }
 }
 
+// 2-bit images (state s at bits 2s..2s+1) spread to one byte each
+__device__ __forceinline__ uint32_t spread2(uint32_t f) {
+  return (f & 3u) | ((f & 0xCu) << 6) | ((f & 0x30u) << 12) | ((f & 0xC0u) << 18);
+}
 template <int G>
 __device__ __forceinline__ uint64_t pack_word_fn(const SplitWord &o) {
-  const uint64_t x = G == 0 ? uint64_t(o.f_cr) : o.f_let;
-  return uint64_t(o.f_dig) | (uint64_t(o.f_v) << 8) | (x << 16);
+  if (G == 0)  // (the CR function's byte 3 is never selected: its states are 0..2)
+    return fn_with_v<G>(uint64_t(spread2(o.f_dig)) | (uint64_t(spread2(o.f_cr)) << 32), o.f_v);
+  return uint64_t(o.f_dig) | (uint64_t(o.f_v) << 8) | (o.f_let << 16);
 }
 
 // Per-byte machines with known inputs: digit-group starts, the v bits (VN
@@ -514,11 +536,11 @@ __device__ __forceinline__ void split_agg_body(const EncodeArgs &a) {
   split_word<G>(a, w, m, o);
   const bool owned = lane >= 1 && lane <= int(TILE_WORDS);
   const uint64_t pk = pack_word_fn<G>(o);
-  uint64_t ltr = owned ? (pk & ~uint64_t(0x300)) : ltr_id<G>();
+  uint64_t ltr = owned ? fn_ltr<G>(pk) : ltr_id<G>();
   uint32_t fv = owned ? o.f_v : FV_ID;
   wave_scan_fns<G>(ltr, fv, lane);
   const uint32_t fv0 = __shfl(fv, 0, 64);
-  if (lane == 63) a.ws.tile_fn[t] = ltr | (uint64_t(fv0) << 8);
+  if (lane == 63) a.ws.tile_fn[t] = fn_with_v<G>(ltr, fv0);
 }
 __global__ void __launch_bounds__(64) k_split_agg(EncodeArgs a) { split_agg_body<0>(a); }
 __global__ void __launch_bounds__(64) k_split_agg_o200k(EncodeArgs a) { let_fill(); split_agg_body<1>(a); }
@@ -535,8 +557,8 @@ __device__ __forceinline__ void scan_split_body(const EncodeArgs &a) {
   const uint32_t t0 = tid * per, t1 = min(T, t0 + per);
   uint64_t f = ltr_id<G>();
   uint32_t gv = FV_ID;
-  for (uint32_t t = t0; t < t1; ++t) f = ltr_then<G>(f, a.ws.tile_fn[t] & ~uint64_t(0x300));
-  for (uint32_t t = t1; t > t0; --t) gv = fv_then(gv, uint32_t(a.ws.tile_fn[t - 1] >> 8) & 3u);
+  for (uint32_t t = t0; t < t1; ++t) f = ltr_then<G>(f, fn_ltr<G>(a.ws.tile_fn[t]));
+  for (uint32_t t = t1; t > t0; --t) gv = fv_then(gv, fn_v<G>(a.ws.tile_fn[t - 1]));
   // scans over threads: LTR for (digit, CR / letter), RTL for v
   __shared__ uint64_t s_wf[33];
   __shared__ uint32_t s_wg[33];
@@ -552,19 +574,19 @@ __device__ __forceinline__ void scan_split_body(const EncodeArgs &a) {
   const uint64_t ex_f = tid > 0 ? s_f[tid - 1] : ltr_id<G>();
   const uint32_t ex_g = tid + 1 < 1024 ? s_g[tid + 1] : FV_ID;
   // the text starts outside any digit run, with no CR run / in state F
-  uint32_t dig = fdig_apply(uint32_t(ex_f & 0xFFu), 3u);
+  uint32_t dig = ltr_apply_dig<G>(ex_f, 3u);
   uint32_t x = ltr_apply_x<G>(ex_f, 0u);
   for (uint32_t t = t0; t < t1; ++t) {
     a.ws.tile_carry[t] = (a.ws.tile_carry[t] & ~0xFFFFu) | dig | (x << 8);
     const uint64_t fn = a.ws.tile_fn[t];
-    dig = fdig_apply(uint32_t(fn & 0xFFu), dig);
+    dig = ltr_apply_dig<G>(fn, dig);
     x = ltr_apply_x<G>(fn, x);
   }
   __syncthreads();
   uint32_t v = fv_apply(ex_g, 0u);  // past the end of the text: a break
   for (uint32_t t = t1; t > t0; --t) {
     a.ws.tile_carry[t - 1] = (a.ws.tile_carry[t - 1] & 0xFFFFu) | (v << 16);
-    v = fv_apply(uint32_t(a.ws.tile_fn[t - 1] >> 8) & 3u, v);
+    v = fv_apply(fn_v<G>(a.ws.tile_fn[t - 1]), v);
   }
 }
 __global__ void __launch_bounds__(1024) k_scan_split(EncodeArgs a) { scan_split_body<0>(a); }
@@ -582,14 +604,14 @@ __device__ __forceinline__ uint32_t carry_direct(const EncodeArgs &a, uint32_t t
   const uint32_t per_l = (t + 63) / 64, per_r = (T - 1 - t + 63) / 64;
   uint64_t f = ltr_id<G>();
   const uint32_t l0 = min(t, uint32_t(lane) * per_l), l1 = min(t, l0 + per_l);
-  fold_run(a.ws.tile_fn, l0, l1, [&](uint32_t, uint64_t x) { f = ltr_then<G>(f, x & ~uint64_t(0x300)); });
+  fold_run(a.ws.tile_fn, l0, l1, [&](uint32_t, uint64_t x) { f = ltr_then<G>(f, fn_ltr<G>(x)); });
   uint32_t gv = FV_ID;
   const uint32_t r0 = min(T, t + 1 + uint32_t(lane) * per_r), r1 = min(T, r0 + per_r);
-  fold_run_rev(a.ws.tile_fn, r0, r1, [&](uint32_t, uint64_t x) { gv = fv_then(gv, uint32_t(x >> 8) & 3u); });
+  fold_run_rev(a.ws.tile_fn, r0, r1, [&](uint32_t, uint64_t x) { gv = fv_then(gv, fn_v<G>(x)); });
   wave_scan_fns<G>(f, gv, lane);
   const uint64_t all_f = __shfl(static_cast<unsigned long long>(f), 63, 64);
   const uint32_t all_g = __shfl(gv, 0, 64);
-  const uint32_t dig = fdig_apply(uint32_t(all_f & 0xFFu), 3u);
+  const uint32_t dig = ltr_apply_dig<G>(all_f, 3u);
   const uint32_t x = ltr_apply_x<G>(all_f, 0u);
   const uint32_t v = fv_apply(all_g, 0u);
   return dig | (x << 8) | (v << 16);
@@ -649,7 +671,7 @@ __device__ __forceinline__ void split_body(const EncodeArgs &a) {
   const bool owned = lane >= 1 && lane <= int(TILE_WORDS) && w < int64_t(a.n_words);
   const bool mine = lane >= 1 && lane <= int(TILE_WORDS);
   const uint64_t pk = pack_word_fn<G>(o);
-  uint64_t ltr = mine ? (pk & ~uint64_t(0x300)) : ltr_id<G>();
+  uint64_t ltr = mine ? fn_ltr<G>(pk) : ltr_id<G>();
   uint32_t fv = mine ? o.f_v : FV_ID;
   wave_scan_fns<G>(ltr, fv, lane);
   // exclusive: state entering this lane's word
@@ -658,7 +680,7 @@ __device__ __forceinline__ void split_body(const EncodeArgs &a) {
   if (lane == 0) exl = ltr_id<G>();
   if (lane == 63) exv = FV_ID;
   const uint32_t carry = a.n_tiles <= FUSE_TILES ? carry_direct<G>(a, t, lane) : a.ws.tile_carry[t];
-  const uint32_t ph = fdig_apply(uint32_t(exl & 0xFFu), carry & 0xFFu);
+  const uint32_t ph = ltr_apply_dig<G>(exl, carry & 0xFFu);
   const uint32_t xs = ltr_apply_x<G>(exl, (carry >> 8) & 0xFFu);
   const uint32_t v = fv_apply(exv, (carry >> 16) & 1u);
   const uint64_t pCRm = prev_cr(o);
