@@ -32,14 +32,35 @@ __device__ __forceinline__ uint64_t shfl_down64(uint64_t v, int d) {
   return __shfl_down(static_cast<unsigned long long>(v), d, 64);
 }
 
+// Inclusive scans over the 64 lanes of the wave (every lane active) by DPP
+// moves: row shifts by 1, 2, 4 and 8 within each row of 16 lanes, then the
+// last lane of rows 0 and 2 into rows 1 and 3, then lane 31 into rows 2 and
+// 3.  A lane without a source in a step takes the identity.  op(earlier,
+// later).  (Shuffles through the LDS crossbar wait for it at every step.)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v, uint32_t id) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(id), int(v), CTRL, ROW_MASK, 0xf, false));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_mov(uint64_t v, uint64_t id) {
+  return uint64_t(dpp_mov<CTRL, ROW_MASK>(uint32_t(v), uint32_t(id))) |
+         (uint64_t(dpp_mov<CTRL, ROW_MASK>(uint32_t(v >> 32), uint32_t(id >> 32))) << 32);
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_incl_scan(T v, T id, Op op) {
+  v = op(dpp_mov<0x111, 0xf>(v, id), v);  // row_shr:1
+  v = op(dpp_mov<0x112, 0xf>(v, id), v);  // row_shr:2
+  v = op(dpp_mov<0x114, 0xf>(v, id), v);  // row_shr:4
+  v = op(dpp_mov<0x118, 0xf>(v, id), v);  // row_shr:8
+  v = op(dpp_mov<0x142, 0xa>(v, id), v);  // row_bcast:15
+  v = op(dpp_mov<0x143, 0xc>(v, id), v);  // row_bcast:31
+  return v;
+}
+
 // Inclusive prefix sum over the 64 lanes of the wave.
 __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
-  return v;
+  (void)lane;
+  return wave_incl_scan(v, 0u, [](uint32_t x, uint32_t y) { return x + y; });
 }
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
 #pragma unroll
@@ -111,12 +132,11 @@ __device__ __forceinline__ T block_incl_scan_rev(T v, T id, Op op, T *sh) {
 }
 
 __device__ __forceinline__ int64_t wave_incl_max(int64_t v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int64_t o = __shfl_up(static_cast<long long>(v), d, 64);
-    if (lane >= d && o > v) v = o;
-  }
-  return v;
+  (void)lane;
+  const uint64_t lo = uint64_t(INT64_MIN);  // the identity of max
+  return int64_t(wave_incl_scan(uint64_t(v), lo, [](uint64_t x, uint64_t y) {
+    return int64_t(x) > int64_t(y) ? x : y;
+  }));
 }
 
 // ---------------------------------------------------------------------------

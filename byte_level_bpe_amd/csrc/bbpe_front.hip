@@ -271,12 +271,8 @@ __device__ __forceinline__ uint64_t from_bit(int x) {
 }
 
 __device__ __forceinline__ unsigned long long wave_incl_sum64(unsigned long long v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const unsigned long long o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
-  return v;
+  (void)lane;
+  return wave_incl_scan(static_cast<uint64_t>(v), uint64_t(0), [](uint64_t x, uint64_t y) { return x + y; });
 }
 
 __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {

@@ -513,11 +513,10 @@ __device__ __forceinline__ uint64_t prev_cr(const SplitWord &o) {
 // order, the v part inclusive in reverse lane order.
 template <int G>
 __device__ __forceinline__ void wave_scan_fns(uint64_t &ltr, uint32_t &fv, int lane) {
+  ltr = wave_incl_scan(ltr, ltr_id<G>(), [](uint64_t x, uint64_t y) { return ltr_then<G>(x, y); });
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const uint64_t pl = __shfl_up(static_cast<unsigned long long>(ltr), d, 64);
     const uint32_t nv = __shfl_down(fv, d, 64);
-    if (lane >= d) ltr = ltr_then<G>(pl, ltr);
     if (lane + d < 64) fv = fv_then(nv, fv);
   }
 }
