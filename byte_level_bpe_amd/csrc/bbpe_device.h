@@ -62,10 +62,18 @@ __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v, int lane) {
   (void)lane;
   return wave_incl_scan(v, 0u, [](uint32_t x, uint32_t y) { return x + y; });
 }
+// lane 63's value, in every lane
+__device__ __forceinline__ uint32_t lane63(uint32_t v) { return uint32_t(__builtin_amdgcn_readlane(int(v), 63)); }
+__device__ __forceinline__ uint64_t lane63(uint64_t v) {
+  return uint64_t(lane63(uint32_t(v))) | (uint64_t(lane63(uint32_t(v >> 32))) << 32);
+}
+// op over the 64 lanes, in every lane (every lane active)
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, T id, Op op) {
+  return lane63(wave_incl_scan(v, id, op));
+}
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-  return v;
+  return wave_reduce(v, 0u, [](uint32_t x, uint32_t y) { return x + y; });
 }
 // Inclusive scan of op (associative, identity id) over the threads of a
 // block of NT threads in thread order: a wave scan by shuffles, then the

@@ -47,23 +47,16 @@ __global__ void __launch_bounds__(64) k_count(EncodeArgs a) {
     last = int32_t(excl + uint32_t(__popcll(m.lead & (bit(hb) - 1))));
   }
   // max over lanes
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    int32_t o = __shfl_xor(last, d, 64);
-    last = o > last ? o : last;
-  }
+  last = int32_t(wave_reduce(uint32_t(last), uint32_t(INT32_MIN),
+                             [](uint32_t x, uint32_t y) { return int32_t(x) > int32_t(y) ? x : y; }));
   if (lane == 63) {
     a.ws.tile_nchar[t] = incl;  // owned lanes only contribute
   }
   if (lane == 0) a.ws.tile_lastchg[t] = last;
 
   {
-    unsigned long long e = (owned && m.err < 64) ? (unsigned long long)(base + m.err) : ~0ull;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const unsigned long long o = __shfl_xor(e, d, 64);
-      e = o < e ? o : e;
-    }
+    const uint64_t e = wave_reduce(uint64_t((owned && m.err < 64) ? uint64_t(base + m.err) : ~0ull), uint64_t(~0ull),
+                                   [](uint64_t x, uint64_t y) { return x < y ? x : y; });
     if (lane == 0) a.ws.tile_err[t] = e;
   }
   if (owned) {
@@ -313,13 +306,10 @@ __global__ void __launch_bounds__(64) k_spans(EncodeArgs a) {
     }
     const unsigned long long incl_s = wave_incl_sum64(sum, lane);
     run_excl = incl_s - sum;
-    long long mx = mx_rel >= 0 ? (long long)run_excl + mx_rel : -1;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const long long o = __shfl_xor(mx, d, 64);
-      mx = o > mx ? o : mx;
-    }
-    tile_base = __shfl(incl_s, 63, 64);
+    const long long mx = int64_t(wave_reduce(uint64_t(mx_rel >= 0 ? (long long)run_excl + mx_rel : -1),
+                                             uint64_t(INT64_MIN),
+                                             [](uint64_t x, uint64_t y) { return int64_t(x) > int64_t(y) ? x : y; }));
+    tile_base = lane63(uint64_t(incl_s));
     chg_carry = mx;
     // the offsets check over every tile and the status, by block 0 alone:
     // with offsets that decrease somewhere the other blocks' results are
