@@ -75,7 +75,7 @@ constexpr uint32_t PROBE_BLOCK = 512;
 // Texts of at most FUSE_TILES tiles skip the one-workgroup tile scans of the
 // split functions and of the unit counts: every block of k_split / k_pieces
 // folds the tiles before (and, for the lookahead, after) it itself.
-constexpr uint32_t FUSE_TILES = 2048;
+constexpr uint32_t FUSE_TILES = 4096;
 constexpr uint64_t PROBE_SMALL = 1u << 20;  // texts below this: one unit per probe thread
 constexpr uint64_t PROBE_MID = 1u << 23;    // texts from this: two units per probe thread
 // Texts from this size on use the word cache.  Below it the short tier's

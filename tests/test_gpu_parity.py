@@ -423,13 +423,14 @@ def test_short_units_adversarial_tables(seed):
 
 @pytest.mark.parametrize("extra", [0, 1])
 def test_tile_scans_folded_and_not(extra):
-    """Texts of exactly 2,048 tiles (the split and unit-count scans folded
-    into the per-tile kernels) and one byte more (the one-workgroup scans)."""
+    """Texts of exactly 4,096 tiles (the character, split and unit-count
+    scans folded into the per-tile kernels) and one byte more (the
+    one-workgroup scans)."""
     from synth import configs
     w = configs.main()
     tok, orc = make(w.tokens, w.specials, w.grammar)
     base = w.segments[0][0]
-    n = 2048 * 62 * 64 + extra
+    n = 4096 * 62 * 64 + extra
     text = (base * (n // len(base) + 1))[:n]
     while (text[-1] & 0xC0) == 0x80 or text[-1] >= 0xC0:  # end on a whole character
         text = text[:-1] + b"x"
