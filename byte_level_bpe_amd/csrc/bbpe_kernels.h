@@ -81,7 +81,7 @@ constexpr uint64_t PROBE_MID = 1u << 23;    // texts from this: two units per pr
 // Texts from this size on use the word cache.  Below it the short tier's
 // units fit in about one generation of resident waves, so its length is
 // its longest chain of merge rounds, which the cache's election only delays.
-constexpr uint64_t WORD_CACHE_MIN = 16u << 20;
+constexpr uint64_t WORD_CACHE_MIN = 8u << 20;
 
 constexpr int32_t UID_MERGED = -1;
 constexpr int32_t UID_FOLLOW = -2;  // UID_FOLLOW - j: follows unit j
