@@ -37,14 +37,20 @@ __global__ void __launch_bounds__(1024) k_scan_tiles_np(EncodeArgs a) {
   const uint32_t tid = threadIdx.x;
   const uint32_t per = (T + 1023) / 1024;
   const uint32_t t0 = tid * per, t1 = min(T, t0 + per);
+  // (each thread's tiles FOLD_BATCH at a time, a batch's loads issued first)
   uint32_t sum = 0;
-  for (uint32_t t = t0; t < t1; ++t) sum += a.ws.tile_np[t];
+  fold_run(a.ws.tile_np, t0, t1, [&](uint32_t, uint32_t c) { sum += c; });
   uint32_t total;
   uint32_t run = block_incl_scan<1024>(sum, 0u, [](uint32_t x, uint32_t y) { return x + y; }, s_sum, total) - sum;
-  for (uint32_t t = t0; t < t1; ++t) {
-    const uint32_t c = a.ws.tile_np[t];
-    a.ws.tile_np[t] = run;
-    run += c;
+  for (uint32_t q = t0; q < t1; q += FOLD_BATCH) {
+    uint32_t c[FOLD_BATCH];
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j) c[j] = q + j < t1 ? a.ws.tile_np[q + j] : 0u;
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j) {
+      if (q + j < t1) a.ws.tile_np[q + j] = run;
+      run += c[j];
+    }
   }
   if (tid == 1023) {
     a.ws.tile_np[T] = total;

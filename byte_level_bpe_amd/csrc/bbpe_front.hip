@@ -117,12 +117,26 @@ __global__ void __launch_bounds__(1024) k_scan_chars(EncodeArgs a) {
   const uint32_t tid = threadIdx.x;
   const uint32_t per = (T + 1023) / 1024;
   const uint32_t t0 = tid * per, t1 = min(T, t0 + per);
+  // (each thread's tiles are read FOLD_BATCH at a time, the loads of a
+  // batch issued before any is used)
   unsigned long long sum = 0, err = ~0ull;
   uint32_t bad = 0;
-  for (uint32_t t = t0; t < t1; ++t) {
-    sum += a.ws.tile_nchar[t];
-    err = min(err, a.ws.tile_err[t]);
-    bad |= a.ws.tile_bad[t];
+  for (uint32_t q = t0; q < t1; q += FOLD_BATCH) {
+    uint32_t nc[FOLD_BATCH], bv[FOLD_BATCH];
+    unsigned long long ev[FOLD_BATCH];
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j) {
+      const bool in = q + j < t1;
+      nc[j] = in ? a.ws.tile_nchar[q + j] : 0u;
+      ev[j] = in ? a.ws.tile_err[q + j] : ~0ull;
+      bv[j] = in ? a.ws.tile_bad[q + j] : 0u;
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j) {
+      sum += nc[j];
+      err = min(err, ev[j]);
+      bad |= bv[j];
+    }
   }
   // the status block: first invalid byte, offsets check, counters cleared
   {
@@ -154,11 +168,22 @@ __global__ void __launch_bounds__(1024) k_scan_chars(EncodeArgs a) {
       block_incl_scan<1024>(sum, 0ull, [](unsigned long long x, unsigned long long y) { return x + y; },
                             s_sum, total) - sum;  // exclusive
   long long mx = -1;
-  for (uint32_t t = t0; t < t1; ++t) {
-    a.ws.tile_charbase[t] = run;
-    const int32_t lc = a.ws.tile_lastchg[t];
-    if (lc >= 0) mx = max(mx, (long long)(run + uint32_t(lc)));
-    run += a.ws.tile_nchar[t];
+  const unsigned long long run0 = run;  // characters before this thread's first tile
+  for (uint32_t q = t0; q < t1; q += FOLD_BATCH) {
+    uint32_t nc[FOLD_BATCH];
+    int32_t lcv[FOLD_BATCH];
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j) {
+      const bool in = q + j < t1;
+      nc[j] = in ? a.ws.tile_nchar[q + j] : 0u;
+      lcv[j] = in ? a.ws.tile_lastchg[q + j] : -1;
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j) {
+      if (q + j < t1) a.ws.tile_charbase[q + j] = run;
+      if (lcv[j] >= 0) mx = max(mx, (long long)(run + uint32_t(lcv[j])));
+      run += nc[j];
+    }
   }
   long long mall;
   const long long mincl =
@@ -168,10 +193,22 @@ __global__ void __launch_bounds__(1024) k_scan_chars(EncodeArgs a) {
   s_incl[tid] = mincl;
   __syncthreads();
   long long carry = tid > 0 ? s_incl[tid - 1] : -1;
-  for (uint32_t t = t0; t < t1; ++t) {
-    a.ws.tile_chgcarry[t] = carry;
-    const int32_t lc = a.ws.tile_lastchg[t];
-    if (lc >= 0) carry = max(carry, (long long)(a.ws.tile_charbase[t] + uint32_t(lc)));
+  unsigned long long base = run0;
+  for (uint32_t q = t0; q < t1; q += FOLD_BATCH) {
+    uint32_t nc[FOLD_BATCH];
+    int32_t lcv[FOLD_BATCH];
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j) {
+      const bool in = q + j < t1;
+      nc[j] = in ? a.ws.tile_nchar[q + j] : 0u;
+      lcv[j] = in ? a.ws.tile_lastchg[q + j] : -1;
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j) {
+      if (q + j < t1) a.ws.tile_chgcarry[q + j] = carry;
+      if (lcv[j] >= 0) carry = max(carry, (long long)(base + uint32_t(lcv[j])));
+      base += nc[j];
+    }
   }
   __syncthreads();
   for (uint32_t s = tid; s <= a.n_seg; s += 1024) {

@@ -556,8 +556,9 @@ __device__ __forceinline__ void scan_split_body(const EncodeArgs &a) {
   const uint32_t t0 = tid * per, t1 = min(T, t0 + per);
   uint64_t f = ltr_id<G>();
   uint32_t gv = FV_ID;
-  for (uint32_t t = t0; t < t1; ++t) f = ltr_then<G>(f, fn_ltr<G>(a.ws.tile_fn[t]));
-  for (uint32_t t = t1; t > t0; --t) gv = fv_then(gv, fn_v<G>(a.ws.tile_fn[t - 1]));
+  // (each thread's tiles FOLD_BATCH at a time, a batch's loads issued first)
+  fold_run(a.ws.tile_fn, t0, t1, [&](uint32_t, uint64_t x) { f = ltr_then<G>(f, fn_ltr<G>(x)); });
+  fold_run_rev(a.ws.tile_fn, t0, t1, [&](uint32_t, uint64_t x) { gv = fv_then(gv, fn_v<G>(x)); });
   // scans over threads: LTR for (digit, CR / letter), RTL for v
   __shared__ uint64_t s_wf[33];
   __shared__ uint32_t s_wg[33];
@@ -575,17 +576,36 @@ __device__ __forceinline__ void scan_split_body(const EncodeArgs &a) {
   // the text starts outside any digit run, with no CR run / in state F
   uint32_t dig = ltr_apply_dig<G>(ex_f, 3u);
   uint32_t x = ltr_apply_x<G>(ex_f, 0u);
-  for (uint32_t t = t0; t < t1; ++t) {
-    a.ws.tile_carry[t] = (a.ws.tile_carry[t] & ~0xFFFFu) | dig | (x << 8);
-    const uint64_t fn = a.ws.tile_fn[t];
-    dig = ltr_apply_dig<G>(fn, dig);
-    x = ltr_apply_x<G>(fn, x);
-  }
-  __syncthreads();
   uint32_t v = fv_apply(ex_g, 0u);  // past the end of the text: a break
-  for (uint32_t t = t1; t > t0; --t) {
-    a.ws.tile_carry[t - 1] = (a.ws.tile_carry[t - 1] & 0xFFFFu) | (v << 16);
-    v = fv_apply(fn_v<G>(a.ws.tile_fn[t - 1]), v);
+  // the state entering every tile: the left-to-right parts forward, the
+  // lookahead backward, each tile's carry written once
+  for (uint32_t q = t0; q < t1; q += FOLD_BATCH) {
+    uint64_t fn[FOLD_BATCH];
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j) fn[j] = q + j < t1 ? a.ws.tile_fn[q + j] : 0ull;
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j) {
+      if (q + j >= t1) continue;
+      a.ws.tile_carry[q + j] = dig | (x << 8);  // (the lookahead is added below)
+      dig = ltr_apply_dig<G>(fn[j], dig);
+      x = ltr_apply_x<G>(fn[j], x);
+    }
+  }
+  for (uint32_t q = t1; q > t0; q -= min(q - t0, FOLD_BATCH)) {
+    uint64_t fn[FOLD_BATCH];
+    uint32_t cv[FOLD_BATCH];
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j) {
+      const bool in = q - t0 > j;
+      fn[j] = in ? a.ws.tile_fn[q - 1 - j] : 0ull;
+      cv[j] = in ? a.ws.tile_carry[q - 1 - j] : 0u;
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < FOLD_BATCH; ++j) {
+      if (q - t0 <= j) continue;
+      a.ws.tile_carry[q - 1 - j] = (cv[j] & 0xFFFFu) | (v << 16);
+      v = fv_apply(fn_v<G>(fn[j]), v);
+    }
   }
 }
 __global__ void __launch_bounds__(1024) k_scan_split(EncodeArgs a) { scan_split_body<0>(a); }
